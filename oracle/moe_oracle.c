@@ -1,0 +1,383 @@
+/*
+ * moe_oracle.c -- plain, slow, obviously-correct CPU oracle for the local
+ * W4A16 mixture-of-experts forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: it exists so that tests, the smoke check and the CPU
+ * baseline of the benchmark can compare the HIP kernels against a definition
+ * that a reader can check against the source pages by eye.  It shares no code,
+ * header, table or constant with the GPU library.
+ *
+ * Sources (web pages; cited by tag and section):
+ *   [P1] lmdeploy PR #4947, "feat(pytorch): add CuTeDSL W4A16 MoE backend"
+ *   [P2] flashinfer PR #5186, "perf: reduce split W4A16 routing and output
+ *        overhead"
+ *   [P3] TensorRT-LLM PR #18313, "Add W4A16 per-channel weight-only support
+ *        for Cutlass fused MoE"
+ *
+ * What the method computes (restated from the pages):
+ *   - Expert weights are symmetric INT4 with one 16-bit scale per 32-wide
+ *     group along the reduction dim ([P1] BC-breaking: "INT4 group-size 32",
+ *     BF16 scales), or one scale per output channel ([P3] Checkpoint format);
+ *     scale = absmax / 7, two INT4 values per byte, even logical index in the
+ *     low nibble ([P3] Checkpoint format).
+ *   - Weights are dequantized (q * s) and multiplied with 16-bit activations
+ *     with FP32 accumulation ([P1] Modification).
+ *   - Per route: gate/up GEMM, SiLU(gate) * up (or the non-gated ReLU^2 of
+ *     [P3] Validation), down GEMM ([P1] Benchmark, timed steps).
+ *   - Routes whose expert id is not local are invalid and contribute nothing
+ *     ([P1] Modification, "invalid routes and masked expert counts").
+ *   - Expert outputs are combined in FP32 in fixed top-k order before a single
+ *     16-bit cast ([P2] Description, "Contract").  The oracle returns the FP32
+ *     sum itself: it never rounds to 16 bits.
+ *
+ * Precision: FP32 throughout, as the pages fix it (FP32 accumulation, FP32
+ * combine).  Build with -ffp-contract=off so that no multiply-add is fused and
+ * every sum is the plain ascending-index sum written below.
+ *
+ * Readings of points the pages leave open (each is listed with its reason in
+ * the design notes of the repository):
+ *   - INT4 values are two's-complement signed (-8..7).
+ *   - In group mode the INT4 values are packed along the reduction dim K, in
+ *     per-channel mode along the output dim N.
+ *   - The fused gate/up tensor holds gate rows [0, I) then up rows [I, 2I).
+ *   - silu(z) = z / (1 + exp(-z)).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_DT_BF16 = 0, OR_DT_FP16 = 1 };
+enum { OR_ACT_SILU_GATED = 0, OR_ACT_RELU2 = 1 };
+enum { OR_Q_GROUP_K = 0, OR_Q_PER_CHANNEL = 1 };
+
+/* ------------------------------------------------------------------------ */
+/* 16-bit float encodings (IEEE binary16 and bfloat16), written out by hand.  */
+/* ------------------------------------------------------------------------ */
+
+static float bits_to_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+static uint32_t f32_to_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
+/* bfloat16 is the upper half of a binary32 word. */
+static float bf16_to_f32(uint16_t h) { return bits_to_f32((uint32_t)h << 16); }
+
+/* binary32 -> bfloat16, round to nearest, ties to even; NaN stays NaN. */
+static uint16_t f32_to_bf16(float f) {
+  uint32_t u = f32_to_bits(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7fffu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+/* binary16 -> binary32, exact (normals, subnormals, zeros, inf, NaN). */
+static float f16_to_f32(uint16_t h) {
+  uint32_t sign = (uint32_t)(h >> 15) << 31;
+  uint32_t e = (h >> 10) & 0x1fu, m = h & 0x3ffu;
+  if (e == 0x1f) return bits_to_f32(sign | 0x7f800000u | (m << 13));
+  if (e == 0) {
+    /* subnormal: value = m * 2^-24, exactly representable in binary32 */
+    float v = (float)m * 0x1p-24f;
+    return sign ? -v : v;
+  }
+  return bits_to_f32(sign | ((e + 112u) << 23) | (m << 13));
+}
+
+/* binary32 -> binary16, round to nearest, ties to even, overflow to inf. */
+static uint16_t f32_to_f16(float f) {
+  uint32_t u = f32_to_bits(f);
+  uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return (uint16_t)(sign | 0x7e00u);          /* NaN */
+  if (a >= 0x477ff000u) return (uint16_t)(sign | 0x7c00u);         /* >= 65520 rounds to inf */
+  if (a < 0x38800000u) {
+    /* result is subnormal (or zero): value / 2^-24 rounded to an integer */
+    float v = bits_to_f32(a);
+    float scaled = v * 0x1p24f;                     /* exact: power-of-two scale */
+    float r = nearbyintf(scaled);                   /* default mode: ties to even */
+    return (uint16_t)(sign | (uint16_t)r);          /* r <= 1024 -> may become the min normal */
+  }
+  /* normal range: keep 10 mantissa bits, round the 13 dropped bits */
+  uint32_t e = (a >> 23) - 112u;
+  uint32_t m = a & 0x7fffffu;
+  uint32_t keep = m >> 13, rest = m & 0x1fffu;
+  uint32_t out = (e << 10) | keep;
+  if (rest > 0x1000u || (rest == 0x1000u && (keep & 1u))) out += 1u; /* carry may bump exponent */
+  return (uint16_t)(sign | out);
+}
+
+static float h16_to_f32(uint16_t h, int dtype) {
+  return dtype == OR_DT_FP16 ? f16_to_f32(h) : bf16_to_f32(h);
+}
+static uint16_t f32_to_h16(float f, int dtype) {
+  return dtype == OR_DT_FP16 ? f32_to_f16(f) : f32_to_bf16(f);
+}
+
+void oracle_h16_to_f32(const uint16_t* in, int64_t n, int32_t dtype, float* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = h16_to_f32(in[i], dtype);
+}
+void oracle_f32_to_h16(const float* in, int64_t n, int32_t dtype, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = f32_to_h16(in[i], dtype);
+}
+
+/* ------------------------------------------------------------------------ */
+/* INT4 packing: two values per byte, even logical index in the low nibble,  */
+/* two's-complement signed values ([P3] Checkpoint format).                  */
+/* ------------------------------------------------------------------------ */
+
+static int sext4(int v) { return v >= 8 ? v - 16 : v; }
+
+/* out[2i] = low nibble of packed[i], out[2i+1] = high nibble, sign-extended. */
+void oracle_unpack_int4(const uint8_t* packed, int64_t n_bytes, int8_t* out) {
+  for (int64_t i = 0; i < n_bytes; ++i) {
+    out[2 * i] = (int8_t)sext4(packed[i] & 0xf);
+    out[2 * i + 1] = (int8_t)sext4(packed[i] >> 4);
+  }
+}
+
+/* inverse of unpack for q in [-8, 7]; n must be even. */
+void oracle_pack_int4(const int8_t* q, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n / 2; ++i)
+    out[i] = (uint8_t)(((uint8_t)q[2 * i] & 0xfu) | (((uint8_t)q[2 * i + 1] & 0xfu) << 4));
+}
+
+/* ------------------------------------------------------------------------ */
+/* Symmetric quantization, scale = absmax / 7 ([P3] Checkpoint format).       */
+/* The scale is stored in 16 bits; q = clamp(round_half_even(w / s), -8, 7)   */
+/* with the division by the stored (rounded) scale; an all-zero group has     */
+/* s = 0 and q = 0.                                                          */
+/* ------------------------------------------------------------------------ */
+
+static int8_t quant_one(float w, float s) {
+  if (s == 0.0f) return 0;
+  float r = nearbyintf(w / s);
+  if (r < -8.0f) r = -8.0f;
+  if (r > 7.0f) r = 7.0f;
+  return (int8_t)r;
+}
+
+/* w [rows][cols] -> q [rows][cols], scales [rows][cols/group] */
+void oracle_quantize_group(const float* w, int64_t rows, int64_t cols, int32_t group,
+                           int32_t dtype, int8_t* q, uint16_t* scales) {
+  int64_t ng = cols / group;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t g = 0; g < ng; ++g) {
+      const float* src = w + r * cols + g * group;
+      float amax = 0.0f;
+      for (int32_t j = 0; j < group; ++j) {
+        float a = fabsf(src[j]);
+        if (a > amax) amax = a;
+      }
+      uint16_t sb = f32_to_h16(amax / 7.0f, dtype);
+      scales[r * ng + g] = sb;
+      float s = h16_to_f32(sb, dtype);
+      for (int32_t j = 0; j < group; ++j) q[r * cols + g * group + j] = quant_one(src[j], s);
+    }
+}
+
+/* w [rows][cols], one scale per row (output channel) -> q [rows][cols], scales [rows] */
+void oracle_quantize_per_channel(const float* w, int64_t rows, int64_t cols, int32_t dtype,
+                                 int8_t* q, uint16_t* scales) {
+  for (int64_t r = 0; r < rows; ++r) {
+    float amax = 0.0f;
+    for (int64_t j = 0; j < cols; ++j) {
+      float a = fabsf(w[r * cols + j]);
+      if (a > amax) amax = a;
+    }
+    uint16_t sb = f32_to_h16(amax / 7.0f, dtype);
+    scales[r] = sb;
+    float s = h16_to_f32(sb, dtype);
+    for (int64_t j = 0; j < cols; ++j) q[r * cols + j] = quant_one(w[r * cols + j], s);
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dequantization of one expert's matrix of logical shape [n_out][k_in].      */
+/* Group mode: packed [n_out][k_in/2] along K, scales [n_out][k_in/group].    */
+/* Per-channel: packed [n_out/2][k_in] along N, scales [n_out].               */
+/* W[n][k] = float(q[n][k]) * float(s), exact in FP32.                       */
+/* ------------------------------------------------------------------------ */
+
+void oracle_dequant_matrix(const uint8_t* packed, const uint16_t* scales, int64_t n_out,
+                           int64_t k_in, int32_t layout, int32_t group, int32_t dtype,
+                           float* w_out) {
+  for (int64_t n = 0; n < n_out; ++n)
+    for (int64_t k = 0; k < k_in; ++k) {
+      int q;
+      float s;
+      if (layout == OR_Q_GROUP_K) {
+        uint8_t b = packed[n * (k_in / 2) + k / 2];
+        q = sext4((k % 2 == 0) ? (b & 0xf) : (b >> 4));
+        s = h16_to_f32(scales[n * (k_in / group) + k / group], dtype);
+      } else {
+        uint8_t b = packed[(n / 2) * k_in + k];
+        q = sext4((n % 2 == 0) ? (b & 0xf) : (b >> 4));
+        s = h16_to_f32(scales[n], dtype);
+      }
+      w_out[n * k_in + k] = (float)q * s;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Route preparation ([P1] Benchmark: "route preparation"; [P2] Description: */
+/* route guards, padded fallback; [P1] Modification: invalid routes, masked  */
+/* expert counts).                                                           */
+/*   valid(t,k) iff off <= ids[t,k] < off + E, local expert e = id - off     */
+/*   counts[e]     number of valid routes of e                               */
+/*   offsets[e]    exclusive prefix sum of round_up(counts[e], block_m),     */
+/*                 offsets[E] = padded total                                 */
+/*   sorted[p]     flat route index t*K+k, ascending within each expert;     */
+/*                 padding positions hold -1                                 */
+/*   slot[t*K+k]   position p of the route in sorted, or -1 if invalid       */
+/* Returns the padded total, or -1 if it exceeds sorted_cap.                 */
+/* ------------------------------------------------------------------------ */
+
+int64_t oracle_prepare_routes(const int32_t* ids, int64_t T, int32_t K, int32_t E, int32_t off,
+                              int32_t block_m, int32_t* counts, int32_t* offsets, int32_t* sorted,
+                              int64_t sorted_cap, int32_t* slot) {
+  int64_t R = T * (int64_t)K;
+  for (int32_t e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t r = 0; r < R; ++r) {
+    int64_t g = ids[r];
+    if (g >= off && g < (int64_t)off + E) counts[g - off] += 1;
+  }
+  int64_t acc = 0;
+  for (int32_t e = 0; e < E; ++e) {
+    offsets[e] = (int32_t)acc;
+    acc += ((int64_t)counts[e] + block_m - 1) / block_m * block_m;
+  }
+  offsets[E] = (int32_t)acc;
+  if (acc > sorted_cap) return -1;
+  for (int64_t p = 0; p < acc; ++p) sorted[p] = -1;
+  int32_t* fill = (int32_t*)calloc((size_t)(E > 0 ? E : 1), sizeof(int32_t));
+  for (int64_t r = 0; r < R; ++r) {
+    int64_t g = ids[r];
+    if (g >= off && g < (int64_t)off + E) {
+      int32_t e = (int32_t)(g - off);
+      int64_t p = offsets[e] + fill[e];
+      fill[e] += 1;
+      sorted[p] = (int32_t)r;
+      slot[r] = (int32_t)p;
+    } else {
+      slot[r] = -1;
+    }
+  }
+  free(fill);
+  return acc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The forward pass.                                                         */
+/*   x       [T][H] 16-bit (bf16 or fp16 by dtype), upcast exactly to FP32   */
+/*   w13     gate/up (gated: N1 = 2I rows, gate [0,I), up [I,2I)) or the     */
+/*           non-gated w1 (N1 = I rows), logical shape [E][N1][H]            */
+/*   w2      down projection, logical shape [E][H][I]                        */
+/*   ids     [T][K] global expert ids, wts [T][K] FP32 routing weights       */
+/*   out     [T][H] FP32: sum over k ascending of wts*y over valid routes;   */
+/*           exactly 0 for a token without a valid route                     */
+/*   y_route optional [T*K][H] FP32 per-route expert outputs (rows of        */
+/*           invalid routes are left untouched)                              */
+/* ------------------------------------------------------------------------ */
+
+static float silu(float z) { return z / (1.0f + expf(-z)); }
+
+int oracle_moe_forward(int64_t T, int32_t H, int32_t I, int32_t E, int32_t off, int32_t K,
+                       int32_t group, int32_t act, int32_t layout, int32_t dtype,
+                       const uint16_t* x, const uint8_t* w13p, const uint16_t* w13s,
+                       const uint8_t* w2p, const uint16_t* w2s, const int32_t* ids,
+                       const float* wts, float* out, float* y_route, int32_t nthreads) {
+  const int64_t N1 = (act == OR_ACT_SILU_GATED) ? 2 * (int64_t)I : I;
+  const int64_t R = T * (int64_t)K;
+  /* bytes and scale entries per expert in each layout */
+  const int64_t w13_bytes = N1 * H / 2, w2_bytes = (int64_t)H * I / 2;
+  const int64_t w13_sc = (layout == OR_Q_GROUP_K) ? N1 * (H / group) : N1;
+  const int64_t w2_sc = (layout == OR_Q_GROUP_K) ? (int64_t)H * (I / group) : H;
+
+  float* Y = y_route ? y_route : (float*)malloc((size_t)(R > 0 ? R : 1) * H * sizeof(float));
+  if (!Y) return -1;
+
+  /* upcast x once (exact) */
+  float* xf = (float*)malloc((size_t)(T > 0 ? T : 1) * H * sizeof(float));
+  if (!xf) { if (!y_route) free(Y); return -1; }
+  for (int64_t i = 0; i < T * H; ++i) xf[i] = h16_to_f32(x[i], dtype);
+
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+
+  /* one expert at a time: dequantize it, then run every route that chose it */
+#pragma omp parallel
+  {
+    float* W13 = (float*)malloc((size_t)N1 * H * sizeof(float));
+    float* W2 = (float*)malloc((size_t)H * I * sizeof(float));
+    float* h = (float*)malloc((size_t)N1 * sizeof(float));
+    float* a = (float*)malloc((size_t)I * sizeof(float));
+#pragma omp for schedule(dynamic, 1)
+    for (int32_t e = 0; e < E; ++e) {
+      int any = 0;
+      for (int64_t r = 0; r < R && !any; ++r) any = (ids[r] == off + e);
+      if (!any) continue;
+      oracle_dequant_matrix(w13p + e * w13_bytes, w13s + e * w13_sc, N1, H, layout, group, dtype, W13);
+      oracle_dequant_matrix(w2p + e * w2_bytes, w2s + e * w2_sc, H, I, layout, group, dtype, W2);
+      for (int64_t r = 0; r < R; ++r) {
+        if (ids[r] != off + e) continue;
+        const float* xr = xf + (r / K) * H;
+        /* gate/up (or w1) GEMM: ascending reduction index */
+        for (int64_t n = 0; n < N1; ++n) {
+          float s = 0.0f;
+          for (int32_t j = 0; j < H; ++j) s += xr[j] * W13[n * H + j];
+          h[n] = s;
+        }
+        /* activation */
+        for (int32_t i = 0; i < I; ++i) {
+          if (act == OR_ACT_SILU_GATED) {
+            a[i] = silu(h[i]) * h[I + i];
+          } else {
+            float p = h[i] > 0.0f ? h[i] : 0.0f;
+            a[i] = p * p;
+          }
+        }
+        /* down GEMM */
+        float* yr = Y + r * H;
+        for (int32_t m = 0; m < H; ++m) {
+          float s = 0.0f;
+          for (int32_t i = 0; i < I; ++i) s += a[i] * W2[(int64_t)m * I + i];
+          yr[m] = s;
+        }
+      }
+    }
+    free(W13); free(W2); free(h); free(a);
+  }
+
+  /* combine: FP32, fixed top-k order, invalid routes skipped */
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    for (int32_t m = 0; m < H; ++m) {
+      float acc = 0.0f;
+      for (int32_t k = 0; k < K; ++k) {
+        int64_t r = t * K + k;
+        int64_t g = ids[r];
+        if (g >= off && g < (int64_t)off + E) acc += wts[r] * Y[r * H + m];
+      }
+      out[t * H + m] = acc;
+    }
+  }
+
+  free(xf);
+  if (!y_route) free(Y);
+  return 0;
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -1,0 +1,440 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each test fixes part of the oracle against mathematics or an independent
+implementation: the page's packing rule on hand-written bytes, exact round
+trips, closed-form outputs, a float64 numpy textbook FFN, a dense brute-force
+evaluation of every expert, brute-force route tables and exact invariances.
+A plausible slip anywhere in the oracle (a swapped nibble, gate/up order, a
+dropped route, a wrong index or sign) fails at least one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from w4a16_mixture_experts_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# independent helpers (numpy bit tricks, float64)
+# ---------------------------------------------------------------------------
+
+def np_unpack(b):
+    """Sign-extend nibbles with arithmetic shifts (no branches, no table)."""
+    b = np.asarray(b, np.uint8)
+    lo = (b << 4).view(np.int8) >> 4
+    hi = b.view(np.int8) >> 4
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+def np_h16(bits, dtype):
+    bits = np.asarray(bits, np.uint16)
+    if dtype == oracle.DT_BF16:
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return bits.view(np.float16).astype(np.float64)
+
+
+def np_dequant(packed, scales, layout, dtype, group=32):
+    """fp64 dequantized [E, n_out, k_in] from packed weights, written independently."""
+    packed = np.asarray(packed)
+    s = np_h16(scales, dtype)
+    if layout == oracle.Q_GROUP_K:
+        q = np_unpack(packed).astype(np.float64)             # [E, n, k]
+        E, n, k = q.shape
+        return q * np.repeat(s, group, axis=2)
+    # per-channel: packed [E, n/2, k] along n
+    E, half, k = packed.shape
+    lo = ((packed << 4).view(np.int8) >> 4).astype(np.float64)
+    hi = (packed.view(np.int8) >> 4).astype(np.float64)
+    q = np.empty((E, 2 * half, k))
+    q[:, 0::2, :] = lo
+    q[:, 1::2, :] = hi
+    return q * s[:, :, None]
+
+
+def np_ffn(x, w13, w2, gated):
+    h = x @ w13.T
+    if gated:
+        I = w13.shape[0] // 2
+        g, u = h[..., :I], h[..., I:]
+        a = g / (1.0 + np.exp(-g)) * u
+    else:
+        a = np.maximum(h, 0.0) ** 2
+    return a @ w2.T
+
+
+def bits(t):
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def run_oracle(wl, W, tok, **kw):
+    return oracle.moe_forward(
+        bits(tok.x), W.w13_packed.numpy(), bits(W.w13_scales), W.w2_packed.numpy(),
+        bits(W.w2_scales), tok.topk_ids.numpy(), tok.topk_weights.numpy(), hidden=wl.hidden,
+        inter=wl.inter, num_experts=wl.num_experts, expert_offset=wl.expert_offset,
+        act=oracle.ACT_SILU_GATED if wl.gated else oracle.ACT_RELU2,
+        layout=oracle.Q_PER_CHANNEL if wl.per_channel else oracle.Q_GROUP_K,
+        dtype=oracle.DT_FP16 if wl.dtype == torch.float16 else oracle.DT_BF16, **kw)
+
+
+def dt_code(wl):
+    return oracle.DT_FP16 if wl.dtype == torch.float16 else oracle.DT_BF16
+
+
+# ---------------------------------------------------------------------------
+# 16-bit conversions against numpy / torch
+# ---------------------------------------------------------------------------
+
+SPECIALS = np.array([0.0, -0.0, 1.0, -1.0, 65504.0, 65519.0, 65520.0, 1e30, -1e30, np.inf,
+                     -np.inf, 6.1e-5, 5.96e-8, 2.98e-8, 2.99e-8, 1e-40, 3.0e38, 1.00390625,
+                     1.0078125, 1.01171875, 0.1, 1.0 / 3.0], np.float32)
+
+
+@pytest.mark.parametrize("dtype", [oracle.DT_BF16, oracle.DT_FP16])
+def test_h16_conversions_match_numpy_and_torch(dtype):
+    rng = np.random.default_rng(1)
+    x = np.concatenate([SPECIALS, rng.standard_normal(20000).astype(np.float32) * 10,
+                        (rng.standard_normal(5000) * 1e-6).astype(np.float32)])
+    got = oracle.f32_to_h16(x, dtype)
+    if dtype == oracle.DT_FP16:
+        want = x.astype(np.float16).view(np.uint16)
+    else:
+        want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, want)
+    # every 16-bit pattern back to fp32 (NaNs compared as NaN)
+    allbits = np.arange(65536, dtype=np.uint16)
+    back = oracle.h16_to_f32(allbits, dtype)
+    ref = np_h16(allbits, dtype).astype(np.float32)
+    np.testing.assert_array_equal(np.isnan(back), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(back[ok].view(np.uint32), ref[ok].view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# packing (page rule, exhaustive)
+# ---------------------------------------------------------------------------
+
+def test_nibble_fixture():
+    rows = [ln.split() for ln in open(os.path.join(GOLDEN, "nibbles.txt"))
+            if ln.strip() and not ln.startswith("#")]
+    b = np.array([int(r[0], 16) for r in rows], np.uint8)
+    want = np.array([[int(r[1]), int(r[2])] for r in rows], np.int8).reshape(-1)
+    np.testing.assert_array_equal(oracle.unpack_int4(b), want)
+    np.testing.assert_array_equal(oracle.pack_int4(want), b)
+
+
+def test_nibbles_exhaustive_and_round_trip():
+    b = np.arange(256, dtype=np.uint8)
+    q = oracle.unpack_int4(b)
+    np.testing.assert_array_equal(q, np_unpack(b))
+    assert q.min() == -8 and q.max() == 7
+    np.testing.assert_array_equal(oracle.pack_int4(q), b)
+    pairs = np.array([[lo, hi] for lo in range(-8, 8) for hi in range(-8, 8)], np.int8).ravel()
+    np.testing.assert_array_equal(oracle.unpack_int4(oracle.pack_int4(pairs)), pairs)
+
+
+# ---------------------------------------------------------------------------
+# quantizer: exact round trip, an exact-rational example, the generator
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [oracle.DT_BF16, oracle.DT_FP16])
+def test_quantize_dequant_round_trip(dtype):
+    rng = np.random.default_rng(2)
+    rows, cols = 16, 128
+    q = rng.integers(-7, 8, size=(rows, cols)).astype(np.int8)
+    q[:, ::32] = rng.choice([-7, 7], size=(rows, cols // 32))      # every group hits |q| = 7
+    s = oracle.f32_to_h16(np.exp(rng.uniform(-9, -2, size=(rows, cols // 32))), dtype)
+    w = q.astype(np.float32) * np.repeat(oracle.h16_to_f32(s, dtype), 32, axis=1)
+    q2, s2 = oracle.quantize_group(w, 32, dtype)
+    np.testing.assert_array_equal(s2, s)
+    np.testing.assert_array_equal(q2, q)
+    # per-channel: one |q| = 7 per row
+    qc = rng.integers(-7, 8, size=(rows, cols)).astype(np.int8)
+    qc[:, 5] = 7
+    sc = oracle.f32_to_h16(np.exp(rng.uniform(-9, -2, size=rows)), dtype)
+    wc = qc.astype(np.float32) * oracle.h16_to_f32(sc, dtype)[:, None]
+    q3, s3 = oracle.quantize_per_channel(wc, dtype)
+    np.testing.assert_array_equal(s3, sc)
+    np.testing.assert_array_equal(q3, qc)
+
+
+def test_quantize_exact_rational_example():
+    """scale = absmax/7 rounded to bf16; q = nearest (ties to even) of w/scale."""
+    from fractions import Fraction as F
+    w = np.zeros((1, 32), np.float32)
+    w[0, :6] = [0.7, -0.35, 0.05, -0.7, 0.3, 0.0]
+    q, s = oracle.quantize_group(w, 32, oracle.DT_BF16)
+    sv = float(np_h16(s, oracle.DT_BF16)[0, 0])
+    # bf16 of 0.1 (0.7/7 in fp32) is 0.10009765625 = 205 * 2^-11
+    assert sv == 205 * 2.0 ** -11
+    want = []
+    for v in w[0]:
+        r = F(float(v)) / F(sv)
+        fl = math.floor(r)
+        frac = r - fl
+        n = fl + (1 if frac > F(1, 2) or (frac == F(1, 2) and fl % 2 == 1) else 0)
+        want.append(max(-8, min(7, n)))
+    np.testing.assert_array_equal(q[0], np.array(want, np.int8))
+    assert list(q[0, :6]) == [7, -3, 0, -7, 3, 0]
+    # an all-zero group has scale 0 and codes 0
+    qz, sz = oracle.quantize_group(np.zeros((2, 64), np.float32), 32, oracle.DT_BF16)
+    assert not qz.any() and not sz.any()
+
+
+@pytest.mark.parametrize("per_channel,dtype", [(False, torch.bfloat16), (True, torch.bfloat16),
+                                               (False, torch.float16), (True, torch.float16)])
+def test_generator_quantizer_equals_oracle(per_channel, dtype):
+    wl = synth.custom(E=2, H=64, I=96, K=2, per_channel=per_channel, dtype=dtype, seed=5)
+    W = synth.make_weights(wl)
+    masters = synth.make_weights_fp32(wl)
+    dt = dt_code(wl)
+    for e, (w13, w2) in enumerate(masters):
+        for w, packed, sc in ((w13, W.w13_packed[e], W.w13_scales[e]),
+                              (w2, W.w2_packed[e], W.w2_scales[e])):
+            if per_channel:
+                q, s = oracle.quantize_per_channel(w.numpy(), dt)
+                want_packed = oracle.pack_int4(q.T.copy()).T       # pairs of rows
+            else:
+                q, s = oracle.quantize_group(w.numpy(), 32, dt)
+                want_packed = oracle.pack_int4(q)
+            np.testing.assert_array_equal(bits(sc), s)
+            np.testing.assert_array_equal(packed.numpy(), want_packed)
+
+
+@pytest.mark.parametrize("layout", [oracle.Q_GROUP_K, oracle.Q_PER_CHANNEL])
+def test_dequant_matrix_matches_numpy(layout):
+    wl = synth.custom(E=1, H=64, I=96, K=1, per_channel=layout == oracle.Q_PER_CHANNEL, seed=3)
+    W = synth.make_weights(wl)
+    got = oracle.dequant_matrix(W.w13_packed[0].numpy(), bits(W.w13_scales[0]), 2 * 96, 64,
+                                layout, 32, oracle.DT_BF16)
+    want = np_dequant(W.w13_packed.numpy(), bits(W.w13_scales), layout, oracle.DT_BF16)[0]
+    np.testing.assert_array_equal(got.astype(np.float64), want)       # q*s exact in fp32
+
+
+# ---------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------
+
+def _golden_closed_form():
+    vals = {}
+    for ln in open(os.path.join(GOLDEN, "closed_form.txt")):
+        ln = ln.split("#")[0].strip()
+        if ln:
+            k, v = ln.split()[:2]
+            vals[k] = float(v)
+    return vals
+
+
+def _bf16_bits(v):
+    return int(torch.tensor(v, dtype=torch.float32).to(torch.bfloat16).view(torch.int16)) & 0xFFFF
+
+
+def _closed_form_case(per_channel, gated=True, x_val=1.0, K=1, wts=(1.0,)):
+    E, H, I = 1, 64, 32
+    N1 = 2 * I if gated else I
+    q13 = np.ones((N1, H), np.int8)
+    if gated:
+        q13[I:] = 2
+    q2 = np.ones((H, I), np.int8)
+    s6, s5 = _bf16_bits(2.0 ** -6), _bf16_bits(2.0 ** -5)
+    if per_channel:
+        w13p = oracle.pack_int4(q13.T.copy()).T[None].copy()
+        w2p = oracle.pack_int4(q2.T.copy()).T[None].copy()
+        w13s = np.full((1, N1), s6, np.uint16)
+        w2s = np.full((1, H), s5, np.uint16)
+    else:
+        w13p = oracle.pack_int4(q13)[None]
+        w2p = oracle.pack_int4(q2)[None]
+        w13s = np.full((1, N1, H // 32), s6, np.uint16)
+        w2s = np.full((1, H, I // 32), s5, np.uint16)
+    x = np.full((1, H), _bf16_bits(x_val), np.uint16)
+    ids = np.zeros((1, K), np.int32)
+    w = np.array([wts], np.float32)
+    return oracle.moe_forward(x, w13p, w13s, w2p, w2s, ids, w, hidden=H, inter=I, num_experts=E,
+                              act=oracle.ACT_SILU_GATED if gated else oracle.ACT_RELU2,
+                              layout=oracle.Q_PER_CHANNEL if per_channel else oracle.Q_GROUP_K)
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_closed_form(per_channel):
+    g = _golden_closed_form()
+    out = _closed_form_case(per_channel)
+    assert out.shape == (1, 64)
+    np.testing.assert_allclose(out, g["gated_out"], rtol=1e-6)
+    assert abs(out[0, 0] - g["gated_out_swapped"]) > 0.1          # gate rows come first
+    assert _bf16_bits(float(out[0, 0])) == _bf16_bits(g["gated_out_bf16"])
+    np.testing.assert_allclose(_closed_form_case(per_channel, gated=False), g["relu2_out_x_pos"],
+                               rtol=0)
+    np.testing.assert_array_equal(_closed_form_case(per_channel, gated=False, x_val=-1.0),
+                                  g["relu2_out_x_neg"])
+    dup = _closed_form_case(per_channel, K=2, wts=(0.25, 0.5))
+    np.testing.assert_allclose(dup, g["dup_routes_0.25_0.5"], rtol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# textbook FFN and dense brute force (float64 numpy)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("per_channel,gated,dtype", [
+    (False, True, torch.bfloat16), (True, True, torch.bfloat16),
+    (False, False, torch.float16), (True, False, torch.float16)])
+def test_single_expert_equals_textbook_ffn(per_channel, gated, dtype):
+    wl = synth.custom(E=3, H=128, I=64, K=1, gated=gated, per_channel=per_channel, dtype=dtype,
+                      seed=11)
+    W = synth.make_weights(wl)
+    tok = synth.make_tokens(wl, 5)
+    tok.topk_ids[:] = 1
+    tok.topk_weights[:] = 1.0
+    out = run_oracle(wl, W, tok)
+    lay = oracle.Q_PER_CHANNEL if per_channel else oracle.Q_GROUP_K
+    dt = dt_code(wl)
+    w13 = np_dequant(W.w13_packed.numpy(), bits(W.w13_scales), lay, dt)[1]
+    w2 = np_dequant(W.w2_packed.numpy(), bits(W.w2_scales), lay, dt)[1]
+    x = np_h16(bits(tok.x), dt)
+    want = np_ffn(x, w13, w2, gated)
+    np.testing.assert_allclose(out, want, rtol=1e-4, atol=1e-5 * np.abs(want).max())
+
+
+@pytest.mark.parametrize("per_channel,gated,offset,E_global", [
+    (False, True, 0, 6), (True, True, 0, 6), (False, False, 0, 6), (False, True, 4, 16)])
+def test_brute_force_dense_all_experts(per_channel, gated, offset, E_global):
+    E, H, I, K, T = 6, 64, 96, 3, 7
+    wl = synth.custom(E=E, H=H, I=I, K=K, gated=gated, per_channel=per_channel, seed=23,
+                      E_global=E_global, offset=offset)
+    W = synth.make_weights(wl)
+    tok = synth.make_tokens(wl, T)
+    ids = tok.topk_ids.numpy()
+    # plant invalid ids: negative, past the end, and (with an offset) below it
+    ids[0, 1] = -1
+    ids[2, 0] = offset + E + 3
+    ids[3, :] = -7                                            # a token without a valid route
+    out = run_oracle(wl, W, tok)
+    lay = oracle.Q_PER_CHANNEL if per_channel else oracle.Q_GROUP_K
+    w13 = np_dequant(W.w13_packed.numpy(), bits(W.w13_scales), lay, oracle.DT_BF16)
+    w2 = np_dequant(W.w2_packed.numpy(), bits(W.w2_scales), lay, oracle.DT_BF16)
+    x = np_h16(bits(tok.x), oracle.DT_BF16)
+    Y = np.stack([np_ffn(x, w13[e], w2[e], gated) for e in range(E)], axis=1)   # [T, E, H]
+    M = np.zeros((T, E))
+    for t in range(T):
+        for k in range(K):
+            e = ids[t, k] - offset
+            if 0 <= e < E:
+                M[t, e] += tok.topk_weights[t, k].item()
+    want = np.einsum("te,teh->th", M, Y)
+    scale = np.abs(want).max()
+    np.testing.assert_allclose(out, want, rtol=1e-4, atol=1e-5 * scale)
+    assert not out[3].any() and not np.signbit(out[3]).any()        # exactly +0
+
+
+def test_per_route_outputs_match_brute_force():
+    E, H, I, K, T = 4, 64, 64, 2, 5
+    wl = synth.custom(E=E, H=H, I=I, K=K, seed=31)
+    W = synth.make_weights(wl)
+    tok = synth.make_tokens(wl, T)
+    tok.topk_ids[1, 1] = 99
+    out, yr = run_oracle(wl, W, tok, want_routes=True)
+    w13 = np_dequant(W.w13_packed.numpy(), bits(W.w13_scales), oracle.Q_GROUP_K, oracle.DT_BF16)
+    w2 = np_dequant(W.w2_packed.numpy(), bits(W.w2_scales), oracle.Q_GROUP_K, oracle.DT_BF16)
+    x = np_h16(bits(tok.x), oracle.DT_BF16)
+    for t in range(T):
+        for k in range(K):
+            e = int(tok.topk_ids[t, k])
+            r = t * K + k
+            if e >= E:
+                assert np.isnan(yr[r]).all()                       # never written
+                continue
+            want = np_ffn(x[t], w13[e], w2[e], True)
+            np.testing.assert_allclose(yr[r], want, rtol=1e-4, atol=1e-5 * np.abs(want).max())
+
+
+# ---------------------------------------------------------------------------
+# exact invariances
+# ---------------------------------------------------------------------------
+
+def test_invariances_bitwise():
+    E, H, I, K, T = 5, 64, 64, 3, 9
+    wl = synth.custom(E=E, H=H, I=I, K=K, seed=41)
+    W = synth.make_weights(wl)
+    tok = synth.make_tokens(wl, T)
+    base = run_oracle(wl, W, tok)
+    # (i) weights x2 -> output x2 exactly
+    tok2 = synth.Tokens(tok.x, tok.topk_ids, tok.topk_weights * 2)
+    np.testing.assert_array_equal(run_oracle(wl, W, tok2), base * 2)
+    # (ii) token permutation -> output permutation exactly
+    perm = torch.randperm(T, generator=torch.Generator().manual_seed(0))
+    tokp = synth.Tokens(tok.x[perm].contiguous(), tok.topk_ids[perm].contiguous(),
+                        tok.topk_weights[perm].contiguous())
+    np.testing.assert_array_equal(run_oracle(wl, W, tokp), base[perm.numpy()])
+    # (iii) one invalid id for another -> same bits; all invalid -> zeros
+    ids_a = tok.topk_ids.clone()
+    ids_a[2, 1] = -3
+    ids_b = tok.topk_ids.clone()
+    ids_b[2, 1] = 1000
+    oa = run_oracle(wl, W, synth.Tokens(tok.x, ids_a, tok.topk_weights))
+    ob = run_oracle(wl, W, synth.Tokens(tok.x, ids_b, tok.topk_weights))
+    np.testing.assert_array_equal(oa, ob)
+    assert not np.array_equal(oa, base)
+    allbad = torch.full_like(tok.topk_ids, E)
+    np.testing.assert_array_equal(run_oracle(wl, W, synth.Tokens(tok.x, allbad,
+                                                                 tok.topk_weights)), 0.0)
+    # (iv) relabel experts consistently -> same bits
+    pe = torch.tensor([3, 0, 4, 1, 2])                     # new id of old expert e
+    inv = torch.argsort(pe)
+    Wr = synth.Weights(W.w13_packed[inv].contiguous(), W.w13_scales[inv].contiguous(),
+                       W.w2_packed[inv].contiguous(), W.w2_scales[inv].contiguous())
+    ids_r = pe[tok.topk_ids.long()].to(torch.int32)
+    np.testing.assert_array_equal(run_oracle(wl, Wr, synth.Tokens(tok.x, ids_r,
+                                                                  tok.topk_weights)), base)
+
+
+def test_empty_batch():
+    wl = synth.custom(E=2, H=64, I=32, K=2)
+    W = synth.make_weights(wl)
+    tok = synth.make_tokens(wl, 0)
+    assert run_oracle(wl, W, tok).shape == (0, 64)
+
+
+# ---------------------------------------------------------------------------
+# route tables against brute force
+# ---------------------------------------------------------------------------
+
+def brute_routes(ids, E, off, bm):
+    T, K = ids.shape
+    flat = ids.reshape(-1)
+    per = [[r for r in range(T * K) if flat[r] - off == e] for e in range(E)]
+    counts = [len(p) for p in per]
+    offsets = [0]
+    for c in counts:
+        offsets.append(offsets[-1] + -(-c // bm) * bm)
+    srt = [-1] * offsets[-1]
+    slot = [-1] * (T * K)
+    for e, p in enumerate(per):
+        for j, r in enumerate(p):
+            srt[offsets[e] + j] = r
+            slot[r] = offsets[e] + j
+    return counts, offsets, srt, slot
+
+
+@pytest.mark.parametrize("T,K,E,E_global,off,bm", [
+    (16, 2, 8, 8, 0, 16), (7, 3, 5, 9, 2, 4), (1, 8, 384, 384, 0, 16), (33, 6, 128, 128, 0, 64),
+    (0, 4, 8, 8, 0, 16), (50, 8, 32, 256, 0, 32), (40, 8, 32, 256, 96, 1)])
+def test_prepare_routes_brute_force(T, K, E, E_global, off, bm):
+    rng = np.random.default_rng(T * 1000 + K)
+    ids = rng.integers(-2, E_global + 2, size=(T, K)).astype(np.int32)
+    counts, offsets, srt, slot = oracle.prepare_routes(ids, E, off, bm)
+    bc, bo, bs, bsl = brute_routes(ids, E, off, bm)
+    assert counts.tolist() == bc and offsets.tolist() == bo
+    assert srt.tolist() == bs and slot.tolist() == bsl
+    # invariants: padded offsets are multiples of bm; slot inverts sorted
+    assert all(o % bm == 0 for o in offsets)
+    for r, p in enumerate(slot):
+        if p >= 0:
+            assert srt[p] == r
