@@ -1,0 +1,184 @@
+/*
+ * w4a16_moe.h -- C ABI of the MI355X (gfx950) local W4A16 mixture-of-experts
+ * forward pass.
+ *
+ * Sources (web pages, cited by tag and section):
+ *   [P1] lmdeploy PR #4947, "feat(pytorch): add CuTeDSL W4A16 MoE backend"
+ *   [P2] flashinfer PR #5186, "perf: reduce split W4A16 routing and output
+ *        overhead"
+ *   [P3] TensorRT-LLM PR #18313, "Add W4A16 per-channel weight-only support
+ *        for Cutlass fused MoE"
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  Tensors are
+ *     row-major and contiguous.  Activations, packed weights, outputs and the
+ *     workspace must be 16-byte aligned, scales 4-byte aligned.
+ *   - 16-bit floating-point tensors (x, scales, out) all share desc->dtype.
+ *   - Nothing is allocated per call and nothing synchronizes: work is enqueued
+ *     on `stream` (0 = the null stream) and the call returns.  No device value
+ *     is read back, so a call can be captured in a HIP graph.
+ *   - Argument checking happens on the host before anything is enqueued.  A
+ *     rejected call enqueues nothing and returns a status; the thread-local
+ *     w4a16_last_error_message() then names the offending tensor or field.
+ *     Launch failures return W4A16_ERR_HIP.  Faults inside kernels surface at
+ *     the caller's next synchronization, like any HIP error.
+ *   - A route whose expert id is outside [expert_offset, expert_offset + E) is
+ *     an invalid route, not an error: it contributes nothing ([P1]
+ *     Modification, "invalid routes and masked expert counts").
+ *   - Calls on distinct workspaces are independent; two calls that share a
+ *     workspace must be ordered on one stream.
+ */
+#ifndef W4A16_MOE_H
+#define W4A16_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* w4a16_stream_t; /* a hipStream_t */
+
+typedef enum {
+  W4A16_OK = 0,
+  W4A16_ERR_INVALID_ARG = 1,          /* malformed descriptor or pointer    */
+  W4A16_ERR_UNSUPPORTED = 2,          /* well-formed but not implemented    */
+  W4A16_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes below the required */
+  W4A16_ERR_HIP = 4                   /* a HIP launch call failed           */
+} w4a16_status_t;
+
+typedef enum { W4A16_DT_BF16 = 0, W4A16_DT_FP16 = 1 } w4a16_dtype_t;
+
+/* Expert activation: gated SiLU(gate) * up over a fused gate/up weight whose
+ * rows [0, I) are gate and [I, 2I) are up ([P1] Benchmark, timed steps), or
+ * the non-gated ReLU^2 = max(h, 0)^2 over a single up weight ([P3]
+ * Validation). */
+typedef enum { W4A16_ACT_SILU_GATED = 0, W4A16_ACT_RELU2 = 1 } w4a16_act_t;
+
+/* Weight quantization layout ([P3] Checkpoint format for the packing rule:
+ * two INT4 per byte, even logical index in the low nibble, symmetric
+ * two's-complement values, scale = absmax / 7).
+ *   GROUP_K      one 16-bit scale per group_size (= 32) consecutive values of
+ *                the reduction dim, packed along the reduction dim
+ *                ([P1] BC-breaking, "INT4 group-size 32").
+ *   PER_CHANNEL  one 16-bit scale per output channel, packed along the output
+ *                dim ([P3] Description and Checkpoint format). */
+typedef enum { W4A16_Q_GROUP_K = 0, W4A16_Q_PER_CHANNEL = 1 } w4a16_qlayout_t;
+
+/* Problem descriptor (host memory, read during the call only).
+ *   Logical weight shapes, with N1 = 2*I for SILU_GATED and N1 = I for RELU2:
+ *     w13 [E][N1][H]   (gate/up, or w1)       w2 [E][H][I]   (down)
+ *   Packed storage:
+ *     GROUP_K:      w13_packed u8 [E][N1][H/2],   w13_scales [E][N1][H/32]
+ *                   w2_packed  u8 [E][H][I/2],    w2_scales  [E][H][I/32]
+ *     PER_CHANNEL:  w13_packed u8 [E][N1/2][H],   w13_scales [E][N1]
+ *                   w2_packed  u8 [E][H/2][I],    w2_scales  [E][H]
+ *   Supported: H and I multiples of 64, 1 <= E <= 1024, 1 <= top_k <= 32,
+ *   group_size 32 for GROUP_K.
+ *   force_* fields select a variant for testing; 0 means "choose from the
+ *   route count".  Every variant computes the same function. */
+typedef struct {
+  int32_t num_tokens;         /* T >= 0; T = 0 enqueues nothing                   */
+  int32_t hidden;             /* H                                                */
+  int32_t intermediate;       /* I                                                */
+  int32_t num_local_experts;  /* E                                                */
+  int32_t expert_offset;      /* global id of local expert 0                      */
+  int32_t top_k;              /* K                                                */
+  int32_t group_size;         /* 32 for GROUP_K, ignored for PER_CHANNEL          */
+  int32_t dtype;              /* w4a16_dtype_t                                    */
+  int32_t act;                /* w4a16_act_t                                      */
+  int32_t qlayout;            /* w4a16_qlayout_t                                  */
+  int32_t force_block_m;      /* 0 or 16/32/64: rows per expert tile             */
+  int32_t force_split_k;      /* 0 or >= 1: partitions of the gate/up reduction   */
+  int32_t force_down;         /* 0, 1 = grouped down GEMM + combine kernel,
+                                 2 = per-token down GEMM with the combine fused   */
+} w4a16_moe_desc_t;
+
+/* Variant the library runs for a descriptor (for tests and reports). */
+typedef struct {
+  int32_t block_m;            /* rows per expert tile (route padding unit)       */
+  int32_t split_k;            /* partitions of the gate/up reduction             */
+  int32_t k_chunk;            /* reduction length per partition                  */
+  int32_t down_mode;          /* 1 grouped + combine, 2 fused per token          */
+  int64_t max_positions;      /* capacity of the padded route list               */
+  int64_t max_tiles;          /* capacity of the expert tile list                */
+  size_t workspace_bytes;     /* bytes w4a16_moe_forward needs                   */
+} w4a16_moe_plan_t;
+
+/* Bytes of device workspace w4a16_moe_forward needs for this descriptor
+ * (depends on num_tokens).  Errors as for the forward's checks. */
+w4a16_status_t w4a16_moe_workspace_size(const w4a16_moe_desc_t* desc, size_t* bytes);
+
+/* The variant the forward will run for this descriptor. */
+w4a16_status_t w4a16_moe_get_plan(const w4a16_moe_desc_t* desc, w4a16_moe_plan_t* plan);
+
+/* The local W4A16 fused-MoE forward ([P1] Benchmark: route preparation,
+ * gate/up GEMM, SiLU, down GEMM and weighted reduction; [P2] Description,
+ * "Contract": FP32 combine in fixed top-k order before one 16-bit cast).
+ *   x             [T][H]  16-bit activations
+ *   w13_*, w2_*   packed INT4 weights and 16-bit scales, layouts above
+ *   topk_ids      [T][K]  int32 global expert ids (out-of-range -> invalid)
+ *   topk_weights  [T][K]  fp32 routing weights, applied as given
+ *   out           [T][H]  16-bit; out[t] = cast16(sum over k ascending of
+ *                 topk_weights[t][k] * expert_output(t, k)) over valid routes,
+ *                 +0 where a token has no valid route
+ *   workspace     device scratch of at least w4a16_moe_workspace_size bytes;
+ *                 its contents on entry do not matter and are clobbered.
+ * The result does not depend on scheduling: every sum has a fixed order, so
+ * repeated calls with the same inputs and variant give identical bits. */
+w4a16_status_t w4a16_moe_forward(const void* x, const uint8_t* w13_packed,
+                                 const void* w13_scales, const uint8_t* w2_packed,
+                                 const void* w2_scales, const int32_t* topk_ids,
+                                 const float* topk_weights, void* out,
+                                 const w4a16_moe_desc_t* desc, void* workspace,
+                                 size_t workspace_bytes, w4a16_stream_t stream);
+
+/* w4a16_moe_forward, plus stage timing: stage_events[2*i] and
+ * stage_events[2*i+1] (hipEvent_t created by the caller; null entries are
+ * skipped) are recorded on `stream` right before and after stage i:
+ *   i = 0 route preparation, 1 gate/up GEMM, 2 down GEMM (fused with the
+ *   combine in the per-token variant), 3 combine (grouped variant only).
+ * n_events is the length of stage_events (0..8).  Same results as the
+ * forward; meant for benchmarks. */
+w4a16_status_t w4a16_moe_forward_timed(const void* x, const uint8_t* w13_packed,
+                                       const void* w13_scales, const uint8_t* w2_packed,
+                                       const void* w2_scales, const int32_t* topk_ids,
+                                       const float* topk_weights, void* out,
+                                       const w4a16_moe_desc_t* desc, void* workspace,
+                                       size_t workspace_bytes, w4a16_stream_t stream,
+                                       void* const* stage_events, int32_t n_events);
+
+/* Route preparation alone, with the same device code the forward runs ([P1]
+ * Benchmark, "route preparation"; [P2] Description, route guards and padded
+ * fallback).  Uses desc->num_tokens, top_k, num_local_experts, expert_offset.
+ *   counts        [E]     valid routes per local expert
+ *   offsets       [E+1]   exclusive prefix sum of counts rounded up to
+ *                         block_m (1..256); offsets[E] = padded total
+ *   sorted_routes [sorted_capacity]  flat route index t*K+k of each padded
+ *                         position, ascending within an expert; padding -1.
+ *                         Positions at or past offsets[E] are not written.
+ *   route_slot    [T*K]   position of each route in sorted_routes, or -1
+ *   sorted_capacity must be >= T*K + min(E, T*K) * (block_m - 1). */
+w4a16_status_t w4a16_moe_prepare_routes(const w4a16_moe_desc_t* desc, const int32_t* topk_ids,
+                                        int32_t block_m, int32_t* counts, int32_t* offsets,
+                                        int32_t* sorted_routes, int64_t sorted_capacity,
+                                        int32_t* route_slot, w4a16_stream_t stream);
+
+/* Nibble unpacking with the device conversion the GEMMs use ([P3] Checkpoint
+ * format): out[2i] = low nibble of packed[i], out[2i+1] = high nibble, both as
+ * two's-complement int8 in [-8, 7].  out holds 2*n_bytes int8. */
+w4a16_status_t w4a16_unpack_int4(const uint8_t* packed, int64_t n_bytes, int8_t* out,
+                                 w4a16_stream_t stream);
+
+/* Static text for a status code. */
+const char* w4a16_status_string(w4a16_status_t status);
+
+/* Thread-local text of the last rejected call on this thread ("" if none). */
+const char* w4a16_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_MOE_H */

@@ -1,0 +1,138 @@
+"""Host-side tests of the C ABI: the library loads, exports every declared
+entry point, and rejects malformed calls before anything reaches a GPU
+(strict errors that name the offending tensor or field)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from w4a16_mixture_experts_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "w4a16_moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    names = declared_functions()
+    assert {"w4a16_moe_forward", "w4a16_moe_workspace_size", "w4a16_moe_prepare_routes",
+            "w4a16_unpack_int4", "w4a16_status_string", "w4a16_last_error_message",
+            "w4a16_moe_get_plan"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    L = B.lib()
+    assert L.w4a16_status_string(0) == b"ok"
+    assert L.w4a16_status_string(3) == b"workspace too small"
+    assert L.w4a16_status_string(99) == b"unknown status"
+
+
+def good(**kw):
+    d = dict(num_tokens=4, hidden=256, intermediate=384, num_local_experts=8, top_k=2)
+    d.update(kw)
+    return B.make_desc(**d)
+
+
+@pytest.mark.parametrize("field,value,status,needle", [
+    ("num_tokens", -1, 1, "num_tokens"),
+    ("hidden", 0, 1, "hidden"),
+    ("intermediate", -64, 1, "intermediate"),
+    ("num_local_experts", 0, 1, "num_local_experts"),
+    ("top_k", 0, 1, "top_k"),
+    ("dtype", 7, 1, "dtype"),
+    ("act", 3, 1, "act"),
+    ("qlayout", 2, 1, "qlayout"),
+    ("num_local_experts", 2000, 2, "num_local_experts"),
+    ("top_k", 33, 2, "top_k"),
+    ("group_size", 64, 2, "group_size"),
+    ("hidden", 96, 2, "hidden=96"),
+    ("intermediate", 1828, 2, "intermediate=1828"),
+    ("force_block_m", 48, 1, "force_block_m"),
+    ("force_split_k", -2, 1, "force_split_k"),
+    ("force_down", 5, 1, "force_down"),
+])
+def test_descriptor_errors(field, value, status, needle):
+    d = good()
+    setattr(d, field, value)
+    n = ctypes.c_size_t(0)
+    st = B.lib().w4a16_moe_workspace_size(ctypes.byref(d), ctypes.byref(n))
+    assert st == status
+    assert needle in B.lib().w4a16_last_error_message().decode()
+    with pytest.raises(B.W4A16Error) as ei:
+        B.workspace_size(d)
+    assert ei.value.status == status
+
+
+def test_null_descriptor():
+    n = ctypes.c_size_t(0)
+    assert B.lib().w4a16_moe_workspace_size(None, ctypes.byref(n)) == 1
+    assert b"desc" in B.lib().w4a16_last_error_message()
+
+
+def test_forward_rejects_before_launch():
+    L = B.lib()
+    d = good()
+    need = B.workspace_size(d)
+    P = ctypes.c_void_p
+    fake = [P(0x10000 * (i + 1)) for i in range(8)]
+    ws = P(0x900000)
+    # null pointer named
+    args = list(fake)
+    args[2] = None
+    assert L.w4a16_moe_forward(*args, ctypes.byref(d), ws, need, None) == 1
+    assert b"w13_scales" in L.w4a16_last_error_message()
+    # misaligned packed weights named
+    args = list(fake)
+    args[1] = P(0x10008)
+    assert L.w4a16_moe_forward(*args, ctypes.byref(d), ws, need, None) == 1
+    assert b"w13_packed" in L.w4a16_last_error_message()
+    # workspace too small
+    assert L.w4a16_moe_forward(*fake, ctypes.byref(d), ws, need - 1, None) == 3
+    assert b"workspace" in L.w4a16_last_error_message()
+    # zero tokens: nothing enqueued, OK even with null pointers
+    d0 = good(num_tokens=0)
+    assert L.w4a16_moe_forward(*([None] * 8), ctypes.byref(d0), None, 0, None) == 0
+
+
+def test_prepare_routes_and_unpack_argument_errors():
+    L = B.lib()
+    d = good()
+    P = ctypes.c_void_p
+    args = [P(0x1000)] * 4
+    assert L.w4a16_moe_prepare_routes(ctypes.byref(d), P(0x1000), 0, *args[:3], 100, args[3],
+                                      None) == 1
+    assert b"block_m" in L.w4a16_last_error_message()
+    assert L.w4a16_moe_prepare_routes(ctypes.byref(d), P(0x1000), 16, *args[:3], 10, args[3],
+                                      None) == 1
+    assert b"capacity" in L.w4a16_last_error_message()
+    assert L.w4a16_unpack_int4(None, 16, P(0x1000), None) == 1
+    assert L.w4a16_unpack_int4(P(0x1000), -1, P(0x1000), None) == 1
+    assert L.w4a16_unpack_int4(None, 0, None, None) == 0
+
+
+def test_plans_by_route_count():
+    # decode: small tiles, split-K, per-token down kernel
+    p1 = B.get_plan(B.make_desc(num_tokens=1, hidden=7168, intermediate=256,
+                                num_local_experts=384, top_k=8))
+    assert p1.block_m == 16 and p1.split_k > 1 and p1.down_mode == 2
+    assert p1.k_chunk % 128 == 0 and p1.split_k * p1.k_chunk >= 7168
+    # prefill: big tiles, no split, grouped down + combine
+    p2 = B.get_plan(B.make_desc(num_tokens=2048, hidden=7168, intermediate=256,
+                                num_local_experts=384, top_k=8))
+    assert p2.block_m == 64 and p2.split_k == 1 and p2.down_mode == 1
+    assert p2.max_positions == 2048 * 8 + 384 * 63
+    # forcing is honoured and the workspace follows the plan
+    d = B.make_desc(num_tokens=16, hidden=256, intermediate=384, num_local_experts=8, top_k=2,
+                    force_block_m=32, force_split_k=2, force_down=1)
+    p3 = B.get_plan(d)
+    assert (p3.block_m, p3.split_k, p3.down_mode) == (32, 2, 1)
+    assert p3.workspace_bytes == B.workspace_size(d)

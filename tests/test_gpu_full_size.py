@@ -1,0 +1,28 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (automatic plan).  The oracle recomputes a sample of token
+rows; each token's output depends only on its own routes, so those rows are
+exact references for the rows the GPU produced inside the full batch."""
+import numpy as np
+import pytest
+import torch
+
+from moe_check import assert_close, forward, oracle_out, tokens, weights
+from w4a16_mixture_experts_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+FULL = [("kimi_tp8", 2048), ("kimi_tp8", 256), ("deepseek_local", 2048), ("per_channel", 256),
+        ("relu2_skew", 4096)]
+
+
+@pytest.mark.parametrize("name,T", FULL)
+def test_full_size_sampled_rows(name, T):
+    wl = synth.WORKLOADS[name]
+    Wc, Wg = weights(name)
+    tc = tokens(wl, T)
+    out = forward(wl, Wg, tc.to("cuda"))
+    rng = np.random.default_rng(T)
+    rows = sorted(set([0, T - 1] + rng.choice(T, size=6, replace=False).tolist()))
+    ref = oracle_out(wl, Wc, tc, rows=rows)
+    assert_close(out[torch.as_tensor(rows, device="cuda")], ref, f"{name} T={T} rows={rows}")
+    assert torch.isfinite(out.float()).all()

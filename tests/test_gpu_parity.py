@@ -1,0 +1,252 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Integer work (nibble unpacking, route tables) must match bit for bit; the
+16-bit MoE outputs must be within NRMSE <= 5e-3 and max-abs <= 2e-2 of the
+FP32 oracle.  Sizes are chosen so the oracle finishes in seconds while still
+spanning several tiles, split-K partitions and ragged tails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_check import assert_close, bits, errors, forward, oracle_out, tokens, weights
+from w4a16_mixture_experts_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------------------
+# integer work: bit-exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 256, 257, 4099])
+def test_unpack_bit_exact(n):
+    rng = np.random.default_rng(n)
+    b = np.concatenate([np.arange(256, dtype=np.uint8), rng.integers(0, 256, n, dtype=np.uint8)])
+    b = b[:n] if n < 256 else b
+    got = binding.unpack_int4(torch.from_numpy(b).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got.cpu().numpy(), oracle.unpack_int4(b))
+
+
+ROUTE_CASES = [
+    # T, K, E, E_global, offset, block_m
+    (1, 8, 384, 384, 0, 16), (8, 8, 384, 384, 0, 16), (16, 2, 8, 8, 0, 16),
+    (2048, 8, 384, 384, 0, 64), (4096, 6, 128, 128, 0, 64), (2048, 8, 32, 256, 0, 64),
+    (7, 3, 5, 9, 2, 4), (33, 4, 60, 60, 0, 32), (100, 8, 1024, 1024, 0, 1),
+    (5, 2, 8, 8, 0, 256), (0, 4, 8, 8, 0, 16),
+]
+
+
+@pytest.mark.parametrize("T,K,E,Eg,off,bm", ROUTE_CASES)
+def test_route_prep_bit_exact(T, K, E, Eg, off, bm):
+    rng = np.random.default_rng(T + 7 * K + E)
+    ids = rng.integers(-3, Eg + 3, size=(T, K)).astype(np.int32)
+    if T > 4:
+        ids[T // 2] = Eg + 1            # a token without a valid route
+    counts, offsets, srt, slot = oracle.prepare_routes(ids, E, off, bm)
+    gc, go, gs, gsl = binding.prepare_routes(torch.from_numpy(ids).cuda(), E, off, bm)
+    torch.cuda.synchronize()
+    total = int(offsets[-1])
+    np.testing.assert_array_equal(gc.cpu().numpy(), counts)
+    np.testing.assert_array_equal(go.cpu().numpy(), offsets)
+    np.testing.assert_array_equal(gs.cpu().numpy()[:total], srt)
+    np.testing.assert_array_equal(gsl.cpu().numpy(), slot)
+
+
+def test_route_prep_skewed_and_local_share():
+    for name, T in (("relu2_skew", 1024), ("deepseek_local", 512)):
+        wl = synth.WORKLOADS[name]
+        tok = synth.make_tokens(wl, T)
+        ids = tok.topk_ids.numpy()
+        counts, offsets, srt, slot = oracle.prepare_routes(ids, wl.num_experts, 0, 64)
+        gc, go, gs, gsl = binding.prepare_routes(tok.topk_ids.cuda(), wl.num_experts, 0, 64)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(gc.cpu().numpy(), counts)
+        np.testing.assert_array_equal(go.cpu().numpy(), offsets)
+        np.testing.assert_array_equal(gs.cpu().numpy()[:int(offsets[-1])], srt)
+        np.testing.assert_array_equal(gsl.cpu().numpy(), slot)
+
+
+# ---------------------------------------------------------------------------
+# forward parity, every variant on the small gated workload
+# ---------------------------------------------------------------------------
+
+VARIANTS = [dict(force_block_m=bm, force_split_k=s, force_down=d)
+            for bm in (16, 32, 64) for s in (1, 2, 3) for d in (1, 2)]
+
+
+@pytest.mark.parametrize("force", VARIANTS, ids=lambda f: "bm{force_block_m}-s{force_split_k}-d{force_down}".format(**f))
+def test_tiny_all_variants(force):
+    wl = synth.WORKLOADS["tiny"]
+    Wc, Wg = weights("tiny")
+    tc = tokens(wl, 16)
+    out = forward(wl, Wg, tc.to("cuda"), **force)
+    assert_close(out, oracle_out(wl, Wc, tc), f"tiny {force}")
+
+
+@pytest.mark.parametrize("name,T", [
+    ("kimi_tp8", 1), ("kimi_tp8", 8), ("kimi_tp8", 32), ("deepseek_local", 1),
+    ("deepseek_local", 16), ("per_channel", 1), ("per_channel", 8), ("relu2_skew", 32)])
+def test_configs_small_token_counts(name, T):
+    wl = synth.WORKLOADS[name]
+    Wc, Wg = weights(name)
+    tc = tokens(wl, T)
+    out = forward(wl, Wg, tc.to("cuda"))
+    assert_close(out, oracle_out(wl, Wc, tc), f"{name} T={T}")
+
+
+@pytest.mark.parametrize("name,T,force", [
+    ("kimi_tp8", 8, dict(force_down=1)), ("kimi_tp8", 32, dict(force_down=2)),
+    ("kimi_tp8", 8, dict(force_split_k=1)), ("kimi_tp8", 32, dict(force_block_m=64)),
+    ("per_channel", 8, dict(force_down=1, force_split_k=3)),
+    ("relu2_skew", 32, dict(force_down=2, force_block_m=16, force_split_k=5)),
+    ("deepseek_local", 16, dict(force_down=1, force_block_m=32))])
+def test_config_variants(name, T, force):
+    wl = synth.WORKLOADS[name]
+    Wc, Wg = weights(name)
+    tc = tokens(wl, T)
+    out = forward(wl, Wg, tc.to("cuda"), **force)
+    assert_close(out, oracle_out(wl, Wc, tc), f"{name} T={T} {force}")
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+
+def _small(name="tiny"):
+    wl = synth.WORKLOADS[name]
+    Wc, Wg = weights(name)
+    return wl, Wc, Wg
+
+
+def test_zero_tokens():
+    wl, Wc, Wg = _small()
+    tok = tokens(wl, 0, "cuda")
+    out = forward(wl, Wg, tok)
+    assert out.shape == (0, wl.hidden)
+
+
+@pytest.mark.parametrize("down", [1, 2])
+def test_invalid_routes_and_empty_tokens(down):
+    wl, Wc, Wg = _small()
+    tc = tokens(wl, 16)
+    ids = tc.topk_ids.clone()
+    ids[0, :] = -1                    # no valid route
+    ids[3, 1] = wl.num_experts        # one past the end
+    ids[5, 0] = 2 ** 31 - 1
+    ids[7, :] = -(2 ** 31)
+    tc = synth.Tokens(tc.x, ids, tc.topk_weights)
+    out = forward(wl, Wg, tc.to("cuda"), force_down=down)
+    ref = oracle_out(wl, Wc, tc)
+    assert_close(out, ref, "invalid routes")
+    o = out.cpu()
+    assert (o[0] == 0).all() and (o[7] == 0).all()
+    assert not torch.signbit(o[0].float()).any()
+
+
+@pytest.mark.parametrize("down", [1, 2])
+def test_all_routes_invalid_gives_zeros(down):
+    wl, Wc, Wg = _small()
+    tc = tokens(wl, 16)
+    ids = torch.full_like(tc.topk_ids, 100)
+    out = forward(wl, Wg, synth.Tokens(tc.x, ids, tc.topk_weights).to("cuda"), force_down=down)
+    assert (out.cpu() == 0).all()
+
+
+def test_single_expert_receives_everything():
+    wl, Wc, Wg = _small()
+    tc = tokens(wl, 40)
+    ids = torch.full_like(tc.topk_ids, 3)       # duplicate ids: each route counts
+    tc = synth.Tokens(tc.x, ids, tc.topk_weights)
+    for bm in (16, 32, 64):
+        out = forward(wl, Wg, tc.to("cuda"), force_block_m=bm)
+        assert_close(out, oracle_out(wl, Wc, tc), f"one expert bm={bm}")
+
+
+def test_poisoned_workspace_and_output():
+    """Workspace and output filled with NaN patterns before the call: nothing
+    uninitialised may leak (empty split-K partitions, padding rows)."""
+    wl, Wc, Wg = _small()
+    tc = tokens(wl, 16)
+    tg = tc.to("cuda")
+    ref = oracle_out(wl, Wc, tc)
+    for force in (dict(force_split_k=3, force_down=2), dict(force_split_k=2, force_down=1,
+                                                              force_block_m=64)):
+        d = binding.desc_for(wl, 16, **force)
+        ws = torch.full((binding.workspace_size(d),), 0xFF, dtype=torch.uint8, device="cuda")
+        out = torch.full((16, wl.hidden), float("nan"), dtype=wl.dtype, device="cuda")
+        binding.forward_workload(wl, Wg, tg, out=out, workspace=ws, **force)
+        torch.cuda.synchronize()
+        assert_close(out, ref, f"poisoned {force}")
+
+
+def test_split_partitions_cover_the_reduction_exactly():
+    """Partitions are whole 128-blocks and never empty: the planner clamps the
+    requested count, and every partition writes its full partial."""
+    wl, Wc, Wg = _small()                          # H = 256 -> 2 blocks of 128
+    tc = tokens(wl, 16)
+    out = forward(wl, Wg, tc.to("cuda"), force_split_k=2, force_block_m=16)
+    assert_close(out, oracle_out(wl, Wc, tc), "split 2 of 2 blocks")
+    pl = binding.get_plan(binding.desc_for(wl, 16, force_split_k=64))
+    assert pl.split_k == 2 and pl.k_chunk == 128
+
+
+# ---------------------------------------------------------------------------
+# determinism, invariances, graph replay
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,T", [("tiny", 16), ("kimi_tp8", 8), ("kimi_tp8", 32)])
+def test_bitwise_repeatable(name, T):
+    wl = synth.WORKLOADS[name]
+    _, Wg = weights(name)
+    tg = tokens(wl, T, "cuda")
+    a = forward(wl, Wg, tg)
+    for _ in range(3):
+        b = forward(wl, Wg, tg)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("down", [1, 2])
+def test_gpu_invariances_bitwise(down):
+    wl, Wc, Wg = _small()
+    tc = tokens(wl, 16)
+    base = forward(wl, Wg, tc.to("cuda"), force_down=down).cpu()
+    # routing weights x2 -> output x2 exactly
+    t2 = synth.Tokens(tc.x, tc.topk_ids, tc.topk_weights * 2)
+    o2 = forward(wl, Wg, t2.to("cuda"), force_down=down).cpu()
+    assert torch.equal(o2.float(), base.float() * 2)
+    # token permutation -> output permutation exactly
+    perm = torch.randperm(16, generator=torch.Generator().manual_seed(1))
+    tp = synth.Tokens(tc.x[perm].contiguous(), tc.topk_ids[perm].contiguous(),
+                      tc.topk_weights[perm].contiguous())
+    op = forward(wl, Wg, tp.to("cuda"), force_down=down).cpu()
+    assert torch.equal(op.view(torch.int16), base[perm].view(torch.int16))
+
+
+def test_hip_graph_replay():
+    wl = synth.WORKLOADS["kimi_tp8"]
+    Wc, Wg = weights("kimi_tp8")
+    for T in (1, 32):
+        tg = tokens(wl, T, "cuda")
+        d = binding.desc_for(wl, T)
+        ws = torch.empty(binding.workspace_size(d), dtype=torch.uint8, device="cuda")
+        out = torch.empty(T, wl.hidden, dtype=wl.dtype, device="cuda")
+        eager = forward(wl, Wg, tg).clone()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            binding.forward_workload(wl, Wg, tg, out=out, workspace=ws)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            binding.forward_workload(wl, Wg, tg, out=out, workspace=ws)
+        for _ in range(3):
+            out.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
+            forward(wl, Wg, tg)                      # eager work between replays

@@ -1,0 +1,233 @@
+"""Thin Python binding of the C ABI in include/w4a16_moe.h (ctypes).
+
+Argument marshalling only: tensors are checked for device, dtype and
+contiguity, then their data pointers and the current HIP stream are passed to
+libw4a16moe.so.  Every step of the forward pass runs in the library's HIP
+kernels; there is no fallback: if the library is missing, loading fails.
+PyTorch provides device memory (outputs, workspace) and the stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4a16moe.so")
+
+DT_BF16, DT_FP16 = 0, 1
+ACT_SILU_GATED, ACT_RELU2 = 0, 1
+Q_GROUP_K, Q_PER_CHANNEL = 0, 1
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP"}
+
+
+class MoeDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_tokens", "hidden", "intermediate", "num_local_experts", "expert_offset", "top_k",
+        "group_size", "dtype", "act", "qlayout", "force_block_m", "force_split_k", "force_down")]
+
+
+class MoePlan(ctypes.Structure):
+    _fields_ = [("block_m", ctypes.c_int32), ("split_k", ctypes.c_int32),
+                ("k_chunk", ctypes.c_int32), ("down_mode", ctypes.c_int32),
+                ("max_positions", ctypes.c_int64), ("max_tiles", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+_lib = None
+
+
+def lib():
+    """Load libw4a16moe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m w4a16_mixture_experts_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    pdesc = ctypes.POINTER(MoeDesc)
+    L.w4a16_moe_workspace_size.argtypes = [pdesc, ctypes.POINTER(sz)]
+    L.w4a16_moe_get_plan.argtypes = [pdesc, ctypes.POINTER(MoePlan)]
+    L.w4a16_moe_forward.argtypes = [P, P, P, P, P, P, P, P, pdesc, P, sz, P]
+    L.w4a16_moe_forward_timed.argtypes = [P, P, P, P, P, P, P, P, pdesc, P, sz, P, P, i32]
+    L.w4a16_moe_prepare_routes.argtypes = [pdesc, P, i32, P, P, P, i64, P, P]
+    L.w4a16_unpack_int4.argtypes = [P, i64, P, P]
+    L.w4a16_status_string.argtypes = [i32]
+    L.w4a16_status_string.restype = ctypes.c_char_p
+    L.w4a16_last_error_message.restype = ctypes.c_char_p
+    for f in ("w4a16_moe_workspace_size", "w4a16_moe_get_plan", "w4a16_moe_forward",
+              "w4a16_moe_forward_timed",
+              "w4a16_moe_prepare_routes", "w4a16_unpack_int4"):
+        getattr(L, f).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise W4A16Error(status, lib().w4a16_last_error_message().decode())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(name: str, t: torch.Tensor, dtypes, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def make_desc(*, num_tokens: int, hidden: int, intermediate: int, num_local_experts: int,
+              top_k: int, expert_offset: int = 0, dtype=torch.bfloat16, gated: bool = True,
+              per_channel: bool = False, group_size: int = 32, force_block_m: int = 0,
+              force_split_k: int = 0, force_down: int = 0) -> MoeDesc:
+    return MoeDesc(num_tokens, hidden, intermediate, num_local_experts, expert_offset, top_k,
+                   group_size, DT_FP16 if dtype == torch.float16 else DT_BF16,
+                   ACT_SILU_GATED if gated else ACT_RELU2,
+                   Q_PER_CHANNEL if per_channel else Q_GROUP_K, force_block_m, force_split_k,
+                   force_down)
+
+
+def workspace_size(desc: MoeDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().w4a16_moe_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return int(n.value)
+
+
+def get_plan(desc: MoeDesc) -> MoePlan:
+    pl = MoePlan()
+    _check(lib().w4a16_moe_get_plan(ctypes.byref(desc), ctypes.byref(pl)))
+    return pl
+
+
+def desc_for(wl, T: int, **force) -> MoeDesc:
+    """Descriptor of a synthetic workload (w4a16_mixture_experts_amd.synth)."""
+    return make_desc(num_tokens=T, hidden=wl.hidden, intermediate=wl.inter,
+                     num_local_experts=wl.num_experts, top_k=wl.top_k,
+                     expert_offset=wl.expert_offset, dtype=wl.dtype, gated=wl.gated,
+                     per_channel=wl.per_channel, **force)
+
+
+def moe_forward(x, w13_packed, w13_scales, w2_packed, w2_scales, topk_ids, topk_weights, *,
+                intermediate: int, num_local_experts: int, expert_offset: int = 0,
+                gated: bool = True, per_channel: bool = False, out=None, workspace=None,
+                force_block_m: int = 0, force_split_k: int = 0, force_down: int = 0,
+                stream=None, stage_events=None) -> torch.Tensor:
+    """Local W4A16 MoE forward: returns out [T, H] in x's dtype.
+
+    stage_events: optional list of up to 8 torch.cuda.Event(enable_timing=True);
+    events 2i and 2i+1 are recorded around stage i (0 route preparation,
+    1 gate/up GEMM, 2 down GEMM, 3 combine) on the stream the kernels use.
+    """
+    half = (torch.bfloat16, torch.float16)
+    _dev("x", x, half)
+    dev = x.device
+    T, H = x.shape
+    _dev("w13_packed", w13_packed, (torch.uint8,), dev)
+    _dev("w2_packed", w2_packed, (torch.uint8,), dev)
+    _dev("w13_scales", w13_scales, (x.dtype,), dev)
+    _dev("w2_scales", w2_scales, (x.dtype,), dev)
+    _dev("topk_ids", topk_ids, (torch.int32,), dev)
+    _dev("topk_weights", topk_weights, (torch.float32,), dev)
+    if topk_ids.dim() != 2 or topk_ids.shape[0] != T or topk_weights.shape != topk_ids.shape:
+        raise ValueError("topk_ids/topk_weights: expected [T, K] matching x")
+    E = num_local_experts
+    I = intermediate
+    N1 = 2 * I if gated else I
+    if per_channel:
+        want = {"w13_packed": (E, N1 // 2, H), "w13_scales": (E, N1),
+                "w2_packed": (E, H // 2, I), "w2_scales": (E, H)}
+    else:
+        want = {"w13_packed": (E, N1, H // 2), "w13_scales": (E, N1, H // 32),
+                "w2_packed": (E, H, I // 2), "w2_scales": (E, H, I // 32)}
+    for name, t in (("w13_packed", w13_packed), ("w13_scales", w13_scales),
+                    ("w2_packed", w2_packed), ("w2_scales", w2_scales)):
+        if tuple(t.shape) != want[name]:
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {want[name]}")
+    desc = make_desc(num_tokens=T, hidden=H, intermediate=I, num_local_experts=E,
+                     top_k=topk_ids.shape[1], expert_offset=expert_offset, dtype=x.dtype,
+                     gated=gated, per_channel=per_channel, force_block_m=force_block_m,
+                     force_split_k=force_split_k, force_down=force_down)
+    nbytes = workspace_size(desc)
+    if out is None:
+        out = torch.empty(T, H, dtype=x.dtype, device=dev)
+    else:
+        _dev("out", out, (x.dtype,), dev)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    else:
+        _dev("workspace", workspace, (torch.uint8,), dev)
+    args = (_ptr(x), _ptr(w13_packed), _ptr(w13_scales), _ptr(w2_packed), _ptr(w2_scales),
+            _ptr(topk_ids), _ptr(topk_weights), _ptr(out), ctypes.byref(desc), _ptr(workspace),
+            workspace.numel(), _stream(stream))
+    if stage_events is None:
+        _check(lib().w4a16_moe_forward(*args))
+    else:
+        st = stream if stream is not None else torch.cuda.current_stream()
+        for ev in stage_events:
+            if ev is not None and not ev.cuda_event:
+                ev.record(st)                 # torch creates its events lazily
+        handles = (ctypes.c_void_p * len(stage_events))(
+            *[ev.cuda_event if ev is not None else None for ev in stage_events])
+        _check(lib().w4a16_moe_forward_timed(*args, handles, len(stage_events)))
+    return out
+
+
+def forward_workload(wl, W, tok, **kw) -> torch.Tensor:
+    """moe_forward on synth.Weights / synth.Tokens already on the GPU."""
+    return moe_forward(tok.x, W.w13_packed, W.w13_scales, W.w2_packed, W.w2_scales,
+                       tok.topk_ids, tok.topk_weights, intermediate=wl.inter,
+                       num_local_experts=wl.num_experts, expert_offset=wl.expert_offset,
+                       gated=wl.gated, per_channel=wl.per_channel, **kw)
+
+
+def prepare_routes(topk_ids: torch.Tensor, num_local_experts: int, expert_offset: int,
+                   block_m: int, stream=None):
+    """Route tables from the device kernel: (counts, offsets, sorted, slot)."""
+    _dev("topk_ids", topk_ids, (torch.int32,))
+    T, K = topk_ids.shape
+    R = T * K
+    E = num_local_experts
+    dev = topk_ids.device
+    cap = R + min(E, R) * (block_m - 1)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    srt = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    slot = torch.empty(max(R, 1), dtype=torch.int32, device=dev)
+    desc = MoeDesc(T, 64, 64, E, expert_offset, K, 32, 0, 0, 0, 0, 0, 0)
+    _check(lib().w4a16_moe_prepare_routes(ctypes.byref(desc), _ptr(topk_ids), block_m,
+                                          _ptr(counts), _ptr(offsets), _ptr(srt), cap,
+                                          _ptr(slot), _stream(stream)))
+    return counts, offsets, srt, slot[:R]
+
+
+def unpack_int4(packed: torch.Tensor, stream=None) -> torch.Tensor:
+    _dev("packed", packed, (torch.uint8,))
+    out = torch.empty(packed.numel() * 2, dtype=torch.int8, device=packed.device)
+    _check(lib().w4a16_unpack_int4(_ptr(packed), packed.numel(), _ptr(out), _stream(stream)))
+    return out

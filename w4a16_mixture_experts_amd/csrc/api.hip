@@ -1,0 +1,469 @@
+// api.hip -- host side of the C ABI: argument checks, the variant plan,
+// workspace carving and kernel enqueueing.  Nothing here allocates device
+// memory, synchronizes or reads device values back.
+//
+// Sources: [P1] lmdeploy PR #4947, "feat(pytorch): add CuTeDSL W4A16 MoE
+// backend" (Modification: small-batch split-K, route-count-based tile
+// selection; BC-breaking: explicit selections are strict errors);
+// [P3] TensorRT-LLM PR #18313, "Add W4A16 per-channel weight-only support for
+// Cutlass fused MoE" (Description: diagnostics that name the offending tensor
+// instead of a bare assertion).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <cmath>
+#include <string>
+
+#include "../../include/w4a16_moe.h"
+#include "device.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+w4a16_status_t fail(w4a16_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Plan {
+  int bm = 16, ms = 1, split = 1, kchunk = 0, down_mode = 2;
+  int n_tiles_up = 0, n_tiles_down = 0, mode_up = 0;
+  int64_t R = 0, P = 0, MT = 0;
+  int N1 = 0;
+  size_t off_counts = 0, off_offsets = 0, off_slot = 0, off_sorted = 0, off_tile = 0,
+         off_counters = 0, off_act = 0, off_partial = 0, off_y = 0, total = 0;
+};
+
+w4a16_status_t check_desc(const w4a16_moe_desc_t* d) {
+  if (d == nullptr) return fail(W4A16_ERR_INVALID_ARG, "desc: null pointer");
+  if (d->num_tokens < 0) return fail(W4A16_ERR_INVALID_ARG, "desc.num_tokens: %d < 0", d->num_tokens);
+  if (d->hidden <= 0) return fail(W4A16_ERR_INVALID_ARG, "desc.hidden: %d <= 0", d->hidden);
+  if (d->intermediate <= 0)
+    return fail(W4A16_ERR_INVALID_ARG, "desc.intermediate: %d <= 0", d->intermediate);
+  if (d->num_local_experts <= 0)
+    return fail(W4A16_ERR_INVALID_ARG, "desc.num_local_experts: %d <= 0", d->num_local_experts);
+  if (d->top_k <= 0) return fail(W4A16_ERR_INVALID_ARG, "desc.top_k: %d <= 0", d->top_k);
+  if (d->dtype != W4A16_DT_BF16 && d->dtype != W4A16_DT_FP16)
+    return fail(W4A16_ERR_INVALID_ARG, "desc.dtype: unknown value %d", d->dtype);
+  if (d->act != W4A16_ACT_SILU_GATED && d->act != W4A16_ACT_RELU2)
+    return fail(W4A16_ERR_INVALID_ARG, "desc.act: unknown value %d", d->act);
+  if (d->qlayout != W4A16_Q_GROUP_K && d->qlayout != W4A16_Q_PER_CHANNEL)
+    return fail(W4A16_ERR_INVALID_ARG, "desc.qlayout: unknown value %d", d->qlayout);
+  if (d->num_local_experts > 1024)
+    return fail(W4A16_ERR_UNSUPPORTED, "desc.num_local_experts: %d > 1024", d->num_local_experts);
+  if (d->top_k > 32) return fail(W4A16_ERR_UNSUPPORTED, "desc.top_k: %d > 32", d->top_k);
+  if (d->qlayout == W4A16_Q_GROUP_K && d->group_size != 32)
+    return fail(W4A16_ERR_UNSUPPORTED, "desc.group_size: %d (only 32 is supported)", d->group_size);
+  if (d->hidden % 64 != 0)
+    return fail(W4A16_ERR_UNSUPPORTED,
+                "w13_packed/w2_packed: hidden=%d is not a multiple of 64", d->hidden);
+  if (d->intermediate % 64 != 0)
+    return fail(W4A16_ERR_UNSUPPORTED,
+                "w13_packed/w2_packed: intermediate=%d is not a multiple of 64", d->intermediate);
+  const int64_t R = static_cast<int64_t>(d->num_tokens) * d->top_k;
+  if (R > (int64_t(1) << 26))
+    return fail(W4A16_ERR_UNSUPPORTED, "topk_ids: %lld routes exceed 2^26", (long long)R);
+  if (d->force_block_m != 0 && d->force_block_m != 16 && d->force_block_m != 32 &&
+      d->force_block_m != 64)
+    return fail(W4A16_ERR_INVALID_ARG, "desc.force_block_m: %d (0, 16, 32 or 64)", d->force_block_m);
+  if (d->force_split_k < 0)
+    return fail(W4A16_ERR_INVALID_ARG, "desc.force_split_k: %d < 0", d->force_split_k);
+  if (d->force_down < 0 || d->force_down > 2)
+    return fail(W4A16_ERR_INVALID_ARG, "desc.force_down: %d (0, 1 or 2)", d->force_down);
+  return W4A16_OK;
+}
+
+// Variant selection from the route count R = T*K ([P1] Modification:
+// route-count-based tile selection and small-batch split-K).
+Plan make_plan(const w4a16_moe_desc_t* d) {
+  Plan pl;
+  const int E = d->num_local_experts, H = d->hidden, I = d->intermediate, K = d->top_k;
+  const bool gated = d->act == W4A16_ACT_SILU_GATED;
+  pl.R = static_cast<int64_t>(d->num_tokens) * K;
+  pl.N1 = gated ? 2 * I : I;
+  pl.mode_up = gated ? w4moe::MODE_UP_GATED : w4moe::MODE_UP_RELU2;
+
+  // expected routes per touched expert under uniform routing
+  const double R = static_cast<double>(pl.R);
+  const double D = std::max(1.0, E * (1.0 - std::pow(1.0 - 1.0 / E, R)));
+  const double per_expert = R / D;
+  if (d->force_block_m) pl.bm = d->force_block_m;
+  else pl.bm = per_expert <= 16 ? 16 : (per_expert <= 32 ? 32 : 64);
+  pl.ms = pl.bm / 16;
+
+  const int64_t touched = std::min<int64_t>(E, pl.R);
+  pl.P = pl.R + touched * (pl.bm - 1);
+  pl.MT = pl.P / pl.bm;
+  pl.n_tiles_up = gated ? (I + w4moe::kWgColsGated - 1) / w4moe::kWgColsGated
+                        : (I + w4moe::kWgColsPlain - 1) / w4moe::kWgColsPlain;
+  pl.n_tiles_down = (H + w4moe::kWgColsPlain - 1) / w4moe::kWgColsPlain;
+
+  // split-K: aim for >= 1024 workgroups in the gate/up GEMM
+  const double tiles_est = D * std::ceil(per_expert / pl.bm);
+  const int kblocks = H / 128 > 0 ? H / 128 : 1;
+  int split = d->force_split_k;
+  if (split == 0) {
+    const double wgs = tiles_est * pl.n_tiles_up;
+    split = static_cast<int>(std::ceil(1024.0 / std::max(1.0, wgs)));
+  }
+  split = std::max(1, std::min(split, (H + 127) / 128));
+  (void)kblocks;
+  pl.kchunk = ((H + split - 1) / split + 127) / 128 * 128;
+  pl.split = (H + pl.kchunk - 1) / pl.kchunk;
+
+  if (d->force_down) pl.down_mode = d->force_down;
+  else pl.down_mode = pl.R <= 64 ? 2 : 1;
+
+  // workspace carve (256-byte aligned pieces)
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  pl.off_counts = take(sizeof(int32_t) * E);
+  pl.off_offsets = take(sizeof(int32_t) * (E + 1));
+  pl.off_slot = take(sizeof(int32_t) * std::max<int64_t>(pl.R, 1));
+  pl.off_sorted = take(sizeof(int32_t) * std::max<int64_t>(pl.P, 1));
+  pl.off_tile = take(sizeof(int32_t) * std::max<int64_t>(pl.MT, 1));
+  pl.off_counters = take(pl.split > 1 ? sizeof(int32_t) * pl.MT * pl.n_tiles_up : 0);
+  pl.off_act = take(sizeof(uint16_t) * pl.P * I);
+  pl.off_partial = take(pl.split > 1 ? sizeof(float) * pl.split * pl.P * pl.N1 : 0);
+  pl.off_y = take(pl.down_mode == 1 ? sizeof(uint16_t) * pl.P * H : 0);
+  pl.total = off;
+  return pl;
+}
+
+// Grid limits of the launches a plan makes.
+w4a16_status_t check_plan(const w4a16_moe_desc_t* d, const Plan& pl) {
+  if (pl.MT > 65535)
+    return fail(W4A16_ERR_UNSUPPORTED, "topk_ids: %lld expert tiles exceed 65535 (too many routes)",
+                (long long)pl.MT);
+  if (d->num_tokens > 65535)
+    return fail(W4A16_ERR_UNSUPPORTED, "x: num_tokens=%d exceeds 65535", d->num_tokens);
+  return W4A16_OK;
+}
+
+bool misaligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+w4a16_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return W4A16_OK;
+  return fail(W4A16_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w4a16_status_string(w4a16_status_t s) {
+  switch (s) {
+    case W4A16_OK: return "ok";
+    case W4A16_ERR_INVALID_ARG: return "invalid argument";
+    case W4A16_ERR_UNSUPPORTED: return "unsupported configuration";
+    case W4A16_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case W4A16_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* w4a16_last_error_message(void) { return g_last_error.c_str(); }
+
+w4a16_status_t w4a16_moe_workspace_size(const w4a16_moe_desc_t* desc, size_t* bytes) {
+  const w4a16_status_t st = check_desc(desc);
+  if (st != W4A16_OK) return st;
+  if (bytes == nullptr) return fail(W4A16_ERR_INVALID_ARG, "bytes: null pointer");
+  const Plan pl = make_plan(desc);
+  const w4a16_status_t st2 = check_plan(desc, pl);
+  if (st2 != W4A16_OK) return st2;
+  *bytes = pl.total;
+  return W4A16_OK;
+}
+
+w4a16_status_t w4a16_moe_get_plan(const w4a16_moe_desc_t* desc, w4a16_moe_plan_t* plan) {
+  const w4a16_status_t st = check_desc(desc);
+  if (st != W4A16_OK) return st;
+  if (plan == nullptr) return fail(W4A16_ERR_INVALID_ARG, "plan: null pointer");
+  const Plan pl = make_plan(desc);
+  const w4a16_status_t st2 = check_plan(desc, pl);
+  if (st2 != W4A16_OK) return st2;
+  plan->block_m = pl.bm;
+  plan->split_k = pl.split;
+  plan->k_chunk = pl.kchunk;
+  plan->down_mode = pl.down_mode;
+  plan->max_positions = pl.P;
+  plan->max_tiles = pl.MT;
+  plan->workspace_bytes = pl.total;
+  return W4A16_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+struct StageEvents {
+  hipEvent_t* ev;
+  int n;
+  hipStream_t s;
+  hipError_t mark(int i) const {
+    return (ev != nullptr && i < n && ev[i] != nullptr) ? hipEventRecord(ev[i], s) : hipSuccess;
+  }
+};
+
+w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void* w13_scales,
+                            const uint8_t* w2_packed, const void* w2_scales,
+                            const int32_t* topk_ids, const float* topk_weights, void* out,
+                            const w4a16_moe_desc_t* desc, void* workspace, size_t workspace_bytes,
+                            w4a16_stream_t stream_, hipEvent_t* events, int n_events) {
+  w4a16_status_t st = check_desc(desc);
+  if (st != W4A16_OK) return st;
+  const Plan pl = make_plan(desc);
+  st = check_plan(desc, pl);
+  if (st != W4A16_OK) return st;
+  if (n_events < 0) return fail(W4A16_ERR_INVALID_ARG, "n_events: %d < 0", n_events);
+  if (desc->num_tokens == 0) return W4A16_OK;
+
+  struct {
+    const void* p;
+    const char* name;
+    size_t align;
+  } ptrs[] = {{x, "x", 16},           {w13_packed, "w13_packed", 16}, {w13_scales, "w13_scales", 4},
+              {w2_packed, "w2_packed", 16}, {w2_scales, "w2_scales", 4}, {topk_ids, "topk_ids", 4},
+              {topk_weights, "topk_weights", 4}, {out, "out", 16}, {workspace, "workspace", 16}};
+  for (const auto& q : ptrs) {
+    if (q.p == nullptr) return fail(W4A16_ERR_INVALID_ARG, "%s: null pointer", q.name);
+    if (misaligned(q.p, q.align))
+      return fail(W4A16_ERR_INVALID_ARG, "%s: address not %zu-byte aligned", q.name, q.align);
+  }
+  if (workspace_bytes < pl.total)
+    return fail(W4A16_ERR_WORKSPACE_TOO_SMALL, "workspace: %zu bytes given, %zu needed",
+                workspace_bytes, pl.total);
+
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  const StageEvents evs{events, n_events, stream};
+  const int E = desc->num_local_experts, H = desc->hidden, I = desc->intermediate;
+  const int K = desc->top_k;
+  const bool group = desc->qlayout == W4A16_Q_GROUP_K;
+  char* ws = static_cast<char*>(workspace);
+  auto* counts = reinterpret_cast<int32_t*>(ws + pl.off_counts);
+  auto* offsets = reinterpret_cast<int32_t*>(ws + pl.off_offsets);
+  auto* slot = reinterpret_cast<int32_t*>(ws + pl.off_slot);
+  auto* sorted = reinterpret_cast<int32_t*>(ws + pl.off_sorted);
+  auto* tile = reinterpret_cast<int32_t*>(ws + pl.off_tile);
+  auto* counters = reinterpret_cast<int32_t*>(ws + pl.off_counters);
+  auto* act = reinterpret_cast<uint16_t*>(ws + pl.off_act);
+  auto* partial = reinterpret_cast<float*>(ws + pl.off_partial);
+  auto* ybuf = reinterpret_cast<uint16_t*>(ws + pl.off_y);
+
+  // a1: route preparation (also zeroes the split-K arrival counters)
+  st = hip_status(evs.mark(0), "stage event");
+  if (st != W4A16_OK) return st;
+  st = hip_status(w4moe::launch_route_prep(topk_ids, static_cast<int>(pl.R), E,
+                                           desc->expert_offset, pl.bm, counts, offsets, sorted,
+                                           slot, tile, counters,
+                                           pl.split > 1 ? static_cast<int>(pl.MT * pl.n_tiles_up) : 0,
+                                           stream),
+                  "route preparation launch");
+  if (st == W4A16_OK) st = hip_status(evs.mark(1), "stage event");
+  if (st != W4A16_OK) return st;
+
+  // a2-a4: gathered gate/up (or w1) GEMM with the activation epilogue
+  const int64_t w13_bytes = static_cast<int64_t>(pl.N1) * H / 2;
+  const int64_t w13_sc = group ? static_cast<int64_t>(pl.N1) * (H / 32) : pl.N1;
+  const int64_t w2_bytes = static_cast<int64_t>(H) * I / 2;
+  const int64_t w2_sc = group ? static_cast<int64_t>(H) * (I / 32) : H;
+
+  w4moe::GemmParams up{};
+  up.a = static_cast<const uint16_t*>(x);
+  up.lda = H;
+  up.sorted = sorted;
+  up.top_k = K;
+  up.wq = w13_packed;
+  up.ws = static_cast<const uint16_t*>(w13_scales);
+  up.wq_expert_bytes = w13_bytes;
+  up.ws_expert_elems = w13_sc;
+  up.K = H;
+  up.n_cols = I;
+  up.up_rows = I;
+  up.tile_expert = tile;
+  up.offsets = offsets;
+  up.E = E;
+  up.bm = pl.bm;
+  up.split = pl.split;
+  up.kchunk = pl.kchunk;
+  up.partial = partial;
+  up.counters = counters;
+  up.P = pl.P;
+  up.n_total = pl.N1;
+  up.out = act;
+  up.ldo = I;
+  up.n_tiles = pl.n_tiles_up;
+  st = hip_status(evs.mark(2), "stage event");
+  if (st != W4A16_OK) return st;
+  st = hip_status(w4moe::launch_grouped_gemm(up, desc->dtype, desc->qlayout, pl.ms, pl.mode_up,
+                                             static_cast<int>(pl.MT), stream),
+                  "gate/up GEMM launch");
+  if (st == W4A16_OK) st = hip_status(evs.mark(3), "stage event");
+  if (st != W4A16_OK) return st;
+
+  if (pl.down_mode == 2) {
+    // a5+a6 fused per token
+    w4moe::FusedDownParams fd{};
+    fd.act = act;
+    fd.wq = w2_packed;
+    fd.ws = static_cast<const uint16_t*>(w2_scales);
+    fd.wq_expert_bytes = w2_bytes;
+    fd.ws_expert_elems = w2_sc;
+    fd.ids = topk_ids;
+    fd.wts = topk_weights;
+    fd.slot = slot;
+    fd.top_k = K;
+    fd.E = E;
+    fd.off = desc->expert_offset;
+    fd.I = I;
+    fd.H = H;
+    fd.out = static_cast<uint16_t*>(out);
+    st = hip_status(evs.mark(4), "stage event");
+    if (st != W4A16_OK) return st;
+    st = hip_status(w4moe::launch_fused_down(fd, desc->dtype, desc->qlayout, desc->num_tokens,
+                                             stream),
+                    "fused down GEMM launch");
+    if (st == W4A16_OK) st = hip_status(evs.mark(5), "stage event");
+    return st;
+  }
+
+  // a5: grouped down GEMM -> 16-bit expert outputs
+  w4moe::GemmParams dn{};
+  dn.a = act;
+  dn.lda = I;
+  dn.sorted = sorted;
+  dn.top_k = K;
+  dn.wq = w2_packed;
+  dn.ws = static_cast<const uint16_t*>(w2_scales);
+  dn.wq_expert_bytes = w2_bytes;
+  dn.ws_expert_elems = w2_sc;
+  dn.K = I;
+  dn.n_cols = H;
+  dn.up_rows = 0;
+  dn.tile_expert = tile;
+  dn.offsets = offsets;
+  dn.E = E;
+  dn.bm = pl.bm;
+  dn.split = 1;
+  dn.kchunk = I;
+  dn.partial = nullptr;
+  dn.counters = nullptr;
+  dn.P = pl.P;
+  dn.n_total = H;
+  dn.out = ybuf;
+  dn.ldo = H;
+  dn.n_tiles = pl.n_tiles_down;
+  st = hip_status(evs.mark(4), "stage event");
+  if (st != W4A16_OK) return st;
+  st = hip_status(w4moe::launch_grouped_gemm(dn, desc->dtype, desc->qlayout, pl.ms,
+                                             w4moe::MODE_DOWN, static_cast<int>(pl.MT), stream),
+                  "down GEMM launch");
+  if (st == W4A16_OK) st = hip_status(evs.mark(5), "stage event");
+  if (st != W4A16_OK) return st;
+
+  // a6: FP32 combine in fixed top-k order, one 16-bit cast
+  w4moe::CombineParams cb{};
+  cb.y = ybuf;
+  cb.slot = slot;
+  cb.wts = topk_weights;
+  cb.top_k = K;
+  cb.H = H;
+  cb.out = static_cast<uint16_t*>(out);
+  st = hip_status(evs.mark(6), "stage event");
+  if (st != W4A16_OK) return st;
+  st = hip_status(w4moe::launch_combine(cb, desc->dtype, desc->num_tokens, stream),
+                  "combine launch");
+  if (st == W4A16_OK) st = hip_status(evs.mark(7), "stage event");
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+w4a16_status_t w4a16_moe_forward(const void* x, const uint8_t* w13_packed, const void* w13_scales,
+                                 const uint8_t* w2_packed, const void* w2_scales,
+                                 const int32_t* topk_ids, const float* topk_weights, void* out,
+                                 const w4a16_moe_desc_t* desc, void* workspace,
+                                 size_t workspace_bytes, w4a16_stream_t stream) {
+  return forward_impl(x, w13_packed, w13_scales, w2_packed, w2_scales, topk_ids, topk_weights,
+                      out, desc, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+w4a16_status_t w4a16_moe_forward_timed(const void* x, const uint8_t* w13_packed,
+                                       const void* w13_scales, const uint8_t* w2_packed,
+                                       const void* w2_scales, const int32_t* topk_ids,
+                                       const float* topk_weights, void* out,
+                                       const w4a16_moe_desc_t* desc, void* workspace,
+                                       size_t workspace_bytes, w4a16_stream_t stream,
+                                       void* const* stage_events, int32_t n_events) {
+  return forward_impl(x, w13_packed, w13_scales, w2_packed, w2_scales, topk_ids, topk_weights,
+                      out, desc, workspace, workspace_bytes, stream,
+                      reinterpret_cast<hipEvent_t*>(const_cast<void**>(stage_events)), n_events);
+}
+
+w4a16_status_t w4a16_moe_prepare_routes(const w4a16_moe_desc_t* desc, const int32_t* topk_ids,
+                                        int32_t block_m, int32_t* counts, int32_t* offsets,
+                                        int32_t* sorted_routes, int64_t sorted_capacity,
+                                        int32_t* route_slot, w4a16_stream_t stream_) {
+  if (desc == nullptr) return fail(W4A16_ERR_INVALID_ARG, "desc: null pointer");
+  if (desc->num_tokens < 0)
+    return fail(W4A16_ERR_INVALID_ARG, "desc.num_tokens: %d < 0", desc->num_tokens);
+  if (desc->top_k <= 0 || desc->top_k > 32)
+    return fail(W4A16_ERR_INVALID_ARG, "desc.top_k: %d (1..32)", desc->top_k);
+  if (desc->num_local_experts <= 0 || desc->num_local_experts > 1024)
+    return fail(W4A16_ERR_INVALID_ARG, "desc.num_local_experts: %d (1..1024)",
+                desc->num_local_experts);
+  if (block_m < 1 || block_m > 256)
+    return fail(W4A16_ERR_INVALID_ARG, "block_m: %d (1..256)", block_m);
+  const int64_t R = static_cast<int64_t>(desc->num_tokens) * desc->top_k;
+  if (R > (int64_t(1) << 26))
+    return fail(W4A16_ERR_UNSUPPORTED, "topk_ids: %lld routes exceed 2^26", (long long)R);
+  const int64_t need = R + std::min<int64_t>(desc->num_local_experts, R) * (block_m - 1);
+  if (sorted_capacity < need)
+    return fail(W4A16_ERR_INVALID_ARG, "sorted_routes: capacity %lld < %lld",
+                (long long)sorted_capacity, (long long)need);
+  struct {
+    const void* p;
+    const char* name;
+  } ptrs[] = {{counts, "counts"}, {offsets, "offsets"}, {sorted_routes, "sorted_routes"},
+              {route_slot, "route_slot"}, {topk_ids, "topk_ids"}};
+  for (const auto& q : ptrs) {
+    if (q.p == nullptr && !(R == 0 && (q.p == route_slot || q.p == topk_ids || q.p == sorted_routes)))
+      return fail(W4A16_ERR_INVALID_ARG, "%s: null pointer", q.name);
+  }
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  return hip_status(w4moe::launch_route_prep(topk_ids, static_cast<int>(R),
+                                             desc->num_local_experts, desc->expert_offset,
+                                             block_m, counts, offsets, sorted_routes, route_slot,
+                                             nullptr, nullptr, 0, stream),
+                    "route preparation launch");
+}
+
+w4a16_status_t w4a16_unpack_int4(const uint8_t* packed, int64_t n_bytes, int8_t* out,
+                                 w4a16_stream_t stream_) {
+  if (n_bytes < 0) return fail(W4A16_ERR_INVALID_ARG, "n_bytes: %lld < 0", (long long)n_bytes);
+  if (n_bytes == 0) return W4A16_OK;
+  if (packed == nullptr) return fail(W4A16_ERR_INVALID_ARG, "packed: null pointer");
+  if (out == nullptr) return fail(W4A16_ERR_INVALID_ARG, "out: null pointer");
+  if (n_bytes > (int64_t(1) << 33))
+    return fail(W4A16_ERR_UNSUPPORTED, "n_bytes: %lld too large", (long long)n_bytes);
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  return hip_status(w4moe::launch_unpack(packed, n_bytes, out, stream), "unpack launch");
+}
+
+}  // extern "C"
