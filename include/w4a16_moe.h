@@ -89,18 +89,19 @@ typedef struct {
   int32_t dtype;              /* w4a16_dtype_t                                    */
   int32_t act;                /* w4a16_act_t                                      */
   int32_t qlayout;            /* w4a16_qlayout_t                                  */
-  int32_t force_block_m;      /* 0 or 16/32/64: rows per expert tile             */
-  int32_t force_split_k;      /* 0 or >= 1: partitions of the gate/up reduction   */
-  int32_t force_down;         /* 0, 1 = grouped down GEMM + combine kernel,
-                                 2 = per-token down GEMM with the combine fused   */
+  int32_t force_path;         /* 0, 1 = grouped (route preparation, expert tiles,
+                                 down GEMM, combine kernel), 2 = small batch (no
+                                 route preparation; needs T*K <= 256)            */
+  int32_t force_block_m;      /* grouped path: 0 or 16/32/64 rows per expert tile */
 } w4a16_moe_desc_t;
 
 /* Variant the library runs for a descriptor (for tests and reports). */
 typedef struct {
-  int32_t block_m;            /* rows per expert tile (route padding unit)       */
-  int32_t split_k;            /* partitions of the gate/up reduction             */
-  int32_t k_chunk;            /* reduction length per partition                  */
-  int32_t down_mode;          /* 1 grouped + combine, 2 fused per token          */
+  int32_t path;               /* 1 grouped, 2 small batch                        */
+  int32_t block_m;            /* grouped path: rows per expert tile              */
+  int32_t k_slice;            /* gate/up reduction slice per wave (8 waves split
+                                 the reduction when tiles have few rows)         */
+  int32_t reserved;
   int64_t max_positions;      /* capacity of the padded route list               */
   int64_t max_tiles;          /* capacity of the expert tile list                */
   size_t workspace_bytes;     /* bytes w4a16_moe_forward needs                   */

@@ -57,8 +57,7 @@ def good(**kw):
     ("hidden", 96, 2, "hidden=96"),
     ("intermediate", 1828, 2, "intermediate=1828"),
     ("force_block_m", 48, 1, "force_block_m"),
-    ("force_split_k", -2, 1, "force_split_k"),
-    ("force_down", 5, 1, "force_down"),
+    ("force_path", 3, 1, "force_path"),
 ])
 def test_descriptor_errors(field, value, status, needle):
     d = good()
@@ -120,19 +119,37 @@ def test_prepare_routes_and_unpack_argument_errors():
 
 
 def test_plans_by_route_count():
-    # decode: small tiles, split-K, per-token down kernel
+    # decode: small-batch path, the reduction split over 8 waves in 128-blocks
     p1 = B.get_plan(B.make_desc(num_tokens=1, hidden=7168, intermediate=256,
                                 num_local_experts=384, top_k=8))
-    assert p1.block_m == 16 and p1.split_k > 1 and p1.down_mode == 2
-    assert p1.k_chunk % 128 == 0 and p1.split_k * p1.k_chunk >= 7168
-    # prefill: big tiles, no split, grouped down + combine
+    assert p1.path == 2 and p1.k_slice == 7 * 128
+    # prefill: grouped path with 64-row expert tiles
     p2 = B.get_plan(B.make_desc(num_tokens=2048, hidden=7168, intermediate=256,
                                 num_local_experts=384, top_k=8))
-    assert p2.block_m == 64 and p2.split_k == 1 and p2.down_mode == 1
+    assert p2.path == 1 and p2.block_m == 64
     assert p2.max_positions == 2048 * 8 + 384 * 63
     # forcing is honoured and the workspace follows the plan
     d = B.make_desc(num_tokens=16, hidden=256, intermediate=384, num_local_experts=8, top_k=2,
-                    force_block_m=32, force_split_k=2, force_down=1)
+                    force_block_m=32, force_path=1)
     p3 = B.get_plan(d)
-    assert (p3.block_m, p3.split_k, p3.down_mode) == (32, 2, 1)
+    assert (p3.path, p3.block_m) == (1, 32)
     assert p3.workspace_bytes == B.workspace_size(d)
+
+
+def test_small_batch_path_limits():
+    # more than 64 routes (one wave's ballot) cannot take the small-batch path
+    d = B.make_desc(num_tokens=9, hidden=256, intermediate=384, num_local_experts=8, top_k=8,
+                    force_path=2)
+    with pytest.raises(B.W4A16Error) as ei:
+        B.workspace_size(d)
+    assert ei.value.status == 2 and "routes" in ei.value.message
+    d.num_tokens = 8
+    assert B.get_plan(d).path == 2
+    # hidden sizes beyond 8 waves x 1024 cannot take it either
+    d2 = B.make_desc(num_tokens=1, hidden=8256, intermediate=384, num_local_experts=8, top_k=2,
+                     force_path=2)
+    with pytest.raises(B.W4A16Error) as ei:
+        B.workspace_size(d2)
+    assert "hidden" in ei.value.message
+    d2.force_path = 0
+    assert B.get_plan(d2).path == 1

@@ -73,11 +73,10 @@ def test_route_prep_skewed_and_local_share():
 # forward parity, every variant on the small gated workload
 # ---------------------------------------------------------------------------
 
-VARIANTS = [dict(force_block_m=bm, force_split_k=s, force_down=d)
-            for bm in (16, 32, 64) for s in (1, 2, 3) for d in (1, 2)]
+VARIANTS = [dict(force_path=2)] + [dict(force_path=1, force_block_m=bm) for bm in (16, 32, 64)]
 
 
-@pytest.mark.parametrize("force", VARIANTS, ids=lambda f: "bm{force_block_m}-s{force_split_k}-d{force_down}".format(**f))
+@pytest.mark.parametrize("force", VARIANTS, ids=lambda f: "path{force_path}-bm{0}".format(f.get("force_block_m", 0), **f))
 def test_tiny_all_variants(force):
     wl = synth.WORKLOADS["tiny"]
     Wc, Wg = weights("tiny")
@@ -98,11 +97,15 @@ def test_configs_small_token_counts(name, T):
 
 
 @pytest.mark.parametrize("name,T,force", [
-    ("kimi_tp8", 8, dict(force_down=1)), ("kimi_tp8", 32, dict(force_down=2)),
-    ("kimi_tp8", 8, dict(force_split_k=1)), ("kimi_tp8", 32, dict(force_block_m=64)),
-    ("per_channel", 8, dict(force_down=1, force_split_k=3)),
-    ("relu2_skew", 32, dict(force_down=2, force_block_m=16, force_split_k=5)),
-    ("deepseek_local", 16, dict(force_down=1, force_block_m=32))])
+    ("kimi_tp8", 8, dict(force_path=1)), ("kimi_tp8", 4, dict(force_path=2)),
+    ("kimi_tp8", 8, dict(force_path=1, force_block_m=32)),
+    ("kimi_tp8", 32, dict(force_path=1, force_block_m=64)),
+    ("per_channel", 8, dict(force_path=1, force_block_m=16)),
+    ("per_channel", 8, dict(force_path=1, force_block_m=32)),
+    ("relu2_skew", 8, dict(force_path=2)),
+    ("relu2_skew", 32, dict(force_path=1, force_block_m=32)),
+    ("deepseek_local", 16, dict(force_path=1, force_block_m=32)),
+    ("deepseek_local", 16, dict(force_path=1, force_block_m=16))])
 def test_config_variants(name, T, force):
     wl = synth.WORKLOADS[name]
     Wc, Wg = weights(name)
@@ -128,8 +131,8 @@ def test_zero_tokens():
     assert out.shape == (0, wl.hidden)
 
 
-@pytest.mark.parametrize("down", [1, 2])
-def test_invalid_routes_and_empty_tokens(down):
+@pytest.mark.parametrize("path", [1, 2])
+def test_invalid_routes_and_empty_tokens(path):
     wl, Wc, Wg = _small()
     tc = tokens(wl, 16)
     ids = tc.topk_ids.clone()
@@ -138,7 +141,7 @@ def test_invalid_routes_and_empty_tokens(down):
     ids[5, 0] = 2 ** 31 - 1
     ids[7, :] = -(2 ** 31)
     tc = synth.Tokens(tc.x, ids, tc.topk_weights)
-    out = forward(wl, Wg, tc.to("cuda"), force_down=down)
+    out = forward(wl, Wg, tc.to("cuda"), force_path=path)
     ref = oracle_out(wl, Wc, tc)
     assert_close(out, ref, "invalid routes")
     o = out.cpu()
@@ -146,23 +149,26 @@ def test_invalid_routes_and_empty_tokens(down):
     assert not torch.signbit(o[0].float()).any()
 
 
-@pytest.mark.parametrize("down", [1, 2])
-def test_all_routes_invalid_gives_zeros(down):
+@pytest.mark.parametrize("path", [1, 2])
+def test_all_routes_invalid_gives_zeros(path):
     wl, Wc, Wg = _small()
     tc = tokens(wl, 16)
     ids = torch.full_like(tc.topk_ids, 100)
-    out = forward(wl, Wg, synth.Tokens(tc.x, ids, tc.topk_weights).to("cuda"), force_down=down)
+    out = forward(wl, Wg, synth.Tokens(tc.x, ids, tc.topk_weights).to("cuda"), force_path=path)
     assert (out.cpu() == 0).all()
 
 
 def test_single_expert_receives_everything():
     wl, Wc, Wg = _small()
-    tc = tokens(wl, 40)
+    tc = tokens(wl, 32)
     ids = torch.full_like(tc.topk_ids, 3)       # duplicate ids: each route counts
     tc = synth.Tokens(tc.x, ids, tc.topk_weights)
+    ref = oracle_out(wl, Wc, tc)
     for bm in (16, 32, 64):
-        out = forward(wl, Wg, tc.to("cuda"), force_block_m=bm)
-        assert_close(out, oracle_out(wl, Wc, tc), f"one expert bm={bm}")
+        out = forward(wl, Wg, tc.to("cuda"), force_path=1, force_block_m=bm)
+        assert_close(out, ref, f"one expert bm={bm}")
+    out = forward(wl, Wg, tc.to("cuda"), force_path=2)           # 64 rows, 16 passes of 4
+    assert_close(out, ref, "one expert small-batch path")
 
 
 def test_poisoned_workspace_and_output():
@@ -172,8 +178,8 @@ def test_poisoned_workspace_and_output():
     tc = tokens(wl, 16)
     tg = tc.to("cuda")
     ref = oracle_out(wl, Wc, tc)
-    for force in (dict(force_split_k=3, force_down=2), dict(force_split_k=2, force_down=1,
-                                                              force_block_m=64)):
+    for force in (dict(force_path=2), dict(force_path=1, force_block_m=16),
+                  dict(force_path=1, force_block_m=64)):
         d = binding.desc_for(wl, 16, **force)
         ws = torch.full((binding.workspace_size(d),), 0xFF, dtype=torch.uint8, device="cuda")
         out = torch.full((16, wl.hidden), float("nan"), dtype=wl.dtype, device="cuda")
@@ -182,15 +188,15 @@ def test_poisoned_workspace_and_output():
         assert_close(out, ref, f"poisoned {force}")
 
 
-def test_split_partitions_cover_the_reduction_exactly():
-    """Partitions are whole 128-blocks and never empty: the planner clamps the
-    requested count, and every partition writes its full partial."""
-    wl, Wc, Wg = _small()                          # H = 256 -> 2 blocks of 128
+def test_reduction_slices_cover_every_block():
+    """The small-batch gate/up kernel splits the reduction over 8 waves in
+    128-blocks; with H = 256 six waves get nothing and must add exact zeros."""
+    wl, Wc, Wg = _small()
     tc = tokens(wl, 16)
-    out = forward(wl, Wg, tc.to("cuda"), force_split_k=2, force_block_m=16)
-    assert_close(out, oracle_out(wl, Wc, tc), "split 2 of 2 blocks")
-    pl = binding.get_plan(binding.desc_for(wl, 16, force_split_k=64))
-    assert pl.split_k == 2 and pl.k_chunk == 128
+    pl = binding.get_plan(binding.desc_for(wl, 16, force_path=2))
+    assert pl.k_slice == 128
+    out = forward(wl, Wg, tc.to("cuda"), force_path=2)
+    assert_close(out, oracle_out(wl, Wc, tc), "H=256 over 8 waves")
 
 
 # ---------------------------------------------------------------------------
@@ -208,20 +214,20 @@ def test_bitwise_repeatable(name, T):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-@pytest.mark.parametrize("down", [1, 2])
-def test_gpu_invariances_bitwise(down):
+@pytest.mark.parametrize("path", [1, 2])
+def test_gpu_invariances_bitwise(path):
     wl, Wc, Wg = _small()
     tc = tokens(wl, 16)
-    base = forward(wl, Wg, tc.to("cuda"), force_down=down).cpu()
+    base = forward(wl, Wg, tc.to("cuda"), force_path=path).cpu()
     # routing weights x2 -> output x2 exactly
     t2 = synth.Tokens(tc.x, tc.topk_ids, tc.topk_weights * 2)
-    o2 = forward(wl, Wg, t2.to("cuda"), force_down=down).cpu()
+    o2 = forward(wl, Wg, t2.to("cuda"), force_path=path).cpu()
     assert torch.equal(o2.float(), base.float() * 2)
     # token permutation -> output permutation exactly
     perm = torch.randperm(16, generator=torch.Generator().manual_seed(1))
     tp = synth.Tokens(tc.x[perm].contiguous(), tc.topk_ids[perm].contiguous(),
                       tc.topk_weights[perm].contiguous())
-    op = forward(wl, Wg, tp.to("cuda"), force_down=down).cpu()
+    op = forward(wl, Wg, tp.to("cuda"), force_path=path).cpu()
     assert torch.equal(op.view(torch.int16), base[perm].view(torch.int16))
 
 

@@ -36,12 +36,12 @@ w4a16_status_t fail(w4a16_status_t st, const char* fmt, ...) {
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Plan {
-  int bm = 16, ms = 1, split = 1, kchunk = 0, down_mode = 2;
+  int path = 2, bm = 16, ms = 1, kslice = 128, nkb = 1, nkb_tile = 1;
   int n_tiles_up = 0, n_tiles_down = 0, mode_up = 0;
-  int64_t R = 0, P = 0, MT = 0;
+  int64_t R = 0, P = 0, MT = 0, items = 0;
   int N1 = 0;
   size_t off_counts = 0, off_offsets = 0, off_slot = 0, off_sorted = 0, off_tile = 0,
-         off_counters = 0, off_act = 0, off_partial = 0, off_y = 0, total = 0;
+         off_act = 0, off_y = 0, total = 0;
 };
 
 w4a16_status_t check_desc(const w4a16_moe_desc_t* d) {
@@ -76,15 +76,19 @@ w4a16_status_t check_desc(const w4a16_moe_desc_t* d) {
   if (d->force_block_m != 0 && d->force_block_m != 16 && d->force_block_m != 32 &&
       d->force_block_m != 64)
     return fail(W4A16_ERR_INVALID_ARG, "desc.force_block_m: %d (0, 16, 32 or 64)", d->force_block_m);
-  if (d->force_split_k < 0)
-    return fail(W4A16_ERR_INVALID_ARG, "desc.force_split_k: %d < 0", d->force_split_k);
-  if (d->force_down < 0 || d->force_down > 2)
-    return fail(W4A16_ERR_INVALID_ARG, "desc.force_down: %d (0, 1 or 2)", d->force_down);
+  if (d->force_path < 0 || d->force_path > 2)
+    return fail(W4A16_ERR_INVALID_ARG, "desc.force_path: %d (0, 1 or 2)", d->force_path);
   return W4A16_OK;
 }
 
 // Variant selection from the route count R = T*K ([P1] Modification:
 // route-count-based tile selection and small-batch split-K).
+//   path 2 (small batch): R <= 64.  No route preparation; the gate/up kernel
+//     finds each touched expert's rows in the ids and splits the reduction
+//     over 8 waves; the down kernel combines per token.
+//   path 1 (grouped): route preparation into block_m-row expert tiles, the
+//     gate/up GEMM per tile (block_m 16: the 8-wave split-reduction kernel),
+//     the grouped down GEMM and the FP32 combine.
 Plan make_plan(const w4a16_moe_desc_t* d) {
   Plan pl;
   const int E = d->num_local_experts, H = d->hidden, I = d->intermediate, K = d->top_k;
@@ -92,6 +96,24 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
   pl.R = static_cast<int64_t>(d->num_tokens) * K;
   pl.N1 = gated ? 2 * I : I;
   pl.mode_up = gated ? w4moe::MODE_UP_GATED : w4moe::MODE_UP_RELU2;
+  const int down_blocks = (I + 127) / 128;
+  pl.items = static_cast<int64_t>(K) *
+             ((down_blocks + w4moe::kDecDownSliceBlocks - 1) / w4moe::kDecDownSliceBlocks);
+
+  if (d->force_path) pl.path = d->force_path;
+  else pl.path = (pl.R <= w4moe::kSmallMaxRoutes && pl.items <= w4moe::kDecMaxItems &&
+                  H <= 8 * w4moe::kSmallMaxSlice &&
+                  static_cast<int64_t>(K) * I <= w4moe::kDecActLoads * w4moe::kDecThreadsAll * 8)
+                     ? 2 : 1;
+
+  // per-wave reduction slice of the split-reduction gate/up kernels
+  // (16 waves on the small-batch path, 8 on grouped 16-row tiles)
+  const int up_blocks = (H + 127) / 128;
+  const int waves = 8;  // reduction slices of both split-reduction kernels
+  const int per_wave = (up_blocks + waves - 1) / waves;
+  pl.kslice = per_wave * 128;
+  pl.nkb = per_wave;  // small-batch kernel: exact; 16-row tile kernel: rounded to 1/2/4
+  pl.nkb_tile = per_wave <= 1 ? 1 : (per_wave <= 2 ? 2 : 4);
 
   // expected routes per touched expert under uniform routing
   const double R = static_cast<double>(pl.R);
@@ -108,38 +130,23 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
                         : (I + w4moe::kWgColsPlain - 1) / w4moe::kWgColsPlain;
   pl.n_tiles_down = (H + w4moe::kWgColsPlain - 1) / w4moe::kWgColsPlain;
 
-  // split-K: aim for >= 1024 workgroups in the gate/up GEMM
-  const double tiles_est = D * std::ceil(per_expert / pl.bm);
-  const int kblocks = H / 128 > 0 ? H / 128 : 1;
-  int split = d->force_split_k;
-  if (split == 0) {
-    const double wgs = tiles_est * pl.n_tiles_up;
-    split = static_cast<int>(std::ceil(1024.0 / std::max(1.0, wgs)));
-  }
-  split = std::max(1, std::min(split, (H + 127) / 128));
-  (void)kblocks;
-  pl.kchunk = ((H + split - 1) / split + 127) / 128 * 128;
-  pl.split = (H + pl.kchunk - 1) / pl.kchunk;
-
-  if (d->force_down) pl.down_mode = d->force_down;
-  else pl.down_mode = pl.R <= 64 ? 2 : 1;
-
-  // workspace carve (256-byte aligned pieces)
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
     off = align_up(off + bytes, 256);
     return o;
   };
-  pl.off_counts = take(sizeof(int32_t) * E);
-  pl.off_offsets = take(sizeof(int32_t) * (E + 1));
-  pl.off_slot = take(sizeof(int32_t) * std::max<int64_t>(pl.R, 1));
-  pl.off_sorted = take(sizeof(int32_t) * std::max<int64_t>(pl.P, 1));
-  pl.off_tile = take(sizeof(int32_t) * std::max<int64_t>(pl.MT, 1));
-  pl.off_counters = take(pl.split > 1 ? sizeof(int32_t) * pl.MT * pl.n_tiles_up : 0);
-  pl.off_act = take(sizeof(uint16_t) * pl.P * I);
-  pl.off_partial = take(pl.split > 1 ? sizeof(float) * pl.split * pl.P * pl.N1 : 0);
-  pl.off_y = take(pl.down_mode == 1 ? sizeof(uint16_t) * pl.P * H : 0);
+  if (pl.path == 2) {
+    pl.off_act = take(sizeof(float) * std::max<int64_t>(pl.R, 1) * pl.N1);  // FP32 pre-activations
+  } else {
+    pl.off_counts = take(sizeof(int32_t) * E);
+    pl.off_offsets = take(sizeof(int32_t) * (E + 1));
+    pl.off_slot = take(sizeof(int32_t) * std::max<int64_t>(pl.R, 1));
+    pl.off_sorted = take(sizeof(int32_t) * std::max<int64_t>(pl.P, 1));
+    pl.off_tile = take(sizeof(int32_t) * std::max<int64_t>(pl.MT, 1));
+    pl.off_act = take(sizeof(uint16_t) * pl.P * I);
+    pl.off_y = take(sizeof(uint16_t) * pl.P * H);
+  }
   pl.total = off;
   return pl;
 }
@@ -151,6 +158,21 @@ w4a16_status_t check_plan(const w4a16_moe_desc_t* d, const Plan& pl) {
                 (long long)pl.MT);
   if (d->num_tokens > 65535)
     return fail(W4A16_ERR_UNSUPPORTED, "x: num_tokens=%d exceeds 65535", d->num_tokens);
+  if (pl.path == 2 && pl.R > w4moe::kSmallMaxRoutes)
+    return fail(W4A16_ERR_UNSUPPORTED, "topk_ids: %lld routes exceed the small-batch path's %d",
+                (long long)pl.R, w4moe::kSmallMaxRoutes);
+  if (pl.path == 2 && d->hidden > 8 * w4moe::kSmallMaxSlice)
+    return fail(W4A16_ERR_UNSUPPORTED, "x: hidden=%d exceeds the small-batch path's %d",
+                d->hidden, 8 * w4moe::kSmallMaxSlice);
+  if (pl.path == 2 &&
+      static_cast<int64_t>(d->top_k) * d->intermediate > w4moe::kDecActLoads * w4moe::kDecThreadsAll * 8)
+    return fail(W4A16_ERR_UNSUPPORTED,
+                "topk_ids/w2_packed: top_k * intermediate = %lld exceeds the small-batch path's %d",
+                (long long)d->top_k * d->intermediate, w4moe::kDecActLoads * w4moe::kDecThreadsAll * 8);
+  if (pl.path == 2 && pl.items > w4moe::kDecMaxItems)
+    return fail(W4A16_ERR_UNSUPPORTED,
+                "w2_packed: top_k * slices = %lld exceeds the small-batch path's %d",
+                (long long)pl.items, w4moe::kDecMaxItems);
   return W4A16_OK;
 }
 
@@ -196,10 +218,9 @@ w4a16_status_t w4a16_moe_get_plan(const w4a16_moe_desc_t* desc, w4a16_moe_plan_t
   const Plan pl = make_plan(desc);
   const w4a16_status_t st2 = check_plan(desc, pl);
   if (st2 != W4A16_OK) return st2;
+  plan->path = pl.path;
   plan->block_m = pl.bm;
-  plan->split_k = pl.split;
-  plan->k_chunk = pl.kchunk;
-  plan->down_mode = pl.down_mode;
+  plan->k_slice = pl.kslice;
   plan->max_positions = pl.P;
   plan->max_tiles = pl.MT;
   plan->workspace_bytes = pl.total;
@@ -259,87 +280,131 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
   auto* slot = reinterpret_cast<int32_t*>(ws + pl.off_slot);
   auto* sorted = reinterpret_cast<int32_t*>(ws + pl.off_sorted);
   auto* tile = reinterpret_cast<int32_t*>(ws + pl.off_tile);
-  auto* counters = reinterpret_cast<int32_t*>(ws + pl.off_counters);
   auto* act = reinterpret_cast<uint16_t*>(ws + pl.off_act);
-  auto* partial = reinterpret_cast<float*>(ws + pl.off_partial);
   auto* ybuf = reinterpret_cast<uint16_t*>(ws + pl.off_y);
 
-  // a1: route preparation (also zeroes the split-K arrival counters)
+  const int64_t w13_bytes = static_cast<int64_t>(pl.N1) * H / 2;
+  const int64_t w13_sc = group ? static_cast<int64_t>(pl.N1) * (H / 32) : pl.N1;
+  const int64_t w2_bytes = static_cast<int64_t>(H) * I / 2;
+  const int64_t w2_sc = group ? static_cast<int64_t>(H) * (I / 32) : H;
+  const bool gated = desc->act == W4A16_ACT_SILU_GATED;
+
+  w4moe::DecodeUpParams du{};
+  du.x = static_cast<const uint16_t*>(x);
+  du.lda = H;
+  du.ids = topk_ids;
+  du.R = static_cast<int>(pl.R);
+  du.top_k = K;
+  du.E = E;
+  du.off = desc->expert_offset;
+  du.sorted = sorted;
+  du.tile_expert = tile;
+  du.offsets = offsets;
+  du.wq = w13_packed;
+  du.ws = static_cast<const uint16_t*>(w13_scales);
+  du.wq_expert_bytes = w13_bytes;
+  du.ws_expert_elems = w13_sc;
+  du.K = H;
+  du.kslice = pl.kslice;
+  du.n_cols = I;
+  du.up_rows = I;
+  du.act = act;
+  du.ldo = I;
+
+  if (pl.path == 2) {
+    // small batch: FP32 pre-activations per touched expert (rows found in the
+    // ids), then the activation, the down GEMM and the combine per token
+    w4moe::SmallHParams sh{};
+    sh.x = static_cast<const uint16_t*>(x);
+    sh.lda = H;
+    sh.ids = topk_ids;
+    sh.R = static_cast<int>(pl.R);
+    sh.top_k = K;
+    sh.E = E;
+    sh.off = desc->expert_offset;
+    sh.wq = w13_packed;
+    sh.ws = static_cast<const uint16_t*>(w13_scales);
+    sh.wq_expert_bytes = w13_bytes;
+    sh.ws_expert_elems = w13_sc;
+    sh.K = H;
+    sh.kslice = pl.kslice;
+    sh.h = reinterpret_cast<float*>(ws + pl.off_act);
+    sh.ldh = pl.N1;
+    st = hip_status(evs.mark(2), "stage event");
+    if (st != W4A16_OK) return st;
+    st = hip_status(w4moe::launch_small_h(sh, desc->dtype, desc->qlayout, pl.nkb, pl.N1, stream),
+                    "gate/up GEMM launch");
+    if (st == W4A16_OK) st = hip_status(evs.mark(3), "stage event");
+    if (st != W4A16_OK) return st;
+    w4moe::DecodeDownParams dd{};
+    dd.h = sh.h;
+    dd.ldh = pl.N1;
+    dd.wq = w2_packed;
+    dd.ws = static_cast<const uint16_t*>(w2_scales);
+    dd.wq_expert_bytes = w2_bytes;
+    dd.ws_expert_elems = w2_sc;
+    dd.ids = topk_ids;
+    dd.wts = topk_weights;
+    dd.top_k = K;
+    dd.E = E;
+    dd.off = desc->expert_offset;
+    dd.I = I;
+    dd.H = H;
+    dd.out = static_cast<uint16_t*>(out);
+    st = hip_status(evs.mark(4), "stage event");
+    if (st != W4A16_OK) return st;
+    st = hip_status(w4moe::launch_decode_down(dd, desc->dtype, desc->qlayout, gated,
+                                              desc->num_tokens, stream),
+                    "down GEMM launch");
+    if (st == W4A16_OK) st = hip_status(evs.mark(5), "stage event");
+    return st;
+  }
+
+  // a1: route preparation into block_m-row expert tiles
   st = hip_status(evs.mark(0), "stage event");
   if (st != W4A16_OK) return st;
   st = hip_status(w4moe::launch_route_prep(topk_ids, static_cast<int>(pl.R), E,
                                            desc->expert_offset, pl.bm, counts, offsets, sorted,
-                                           slot, tile, counters,
-                                           pl.split > 1 ? static_cast<int>(pl.MT * pl.n_tiles_up) : 0,
-                                           stream),
+                                           slot, tile, nullptr, 0, stream),
                   "route preparation launch");
   if (st == W4A16_OK) st = hip_status(evs.mark(1), "stage event");
   if (st != W4A16_OK) return st;
 
   // a2-a4: gathered gate/up (or w1) GEMM with the activation epilogue
-  const int64_t w13_bytes = static_cast<int64_t>(pl.N1) * H / 2;
-  const int64_t w13_sc = group ? static_cast<int64_t>(pl.N1) * (H / 32) : pl.N1;
-  const int64_t w2_bytes = static_cast<int64_t>(H) * I / 2;
-  const int64_t w2_sc = group ? static_cast<int64_t>(H) * (I / 32) : H;
-
-  w4moe::GemmParams up{};
-  up.a = static_cast<const uint16_t*>(x);
-  up.lda = H;
-  up.sorted = sorted;
-  up.top_k = K;
-  up.wq = w13_packed;
-  up.ws = static_cast<const uint16_t*>(w13_scales);
-  up.wq_expert_bytes = w13_bytes;
-  up.ws_expert_elems = w13_sc;
-  up.K = H;
-  up.n_cols = I;
-  up.up_rows = I;
-  up.tile_expert = tile;
-  up.offsets = offsets;
-  up.E = E;
-  up.bm = pl.bm;
-  up.split = pl.split;
-  up.kchunk = pl.kchunk;
-  up.partial = partial;
-  up.counters = counters;
-  up.P = pl.P;
-  up.n_total = pl.N1;
-  up.out = act;
-  up.ldo = I;
-  up.n_tiles = pl.n_tiles_up;
   st = hip_status(evs.mark(2), "stage event");
   if (st != W4A16_OK) return st;
-  st = hip_status(w4moe::launch_grouped_gemm(up, desc->dtype, desc->qlayout, pl.ms, pl.mode_up,
-                                             static_cast<int>(pl.MT), stream),
-                  "gate/up GEMM launch");
+  if (pl.bm == 16) {
+    du.rows_from_ids = 0;
+    du.act_by_route = 0;
+    st = hip_status(w4moe::launch_decode_up(du, desc->dtype, desc->qlayout, gated, pl.nkb_tile,
+                                            static_cast<int>(pl.MT), stream),
+                    "gate/up GEMM launch");
+  } else {
+    w4moe::GemmParams up{};
+    up.a = static_cast<const uint16_t*>(x);
+    up.lda = H;
+    up.sorted = sorted;
+    up.top_k = K;
+    up.wq = w13_packed;
+    up.ws = static_cast<const uint16_t*>(w13_scales);
+    up.wq_expert_bytes = w13_bytes;
+    up.ws_expert_elems = w13_sc;
+    up.K = H;
+    up.n_cols = I;
+    up.up_rows = I;
+    up.tile_expert = tile;
+    up.offsets = offsets;
+    up.E = E;
+    up.bm = pl.bm;
+    up.out = act;
+    up.ldo = I;
+    up.n_tiles = pl.n_tiles_up;
+    st = hip_status(w4moe::launch_grouped_gemm(up, desc->dtype, desc->qlayout, pl.ms, pl.mode_up,
+                                               static_cast<int>(pl.MT), stream),
+                    "gate/up GEMM launch");
+  }
   if (st == W4A16_OK) st = hip_status(evs.mark(3), "stage event");
   if (st != W4A16_OK) return st;
-
-  if (pl.down_mode == 2) {
-    // a5+a6 fused per token
-    w4moe::FusedDownParams fd{};
-    fd.act = act;
-    fd.wq = w2_packed;
-    fd.ws = static_cast<const uint16_t*>(w2_scales);
-    fd.wq_expert_bytes = w2_bytes;
-    fd.ws_expert_elems = w2_sc;
-    fd.ids = topk_ids;
-    fd.wts = topk_weights;
-    fd.slot = slot;
-    fd.top_k = K;
-    fd.E = E;
-    fd.off = desc->expert_offset;
-    fd.I = I;
-    fd.H = H;
-    fd.out = static_cast<uint16_t*>(out);
-    st = hip_status(evs.mark(4), "stage event");
-    if (st != W4A16_OK) return st;
-    st = hip_status(w4moe::launch_fused_down(fd, desc->dtype, desc->qlayout, desc->num_tokens,
-                                             stream),
-                    "fused down GEMM launch");
-    if (st == W4A16_OK) st = hip_status(evs.mark(5), "stage event");
-    return st;
-  }
 
   // a5: grouped down GEMM -> 16-bit expert outputs
   w4moe::GemmParams dn{};
@@ -358,12 +423,6 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
   dn.offsets = offsets;
   dn.E = E;
   dn.bm = pl.bm;
-  dn.split = 1;
-  dn.kchunk = I;
-  dn.partial = nullptr;
-  dn.counters = nullptr;
-  dn.P = pl.P;
-  dn.n_total = H;
   dn.out = ybuf;
   dn.ldo = H;
   dn.n_tiles = pl.n_tiles_down;

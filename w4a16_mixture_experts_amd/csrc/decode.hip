@@ -1,0 +1,769 @@
+// decode.hip -- the small-batch path of the local W4A16 MoE forward: two
+// kernels, no route preparation pass.
+//
+// Sources (web pages, cited by tag and section):
+//   [P1] lmdeploy PR #4947, "feat(pytorch): add CuTeDSL W4A16 MoE backend"
+//        Modification: small-batch split-K, register-side INT4 dequantization,
+//        FP32 accumulation; invalid routes and masked expert counts.
+//   [P2] flashinfer PR #5186, "perf: reduce split W4A16 routing and output
+//        overhead"  Description, "Contract": FP32 combine in fixed top-k
+//        order before one 16-bit cast, no atomics.
+//
+// decode_up_kernel   grid (route slots or expert tiles) x (column tiles),
+//   8 waves.  Row source, selected by `rows_from_ids`:
+//     - from the ids themselves: the workgroup of route slot r reads all R
+//       ids, keeps the routes whose expert equals that of r (ascending), and
+//       proceeds only if r is the first of them, so every touched expert is
+//       handled exactly once and its weights are streamed once;
+//     - from a 16-row tile of the route-prepared list.
+//   The 8 waves split the reduction dim into contiguous slices; each wave's
+//   FP32 partial tile goes to LDS and wave 0 adds the slices in slice order,
+//   applies SiLU(gate)*up or ReLU^2 and writes the 16-bit activation rows.
+//   No partial sums leave the workgroup, so no cross-workgroup fence or
+//   counter is needed, and the result is independent of scheduling.
+//
+// decode_down_kernel  grid (32 output columns) x (tokens), 8 waves.  Work
+//   items are (route k, 256-wide slice of the reduction); each wave computes
+//   its items' 32 partial outputs in FP32 (one MFMA row: a route is a single
+//   activation row) into LDS; then 32 lanes add, for k = 0..K-1 in order,
+//   w[t,k] * (sum of k's slices in slice order) and cast once to 16 bits.
+#include "device.h"
+#include "internal.h"
+
+namespace w4moe {
+
+namespace {
+
+constexpr int kDecWaves = 8;
+constexpr int kDecThreads = kDecWaves * 64;
+
+template <int LAYOUT>
+struct BBlk {
+  uint32_t d[LAYOUT == Q_GROUP_K ? 4 : 8];
+  uint32_t s[2];
+};
+
+template <int LAYOUT>
+__device__ __forceinline__ void ld_b(BBlk<LAYOUT>& b, const uint8_t* brow, const uint16_t* srow,
+                                     int k0, int ng, int g, bool on, const void* safe) {
+  if constexpr (LAYOUT == Q_GROUP_K) {
+    const u32x4 v = load16_if(on && g < ng, brow + (k0 >> 1) + 16 * g, safe);
+    b.d[0] = v[0]; b.d[1] = v[1]; b.d[2] = v[2]; b.d[3] = v[3];
+    const uint32_t* sp = reinterpret_cast<const uint32_t*>(srow + (k0 >> 5));
+    b.s[0] = load4_if(on, sp, safe);
+    b.s[1] = load4_if(on && ng > 2, sp + 1, safe);
+  } else {
+    const bool ok = on && g < ng;
+    const u32x4 v0 = load16_if(ok, brow + k0 + 32 * g, safe);
+    const u32x4 v1 = load16_if(ok, brow + k0 + 32 * g + 16, safe);
+    b.d[0] = v0[0]; b.d[1] = v0[1]; b.d[2] = v0[2]; b.d[3] = v0[3];
+    b.d[4] = v1[0]; b.d[5] = v1[1]; b.d[6] = v1[2]; b.d[7] = v1[3];
+    b.s[0] = b.s[1] = 0u;
+    (void)srow;
+  }
+}
+
+template <int LAYOUT>
+__device__ __forceinline__ void tr_b(BBlk<LAYOUT>& b) {
+  if constexpr (LAYOUT == Q_GROUP_K) {
+    transpose_rows4(b.d[0], b.d[1], b.d[2], b.d[3]);
+  } else {
+    transpose_rows4(b.d[0], b.d[2], b.d[4], b.d[6]);
+    transpose_rows4(b.d[1], b.d[3], b.d[5], b.d[7]);
+  }
+}
+
+template <int DT, int LAYOUT>
+__device__ __forceinline__ u32x4 b_op(const BBlk<LAYOUT>& b, int j, int par) {
+  if constexpr (LAYOUT == Q_GROUP_K) {
+    return nibbles_to_h16<DT>(b.d[j]);
+  } else {
+    const int sh = 4 * par;
+    return bytes_to_h16<DT>(b.d[2 * j] >> sh, b.d[2 * j + 1] >> sh);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float sc_of(uint32_t pair, int j) {
+  return H16<DT>::to_f32((j & 1) ? (pair >> 16) : (pair & 0xffffu));
+}
+
+__device__ __forceinline__ u32x4 z4() {
+  u32x4 z;
+  z[0] = z[1] = z[2] = z[3] = 0u;
+  return z;
+}
+
+__device__ __forceinline__ int local_id(int32_t g, int E, int off) {
+  const int64_t e = static_cast<int64_t>(g) - off;
+  return (e >= 0 && e < E) ? static_cast<int>(e) : -1;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// gate/up (or w1) GEMM for few rows per expert, reduction split over 8 waves
+// ---------------------------------------------------------------------------
+template <int DT, int LAYOUT, bool GATED, int NKB>
+__global__ void __launch_bounds__(kDecThreads)
+decode_up_kernel(const DecodeUpParams p) {
+  using T = H16<DT>;
+  constexpr int NSUB = 2;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int c = lane & 15, g = lane >> 4, par = c & 1;
+  const int nt = blockIdx.y;
+
+  __shared__ int s_rows[kDecMaxRows];
+  __shared__ int s_wcnt[kDecWaves];
+  __shared__ f32x4 s_red[kDecWaves][NSUB][64];
+
+  int M = 0, e = 0;
+  if (p.rows_from_ids) {
+    // rows: every route with the same expert as route slot blockIdx.x
+    const int r0 = blockIdx.x;
+    const int32_t gid = p.ids[r0];
+    e = local_id(gid, p.E, p.off);
+    if (e < 0) return;  // invalid route: nothing to do (uniform)
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int base = 0; base < p.R; base += kDecThreads) {
+      const int j = base + tid;
+      const bool m = (j < p.R) && (p.ids[j] == gid);
+      const uint64_t bal = __ballot(m);
+      if (lane == 0) s_wcnt[w] = __popcll(bal);
+      __syncthreads();
+      int before = M;
+      for (int v = 0; v < w; ++v) before += s_wcnt[v];
+      int tot = M;
+      for (int v = 0; v < kDecWaves; ++v) tot += s_wcnt[v];
+      if (m) {
+        const int idx = before + __popcll(bal & below);
+        if (idx < kDecMaxRows) s_rows[idx] = j;
+      }
+      M = tot;
+      __syncthreads();
+    }
+    if (s_rows[0] != r0) return;  // another slot owns this expert (uniform)
+    if (M > kDecMaxRows) M = kDecMaxRows;  // cannot happen for R <= kDecMaxRows
+  } else {
+    // rows: one 16-row tile of the route-prepared list
+    const int tile = blockIdx.x;
+    if (tile * 16 >= p.offsets[p.E]) return;
+    e = p.tile_expert[tile];
+    if (tid < 16) s_rows[tid] = p.sorted[tile * 16 + tid];
+    __syncthreads();
+    M = 0;
+    while (M < 16 && s_rows[M] >= 0) ++M;
+  }
+
+  // this workgroup's weight rows: gated -> 16 gate + 16 up rows, else 32 rows
+  int col[NSUB], wrow[NSUB];
+  bool on[NSUB];
+  if constexpr (GATED) {
+    const int i0 = nt * 16;
+    on[0] = on[1] = i0 < p.n_cols;
+    col[0] = col[1] = i0 + c;
+    wrow[0] = i0 + c;
+    wrow[1] = p.up_rows + i0 + c;
+  } else {
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      on[s] = nt * 32 + 16 * s < p.n_cols;
+      col[s] = nt * 32 + 16 * s + c;
+      wrow[s] = col[s];
+    }
+  }
+  const uint8_t* wq_e = p.wq + static_cast<int64_t>(e) * p.wq_expert_bytes;
+  const uint16_t* ws_e = p.ws + static_cast<int64_t>(e) * p.ws_expert_elems;
+  const uint8_t* brow[NSUB];
+  const uint16_t* srow[NSUB];
+  float scol[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    if constexpr (LAYOUT == Q_GROUP_K) {
+      brow[s] = wq_e + static_cast<int64_t>(wrow[s]) * (p.K >> 1);
+      srow[s] = ws_e + static_cast<int64_t>(wrow[s]) * (p.K >> 5);
+      scol[s] = 0.0f;
+    } else {
+      brow[s] = wq_e + static_cast<int64_t>(wrow[s] >> 1) * p.K;
+      srow[s] = nullptr;
+      scol[s] = on[s] ? T::to_f32(ws_e[wrow[s]]) : 0.0f;
+    }
+  }
+
+  u32x4 bconst;
+  bconst[0] = bconst[1] = bconst[2] = bconst[3] = T::kNegOneHalf2;
+  const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
+  const int kb = w * p.kslice;
+  const int ke = min(p.K, kb + p.kslice);
+
+  for (int m0 = 0; m0 < M; m0 += 16) {
+    // A row of this lane (row c of the 16-row subtile)
+    const uint16_t* arow = nullptr;
+    if (m0 + c < M) arow = p.x + static_cast<int64_t>(s_rows[m0 + c] / p.top_k) * p.lda;
+
+    f32x4 acc[NSUB];
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) acc[s] = fzero;
+
+    for (int kb0 = kb; kb0 < ke; kb0 += NKB * 128) {
+      // issue every weight load of this batch first (the HBM stream)
+      BBlk<LAYOUT> b[NKB][NSUB];
+#pragma unroll
+      for (int i = 0; i < NKB; ++i) {
+        const int k0 = kb0 + 128 * i;
+        const int ng = k0 < ke ? min(4, (ke - k0) >> 5) : 0;
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) ld_b<LAYOUT>(b[i][s], brow[s], srow[s], k0, ng, g, on[s] && ng > 0, p.wq);
+      }
+      // activations (L2-resident rows of x)
+      u32x4 a[NKB][4];
+#pragma unroll
+      for (int i = 0; i < NKB; ++i) {
+        const int k0 = kb0 + 128 * i;
+        const int ng = k0 < ke ? min(4, (ke - k0) >> 5) : 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          a[i][j] = permute_a(load16_if(arow != nullptr && j < ng, arow + k0 + 32 * j + 8 * g, p.x));
+      }
+#pragma unroll
+      for (int i = 0; i < NKB; ++i) {
+        const int k0 = kb0 + 128 * i;
+        if (k0 >= ke) break;
+        const int ng = min(4, (ke - k0) >> 5);
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) tr_b<LAYOUT>(b[i][s]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (j >= ng) break;
+          const f32x4 corr = T::mfma(a[i][j], bconst, fzero);
+#pragma unroll
+          for (int s = 0; s < NSUB; ++s) {
+            if (!on[s]) continue;
+            const float sc = (LAYOUT == Q_GROUP_K) ? sc_of<DT>(b[i][s].s[j >> 1], j) : scol[s];
+            const f32x4 t = T::mfma(a[i][j], b_op<DT, LAYOUT>(b[i][s], j, par), corr);
+            acc[s][0] = fmaf(sc, t[0], acc[s][0]);
+            acc[s][1] = fmaf(sc, t[1], acc[s][1]);
+            acc[s][2] = fmaf(sc, t[2], acc[s][2]);
+            acc[s][3] = fmaf(sc, t[3], acc[s][3]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) s_red[w][s][lane] = acc[s];
+    __syncthreads();
+    if (w == 0) {
+      f32x4 v[NSUB];
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) {
+        v[s] = s_red[0][s][lane];
+        for (int q = 1; q < kDecWaves; ++q) {
+          const f32x4 u = s_red[q][s][lane];
+          v[s][0] += u[0]; v[s][1] += u[1]; v[s][2] += u[2]; v[s][3] += u[3];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 4 * g + i;
+        if (m >= M) continue;
+        const int64_t orow = p.act_by_route ? s_rows[m] : static_cast<int64_t>(blockIdx.x) * 16 + m;
+        uint16_t* o = p.act + orow * p.ldo;
+        if constexpr (GATED) {
+          if (on[0]) o[(col[0] & ~7) | a_pos(col[0] & 7)] =
+              T::from_f32(silu(16.0f * v[0][i]) * (16.0f * v[1][i]));
+        } else {
+#pragma unroll
+          for (int s = 0; s < NSUB; ++s) {
+            if (!on[s]) continue;
+            const float h = fmaxf(16.0f * v[s][i], 0.0f);
+            o[(col[s] & ~7) | a_pos(col[s] & 7)] = T::from_f32(h * h);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// small batch gate/up (T*K <= 64): pre-activations h = x W13^T in FP32 for one
+// 16-row weight subtile of one touched expert; 8 waves split the reduction.
+// ---------------------------------------------------------------------------
+// The rows of the expert come from one ballot over the ids; the workgroup of
+// the first route of an expert does the work, so each touched expert's
+// weights are streamed once.  Gate and up subtiles are separate workgroups
+// (the activation is applied by the down kernel), which gives 2*I/16
+// workgroups per touched expert.
+// Up to 4 rows per pass sit at MFMA rows 0, 4, 8, 12: result row 4q is
+// element 0 of lane row q, so one FMA per MFMA applies the group scale.  The
+// staged rows are read by lanes c % 4 == 0; the other lanes feed zeros.
+// Memory order: ids; then, in flight together, the subtile's scales (staged
+// in LDS), each wave's slice of the x rows (staged in its own LDS region) and
+// all weights of the wave's slice (registers); a wait for the first two, one
+// barrier, a branch-free MFMA section, a fixed-order reduction over slices.
+template <int DT, int LAYOUT, int NKB>
+__global__ void __launch_bounds__(kSmallThreads)
+small_h_kernel(const SmallHParams p) {
+  using T = H16<DT>;
+  constexpr bool GROUP = LAYOUT == Q_GROUP_K;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int c = lane & 15, g = lane >> 4, par = c & 1;
+  const int nt = blockIdx.y;
+  const int r0 = blockIdx.x;
+
+  extern __shared__ uint16_t s_dyn[];  // [16 rows][K/32] scales, then per wave [4][kslice + 8] x
+  __shared__ float s_red[kSmallWaves][64];
+
+  // rows: the routes whose id equals route r0's id (R <= 64: one ballot)
+  const int32_t gid = p.ids[r0];
+  const int e = local_id(gid, p.E, p.off);
+  if (e < 0) return;  // invalid route: nothing to do (uniform)
+  const int32_t my_id = p.ids[lane < p.R ? lane : r0];
+  const uint64_t match = __ballot(lane < p.R && my_id == gid);
+  if (__builtin_ctzll(match) != r0) return;  // an earlier slot owns this expert (uniform)
+  const int M = __popcll(match);
+
+  const int wrow = nt * 16 + c;                   // weight row (output column of h)
+  const uint8_t* wq_e = p.wq + static_cast<int64_t>(e) * p.wq_expert_bytes;
+  const uint16_t* ws_e = p.ws + static_cast<int64_t>(e) * p.ws_expert_elems;
+  const uint32_t boff = GROUP ? static_cast<uint32_t>(wrow) * (p.K >> 1)
+                              : static_cast<uint32_t>(wrow >> 1) * p.K;
+  const int ngr = p.K >> 5;                       // scale groups per weight row
+  uint16_t* s_sc = s_dyn;                         // [16][ngr]
+  const int sc_elems = GROUP ? 16 * ngr : 0;
+  const int xs = p.kslice + 8;                    // staged x row stride (16 B padding)
+  uint16_t* my_x = s_dyn + ((sc_elems + 7) & ~7) + w * kSmallRows * xs;
+  const int kb = w * p.kslice;
+  const int ke = min(p.K, kb + p.kslice);
+  const int nck = (ke > kb) ? (ke - kb) >> 3 : 0; // 8-value chunks per x row in the slice
+  const int q_row = c >> 2;
+  const bool feed_lane = (c & 3) == 0;
+
+  // (1) the subtile's scales: rows nt*16..+15 are one run of 16*ngr values
+  //     = 2*ngr 16-byte chunks, copied flat into s_sc
+  const int sc_chunks = GROUP ? 2 * ngr : 0;
+  const bool sc_in = tid < sc_chunks;
+  const u32x4 scv = load16_at(ws_e, 32u * static_cast<uint32_t>(nt) * ngr + 16u * tid, sc_in);
+  const float scol = GROUP ? 0.0f : T::to_f32(load4_if(true, ws_e + wrow, p.ws) & 0xffffu);
+
+  constexpr int XL = (kSmallRows * NKB * 16 + 63) / 64;  // x chunks per lane (4 rows)
+  uint64_t rest = match;
+  const u32x4 bconst = {T::kNegOneHalf2, T::kNegOneHalf2, T::kNegOneHalf2, T::kNegOneHalf2};
+  const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
+
+  // one pass per 4 rows (more than 4 only if one expert takes more than 4 of
+  // the routes; then the weights are streamed once per pass)
+  for (int m0 = 0; m0 < M; m0 += kSmallRows) {
+    const int nr = min(kSmallRows, M - m0);
+    int rrow[kSmallRows];
+#pragma unroll
+    for (int q = 0; q < kSmallRows; ++q) {
+      rrow[q] = (q < nr) ? __builtin_ctzll(rest) : r0;
+      if (q < nr) rest &= rest - 1;
+    }
+    // (2) this wave's slice of the x rows
+    u32x4 xv[XL];
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      const int idx = lane + 64 * i;
+      const int q = nck ? idx / nck : 0, ck = nck ? idx - q * nck : 0;
+      const bool ok = nck > 0 && q < nr;
+      xv[i] = load16_at(p.x, 2u * (static_cast<uint32_t>(rrow[ok ? q : 0] / p.top_k) * p.lda + kb +
+                                   8 * ck), ok);
+    }
+    // (3) every weight of this wave's slice (kslice <= NKB * 128)
+    u32x4 bw[NKB];
+    u32x4 bw2[GROUP ? 1 : NKB];
+#pragma unroll
+    for (int i = 0; i < NKB; ++i) {
+      const int k0 = kb + 128 * i;
+      const int ng = k0 < ke ? min(4, (ke - k0) >> 5) : 0;
+      if constexpr (GROUP) {
+        bw[i] = load16_at(wq_e, boff + (k0 >> 1) + 16 * g, g < ng);
+      } else {
+        bw[i] = load16_at(wq_e, boff + k0 + 32 * g, g < ng);
+        bw2[i] = load16_at(wq_e, boff + k0 + 32 * g + 16, g < ng);
+      }
+    }
+    // stage scales (first pass) and x: their loads were issued before the weights
+    if (m0 == 0 && sc_in) *reinterpret_cast<u32x4*>(s_sc + 8 * tid) = scv;
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      const int idx = lane + 64 * i;
+      const int q = nck ? idx / nck : 0, ck = nck ? idx - q * nck : 0;
+      if (nck > 0 && q < nr) *reinterpret_cast<u32x4*>(my_x + q * xs + 8 * ck) = permute_a(xv[i]);
+    }
+    __syncthreads();
+    const bool feed = feed_lane && q_row < nr;
+    const uint16_t* arow = my_x + (q_row < nr ? q_row : 0) * xs;
+    const uint16_t* srow = s_sc + c * ngr;
+
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NKB; ++i) {
+      const int k0 = kb + 128 * i;
+      const int ng = k0 < ke ? min(4, (ke - k0) >> 5) : 0;
+      const int xo = k0 < ke ? k0 - kb : 0;      // clamp: never read unstaged LDS
+      uint32_t d[4], d2[4];
+      d[0] = bw[i][0]; d[1] = bw[i][1]; d[2] = bw[i][2]; d[3] = bw[i][3];
+      if constexpr (GROUP) {
+        transpose_rows4(d[0], d[1], d[2], d[3]);
+      } else {
+        d2[0] = bw2[i][0]; d2[1] = bw2[i][1]; d2[2] = bw2[i][2]; d2[3] = bw2[i][3];
+        // 8 dwords per lane: evens and odds transposed separately
+        transpose_rows4(d[0], d[2], d2[0], d2[2]);
+        transpose_rows4(d[1], d[3], d2[1], d2[3]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool gv = j < ng;
+        // only staged values are used: other lanes and groups feed zeros
+        const bool fa = feed && gv;
+        const u32x4 av = *reinterpret_cast<const u32x4*>(arow + (fa ? xo + 32 * j + 8 * g : 0));
+        u32x4 a;
+        a[0] = fa ? av[0] : 0u;
+        a[1] = fa ? av[1] : 0u;
+        a[2] = fa ? av[2] : 0u;
+        a[3] = fa ? av[3] : 0u;
+        float sc;
+        u32x4 bop;
+        if constexpr (GROUP) {
+          sc = T::to_f32(srow[gv ? (k0 >> 5) + j : 0]);
+          bop = nibbles_to_h16<DT>(d[j]);
+        } else {
+          sc = scol;
+          // sub-chunk j = dwords (2j, 2j+1) of the lane's 8
+          const uint32_t lo = (j < 2) ? d[2 * j] : d2[2 * j - 4];
+          const uint32_t hi = (j < 2) ? d[2 * j + 1] : d2[2 * j - 3];
+          bop = bytes_to_h16<DT>(lo >> (4 * par), hi >> (4 * par));
+        }
+        sc = gv ? sc : 0.0f;
+        const f32x4 corr = T::mfma(a, bconst, fzero);
+        const f32x4 t = T::mfma(a, bop, corr);
+        acc = fmaf(sc, t[0], acc);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    s_red[w][lane] = acc;
+    __syncthreads();
+    // wave 0: slices in order; lane row g holds staged row g (element 0)
+    if (w == 0 && g < nr) {
+      float v = s_red[0][lane];
+      for (int q = 1; q < kSmallWaves; ++q) v += s_red[q][lane];
+      p.h[static_cast<int64_t>(rrow[g]) * p.ldh + wrow] = 16.0f * v;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// small batch down GEMM of each route of one token + FP32 combine in top-k
+// order; the activation of the token's routes is formed in the prologue
+// ---------------------------------------------------------------------------
+// Prologue: the FP32 pre-activations of the token's K routes (issued first),
+// then the weights of each wave's first work item; SiLU(gate)*up or ReLU^2
+// is computed once per value, rounded to 16 bits and staged in LDS in A
+// operand order.  Work items are (route k, 256-wide slice of the reduction);
+// each wave computes its items' 32 partial outputs (one MFMA row: a route is
+// a single activation row) into LDS; then 32 lanes add, for k = 0..K-1 in
+// order, w[t,k] * (sum of k's slices in slice order) and cast once.
+template <int DT, int LAYOUT, bool GATED, int AL>
+__global__ void __launch_bounds__(kDecThreads)
+decode_down_kernel(const DecodeDownParams p) {
+  using T = H16<DT>;
+  constexpr int NSUB = 2;
+  constexpr int SL = kDecDownSliceBlocks;  // blocks of 128 per item
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int c = lane & 15, g = lane >> 4, par = c & 1;
+  const int n0 = blockIdx.x * 32;
+  const int t = blockIdx.y;
+  const int nblk = (p.I + 127) / 128;
+  const int nsl = (nblk + SL - 1) / SL;
+  const int items = p.top_k * nsl;
+  const int as = p.I + 8;                  // staged activation row stride
+
+  extern __shared__ uint16_t s_act[];      // [top_k][I + 8], A operand order
+  __shared__ float s_y[kDecMaxItems][32];
+
+  bool on[NSUB];
+  int wrow[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    on[s] = n0 + 16 * s < p.H;
+    wrow[s] = n0 + 16 * s + c;
+  }
+
+  // (1) pre-activations of the token's routes (8 values per chunk)
+  const int ich = p.I >> 3;
+  const int nch = p.top_k * ich;
+  f32x4 hg[AL][2], hu[AL][2];  // AL: activation chunks per thread (>= top_k * I / 8 / 512)
+#pragma unroll
+  for (int i = 0; i < AL; ++i) {
+    const int idx = tid + kDecThreads * i;
+    const int k = idx < nch ? idx / ich : 0, cc = idx < nch ? idx - k * ich : 0;
+    const int r = t * p.top_k + k;
+    const bool ok = idx < nch && local_id(p.ids[r], p.E, p.off) >= 0;
+    const uint32_t off = 4u * (static_cast<uint32_t>(r) * p.ldh + 8 * cc);
+    const u32x4 g0 = load16_at(p.h, off, ok), g1 = load16_at(p.h, off + 16, ok);
+    hg[i][0] = __builtin_bit_cast(f32x4, g0);
+    hg[i][1] = __builtin_bit_cast(f32x4, g1);
+    if constexpr (GATED) {
+      const u32x4 u0 = load16_at(p.h, off + 4u * p.I, ok), u1 = load16_at(p.h, off + 4u * p.I + 16, ok);
+      hu[i][0] = __builtin_bit_cast(f32x4, u0);
+      hu[i][1] = __builtin_bit_cast(f32x4, u1);
+    }
+  }
+
+  // (2) weights of the first item of this wave
+  auto item_ptrs = [&](int it, int& r, int& e, uint32_t& boff0, uint32_t& boff1, const uint8_t*& wq_e,
+                       const uint16_t*& ws_e) {
+    const int k = it / nsl;
+    r = t * p.top_k + k;
+    e = local_id(p.ids[r], p.E, p.off);
+    const int ee = e >= 0 ? e : 0;
+    wq_e = p.wq + static_cast<int64_t>(ee) * p.wq_expert_bytes;
+    ws_e = p.ws + static_cast<int64_t>(ee) * p.ws_expert_elems;
+    boff0 = LAYOUT == Q_GROUP_K ? static_cast<uint32_t>(wrow[0]) * (p.I >> 1)
+                                : static_cast<uint32_t>(wrow[0] >> 1) * p.I;
+    boff1 = LAYOUT == Q_GROUP_K ? static_cast<uint32_t>(wrow[1]) * (p.I >> 1)
+                                : static_cast<uint32_t>(wrow[1] >> 1) * p.I;
+  };
+  auto load_item = [&](int it, BBlk<LAYOUT> (&b)[SL][NSUB], float (&scol)[NSUB], int& e, int& r) {
+    uint32_t bo[NSUB];
+    const uint8_t* wq_e;
+    const uint16_t* ws_e;
+    item_ptrs(it, r, e, bo[0], bo[1], wq_e, ws_e);
+    const int sl = it - (it / nsl) * nsl;
+    const int kb = sl * SL * 128;
+    const int ke = min(p.I, kb + SL * 128);
+#pragma unroll
+    for (int i = 0; i < SL; ++i) {
+      const int k0 = kb + 128 * i;
+      const int ng = k0 < ke ? min(4, (ke - k0) >> 5) : 0;
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) {
+        const bool ok = e >= 0 && on[s] && ng > 0;
+        if constexpr (LAYOUT == Q_GROUP_K) {
+          const u32x4 v = load16_at(wq_e, bo[s] + (k0 >> 1) + 16 * g, ok && g < ng);
+          b[i][s].d[0] = v[0]; b[i][s].d[1] = v[1]; b[i][s].d[2] = v[2]; b[i][s].d[3] = v[3];
+          const uint32_t so = 2u * (static_cast<uint32_t>(wrow[s]) * (p.I >> 5) + (k0 >> 5));
+          b[i][s].s[0] = load4_if(ok, reinterpret_cast<const char*>(ws_e) + so, p.ws);
+          b[i][s].s[1] = load4_if(ok && ng > 2, reinterpret_cast<const char*>(ws_e) + so + 4, p.ws);
+        } else {
+          const u32x4 v0 = load16_at(wq_e, bo[s] + k0 + 32 * g, ok && g < ng);
+          const u32x4 v1 = load16_at(wq_e, bo[s] + k0 + 32 * g + 16, ok && g < ng);
+          b[i][s].d[0] = v0[0]; b[i][s].d[1] = v0[1]; b[i][s].d[2] = v0[2]; b[i][s].d[3] = v0[3];
+          b[i][s].d[4] = v1[0]; b[i][s].d[5] = v1[1]; b[i][s].d[6] = v1[2]; b[i][s].d[7] = v1[3];
+          b[i][s].s[0] = b[i][s].s[1] = 0u;
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s)
+      scol[s] = (LAYOUT == Q_GROUP_K) ? 0.0f
+                : T::to_f32(load4_if(e >= 0 && on[s], ws_e + wrow[s], p.ws) & 0xffffu);
+  };
+
+  BBlk<LAYOUT> b[SL][NSUB];
+  float scol[NSUB];
+  int e_cur = -1, r_cur = 0;
+  if (w < items) load_item(w, b, scol, e_cur, r_cur);
+
+  // (3) activation: computed once per value, 16-bit, A operand order
+#pragma unroll
+  for (int i = 0; i < AL; ++i) {
+    const int idx = tid + kDecThreads * i;
+    if (idx < nch) {
+      const int k = idx / ich, cc = idx - k * ich;
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float hv = hg[i][q >> 2][q & 3];
+        if constexpr (GATED) {
+          v[q] = silu(hv) * hu[i][q >> 2][q & 3];
+        } else {
+          const float hp = fmaxf(hv, 0.0f);
+          v[q] = hp * hp;
+        }
+      }
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = static_cast<uint32_t>(T::from_f32(v[2 * q])) |
+               (static_cast<uint32_t>(T::from_f32(v[2 * q + 1])) << 16);
+      *reinterpret_cast<u32x4*>(s_act + k * as + 8 * cc) = permute_a(o);
+    }
+  }
+  __syncthreads();
+
+  const u32x4 bconst = {T::kNegOneHalf2, T::kNegOneHalf2, T::kNegOneHalf2, T::kNegOneHalf2};
+  const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
+  for (int it = w; it < items; it += kDecWaves) {
+    if (it != w) load_item(it, b, scol, e_cur, r_cur);
+    const int k = it / nsl, sl = it - k * nsl;
+    float y[NSUB] = {0.0f, 0.0f};
+    if (e_cur >= 0) {
+      const uint16_t* arow = s_act + k * as;
+      const int kb = sl * SL * 128;
+      const int ke = min(p.I, kb + SL * 128);
+#pragma unroll
+      for (int i = 0; i < SL; ++i) {
+        const int k0 = kb + 128 * i;
+        const int ng = k0 < ke ? min(4, (ke - k0) >> 5) : 0;
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) tr_b<LAYOUT>(b[i][s]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool gv = j < ng;
+          const bool fa = c == 0 && gv;
+          const u32x4 av = *reinterpret_cast<const u32x4*>(arow + (fa ? k0 + 32 * j + 8 * g : 0));
+          u32x4 a;
+          a[0] = fa ? av[0] : 0u;
+          a[1] = fa ? av[1] : 0u;
+          a[2] = fa ? av[2] : 0u;
+          a[3] = fa ? av[3] : 0u;
+          const f32x4 corr = T::mfma(a, bconst, fzero);
+#pragma unroll
+          for (int s = 0; s < NSUB; ++s) {
+            float sc = (LAYOUT == Q_GROUP_K) ? sc_of<DT>(b[i][s].s[j >> 1], j) : scol[s];
+            sc = (gv && on[s]) ? sc : 0.0f;
+            const f32x4 tt = T::mfma(a, b_op<DT, LAYOUT>(b[i][s], j, par), corr);
+            y[s] = fmaf(sc, tt[0], y[s]);
+          }
+        }
+      }
+    }
+    if (lane < 16) {
+      s_y[it][c] = y[0];
+      s_y[it][16 + c] = y[1];
+    }
+  }
+  __syncthreads();
+  if (tid < 32 && n0 + tid < p.H) {
+    float acc = 0.0f;
+    for (int k = 0; k < p.top_k; ++k) {
+      const int r = t * p.top_k + k;
+      if (local_id(p.ids[r], p.E, p.off) < 0) continue;  // invalid route: nothing
+      float y = s_y[k * nsl][tid];
+      for (int sl = 1; sl < nsl; ++sl) y += s_y[k * nsl + sl][tid];
+      acc += p.wts[r] * (16.0f * y);
+    }
+    p.out[static_cast<int64_t>(t) * p.H + n0 + tid] = T::from_f32(acc);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+
+template <typename F>
+static hipError_t allow_lds(F* kernel, size_t lds) {
+  // dynamic LDS beyond 64 KiB must be opted into per kernel (gfx950 has 160 KiB)
+  if (lds <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+}
+
+// ---------------------------------------------------------------------------
+template <int DT, int LAYOUT, bool GATED>
+static hipError_t launch_dec_up_nkb(const DecodeUpParams& p, int nkb, dim3 grid, hipStream_t st) {
+  switch (nkb) {
+    case 1: hipLaunchKernelGGL((decode_up_kernel<DT, LAYOUT, GATED, 1>), grid, dim3(kDecThreads), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((decode_up_kernel<DT, LAYOUT, GATED, 2>), grid, dim3(kDecThreads), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((decode_up_kernel<DT, LAYOUT, GATED, 4>), grid, dim3(kDecThreads), 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int DT, int LAYOUT>
+static hipError_t launch_dec_up_g(const DecodeUpParams& p, bool gated, int nkb, dim3 grid,
+                                  hipStream_t st) {
+  return gated ? launch_dec_up_nkb<DT, LAYOUT, true>(p, nkb, grid, st)
+               : launch_dec_up_nkb<DT, LAYOUT, false>(p, nkb, grid, st);
+}
+
+hipError_t launch_decode_up(const DecodeUpParams& p, int dtype, int layout, bool gated, int nkb,
+                            int grid_x, hipStream_t stream) {
+  const int n_tiles = gated ? (p.n_cols + 15) / 16 : (p.n_cols + 31) / 32;
+  const dim3 grid(grid_x, n_tiles);
+  if (dtype == DT_BF16)
+    return layout == Q_GROUP_K ? launch_dec_up_g<DT_BF16, Q_GROUP_K>(p, gated, nkb, grid, stream)
+                               : launch_dec_up_g<DT_BF16, Q_PER_CHANNEL>(p, gated, nkb, grid, stream);
+  return layout == Q_GROUP_K ? launch_dec_up_g<DT_FP16, Q_GROUP_K>(p, gated, nkb, grid, stream)
+                             : launch_dec_up_g<DT_FP16, Q_PER_CHANNEL>(p, gated, nkb, grid, stream);
+}
+
+
+template <int DT, int LAYOUT, int NKB>
+static hipError_t launch_small_h_k(const SmallHParams& p, dim3 grid, size_t lds, hipStream_t st) {
+  const hipError_t err = allow_lds(small_h_kernel<DT, LAYOUT, NKB>, lds);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((small_h_kernel<DT, LAYOUT, NKB>), grid, dim3(kSmallThreads), lds, st, p);
+  return hipGetLastError();
+}
+
+template <int DT, int LAYOUT>
+static hipError_t launch_small_h_nkb(const SmallHParams& p, int nkb, dim3 grid, size_t lds,
+                                     hipStream_t st) {
+  // one instantiation per blocks-per-slice count: no wasted loads or registers
+  switch (nkb) {
+    case 1: return launch_small_h_k<DT, LAYOUT, 1>(p, grid, lds, st);
+    case 2: return launch_small_h_k<DT, LAYOUT, 2>(p, grid, lds, st);
+    case 3: return launch_small_h_k<DT, LAYOUT, 3>(p, grid, lds, st);
+    case 4: return launch_small_h_k<DT, LAYOUT, 4>(p, grid, lds, st);
+    case 5: return launch_small_h_k<DT, LAYOUT, 5>(p, grid, lds, st);
+    case 6: return launch_small_h_k<DT, LAYOUT, 6>(p, grid, lds, st);
+    case 7: return launch_small_h_k<DT, LAYOUT, 7>(p, grid, lds, st);
+    case 8: return launch_small_h_k<DT, LAYOUT, 8>(p, grid, lds, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_small_h(const SmallHParams& p, int dtype, int layout, int nkb, int n1,
+                          hipStream_t stream) {
+  const dim3 grid(p.R, n1 / 16);
+  const size_t lds = small_h_lds_bytes(p.K, p.kslice);
+  if (dtype == DT_BF16)
+    return layout == Q_GROUP_K ? launch_small_h_nkb<DT_BF16, Q_GROUP_K>(p, nkb, grid, lds, stream)
+                               : launch_small_h_nkb<DT_BF16, Q_PER_CHANNEL>(p, nkb, grid, lds, stream);
+  return layout == Q_GROUP_K ? launch_small_h_nkb<DT_FP16, Q_GROUP_K>(p, nkb, grid, lds, stream)
+                             : launch_small_h_nkb<DT_FP16, Q_PER_CHANNEL>(p, nkb, grid, lds, stream);
+}
+
+template <int DT, int LAYOUT, bool GATED, int AL>
+static hipError_t launch_dd_k(const DecodeDownParams& p, dim3 grid, size_t lds, hipStream_t st) {
+  const hipError_t err = allow_lds(decode_down_kernel<DT, LAYOUT, GATED, AL>, lds);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((decode_down_kernel<DT, LAYOUT, GATED, AL>), grid, dim3(kDecThreads), lds, st, p);
+  return hipGetLastError();
+}
+
+template <int DT, int LAYOUT, bool GATED>
+static hipError_t launch_dd_al(const DecodeDownParams& p, dim3 grid, size_t lds, hipStream_t st) {
+  const int need = (p.top_k * (p.I / 8) + kDecThreads - 1) / kDecThreads;
+  if (need <= 1) return launch_dd_k<DT, LAYOUT, GATED, 1>(p, grid, lds, st);
+  if (need <= 2) return launch_dd_k<DT, LAYOUT, GATED, 2>(p, grid, lds, st);
+  if (need <= 4) return launch_dd_k<DT, LAYOUT, GATED, 4>(p, grid, lds, st);
+  if (need <= kDecActLoads) return launch_dd_k<DT, LAYOUT, GATED, kDecActLoads>(p, grid, lds, st);
+  return hipErrorInvalidValue;
+}
+
+template <int DT, int LAYOUT>
+static hipError_t launch_dd(const DecodeDownParams& p, bool gated, dim3 grid, size_t lds,
+                            hipStream_t st) {
+  return gated ? launch_dd_al<DT, LAYOUT, true>(p, grid, lds, st)
+               : launch_dd_al<DT, LAYOUT, false>(p, grid, lds, st);
+}
+
+hipError_t launch_decode_down(const DecodeDownParams& p, int dtype, int layout, bool gated, int T,
+                              hipStream_t stream) {
+  const dim3 grid((p.H + 31) / 32, T);
+  const size_t lds = decode_down_lds_bytes(p.top_k, p.I);
+  if (dtype == DT_BF16)
+    return layout == Q_GROUP_K ? launch_dd<DT_BF16, Q_GROUP_K>(p, gated, grid, lds, stream)
+                               : launch_dd<DT_BF16, Q_PER_CHANNEL>(p, gated, grid, lds, stream);
+  return layout == Q_GROUP_K ? launch_dd<DT_FP16, Q_GROUP_K>(p, gated, grid, lds, stream)
+                             : launch_dd<DT_FP16, Q_PER_CHANNEL>(p, gated, grid, lds, stream);
+}
+
+}  // namespace w4moe

@@ -152,6 +152,37 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Loads that never sit inside a lane-divergent branch: a lane whose access
+// is not wanted reads `safe` (any valid address) instead and gets zeros.  A
+// load in a divergent branch makes the compiler wait for it at the branch's
+// end, which would serialize every load of a wave.
+__device__ __forceinline__ u32x4 load16_if(bool ok, const void* p, const void* safe) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(ok ? p : safe);
+  u32x4 r;
+  r[0] = ok ? v[0] : 0u;
+  r[1] = ok ? v[1] : 0u;
+  r[2] = ok ? v[2] : 0u;
+  r[3] = ok ? v[3] : 0u;
+  return r;
+}
+
+// Same with a wave-uniform base and a 32-bit per-lane byte offset (the base
+// lives in scalar registers; an unwanted lane reads offset 0 and gets zeros).
+__device__ __forceinline__ u32x4 load16_at(const void* base, uint32_t off, bool ok) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const char*>(base) + (ok ? off : 0u));
+  u32x4 r;
+  r[0] = ok ? v[0] : 0u;
+  r[1] = ok ? v[1] : 0u;
+  r[2] = ok ? v[2] : 0u;
+  r[3] = ok ? v[3] : 0u;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t load4_if(bool ok, const void* p, const void* safe) {
+  const uint32_t v = *reinterpret_cast<const uint32_t*>(ok ? p : safe);
+  return ok ? v : 0u;
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 }  // namespace w4moe

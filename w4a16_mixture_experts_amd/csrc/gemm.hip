@@ -15,18 +15,10 @@
 //
 // Kernels
 //   grouped_gemm_kernel  one workgroup = one expert tile of block_m padded
-//       route positions x 64 (gated) or 128 output columns x one partition of
-//       the reduction.  UP mode gathers token rows of x and writes the 16-bit
+//       route positions x 64 (gated) or 128 output columns over the whole
+//       reduction.  UP mode gathers token rows of x and writes the 16-bit
 //       activation (SiLU(gate)*up or ReLU^2) in A operand order; DOWN mode
 //       reads those rows and writes 16-bit expert outputs Y.
-//       With split > 1 each partition stores FP32 partial sums; the last
-//       partition to arrive (an agent-scope counter, zeroed by route
-//       preparation) adds the partials in partition order 0..split-1, so the
-//       result does not depend on arrival order.  A partition whose range is
-//       empty stores zeros.
-//   fused_down_kernel    decode path: one wave per (token, 32 columns) runs the
-//       down GEMM of each of the token's routes in top-k order and adds
-//       w * y in FP32 as it goes, so expert outputs never leave registers.
 //   combine_kernel       out[t] = cast16(sum_k w[t,k] * Y[slot[t,k]]) in FP32.
 //
 // Weight streaming: lane (c, g) of a wave reads 16 bytes = one 32-value group
@@ -57,31 +49,19 @@ struct BRaw {
 
 template <int LAYOUT>
 __device__ __forceinline__ void load_b(BRaw<LAYOUT>& b, const uint8_t* brow, const uint16_t* srow,
-                                       int k0, int ng, int g, bool on) {
+                                     int k0, int ng, int g, bool on, const void* safe) {
   if constexpr (LAYOUT == Q_GROUP_K) {
-    if (on && g < ng) {
-      const u32x4 v = load16(brow + (k0 >> 1) + 16 * g);
-      b.d[0] = v[0]; b.d[1] = v[1]; b.d[2] = v[2]; b.d[3] = v[3];
-    } else {
-      b.d[0] = b.d[1] = b.d[2] = b.d[3] = 0u;
-    }
-    if (on) {
-      const uint32_t* sp = reinterpret_cast<const uint32_t*>(srow + (k0 >> 5));
-      b.s[0] = sp[0];
-      b.s[1] = (ng > 2) ? sp[1] : 0u;
-    } else {
-      b.s[0] = b.s[1] = 0u;
-    }
+    const u32x4 v = load16_if(on && g < ng, brow + (k0 >> 1) + 16 * g, safe);
+    b.d[0] = v[0]; b.d[1] = v[1]; b.d[2] = v[2]; b.d[3] = v[3];
+    const uint32_t* sp = reinterpret_cast<const uint32_t*>(srow + (k0 >> 5));
+    b.s[0] = load4_if(on, sp, safe);
+    b.s[1] = load4_if(on && ng > 2, sp + 1, safe);
   } else {
-    if (on && g < ng) {
-      const u32x4 v0 = load16(brow + k0 + 32 * g);
-      const u32x4 v1 = load16(brow + k0 + 32 * g + 16);
-      b.d[0] = v0[0]; b.d[1] = v0[1]; b.d[2] = v0[2]; b.d[3] = v0[3];
-      b.d[4] = v1[0]; b.d[5] = v1[1]; b.d[6] = v1[2]; b.d[7] = v1[3];
-    } else {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) b.d[q] = 0u;
-    }
+    const bool ok = on && g < ng;
+    const u32x4 v0 = load16_if(ok, brow + k0 + 32 * g, safe);
+    const u32x4 v1 = load16_if(ok, brow + k0 + 32 * g + 16, safe);
+    b.d[0] = v0[0]; b.d[1] = v0[1]; b.d[2] = v0[2]; b.d[3] = v0[3];
+    b.d[4] = v1[0]; b.d[5] = v1[1]; b.d[6] = v1[2]; b.d[7] = v1[3];
     b.s[0] = b.s[1] = 0u;
     (void)srow;
   }
@@ -128,8 +108,7 @@ grouped_gemm_kernel(const GemmParams p) {
   const int total = p.offsets[p.E];
   if (mt * p.bm >= total) return;  // whole workgroup: tiles past the padded total
   const int e = p.tile_expert[mt];
-  const int nt = blockIdx.x / p.split;
-  const int sp = blockIdx.x - nt * p.split;
+  const int nt = blockIdx.x;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int c = lane & 15, g = lane >> 4;
 
@@ -198,14 +177,14 @@ grouped_gemm_kernel(const GemmParams p) {
   bconst[0] = bconst[1] = bconst[2] = bconst[3] = T::kNegOneHalf2;
   const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
 
-  const int kb = sp * p.kchunk;
-  const int ke = min(p.K, kb + p.kchunk);
+  const int kb = 0;
+  const int ke = p.K;
 
   BRaw<LAYOUT> bnext[NSUB];
   if (kb < ke) {
     const int ng0 = min(4, (ke - kb) >> 5);
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) load_b<LAYOUT>(bnext[s], brow[s], srow[s], kb, ng0, g, on[s]);
+    for (int s = 0; s < NSUB; ++s) load_b<LAYOUT>(bnext[s], brow[s], srow[s], kb, ng0, g, on[s], p.wq);
   }
 
   for (int k0 = kb; k0 < ke; k0 += 128) {
@@ -218,7 +197,7 @@ grouped_gemm_kernel(const GemmParams p) {
     if (k1 < ke) {
       const int ng1 = min(4, (ke - k1) >> 5);
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s) load_b<LAYOUT>(bnext[s], brow[s], srow[s], k1, ng1, g, on[s]);
+      for (int s = 0; s < NSUB; ++s) load_b<LAYOUT>(bnext[s], brow[s], srow[s], k1, ng1, g, on[s], p.wq);
     }
     // activation fragments of this block
     u32x4 av[MS][4];
@@ -226,12 +205,8 @@ grouped_gemm_kernel(const GemmParams p) {
     for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if (arow[ms] != nullptr && j < ng) {
-          const u32x4 v = load16(arow[ms] + k0 + 32 * j + 8 * g);
-          av[ms][j] = UP ? permute_a(v) : v;
-        } else {
-          av[ms][j] = zero4();
-        }
+        const u32x4 v = load16_if(arow[ms] != nullptr && j < ng, arow[ms] + k0 + 32 * j + 8 * g, p.a);
+        av[ms][j] = UP ? permute_a(v) : v;
       }
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) transpose_b<LAYOUT>(bcur[s]);
@@ -279,48 +254,6 @@ grouped_gemm_kernel(const GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) valid[ms][i] = p.sorted[row_base + 16 * ms + 4 * g + i] >= 0;
 
-  if (p.split > 1) {
-    float* part = p.partial + static_cast<int64_t>(sp) * p.P * p.n_total;
-#pragma unroll
-    for (int ms = 0; ms < MS; ++ms)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (!valid[ms][i]) continue;
-        const int64_t prow = row_base + 16 * ms + 4 * g + i;
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s)
-          if (on[s]) part[prow * p.n_total + wrow[s]] = val[ms][s][i];
-      }
-    __threadfence();
-    __syncthreads();
-    __shared__ int s_last;
-    if (tid == 0) {
-      const int prev = __hip_atomic_fetch_add(p.counters + mt * p.n_tiles + nt, 1,
-                                              __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = (prev == p.split - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    // last partition: add the partials in partition order
-#pragma unroll
-    for (int ms = 0; ms < MS; ++ms)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t prow = row_base + 16 * ms + 4 * g + i;
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) {
-          float v = 0.0f;
-          if (valid[ms][i] && on[s]) {
-            const float* q = p.partial + prow * p.n_total + wrow[s];
-            v = q[0];
-            for (int sp2 = 1; sp2 < p.split; ++sp2) v += q[static_cast<int64_t>(sp2) * p.P * p.n_total];
-          }
-          val[ms][s][i] = v;
-        }
-      }
-  }
-
   // epilogue
 #pragma unroll
   for (int ms = 0; ms < MS; ++ms)
@@ -348,89 +281,6 @@ grouped_gemm_kernel(const GemmParams p) {
         }
       }
     }
-}
-
-// Decode path: the down GEMM of every route of one token, combined in
-// fixed top-k order in FP32 without leaving registers.
-template <int DT, int LAYOUT>
-__global__ void __launch_bounds__(64)
-fused_down_kernel(const FusedDownParams p) {
-  using T = H16<DT>;
-  constexpr int NSUB = 2;
-  const int t = blockIdx.y;
-  const int n0 = blockIdx.x * kFusedCols;
-  const int lane = threadIdx.x, c = lane & 15, g = lane >> 4;
-  const int par = c & 1;
-  bool on[NSUB];
-  int wrow[NSUB];
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    on[s] = n0 + 16 * s < p.H;
-    wrow[s] = n0 + 16 * s + c;
-  }
-  u32x4 bconst;
-  bconst[0] = bconst[1] = bconst[2] = bconst[3] = T::kNegOneHalf2;
-  const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
-  float tot[NSUB] = {0.0f, 0.0f};
-
-  for (int k = 0; k < p.top_k; ++k) {
-    const int r = t * p.top_k + k;
-    const int pos = p.slot[r];
-    if (pos < 0) continue;  // invalid route: contributes nothing
-    const int e = p.ids[r] - p.off;
-    const float wgt = p.wts[r];
-    const uint8_t* wq_e = p.wq + static_cast<int64_t>(e) * p.wq_expert_bytes;
-    const uint16_t* ws_e = p.ws + static_cast<int64_t>(e) * p.ws_expert_elems;
-    const uint8_t* brow[NSUB];
-    const uint16_t* srow[NSUB];
-    float scol[NSUB];
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      if constexpr (LAYOUT == Q_GROUP_K) {
-        brow[s] = wq_e + static_cast<int64_t>(wrow[s]) * (p.I >> 1);
-        srow[s] = ws_e + static_cast<int64_t>(wrow[s]) * (p.I >> 5);
-        scol[s] = 0.0f;
-      } else {
-        brow[s] = wq_e + static_cast<int64_t>(wrow[s] >> 1) * p.I;
-        srow[s] = nullptr;
-        scol[s] = on[s] ? T::to_f32(ws_e[wrow[s]]) : 0.0f;
-      }
-    }
-    const uint16_t* arow = (c == 0) ? p.act + static_cast<int64_t>(pos) * p.I : nullptr;
-    float y[NSUB] = {0.0f, 0.0f};
-    for (int k0 = 0; k0 < p.I; k0 += 128) {
-      const int ng = min(4, (p.I - k0) >> 5);
-      BRaw<LAYOUT> b[NSUB];
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) load_b<LAYOUT>(b[s], brow[s], srow[s], k0, ng, g, on[s]);
-      u32x4 av[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        av[j] = (arow != nullptr && j < ng) ? load16(arow + k0 + 32 * j + 8 * g) : zero4();
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) transpose_b<LAYOUT>(b[s]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (j >= ng) break;
-        const f32x4 corr = T::mfma(av[j], bconst, fzero);
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) {
-          if (!on[s]) continue;
-          const float sc = (LAYOUT == Q_GROUP_K) ? scale_of<DT>(b[s].s[j >> 1], j) : scol[s];
-          const f32x4 tt = T::mfma(av[j], b_operand<DT, LAYOUT>(b[s], j, par), corr);
-          y[s] = fmaf(sc, tt[0], y[s]);
-        }
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) tot[s] += wgt * (16.0f * y[s]);
-  }
-  if (g == 0) {
-    uint16_t* orow = p.out + static_cast<int64_t>(t) * p.H;
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s)
-      if (on[s]) orow[wrow[s]] = T::from_f32(tot[s]);
-  }
 }
 
 template <int DT>
@@ -508,30 +358,13 @@ static hipError_t launch_gg_mode(const GemmParams& p, int ms, int mode, dim3 gri
 
 hipError_t launch_grouped_gemm(const GemmParams& p, int dtype, int layout, int ms, int mode,
                                int max_tiles, hipStream_t stream) {
-  const dim3 grid(p.n_tiles * p.split, max_tiles);
+  const dim3 grid(p.n_tiles, max_tiles);
   if (dtype == DT_BF16) {
     return layout == Q_GROUP_K ? launch_gg_mode<DT_BF16, Q_GROUP_K>(p, ms, mode, grid, stream)
                                : launch_gg_mode<DT_BF16, Q_PER_CHANNEL>(p, ms, mode, grid, stream);
   }
   return layout == Q_GROUP_K ? launch_gg_mode<DT_FP16, Q_GROUP_K>(p, ms, mode, grid, stream)
                              : launch_gg_mode<DT_FP16, Q_PER_CHANNEL>(p, ms, mode, grid, stream);
-}
-
-hipError_t launch_fused_down(const FusedDownParams& p, int dtype, int layout, int T,
-                             hipStream_t stream) {
-  const dim3 grid((p.H + kFusedCols - 1) / kFusedCols, T);
-  if (dtype == DT_BF16) {
-    if (layout == Q_GROUP_K)
-      hipLaunchKernelGGL((fused_down_kernel<DT_BF16, Q_GROUP_K>), grid, dim3(64), 0, stream, p);
-    else
-      hipLaunchKernelGGL((fused_down_kernel<DT_BF16, Q_PER_CHANNEL>), grid, dim3(64), 0, stream, p);
-  } else {
-    if (layout == Q_GROUP_K)
-      hipLaunchKernelGGL((fused_down_kernel<DT_FP16, Q_GROUP_K>), grid, dim3(64), 0, stream, p);
-    else
-      hipLaunchKernelGGL((fused_down_kernel<DT_FP16, Q_PER_CHANNEL>), grid, dim3(64), 0, stream, p);
-  }
-  return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineParams& p, int dtype, int T, hipStream_t stream) {

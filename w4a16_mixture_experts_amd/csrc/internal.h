@@ -13,7 +13,6 @@ enum : int { MODE_UP_GATED = 0, MODE_UP_RELU2 = 1, MODE_DOWN = 2 };
 //   otherwise:     32 columns per wave (two subtiles)
 constexpr int kWgColsGated = 64;
 constexpr int kWgColsPlain = 128;
-constexpr int kFusedCols = 32;  // per-token down kernel: one wave, two subtiles
 constexpr int kCombineCols = 2048;
 
 struct GemmParams {
@@ -32,30 +31,84 @@ struct GemmParams {
   const int32_t* offsets;     // [E+1]; offsets[E] = padded total
   int E;
   int bm;
-  int split;
-  int kchunk;
-  float* partial;             // [split][P][n_total]
-  int32_t* counters;          // [max tiles][n_tiles]
-  int64_t P;
-  int n_total;                // partial row length (N1)
   uint16_t* out;              // UP: act [P][ldo]; DOWN: Y [P][ldo]
   int ldo;
   int n_tiles;
 };
 
-struct FusedDownParams {
-  const uint16_t* act;        // [P][I] (A operand order)
+// small-batch path
+constexpr int kDecMaxRows = 256;          // routes the row scan handles (T*K)
+constexpr int kDecMaxItems = 256;         // (route, slice) items per token
+constexpr int kDecDownSliceBlocks = 2;    // 128-blocks of the reduction per item
+// small-batch gate/up kernel (pre-activations h in FP32)
+constexpr int kSmallMaxRoutes = 64;       // T*K: the row search is one wave's ballot
+constexpr int kSmallWaves = 8;            // reduction slices
+constexpr int kSmallThreads = kSmallWaves * 64;
+constexpr int kSmallRows = 4;             // token rows per pass (MFMA rows 0, 4, 8, 12)
+constexpr int kSmallMaxSlice = 1024;      // reduction per slice: hidden <= 8 * 1024
+static_assert(2 * (8 * kSmallMaxSlice / 32) <= kSmallThreads,
+              "one 16-byte scale chunk per thread covers a 16-row subtile");
+inline size_t small_h_lds_bytes(int K, int kslice) {
+  const size_t sc = ((16 * static_cast<size_t>(K / 32)) + 7) & ~size_t(7);
+  return sizeof(uint16_t) * (sc + static_cast<size_t>(kSmallWaves) * kSmallRows * (kslice + 8));
+}
+
+struct SmallHParams {
+  const uint16_t* x;          // [T][lda]
+  int lda;
+  const int32_t* ids;         // [R] global ids
+  int R, top_k, E, off;
+  const uint8_t* wq;          // w13 packed, expert 0
+  const uint16_t* ws;         // w13 scales, expert 0
+  int64_t wq_expert_bytes;
+  int64_t ws_expert_elems;
+  int K;                      // reduction length (H)
+  int kslice;                 // per-wave slice of K, multiple of 128
+  float* h;                   // [R][ldh] pre-activations (route-indexed)
+  int ldh;                    // N1
+};
+
+struct DecodeUpParams {
+  const uint16_t* x;          // [T][lda]
+  int lda;
+  const int32_t* ids;         // [R] global ids (rows_from_ids)
+  int R, top_k, E, off;
+  int rows_from_ids;          // 1: rows = routes of one expert found in ids
+  const int32_t* sorted;      // rows_from_ids == 0: 16-row tiles of the route list
+  const int32_t* tile_expert;
+  const int32_t* offsets;
+  const uint8_t* wq;
+  const uint16_t* ws;
+  int64_t wq_expert_bytes;
+  int64_t ws_expert_elems;
+  int K;                      // reduction length (H)
+  int kslice;                 // per-wave slice of K, multiple of 128
+  int n_cols;                 // I
+  int up_rows;                // gated: I
+  uint16_t* act;              // activation rows (A operand order)
+  int ldo;
+  int act_by_route;           // 1: row = route index, 0: row = tile position
+};
+
+struct DecodeDownParams {
+  const float* h;             // [R][ldh] FP32 pre-activations, route-indexed
+  int ldh;                    // N1
   const uint8_t* wq;
   const uint16_t* ws;
   int64_t wq_expert_bytes;
   int64_t ws_expert_elems;
   const int32_t* ids;         // [T][K]
   const float* wts;           // [T][K]
-  const int32_t* slot;        // [T*K]
   int top_k, E, off;
   int I, H;
   uint16_t* out;              // [T][H]
 };
+
+constexpr int kDecThreadsAll = 512;       // threads of the small-batch down kernel
+constexpr int kDecActLoads = 8;           // activation chunks per thread: top_k * I <= 8 * 512 * 8
+inline size_t decode_down_lds_bytes(int top_k, int I) {
+  return sizeof(uint16_t) * static_cast<size_t>(top_k) * (I + 8);
+}
 
 struct CombineParams {
   const uint16_t* y;          // [P][H]
@@ -73,8 +126,14 @@ hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, 
 hipError_t launch_grouped_gemm(const GemmParams& p, int dtype, int layout, int ms, int mode,
                                int max_tiles, hipStream_t stream);
 
-hipError_t launch_fused_down(const FusedDownParams& p, int dtype, int layout, int T,
-                             hipStream_t stream);
+hipError_t launch_decode_up(const DecodeUpParams& p, int dtype, int layout, bool gated, int nkb,
+                            int grid_x, hipStream_t stream);
+
+hipError_t launch_small_h(const SmallHParams& p, int dtype, int layout, int nkb, int n1,
+                          hipStream_t stream);
+
+hipError_t launch_decode_down(const DecodeDownParams& p, int dtype, int layout, bool gated, int T,
+                              hipStream_t stream);
 
 hipError_t launch_combine(const CombineParams& p, int dtype, int T, hipStream_t stream);
 

@@ -32,6 +32,7 @@ namespace w4moe {
 constexpr int kRpThreads = 1024;
 constexpr int kRpWaves = kRpThreads / 64;
 constexpr int kRpMaxExperts = 1024;
+constexpr int kRpRound = 16;  // 64-route chunks whose id loads are in flight together
 
 __device__ __forceinline__ int local_expert(int32_t g, int E, int off) {
   const int64_t e = static_cast<int64_t>(g) - off;
@@ -59,23 +60,35 @@ route_prep_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
 
-  // pass 1: per-wave histogram and rank of each route within its wave's slab
-  for (int base = r_beg; base < r_end; base += 64) {
-    const int r = base + lane;
-    const int e = (r < r_end) ? local_expert(ids[r], E, off) : -1;
-    uint64_t match = __ballot(e >= 0);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t m = __ballot(bit);
-      match &= bit ? m : ~m;
+  // pass 1: per-wave histogram and rank of each route within its wave's slab.
+  // The slab is walked in rounds of kRpRound chunks of 64 routes; every id
+  // load of a round is issued before the first is used.
+  for (int rb = r_beg; rb < r_end; rb += 64 * kRpRound) {
+    int ev[kRpRound];
+#pragma unroll
+    for (int q = 0; q < kRpRound; ++q) {
+      const int r = rb + 64 * q + lane;
+      ev[q] = (r < r_end) ? local_expert(ids[r], E, off) : -1;
     }
-    if (e >= 0) {
-      const int rank = __popcll(match & below);
-      const int before = hist[w][e];
-      if (rank == 0) hist[w][e] = before + __popcll(match);
-      slot[r] = before + rank;  // temporary: rank within the slab
-    } else if (r < r_end) {
-      slot[r] = -1;
+#pragma unroll
+    for (int q = 0; q < kRpRound; ++q) {
+      if (rb + 64 * q >= r_end) break;
+      const int r = rb + 64 * q + lane;
+      const int e = ev[q];
+      uint64_t match = __ballot(e >= 0);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        match &= bit ? m : ~m;
+      }
+      if (e >= 0) {
+        const int rank = __popcll(match & below);
+        const int before = hist[w][e];
+        if (rank == 0) hist[w][e] = before + __popcll(match);
+        slot[r] = before + rank;  // temporary: rank within the slab
+      } else if (r < r_end) {
+        slot[r] = -1;
+      }
     }
   }
   __syncthreads();
@@ -124,14 +137,21 @@ route_prep_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm
   __syncthreads();
 
   // pass 2: scatter (each thread revisits exactly the routes it ranked)
-  for (int base = r_beg; base < r_end; base += 64) {
-    const int r = base + lane;
-    if (r < r_end) {
-      const int e = local_expert(ids[r], E, off);
-      if (e >= 0) {
-        const int p = s_off[e] + hist[w][e] + slot[r];
-        sorted[p] = r;
-        slot[r] = p;
+  for (int rb = r_beg; rb < r_end; rb += 64 * kRpRound) {
+    int ev[kRpRound], rk[kRpRound];
+#pragma unroll
+    for (int q = 0; q < kRpRound; ++q) {
+      const int r = rb + 64 * q + lane;
+      ev[q] = (r < r_end) ? local_expert(ids[r], E, off) : -1;
+      rk[q] = (ev[q] >= 0) ? slot[r] : 0;
+    }
+#pragma unroll
+    for (int q = 0; q < kRpRound; ++q) {
+      const int r = rb + 64 * q + lane;
+      if (ev[q] >= 0) {
+        const int pos = s_off[ev[q]] + hist[w][ev[q]] + rk[q];
+        sorted[pos] = r;
+        slot[r] = pos;
       }
     }
   }
