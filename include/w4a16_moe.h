@@ -75,7 +75,8 @@ typedef enum { W4A16_Q_GROUP_K = 0, W4A16_Q_PER_CHANNEL = 1 } w4a16_qlayout_t;
  *     PER_CHANNEL:  w13_packed u8 [E][N1/2][H],   w13_scales [E][N1]
  *                   w2_packed  u8 [E][H/2][I],    w2_scales  [E][H]
  *   Supported: H and I multiples of 64, 1 <= E <= 1024, 1 <= top_k <= 32,
- *   group_size 32 for GROUP_K.
+ *   group_size 32 for GROUP_K, x below 2^31 bytes, one expert's w13 below
+ *   2^30 bytes.
  *   force_* fields select a variant for testing; 0 means "choose from the
  *   route count".  Every variant computes the same function. */
 typedef struct {
@@ -91,8 +92,9 @@ typedef struct {
   int32_t qlayout;            /* w4a16_qlayout_t                                  */
   int32_t force_path;         /* 0, 1 = grouped (route preparation, expert tiles,
                                  down GEMM, combine kernel), 2 = small batch (no
-                                 route preparation; needs T*K <= 256)            */
-  int32_t force_block_m;      /* grouped path: 0 or 16/32/64 rows per expert tile */
+                                 route preparation; needs T*K <= 64)             */
+  int32_t force_block_m;      /* grouped path: 0 (= 64) or 16/32/64 rows per
+                                 expert tile                                     */
 } w4a16_moe_desc_t;
 
 /* Variant the library runs for a descriptor (for tests and reports). */

@@ -136,6 +136,18 @@ def test_plans_by_route_count():
     assert p3.workspace_bytes == B.workspace_size(d)
 
 
+def test_buffer_offset_limits():
+    # x at 2^31 bytes or more: 32-bit buffer offsets cannot address it
+    d = B.make_desc(num_tokens=65536 // 2, hidden=32768, intermediate=256,
+                    num_local_experts=8, top_k=1)
+    with pytest.raises(B.W4A16Error) as ei:
+        B.workspace_size(d)
+    assert ei.value.status == 2 and "x:" in str(ei.value)
+    # one token fewer fits
+    d.num_tokens = 65536 // 2 - 1
+    assert B.workspace_size(d) > 0
+
+
 def test_small_batch_path_limits():
     # more than 64 routes (one wave's ballot) cannot take the small-batch path
     d = B.make_desc(num_tokens=9, hidden=256, intermediate=384, num_local_experts=8, top_k=8,

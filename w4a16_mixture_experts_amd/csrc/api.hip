@@ -12,7 +12,6 @@
 #include <stdio.h>
 
 #include <algorithm>
-#include <cmath>
 #include <string>
 
 #include "../../include/w4a16_moe.h"
@@ -87,8 +86,9 @@ w4a16_status_t check_desc(const w4a16_moe_desc_t* d) {
 //     finds each touched expert's rows in the ids and splits the reduction
 //     over 8 waves; the down kernel combines per token.
 //   path 1 (grouped): route preparation into block_m-row expert tiles, the
-//     gate/up GEMM per tile (block_m 16: the 8-wave split-reduction kernel),
-//     the grouped down GEMM and the FP32 combine.
+//     gate/up GEMM per tile, the grouped down GEMM and the FP32 combine.
+//     block_m 64 (default): LDS-staged tiles that skip empty 16-row subtiles;
+//     16: the 8-wave split-reduction kernel; 32: register-fed tiles.
 Plan make_plan(const w4a16_moe_desc_t* d) {
   Plan pl;
   const int E = d->num_local_experts, H = d->hidden, I = d->intermediate, K = d->top_k;
@@ -115,12 +115,9 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
   pl.nkb = per_wave;  // small-batch kernel: exact; 16-row tile kernel: rounded to 1/2/4
   pl.nkb_tile = per_wave <= 1 ? 1 : (per_wave <= 2 ? 2 : 4);
 
-  // expected routes per touched expert under uniform routing
-  const double R = static_cast<double>(pl.R);
-  const double D = std::max(1.0, E * (1.0 - std::pow(1.0 - 1.0 / E, R)));
-  const double per_expert = R / D;
-  if (d->force_block_m) pl.bm = d->force_block_m;
-  else pl.bm = per_expert <= 16 ? 16 : (per_expert <= 32 ? 32 : 64);
+  // 64-row tiles skip their empty 16-row subtiles, so they are the default at
+  // every route count; 16 and 32 remain selectable
+  pl.bm = d->force_block_m ? d->force_block_m : w4moe::kTileRows;
   pl.ms = pl.bm / 16;
 
   const int64_t touched = std::min<int64_t>(E, pl.R);
@@ -158,6 +155,12 @@ w4a16_status_t check_plan(const w4a16_moe_desc_t* d, const Plan& pl) {
                 (long long)pl.MT);
   if (d->num_tokens > 65535)
     return fail(W4A16_ERR_UNSUPPORTED, "x: num_tokens=%d exceeds 65535", d->num_tokens);
+  // 32-bit buffer offsets: x and one expert's packed weights or scales
+  if (static_cast<int64_t>(d->num_tokens) * d->hidden * 2 >= (int64_t(1) << 31))
+    return fail(W4A16_ERR_UNSUPPORTED, "x: %lld bytes (2^31 or more)",
+                (long long)d->num_tokens * d->hidden * 2);
+  if (static_cast<int64_t>(pl.N1) * d->hidden >= (int64_t(1) << 31))
+    return fail(W4A16_ERR_UNSUPPORTED, "w13_packed: one expert's weights reach 2^30 bytes");
   if (pl.path == 2 && pl.R > w4moe::kSmallMaxRoutes)
     return fail(W4A16_ERR_UNSUPPORTED, "topk_ids: %lld routes exceed the small-batch path's %d",
                 (long long)pl.R, w4moe::kSmallMaxRoutes);
@@ -383,6 +386,7 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
     w4moe::GemmParams up{};
     up.a = static_cast<const uint16_t*>(x);
     up.lda = H;
+    up.a_bytes = static_cast<uint32_t>(sizeof(uint16_t) * desc->num_tokens * H);
     up.sorted = sorted;
     up.top_k = K;
     up.wq = w13_packed;
@@ -399,8 +403,11 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
     up.out = act;
     up.ldo = I;
     up.n_tiles = pl.n_tiles_up;
-    st = hip_status(w4moe::launch_grouped_gemm(up, desc->dtype, desc->qlayout, pl.ms, pl.mode_up,
-                                               static_cast<int>(pl.MT), stream),
+    st = hip_status(pl.bm == w4moe::kTileRows
+                        ? w4moe::launch_tile_gemm(up, desc->dtype, desc->qlayout, pl.mode_up,
+                                                  static_cast<int>(pl.MT), stream)
+                        : w4moe::launch_grouped_gemm(up, desc->dtype, desc->qlayout, pl.ms,
+                                                     pl.mode_up, static_cast<int>(pl.MT), stream),
                     "gate/up GEMM launch");
   }
   if (st == W4A16_OK) st = hip_status(evs.mark(3), "stage event");
@@ -428,8 +435,12 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
   dn.n_tiles = pl.n_tiles_down;
   st = hip_status(evs.mark(4), "stage event");
   if (st != W4A16_OK) return st;
-  st = hip_status(w4moe::launch_grouped_gemm(dn, desc->dtype, desc->qlayout, pl.ms,
-                                             w4moe::MODE_DOWN, static_cast<int>(pl.MT), stream),
+  st = hip_status(pl.bm == w4moe::kTileRows
+                      ? w4moe::launch_tile_gemm(dn, desc->dtype, desc->qlayout, w4moe::MODE_DOWN,
+                                                static_cast<int>(pl.MT), stream)
+                      : w4moe::launch_grouped_gemm(dn, desc->dtype, desc->qlayout, pl.ms,
+                                                   w4moe::MODE_DOWN, static_cast<int>(pl.MT),
+                                                   stream),
                   "down GEMM launch");
   if (st == W4A16_OK) st = hip_status(evs.mark(5), "stage event");
   if (st != W4A16_OK) return st;

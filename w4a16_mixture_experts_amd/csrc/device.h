@@ -69,6 +69,12 @@ struct H16<DT_BF16> {
     __bf16 b = static_cast<__bf16>(f);  // round to nearest even
     return __builtin_bit_cast(uint16_t, b);
   }
+  // c + h0 + h1 for the two values packed in one dword
+  static __device__ __forceinline__ float dot2_ones(uint32_t pair, float c) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
+                                           __builtin_bit_cast(bf16x2, 0x3F803F80u), c, false);
+  }
   static __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -87,6 +93,11 @@ struct H16<DT_FP16> {
   static __device__ __forceinline__ uint16_t from_f32(float f) {
     _Float16 h = static_cast<_Float16>(f);  // round to nearest even
     return __builtin_bit_cast(uint16_t, h);
+  }
+  static __device__ __forceinline__ float dot2_ones(uint32_t pair, float c) {
+    typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair),
+                                  __builtin_bit_cast(f16x2, 0x3C003C00u), c, false);
   }
   static __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
@@ -176,6 +187,22 @@ __device__ __forceinline__ u32x4 load16_at(const void* base, uint32_t off, bool 
   r[2] = ok ? v[2] : 0u;
   r[3] = ok ? v[3] : 0u;
   return r;
+}
+
+// Raw buffer accesses.  A resource covers [base, base + bytes) with bytes
+// below 2^31; a load at an offset at or past the end returns zeros without a
+// memory access, so a masked lane simply uses kOob and needs no select after
+// the load (a select right behind a load forces an early wait on it).
+constexpr uint32_t kOob = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off, bool ok) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ok ? off : kOob, 0, 0));
+}
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off, bool ok) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, ok ? off : kOob, 0, 0);
 }
 
 __device__ __forceinline__ uint32_t load4_if(bool ok, const void* p, const void* safe) {

@@ -14,10 +14,12 @@ enum : int { MODE_UP_GATED = 0, MODE_UP_RELU2 = 1, MODE_DOWN = 2 };
 constexpr int kWgColsGated = 64;
 constexpr int kWgColsPlain = 128;
 constexpr int kCombineCols = 2048;
+constexpr int kTileRows = 64;  // route positions of one LDS-staged expert tile
 
 struct GemmParams {
   const uint16_t* a;          // UP: x [T][lda]; DOWN: act [P][lda] (A operand order)
   int lda;
+  uint32_t a_bytes;           // UP: bytes of x (below 2^31)
   const int32_t* sorted;      // [P] route index or -1 (padding)
   int top_k;
   const uint8_t* wq;          // packed weights, expert 0
@@ -125,6 +127,10 @@ hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, 
 
 hipError_t launch_grouped_gemm(const GemmParams& p, int dtype, int layout, int ms, int mode,
                                int max_tiles, hipStream_t stream);
+
+// 64-row expert tiles (route positions), LDS-staged activations
+hipError_t launch_tile_gemm(const GemmParams& p, int dtype, int layout, int mode, int max_tiles,
+                            hipStream_t stream);
 
 hipError_t launch_decode_up(const DecodeUpParams& p, int dtype, int layout, bool gated, int nkb,
                             int grid_x, hipStream_t stream);
