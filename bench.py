@@ -3,20 +3,25 @@
 
 One step = one forward at every token count of the sweep (route preparation,
 gather, gate/up GEMM, activation, down GEMM, FP32 combine: the whole path) on
-seeded synthetic inputs already resident in HBM.  Each forward is captured in
-a HIP graph and replayed; before every timed replay a read-only pass over a
-512 MiB buffer evicts the L2 caches and the 256 MB Infinity Cache, so weights
-stream from HBM ("cold").  The evicting pass only reads, so no dirty lines are
-left to be written back while the timed forward runs.
-Warm numbers (10 back-to-back replays, the caches holding whatever fits) are
-reported beside them as context.
+seeded synthetic inputs already resident in HBM.  Inside a step, for every
+token count:
+  1. a read-only pass over a 512 MiB buffer evicts the L2 caches and the
+     256 MB Infinity Cache (it only reads, so no dirty lines are left to be
+     written back while the forward runs);
+  2. the forward, captured once in a HIP graph, is replayed between two HIP
+     events: the cold latency (`value` is built from these);
+  3. the cache is evicted again and the forward runs once more as direct
+     calls, with HIP events that the library records around each stage on the
+     stream it launches on: per-stage kernel durations in the same timed
+     region (the `roofline` kernel's average launch duration).
+Warm numbers (10 back-to-back replays, caches holding whatever fits) are
+reported afterwards as context.
 
 Prints ONE JSON line.  `value` is the geometric mean over the token sweep of
-the cold per-forward latency in microseconds (lower is better).  The
-`roofline` object covers the dominant kernel (the stage with the largest
-share of the sweep's time), timed with HIP events recorded by the library
-around each stage on the stream it launches on; `cpu_baseline` times the CPU
-oracle on a bounded sample of the same workload.
+the mean cold per-forward latency in microseconds (lower is better).
+`roofline` covers the dominant kernel (the one with the largest share of the
+sweep's time); `cpu_baseline` times the CPU oracle on a bounded sample of the
+same workload.
 """
 from __future__ import annotations
 
@@ -71,6 +76,55 @@ def workload_bytes_flops(wl, ids, T):
     return stage, total, flops["gate_up_gemm"] + flops["down_gemm"], flops, D, Rv
 
 
+KERNEL_PREFIX = "w4moe::"
+
+
+def kernel_name(wl, plan, stage):
+    """Kernel a stage launches, spelled as the profiler prints it (w/o arguments)."""
+    import torch
+
+    dt = 1 if wl.dtype == torch.float16 else 0
+    lay = 1 if wl.per_channel else 0
+    if plan.path == 2:
+        return {"gate_up_gemm": f"small_h_kernel<{dt}, {lay}, ...>",
+                "down_gemm": f"decode_down_kernel<{dt}, {lay}, ...>"}[stage]
+    if stage == "route_prep":
+        return "route_prep_kernel"
+    if stage == "combine":
+        return f"combine_kernel<{dt}>"
+    if plan.block_m != 64:
+        return f"block_m {plan.block_m} {stage}"
+    mode = 2 if stage == "down_gemm" else (0 if wl.gated else 1)
+    return f"tile_gemm_kernel<{dt}, {lay}, {mode}>"
+
+
+def measured_traffic(kname, tokens):
+    """HBM bytes per launch from the committed counter summary, if it covers this
+    kernel as it is now built (same kernel source hash, same token sweep)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get("kernels", {}).get(kname)
+    if ent is None or ent.get("tokens") != tokens:
+        return None
+    src = os.path.join(ROOT, "w4a16_mixture_experts_amd", "csrc", ent["source"])
+    if not os.path.exists(src) or source_hash(src) != ent.get("source_sha256"):
+        return None
+    return ent["hbm_bytes_per_launch"]
+
+
+def source_hash(path):
+    import hashlib
+
+    h = hashlib.sha256()
+    for p in (path, os.path.join(os.path.dirname(path), "device.h")):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def cpu_baseline(wl, Wg, budget_s):
     """The CPU oracle (as it stands) on a bounded sample of the same sweep."""
     import numpy as np
@@ -113,6 +167,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-graph", action="store_true", help="time eager calls instead")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run a plain elementwise copy (negation) of this many MiB "
+                         "three times: the known-size kernel that scales HBM counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -131,6 +188,16 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     sweep = [int(t) for t in args.tokens.split(",")] if args.tokens else list(wl.tokens)
     dtype_name = "fp16" if wl.dtype == torch.float16 else "bf16"
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 x {args.copy_calibration_mib} MiB read + written")
+        del src, dst
 
     log(f"[bench] generating {wl.name} weights on the GPU")
     Wg = synth.make_weights(wl, device=dev)
@@ -181,6 +248,7 @@ def main():
 
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
 
     def step(record):
         for c in cases:
@@ -188,9 +256,16 @@ def main():
             ev0.record()
             replay(c)
             ev1.record()
-            ev1.synchronize()
-            if record:
-                c["cold"].append(ev0.elapsed_time(ev1) * 1e3)
+            flush()
+            c["fwd"](stage_events=evs)
+            evs[7 if c["plan"].path == 1 else 5].synchronize()
+            if not record:
+                continue
+            c["cold"].append(ev0.elapsed_time(ev1) * 1e3)
+            for si, name in enumerate(STAGES):
+                if name in ("route_prep", "combine") and c["plan"].path == 2:
+                    continue
+                c["stages"][name].append(evs[2 * si].elapsed_time(evs[2 * si + 1]) * 1e3)
 
     for _ in range(args.warmup):
         step(False)
@@ -212,30 +287,18 @@ def main():
             ev1.synchronize()
             c["warm"].append(ev0.elapsed_time(ev1) * 1e3 / 10)
 
-    # per-stage durations (eager calls, library-recorded events, cold caches)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
-    for c in cases:
-        for _ in range(max(5, args.steps // 2)):
-            flush()
-            c["fwd"](stage_events=evs)
-            torch.cuda.synchronize()
-            for si, name in enumerate(STAGES):
-                a, b = evs[2 * si], evs[2 * si + 1]
-                if name in ("route_prep", "combine") and c["plan"].path == 2:
-                    continue
-                c["stages"][name].append(a.elapsed_time(b) * 1e3)
-
-    lat_cold = {c["T"]: statistics.median(c["cold"]) for c in cases}
+    lat_cold = {c["T"]: statistics.fmean(c["cold"]) for c in cases}
     lat_warm = {c["T"]: statistics.median(c["warm"]) for c in cases}
     geo = math.exp(sum(math.log(v) for v in lat_cold.values()) / len(lat_cold))
     table = {}
-    best = None
+    per_kernel = {}   # kernel -> list of (duration us, algorithmic bytes, flops) per launch
     for c in cases:
         T = c["T"]
-        st = {k: statistics.median(v) for k, v in c["stages"].items() if v}
+        st = {k: statistics.fmean(v) for k, v in c["stages"].items() if v}
         down_key = "down_gemm_fused" if c["plan"].path == 2 else "down_gemm"
         row = {
             "latency_us_cold": round(lat_cold[T], 3),
+            "latency_us_cold_median": round(statistics.median(c["cold"]), 3),
             "latency_us_warm": round(lat_warm[T], 3),
             "hbm_gbps_cold": round(c["bytes"] / lat_cold[T] / 1e3, 1),
             "hbm_frac_cold": round(c["bytes"] / lat_cold[T] / 1e3 / HBM_PEAK_GBS, 4),
@@ -247,22 +310,30 @@ def main():
             "plan": {"path": "small-batch" if c["plan"].path == 2 else "grouped",
                      "block_m": c["plan"].block_m, "k_slice": c["plan"].k_slice},
             "stage_us": {k: round(v, 3) for k, v in st.items()},
+            "stage_kernel": {k: kernel_name(wl, c["plan"], k) for k in st},
         }
         for k, v in st.items():
             key = down_key if k == "down_gemm" else k
             if key in c["stage_bytes"] and v > 0:
                 row.setdefault("stage_gbps", {})[k] = round(c["stage_bytes"][key] / v / 1e3, 1)
-            if best is None or v > best[0]:
-                best = (v, T, k, key, c)
+                per_kernel.setdefault(kernel_name(wl, c["plan"], k), []).append(
+                    (v, c["stage_bytes"][key], c["stage_flops"].get(key, 0.0), T))
         table[str(T)] = row
 
-    v, Tb, kname, key, cb = best
-    bts = cb["stage_bytes"].get(key, 0)
-    achieved = bts / v / 1e3
+    # dominant kernel: largest summed duration over the sweep; achieved = mean
+    # algorithmic bytes per launch / mean launch duration
+    kname, launches = max(per_kernel.items(), key=lambda kv: sum(x[0] for x in kv[1]))
+    dur = statistics.fmean(x[0] for x in launches)
+    bts = statistics.fmean(x[1] for x in launches)
+    fl = statistics.fmean(x[2] for x in launches)
+    achieved = bts / dur / 1e3
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": kname, "tokens": Tb, "avg_launch_us": round(v, 3),
-                "algorithmic_bytes_per_launch": int(bts)}
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(kname, [x[3] for x in launches]),
+                "kernel": kname, "tokens": [x[3] for x in launches],
+                "avg_launch_us": round(dur, 3),
+                "algorithmic_bytes_per_launch": int(bts),
+                "mfma_frac": round(fl / dur / 1e6 / MFMA_PEAK_TFLOPS[dtype_name], 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -296,7 +367,8 @@ def main():
                         f"{'SiLU-gated' if wl.gated else 'ReLU^2'}",
             "tokens": sweep,
             "value_definition": "geometric mean over the token sweep of the cold-cache "
-                                "latency of one forward (HIP graph replay)",
+                                "latency of one forward (HIP graph replay), each the mean "
+                                "over the timed steps",
             "parallelism": "single GPU",
             "per_tokens": table,
             "wall_s_timed_region": round(wall, 3),

@@ -199,6 +199,25 @@ def test_reduction_slices_cover_every_block():
     assert_close(out, oracle_out(wl, Wc, tc), "H=256 over 8 waves")
 
 
+@pytest.mark.parametrize("per_channel,gated,dtype", [
+    (False, True, torch.bfloat16), (True, True, torch.bfloat16),
+    (False, False, torch.float16), (True, False, torch.float16)])
+def test_ragged_reduction_tails(per_channel, gated, dtype):
+    """H = 320 and I = 192 end both reductions in a half (64-wide) block; with
+    4 experts, T = 150 fills some experts past one 64-row tile (a full tile and
+    a 1-subtile tail), T = 40 leaves 2 active subtiles per tile, T = 20 runs the
+    small-batch path."""
+    wl = synth.custom("tails", E=4, H=320, I=192, K=2, gated=gated, per_channel=per_channel,
+                      dtype=dtype, seed=5)
+    Wc = synth.make_weights(wl, device="cpu")
+    Wg = Wc.to("cuda")
+    for T, force in ((150, dict(force_path=1)), (40, dict(force_path=1)),
+                     (40, dict(force_path=1, force_block_m=32)), (20, dict(force_path=2))):
+        tc = tokens(wl, T)
+        out = forward(wl, Wg, tc.to("cuda"), **force)
+        assert_close(out, oracle_out(wl, Wc, tc), f"tails T={T} {force}")
+
+
 # ---------------------------------------------------------------------------
 # determinism, invariances, graph replay
 # ---------------------------------------------------------------------------
