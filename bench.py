@@ -1,21 +1,23 @@
 #!/usr/bin/env python3
 """Benchmark of the local W4A16 MoE forward on one MI355X.
 
-One step = one forward at every token count of the sweep (route preparation,
-gather, gate/up GEMM, activation, down GEMM, FP32 combine: the whole path) on
-seeded synthetic inputs already resident in HBM.  Inside a step, for every
-token count:
+A forward is the whole path (route preparation, gather, gate/up GEMM,
+activation, down GEMM, FP32 combine) on seeded synthetic inputs already
+resident in HBM.  One step measures, at every token count of the sweep:
   1. a read-only pass over a 512 MiB buffer evicts the L2 caches and the
      256 MB Infinity Cache (it only reads, so no dirty lines are left to be
      written back while the forward runs);
-  2. the forward, captured once in a HIP graph, is replayed between two HIP
-     events: the cold latency (`value` is built from these);
+  2. cold latency: a HIP graph holding G copies of (eviction pass, forward)
+     and a graph holding G eviction passes alone are replayed back to back
+     between HIP events; the difference divided by G is the device time of
+     one forward on cold caches, without the submission latency of a launch
+     (the pages time graph replays the same way);
   3. the cache is evicted again and the forward runs once more as direct
      calls, with HIP events that the library records around each stage on the
      stream it launches on: per-stage kernel durations in the same timed
      region (the `roofline` kernel's average launch duration).
-Warm numbers (10 back-to-back replays, caches holding whatever fits) are
-reported afterwards as context.
+Warm numbers (a graph of G back-to-back forwards, caches holding whatever
+fits) are reported afterwards as context.
 
 Prints ONE JSON line.  `value` is the geometric mean over the token sweep of
 the mean cold per-forward latency in microseconds (lower is better).
@@ -167,6 +169,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--no-graph", action="store_true", help="time eager calls instead")
+    ap.add_argument("--graph-reps", type=int, default=10,
+                    help="forwards per captured graph (G); per-forward time = graph time / G")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain elementwise copy (negation) of this many MiB "
                          "three times: the known-size kernel that scales HBM counters")
@@ -201,10 +205,30 @@ def main():
 
     log(f"[bench] generating {wl.name} weights on the GPU")
     Wg = synth.make_weights(wl, device=dev)
-    flush_buf = torch.ones(128 * 1024 * 1024, dtype=torch.int32, device=dev)   # 512 MiB
+    flush_rows = torch.ones(16384, 8192, dtype=torch.int32, device=dev)   # 512 MiB
+    flush_out = torch.empty(16384, dtype=torch.int32, device=dev)
 
     def flush():
-        flush_buf.max()     # reads the whole buffer, writes one value
+        # reads the whole buffer, writes 64 KiB; a row-wise reduction needs no
+        # cross-block semaphores (no memset node when captured)
+        torch.amax(flush_rows, dim=1, out=flush_out)
+
+    G = args.graph_reps
+
+    def capture(fn):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    graph_flush = None if args.no_graph else capture(lambda: [flush() for _ in range(G)])
 
     torch.cuda.synchronize()
 
@@ -221,47 +245,56 @@ def main():
 
         fwd()
         torch.cuda.synchronize()
-        graph = None
+        g_cold = g_warm = None
         if not args.no_graph:
-            s = torch.cuda.Stream()
-            s.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(s):
-                fwd()
-            torch.cuda.current_stream().wait_stream(s)
-            torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                fwd()
-            torch.cuda.synchronize()
+            def cold_body(fwd=fwd):
+                for _ in range(G):
+                    flush()
+                    fwd()
+
+            def warm_body(fwd=fwd):
+                for _ in range(G):
+                    fwd()
+
+            g_cold = capture(cold_body)
+            g_warm = capture(warm_body)
         stage_b, total_b, total_f, stage_f, D, Rv = workload_bytes_flops(wl, tok.topk_ids.cpu(), T)
-        cases.append(dict(T=T, tok=tok, fwd=fwd, graph=graph, plan=plan, stage_bytes=stage_b,
+        cases.append(dict(T=T, tok=tok, fwd=fwd, g_cold=g_cold, g_warm=g_warm, plan=plan,
+                          stage_bytes=stage_b,
                           bytes=total_b, flops=total_f, stage_flops=stage_f, D=D, Rv=Rv,
                           cold=[], warm=[], stages={s: [] for s in STAGES}))
         log(f"[bench] T={T}: plan path={plan.path} block_m={plan.block_m} "
             f"k_slice={plan.k_slice} touched experts={D}")
 
-    def replay(c):
-        if c["graph"] is not None:
-            c["graph"].replay()
-        else:
-            c["fwd"]()
-
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
+    ev2 = torch.cuda.Event(enable_timing=True)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
 
     def step(record):
         for c in cases:
-            flush()
-            ev0.record()
-            replay(c)
-            ev1.record()
+            if c["g_cold"] is not None:
+                # G x (evict, forward) minus G x (evict): per-forward device time
+                # without the per-launch submission latency
+                ev0.record()
+                graph_flush.replay()
+                ev1.record()
+                c["g_cold"].replay()
+                ev2.record()
+            else:
+                flush()
+                ev0.record()
+                c["fwd"]()
+                ev1.record()
             flush()
             c["fwd"](stage_events=evs)
             evs[7 if c["plan"].path == 1 else 5].synchronize()
             if not record:
                 continue
-            c["cold"].append(ev0.elapsed_time(ev1) * 1e3)
+            if c["g_cold"] is not None:
+                c["cold"].append((ev1.elapsed_time(ev2) - ev0.elapsed_time(ev1)) * 1e3 / G)
+            else:
+                c["cold"].append(ev0.elapsed_time(ev1) * 1e3)
             for si, name in enumerate(STAGES):
                 if name in ("route_prep", "combine") and c["plan"].path == 2:
                     continue
@@ -277,15 +310,18 @@ def main():
     wall = time.perf_counter() - t0
     log(f"[bench] timed {args.steps} steps in {wall:.2f} s")
 
-    # warm context: 10 back-to-back replays
+    # warm context: G back-to-back forwards in one graph (caches hold what fits)
     for c in cases:
         for _ in range(3):
             ev0.record()
-            for _ in range(10):
-                replay(c)
+            if c["g_warm"] is not None:
+                c["g_warm"].replay()
+            else:
+                for _ in range(G):
+                    c["fwd"]()
             ev1.record()
             ev1.synchronize()
-            c["warm"].append(ev0.elapsed_time(ev1) * 1e3 / 10)
+            c["warm"].append(ev0.elapsed_time(ev1) * 1e3 / G)
 
     lat_cold = {c["T"]: statistics.fmean(c["cold"]) for c in cases}
     lat_warm = {c["T"]: statistics.median(c["warm"]) for c in cases}
@@ -367,8 +403,10 @@ def main():
                         f"{'SiLU-gated' if wl.gated else 'ReLU^2'}",
             "tokens": sweep,
             "value_definition": "geometric mean over the token sweep of the cold-cache "
-                                "latency of one forward (HIP graph replay), each the mean "
-                                "over the timed steps",
+                                "device time of one forward: (graph of G x (cache eviction, "
+                                "forward) - graph of G x eviction) / G, mean over the timed "
+                                "steps",
+            "graph_reps": G,
             "parallelism": "single GPU",
             "per_tokens": table,
             "wall_s_timed_region": round(wall, 3),

@@ -37,6 +37,8 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 struct Plan {
   int path = 2, bm = 16, ms = 1, kslice = 128, nkb = 1, nkb_tile = 1;
   int n_tiles_up = 0, n_tiles_down = 0, mode_up = 0;
+  bool down_resident = false;  // grouped path: down GEMM with the tile's rows resident in LDS
+  int col_steps = 0;
   int64_t R = 0, P = 0, MT = 0, items = 0;
   int N1 = 0;
   size_t off_counts = 0, off_offsets = 0, off_slot = 0, off_sorted = 0, off_tile = 0,
@@ -123,9 +125,22 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
   const int64_t touched = std::min<int64_t>(E, pl.R);
   pl.P = pl.R + touched * (pl.bm - 1);
   pl.MT = pl.P / pl.bm;
-  pl.n_tiles_up = gated ? (I + w4moe::kWgColsGated - 1) / w4moe::kWgColsGated
-                        : (I + w4moe::kWgColsPlain - 1) / w4moe::kWgColsPlain;
-  pl.n_tiles_down = (H + w4moe::kWgColsPlain - 1) / w4moe::kWgColsPlain;
+  const bool tile64 = pl.bm == w4moe::kTileRows;
+  const int cols_gated = tile64 ? w4moe::kTileColsGated : w4moe::kWgColsGated;
+  const int cols_plain = tile64 ? w4moe::kTileColsPlain : w4moe::kWgColsPlain;
+  pl.n_tiles_up = gated ? (I + cols_gated - 1) / cols_gated : (I + cols_plain - 1) / cols_plain;
+  pl.n_tiles_down = (H + cols_plain - 1) / cols_plain;
+  // short reductions: one workgroup per (tile, column chunk) keeps the tile's
+  // activation rows in LDS and walks col_steps column tiles; chunks are sized
+  // so that the tile capacity times the chunks fills the GPU about 8 times
+  pl.down_resident = tile64 && I <= w4moe::kResidentK;
+  if (pl.down_resident) {
+    const int64_t steps = pl.n_tiles_down;
+    const int64_t mt = std::max<int64_t>(pl.MT, 1);
+    const int64_t chunks = std::min<int64_t>(steps, std::max<int64_t>(1, (2048 + mt - 1) / mt));
+    pl.col_steps = static_cast<int>((steps + chunks - 1) / chunks);
+    pl.n_tiles_down = static_cast<int>((steps + pl.col_steps - 1) / pl.col_steps);
+  }
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -435,7 +450,11 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
   dn.n_tiles = pl.n_tiles_down;
   st = hip_status(evs.mark(4), "stage event");
   if (st != W4A16_OK) return st;
-  st = hip_status(pl.bm == w4moe::kTileRows
+  dn.col_steps = pl.col_steps;
+  st = hip_status(pl.down_resident
+                      ? w4moe::launch_down_resident(dn, desc->dtype, desc->qlayout,
+                                                    static_cast<int>(pl.MT), stream)
+                  : pl.bm == w4moe::kTileRows
                       ? w4moe::launch_tile_gemm(dn, desc->dtype, desc->qlayout, w4moe::MODE_DOWN,
                                                 static_cast<int>(pl.MT), stream)
                       : w4moe::launch_grouped_gemm(dn, desc->dtype, desc->qlayout, pl.ms,

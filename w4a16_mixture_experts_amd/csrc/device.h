@@ -205,9 +205,21 @@ __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t of
   return __builtin_amdgcn_raw_buffer_load_b32(r, ok ? off : kOob, 0, 0);
 }
 
+// 16-bit store; a masked lane writes nothing (the store falls outside the
+// resource and is dropped).
+__device__ __forceinline__ void bstore2(__amdgpu_buffer_rsrc_t r, uint32_t off, bool ok,
+                                        uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, ok ? off : kOob, 0, 0);
+}
+
 __device__ __forceinline__ uint32_t load4_if(bool ok, const void* p, const void* safe) {
   const uint32_t v = *reinterpret_cast<const uint32_t*>(ok ? p : safe);
   return ok ? v : 0u;
+}
+
+// Value of the neighbouring lane (lanes 2i and 2i+1 swap), one DPP move.
+__device__ __forceinline__ float swap_lane_pairs(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }

@@ -14,7 +14,10 @@ enum : int { MODE_UP_GATED = 0, MODE_UP_RELU2 = 1, MODE_DOWN = 2 };
 constexpr int kWgColsGated = 64;
 constexpr int kWgColsPlain = 128;
 constexpr int kCombineCols = 2048;
-constexpr int kTileRows = 64;  // route positions of one LDS-staged expert tile
+constexpr int kTileRows = 64;        // route positions of one LDS-staged expert tile
+constexpr int kTileWaves = 8;
+constexpr int kTileColsGated = 128;  // activation columns per tile workgroup (gated)
+constexpr int kTileColsPlain = 256;  // output columns per tile workgroup otherwise
 
 struct GemmParams {
   const uint16_t* a;          // UP: x [T][lda]; DOWN: act [P][lda] (A operand order)
@@ -35,7 +38,8 @@ struct GemmParams {
   int bm;
   uint16_t* out;              // UP: act [P][ldo]; DOWN: Y [P][ldo]
   int ldo;
-  int n_tiles;
+  int n_tiles;                // column tiles (resident down kernel: column chunks)
+  int col_steps;              // resident down kernel: 256-column steps per chunk
 };
 
 // small-batch path
@@ -129,6 +133,9 @@ hipError_t launch_grouped_gemm(const GemmParams& p, int dtype, int layout, int m
                                int max_tiles, hipStream_t stream);
 
 // 64-row expert tiles (route positions), LDS-staged activations
+constexpr int kResidentK = 256;      // reduction the resident down kernel holds in LDS
+hipError_t launch_down_resident(const GemmParams& p, int dtype, int layout, int max_tiles,
+                                hipStream_t stream);
 hipError_t launch_tile_gemm(const GemmParams& p, int dtype, int layout, int mode, int max_tiles,
                             hipStream_t stream);
 

@@ -9,20 +9,25 @@
 //        for Cutlass fused MoE"  Checkpoint format and Validation (gated and
 //        non-gated ReLU^2 experts).
 //
-// tile_gemm_kernel: one workgroup = one expert tile of up to 64 route
-// positions (four 16-row subtiles; empty subtiles are skipped) x 64 (gated:
-// 64 gate + 64 up weight rows) or 128 output columns, over the whole
-// reduction, in 128-wide blocks:
+// tile_gemm_kernel: one workgroup (8 waves) = one expert tile of up to 64
+// route positions (four 16-row subtiles; empty subtiles are skipped) x 256
+// weight rows (gated: 128 gate + 128 up rows = 128 activation columns;
+// otherwise 256 output columns), over the whole reduction in 128-wide blocks:
 //   - the tile's activation rows for block b+1 are loaded while block b is
-//     computed (one 32-value group per thread) and staged in a double-buffered
-//     LDS tile, already in A operand order; UP mode gathers token rows of x,
-//     DOWN mode reads the activation rows of the tile's positions;
+//     computed (16 values per thread) and staged in a double-buffered LDS
+//     tile in A operand order, with each 32-value group's correction sum; UP
+//     mode gathers token rows of x, DOWN mode reads the activation rows of the
+//     tile's positions;
 //   - each wave streams its two 16-row weight subtiles with the lane layout
 //     described in device.h (16 bytes per lane = one quantization group,
 //     a 4x4 dword transpose across lane rows), prefetched one block ahead;
 //   - MFMA j of a block spans one quantization group: exact dequantization,
 //     the group scale applied to the FP32 result;
 //   - one barrier per block.
+// The activation tile is as large as the weight block it meets, and the
+// workgroups of one tile are launched onto one XCD one after another (the
+// dispatcher deals consecutive workgroups to the 8 XCDs in turn), so the
+// re-reads of a tile's activations by its column workgroups hit that XCD's L2.
 // Epilogue: UP writes the 16-bit activation (SiLU(gate)*up or ReLU^2) in A
 // operand order; DOWN writes the 16-bit expert outputs Y.
 #include "device.h"
@@ -33,71 +38,277 @@ namespace w4moe {
 namespace {
 
 constexpr int kTileMs = kTileRows / 16;      // 16-row subtiles
-constexpr int kTileThreads = 256;            // 4 waves
+constexpr int kTileThreads = 64 * kTileWaves;
 constexpr int kAStride = 128 + 8;            // staged row stride (16 B padding)
+constexpr int kXcds = 8;
+constexpr int kWRing = 2;                    // weight blocks in registers (1 in flight)
+constexpr int kNsub = 2;                     // 16-row weight subtiles per wave
 
 template <int DT>
 __device__ __forceinline__ float scale_lo(uint32_t pair) { return H16<DT>::to_f32(pair & 0xffffu); }
 template <int DT>
 __device__ __forceinline__ float scale_hi(uint32_t pair) { return H16<DT>::to_f32(pair >> 16); }
 
+// acc += s * t for every output of a group (s: this lane's column scale)
+template <int NMS>
+__device__ __forceinline__ void scale_accumulate(f32x4 (&acc)[NMS][kNsub],
+                                                 const f32x4 (&t)[NMS][kNsub],
+                                                 const float (&sc)[kNsub]) {
+#pragma unroll
+  for (int ms = 0; ms < NMS; ++ms)
+#pragma unroll
+    for (int s = 0; s < kNsub; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[ms][s][i] = fmaf(sc[s], t[ms][s][i], acc[ms][s][i]);
+}
+
+// One 128-wide reduction block of one 16-row weight subtile, as one lane holds
+// it: group layout: 16 bytes (one quantization group of the lane's row) and
+// the 4 group scales of the row; per-channel: 32 bytes and the dword holding
+// the row's scale.
 template <int LAYOUT>
 struct WBlk {
-  u32x4 d;                       // group layout: 16 bytes; per-channel: first 16 bytes
-  u32x4 d2;                      // per-channel: second 16 bytes
-  uint32_t s0, s1;               // group layout: scales of groups 0..3 (two per dword)
+  u32x4 d;
+  u32x4 d2;                      // per-channel only
+  uint32_t s0, s1;
 };
 
-}  // namespace
+// One expert's packed weights and scales (wave-uniform), and where a wave's
+// two subtiles sit in them (per lane).
+struct WExpert {
+  __amdgpu_buffer_rsrc_t rw, rs;
+};
+struct WSrc {
+  uint32_t boff[kNsub], soff[kNsub];
+  bool on[kNsub];
+};
 
-// One expert tile with NMS active 16-row subtiles (valid routes come first in
-// a tile, so the active subtiles are a prefix).
-template <int DT, int LAYOUT, int MODE, int NMS>
-__device__ __forceinline__ void tile_run(const GemmParams& p, const int row_base, const int e,
-                                         const int nt, uint16_t (*s_a)[kTileRows][kAStride],
-                                         float (*s_corr)[4][kTileRows]) {
-  using T = H16<DT>;
-  constexpr int NSUB = 2;
-  constexpr bool UP = MODE != MODE_DOWN;
+__device__ __forceinline__ WExpert make_wexpert(const GemmParams& p, int e) {
+  WExpert x;
+  x.rw = make_rsrc(p.wq + static_cast<int64_t>(e) * p.wq_expert_bytes,
+                   static_cast<uint32_t>(p.wq_expert_bytes));
+  x.rs = make_rsrc(p.ws + static_cast<int64_t>(e) * p.ws_expert_elems,
+                   static_cast<uint32_t>(2 * p.ws_expert_elems));
+  return x;
+}
+
+template <int LAYOUT>
+__device__ __forceinline__ WSrc make_wsrc(const GemmParams& p, const int (&wrow)[kNsub],
+                                          const bool (&on)[kNsub]) {
   constexpr bool GROUP = LAYOUT == Q_GROUP_K;
+  WSrc w;
+#pragma unroll
+  for (int s = 0; s < kNsub; ++s) {
+    w.on[s] = on[s];
+    w.boff[s] = GROUP ? static_cast<uint32_t>(wrow[s]) * (p.K >> 1)
+                      : static_cast<uint32_t>(wrow[s] >> 1) * p.K;
+    w.soff[s] = GROUP ? 2u * static_cast<uint32_t>(wrow[s]) * (p.K >> 5)
+                      : 2u * static_cast<uint32_t>(wrow[s] & ~1);
+  }
+  return w;
+}
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int c = lane & 15, g = lane >> 4, par = c & 1;
+// Loads of block k0 (reads nothing past the reduction or the output rows:
+// those lanes get zeros, scales included).
+template <int LAYOUT>
+__device__ __forceinline__ void load_wblk(const WExpert& x, const WSrc& w, int k0, int K, int g,
+                                          WBlk<LAYOUT> (&b)[kNsub]) {
+  const int ng = k0 < K ? min(4, (K - k0) >> 5) : 0;
+#pragma unroll
+  for (int s = 0; s < kNsub; ++s) {
+    const bool ok = w.on[s] && g < ng;
+    if constexpr (LAYOUT == Q_GROUP_K) {
+      b[s].d = bload16(x.rw, w.boff[s] + (k0 >> 1) + 16 * g, ok);
+      const uint32_t so = w.soff[s] + 2u * (k0 >> 5);
+      b[s].s0 = bload4(x.rs, so, w.on[s] && ng > 0);
+      b[s].s1 = bload4(x.rs, so + 4, w.on[s] && ng > 2);
+    } else {
+      b[s].d = bload16(x.rw, w.boff[s] + k0 + 32 * g, ok);
+      b[s].d2 = bload16(x.rw, w.boff[s] + k0 + 32 * g + 16, ok);
+      b[s].s0 = bload4(x.rs, w.soff[s], w.on[s] && ng > 0);
+      b[s].s1 = 0u;
+    }
+  }
+}
 
-  // this wave's two weight-row subtiles and the output column of this lane
-  int col[NSUB], wrow[NSUB];
-  bool on[NSUB];
+// acc += A[rows 0..16*NMS) x deq(W block)^T for one 128-block.  `sa` points
+// at LDS element (row 0, first column of the block), rows `stride` apart.
+// All A fragments are read first (LDS latency paid once per block); the
+// correction -1.5 * sum(a) of each group comes from one MFMA against a
+// constant operand.
+template <int DT, int LAYOUT, int NMS, bool UPFRONT = true>
+__device__ __forceinline__ void mma_block(const uint16_t* sa, int stride,
+                                          const WBlk<LAYOUT> (&wb)[kNsub],
+                                          f32x4 (&acc)[NMS][kNsub], int c, int g, int par) {
+  using T = H16<DT>;
+  constexpr bool GROUP = LAYOUT == Q_GROUP_K;
+  // scheduling fences keep the compiler from hoisting the LDS reads of later
+  // blocks (or, without UPFRONT, of later groups) into this one, which would
+  // hold every fragment live at once
+  __builtin_amdgcn_sched_barrier(0);
+  const u32x4 bconst = {T::kNegOneHalf2, T::kNegOneHalf2, T::kNegOneHalf2, T::kNegOneHalf2};
+  const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
+  auto frag = [&](int ms, int j) {
+    return *reinterpret_cast<const u32x4*>(sa + (16 * ms + c) * stride + 32 * j + 8 * g);
+  };
+  u32x4 af[NMS][4];
+  if constexpr (UPFRONT) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int ms = 0; ms < NMS; ++ms) af[ms][j] = frag(ms, j);
+  }
+  // transpose so that MFMA j sees group j
+  uint32_t d[kNsub][8];
+#pragma unroll
+  for (int s = 0; s < kNsub; ++s) {
+    d[s][0] = wb[s].d[0]; d[s][1] = wb[s].d[1]; d[s][2] = wb[s].d[2]; d[s][3] = wb[s].d[3];
+    if constexpr (GROUP) {
+      transpose_rows4(d[s][0], d[s][1], d[s][2], d[s][3]);
+    } else {
+      d[s][4] = wb[s].d2[0]; d[s][5] = wb[s].d2[1]; d[s][6] = wb[s].d2[2]; d[s][7] = wb[s].d2[3];
+      transpose_rows4(d[s][0], d[s][2], d[s][4], d[s][6]);
+      transpose_rows4(d[s][1], d[s][3], d[s][5], d[s][7]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    u32x4 bop[kNsub];
+    float sc[kNsub];
+#pragma unroll
+    for (int s = 0; s < kNsub; ++s) {
+      if constexpr (GROUP) {
+        bop[s] = nibbles_to_h16<DT>(d[s][j]);
+        const uint32_t pr = (j < 2) ? wb[s].s0 : wb[s].s1;
+        sc[s] = (j & 1) ? scale_hi<DT>(pr) : scale_lo<DT>(pr);
+      } else {
+        bop[s] = bytes_to_h16<DT>(d[s][2 * j] >> (4 * par), d[s][2 * j + 1] >> (4 * par));
+        sc[s] = par ? scale_hi<DT>(wb[s].s0) : scale_lo<DT>(wb[s].s0);
+      }
+      // no mask needed: a group past the reduction or a column past the
+      // output reads scale 0 (out-of-range load) and A rows of zeros
+    }
+    f32x4 t[NMS][kNsub];
+#pragma unroll
+    for (int ms = 0; ms < NMS; ++ms) {
+      const u32x4 a = UPFRONT ? af[ms][j] : frag(ms, j);
+      const f32x4 corr = T::mfma(a, bconst, fzero);
+#pragma unroll
+      for (int s = 0; s < kNsub; ++s) t[ms][s] = T::mfma(a, bop[s], corr);
+    }
+    scale_accumulate<NMS>(acc, t, sc);
+    if constexpr (!UPFRONT) __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Valid rows of the lane's 16 * NMS output rows as a bit mask: bit 4ms + i
+// stands for tile row 16ms + 4g + i.
+template <int NMS>
+__device__ __forceinline__ uint32_t valid_rows(const GemmParams& p, int row_base, int g) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int ms = 0; ms < NMS; ++ms)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      m |= (p.sorted[row_base + 16 * ms + 4 * g + i] >= 0 ? 1u : 0u) << (4 * ms + i);
+  return m;
+}
+
+// Epilogue: lane (c, g) holds rows row_base + 16ms + 4g + i of column col[s].
+// UP writes the 16-bit activation in A operand order (padding rows get 0);
+// DOWN writes the 16-bit expert outputs of valid rows.  Stores go through a
+// buffer resource over the tile's 64 output rows (masked lanes store nothing).
+template <int DT, int MODE, int NMS>
+__device__ __forceinline__ void store_outputs(const GemmParams& p, int row_base,
+                                              const f32x4 (&acc)[NMS][kNsub],
+                                              const int (&col)[kNsub], const bool (&on)[kNsub],
+                                              int g, uint32_t vmask) {
+  using T = H16<DT>;
+  const auto ro = make_rsrc(p.out + static_cast<int64_t>(row_base) * p.ldo,
+                            static_cast<uint32_t>(2 * kTileRows * p.ldo));
+#pragma unroll
+  for (int ms = 0; ms < NMS; ++ms) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool valid = (vmask >> (4 * ms + i)) & 1u;
+      const uint32_t rowoff = static_cast<uint32_t>((16 * ms + 4 * g + i) * p.ldo);
+      if constexpr (MODE == MODE_UP_GATED) {
+        const float a = valid ? silu(16.0f * acc[ms][0][i]) * (16.0f * acc[ms][1][i]) : 0.0f;
+        bstore2(ro, 2u * (rowoff + ((col[0] & ~7) | a_pos(col[0] & 7))), on[0], T::from_f32(a));
+      } else if constexpr (MODE == MODE_UP_RELU2) {
+#pragma unroll
+        for (int s = 0; s < kNsub; ++s) {
+          const float h = fmaxf(16.0f * acc[ms][s][i], 0.0f);
+          bstore2(ro, 2u * (rowoff + ((col[s] & ~7) | a_pos(col[s] & 7))), on[s],
+                  T::from_f32(valid ? h * h : 0.0f));
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < kNsub; ++s)
+          bstore2(ro, 2u * (rowoff + col[s]), on[s] && valid, T::from_f32(16.0f * acc[ms][s][i]));
+      }
+    }
+  }
+}
+
+// Rows and columns of wave w's two subtiles in column tile nt.
+template <int MODE>
+__device__ __forceinline__ void wave_columns(const GemmParams& p, int nt, int w, int c,
+                                             int (&col)[kNsub], int (&wrow)[kNsub],
+                                             bool (&on)[kNsub]) {
   if constexpr (MODE == MODE_UP_GATED) {
-    const int i0 = nt * kWgColsGated + w * 16;
+    const int i0 = nt * kTileColsGated + w * 16;
     on[0] = on[1] = i0 < p.n_cols;
     col[0] = col[1] = i0 + c;
     wrow[0] = i0 + c;
     wrow[1] = p.up_rows + i0 + c;
   } else {
-    const int n0 = nt * kWgColsPlain + w * 32;
+    const int n0 = nt * kTileColsPlain + w * 32;
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
+    for (int s = 0; s < kNsub; ++s) {
       on[s] = n0 + 16 * s < p.n_cols;
       col[s] = n0 + 16 * s + c;
       wrow[s] = col[s];
     }
   }
-  const auto rw = make_rsrc(p.wq + static_cast<int64_t>(e) * p.wq_expert_bytes,
-                            static_cast<uint32_t>(p.wq_expert_bytes));
-  const auto rs = make_rsrc(p.ws + static_cast<int64_t>(e) * p.ws_expert_elems,
-                            static_cast<uint32_t>(2 * p.ws_expert_elems));
-  uint32_t boff[NSUB], soff[NSUB];
-  float scol[NSUB];
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    boff[s] = GROUP ? static_cast<uint32_t>(wrow[s]) * (p.K >> 1)
-                    : static_cast<uint32_t>(wrow[s] >> 1) * p.K;
-    soff[s] = GROUP ? 2u * static_cast<uint32_t>(wrow[s]) * (p.K >> 5) : 0u;
-    scol[s] = GROUP ? 0.0f : T::to_f32(bload4(rs, 2u * (wrow[s] & ~1), on[s]) >> (16 * (wrow[s] & 1)));
-  }
+}
 
-  // staging role of this thread: row st_row, 32-value group st_q of each block
-  const int st_row = tid >> 2, st_q = tid & 3;
+// Active 16-row subtiles of a tile: valid routes come first, so they are a
+// prefix (uniform).
+__device__ __forceinline__ int active_subtiles(const GemmParams& p, int row_base) {
+  int nms = 0;
+#pragma unroll
+  for (int ms = 0; ms < kTileMs; ++ms) nms += p.sorted[row_base + 16 * ms] >= 0 ? 1 : 0;
+  return nms;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Streaming tile kernel: the reduction in 128-blocks, activations staged per
+// block into a double-buffered LDS tile.
+// ---------------------------------------------------------------------------
+
+template <int DT, int LAYOUT, int MODE, int NMS>
+__device__ __forceinline__ void tile_run(const GemmParams& p, const int row_base, const int e,
+                                         const int nt, uint16_t (*s_a)[kTileRows][kAStride]) {
+  constexpr bool UP = MODE != MODE_DOWN;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int c = lane & 15, g = lane >> 4, par = c & 1;
+
+  int col[kNsub], wrow[kNsub];
+  bool on[kNsub];
+  wave_columns<MODE>(p, nt, w, c, col, wrow, on);
+  const WExpert wx = make_wexpert(p, e);
+  const WSrc ws = make_wsrc<LAYOUT>(p, wrow, on);
+
+  // staging role of this thread: row st_row, kVals consecutive values of each
+  // 128-block starting at kVals * st_c
+  constexpr int kVals = kTileRows * 128 / kTileThreads;  // 32 (4 waves) or 16 (8 waves)
+  constexpr int kChunks = kVals / 8;                     // 16-byte loads per thread
+  constexpr int kPerRow = 128 / kVals;
+  static_assert(kVals == 32 || kVals == 16, "16 or 32 staged values per thread");
+  const int st_row = tid / kPerRow, st_c = tid % kPerRow;
   const int st_r = p.sorted[row_base + st_row];
   const bool st_ok = st_r >= 0;
   const auto ra = UP ? make_rsrc(p.a, p.a_bytes)
@@ -105,168 +316,202 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, const int row_base
                                  static_cast<uint32_t>(2 * kTileRows * p.lda));
   const uint32_t st_off = 2u * static_cast<uint32_t>(UP ? (st_ok ? st_r / p.top_k : 0) : st_row) *
                           static_cast<uint32_t>(p.lda);
-
-  auto load_a = [&](int k0, u32x4 (&v)[4]) {
-    const bool ok = st_ok && k0 + 32 * st_q < p.K;
+  auto load_a = [&](int k0, u32x4 (&v)[kChunks]) {
+    const bool ok = st_ok && k0 + kVals * st_c < p.K;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) v[h] = bload16(ra, st_off + 2u * (k0 + 32 * st_q + 8 * h), ok);
+    for (int h = 0; h < kChunks; ++h)
+      v[h] = bload16(ra, st_off + 2u * (k0 + kVals * st_c + 8 * h), ok);
   };
-  // staged activations in A operand order, plus the group's correction
-  // -1.5 * sum(a) that turns (24 + q) / 16 back into q / 16
-  auto store_a = [&](int buf, const u32x4 (&v)[4]) {
-    uint16_t* dst = &s_a[buf][st_row][32 * st_q];
-    float sum = 0.0f;
+  // staged activations in A operand order
+  auto store_a = [&](int buf, const u32x4 (&v)[kChunks]) {
+    uint16_t* dst = &s_a[buf][st_row][kVals * st_c];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
+    for (int h = 0; h < kChunks; ++h)
       *reinterpret_cast<u32x4*>(dst + 8 * h) = UP ? permute_a(v[h]) : v[h];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) sum = T::dot2_ones(v[h][q], sum);
-    }
-    s_corr[buf][st_q][st_row] = -1.5f * sum;
-  };
-  auto load_w = [&](int k0, WBlk<LAYOUT> (&b)[NSUB]) {
-    const int ng = k0 < p.K ? min(4, (p.K - k0) >> 5) : 0;
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      const bool ok = on[s] && g < ng;
-      if constexpr (GROUP) {
-        b[s].d = bload16(rw, boff[s] + (k0 >> 1) + 16 * g, ok);
-        const uint32_t so = soff[s] + 2u * (k0 >> 5);
-        b[s].s0 = bload4(rs, so, on[s] && ng > 0);
-        b[s].s1 = bload4(rs, so + 4, on[s] && ng > 2);
-      } else {
-        b[s].d = bload16(rw, boff[s] + k0 + 32 * g, ok);
-        b[s].d2 = bload16(rw, boff[s] + k0 + 32 * g + 16, ok);
-        b[s].s0 = b[s].s1 = 0u;
-      }
-    }
   };
 
-  f32x4 acc[NMS][NSUB];
+  f32x4 acc[NMS][kNsub];
 #pragma unroll
   for (int ms = 0; ms < NMS; ++ms)
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) acc[ms][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < kNsub; ++s) acc[ms][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // prologue: block 0 of A staged, block 0 of the weights in registers
-  {
-    u32x4 av[4];
-    load_a(0, av);
-    store_a(0, av);
-  }
-  WBlk<LAYOUT> wcur[NSUB];
-  load_w(0, wcur);
+  // Pipeline.  Weights: a ring of kWRing register sets, block b + kWRing - 1
+  // is requested while block b is computed.  Activations: block b + 1 is
+  // staged into LDS at the end of step b from registers loaded two steps
+  // earlier.  The loop runs in whole rounds of the ring (register sets need
+  // compile-time indices); steps past the last block only issue masked loads.
+  WBlk<LAYOUT> wr[kWRing][kNsub];
+  u32x4 ar[2][kChunks];
+  load_a(0, ar[0]);
+  load_a(128, ar[1]);
+#pragma unroll
+  for (int i = 0; i < kWRing - 1; ++i) load_wblk<LAYOUT>(wx, ws, 128 * i, p.K, g, wr[i]);
+  store_a(0, ar[0]);
+  load_a(256, ar[0]);
   __syncthreads();
 
   const int nblk = (p.K + 127) >> 7;
-  for (int blk = 0; blk < nblk; ++blk) {
-    const int k0 = blk * 128;
-    const int buf = blk & 1;
-    // next block (reads nothing past the reduction: those loads are masked)
-    u32x4 anext[4];
-    WBlk<LAYOUT> wnext[NSUB];
-    load_a(k0 + 128, anext);
-    load_w(k0 + 128, wnext);
-    const int ng = min(4, (p.K - k0) >> 5);
-    // weights of this block: transpose so that MFMA j sees group j
-    uint32_t d[NSUB][8];
+  for (int blk0 = 0; blk0 < nblk; blk0 += kWRing) {
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      d[s][0] = wcur[s].d[0]; d[s][1] = wcur[s].d[1]; d[s][2] = wcur[s].d[2]; d[s][3] = wcur[s].d[3];
-      if constexpr (GROUP) {
-        transpose_rows4(d[s][0], d[s][1], d[s][2], d[s][3]);
-      } else {
-        d[s][4] = wcur[s].d2[0]; d[s][5] = wcur[s].d2[1]; d[s][6] = wcur[s].d2[2]; d[s][7] = wcur[s].d2[3];
-        transpose_rows4(d[s][0], d[s][2], d[s][4], d[s][6]);
-        transpose_rows4(d[s][1], d[s][3], d[s][5], d[s][7]);
-      }
+    for (int u = 0; u < kWRing; ++u) {
+      const int b = blk0 + u;
+      load_wblk<LAYOUT>(wx, ws, 128 * (b + kWRing - 1), p.K, g, wr[(u + kWRing - 1) % kWRing]);
+      if (b < nblk) mma_block<DT, LAYOUT, NMS>(&s_a[b & 1][0][0], kAStride, wr[u], acc, c, g, par);
+      store_a((b + 1) & 1, ar[(u + 1) & 1]);
+      load_a(128 * (b + 3), ar[(u + 1) & 1]);
+      __syncthreads();
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u32x4 bop[NSUB];
-      float sc[NSUB];
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        if constexpr (GROUP) {
-          bop[s] = nibbles_to_h16<DT>(d[s][j]);
-          const uint32_t pr = (j < 2) ? wcur[s].s0 : wcur[s].s1;
-          sc[s] = (j & 1) ? scale_hi<DT>(pr) : scale_lo<DT>(pr);
-        } else {
-          bop[s] = bytes_to_h16<DT>(d[s][2 * j] >> (4 * par), d[s][2 * j + 1] >> (4 * par));
-          sc[s] = scol[s];
-        }
-        sc[s] = (j < ng && on[s]) ? sc[s] : 0.0f;
-      }
-#pragma unroll
-      for (int ms = 0; ms < NMS; ++ms) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&s_a[buf][16 * ms + c][32 * j + 8 * g]);
-        const f32x4 corr = *reinterpret_cast<const f32x4*>(&s_corr[buf][j][16 * ms + 4 * g]);
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) {
-          const f32x4 t = T::mfma(a, bop[s], corr);
-          acc[ms][s][0] = fmaf(sc[s], t[0], acc[ms][s][0]);
-          acc[ms][s][1] = fmaf(sc[s], t[1], acc[ms][s][1]);
-          acc[ms][s][2] = fmaf(sc[s], t[2], acc[ms][s][2]);
-          acc[ms][s][3] = fmaf(sc[s], t[3], acc[ms][s][3]);
-        }
-      }
-    }
-    store_a(buf ^ 1, anext);
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) wcur[s] = wnext[s];
-    __syncthreads();
   }
+  store_outputs<DT, MODE, NMS>(p, row_base, acc, col, on, g, valid_rows<NMS>(p, row_base, g));
+}
 
-  // epilogue: lane (c, g) holds rows row_base + 16ms + 4g + i, column col[s]
+template <int DT, int LAYOUT, int MODE>
+__global__ void __launch_bounds__(kTileThreads)
+tile_gemm_kernel(const GemmParams p) {
+  __shared__ uint16_t s_a[2][kTileRows][kAStride];
+
+  // workgroup L runs on XCD L % 8; XCD x takes tiles x, x + 8, ... and walks
+  // the column tiles of each tile back to back
+  const int L = blockIdx.x;
+  const int q = L / kXcds;
+  const int mt = kXcds * (q / p.n_tiles) + L % kXcds;
+  const int nt = q % p.n_tiles;
+  const int row_base = mt * kTileRows;
+  if (row_base >= p.offsets[p.E]) return;  // whole workgroup: tile past the padded total
+  const int nms = active_subtiles(p, row_base);
+  const int e = p.tile_expert[mt];
+  switch (nms) {
+    case 1: tile_run<DT, LAYOUT, MODE, 1>(p, row_base, e, nt, s_a); break;
+    case 2: tile_run<DT, LAYOUT, MODE, 2>(p, row_base, e, nt, s_a); break;
+    case 3: tile_run<DT, LAYOUT, MODE, 3>(p, row_base, e, nt, s_a); break;
+    default: tile_run<DT, LAYOUT, MODE, 4>(p, row_base, e, nt, s_a); break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Down GEMM for short reductions (K <= kResidentK): the tile's activation rows
+// stay in LDS for the whole workgroup, which walks p.col_steps column steps of
+// 8 x 32 output columns.  Waves never synchronize after the staging; each
+// requests the next step's weights while it computes the current one.
+// ---------------------------------------------------------------------------
+
+template <int DT, int LAYOUT, int NMS, int NKB>
+__device__ __forceinline__ void down_resident_run(const GemmParams& p, const int row_base,
+                                                  const int e, const int chunk, uint16_t* s_ar) {
+  constexpr int S = NKB * 128 + 8;   // row stride of the resident tile
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int c = lane & 15, g = lane >> 4, par = c & 1;
+
+  // stage the tile's activation rows once (padding rows and columns past K
+  // read zeros)
+  {
+    constexpr int kPerRow = NKB * 16;                       // 16-byte chunks per row
+    constexpr int kIters = kTileRows * kPerRow / kTileThreads;
+    static_assert(kTileRows * kPerRow % kTileThreads == 0, "staging covers the tile");
+    const auto ra = make_rsrc(p.a + static_cast<int64_t>(row_base) * p.lda,
+                              static_cast<uint32_t>(2 * kTileRows * p.lda));
+    u32x4 v[kIters];
 #pragma unroll
-  for (int ms = 0; ms < NMS; ++ms) {
+    for (int i = 0; i < kIters; ++i) {
+      const int idx = tid + i * kTileThreads;
+      const int row = idx / kPerRow, ch = idx % kPerRow;
+      const bool ok = p.sorted[row_base + row] >= 0 && 8 * ch < p.K;
+      v[i] = bload16(ra, 2u * static_cast<uint32_t>(row * p.lda + 8 * ch), ok);
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t prow = row_base + 16 * ms + 4 * g + i;
-      const bool valid = p.sorted[prow] >= 0;
-      uint16_t* orow = p.out + prow * p.ldo;
-      if constexpr (MODE == MODE_UP_GATED) {
-        if (on[0]) {
-          const float a = valid ? silu(16.0f * acc[ms][0][i]) * (16.0f * acc[ms][1][i]) : 0.0f;
-          orow[(col[0] & ~7) | a_pos(col[0] & 7)] = T::from_f32(a);
-        }
-      } else if constexpr (MODE == MODE_UP_RELU2) {
+    for (int i = 0; i < kIters; ++i) {
+      const int idx = tid + i * kTileThreads;
+      const int row = idx / kPerRow, ch = idx % kPerRow;
+      *reinterpret_cast<u32x4*>(s_ar + row * S + 8 * ch) = v[i];
+    }
+  }
+  __syncthreads();
+
+  const int step_begin = chunk * p.col_steps;
+  const int step_end = min(step_begin + p.col_steps, (p.n_cols + kTileColsPlain - 1) / kTileColsPlain);
+
+  const WExpert wx = make_wexpert(p, e);
+  const uint32_t vmask = valid_rows<NMS>(p, row_base, g);
+  // wave w's columns in step st: st * 256 + 32 w + 16 k + c (k = subtile)
+  auto step_src = [&](int st, int (&col)[kNsub], bool (&on)[kNsub]) {
+    const int n0 = st * kTileColsPlain + w * 32;
 #pragma unroll
-        for (int s = 0; s < NSUB; ++s) {
-          if (!on[s]) continue;
-          const float h = fmaxf(16.0f * acc[ms][s][i], 0.0f);
-          orow[(col[s] & ~7) | a_pos(col[s] & 7)] = T::from_f32(valid ? h * h : 0.0f);
-        }
-      } else {
-        if (valid) {
+    for (int k = 0; k < kNsub; ++k) {
+      col[k] = n0 + 16 * k + c;
+      on[k] = st < step_end && n0 + 16 * k < p.n_cols;
+    }
+    return make_wsrc<LAYOUT>(p, col, on);
+  };
+  // two register sets: the next block's weights are requested while the
+  // current block is computed
+  auto load_blk = [&](int st, int kb, WBlk<LAYOUT> (&wb)[kNsub]) {
+    int col[kNsub];
+    bool on[kNsub];
+    const WSrc ws = step_src(st, col, on);
+    load_wblk<LAYOUT>(wx, ws, 128 * kb, p.K, g, wb);
+  };
+  f32x4 acc[NMS][kNsub];
+  auto zero_acc = [&]() {
 #pragma unroll
-          for (int s = 0; s < NSUB; ++s)
-            if (on[s]) orow[col[s]] = T::from_f32(16.0f * acc[ms][s][i]);
-        }
+    for (int ms = 0; ms < NMS; ++ms)
+#pragma unroll
+      for (int k = 0; k < kNsub; ++k) acc[ms][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  auto store_step = [&](int st) {
+    int col[kNsub];
+    bool on[kNsub];
+    step_src(st, col, on);
+    store_outputs<DT, MODE_DOWN, NMS>(p, row_base, acc, col, on, g, vmask);
+  };
+
+  static_assert(NKB == 1 || NKB == 2, "one or two 128-blocks per step");
+  WBlk<LAYOUT> w0[kNsub], w1[kNsub];
+  load_blk(step_begin, 0, w0);
+  if constexpr (NKB == 2) {
+    for (int st = step_begin; st < step_end; ++st) {
+      load_blk(st, 1, w1);
+      zero_acc();
+      mma_block<DT, LAYOUT, NMS, false>(s_ar, S, w0, acc, c, g, par);
+      load_blk(st + 1, 0, w0);
+      mma_block<DT, LAYOUT, NMS, false>(s_ar + 128, S, w1, acc, c, g, par);
+      store_step(st);
+    }
+  } else {
+    for (int st = step_begin; st < step_end; st += 2) {
+      load_blk(st + 1, 0, w1);
+      zero_acc();
+      mma_block<DT, LAYOUT, NMS, false>(s_ar, S, w0, acc, c, g, par);
+      store_step(st);
+      load_blk(st + 2, 0, w0);
+      if (st + 1 < step_end) {
+        zero_acc();
+        mma_block<DT, LAYOUT, NMS, false>(s_ar, S, w1, acc, c, g, par);
+        store_step(st + 1);
       }
     }
   }
 }
 
-template <int DT, int LAYOUT, int MODE>
-__global__ void __launch_bounds__(kTileThreads, 2)
-tile_gemm_kernel(const GemmParams p) {
-  __shared__ uint16_t s_a[2][kTileRows][kAStride];
-  __shared__ float s_corr[2][4][kTileRows];
+template <int DT, int LAYOUT, int NKB>
+__global__ void __launch_bounds__(kTileThreads)
+down_resident_kernel(const GemmParams p) {
+  __shared__ uint16_t s_ar[kTileRows * (NKB * 128 + 8)];
 
-  const int mt = blockIdx.y;
+  // same XCD-aware order as the streaming kernel (n_tiles = column chunks)
+  const int L = blockIdx.x;
+  const int q = L / kXcds;
+  const int mt = kXcds * (q / p.n_tiles) + L % kXcds;
+  const int chunk = q % p.n_tiles;
   const int row_base = mt * kTileRows;
-  if (row_base >= p.offsets[p.E]) return;  // whole workgroup: tile past the padded total
-  int nms = 0;
-#pragma unroll
-  for (int ms = 0; ms < kTileMs; ++ms) nms += p.sorted[row_base + 16 * ms] >= 0 ? 1 : 0;
+  if (row_base >= p.offsets[p.E]) return;
+  const int nms = active_subtiles(p, row_base);
   const int e = p.tile_expert[mt];
-  const int nt = blockIdx.x;
   switch (nms) {
-    case 1: tile_run<DT, LAYOUT, MODE, 1>(p, row_base, e, nt, s_a, s_corr); break;
-    case 2: tile_run<DT, LAYOUT, MODE, 2>(p, row_base, e, nt, s_a, s_corr); break;
-    case 3: tile_run<DT, LAYOUT, MODE, 3>(p, row_base, e, nt, s_a, s_corr); break;
-    default: tile_run<DT, LAYOUT, MODE, 4>(p, row_base, e, nt, s_a, s_corr); break;
+    case 1: down_resident_run<DT, LAYOUT, 1, NKB>(p, row_base, e, chunk, s_ar); break;
+    case 2: down_resident_run<DT, LAYOUT, 2, NKB>(p, row_base, e, chunk, s_ar); break;
+    case 3: down_resident_run<DT, LAYOUT, 3, NKB>(p, row_base, e, chunk, s_ar); break;
+    default: down_resident_run<DT, LAYOUT, 4, NKB>(p, row_base, e, chunk, s_ar); break;
   }
 }
 
@@ -286,9 +531,29 @@ static hipError_t launch_tile_mode(const GemmParams& p, int mode, dim3 grid, hip
   }
 }
 
+template <int DT, int LAYOUT>
+static hipError_t launch_resident_dl(const GemmParams& p, dim3 grid, hipStream_t st) {
+  if (p.K <= 128)
+    hipLaunchKernelGGL((down_resident_kernel<DT, LAYOUT, 1>), grid, dim3(kTileThreads), 0, st, p);
+  else
+    hipLaunchKernelGGL((down_resident_kernel<DT, LAYOUT, 2>), grid, dim3(kTileThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_resident(const GemmParams& p, int dtype, int layout, int max_tiles,
+                                hipStream_t stream) {
+  if (p.K > kResidentK || p.col_steps < 1) return hipErrorInvalidValue;
+  const dim3 grid(kXcds * p.n_tiles * ((max_tiles + kXcds - 1) / kXcds));
+  if (dtype == DT_BF16)
+    return layout == Q_GROUP_K ? launch_resident_dl<DT_BF16, Q_GROUP_K>(p, grid, stream)
+                               : launch_resident_dl<DT_BF16, Q_PER_CHANNEL>(p, grid, stream);
+  return layout == Q_GROUP_K ? launch_resident_dl<DT_FP16, Q_GROUP_K>(p, grid, stream)
+                             : launch_resident_dl<DT_FP16, Q_PER_CHANNEL>(p, grid, stream);
+}
+
 hipError_t launch_tile_gemm(const GemmParams& p, int dtype, int layout, int mode, int max_tiles,
                             hipStream_t stream) {
-  const dim3 grid(p.n_tiles, max_tiles);
+  const dim3 grid(kXcds * p.n_tiles * ((max_tiles + kXcds - 1) / kXcds));
   if (dtype == DT_BF16)
     return layout == Q_GROUP_K ? launch_tile_mode<DT_BF16, Q_GROUP_K>(p, mode, grid, stream)
                                : launch_tile_mode<DT_BF16, Q_PER_CHANNEL>(p, mode, grid, stream);
