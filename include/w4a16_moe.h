@@ -95,6 +95,10 @@ typedef struct {
                                  route preparation; needs T*K <= 64)             */
   int32_t force_block_m;      /* grouped path: 0 (= 64) or 16/32/64 rows per
                                  expert tile                                     */
+  int32_t force_splitk;       /* grouped path with 64-row tiles: 0 = choose from
+                                 the expected routes per expert, 1 = split-K
+                                 gate/up (partials + activation kernel), 2 = the
+                                 streaming gate/up kernel                        */
 } w4a16_moe_desc_t;
 
 /* Variant the library runs for a descriptor (for tests and reports). */
@@ -103,7 +107,7 @@ typedef struct {
   int32_t block_m;            /* grouped path: rows per expert tile              */
   int32_t k_slice;            /* gate/up reduction slice per wave (8 waves split
                                  the reduction when tiles have few rows)         */
-  int32_t reserved;
+  int32_t splitk_chunks;      /* split-K gate/up: reduction chunks (0 = off)     */
   int64_t max_positions;      /* capacity of the padded route list               */
   int64_t max_tiles;          /* capacity of the expert tile list                */
   size_t workspace_bytes;     /* bytes w4a16_moe_forward needs                   */

@@ -58,6 +58,7 @@ def good(**kw):
     ("intermediate", 1828, 2, "intermediate=1828"),
     ("force_block_m", 48, 1, "force_block_m"),
     ("force_path", 3, 1, "force_path"),
+    ("force_splitk", 3, 1, "force_splitk"),
 ])
 def test_descriptor_errors(field, value, status, needle):
     d = good()
@@ -128,6 +129,19 @@ def test_plans_by_route_count():
                                 num_local_experts=384, top_k=8))
     assert p2.path == 1 and p2.block_m == 64
     assert p2.max_positions == 2048 * 8 + 384 * 63
+    assert p2.splitk_chunks == 0          # ~43 routes per expert: streaming gate/up
+    # few routes per expert: split-K gate/up; chunks of an even number of
+    # blocks, at most 18 (the x slice stays in LDS): 56 blocks -> 4 x 14
+    p4 = B.get_plan(B.make_desc(num_tokens=32, hidden=7168, intermediate=256,
+                                num_local_experts=384, top_k=8))
+    assert p4.path == 1 and p4.splitk_chunks == 4
+    assert B.get_plan(B.make_desc(num_tokens=256, hidden=7168, intermediate=256,
+                                  num_local_experts=384, top_k=8)).splitk_chunks == 0
+    d5 = B.make_desc(num_tokens=32, hidden=7168, intermediate=256, num_local_experts=384,
+                     top_k=8, force_splitk=2)
+    assert B.get_plan(d5).splitk_chunks == 0
+    assert B.workspace_size(d5) < B.workspace_size(B.make_desc(
+        num_tokens=32, hidden=7168, intermediate=256, num_local_experts=384, top_k=8))
     # forcing is honoured and the workspace follows the plan
     d = B.make_desc(num_tokens=16, hidden=256, intermediate=384, num_local_experts=8, top_k=2,
                     force_block_m=32, force_path=1)

@@ -73,10 +73,11 @@ def test_route_prep_skewed_and_local_share():
 # forward parity, every variant on the small gated workload
 # ---------------------------------------------------------------------------
 
-VARIANTS = [dict(force_path=2)] + [dict(force_path=1, force_block_m=bm) for bm in (16, 32, 64)]
+VARIANTS = ([dict(force_path=2)] + [dict(force_path=1, force_block_m=bm) for bm in (16, 32, 64)]
+            + [dict(force_path=1, force_splitk=sk) for sk in (1, 2)])
 
 
-@pytest.mark.parametrize("force", VARIANTS, ids=lambda f: "path{force_path}-bm{0}".format(f.get("force_block_m", 0), **f))
+@pytest.mark.parametrize("force", VARIANTS, ids=lambda f: "-".join(f"{k}{v}" for k, v in f.items()))
 def test_tiny_all_variants(force):
     wl = synth.WORKLOADS["tiny"]
     Wc, Wg = weights("tiny")
@@ -105,7 +106,13 @@ def test_configs_small_token_counts(name, T):
     ("relu2_skew", 8, dict(force_path=2)),
     ("relu2_skew", 32, dict(force_path=1, force_block_m=32)),
     ("deepseek_local", 16, dict(force_path=1, force_block_m=32)),
-    ("deepseek_local", 16, dict(force_path=1, force_block_m=16))])
+    ("deepseek_local", 16, dict(force_path=1, force_block_m=16)),
+    ("kimi_tp8", 32, dict(force_path=1, force_splitk=1)),
+    ("kimi_tp8", 32, dict(force_path=1, force_splitk=2)),
+    ("per_channel", 8, dict(force_path=1, force_splitk=1)),
+    ("relu2_skew", 32, dict(force_path=1, force_splitk=1)),
+    ("relu2_skew", 32, dict(force_path=1, force_splitk=2)),
+    ("deepseek_local", 16, dict(force_path=1, force_splitk=1))])
 def test_config_variants(name, T, force):
     wl = synth.WORKLOADS[name]
     Wc, Wg = weights(name)
@@ -211,7 +218,8 @@ def test_ragged_reduction_tails(per_channel, gated, dtype):
                       dtype=dtype, seed=5)
     Wc = synth.make_weights(wl, device="cpu")
     Wg = Wc.to("cuda")
-    for T, force in ((150, dict(force_path=1)), (40, dict(force_path=1)),
+    for T, force in ((150, dict(force_path=1, force_splitk=2)),
+                     (150, dict(force_path=1, force_splitk=1)), (40, dict(force_path=1)),
                      (40, dict(force_path=1, force_block_m=32)), (20, dict(force_path=2))):
         tc = tokens(wl, T)
         out = forward(wl, Wg, tc.to("cuda"), **force)

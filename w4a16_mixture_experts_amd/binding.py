@@ -26,12 +26,12 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
 class MoeDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_tokens", "hidden", "intermediate", "num_local_experts", "expert_offset", "top_k",
-        "group_size", "dtype", "act", "qlayout", "force_path", "force_block_m")]
+        "group_size", "dtype", "act", "qlayout", "force_path", "force_block_m", "force_splitk")]
 
 
 class MoePlan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("block_m", ctypes.c_int32),
-                ("k_slice", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("k_slice", ctypes.c_int32), ("splitk_chunks", ctypes.c_int32),
                 ("max_positions", ctypes.c_int64), ("max_tiles", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_size_t)]
 
@@ -105,12 +105,14 @@ def _dev(name: str, t: torch.Tensor, dtypes, device=None):
 def make_desc(*, num_tokens: int, hidden: int, intermediate: int, num_local_experts: int,
               top_k: int, expert_offset: int = 0, dtype=torch.bfloat16, gated: bool = True,
               per_channel: bool = False, group_size: int = 32, force_path: int = 0,
-              force_block_m: int = 0) -> MoeDesc:
-    """force_path: 0 auto, 1 grouped, 2 small batch; force_block_m: 0 or 16/32/64."""
+              force_block_m: int = 0, force_splitk: int = 0) -> MoeDesc:
+    """force_path: 0 auto, 1 grouped, 2 small batch; force_block_m: 0 or 16/32/64;
+    force_splitk: 0 auto, 1 split-K gate/up, 2 streaming gate/up (64-row tiles)."""
     return MoeDesc(num_tokens, hidden, intermediate, num_local_experts, expert_offset, top_k,
                    group_size, DT_FP16 if dtype == torch.float16 else DT_BF16,
                    ACT_SILU_GATED if gated else ACT_RELU2,
-                   Q_PER_CHANNEL if per_channel else Q_GROUP_K, force_path, force_block_m)
+                   Q_PER_CHANNEL if per_channel else Q_GROUP_K, force_path, force_block_m,
+                   force_splitk)
 
 
 def workspace_size(desc: MoeDesc) -> int:
@@ -136,7 +138,7 @@ def desc_for(wl, T: int, **force) -> MoeDesc:
 def moe_forward(x, w13_packed, w13_scales, w2_packed, w2_scales, topk_ids, topk_weights, *,
                 intermediate: int, num_local_experts: int, expert_offset: int = 0,
                 gated: bool = True, per_channel: bool = False, out=None, workspace=None,
-                force_path: int = 0, force_block_m: int = 0,
+                force_path: int = 0, force_block_m: int = 0, force_splitk: int = 0,
                 stream=None, stage_events=None) -> torch.Tensor:
     """Local W4A16 MoE forward: returns out [T, H] in x's dtype.
 
@@ -172,7 +174,7 @@ def moe_forward(x, w13_packed, w13_scales, w2_packed, w2_scales, topk_ids, topk_
     desc = make_desc(num_tokens=T, hidden=H, intermediate=I, num_local_experts=E,
                      top_k=topk_ids.shape[1], expert_offset=expert_offset, dtype=x.dtype,
                      gated=gated, per_channel=per_channel, force_path=force_path,
-                     force_block_m=force_block_m)
+                     force_block_m=force_block_m, force_splitk=force_splitk)
     nbytes = workspace_size(desc)
     if out is None:
         out = torch.empty(T, H, dtype=x.dtype, device=dev)
@@ -219,7 +221,7 @@ def prepare_routes(topk_ids: torch.Tensor, num_local_experts: int, expert_offset
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     srt = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
     slot = torch.empty(max(R, 1), dtype=torch.int32, device=dev)
-    desc = MoeDesc(T, 64, 64, E, expert_offset, K, 32, 0, 0, 0, 0, 0)
+    desc = MoeDesc(T, 64, 64, E, expert_offset, K, 32, 0, 0, 0, 0, 0, 0)
     _check(lib().w4a16_moe_prepare_routes(ctypes.byref(desc), _ptr(topk_ids), block_m,
                                           _ptr(counts), _ptr(offsets), _ptr(srt), cap,
                                           _ptr(slot), _stream(stream)))

@@ -12,6 +12,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <cmath>
 #include <string>
 
 #include "../../include/w4a16_moe.h"
@@ -39,10 +40,11 @@ struct Plan {
   int n_tiles_up = 0, n_tiles_down = 0, mode_up = 0;
   bool down_resident = false;  // grouped path: down GEMM with the tile's rows resident in LDS
   int col_steps = 0;
+  int splitk_S = 0, splitk_cb = 0;  // split-K gate/up chunks and blocks per chunk (0: off)
   int64_t R = 0, P = 0, MT = 0, items = 0;
   int N1 = 0;
   size_t off_counts = 0, off_offsets = 0, off_slot = 0, off_sorted = 0, off_tile = 0,
-         off_act = 0, off_y = 0, total = 0;
+         off_act = 0, off_y = 0, off_part = 0, total = 0;
 };
 
 w4a16_status_t check_desc(const w4a16_moe_desc_t* d) {
@@ -79,6 +81,8 @@ w4a16_status_t check_desc(const w4a16_moe_desc_t* d) {
     return fail(W4A16_ERR_INVALID_ARG, "desc.force_block_m: %d (0, 16, 32 or 64)", d->force_block_m);
   if (d->force_path < 0 || d->force_path > 2)
     return fail(W4A16_ERR_INVALID_ARG, "desc.force_path: %d (0, 1 or 2)", d->force_path);
+  if (d->force_splitk < 0 || d->force_splitk > 2)
+    return fail(W4A16_ERR_INVALID_ARG, "desc.force_splitk: %d (0, 1 or 2)", d->force_splitk);
   return W4A16_OK;
 }
 
@@ -130,6 +134,27 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
   const int cols_plain = tile64 ? w4moe::kTileColsPlain : w4moe::kWgColsPlain;
   pl.n_tiles_up = gated ? (I + cols_gated - 1) / cols_gated : (I + cols_plain - 1) / cols_plain;
   pl.n_tiles_down = (H + cols_plain - 1) / cols_plain;
+  // split-K gate/up when tiles are expected to hold few routes: the expected
+  // number of touched experts under uniform routing is E (1 - (1 - 1/E)^R)
+  if (tile64 && pl.R > 0) {
+    const double R = static_cast<double>(pl.R);
+    const double D = std::max(1.0, E * (1.0 - std::pow(1.0 - 1.0 / E, R)));
+    // measured crossover: split-K wins at ~1.4 routes per expert (Kimi shard,
+    // 32 tokens), the streaming kernel at ~5 (256 tokens)
+    bool use = R / D <= 3.0;
+    if (d->force_splitk == 1) use = true;
+    if (d->force_splitk == 2) use = false;
+    if (use) {
+      const int nblk = (H + 127) / 128;
+      // chunks of an even number of blocks (scales load per block pair)
+      const int cb_max = ((w4moe::kSplitkMaxLds / (16 * 2) - 8) / 128) & ~1;
+      const int64_t mt = std::max<int64_t>(pl.MT, 1);
+      int S = static_cast<int>(std::max<int64_t>((1024 + mt - 1) / mt, (nblk + cb_max - 1) / cb_max));
+      S = std::max(1, std::min(S, (nblk + 1) / 2));
+      pl.splitk_cb = std::min(cb_max, (((nblk + S - 1) / S) + 1) & ~1);
+      pl.splitk_S = (nblk + pl.splitk_cb - 1) / pl.splitk_cb;
+    }
+  }
   // short reductions: one workgroup per (tile, column chunk) keeps the tile's
   // activation rows in LDS and walks col_steps column tiles; chunks are sized
   // so that the tile capacity times the chunks fills the GPU about 8 times
@@ -158,6 +183,8 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
     pl.off_tile = take(sizeof(int32_t) * std::max<int64_t>(pl.MT, 1));
     pl.off_act = take(sizeof(uint16_t) * pl.P * I);
     pl.off_y = take(sizeof(uint16_t) * pl.P * H);
+    if (pl.splitk_S > 0)
+      pl.off_part = take(sizeof(float) * static_cast<size_t>(pl.splitk_S) * pl.R * pl.N1);
   }
   pl.total = off;
   return pl;
@@ -239,6 +266,7 @@ w4a16_status_t w4a16_moe_get_plan(const w4a16_moe_desc_t* desc, w4a16_moe_plan_t
   plan->path = pl.path;
   plan->block_m = pl.bm;
   plan->k_slice = pl.kslice;
+  plan->splitk_chunks = pl.splitk_S;
   plan->max_positions = pl.P;
   plan->max_tiles = pl.MT;
   plan->workspace_bytes = pl.total;
@@ -418,6 +446,19 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
     up.out = act;
     up.ldo = I;
     up.n_tiles = pl.n_tiles_up;
+    if (pl.splitk_S > 0) {
+      up.part = reinterpret_cast<float*>(ws + pl.off_part);
+      up.S = pl.splitk_S;
+      up.cb = pl.splitk_cb;
+      up.R = static_cast<int>(pl.R);
+      up.n_cols = pl.N1;
+      st = hip_status(w4moe::launch_up_splitk(up, desc->dtype, desc->qlayout,
+                                              static_cast<int>(pl.MT), stream),
+                      "gate/up GEMM launch");
+      if (st == W4A16_OK)
+        st = hip_status(w4moe::launch_splitk_act(up, desc->dtype, gated, pl.P, stream),
+                        "activation launch");
+    } else
     st = hip_status(pl.bm == w4moe::kTileRows
                         ? w4moe::launch_tile_gemm(up, desc->dtype, desc->qlayout, pl.mode_up,
                                                   static_cast<int>(pl.MT), stream)

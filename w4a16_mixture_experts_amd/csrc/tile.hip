@@ -43,6 +43,7 @@ constexpr int kAStride = 128 + 8;            // staged row stride (16 B padding)
 constexpr int kXcds = 8;
 constexpr int kWRing = 2;                    // weight blocks in registers (1 in flight)
 constexpr int kNsub = 2;                     // 16-row weight subtiles per wave
+constexpr int kSplitkRing = 4;               // split-K: weight blocks in registers
 
 template <int DT>
 __device__ __forceinline__ float scale_lo(uint32_t pair) { return H16<DT>::to_f32(pair & 0xffffu); }
@@ -50,14 +51,14 @@ template <int DT>
 __device__ __forceinline__ float scale_hi(uint32_t pair) { return H16<DT>::to_f32(pair >> 16); }
 
 // acc += s * t for every output of a group (s: this lane's column scale)
-template <int NMS>
-__device__ __forceinline__ void scale_accumulate(f32x4 (&acc)[NMS][kNsub],
-                                                 const f32x4 (&t)[NMS][kNsub],
-                                                 const float (&sc)[kNsub]) {
+template <int NMS, int NSUB>
+__device__ __forceinline__ void scale_accumulate(f32x4 (&acc)[NMS][NSUB],
+                                                 const f32x4 (&t)[NMS][NSUB],
+                                                 const float (&sc)[NSUB]) {
 #pragma unroll
   for (int ms = 0; ms < NMS; ++ms)
 #pragma unroll
-    for (int s = 0; s < kNsub; ++s)
+    for (int s = 0; s < NSUB; ++s)
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[ms][s][i] = fmaf(sc[s], t[ms][s][i], acc[ms][s][i]);
 }
@@ -70,17 +71,26 @@ template <int LAYOUT>
 struct WBlk {
   u32x4 d;
   u32x4 d2;                      // per-channel only
-  uint32_t s0, s1;
+  uint32_t s0, s1;               // scales of this block (group layout: 4 groups)
+  uint32_t s2, s3;               // group layout, first block of a pair: the next block's
 };
 
+// How a block's group scales arrive.  Each row's scales of a 128-block are 8
+// bytes; fetched per block, every scale load of a wave touches 16 cache lines
+// for 128 useful bytes, and that dominated the weight stream.  So blocks come
+// in pairs: the first block of a pair loads 16 bytes (both blocks' scales) and
+// hands the second half to its partner (pass_scales).
+enum : int { SC_SINGLE = 0, SC_PAIR_FIRST = 1, SC_PAIR_SECOND = 2 };
+
 // One expert's packed weights and scales (wave-uniform), and where a wave's
-// two subtiles sit in them (per lane).
+// NSUB subtiles sit in them (per lane).
 struct WExpert {
   __amdgpu_buffer_rsrc_t rw, rs;
 };
+template <int NSUB = kNsub>
 struct WSrc {
-  uint32_t boff[kNsub], soff[kNsub];
-  bool on[kNsub];
+  uint32_t boff[NSUB], soff[NSUB];
+  bool on[NSUB];
 };
 
 __device__ __forceinline__ WExpert make_wexpert(const GemmParams& p, int e) {
@@ -92,17 +102,17 @@ __device__ __forceinline__ WExpert make_wexpert(const GemmParams& p, int e) {
   return x;
 }
 
-template <int LAYOUT>
-__device__ __forceinline__ WSrc make_wsrc(const GemmParams& p, const int (&wrow)[kNsub],
-                                          const bool (&on)[kNsub]) {
+template <int LAYOUT, int NSUB = kNsub>
+__device__ __forceinline__ WSrc<NSUB> make_wsrc(int K, const int (&wrow)[NSUB],
+                                                const bool (&on)[NSUB]) {
   constexpr bool GROUP = LAYOUT == Q_GROUP_K;
-  WSrc w;
+  WSrc<NSUB> w;
 #pragma unroll
-  for (int s = 0; s < kNsub; ++s) {
+  for (int s = 0; s < NSUB; ++s) {
     w.on[s] = on[s];
-    w.boff[s] = GROUP ? static_cast<uint32_t>(wrow[s]) * (p.K >> 1)
-                      : static_cast<uint32_t>(wrow[s] >> 1) * p.K;
-    w.soff[s] = GROUP ? 2u * static_cast<uint32_t>(wrow[s]) * (p.K >> 5)
+    w.boff[s] = GROUP ? static_cast<uint32_t>(wrow[s]) * (K >> 1)
+                      : static_cast<uint32_t>(wrow[s] >> 1) * K;
+    w.soff[s] = GROUP ? 2u * static_cast<uint32_t>(wrow[s]) * (K >> 5)
                       : 2u * static_cast<uint32_t>(wrow[s] & ~1);
   }
   return w;
@@ -110,18 +120,24 @@ __device__ __forceinline__ WSrc make_wsrc(const GemmParams& p, const int (&wrow)
 
 // Loads of block k0 (reads nothing past the reduction or the output rows:
 // those lanes get zeros, scales included).
-template <int LAYOUT>
-__device__ __forceinline__ void load_wblk(const WExpert& x, const WSrc& w, int k0, int K, int g,
-                                          WBlk<LAYOUT> (&b)[kNsub]) {
+template <int LAYOUT, int NSUB = kNsub, int SC = SC_SINGLE>
+__device__ __forceinline__ void load_wblk(const WExpert& x, const WSrc<NSUB>& w, int k0, int K,
+                                          int g, WBlk<LAYOUT> (&b)[NSUB]) {
   const int ng = k0 < K ? min(4, (K - k0) >> 5) : 0;
 #pragma unroll
-  for (int s = 0; s < kNsub; ++s) {
+  for (int s = 0; s < NSUB; ++s) {
     const bool ok = w.on[s] && g < ng;
     if constexpr (LAYOUT == Q_GROUP_K) {
       b[s].d = bload16(x.rw, w.boff[s] + (k0 >> 1) + 16 * g, ok);
       const uint32_t so = w.soff[s] + 2u * (k0 >> 5);
-      b[s].s0 = bload4(x.rs, so, w.on[s] && ng > 0);
-      b[s].s1 = bload4(x.rs, so + 4, w.on[s] && ng > 2);
+      if constexpr (SC == SC_PAIR_FIRST) {
+        // groups past the reduction in the window only ever meet A zeros
+        const u32x4 v = bload16(x.rs, so, w.on[s] && ng > 0);
+        b[s].s0 = v[0]; b[s].s1 = v[1]; b[s].s2 = v[2]; b[s].s3 = v[3];
+      } else if constexpr (SC == SC_SINGLE) {
+        b[s].s0 = bload4(x.rs, so, w.on[s] && ng > 0);
+        b[s].s1 = bload4(x.rs, so + 4, w.on[s] && ng > 2);
+      }
     } else {
       b[s].d = bload16(x.rw, w.boff[s] + k0 + 32 * g, ok);
       b[s].d2 = bload16(x.rw, w.boff[s] + k0 + 32 * g + 16, ok);
@@ -131,15 +147,27 @@ __device__ __forceinline__ void load_wblk(const WExpert& x, const WSrc& w, int k
   }
 }
 
+template <int LAYOUT, int NSUB>
+__device__ __forceinline__ void pass_scales(const WBlk<LAYOUT> (&first)[NSUB],
+                                            WBlk<LAYOUT> (&second)[NSUB]) {
+  if constexpr (LAYOUT == Q_GROUP_K) {
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      second[s].s0 = first[s].s2;
+      second[s].s1 = first[s].s3;
+    }
+  }
+}
+
 // acc += A[rows 0..16*NMS) x deq(W block)^T for one 128-block.  `sa` points
 // at LDS element (row 0, first column of the block), rows `stride` apart.
 // All A fragments are read first (LDS latency paid once per block); the
 // correction -1.5 * sum(a) of each group comes from one MFMA against a
 // constant operand.
-template <int DT, int LAYOUT, int NMS, bool UPFRONT = true>
+template <int DT, int LAYOUT, int NMS, bool UPFRONT = true, int NSUB = kNsub>
 __device__ __forceinline__ void mma_block(const uint16_t* sa, int stride,
-                                          const WBlk<LAYOUT> (&wb)[kNsub],
-                                          f32x4 (&acc)[NMS][kNsub], int c, int g, int par) {
+                                          const WBlk<LAYOUT> (&wb)[NSUB],
+                                          f32x4 (&acc)[NMS][NSUB], int c, int g, int par) {
   using T = H16<DT>;
   constexpr bool GROUP = LAYOUT == Q_GROUP_K;
   // scheduling fences keep the compiler from hoisting the LDS reads of later
@@ -159,9 +187,9 @@ __device__ __forceinline__ void mma_block(const uint16_t* sa, int stride,
       for (int ms = 0; ms < NMS; ++ms) af[ms][j] = frag(ms, j);
   }
   // transpose so that MFMA j sees group j
-  uint32_t d[kNsub][8];
+  uint32_t d[NSUB][8];
 #pragma unroll
-  for (int s = 0; s < kNsub; ++s) {
+  for (int s = 0; s < NSUB; ++s) {
     d[s][0] = wb[s].d[0]; d[s][1] = wb[s].d[1]; d[s][2] = wb[s].d[2]; d[s][3] = wb[s].d[3];
     if constexpr (GROUP) {
       transpose_rows4(d[s][0], d[s][1], d[s][2], d[s][3]);
@@ -173,10 +201,10 @@ __device__ __forceinline__ void mma_block(const uint16_t* sa, int stride,
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    u32x4 bop[kNsub];
-    float sc[kNsub];
+    u32x4 bop[NSUB];
+    float sc[NSUB];
 #pragma unroll
-    for (int s = 0; s < kNsub; ++s) {
+    for (int s = 0; s < NSUB; ++s) {
       if constexpr (GROUP) {
         bop[s] = nibbles_to_h16<DT>(d[s][j]);
         const uint32_t pr = (j < 2) ? wb[s].s0 : wb[s].s1;
@@ -188,15 +216,15 @@ __device__ __forceinline__ void mma_block(const uint16_t* sa, int stride,
       // no mask needed: a group past the reduction or a column past the
       // output reads scale 0 (out-of-range load) and A rows of zeros
     }
-    f32x4 t[NMS][kNsub];
+    f32x4 t[NMS][NSUB];
 #pragma unroll
     for (int ms = 0; ms < NMS; ++ms) {
       const u32x4 a = UPFRONT ? af[ms][j] : frag(ms, j);
       const f32x4 corr = T::mfma(a, bconst, fzero);
 #pragma unroll
-      for (int s = 0; s < kNsub; ++s) t[ms][s] = T::mfma(a, bop[s], corr);
+      for (int s = 0; s < NSUB; ++s) t[ms][s] = T::mfma(a, bop[s], corr);
     }
-    scale_accumulate<NMS>(acc, t, sc);
+    scale_accumulate<NMS, NSUB>(acc, t, sc);
     if constexpr (!UPFRONT) __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -300,7 +328,7 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, const int row_base
   bool on[kNsub];
   wave_columns<MODE>(p, nt, w, c, col, wrow, on);
   const WExpert wx = make_wexpert(p, e);
-  const WSrc ws = make_wsrc<LAYOUT>(p, wrow, on);
+  const WSrc<> ws = make_wsrc<LAYOUT>(p.K, wrow, on);
 
   // staging role of this thread: row st_row, kVals consecutive values of each
   // 128-block starting at kVals * st_c
@@ -345,23 +373,27 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, const int row_base
   u32x4 ar[2][kChunks];
   load_a(0, ar[0]);
   load_a(128, ar[1]);
-#pragma unroll
-  for (int i = 0; i < kWRing - 1; ++i) load_wblk<LAYOUT>(wx, ws, 128 * i, p.K, g, wr[i]);
+  static_assert(kWRing == 2, "blocks pair up with the ring (scales per block pair)");
+  load_wblk<LAYOUT, kNsub, SC_PAIR_FIRST>(wx, ws, 0, p.K, g, wr[0]);
   store_a(0, ar[0]);
   load_a(256, ar[0]);
   __syncthreads();
 
   const int nblk = (p.K + 127) >> 7;
-  for (int blk0 = 0; blk0 < nblk; blk0 += kWRing) {
-#pragma unroll
-    for (int u = 0; u < kWRing; ++u) {
-      const int b = blk0 + u;
-      load_wblk<LAYOUT>(wx, ws, 128 * (b + kWRing - 1), p.K, g, wr[(u + kWRing - 1) % kWRing]);
-      if (b < nblk) mma_block<DT, LAYOUT, NMS>(&s_a[b & 1][0][0], kAStride, wr[u], acc, c, g, par);
-      store_a((b + 1) & 1, ar[(u + 1) & 1]);
-      load_a(128 * (b + 3), ar[(u + 1) & 1]);
-      __syncthreads();
-    }
+  for (int blk0 = 0; blk0 < nblk; blk0 += 2) {
+    // even block blk0 (first of its pair) in wr[0], odd block in wr[1]
+    load_wblk<LAYOUT, kNsub, SC_PAIR_SECOND>(wx, ws, 128 * (blk0 + 1), p.K, g, wr[1]);
+    mma_block<DT, LAYOUT, NMS>(&s_a[0][0][0], kAStride, wr[0], acc, c, g, par);
+    pass_scales<LAYOUT, kNsub>(wr[0], wr[1]);
+    store_a(1, ar[1]);
+    load_a(128 * (blk0 + 3), ar[1]);
+    __syncthreads();
+    load_wblk<LAYOUT, kNsub, SC_PAIR_FIRST>(wx, ws, 128 * (blk0 + 2), p.K, g, wr[0]);
+    if (blk0 + 1 < nblk)
+      mma_block<DT, LAYOUT, NMS>(&s_a[1][0][0], kAStride, wr[1], acc, c, g, par);
+    store_a(0, ar[0]);
+    load_a(128 * (blk0 + 4), ar[0]);
+    __syncthreads();
   }
   store_outputs<DT, MODE, NMS>(p, row_base, acc, col, on, g, valid_rows<NMS>(p, row_base, g));
 }
@@ -441,15 +473,17 @@ __device__ __forceinline__ void down_resident_run(const GemmParams& p, const int
       col[k] = n0 + 16 * k + c;
       on[k] = st < step_end && n0 + 16 * k < p.n_cols;
     }
-    return make_wsrc<LAYOUT>(p, col, on);
+    return make_wsrc<LAYOUT>(p.K, col, on);
   };
   // two register sets: the next block's weights are requested while the
   // current block is computed
   auto load_blk = [&](int st, int kb, WBlk<LAYOUT> (&wb)[kNsub]) {
     int col[kNsub];
     bool on[kNsub];
-    const WSrc ws = step_src(st, col, on);
-    load_wblk<LAYOUT>(wx, ws, 128 * kb, p.K, g, wb);
+    const WSrc<> ws = step_src(st, col, on);
+    if constexpr (NKB == 1) load_wblk<LAYOUT, kNsub, SC_SINGLE>(wx, ws, 128 * kb, p.K, g, wb);
+    else if (kb == 0) load_wblk<LAYOUT, kNsub, SC_PAIR_FIRST>(wx, ws, 0, p.K, g, wb);
+    else load_wblk<LAYOUT, kNsub, SC_PAIR_SECOND>(wx, ws, 128, p.K, g, wb);
   };
   f32x4 acc[NMS][kNsub];
   auto zero_acc = [&]() {
@@ -473,6 +507,7 @@ __device__ __forceinline__ void down_resident_run(const GemmParams& p, const int
       load_blk(st, 1, w1);
       zero_acc();
       mma_block<DT, LAYOUT, NMS, false>(s_ar, S, w0, acc, c, g, par);
+      pass_scales<LAYOUT, kNsub>(w0, w1);
       load_blk(st + 1, 0, w0);
       mma_block<DT, LAYOUT, NMS, false>(s_ar + 128, S, w1, acc, c, g, par);
       store_step(st);
@@ -513,6 +548,192 @@ down_resident_kernel(const GemmParams p) {
     case 3: down_resident_run<DT, LAYOUT, 3, NKB>(p, row_base, e, chunk, s_ar); break;
     default: down_resident_run<DT, LAYOUT, 4, NKB>(p, row_base, e, chunk, s_ar); break;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K gate/up GEMM for tiles of few rows ([P1] Modification: small-batch
+// split-K).  Workgroup (tile, K chunk): the tile's x rows over the chunk stay
+// in LDS (one 16-row subtile at a time), and each wave streams its NSUB
+// subtiles of every weight row of the chunk, with no barrier inside the
+// stream.  FP32 partial pre-activations go to part[chunk][route][N1]; the
+// activation kernel below sums the chunks in order.
+// ---------------------------------------------------------------------------
+
+template <int DT, int LAYOUT, int NSUB>
+__global__ void __launch_bounds__(kTileThreads)
+up_splitk_kernel(const GemmParams p) {
+  extern __shared__ uint16_t s_x[];   // [16][cb * 128 + 8]
+  const int mt = blockIdx.x / p.S;
+  const int kc = blockIdx.x % p.S;
+  const int row_base = mt * kTileRows;
+  if (row_base >= p.offsets[p.E]) return;  // whole workgroup: tile past the padded total
+  const int nblk = (p.K + 127) >> 7;
+  const int b0 = kc * p.cb;
+  const int b1 = min(nblk, b0 + p.cb);
+  if (b0 >= b1) return;
+  const int kend = min(p.K, 128 * b1);
+  const int nms = active_subtiles(p, row_base);
+  const int e = p.tile_expert[mt];
+  const int stride = p.cb * 128 + 8;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int c = lane & 15, g = lane >> 4, par = c & 1;
+  const WExpert wx = make_wexpert(p, e);
+  const auto xr = make_rsrc(p.a, p.a_bytes);
+  constexpr int kPassRows = kTileWaves * 16 * NSUB;  // weight rows per column pass
+
+  for (int rp = 0; rp < nms; ++rp) {
+    if (rp > 0) __syncthreads();  // the previous subtile's rows are no longer read
+    // stage x rows of subtile rp over the chunk, in A operand order
+    const int nch = (b1 - b0) * 16;
+    for (int idx = tid; idx < 16 * nch; idx += kTileThreads) {
+      const int row = idx / nch, ch = idx % nch;
+      const int r = p.sorted[row_base + 16 * rp + row];
+      const bool ok = r >= 0 && 128 * b0 + 8 * ch < p.K;
+      const u32x4 v = bload16(xr, 2u * static_cast<uint32_t>((ok ? r / p.top_k : 0) * p.lda +
+                                                             128 * b0 + 8 * ch), ok);
+      *reinterpret_cast<u32x4*>(s_x + row * stride + 8 * ch) = permute_a(v);
+    }
+    __syncthreads();
+    int rts[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rts[i] = p.sorted[row_base + 16 * rp + 4 * g + i];
+
+    for (int n0 = 0; n0 < p.n_cols; n0 += kPassRows) {
+      int wrow[NSUB];
+      bool on[NSUB];
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) {
+        const int r0 = n0 + (w * NSUB + s) * 16;
+        wrow[s] = r0 + c;
+        on[s] = r0 < p.n_cols;
+      }
+      const WSrc<NSUB> ws = make_wsrc<LAYOUT, NSUB>(p.K, wrow, on);
+      f32x4 acc[1][NSUB];
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) acc[0][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // ring of kSplitkRing register sets: block b + kSplitkRing - 1 is
+      // requested while block b is computed (loads past the chunk are masked)
+      // (b0 is even: blocks pair up for their scales, see SC_PAIR_FIRST)
+      static_assert(kSplitkRing % 2 == 0, "block pairs must not straddle the ring");
+      WBlk<LAYOUT> wr[kSplitkRing][NSUB];
+      // block b0 + i into wr[slot]; `first` = i is even (a constant after unrolling)
+      auto load_i = [&](int i, int slot, bool first) {
+        if (first)
+          load_wblk<LAYOUT, NSUB, SC_PAIR_FIRST>(wx, ws, 128 * (b0 + i), kend, g, wr[slot]);
+        else
+          load_wblk<LAYOUT, NSUB, SC_PAIR_SECOND>(wx, ws, 128 * (b0 + i), kend, g, wr[slot]);
+      };
+#pragma unroll
+      for (int i = 0; i < kSplitkRing - 1; ++i) load_i(i, i, i % 2 == 0);
+      for (int b = b0; b < b1; b += kSplitkRing) {
+#pragma unroll
+        for (int u = 0; u < kSplitkRing; ++u) {
+          load_i(b - b0 + u + kSplitkRing - 1, (u + kSplitkRing - 1) % kSplitkRing,
+                 (u + kSplitkRing - 1) % 2 == 0);
+          if (b + u < b1)
+            mma_block<DT, LAYOUT, 1, true, NSUB>(s_x + 128 * (b + u - b0), stride, wr[u], acc, c,
+                                                 g, par);
+          if (u % 2 == 0) pass_scales<LAYOUT, NSUB>(wr[u], wr[u + 1]);
+        }
+      }
+      // FP32 partials of valid rows: lane (c, g) holds rows 4g + i, row wrow[s]
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (rts[i] < 0) continue;
+        float* prow = p.part + (static_cast<int64_t>(kc) * p.R + rts[i]) * p.n_cols;
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s)
+          if (on[s]) prow[wrow[s]] = 16.0f * acc[0][s][i];
+      }
+    }
+  }
+}
+
+// act[p] from the split-K partials of route sorted[p]: the chunks summed in
+// order 0..S-1, then SiLU(gate) * up (or ReLU^2), one 16-bit rounding, stored
+// in A operand order.  One thread per 8 consecutive activation columns.
+template <int DT, bool GATED>
+__global__ void __launch_bounds__(256)
+splitk_act_kernel(const GemmParams p) {
+  using T = H16<DT>;
+  const int I = p.ldo;
+  const int per_row = I / 8;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int pos = static_cast<int>(idx / per_row);
+  const int i0 = 8 * static_cast<int>(idx % per_row);
+  if (pos >= p.offsets[p.E]) return;
+  const int r = p.sorted[pos];
+  if (r < 0) return;  // padding rows are never read
+  float h[8], u[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) h[j] = u[j] = 0.0f;
+  for (int kc = 0; kc < p.S; ++kc) {
+    const float* row = p.part + (static_cast<int64_t>(kc) * p.R + r) * p.n_cols;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(row + i0);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(row + i0 + 4);
+    h[0] += a[0]; h[1] += a[1]; h[2] += a[2]; h[3] += a[3];
+    h[4] += b[0]; h[5] += b[1]; h[6] += b[2]; h[7] += b[3];
+    if constexpr (GATED) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(row + I + i0);
+      const f32x4 y = *reinterpret_cast<const f32x4*>(row + I + i0 + 4);
+      u[0] += x[0]; u[1] += x[1]; u[2] += x[2]; u[3] += x[3];
+      u[4] += y[0]; u[5] += y[1]; u[6] += y[2]; u[7] += y[3];
+    }
+  }
+  uint16_t o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float a;
+    if constexpr (GATED) a = silu(h[j]) * u[j];
+    else { const float z = fmaxf(h[j], 0.0f); a = z * z; }
+    o[a_pos(j)] = T::from_f32(a);
+  }
+  u32x4 v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = static_cast<uint32_t>(o[2 * q]) | (static_cast<uint32_t>(o[2 * q + 1]) << 16);
+  *reinterpret_cast<u32x4*>(p.out + static_cast<int64_t>(pos) * I + i0) = v;
+}
+
+template <typename F>
+static hipError_t allow_lds_tile(F* kernel, size_t lds) {
+  if (lds <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+}
+
+template <int DT, int LAYOUT>
+static hipError_t launch_splitk_dl(const GemmParams& p, int max_tiles, hipStream_t st) {
+  const size_t lds = sizeof(uint16_t) * 16 * (static_cast<size_t>(p.cb) * 128 + 8);
+  const hipError_t err = allow_lds_tile(up_splitk_kernel<DT, LAYOUT, kSplitkNsub>, lds);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((up_splitk_kernel<DT, LAYOUT, kSplitkNsub>), dim3(max_tiles * p.S),
+                     dim3(kTileThreads), lds, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_up_splitk(const GemmParams& p, int dtype, int layout, int max_tiles,
+                            hipStream_t stream) {
+  if (p.S < 1 || p.cb < 1 || 16 * (p.cb * 128 + 8) * 2 > kSplitkMaxLds) return hipErrorInvalidValue;
+  if (dtype == DT_BF16)
+    return layout == Q_GROUP_K ? launch_splitk_dl<DT_BF16, Q_GROUP_K>(p, max_tiles, stream)
+                               : launch_splitk_dl<DT_BF16, Q_PER_CHANNEL>(p, max_tiles, stream);
+  return layout == Q_GROUP_K ? launch_splitk_dl<DT_FP16, Q_GROUP_K>(p, max_tiles, stream)
+                             : launch_splitk_dl<DT_FP16, Q_PER_CHANNEL>(p, max_tiles, stream);
+}
+
+hipError_t launch_splitk_act(const GemmParams& p, int dtype, bool gated, int64_t max_positions,
+                             hipStream_t stream) {
+  if (p.ldo % 8 != 0) return hipErrorInvalidValue;
+  const int64_t threads = max_positions * (p.ldo / 8);
+  const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+  if (dtype == DT_BF16) {
+    if (gated) hipLaunchKernelGGL((splitk_act_kernel<DT_BF16, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((splitk_act_kernel<DT_BF16, false>), grid, dim3(256), 0, stream, p);
+  } else {
+    if (gated) hipLaunchKernelGGL((splitk_act_kernel<DT_FP16, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((splitk_act_kernel<DT_FP16, false>), grid, dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
 }
 
 template <int DT, int LAYOUT, int MODE>
