@@ -82,7 +82,7 @@ KERNEL_PREFIX = "w4moe::"
 
 
 def kernel_name(wl, plan, stage):
-    """Kernel a stage launches, spelled as the profiler prints it (w/o arguments)."""
+    """Kernel(s) a stage launches, spelled as the profiler prints them (w/o arguments)."""
     import torch
 
     dt = 1 if wl.dtype == torch.float16 else 0
@@ -96,8 +96,14 @@ def kernel_name(wl, plan, stage):
         return f"combine_kernel<{dt}>"
     if plan.block_m != 64:
         return f"block_m {plan.block_m} {stage}"
-    mode = 2 if stage == "down_gemm" else (0 if wl.gated else 1)
-    return f"tile_gemm_kernel<{dt}, {lay}, {mode}>"
+    if stage == "gate_up_gemm":
+        if plan.splitk_chunks:
+            return (f"up_splitk_kernel<{dt}, {lay}, 2> + "
+                    f"splitk_act_kernel<{dt}, {'true' if wl.gated else 'false'}>")
+        return f"tile_gemm_kernel<{dt}, {lay}, {0 if wl.gated else 1}>"
+    if wl.inter <= 256:   # the reduction fits the resident down kernel
+        return f"down_resident_kernel<{dt}, {lay}, {1 if wl.inter <= 128 else 2}>"
+    return f"tile_gemm_kernel<{dt}, {lay}, 2>"
 
 
 def measured_traffic(kname, tokens):

@@ -162,6 +162,17 @@ def test_buffer_offset_limits():
     assert B.workspace_size(d) > 0
 
 
+def test_small_batch_path_only_for_short_intermediate():
+    kimi = dict(hidden=7168, intermediate=256, num_local_experts=384, top_k=8)
+    assert B.get_plan(B.make_desc(num_tokens=1, **kimi)).path == 2
+    assert B.get_plan(B.make_desc(num_tokens=8, **kimi)).path == 2
+    # DeepSeek-like local share (I = 2048): the grouped path even for 1 token,
+    # with the split-K gate/up spread over column chunks
+    ds = dict(hidden=7168, intermediate=2048, num_local_experts=32, top_k=8)
+    p = B.get_plan(B.make_desc(num_tokens=1, **ds))
+    assert p.path == 1 and p.splitk_chunks > 0
+
+
 def test_small_batch_path_limits():
     # more than 64 routes (one wave's ballot) cannot take the small-batch path
     d = B.make_desc(num_tokens=9, hidden=256, intermediate=384, num_local_experts=8, top_k=8,

@@ -112,7 +112,9 @@ def test_configs_small_token_counts(name, T):
     ("per_channel", 8, dict(force_path=1, force_splitk=1)),
     ("relu2_skew", 32, dict(force_path=1, force_splitk=1)),
     ("relu2_skew", 32, dict(force_path=1, force_splitk=2)),
-    ("deepseek_local", 16, dict(force_path=1, force_splitk=1))])
+    ("deepseek_local", 16, dict(force_path=1, force_splitk=1)),
+    ("deepseek_local", 1, dict(force_path=2)),
+    ("per_channel", 8, dict(force_path=2))])
 def test_config_variants(name, T, force):
     wl = synth.WORKLOADS[name]
     Wc, Wg = weights(name)

@@ -41,6 +41,7 @@ struct Plan {
   bool down_resident = false;  // grouped path: down GEMM with the tile's rows resident in LDS
   int col_steps = 0;
   int splitk_S = 0, splitk_cb = 0;  // split-K gate/up chunks and blocks per chunk (0: off)
+  int splitk_nc = 0, splitk_passes = 0;  // column chunks, column passes per chunk
   int64_t R = 0, P = 0, MT = 0, items = 0;
   int N1 = 0;
   size_t off_counts = 0, off_offsets = 0, off_slot = 0, off_sorted = 0, off_tile = 0,
@@ -107,8 +108,12 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
              ((down_blocks + w4moe::kDecDownSliceBlocks - 1) / w4moe::kDecDownSliceBlocks);
 
   if (d->force_path) pl.path = d->force_path;
+  // the small-batch down kernel stages every route's pre-activations per
+  // 32-column workgroup: measured faster than the grouped path for 1-8 tokens
+  // when top_k * I is small (the I=256 top-8 shard, the I=1408 top-4
+  // per-channel model), several times slower for the I=2048 top-8 share
   else pl.path = (pl.R <= w4moe::kSmallMaxRoutes && pl.items <= w4moe::kDecMaxItems &&
-                  H <= 8 * w4moe::kSmallMaxSlice &&
+                  H <= 8 * w4moe::kSmallMaxSlice && static_cast<int64_t>(K) * I <= 8192 &&
                   static_cast<int64_t>(K) * I <= w4moe::kDecActLoads * w4moe::kDecThreadsAll * 8)
                      ? 2 : 1;
 
@@ -153,6 +158,14 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
       S = std::max(1, std::min(S, (nblk + 1) / 2));
       pl.splitk_cb = std::min(cb_max, (((nblk + S - 1) / S) + 1) & ~1);
       pl.splitk_S = (nblk + pl.splitk_cb - 1) / pl.splitk_cb;
+      // column chunks so that even a single touched expert spreads over the
+      // GPU (the tile capacity overcounts tiles when few routes are local)
+      const int passes = (pl.N1 + w4moe::kSplitkPassRows - 1) / w4moe::kSplitkPassRows;
+      const int64_t wgs = mt * pl.splitk_S;
+      const int nc = static_cast<int>(
+          std::min<int64_t>(passes, std::max<int64_t>(1, (1024 + wgs - 1) / wgs)));
+      pl.splitk_passes = (passes + nc - 1) / nc;
+      pl.splitk_nc = (passes + pl.splitk_passes - 1) / pl.splitk_passes;
     }
   }
   // short reductions: one workgroup per (tile, column chunk) keeps the tile's
@@ -452,11 +465,14 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
       up.cb = pl.splitk_cb;
       up.R = static_cast<int>(pl.R);
       up.n_cols = pl.N1;
+      up.slot = slot;
+      up.n_tiles = pl.splitk_nc;
+      up.col_steps = pl.splitk_passes;
       st = hip_status(w4moe::launch_up_splitk(up, desc->dtype, desc->qlayout,
                                               static_cast<int>(pl.MT), stream),
                       "gate/up GEMM launch");
       if (st == W4A16_OK)
-        st = hip_status(w4moe::launch_splitk_act(up, desc->dtype, gated, pl.P, stream),
+        st = hip_status(w4moe::launch_splitk_act(up, desc->dtype, gated, stream),
                         "activation launch");
     } else
     st = hip_status(pl.bm == w4moe::kTileRows

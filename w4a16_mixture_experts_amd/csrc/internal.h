@@ -38,13 +38,14 @@ struct GemmParams {
   int bm;
   uint16_t* out;              // UP: act [P][ldo]; DOWN: Y [P][ldo]
   int ldo;
-  int n_tiles;                // column tiles (resident down kernel: column chunks)
-  int col_steps;              // resident down kernel: 256-column steps per chunk
+  int n_tiles;                // column tiles (resident down / split-K: column chunks)
+  int col_steps;              // resident down / split-K: column passes per chunk
   // split-K gate/up (tiles of few rows)
   float* part;                // [S][R][n_cols] FP32 partial pre-activations
   int S;                      // reduction chunks
   int cb;                     // 128-blocks per chunk
   int R;                      // routes (T*K)
+  const int32_t* slot;        // [R] route -> position, -1 for invalid routes
 };
 
 // small-batch path
@@ -140,13 +141,13 @@ hipError_t launch_grouped_gemm(const GemmParams& p, int dtype, int layout, int m
 // 64-row expert tiles (route positions), LDS-staged activations
 constexpr int kResidentK = 256;      // reduction the resident down kernel holds in LDS
 constexpr int kSplitkNsub = 2;       // 16-row weight subtiles per wave in the split-K kernel
+constexpr int kSplitkPassRows = kTileWaves * 16 * kSplitkNsub;  // weight rows per column pass
 constexpr int kSplitkMaxLds = 78 * 1024;   // two workgroups per CU
 hipError_t launch_up_splitk(const GemmParams& p, int dtype, int layout, int max_tiles,
                             hipStream_t stream);
 // act rows from split-K partials (GemmParams: part, S, R, n_cols = N1, ldo = I,
-// sorted, offsets, E, out = act)
-hipError_t launch_splitk_act(const GemmParams& p, int dtype, bool gated, int64_t max_positions,
-                             hipStream_t stream);
+// slot, out = act)
+hipError_t launch_splitk_act(const GemmParams& p, int dtype, bool gated, hipStream_t stream);
 hipError_t launch_down_resident(const GemmParams& p, int dtype, int layout, int max_tiles,
                                 hipStream_t stream);
 hipError_t launch_tile_gemm(const GemmParams& p, int dtype, int layout, int mode, int max_tiles,

@@ -563,8 +563,11 @@ template <int DT, int LAYOUT, int NSUB>
 __global__ void __launch_bounds__(kTileThreads)
 up_splitk_kernel(const GemmParams p) {
   extern __shared__ uint16_t s_x[];   // [16][cb * 128 + 8]
-  const int mt = blockIdx.x / p.S;
-  const int kc = blockIdx.x % p.S;
+  // workgroup = (tile, reduction chunk, column chunk of p.col_steps passes)
+  const int nchunk = p.n_tiles;
+  const int mt = blockIdx.x / (p.S * nchunk);
+  const int kc = (blockIdx.x / nchunk) % p.S;
+  const int cc = blockIdx.x % nchunk;
   const int row_base = mt * kTileRows;
   if (row_base >= p.offsets[p.E]) return;  // whole workgroup: tile past the padded total
   const int nblk = (p.K + 127) >> 7;
@@ -598,7 +601,8 @@ up_splitk_kernel(const GemmParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) rts[i] = p.sorted[row_base + 16 * rp + 4 * g + i];
 
-    for (int n0 = 0; n0 < p.n_cols; n0 += kPassRows) {
+    const int n_end = min(p.n_cols, (cc + 1) * p.col_steps * kPassRows);
+    for (int n0 = cc * p.col_steps * kPassRows; n0 < n_end; n0 += kPassRows) {
       int wrow[NSUB];
       bool on[NSUB];
 #pragma unroll
@@ -649,7 +653,7 @@ up_splitk_kernel(const GemmParams p) {
   }
 }
 
-// act[p] from the split-K partials of route sorted[p]: the chunks summed in
+// act[slot[r]] for route r from its split-K partials: the chunks summed in
 // order 0..S-1, then SiLU(gate) * up (or ReLU^2), one 16-bit rounding, stored
 // in A operand order.  One thread per 8 consecutive activation columns.
 template <int DT, bool GATED>
@@ -659,11 +663,11 @@ splitk_act_kernel(const GemmParams p) {
   const int I = p.ldo;
   const int per_row = I / 8;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int pos = static_cast<int>(idx / per_row);
+  const int r = static_cast<int>(idx / per_row);
   const int i0 = 8 * static_cast<int>(idx % per_row);
-  if (pos >= p.offsets[p.E]) return;
-  const int r = p.sorted[pos];
-  if (r < 0) return;  // padding rows are never read
+  if (r >= p.R) return;
+  const int pos = p.slot[r];
+  if (pos < 0) return;  // invalid route: no position, nothing reads it
   float h[8], u[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) h[j] = u[j] = 0.0f;
@@ -706,14 +710,17 @@ static hipError_t launch_splitk_dl(const GemmParams& p, int max_tiles, hipStream
   const size_t lds = sizeof(uint16_t) * 16 * (static_cast<size_t>(p.cb) * 128 + 8);
   const hipError_t err = allow_lds_tile(up_splitk_kernel<DT, LAYOUT, kSplitkNsub>, lds);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((up_splitk_kernel<DT, LAYOUT, kSplitkNsub>), dim3(max_tiles * p.S),
-                     dim3(kTileThreads), lds, st, p);
+  hipLaunchKernelGGL((up_splitk_kernel<DT, LAYOUT, kSplitkNsub>),
+                     dim3(max_tiles * p.S * p.n_tiles), dim3(kTileThreads), lds, st, p);
   return hipGetLastError();
 }
 
 hipError_t launch_up_splitk(const GemmParams& p, int dtype, int layout, int max_tiles,
                             hipStream_t stream) {
-  if (p.S < 1 || p.cb < 1 || 16 * (p.cb * 128 + 8) * 2 > kSplitkMaxLds) return hipErrorInvalidValue;
+  if (p.S < 1 || p.cb < 1 || p.n_tiles < 1 || p.col_steps < 1 ||
+      16 * (p.cb * 128 + 8) * 2 > kSplitkMaxLds ||
+      static_cast<int64_t>(max_tiles) * p.S * p.n_tiles > 0x7fffffff)
+    return hipErrorInvalidValue;
   if (dtype == DT_BF16)
     return layout == Q_GROUP_K ? launch_splitk_dl<DT_BF16, Q_GROUP_K>(p, max_tiles, stream)
                                : launch_splitk_dl<DT_BF16, Q_PER_CHANNEL>(p, max_tiles, stream);
@@ -721,10 +728,9 @@ hipError_t launch_up_splitk(const GemmParams& p, int dtype, int layout, int max_
                              : launch_splitk_dl<DT_FP16, Q_PER_CHANNEL>(p, max_tiles, stream);
 }
 
-hipError_t launch_splitk_act(const GemmParams& p, int dtype, bool gated, int64_t max_positions,
-                             hipStream_t stream) {
-  if (p.ldo % 8 != 0) return hipErrorInvalidValue;
-  const int64_t threads = max_positions * (p.ldo / 8);
+hipError_t launch_splitk_act(const GemmParams& p, int dtype, bool gated, hipStream_t stream) {
+  if (p.ldo % 8 != 0 || p.R < 1) return hipErrorInvalidValue;
+  const int64_t threads = static_cast<int64_t>(p.R) * (p.ldo / 8);
   const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
   if (dtype == DT_BF16) {
     if (gated) hipLaunchKernelGGL((splitk_act_kernel<DT_BF16, true>), grid, dim3(256), 0, stream, p);
