@@ -166,11 +166,17 @@ w4a16_status_t w4a16_moe_forward_timed(const void* x, const uint8_t* w13_packed,
  *                         position, ascending within an expert; padding -1.
  *                         Positions at or past offsets[E] are not written.
  *   route_slot    [T*K]   position of each route in sorted_routes, or -1
+ *   chunk_scratch NULL, or W4A16_ROUTE_CHUNKS_MAX * E int32 of device scratch
+ *                 (contents on entry do not matter): with it the routes are
+ *                 ranked in up to W4A16_ROUTE_CHUNKS_MAX chunks in parallel, as
+ *                 in the forward; without it in one chunk.  Same results.
  *   sorted_capacity must be >= T*K + min(E, T*K) * (block_m - 1). */
+#define W4A16_ROUTE_CHUNKS_MAX 32
 w4a16_status_t w4a16_moe_prepare_routes(const w4a16_moe_desc_t* desc, const int32_t* topk_ids,
                                         int32_t block_m, int32_t* counts, int32_t* offsets,
                                         int32_t* sorted_routes, int64_t sorted_capacity,
-                                        int32_t* route_slot, w4a16_stream_t stream);
+                                        int32_t* route_slot, int32_t* chunk_scratch,
+                                        w4a16_stream_t stream);
 
 /* Nibble unpacking with the device conversion the GEMMs use ([P3] Checkpoint
  * format): out[2i] = low nibble of packed[i], out[2i+1] = high nibble, both as

@@ -109,10 +109,10 @@ def test_prepare_routes_and_unpack_argument_errors():
     P = ctypes.c_void_p
     args = [P(0x1000)] * 4
     assert L.w4a16_moe_prepare_routes(ctypes.byref(d), P(0x1000), 0, *args[:3], 100, args[3],
-                                      None) == 1
+                                      None, None) == 1
     assert b"block_m" in L.w4a16_last_error_message()
     assert L.w4a16_moe_prepare_routes(ctypes.byref(d), P(0x1000), 16, *args[:3], 10, args[3],
-                                      None) == 1
+                                      None, None) == 1
     assert b"capacity" in L.w4a16_last_error_message()
     assert L.w4a16_unpack_int4(None, 16, P(0x1000), None) == 1
     assert L.w4a16_unpack_int4(P(0x1000), -1, P(0x1000), None) == 1

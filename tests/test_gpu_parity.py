@@ -34,19 +34,22 @@ ROUTE_CASES = [
     # T, K, E, E_global, offset, block_m
     (1, 8, 384, 384, 0, 16), (8, 8, 384, 384, 0, 16), (16, 2, 8, 8, 0, 16),
     (2048, 8, 384, 384, 0, 64), (4096, 6, 128, 128, 0, 64), (2048, 8, 32, 256, 0, 64),
+    (8192, 8, 384, 384, 0, 64),
     (7, 3, 5, 9, 2, 4), (33, 4, 60, 60, 0, 32), (100, 8, 1024, 1024, 0, 1),
     (5, 2, 8, 8, 0, 256), (0, 4, 8, 8, 0, 16),
 ]
 
 
+@pytest.mark.parametrize("chunked", [True, False], ids=["chunked", "one-chunk"])
 @pytest.mark.parametrize("T,K,E,Eg,off,bm", ROUTE_CASES)
-def test_route_prep_bit_exact(T, K, E, Eg, off, bm):
+def test_route_prep_bit_exact(T, K, E, Eg, off, bm, chunked):
     rng = np.random.default_rng(T + 7 * K + E)
     ids = rng.integers(-3, Eg + 3, size=(T, K)).astype(np.int32)
     if T > 4:
         ids[T // 2] = Eg + 1            # a token without a valid route
     counts, offsets, srt, slot = oracle.prepare_routes(ids, E, off, bm)
-    gc, go, gs, gsl = binding.prepare_routes(torch.from_numpy(ids).cuda(), E, off, bm)
+    gc, go, gs, gsl = binding.prepare_routes(torch.from_numpy(ids).cuda(), E, off, bm,
+                                             chunked=chunked)
     torch.cuda.synchronize()
     total = int(offsets[-1])
     np.testing.assert_array_equal(gc.cpu().numpy(), counts)

@@ -61,7 +61,7 @@ def lib():
     L.w4a16_moe_get_plan.argtypes = [pdesc, ctypes.POINTER(MoePlan)]
     L.w4a16_moe_forward.argtypes = [P, P, P, P, P, P, P, P, pdesc, P, sz, P]
     L.w4a16_moe_forward_timed.argtypes = [P, P, P, P, P, P, P, P, pdesc, P, sz, P, P, i32]
-    L.w4a16_moe_prepare_routes.argtypes = [pdesc, P, i32, P, P, P, i64, P, P]
+    L.w4a16_moe_prepare_routes.argtypes = [pdesc, P, i32, P, P, P, i64, P, P, P]
     L.w4a16_unpack_int4.argtypes = [P, i64, P, P]
     L.w4a16_status_string.argtypes = [i32]
     L.w4a16_status_string.restype = ctypes.c_char_p
@@ -208,9 +208,13 @@ def forward_workload(wl, W, tok, **kw) -> torch.Tensor:
                        gated=wl.gated, per_channel=wl.per_channel, **kw)
 
 
+ROUTE_CHUNKS_MAX = 32
+
+
 def prepare_routes(topk_ids: torch.Tensor, num_local_experts: int, expert_offset: int,
-                   block_m: int, stream=None):
-    """Route tables from the device kernel: (counts, offsets, sorted, slot)."""
+                   block_m: int, stream=None, chunked: bool = True):
+    """Route tables from the device kernels: (counts, offsets, sorted, slot).
+    chunked: rank in parallel chunks as the forward does (else one chunk)."""
     _dev("topk_ids", topk_ids, (torch.int32,))
     T, K = topk_ids.shape
     R = T * K
@@ -222,9 +226,12 @@ def prepare_routes(topk_ids: torch.Tensor, num_local_experts: int, expert_offset
     srt = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
     slot = torch.empty(max(R, 1), dtype=torch.int32, device=dev)
     desc = MoeDesc(T, 64, 64, E, expert_offset, K, 32, 0, 0, 0, 0, 0, 0)
+    scratch = (torch.empty(ROUTE_CHUNKS_MAX * E, dtype=torch.int32, device=dev)
+               if chunked else None)
     _check(lib().w4a16_moe_prepare_routes(ctypes.byref(desc), _ptr(topk_ids), block_m,
                                           _ptr(counts), _ptr(offsets), _ptr(srt), cap,
-                                          _ptr(slot), _stream(stream)))
+                                          _ptr(slot), _ptr(scratch) if chunked else None,
+                                          _stream(stream)))
     return counts, offsets, srt, slot[:R]
 
 

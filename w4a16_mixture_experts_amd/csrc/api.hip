@@ -19,6 +19,9 @@
 #include "device.h"
 #include "internal.h"
 
+static_assert(W4A16_ROUTE_CHUNKS_MAX == w4moe::kRouteChunksMax,
+              "the header states the route scratch size");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -45,7 +48,7 @@ struct Plan {
   int64_t R = 0, P = 0, MT = 0, items = 0;
   int N1 = 0;
   size_t off_counts = 0, off_offsets = 0, off_slot = 0, off_sorted = 0, off_tile = 0,
-         off_act = 0, off_y = 0, off_part = 0, total = 0;
+         off_act = 0, off_y = 0, off_part = 0, off_chunks = 0, total = 0;
 };
 
 w4a16_status_t check_desc(const w4a16_moe_desc_t* d) {
@@ -190,6 +193,7 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
     pl.off_act = take(sizeof(float) * std::max<int64_t>(pl.R, 1) * pl.N1);  // FP32 pre-activations
   } else {
     pl.off_counts = take(sizeof(int32_t) * E);
+    pl.off_chunks = take(sizeof(int32_t) * w4moe::kRouteChunksMax * E);
     pl.off_offsets = take(sizeof(int32_t) * (E + 1));
     pl.off_slot = take(sizeof(int32_t) * std::max<int64_t>(pl.R, 1));
     pl.off_sorted = take(sizeof(int32_t) * std::max<int64_t>(pl.P, 1));
@@ -424,7 +428,8 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
   if (st != W4A16_OK) return st;
   st = hip_status(w4moe::launch_route_prep(topk_ids, static_cast<int>(pl.R), E,
                                            desc->expert_offset, pl.bm, counts, offsets, sorted,
-                                           slot, tile, nullptr, 0, stream),
+                                           slot, tile,
+                                           reinterpret_cast<int32_t*>(ws + pl.off_chunks), stream),
                   "route preparation launch");
   if (st == W4A16_OK) st = hip_status(evs.mark(1), "stage event");
   if (st != W4A16_OK) return st;
@@ -565,7 +570,8 @@ w4a16_status_t w4a16_moe_forward_timed(const void* x, const uint8_t* w13_packed,
 w4a16_status_t w4a16_moe_prepare_routes(const w4a16_moe_desc_t* desc, const int32_t* topk_ids,
                                         int32_t block_m, int32_t* counts, int32_t* offsets,
                                         int32_t* sorted_routes, int64_t sorted_capacity,
-                                        int32_t* route_slot, w4a16_stream_t stream_) {
+                                        int32_t* route_slot, int32_t* chunk_scratch,
+                                        w4a16_stream_t stream_) {
   if (desc == nullptr) return fail(W4A16_ERR_INVALID_ARG, "desc: null pointer");
   if (desc->num_tokens < 0)
     return fail(W4A16_ERR_INVALID_ARG, "desc.num_tokens: %d < 0", desc->num_tokens);
@@ -596,7 +602,7 @@ w4a16_status_t w4a16_moe_prepare_routes(const w4a16_moe_desc_t* desc, const int3
   return hip_status(w4moe::launch_route_prep(topk_ids, static_cast<int>(R),
                                              desc->num_local_experts, desc->expert_offset,
                                              block_m, counts, offsets, sorted_routes, route_slot,
-                                             nullptr, nullptr, 0, stream),
+                                             nullptr, chunk_scratch, stream),
                     "route preparation launch");
 }
 

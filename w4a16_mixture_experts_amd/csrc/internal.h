@@ -130,10 +130,13 @@ struct CombineParams {
   uint16_t* out;              // [T][H]
 };
 
+// Route preparation (three launches).  chunk_hist: kRouteChunksMax * E ints of
+// scratch, or null for a single-chunk (slower for many routes) preparation.
+constexpr int kRouteChunksMax = 32;
+int route_prep_chunk(int R);
 hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, int32_t* counts,
                              int32_t* offsets, int32_t* sorted, int32_t* slot,
-                             int32_t* tile_expert, int32_t* zero_buf, int zero_n,
-                             hipStream_t stream);
+                             int32_t* tile_expert, int32_t* chunk_hist, hipStream_t stream);
 
 hipError_t launch_grouped_gemm(const GemmParams& p, int dtype, int layout, int ms, int mode,
                                int max_tiles, hipStream_t stream);

@@ -6,7 +6,7 @@
 // [P2] flashinfer PR #5186, "perf: reduce split W4A16 routing and output
 // overhead" (Description: route guards, padded fallback).
 //
-// One workgroup of 1024 threads (16 waves) builds, from topk_ids [R = T*K]:
+// From topk_ids [R = T*K] it builds
 //   counts[e]       valid routes of local expert e
 //   offsets[e]      exclusive prefix of counts rounded up to block_m
 //   sorted[p]       route index r = t*K + k at padded position p, ascending
@@ -14,64 +14,170 @@
 //   slot[r]         p of route r, or -1 for an invalid route
 //   tile_expert[i]  expert of tile i (positions [i*block_m, (i+1)*block_m));
 //                   skipped when the pointer is null
-// and zeroes the split-K arrival counters of the gate/up kernel.
 //
-// Stable counting sort without atomics: wave w owns the contiguous slab
-// [w*S, (w+1)*S) of routes and walks it 64 routes at a time.  Lanes holding
-// the same expert are found with one ballot per expert-id bit; a lane's rank
-// is the number of matching lanes below it, and the lowest matching lane
-// bumps the wave's LDS histogram.  A block-wide pass turns the 16 histograms
-// into per-wave bases and padded offsets, and a second walk over the slabs
-// scatters every route to offsets[e] + base[w][e] + rank.  Ascending order
-// within an expert follows from slabs, chunks and lanes all being in order.
+// A stable counting sort without atomics.  Up to 1024 routes: one workgroup
+// (rp_fused_kernel).  Otherwise two launches:
+//   1. rp_rank_kernel: workgroup c takes the contiguous chunk c of routes;
+//      each of its waves walks a slab of the chunk 64 routes at a time.
+//      Lanes holding the same expert are found with one ballot per expert-id
+//      bit; a lane's rank is the number of matching lanes below it.  A
+//      wave's LDS histogram gives ranks across its chunks; a prefix over the
+//      waves gives each route's rank within the chunk (written to slot[r])
+//      and the chunk's per-expert counts (chunk_hist[c][e]).
+//   2. rp_scatter_kernel: each workgroup redoes the per-expert scan (chunk
+//      bases, totals, padded sizes, offsets) and scatters its chunk,
+//      p = offsets[e] + base[c][e] + rank; workgroup 0 writes counts,
+//      offsets, the padding and the tile -> expert map.
+// Ascending order within an expert follows from chunks, slabs, 64-route
+// pieces and lanes all being in route order.
+#include <algorithm>
+
 #include "device.h"
 #include "internal.h"
 
 namespace w4moe {
 
-constexpr int kRpThreads = 1024;
+namespace {
+
+constexpr int kRpThreads = 256;            // ranking/scatter workgroup (4 waves)
 constexpr int kRpWaves = kRpThreads / 64;
+constexpr int kRpScanThreads = 1024;       // one thread per expert (E <= 1024)
 constexpr int kRpMaxExperts = 1024;
-constexpr int kRpRound = 16;  // 64-route chunks whose id loads are in flight together
 
 __device__ __forceinline__ int local_expert(int32_t g, int E, int off) {
   const int64_t e = static_cast<int64_t>(g) - off;
   return (e >= 0 && e < E) ? static_cast<int>(e) : -1;
 }
 
-__global__ void __launch_bounds__(kRpThreads)
-route_prep_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm,
-                  int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                  int32_t* __restrict__ sorted, int32_t* __restrict__ slot,
-                  int32_t* __restrict__ tile_expert, int32_t* __restrict__ zero_buf,
-                  int zero_n) {
-  __shared__ int32_t hist[kRpWaves][kRpMaxExperts];
-  __shared__ int32_t wave_tot[kRpWaves];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+// Padding positions (-1) and the tile -> expert map, one wave per expert at a
+// time so that each store instruction writes consecutive positions (a thread
+// per expert would scatter every store over 64 experts' ranges).
+__device__ __forceinline__ void fill_padding_and_tiles(int E, int bm, const int32_t* s_off,
+                                                       const int32_t* s_cnt, int32_t* sorted,
+                                                       int32_t* tile_expert, int waves) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int e = w; e < E; e += waves) {
+    const int beg = s_off[e], end = s_off[e + 1];
+    for (int p = beg + s_cnt[e] + lane; p < end; p += 64) sorted[p] = -1;
+    if (tile_expert != nullptr)
+      for (int i = beg / bm + lane; i < end / bm; i += 64) tile_expert[i] = e;
+  }
+}
 
-  for (int i = tid; i < zero_n; i += kRpThreads) zero_buf[i] = 0;
+}  // namespace
+
+// Up to kRpFusedRoutes routes: the whole preparation in one workgroup (16
+// waves, one 64-route piece each).
+constexpr int kRpFusedRoutes = 1024;
+
+__global__ void __launch_bounds__(kRpScanThreads)
+rp_fused_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm,
+                int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                int32_t* __restrict__ sorted, int32_t* __restrict__ slot,
+                int32_t* __restrict__ tile_expert) {
+  constexpr int kW = kRpScanThreads / 64;
+  __shared__ int32_t hist[kW][kRpMaxExperts];
+  __shared__ int32_t wave_tot[kW];
+  __shared__ int32_t s_off[kRpMaxExperts + 1];
+  __shared__ int32_t s_cnt[kRpMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r = tid;  // route r = 64 w + lane: wave w holds the w-th piece
+  const int e = r < R ? local_expert(ids[r], E, off) : -1;
+  for (int x = lane; x < E; x += 64) hist[w][x] = 0;
+  // rank within the wave's piece (one ballot per expert-id bit)
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  uint64_t match = __ballot(e >= 0);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t m = __ballot(bit);
+    match &= bit ? m : ~m;
+  }
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int rank = __popcll(match & below);
+  __syncthreads();
+  if (e >= 0 && rank == 0) hist[w][e] = __popcll(match);
+  __syncthreads();
+  // per expert: wave bases (in place), totals, padded sizes
+  int padded = 0, total = 0;
+  if (tid < E) {
+#pragma unroll
+    for (int v = 0; v < kW; ++v) {
+      const int n = hist[v][tid];
+      hist[v][tid] = total;
+      total += n;
+    }
+    counts[tid] = total;
+    padded = (total + bm - 1) / bm * bm;
+  }
+  int incl = padded;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  if (lane == 63) wave_tot[w] = incl;
+  __syncthreads();
+  if (w == 0) {
+    int t = (lane < kW) ? wave_tot[lane] : 0;
+    for (int d = 1; d < kW; d <<= 1) {
+      const int v = __shfl_up(t, d, 64);
+      if (lane >= d) t += v;
+    }
+    if (lane < kW) wave_tot[lane] = t;
+  }
+  __syncthreads();
+  const int excl = incl - padded + (w > 0 ? wave_tot[w - 1] : 0);
+  if (tid < E) {
+    offsets[tid] = excl;
+    s_off[tid] = excl;
+    s_cnt[tid] = total;
+  }
+  if (tid == 0) {
+    offsets[E] = wave_tot[kW - 1];
+    s_off[E] = wave_tot[kW - 1];
+  }
+  __syncthreads();
+  if (r < R) {
+    if (e >= 0) {
+      const int pos = s_off[e] + hist[w][e] + rank;
+      sorted[pos] = r;
+      slot[r] = pos;
+    } else {
+      slot[r] = -1;
+    }
+  }
+  fill_padding_and_tiles(E, bm, s_off, s_cnt, sorted, tile_expert, kW);
+}
+
+__global__ void __launch_bounds__(kRpThreads)
+rp_rank_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int chunk,
+               int32_t* __restrict__ slot, int32_t* __restrict__ chunk_hist) {
+  __shared__ int32_t hist[kRpWaves][kRpMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c = blockIdx.x;
   for (int e = lane; e < E; e += 64) hist[w][e] = 0;
   __syncthreads();
 
-  const int slab = ((R + kRpWaves - 1) / kRpWaves + 63) & ~63;
-  const int r_beg = w * slab;
-  const int r_end = min(R, r_beg + slab);
+  const int c_beg = c * chunk;
+  const int c_end = min(R, c_beg + chunk);
+  const int slab = ((chunk + kRpWaves - 1) / kRpWaves + 63) & ~63;
+  const int r_beg = c_beg + w * slab;
+  const int r_end = min(c_end, r_beg + slab);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
 
-  // pass 1: per-wave histogram and rank of each route within its wave's slab.
-  // The slab is walked in rounds of kRpRound chunks of 64 routes; every id
-  // load of a round is issued before the first is used.
-  for (int rb = r_beg; rb < r_end; rb += 64 * kRpRound) {
-    int ev[kRpRound];
+  // rank of each route within this wave's slab (ids of 4 pieces in flight)
+  constexpr int kRound = 4;
+  for (int rb = r_beg; rb < r_end; rb += 64 * kRound) {
+    int ev[kRound];
 #pragma unroll
-    for (int q = 0; q < kRpRound; ++q) {
+    for (int q = 0; q < kRound; ++q) {
       const int r = rb + 64 * q + lane;
       ev[q] = (r < r_end) ? local_expert(ids[r], E, off) : -1;
     }
 #pragma unroll
-    for (int q = 0; q < kRpRound; ++q) {
+    for (int q = 0; q < kRound; ++q) {
       if (rb + 64 * q >= r_end) break;
       const int r = rb + 64 * q + lane;
       const int e = ev[q];
@@ -85,29 +191,66 @@ route_prep_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm
         const int rank = __popcll(match & below);
         const int before = hist[w][e];
         if (rank == 0) hist[w][e] = before + __popcll(match);
-        slot[r] = before + rank;  // temporary: rank within the slab
+        slot[r] = before + rank;  // temporary: rank within the wave's slab
       } else if (r < r_end) {
         slot[r] = -1;
       }
     }
   }
   __syncthreads();
-
-  // per expert: exclusive prefix over waves, counts, padded sizes
-  // (one thread per expert; E <= 1024)
-  int padded = 0, my_count = 0;
-  if (tid < E) {
+  // per expert: wave bases within the chunk (in place) and the chunk total
+  for (int e = tid; e < E; e += kRpThreads) {
     int run = 0;
+#pragma unroll
     for (int v = 0; v < kRpWaves; ++v) {
-      const int c = hist[v][tid];
-      hist[v][tid] = run;
-      run += c;
+      const int n = hist[v][e];
+      hist[v][e] = run;
+      run += n;
     }
-    counts[tid] = run;
-    my_count = run;
-    padded = (run + bm - 1) / bm * bm;
+    chunk_hist[static_cast<int64_t>(c) * E + e] = run;
   }
-  // block-wide exclusive scan of padded sizes over experts
+  __syncthreads();
+  // rank within the chunk
+  for (int rb = r_beg; rb < r_end; rb += 64) {
+    const int r = rb + lane;
+    if (r < r_end) {
+      const int e = local_expert(ids[r], E, off);
+      if (e >= 0) slot[r] += hist[w][e];
+    }
+  }
+}
+
+// Every workgroup redoes the (small) per-expert scan, so that no separate
+// launch is needed: chunk counts of each expert (all loads in flight), the
+// totals, their padded sizes, the scan over experts; then workgroup c
+// scatters chunk c, and workgroup 0 also writes counts, offsets, padding and
+// the tile -> expert map.  chunk_hist may alias counts (one chunk: the only
+// workgroup reads a count before writing it, in the same thread).
+__global__ void __launch_bounds__(kRpScanThreads)
+rp_scatter_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm, int chunk,
+                  int n_chunks, const int32_t* chunk_hist, int32_t* counts,
+                  int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
+                  int32_t* __restrict__ slot, int32_t* __restrict__ tile_expert) {
+  constexpr int kW = kRpScanThreads / 64;
+  __shared__ int32_t wave_tot[kW];
+  __shared__ int32_t s_off[kRpMaxExperts + 1];
+  __shared__ int32_t s_cnt[kRpMaxExperts];
+  __shared__ int32_t s_base[kRpMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c = blockIdx.x;
+  int padded = 0, total = 0, base = 0;
+  if (tid < E) {
+    int n[kRouteChunksMax];
+#pragma unroll
+    for (int q = 0; q < kRouteChunksMax; ++q)
+      n[q] = q < n_chunks ? chunk_hist[static_cast<int64_t>(q) * E + tid] : 0;
+#pragma unroll
+    for (int q = 0; q < kRouteChunksMax; ++q) {
+      if (q == c) base = total;
+      total += n[q];
+    }
+    padded = (total + bm - 1) / bm * bm;
+  }
   int incl = padded;
   for (int d = 1; d < 64; d <<= 1) {
     const int v = __shfl_up(incl, d, 64);
@@ -116,60 +259,69 @@ route_prep_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm
   if (lane == 63) wave_tot[w] = incl;
   __syncthreads();
   if (w == 0) {
-    int t = (lane < kRpWaves) ? wave_tot[lane] : 0;
-    for (int d = 1; d < kRpWaves; d <<= 1) {
+    int t = (lane < kW) ? wave_tot[lane] : 0;
+    for (int d = 1; d < kW; d <<= 1) {
       const int v = __shfl_up(t, d, 64);
       if (lane >= d) t += v;
     }
-    if (lane < kRpWaves) wave_tot[lane] = t;  // inclusive totals per wave
+    if (lane < kW) wave_tot[lane] = t;  // inclusive totals per wave
   }
   __syncthreads();
   const int excl = incl - padded + (w > 0 ? wave_tot[w - 1] : 0);
-  __shared__ int32_t s_off[kRpMaxExperts + 1];
   if (tid < E) {
-    offsets[tid] = excl;
     s_off[tid] = excl;
+    s_cnt[tid] = total;
+    s_base[tid] = base;
   }
-  if (tid == 0) {
-    offsets[E] = wave_tot[kRpWaves - 1];
-    s_off[E] = wave_tot[kRpWaves - 1];
-  }
+  if (tid == 0) s_off[E] = wave_tot[kW - 1];
   __syncthreads();
+  const int c_end = min(R, (c + 1) * chunk);
+  for (int r = c * chunk + tid; r < c_end; r += kRpScanThreads) {
+    const int e = local_expert(ids[r], E, off);
+    if (e < 0) continue;  // slot[r] is already -1
+    const int pos = s_off[e] + s_base[e] + slot[r];
+    sorted[pos] = r;
+    slot[r] = pos;
+  }
+  if (c == 0) {
+    if (tid < E) {
+      counts[tid] = s_cnt[tid];
+      offsets[tid] = s_off[tid];
+    }
+    if (tid == 0) offsets[E] = s_off[E];
+    fill_padding_and_tiles(E, bm, s_off, s_cnt, sorted, tile_expert, kW);
+  }
+}
 
-  // pass 2: scatter (each thread revisits exactly the routes it ranked)
-  for (int rb = r_beg; rb < r_end; rb += 64 * kRpRound) {
-    int ev[kRpRound], rk[kRpRound];
-#pragma unroll
-    for (int q = 0; q < kRpRound; ++q) {
-      const int r = rb + 64 * q + lane;
-      ev[q] = (r < r_end) ? local_expert(ids[r], E, off) : -1;
-      rk[q] = (ev[q] >= 0) ? slot[r] : 0;
-    }
-#pragma unroll
-    for (int q = 0; q < kRpRound; ++q) {
-      const int r = rb + 64 * q + lane;
-      if (ev[q] >= 0) {
-        const int pos = s_off[ev[q]] + hist[w][ev[q]] + rk[q];
-        sorted[pos] = r;
-        slot[r] = pos;
-      }
-    }
-  }
-  // padding positions and the tile -> expert map (thread e owns expert e)
-  if (tid < E) {
-    const int beg = s_off[tid], end = s_off[tid + 1];
-    for (int p = beg + my_count; p < end; ++p) sorted[p] = -1;
-    if (tile_expert != nullptr)
-      for (int i = beg / bm; i < end / bm; ++i) tile_expert[i] = tid;
-  }
+int route_prep_chunk(int R) {
+  // at most kRouteChunksMax chunks, at least 1024 routes per chunk
+  const int per = (R + kRouteChunksMax - 1) / kRouteChunksMax;
+  return std::max(1024, (per + 63) & ~63);
 }
 
 hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, int32_t* counts,
                              int32_t* offsets, int32_t* sorted, int32_t* slot,
-                             int32_t* tile_expert, int32_t* zero_buf, int zero_n,
-                             hipStream_t stream) {
-  hipLaunchKernelGGL(route_prep_kernel, dim3(1), dim3(kRpThreads), 0, stream, ids, R, E, off, bm,
-                     counts, offsets, sorted, slot, tile_expert, zero_buf, zero_n);
+                             int32_t* tile_expert, int32_t* chunk_hist, hipStream_t stream) {
+  if (E < 1 || E > kRpMaxExperts || R < 0) return hipErrorInvalidValue;
+  // without scratch: one chunk, whose counts live in `counts` itself (the
+  // scan overwrites them with the totals) and whose base is 0
+  const bool one = chunk_hist == nullptr;
+  const int chunk = one ? std::max(R, 1) : route_prep_chunk(R);
+  const int n_chunks = R > 0 ? (R + chunk - 1) / chunk : 0;
+  int32_t* hist = one ? counts : chunk_hist;
+  if (R <= kRpFusedRoutes) {
+    hipLaunchKernelGGL(rp_fused_kernel, dim3(1), dim3(kRpScanThreads), 0, stream, ids, R, E, off,
+                       bm, counts, offsets, sorted, slot, tile_expert);
+    return hipGetLastError();
+  }
+  // R > kRpFusedRoutes here, so there is at least one chunk
+  hipLaunchKernelGGL(rp_rank_kernel, dim3(n_chunks), dim3(kRpThreads), 0, stream, ids, R, E, off,
+                     chunk, slot, hist);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(rp_scatter_kernel, dim3(n_chunks), dim3(kRpScanThreads), 0, stream, ids, R,
+                     E, off, bm, chunk, n_chunks, hist, counts, offsets, sorted, slot,
+                     tile_expert);
   return hipGetLastError();
 }
 
