@@ -380,6 +380,7 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
     w4moe::SmallHParams sh{};
     sh.x = static_cast<const uint16_t*>(x);
     sh.lda = H;
+    sh.T = static_cast<int>(desc->num_tokens);
     sh.ids = topk_ids;
     sh.R = static_cast<int>(pl.R);
     sh.top_k = K;

@@ -297,81 +297,80 @@ decode_up_kernel(const DecodeUpParams p) {
 // Up to 4 rows per pass sit at MFMA rows 0, 4, 8, 12: result row 4q is
 // element 0 of lane row q, so one FMA per MFMA applies the group scale.  The
 // staged rows are read by lanes c % 4 == 0; the other lanes feed zeros.
-// Memory order: ids; then, in flight together, the subtile's scales (staged
-// in LDS), each wave's slice of the x rows (staged in its own LDS region) and
-// all weights of the wave's slice (registers); a wait for the first two, one
-// barrier, a branch-free MFMA section, a fixed-order reduction over slices.
+// Memory order: one load of the ids; then, in flight together, every weight,
+// group scale and x value of the wave's slice (raw buffer loads: masked
+// lanes read zeros, so nothing waits on a load before its use).  Each wave
+// stages only its own slice of x (no barrier), and one barrier precedes the
+// fixed-order sum over slices.  Two dependent memory round trips in all.
 template <int DT, int LAYOUT, int NKB>
 __global__ void __launch_bounds__(kSmallThreads)
 small_h_kernel(const SmallHParams p) {
   using T = H16<DT>;
   constexpr bool GROUP = LAYOUT == Q_GROUP_K;
+  constexpr int CH = NKB * 16;  // 8-value chunks per staged x row of a slice
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int c = lane & 15, g = lane >> 4, par = c & 1;
-  const int nt = blockIdx.y;
-  const int r0 = blockIdx.x;
+  // column tiles are the fast grid dimension: consecutive workgroups stream
+  // consecutive 16-row slabs of one expert
+  const int nt = blockIdx.x;
+  const int r0 = blockIdx.y;
 
-  extern __shared__ uint16_t s_dyn[];  // [16 rows][K/32] scales, then per wave [4][kslice + 8] x
+  extern __shared__ uint16_t s_dyn[];  // per wave [kSmallRows][kslice + 8] x, A order
   __shared__ float s_red[kSmallWaves][64];
 
-  // rows: the routes whose id equals route r0's id (R <= 64: one ballot)
-  const int32_t gid = p.ids[r0];
+  // rows: the routes whose id equals route r0's id (R <= 64: one load, one ballot)
+  const auto rids = make_rsrc(p.ids, 4u * static_cast<uint32_t>(p.R));
+  const int32_t my_id = static_cast<int32_t>(bload4(rids, 4u * lane, lane < p.R));
+  const int32_t gid = __builtin_amdgcn_readlane(my_id, r0);
   const int e = local_id(gid, p.E, p.off);
   if (e < 0) return;  // invalid route: nothing to do (uniform)
-  const int32_t my_id = p.ids[lane < p.R ? lane : r0];
   const uint64_t match = __ballot(lane < p.R && my_id == gid);
   if (__builtin_ctzll(match) != r0) return;  // an earlier slot owns this expert (uniform)
   const int M = __popcll(match);
+  const int my_tok = lane / p.top_k;  // token of route `lane`
 
-  const int wrow = nt * 16 + c;                   // weight row (output column of h)
-  const uint8_t* wq_e = p.wq + static_cast<int64_t>(e) * p.wq_expert_bytes;
-  const uint16_t* ws_e = p.ws + static_cast<int64_t>(e) * p.ws_expert_elems;
+  const int wrow = nt * 16 + c;  // weight row (output column of h)
+  const auto rw = make_rsrc(p.wq + static_cast<int64_t>(e) * p.wq_expert_bytes,
+                            static_cast<uint32_t>(p.wq_expert_bytes));
+  const auto rs = make_rsrc(p.ws + static_cast<int64_t>(e) * p.ws_expert_elems,
+                            static_cast<uint32_t>(2 * p.ws_expert_elems));
+  const auto rx = make_rsrc(p.x, 2u * static_cast<uint32_t>(p.T) * static_cast<uint32_t>(p.lda));
   const uint32_t boff = GROUP ? static_cast<uint32_t>(wrow) * (p.K >> 1)
                               : static_cast<uint32_t>(wrow >> 1) * p.K;
-  const int ngr = p.K >> 5;                       // scale groups per weight row
-  uint16_t* s_sc = s_dyn;                         // [16][ngr]
-  const int sc_elems = GROUP ? 16 * ngr : 0;
-  const int xs = p.kslice + 8;                    // staged x row stride (16 B padding)
-  uint16_t* my_x = s_dyn + ((sc_elems + 7) & ~7) + w * kSmallRows * xs;
+  const uint32_t soff = GROUP ? 2u * static_cast<uint32_t>(wrow) * (p.K >> 5) : 2u * wrow;
+  const int xs = p.kslice + 8;  // staged x row stride (16 B padding)
+  uint16_t* my_x = s_dyn + w * kSmallRows * xs;
   const int kb = w * p.kslice;
   const int ke = min(p.K, kb + p.kslice);
-  const int nck = (ke > kb) ? (ke - kb) >> 3 : 0; // 8-value chunks per x row in the slice
   const int q_row = c >> 2;
   const bool feed_lane = (c & 3) == 0;
-
-  // (1) the subtile's scales: rows nt*16..+15 are one run of 16*ngr values
-  //     = 2*ngr 16-byte chunks, copied flat into s_sc
-  const int sc_chunks = GROUP ? 2 * ngr : 0;
-  const bool sc_in = tid < sc_chunks;
-  const u32x4 scv = load16_at(ws_e, 32u * static_cast<uint32_t>(nt) * ngr + 16u * tid, sc_in);
-  const float scol = GROUP ? 0.0f : T::to_f32(load4_if(true, ws_e + wrow, p.ws) & 0xffffu);
-
-  constexpr int XL = (kSmallRows * NKB * 16 + 63) / 64;  // x chunks per lane (4 rows)
-  uint64_t rest = match;
   const u32x4 bconst = {T::kNegOneHalf2, T::kNegOneHalf2, T::kNegOneHalf2, T::kNegOneHalf2};
   const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
 
   // one pass per 4 rows (more than 4 only if one expert takes more than 4 of
   // the routes; then the weights are streamed once per pass)
+  uint64_t rest = match;
   for (int m0 = 0; m0 < M; m0 += kSmallRows) {
     const int nr = min(kSmallRows, M - m0);
-    int rrow[kSmallRows];
+    int rrow[kSmallRows], tok[kSmallRows];
 #pragma unroll
     for (int q = 0; q < kSmallRows; ++q) {
       rrow[q] = (q < nr) ? __builtin_ctzll(rest) : r0;
       if (q < nr) rest &= rest - 1;
+      tok[q] = __builtin_amdgcn_readlane(my_tok, rrow[q]);
     }
-    // (2) this wave's slice of the x rows
-    u32x4 xv[XL];
+    // (1) this wave's slice of the staged rows (issued first: they are staged
+    //     while the weights are still in flight): chunk idx -> row idx / CH
+    u32x4 xv[NKB];
 #pragma unroll
-    for (int i = 0; i < XL; ++i) {
+    for (int i = 0; i < NKB; ++i) {
       const int idx = lane + 64 * i;
-      const int q = nck ? idx / nck : 0, ck = nck ? idx - q * nck : 0;
-      const bool ok = nck > 0 && q < nr;
-      xv[i] = load16_at(p.x, 2u * (static_cast<uint32_t>(rrow[ok ? q : 0] / p.top_k) * p.lda + kb +
-                                   8 * ck), ok);
+      const int q = idx / CH, ck = idx - q * CH;
+      const int tq = q == 0 ? tok[0] : q == 1 ? tok[1] : q == 2 ? tok[2] : tok[3];
+      const bool ok = q < nr && kb + 8 * ck < ke;
+      xv[i] = bload16(rx, 2u * (static_cast<uint32_t>(tq) * p.lda + kb + 8 * ck), ok);
     }
-    // (3) every weight of this wave's slice (kslice <= NKB * 128)
+    // (2) every weight of this wave's slice (kslice <= NKB * 128)
     u32x4 bw[NKB];
     u32x4 bw2[GROUP ? 1 : NKB];
 #pragma unroll
@@ -379,31 +378,41 @@ small_h_kernel(const SmallHParams p) {
       const int k0 = kb + 128 * i;
       const int ng = k0 < ke ? min(4, (ke - k0) >> 5) : 0;
       if constexpr (GROUP) {
-        bw[i] = load16_at(wq_e, boff + (k0 >> 1) + 16 * g, g < ng);
+        bw[i] = bload16(rw, boff + (k0 >> 1) + 16 * g, g < ng);
       } else {
-        bw[i] = load16_at(wq_e, boff + k0 + 32 * g, g < ng);
-        bw2[i] = load16_at(wq_e, boff + k0 + 32 * g + 16, g < ng);
+        bw[i] = bload16(rw, boff + k0 + 32 * g, g < ng);
+        bw2[i] = bload16(rw, boff + k0 + 32 * g + 16, g < ng);
       }
     }
-    // stage scales (first pass) and x: their loads were issued before the weights
-    if (m0 == 0 && sc_in) *reinterpret_cast<u32x4*>(s_sc + 8 * tid) = scv;
+    // (3) group scales of the slice: 4 per block (8 bytes) of row wrow
+    u32x2 sc2[GROUP ? NKB : 1];
+    uint32_t scol_bits = 0;
+    if constexpr (GROUP) {
 #pragma unroll
-    for (int i = 0; i < XL; ++i) {
-      const int idx = lane + 64 * i;
-      const int q = nck ? idx / nck : 0, ck = nck ? idx - q * nck : 0;
-      if (nck > 0 && q < nr) *reinterpret_cast<u32x4*>(my_x + q * xs + 8 * ck) = permute_a(xv[i]);
+      for (int i = 0; i < NKB; ++i) {
+        const int k0 = kb + 128 * i;
+        sc2[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                               rs, k0 < ke ? soff + 2u * (k0 >> 5) : kOob, 0, 0));
+      }
+    } else {
+      scol_bits = bload4(rs, soff & ~3u, true) >> (16 * (wrow & 1));
     }
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NKB; ++i) {
+      const int idx = lane + 64 * i;
+      const int q = idx / CH, ck = idx - q * CH;
+      *reinterpret_cast<u32x4*>(my_x + q * xs + 8 * ck) = permute_a(xv[i]);
+    }
+    // the wave reads back only what its own lanes wrote: LDS order suffices
     const bool feed = feed_lane && q_row < nr;
-    const uint16_t* arow = my_x + (q_row < nr ? q_row : 0) * xs;
-    const uint16_t* srow = s_sc + c * ngr;
+    const uint16_t* arow = my_x + q_row * xs;
+    const float scol = T::to_f32(scol_bits & 0xffffu);
 
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < NKB; ++i) {
       const int k0 = kb + 128 * i;
       const int ng = k0 < ke ? min(4, (ke - k0) >> 5) : 0;
-      const int xo = k0 < ke ? k0 - kb : 0;      // clamp: never read unstaged LDS
       uint32_t d[4], d2[4];
       d[0] = bw[i][0]; d[1] = bw[i][1]; d[2] = bw[i][2]; d[3] = bw[i][3];
       if constexpr (GROUP) {
@@ -417,18 +426,17 @@ small_h_kernel(const SmallHParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const bool gv = j < ng;
-        // only staged values are used: other lanes and groups feed zeros
-        const bool fa = feed && gv;
-        const u32x4 av = *reinterpret_cast<const u32x4*>(arow + (fa ? xo + 32 * j + 8 * g : 0));
+        const u32x4 av = *reinterpret_cast<const u32x4*>(arow + 128 * i + 32 * j + 8 * g);
         u32x4 a;
-        a[0] = fa ? av[0] : 0u;
-        a[1] = fa ? av[1] : 0u;
-        a[2] = fa ? av[2] : 0u;
-        a[3] = fa ? av[3] : 0u;
+        a[0] = feed ? av[0] : 0u;
+        a[1] = feed ? av[1] : 0u;
+        a[2] = feed ? av[2] : 0u;
+        a[3] = feed ? av[3] : 0u;
         float sc;
         u32x4 bop;
         if constexpr (GROUP) {
-          sc = T::to_f32(srow[gv ? (k0 >> 5) + j : 0]);
+          const uint32_t pair = sc2[i][j >> 1];
+          sc = T::to_f32((j & 1) ? (pair >> 16) : (pair & 0xffffu));
           bop = nibbles_to_h16<DT>(d[j]);
         } else {
           sc = scol;
@@ -442,7 +450,6 @@ small_h_kernel(const SmallHParams p) {
         const f32x4 t = T::mfma(a, bop, corr);
         acc = fmaf(sc, t[0], acc);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
     s_red[w][lane] = acc;
     __syncthreads();
@@ -721,8 +728,8 @@ static hipError_t launch_small_h_nkb(const SmallHParams& p, int nkb, dim3 grid, 
 
 hipError_t launch_small_h(const SmallHParams& p, int dtype, int layout, int nkb, int n1,
                           hipStream_t stream) {
-  const dim3 grid(p.R, n1 / 16);
-  const size_t lds = small_h_lds_bytes(p.K, p.kslice);
+  const dim3 grid(n1 / 16, p.R);
+  const size_t lds = small_h_lds_bytes(p.kslice);
   if (dtype == DT_BF16)
     return layout == Q_GROUP_K ? launch_small_h_nkb<DT_BF16, Q_GROUP_K>(p, nkb, grid, lds, stream)
                                : launch_small_h_nkb<DT_BF16, Q_PER_CHANNEL>(p, nkb, grid, lds, stream);

@@ -58,16 +58,14 @@ constexpr int kSmallWaves = 8;            // reduction slices
 constexpr int kSmallThreads = kSmallWaves * 64;
 constexpr int kSmallRows = 4;             // token rows per pass (MFMA rows 0, 4, 8, 12)
 constexpr int kSmallMaxSlice = 1024;      // reduction per slice: hidden <= 8 * 1024
-static_assert(2 * (8 * kSmallMaxSlice / 32) <= kSmallThreads,
-              "one 16-byte scale chunk per thread covers a 16-row subtile");
-inline size_t small_h_lds_bytes(int K, int kslice) {
-  const size_t sc = ((16 * static_cast<size_t>(K / 32)) + 7) & ~size_t(7);
-  return sizeof(uint16_t) * (sc + static_cast<size_t>(kSmallWaves) * kSmallRows * (kslice + 8));
+inline size_t small_h_lds_bytes(int kslice) {
+  return sizeof(uint16_t) * static_cast<size_t>(kSmallWaves) * kSmallRows * (kslice + 8);
 }
 
 struct SmallHParams {
   const uint16_t* x;          // [T][lda]
   int lda;
+  int T;                      // tokens (rows of x)
   const int32_t* ids;         // [R] global ids
   int R, top_k, E, off;
   const uint8_t* wq;          // w13 packed, expert 0
