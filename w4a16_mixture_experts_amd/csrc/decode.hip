@@ -467,13 +467,16 @@ small_h_kernel(const SmallHParams p) {
 // small batch down GEMM of each route of one token + FP32 combine in top-k
 // order; the activation of the token's routes is formed in the prologue
 // ---------------------------------------------------------------------------
-// Prologue: the FP32 pre-activations of the token's K routes (issued first),
-// then the weights of each wave's first work item; SiLU(gate)*up or ReLU^2
-// is computed once per value, rounded to 16 bits and staged in LDS in A
-// operand order.  Work items are (route k, 256-wide slice of the reduction);
-// each wave computes its items' 32 partial outputs (one MFMA row: a route is
-// a single activation row) into LDS; then 32 lanes add, for k = 0..K-1 in
-// order, w[t,k] * (sum of k's slices in slice order) and cast once.
+// Memory order: one load of the token's ids and weights (lane k holds route
+// k); then, in flight together, the FP32 pre-activations of the token's
+// routes and the weights of each wave's first work item (raw buffer loads:
+// masked lanes read zeros, nothing waits on a load before its use).
+// SiLU(gate)*up or ReLU^2 is computed once per value, rounded to 16 bits and
+// staged in LDS in A operand order.  Work items are (route k, 256-wide slice
+// of the reduction); each wave computes its items' 32 partial outputs (one
+// MFMA row: a route is a single activation row) into LDS; then 32 lanes add,
+// for k = 0..K-1 in order, w[t,k] * (sum of k's slices in slice order) and
+// cast once.
 template <int DT, int LAYOUT, bool GATED, int AL>
 __global__ void __launch_bounds__(kDecThreads)
 decode_down_kernel(const DecodeDownParams p) {
@@ -492,6 +495,13 @@ decode_down_kernel(const DecodeDownParams p) {
   extern __shared__ uint16_t s_act[];      // [top_k][I + 8], A operand order
   __shared__ float s_y[kDecMaxItems][32];
 
+  // (1) the token's routes: lane k < top_k holds id, local expert and weight
+  const uint32_t r_base = static_cast<uint32_t>(t) * p.top_k;
+  const auto rids = make_rsrc(p.ids + r_base, 4u * p.top_k);
+  const auto rwts = make_rsrc(p.wts + r_base, 4u * p.top_k);
+  const int e_lane = local_id(static_cast<int32_t>(bload4(rids, 4u * lane, lane < p.top_k)), p.E, p.off);
+  const float wt_lane = __uint_as_float(bload4(rwts, 4u * lane, lane < p.top_k));
+
   bool on[NSUB];
   int wrow[NSUB];
 #pragma unroll
@@ -500,47 +510,40 @@ decode_down_kernel(const DecodeDownParams p) {
     wrow[s] = n0 + 16 * s + c;
   }
 
-  // (1) pre-activations of the token's routes (8 values per chunk)
+  // (2) pre-activations of the token's routes (8 values per chunk)
   const int ich = p.I >> 3;
   const int nch = p.top_k * ich;
+  const auto rh = make_rsrc(p.h + static_cast<int64_t>(r_base) * p.ldh, 4u * p.top_k * p.ldh);
   f32x4 hg[AL][2], hu[AL][2];  // AL: activation chunks per thread (>= top_k * I / 8 / 512)
 #pragma unroll
   for (int i = 0; i < AL; ++i) {
     const int idx = tid + kDecThreads * i;
     const int k = idx < nch ? idx / ich : 0, cc = idx < nch ? idx - k * ich : 0;
-    const int r = t * p.top_k + k;
-    const bool ok = idx < nch && local_id(p.ids[r], p.E, p.off) >= 0;
-    const uint32_t off = 4u * (static_cast<uint32_t>(r) * p.ldh + 8 * cc);
-    const u32x4 g0 = load16_at(p.h, off, ok), g1 = load16_at(p.h, off + 16, ok);
-    hg[i][0] = __builtin_bit_cast(f32x4, g0);
-    hg[i][1] = __builtin_bit_cast(f32x4, g1);
+    const bool ok = idx < nch && __shfl(e_lane, k) >= 0;
+    const uint32_t off = 4u * (static_cast<uint32_t>(k) * p.ldh + 8 * cc);
+    hg[i][0] = __builtin_bit_cast(f32x4, bload16(rh, off, ok));
+    hg[i][1] = __builtin_bit_cast(f32x4, bload16(rh, off + 16, ok));
     if constexpr (GATED) {
-      const u32x4 u0 = load16_at(p.h, off + 4u * p.I, ok), u1 = load16_at(p.h, off + 4u * p.I + 16, ok);
-      hu[i][0] = __builtin_bit_cast(f32x4, u0);
-      hu[i][1] = __builtin_bit_cast(f32x4, u1);
+      hu[i][0] = __builtin_bit_cast(f32x4, bload16(rh, off + 4u * p.I, ok));
+      hu[i][1] = __builtin_bit_cast(f32x4, bload16(rh, off + 4u * p.I + 16, ok));
     }
   }
 
-  // (2) weights of the first item of this wave
-  auto item_ptrs = [&](int it, int& r, int& e, uint32_t& boff0, uint32_t& boff1, const uint8_t*& wq_e,
-                       const uint16_t*& ws_e) {
+  // (3) weights of a work item (route k, reduction slice sl)
+  const uint32_t boff[NSUB] = {
+      LAYOUT == Q_GROUP_K ? static_cast<uint32_t>(wrow[0]) * (p.I >> 1)
+                          : static_cast<uint32_t>(wrow[0] >> 1) * p.I,
+      LAYOUT == Q_GROUP_K ? static_cast<uint32_t>(wrow[1]) * (p.I >> 1)
+                          : static_cast<uint32_t>(wrow[1] >> 1) * p.I};
+  auto load_item = [&](int it, BBlk<LAYOUT> (&b)[SL][NSUB], float (&scol)[NSUB], int& e) {
     const int k = it / nsl;
-    r = t * p.top_k + k;
-    e = local_id(p.ids[r], p.E, p.off);
+    e = __builtin_amdgcn_readlane(e_lane, k);
     const int ee = e >= 0 ? e : 0;
-    wq_e = p.wq + static_cast<int64_t>(ee) * p.wq_expert_bytes;
-    ws_e = p.ws + static_cast<int64_t>(ee) * p.ws_expert_elems;
-    boff0 = LAYOUT == Q_GROUP_K ? static_cast<uint32_t>(wrow[0]) * (p.I >> 1)
-                                : static_cast<uint32_t>(wrow[0] >> 1) * p.I;
-    boff1 = LAYOUT == Q_GROUP_K ? static_cast<uint32_t>(wrow[1]) * (p.I >> 1)
-                                : static_cast<uint32_t>(wrow[1] >> 1) * p.I;
-  };
-  auto load_item = [&](int it, BBlk<LAYOUT> (&b)[SL][NSUB], float (&scol)[NSUB], int& e, int& r) {
-    uint32_t bo[NSUB];
-    const uint8_t* wq_e;
-    const uint16_t* ws_e;
-    item_ptrs(it, r, e, bo[0], bo[1], wq_e, ws_e);
-    const int sl = it - (it / nsl) * nsl;
+    const auto rw = make_rsrc(p.wq + static_cast<int64_t>(ee) * p.wq_expert_bytes,
+                              static_cast<uint32_t>(p.wq_expert_bytes));
+    const auto rs = make_rsrc(p.ws + static_cast<int64_t>(ee) * p.ws_expert_elems,
+                              static_cast<uint32_t>(2 * p.ws_expert_elems));
+    const int sl = it - k * nsl;
     const int kb = sl * SL * 128;
     const int ke = min(p.I, kb + SL * 128);
 #pragma unroll
@@ -551,14 +554,16 @@ decode_down_kernel(const DecodeDownParams p) {
       for (int s = 0; s < NSUB; ++s) {
         const bool ok = e >= 0 && on[s] && ng > 0;
         if constexpr (LAYOUT == Q_GROUP_K) {
-          const u32x4 v = load16_at(wq_e, bo[s] + (k0 >> 1) + 16 * g, ok && g < ng);
+          const u32x4 v = bload16(rw, boff[s] + (k0 >> 1) + 16 * g, ok && g < ng);
           b[i][s].d[0] = v[0]; b[i][s].d[1] = v[1]; b[i][s].d[2] = v[2]; b[i][s].d[3] = v[3];
           const uint32_t so = 2u * (static_cast<uint32_t>(wrow[s]) * (p.I >> 5) + (k0 >> 5));
-          b[i][s].s[0] = load4_if(ok, reinterpret_cast<const char*>(ws_e) + so, p.ws);
-          b[i][s].s[1] = load4_if(ok && ng > 2, reinterpret_cast<const char*>(ws_e) + so + 4, p.ws);
+          const u32x2 sv = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, ok ? so : kOob, 0, 0));
+          b[i][s].s[0] = sv[0];
+          b[i][s].s[1] = sv[1];
         } else {
-          const u32x4 v0 = load16_at(wq_e, bo[s] + k0 + 32 * g, ok && g < ng);
-          const u32x4 v1 = load16_at(wq_e, bo[s] + k0 + 32 * g + 16, ok && g < ng);
+          const u32x4 v0 = bload16(rw, boff[s] + k0 + 32 * g, ok && g < ng);
+          const u32x4 v1 = bload16(rw, boff[s] + k0 + 32 * g + 16, ok && g < ng);
           b[i][s].d[0] = v0[0]; b[i][s].d[1] = v0[1]; b[i][s].d[2] = v0[2]; b[i][s].d[3] = v0[3];
           b[i][s].d[4] = v1[0]; b[i][s].d[5] = v1[1]; b[i][s].d[6] = v1[2]; b[i][s].d[7] = v1[3];
           b[i][s].s[0] = b[i][s].s[1] = 0u;
@@ -567,16 +572,17 @@ decode_down_kernel(const DecodeDownParams p) {
     }
 #pragma unroll
     for (int s = 0; s < NSUB; ++s)
-      scol[s] = (LAYOUT == Q_GROUP_K) ? 0.0f
-                : T::to_f32(load4_if(e >= 0 && on[s], ws_e + wrow[s], p.ws) & 0xffffu);
+      scol[s] = (LAYOUT == Q_GROUP_K)
+                    ? 0.0f
+                    : T::to_f32(bload4(rs, (2u * wrow[s]) & ~3u, e >= 0 && on[s]) >> (16 * (wrow[s] & 1)));
   };
 
   BBlk<LAYOUT> b[SL][NSUB];
   float scol[NSUB];
-  int e_cur = -1, r_cur = 0;
-  if (w < items) load_item(w, b, scol, e_cur, r_cur);
+  int e_cur = -1;
+  if (w < items) load_item(w, b, scol, e_cur);
 
-  // (3) activation: computed once per value, 16-bit, A operand order
+  // (4) activation: computed once per value, 16-bit, A operand order
 #pragma unroll
   for (int i = 0; i < AL; ++i) {
     const int idx = tid + kDecThreads * i;
@@ -606,7 +612,7 @@ decode_down_kernel(const DecodeDownParams p) {
   const u32x4 bconst = {T::kNegOneHalf2, T::kNegOneHalf2, T::kNegOneHalf2, T::kNegOneHalf2};
   const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
   for (int it = w; it < items; it += kDecWaves) {
-    if (it != w) load_item(it, b, scol, e_cur, r_cur);
+    if (it != w) load_item(it, b, scol, e_cur);
     const int k = it / nsl, sl = it - k * nsl;
     float y[NSUB] = {0.0f, 0.0f};
     if (e_cur >= 0) {
@@ -646,16 +652,16 @@ decode_down_kernel(const DecodeDownParams p) {
     }
   }
   __syncthreads();
-  if (tid < 32 && n0 + tid < p.H) {
+  if (tid < 32) {
     float acc = 0.0f;
     for (int k = 0; k < p.top_k; ++k) {
-      const int r = t * p.top_k + k;
-      if (local_id(p.ids[r], p.E, p.off) < 0) continue;  // invalid route: nothing
+      if (__builtin_amdgcn_readlane(e_lane, k) < 0) continue;  // invalid route: nothing
       float y = s_y[k * nsl][tid];
       for (int sl = 1; sl < nsl; ++sl) y += s_y[k * nsl + sl][tid];
-      acc += p.wts[r] * (16.0f * y);
+      const float wk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wt_lane), k));
+      acc += wk * (16.0f * y);
     }
-    p.out[static_cast<int64_t>(t) * p.H + n0 + tid] = T::from_f32(acc);
+    if (n0 + tid < p.H) p.out[static_cast<int64_t>(t) * p.H + n0 + tid] = T::from_f32(acc);
   }
 }
 
