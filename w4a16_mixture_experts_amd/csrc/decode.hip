@@ -295,8 +295,7 @@ decode_up_kernel(const DecodeUpParams p) {
 // (the activation is applied by the down kernel), which gives 2*I/16
 // workgroups per touched expert.
 // Up to 4 rows per pass sit at MFMA rows 0, 4, 8, 12: result row 4q is
-// element 0 of lane row q, so one FMA per MFMA applies the group scale.  The
-// staged rows are read by lanes c % 4 == 0; the other lanes feed zeros.
+// element 0 of lane row q, so one FMA per MFMA applies the group scale.
 // Memory order: one load of the ids; then, in flight together, every weight,
 // group scale and x value of the wave's slice (raw buffer loads: masked
 // lanes read zeros, so nothing waits on a load before its use).  Each wave
@@ -343,7 +342,6 @@ small_h_kernel(const SmallHParams p) {
   const int kb = w * p.kslice;
   const int ke = min(p.K, kb + p.kslice);
   const int q_row = c >> 2;
-  const bool feed_lane = (c & 3) == 0;
   const u32x4 bconst = {T::kNegOneHalf2, T::kNegOneHalf2, T::kNegOneHalf2, T::kNegOneHalf2};
   const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
 
@@ -397,22 +395,35 @@ small_h_kernel(const SmallHParams p) {
     } else {
       scol_bits = bload4(rs, soff & ~3u, true) >> (16 * (wrow & 1));
     }
+    // every load above is issued before anything below is scheduled (the
+    // scheduler would otherwise sink weight loads next to their use)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NKB; ++i) {
       const int idx = lane + 64 * i;
       const int q = idx / CH, ck = idx - q * CH;
       *reinterpret_cast<u32x4*>(my_x + q * xs + 8 * ck) = permute_a(xv[i]);
     }
-    // the wave reads back only what its own lanes wrote: LDS order suffices
-    const bool feed = feed_lane && q_row < nr;
+    // the wave reads back only what its own lanes wrote: LDS order suffices.
+    // Every lane feeds staged row c / 4: rows 4q of the MFMA carry route q;
+    // the other rows only reach outputs t[1..3], which are never used, and
+    // rows q >= nr are staged zeros whose outputs are never stored.
     const uint16_t* arow = my_x + q_row * xs;
     const float scol = T::to_f32(scol_bits & 0xffffu);
 
+    // A fragments of a block, read one block ahead of their use
+    u32x4 af[2][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) af[0][j] = *reinterpret_cast<const u32x4*>(arow + 32 * j + 8 * g);
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < NKB; ++i) {
-      const int k0 = kb + 128 * i;
-      const int ng = k0 < ke ? min(4, (ke - k0) >> 5) : 0;
+      if (i + 1 < NKB) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          af[(i + 1) & 1][j] =
+              *reinterpret_cast<const u32x4*>(arow + 128 * (i + 1) + 32 * j + 8 * g);
+      }
       uint32_t d[4], d2[4];
       d[0] = bw[i][0]; d[1] = bw[i][1]; d[2] = bw[i][2]; d[3] = bw[i][3];
       if constexpr (GROUP) {
@@ -423,15 +434,11 @@ small_h_kernel(const SmallHParams p) {
         transpose_rows4(d[0], d[2], d2[0], d2[2]);
         transpose_rows4(d[1], d[3], d2[1], d2[3]);
       }
+      // groups past the end of the reduction have zero x and zero weights,
+      // so t = 0 there and the (finite) scale read beside them is harmless
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bool gv = j < ng;
-        const u32x4 av = *reinterpret_cast<const u32x4*>(arow + 128 * i + 32 * j + 8 * g);
-        u32x4 a;
-        a[0] = feed ? av[0] : 0u;
-        a[1] = feed ? av[1] : 0u;
-        a[2] = feed ? av[2] : 0u;
-        a[3] = feed ? av[3] : 0u;
+        const u32x4 a = af[i & 1][j];
         float sc;
         u32x4 bop;
         if constexpr (GROUP) {
@@ -445,7 +452,6 @@ small_h_kernel(const SmallHParams p) {
           const uint32_t hi = (j < 2) ? d[2 * j + 1] : d2[2 * j - 3];
           bop = bytes_to_h16<DT>(lo >> (4 * par), hi >> (4 * par));
         }
-        sc = gv ? sc : 0.0f;
         const f32x4 corr = T::mfma(a, bconst, fzero);
         const f32x4 t = T::mfma(a, bop, corr);
         acc = fmaf(sc, t[0], acc);
