@@ -314,7 +314,8 @@ small_h_kernel(const SmallHParams p) {
   const int nt = blockIdx.x;
   const int r0 = blockIdx.y;
 
-  extern __shared__ uint16_t s_dyn[];  // per wave [kSmallRows][kslice + 8] x, A order
+  extern __shared__ uint16_t s_dyn[];  // per wave [kSmallRows][kslice + 8] x (A order), then
+                                       // per wave [16][32] group scales
   __shared__ float s_red[kSmallWaves][64];
 
   // rows: the routes whose id equals route r0's id (R <= 64: one load, one ballot)
@@ -339,6 +340,7 @@ small_h_kernel(const SmallHParams p) {
   const uint32_t soff = GROUP ? 2u * static_cast<uint32_t>(wrow) * (p.K >> 5) : 2u * wrow;
   const int xs = p.kslice + 8;  // staged x row stride (16 B padding)
   uint16_t* my_x = s_dyn + w * kSmallRows * xs;
+  uint16_t* my_sc = s_dyn + kSmallWaves * kSmallRows * xs + w * 16 * 32;  // [16 rows][32 scales]
   const int kb = w * p.kslice;
   const int ke = min(p.K, kb + p.kslice);
   const int q_row = c >> 2;
@@ -368,7 +370,19 @@ small_h_kernel(const SmallHParams p) {
       const bool ok = q < nr && kb + 8 * ck < ke;
       xv[i] = bload16(rx, 2u * (static_cast<uint32_t>(tq) * p.lda + kb + 8 * ck), ok);
     }
-    // (2) every weight of this wave's slice (kslice <= NKB * 128)
+    // (2) group scales of the slice (at most 64 bytes per row): one 16-byte
+    //     load per lane covers the wave's 16 rows (lane l: row l / 4, part
+    //     l % 4), staged in the wave's own LDS region
+    u32x4 scv;
+    uint32_t scol_bits = 0;
+    if constexpr (GROUP) {
+      const uint32_t so = 2u * (static_cast<uint32_t>(nt * 16 + (lane >> 2)) * (p.K >> 5) +
+                                (kb >> 5)) + 16u * (lane & 3);
+      scv = bload16(rs, so, kb < p.K);
+    } else {
+      scol_bits = bload4(rs, soff & ~3u, true) >> (16 * (wrow & 1));
+    }
+    // (3) every weight of this wave's slice (kslice <= NKB * 128)
     u32x4 bw[NKB];
     u32x4 bw2[GROUP ? 1 : NKB];
 #pragma unroll
@@ -382,19 +396,6 @@ small_h_kernel(const SmallHParams p) {
         bw2[i] = bload16(rw, boff + k0 + 32 * g + 16, g < ng);
       }
     }
-    // (3) group scales of the slice: 4 per block (8 bytes) of row wrow
-    u32x2 sc2[GROUP ? NKB : 1];
-    uint32_t scol_bits = 0;
-    if constexpr (GROUP) {
-#pragma unroll
-      for (int i = 0; i < NKB; ++i) {
-        const int k0 = kb + 128 * i;
-        sc2[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                               rs, k0 < ke ? soff + 2u * (k0 >> 5) : kOob, 0, 0));
-      }
-    } else {
-      scol_bits = bload4(rs, soff & ~3u, true) >> (16 * (wrow & 1));
-    }
     // every load above is issued before anything below is scheduled (the
     // scheduler would otherwise sink weight loads next to their use)
     __builtin_amdgcn_sched_barrier(0);
@@ -404,6 +405,7 @@ small_h_kernel(const SmallHParams p) {
       const int q = idx / CH, ck = idx - q * CH;
       *reinterpret_cast<u32x4*>(my_x + q * xs + 8 * ck) = permute_a(xv[i]);
     }
+    if constexpr (GROUP) *reinterpret_cast<u32x4*>(my_sc + 8 * lane) = scv;
     // the wave reads back only what its own lanes wrote: LDS order suffices.
     // Every lane feeds staged row c / 4: rows 4q of the MFMA carry route q;
     // the other rows only reach outputs t[1..3], which are never used, and
@@ -434,6 +436,8 @@ small_h_kernel(const SmallHParams p) {
         transpose_rows4(d[0], d[2], d2[0], d2[2]);
         transpose_rows4(d[1], d[3], d2[1], d2[3]);
       }
+      u32x2 sc2 = {0u, 0u};
+      if constexpr (GROUP) sc2 = *reinterpret_cast<const u32x2*>(my_sc + 32 * c + 4 * i);
       // groups past the end of the reduction have zero x and zero weights,
       // so t = 0 there and the (finite) scale read beside them is harmless
 #pragma unroll
@@ -442,7 +446,7 @@ small_h_kernel(const SmallHParams p) {
         float sc;
         u32x4 bop;
         if constexpr (GROUP) {
-          const uint32_t pair = sc2[i][j >> 1];
+          const uint32_t pair = sc2[j >> 1];
           sc = T::to_f32((j & 1) ? (pair >> 16) : (pair & 0xffffu));
           bop = nibbles_to_h16<DT>(d[j]);
         } else {

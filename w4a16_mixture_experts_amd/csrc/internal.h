@@ -59,7 +59,7 @@ constexpr int kSmallThreads = kSmallWaves * 64;
 constexpr int kSmallRows = 4;             // token rows per pass (MFMA rows 0, 4, 8, 12)
 constexpr int kSmallMaxSlice = 1024;      // reduction per slice: hidden <= 8 * 1024
 inline size_t small_h_lds_bytes(int kslice) {
-  return sizeof(uint16_t) * static_cast<size_t>(kSmallWaves) * kSmallRows * (kslice + 8);
+  return sizeof(uint16_t) * static_cast<size_t>(kSmallWaves) * (kSmallRows * (kslice + 8) + 16 * 32);
 }
 
 struct SmallHParams {
