@@ -44,6 +44,12 @@ constexpr int kXcds = 8;
 constexpr int kWRing = 2;                    // weight blocks in registers (1 in flight)
 constexpr int kNsub = 2;                     // 16-row weight subtiles per wave
 constexpr int kSplitkRing = 4;               // split-K: weight blocks in registers
+constexpr int kSplitkXLoads = 10;            // split-K: staged x chunks per thread (cb <= 19)
+// streaming tile kernel with LDS-staged group scales: 16-byte chunks per
+// thread (256 rows x K/32 scales; K/32 <= 16 * kScLoads) and the LDS it needs
+constexpr int kScLoads = 15;
+constexpr int kScMaxGroups = 16 * kScLoads;
+inline size_t tile_scale_lds_bytes(int K) { return sizeof(uint16_t) * 256 * static_cast<size_t>(K / 32); }
 
 template <int DT>
 __device__ __forceinline__ float scale_lo(uint32_t pair) { return H16<DT>::to_f32(pair & 0xffffu); }
@@ -79,8 +85,9 @@ struct WBlk {
 // bytes; fetched per block, every scale load of a wave touches 16 cache lines
 // for 128 useful bytes, and that dominated the weight stream.  So blocks come
 // in pairs: the first block of a pair loads 16 bytes (both blocks' scales) and
-// hands the second half to its partner (pass_scales).
-enum : int { SC_SINGLE = 0, SC_PAIR_FIRST = 1, SC_PAIR_SECOND = 2 };
+// hands the second half to its partner (pass_scales).  SC_NONE loads no
+// scales: the streaming tile kernel reads them from LDS.
+enum : int { SC_SINGLE = 0, SC_PAIR_FIRST = 1, SC_PAIR_SECOND = 2, SC_NONE = 3 };
 
 // One expert's packed weights and scales (wave-uniform), and where a wave's
 // NSUB subtiles sit in them (per lane).
@@ -229,6 +236,63 @@ __device__ __forceinline__ void mma_block(const uint16_t* sa, int stride,
   }
 }
 
+// mma_block with the group scales taken from the first block of the pair
+// (`second` selects its upper half); per-channel layouts use wb's own scale.
+template <int DT, int LAYOUT, int NMS, int NSUB>
+__device__ __forceinline__ void mma_block2(const uint16_t* sa, int stride,
+                                           const WBlk<LAYOUT> (&wb)[NSUB],
+                                           const WBlk<LAYOUT> (&wsc)[NSUB], int second,
+                                           f32x4 (&acc)[NMS][NSUB], int c, int g, int par) {
+  using T = H16<DT>;
+  constexpr bool GROUP = LAYOUT == Q_GROUP_K;
+  __builtin_amdgcn_sched_barrier(0);
+  const u32x4 bconst = {T::kNegOneHalf2, T::kNegOneHalf2, T::kNegOneHalf2, T::kNegOneHalf2};
+  const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
+  u32x4 af[NMS][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int ms = 0; ms < NMS; ++ms)
+      af[ms][j] = *reinterpret_cast<const u32x4*>(sa + (16 * ms + c) * stride + 32 * j + 8 * g);
+  uint32_t d[NSUB][8];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    d[s][0] = wb[s].d[0]; d[s][1] = wb[s].d[1]; d[s][2] = wb[s].d[2]; d[s][3] = wb[s].d[3];
+    if constexpr (GROUP) {
+      transpose_rows4(d[s][0], d[s][1], d[s][2], d[s][3]);
+    } else {
+      d[s][4] = wb[s].d2[0]; d[s][5] = wb[s].d2[1]; d[s][6] = wb[s].d2[2]; d[s][7] = wb[s].d2[3];
+      transpose_rows4(d[s][0], d[s][2], d[s][4], d[s][6]);
+      transpose_rows4(d[s][1], d[s][3], d[s][5], d[s][7]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    u32x4 bop[NSUB];
+    float sc[NSUB];
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      if constexpr (GROUP) {
+        bop[s] = nibbles_to_h16<DT>(d[s][j]);
+        const uint32_t pr = second ? ((j < 2) ? wsc[s].s2 : wsc[s].s3)
+                                   : ((j < 2) ? wsc[s].s0 : wsc[s].s1);
+        sc[s] = (j & 1) ? scale_hi<DT>(pr) : scale_lo<DT>(pr);
+      } else {
+        bop[s] = bytes_to_h16<DT>(d[s][2 * j] >> (4 * par), d[s][2 * j + 1] >> (4 * par));
+        sc[s] = par ? scale_hi<DT>(wb[s].s0) : scale_lo<DT>(wb[s].s0);
+      }
+    }
+    f32x4 t[NMS][NSUB];
+#pragma unroll
+    for (int ms = 0; ms < NMS; ++ms) {
+      const f32x4 corr = T::mfma(af[ms][j], bconst, fzero);
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) t[ms][s] = T::mfma(af[ms][j], bop[s], corr);
+    }
+    scale_accumulate<NMS, NSUB>(acc, t, sc);
+  }
+}
+
 // Valid rows of the lane's 16 * NMS output rows as a bit mask: bit 4ms + i
 // stands for tile row 16ms + 4g + i.
 template <int NMS>
@@ -317,9 +381,10 @@ __device__ __forceinline__ int active_subtiles(const GemmParams& p, int row_base
 // block into a double-buffered LDS tile.
 // ---------------------------------------------------------------------------
 
-template <int DT, int LAYOUT, int MODE, int NMS>
+template <int DT, int LAYOUT, int MODE, int NMS, bool SCL>
 __device__ __forceinline__ void tile_run(const GemmParams& p, const int row_base, const int e,
-                                         const int nt, uint16_t (*s_a)[kTileRows][kAStride]) {
+                                         const int nt, uint16_t (*s_a)[kTileRows][kAStride],
+                                         uint16_t* s_sc) {
   constexpr bool UP = MODE != MODE_DOWN;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int c = lane & 15, g = lane >> 4, par = c & 1;
@@ -371,6 +436,75 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, const int row_base
   // compile-time indices); steps past the last block only issue masked loads.
   WBlk<LAYOUT> wr[kWRing][kNsub];
   u32x4 ar[2][kChunks];
+  const int nblk = (p.K + 127) >> 7;
+  if constexpr (SCL) {
+    // Group scales of the workgroup's 256 weight rows for the whole
+    // reduction, staged once: every row's scales are contiguous, and so are
+    // the rows of a range (gated: the 128 gate rows, then the 128 up rows),
+    // so the copy is linear and every load instruction covers whole cache
+    // lines.  Fetched per block from HBM, each scale load touched 16 lines
+    // for 128 useful bytes, and that cost a fifth of the kernel.
+    const int gpr = p.K >> 5;                        // groups (scales) per row
+    const uint32_t rbytes = 2u * gpr;                // bytes per row
+    const int nranges = MODE == MODE_UP_GATED ? 2 : 1;
+    const int rrows = MODE == MODE_UP_GATED ? 128 : 256;     // rows per range
+    const uint32_t rchunks = static_cast<uint32_t>(rrows) * rbytes / 16;  // 16-byte chunks per range
+    u32x4 sv[kScLoads];
+#pragma unroll
+    for (int i = 0; i < kScLoads; ++i) {
+      const uint32_t ch = static_cast<uint32_t>(tid + kTileThreads * i);
+      const int rg = ch < rchunks ? 0 : 1;
+      const uint32_t lc = ch - rg * rchunks;
+      const int row0 = MODE == MODE_UP_GATED ? (rg ? p.up_rows : 0) + nt * kTileColsGated
+                                             : nt * kTileColsPlain;
+      sv[i] = bload16(wx.rs, static_cast<uint32_t>(row0) * rbytes + 16u * lc,
+                      rg < nranges && lc < rchunks);
+    }
+    load_a(0, ar[0]);
+    load_a(128, ar[1]);
+    load_wblk<LAYOUT, kNsub, SC_NONE>(wx, ws, 0, p.K, g, wr[0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kScLoads; ++i) {
+      const uint32_t ch = static_cast<uint32_t>(tid + kTileThreads * i);
+      if (ch < static_cast<uint32_t>(nranges) * rchunks)
+        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(s_sc) + 16u * ch) = sv[i];
+    }
+    store_a(0, ar[0]);
+    load_a(256, ar[0]);
+    __syncthreads();
+
+    // LDS rows of this lane's two weight rows
+    int lrow[kNsub];
+#pragma unroll
+    for (int s2 = 0; s2 < kNsub; ++s2)
+      lrow[s2] = MODE == MODE_UP_GATED ? 128 * s2 + 16 * w + c : 32 * w + 16 * s2 + c;
+    auto set_scales = [&](int blk, WBlk<LAYOUT> (&b)[kNsub]) {
+#pragma unroll
+      for (int s2 = 0; s2 < kNsub; ++s2) {
+        const uint32_t* sp =
+            reinterpret_cast<const uint32_t*>(s_sc + lrow[s2] * gpr + 4 * blk);
+        b[s2].s0 = sp[0];
+        b[s2].s1 = sp[1];
+      }
+    };
+    for (int blk0 = 0; blk0 < nblk; blk0 += 2) {
+      load_wblk<LAYOUT, kNsub, SC_NONE>(wx, ws, 128 * (blk0 + 1), p.K, g, wr[1]);
+      set_scales(blk0, wr[0]);
+      mma_block<DT, LAYOUT, NMS>(&s_a[0][0][0], kAStride, wr[0], acc, c, g, par);
+      store_a(1, ar[1]);
+      load_a(128 * (blk0 + 3), ar[1]);
+      __syncthreads();
+      load_wblk<LAYOUT, kNsub, SC_NONE>(wx, ws, 128 * (blk0 + 2), p.K, g, wr[0]);
+      if (blk0 + 1 < nblk) {
+        set_scales(blk0 + 1, wr[1]);
+        mma_block<DT, LAYOUT, NMS>(&s_a[1][0][0], kAStride, wr[1], acc, c, g, par);
+      }
+      store_a(0, ar[0]);
+      load_a(128 * (blk0 + 4), ar[0]);
+      __syncthreads();
+    }
+  } else {
   load_a(0, ar[0]);
   load_a(128, ar[1]);
   static_assert(kWRing == 2, "blocks pair up with the ring (scales per block pair)");
@@ -379,7 +513,6 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, const int row_base
   load_a(256, ar[0]);
   __syncthreads();
 
-  const int nblk = (p.K + 127) >> 7;
   for (int blk0 = 0; blk0 < nblk; blk0 += 2) {
     // even block blk0 (first of its pair) in wr[0], odd block in wr[1]
     load_wblk<LAYOUT, kNsub, SC_PAIR_SECOND>(wx, ws, 128 * (blk0 + 1), p.K, g, wr[1]);
@@ -395,13 +528,16 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, const int row_base
     load_a(128 * (blk0 + 4), ar[0]);
     __syncthreads();
   }
+  }
   store_outputs<DT, MODE, NMS>(p, row_base, acc, col, on, g, valid_rows<NMS>(p, row_base, g));
 }
 
-template <int DT, int LAYOUT, int MODE>
+template <int DT, int LAYOUT, int MODE, bool SCL>
 __global__ void __launch_bounds__(kTileThreads)
 tile_gemm_kernel(const GemmParams p) {
   __shared__ uint16_t s_a[2][kTileRows][kAStride];
+  extern __shared__ uint16_t s_dyn[];  // SCL: [256 rows][K / 32] group scales
+  uint16_t* s_sc = SCL ? s_dyn : nullptr;
 
   // workgroup L runs on XCD L % 8; XCD x takes tiles x, x + 8, ... and walks
   // the column tiles of each tile back to back
@@ -414,10 +550,10 @@ tile_gemm_kernel(const GemmParams p) {
   const int nms = active_subtiles(p, row_base);
   const int e = p.tile_expert[mt];
   switch (nms) {
-    case 1: tile_run<DT, LAYOUT, MODE, 1>(p, row_base, e, nt, s_a); break;
-    case 2: tile_run<DT, LAYOUT, MODE, 2>(p, row_base, e, nt, s_a); break;
-    case 3: tile_run<DT, LAYOUT, MODE, 3>(p, row_base, e, nt, s_a); break;
-    default: tile_run<DT, LAYOUT, MODE, 4>(p, row_base, e, nt, s_a); break;
+    case 1: tile_run<DT, LAYOUT, MODE, 1, SCL>(p, row_base, e, nt, s_a, s_sc); break;
+    case 2: tile_run<DT, LAYOUT, MODE, 2, SCL>(p, row_base, e, nt, s_a, s_sc); break;
+    case 3: tile_run<DT, LAYOUT, MODE, 3, SCL>(p, row_base, e, nt, s_a, s_sc); break;
+    default: tile_run<DT, LAYOUT, MODE, 4, SCL>(p, row_base, e, nt, s_a, s_sc); break;
   }
 }
 
@@ -586,20 +722,31 @@ up_splitk_kernel(const GemmParams p) {
 
   for (int rp = 0; rp < nms; ++rp) {
     if (rp > 0) __syncthreads();  // the previous subtile's rows are no longer read
-    // stage x rows of subtile rp over the chunk, in A operand order
+    // stage x rows of subtile rp over the chunk, in A operand order: the
+    // token of each of the 16 rows (lane l: row l % 16), then every x chunk
+    // in flight at once, then the LDS stores
     const int nch = (b1 - b0) * 16;
-    for (int idx = tid; idx < 16 * nch; idx += kTileThreads) {
-      const int row = idx / nch, ch = idx % nch;
-      const int r = p.sorted[row_base + 16 * rp + row];
-      const bool ok = r >= 0 && 128 * b0 + 8 * ch < p.K;
-      const u32x4 v = bload16(xr, 2u * static_cast<uint32_t>((ok ? r / p.top_k : 0) * p.lda +
-                                                             128 * b0 + 8 * ch), ok);
-      *reinterpret_cast<u32x4*>(s_x + row * stride + 8 * ch) = permute_a(v);
+    const int my_r = p.sorted[row_base + 16 * rp + c];
+    const int my_tok = my_r >= 0 ? my_r / p.top_k : -1;
+    u32x4 xv[kSplitkXLoads];
+#pragma unroll
+    for (int i = 0; i < kSplitkXLoads; ++i) {
+      const int idx = tid + kTileThreads * i;
+      const int row = idx / nch, ch = idx - row * nch;
+      const int tok = __shfl(my_tok, row & 15);
+      const bool ok = idx < 16 * nch && tok >= 0 && 128 * b0 + 8 * ch < p.K;
+      xv[i] = bload16(xr, 2u * static_cast<uint32_t>((ok ? tok : 0) * p.lda + 128 * b0 + 8 * ch), ok);
+    }
+#pragma unroll
+    for (int i = 0; i < kSplitkXLoads; ++i) {
+      const int idx = tid + kTileThreads * i;
+      const int row = idx / nch, ch = idx - row * nch;
+      if (idx < 16 * nch) *reinterpret_cast<u32x4*>(s_x + row * stride + 8 * ch) = permute_a(xv[i]);
     }
     __syncthreads();
     int rts[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rts[i] = p.sorted[row_base + 16 * rp + 4 * g + i];
+    for (int i = 0; i < 4; ++i) rts[i] = __shfl(my_r, 4 * g + i);
 
     const int n_end = min(p.n_cols, (cc + 1) * p.col_steps * kPassRows);
     for (int n0 = cc * p.col_steps * kPassRows; n0 < n_end; n0 += kPassRows) {
@@ -632,12 +779,17 @@ up_splitk_kernel(const GemmParams p) {
       for (int b = b0; b < b1; b += kSplitkRing) {
 #pragma unroll
         for (int u = 0; u < kSplitkRing; ++u) {
-          load_i(b - b0 + u + kSplitkRing - 1, (u + kSplitkRing - 1) % kSplitkRing,
-                 (u + kSplitkRing - 1) % 2 == 0);
+          // the second block of a pair reads its scales from the first
+          // block's registers, so the load that refills that slot (the next
+          // pair's first block) is issued after it; no scale register is
+          // copied, and every register keeps its place around the loop
+          if (u % 2 == 0)
+            load_i(b - b0 + u + kSplitkRing - 1, (u + kSplitkRing - 1) % kSplitkRing, false);
           if (b + u < b1)
-            mma_block<DT, LAYOUT, 1, true, NSUB>(s_x + 128 * (b + u - b0), stride, wr[u], acc, c,
-                                                 g, par);
-          if (u % 2 == 0) pass_scales<LAYOUT, NSUB>(wr[u], wr[u + 1]);
+            mma_block2<DT, LAYOUT, 1, NSUB>(s_x + 128 * (b + u - b0), stride, wr[u], wr[u & ~1],
+                                            u % 2, acc, c, g, par);
+          if (u % 2 == 1)
+            load_i(b - b0 + u + kSplitkRing - 1, (u + kSplitkRing - 1) % kSplitkRing, true);
         }
       }
       // FP32 partials of valid rows: lane (c, g) holds rows 4g + i, row wrow[s]
@@ -699,8 +851,8 @@ splitk_act_kernel(const GemmParams p) {
 }
 
 template <typename F>
-static hipError_t allow_lds_tile(F* kernel, size_t lds) {
-  if (lds <= 65536) return hipSuccess;
+static hipError_t allow_lds_tile(F* kernel, size_t lds, size_t static_lds = 0) {
+  if (lds + static_lds <= 65536) return hipSuccess;
   return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
 }
@@ -744,7 +896,19 @@ hipError_t launch_splitk_act(const GemmParams& p, int dtype, bool gated, hipStre
 
 template <int DT, int LAYOUT, int MODE>
 static hipError_t launch_tile_k(const GemmParams& p, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((tile_gemm_kernel<DT, LAYOUT, MODE>), grid, dim3(kTileThreads), 0, st, p);
+  // group scales staged in LDS when they fit (every group layout up to
+  // K = 32 * kScMaxGroups); otherwise fetched per block pair
+  if (LAYOUT == Q_GROUP_K && p.K / 32 <= kScMaxGroups) {
+    const size_t lds = tile_scale_lds_bytes(p.K);
+    const hipError_t err = allow_lds_tile(tile_gemm_kernel<DT, LAYOUT, MODE, true>, lds,
+                                          sizeof(uint16_t) * 2 * kTileRows * kAStride);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((tile_gemm_kernel<DT, LAYOUT, MODE, true>), grid, dim3(kTileThreads), lds, st,
+                       p);
+  } else {
+    hipLaunchKernelGGL((tile_gemm_kernel<DT, LAYOUT, MODE, false>), grid, dim3(kTileThreads), 0,
+                       st, p);
+  }
   return hipGetLastError();
 }
 
