@@ -45,6 +45,7 @@ constexpr int kWRing = 2;                    // weight blocks in registers (1 in
 constexpr int kNsub = 2;                     // 16-row weight subtiles per wave
 constexpr int kSplitkRing = 4;               // split-K: weight blocks in registers
 constexpr int kSplitkXLoads = 10;            // split-K: staged x chunks per thread (cb <= 19)
+constexpr int kSplitkScLoads = 10;           // split-K: 8-byte scale loads per lane (32 rows x cb <= 640)
 // streaming tile kernel with LDS-staged group scales: 16-byte chunks per
 // thread (256 rows x K/32 scales; K/32 <= 16 * kScLoads) and the LDS it needs
 constexpr int kScLoads = 15;
@@ -698,7 +699,7 @@ down_resident_kernel(const GemmParams p) {
 template <int DT, int LAYOUT, int NSUB>
 __global__ void __launch_bounds__(kTileThreads)
 up_splitk_kernel(const GemmParams p) {
-  extern __shared__ uint16_t s_x[];   // [16][cb * 128 + 8]
+  extern __shared__ uint16_t s_x[];   // [16][cb * 128 + 8], then per wave [32][4 * cb] scales
   // workgroup = (tile, reduction chunk, column chunk of p.col_steps passes)
   const int nchunk = p.n_tiles;
   const int mt = blockIdx.x / (p.S * nchunk);
@@ -762,34 +763,82 @@ up_splitk_kernel(const GemmParams p) {
       f32x4 acc[1][NSUB];
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) acc[0][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // ring of kSplitkRing register sets: block b + kSplitkRing - 1 is
-      // requested while block b is computed (loads past the chunk are masked)
-      // (b0 is even: blocks pair up for their scales, see SC_PAIR_FIRST)
       static_assert(kSplitkRing % 2 == 0, "block pairs must not straddle the ring");
       WBlk<LAYOUT> wr[kSplitkRing][NSUB];
-      // block b0 + i into wr[slot]; `first` = i is even (a constant after unrolling)
-      auto load_i = [&](int i, int slot, bool first) {
-        if (first)
-          load_wblk<LAYOUT, NSUB, SC_PAIR_FIRST>(wx, ws, 128 * (b0 + i), kend, g, wr[slot]);
-        else
-          load_wblk<LAYOUT, NSUB, SC_PAIR_SECOND>(wx, ws, 128 * (b0 + i), kend, g, wr[slot]);
-      };
+      if constexpr (LAYOUT == Q_GROUP_K) {
+        // group scales of the wave's 32 rows over the chunk, staged in the
+        // wave's own LDS region (read back only by the wave: no barrier);
+        // 8 bytes (4 groups) per row and block
+        const int nb = b1 - b0;
+        uint16_t* my_sc = s_x + 16 * stride + w * 32 * 4 * p.cb;  // [32 rows][4 * cb]
+        {
+          u32x2 sv[kSplitkScLoads];
 #pragma unroll
-      for (int i = 0; i < kSplitkRing - 1; ++i) load_i(i, i, i % 2 == 0);
-      for (int b = b0; b < b1; b += kSplitkRing) {
+          for (int i = 0; i < kSplitkScLoads; ++i) {
+            const int idx = lane + 64 * i;           // (row, block) = (idx / nb, idx % nb)
+            const int row = idx / nb, blk = idx - row * nb;
+            const int grow = n0 + 16 * w * NSUB + row;  // weight row
+            const bool ok = row < 32 && grow < p.n_cols;
+            const uint32_t so = 2u * (static_cast<uint32_t>(grow) * (p.K >> 5) + 4 * (b0 + blk));
+            sv[i] = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_raw_buffer_load_b64(wx.rs, ok ? so : kOob, 0, 0));
+          }
+          // the first weight blocks go out before the scales are stored
 #pragma unroll
-        for (int u = 0; u < kSplitkRing; ++u) {
-          // the second block of a pair reads its scales from the first
-          // block's registers, so the load that refills that slot (the next
-          // pair's first block) is issued after it; no scale register is
-          // copied, and every register keeps its place around the loop
-          if (u % 2 == 0)
-            load_i(b - b0 + u + kSplitkRing - 1, (u + kSplitkRing - 1) % kSplitkRing, false);
-          if (b + u < b1)
-            mma_block2<DT, LAYOUT, 1, NSUB>(s_x + 128 * (b + u - b0), stride, wr[u], wr[u & ~1],
-                                            u % 2, acc, c, g, par);
-          if (u % 2 == 1)
-            load_i(b - b0 + u + kSplitkRing - 1, (u + kSplitkRing - 1) % kSplitkRing, true);
+          for (int i = 0; i < kSplitkRing - 1; ++i)
+            load_wblk<LAYOUT, NSUB, SC_NONE>(wx, ws, 128 * (b0 + i), kend, g, wr[i]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < kSplitkScLoads; ++i) {
+            const int idx = lane + 64 * i;
+            const int row = idx / nb, blk = idx - row * nb;
+            if (row < 32) *reinterpret_cast<u32x2*>(my_sc + row * 4 * p.cb + 4 * blk) = sv[i];
+          }
+        }
+        for (int b = b0; b < b1; b += kSplitkRing) {
+#pragma unroll
+          for (int u = 0; u < kSplitkRing; ++u) {
+            load_wblk<LAYOUT, NSUB, SC_NONE>(wx, ws, 128 * (b + u + kSplitkRing - 1), kend, g,
+                                             wr[(u + kSplitkRing - 1) % kSplitkRing]);
+            if (b + u < b1) {
+#pragma unroll
+              for (int s2 = 0; s2 < NSUB; ++s2) {
+                const u32x2 sp = *reinterpret_cast<const u32x2*>(
+                    my_sc + (16 * s2 + c) * 4 * p.cb + 4 * (b + u - b0));
+                wr[u][s2].s0 = sp[0];
+                wr[u][s2].s1 = sp[1];
+              }
+              mma_block<DT, LAYOUT, 1, true, NSUB>(s_x + 128 * (b + u - b0), stride, wr[u], acc, c,
+                                                   g, par);
+            }
+          }
+        }
+      } else {
+        // ring of kSplitkRing register sets: block b + kSplitkRing - 1 is
+        // requested while block b is computed (loads past the chunk are
+        // masked); block b0 + i into wr[slot], `first` = i is even
+        auto load_i = [&](int i, int slot, bool first) {
+          if (first)
+            load_wblk<LAYOUT, NSUB, SC_PAIR_FIRST>(wx, ws, 128 * (b0 + i), kend, g, wr[slot]);
+          else
+            load_wblk<LAYOUT, NSUB, SC_PAIR_SECOND>(wx, ws, 128 * (b0 + i), kend, g, wr[slot]);
+        };
+#pragma unroll
+        for (int i = 0; i < kSplitkRing - 1; ++i) load_i(i, i, i % 2 == 0);
+        for (int b = b0; b < b1; b += kSplitkRing) {
+#pragma unroll
+          for (int u = 0; u < kSplitkRing; ++u) {
+            // the second block of a pair reads its scales from the first
+            // block's registers, so the load that refills that slot (the
+            // next pair's first block) is issued after it
+            if (u % 2 == 0)
+              load_i(b - b0 + u + kSplitkRing - 1, (u + kSplitkRing - 1) % kSplitkRing, false);
+            if (b + u < b1)
+              mma_block2<DT, LAYOUT, 1, NSUB>(s_x + 128 * (b + u - b0), stride, wr[u], wr[u & ~1],
+                                              u % 2, acc, c, g, par);
+            if (u % 2 == 1)
+              load_i(b - b0 + u + kSplitkRing - 1, (u + kSplitkRing - 1) % kSplitkRing, true);
+          }
         }
       }
       // FP32 partials of valid rows: lane (c, g) holds rows 4g + i, row wrow[s]
@@ -859,7 +908,9 @@ static hipError_t allow_lds_tile(F* kernel, size_t lds, size_t static_lds = 0) {
 
 template <int DT, int LAYOUT>
 static hipError_t launch_splitk_dl(const GemmParams& p, int max_tiles, hipStream_t st) {
-  const size_t lds = sizeof(uint16_t) * 16 * (static_cast<size_t>(p.cb) * 128 + 8);
+  // x slice [16][cb * 128 + 8], then (group layout) per wave [32][4 * cb] scales
+  const size_t lds = sizeof(uint16_t) * (16 * (static_cast<size_t>(p.cb) * 128 + 8) +
+                                         (LAYOUT == Q_GROUP_K ? kTileWaves * 32 * 4 * p.cb : 0));
   const hipError_t err = allow_lds_tile(up_splitk_kernel<DT, LAYOUT, kSplitkNsub>, lds);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((up_splitk_kernel<DT, LAYOUT, kSplitkNsub>),
@@ -870,7 +921,8 @@ static hipError_t launch_splitk_dl(const GemmParams& p, int max_tiles, hipStream
 hipError_t launch_up_splitk(const GemmParams& p, int dtype, int layout, int max_tiles,
                             hipStream_t stream) {
   if (p.S < 1 || p.cb < 1 || p.n_tiles < 1 || p.col_steps < 1 ||
-      16 * (p.cb * 128 + 8) * 2 > kSplitkMaxLds ||
+      16 * (p.cb * 128 + 8) * 2 > kSplitkMaxLds || 16 * 16 * p.cb > kSplitkXLoads * kTileThreads ||
+      32 * p.cb > 64 * kSplitkScLoads ||
       static_cast<int64_t>(max_tiles) * p.S * p.n_tiles > 0x7fffffff)
     return hipErrorInvalidValue;
   if (dtype == DT_BF16)
