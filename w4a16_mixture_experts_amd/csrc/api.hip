@@ -459,6 +459,7 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
     up.n_cols = I;
     up.up_rows = I;
     up.tile_expert = tile;
+    up.tiles = static_cast<int>(pl.MT);
     up.offsets = offsets;
     up.E = E;
     up.bm = pl.bm;
@@ -505,6 +506,7 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
   dn.n_cols = H;
   dn.up_rows = 0;
   dn.tile_expert = tile;
+  dn.tiles = static_cast<int>(pl.MT);
   dn.offsets = offsets;
   dn.E = E;
   dn.bm = pl.bm;

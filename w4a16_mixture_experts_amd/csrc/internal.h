@@ -46,6 +46,7 @@ struct GemmParams {
   int cb;                     // 128-blocks per chunk
   int R;                      // routes (T*K)
   const int32_t* slot;        // [R] route -> position, -1 for invalid routes
+  int tiles;                  // entries of tile_expert (positions / bm)
 };
 
 // small-batch path

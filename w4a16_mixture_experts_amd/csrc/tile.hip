@@ -385,7 +385,7 @@ __device__ __forceinline__ int active_subtiles(const GemmParams& p, int row_base
 template <int DT, int LAYOUT, int MODE, int NMS, bool SCL>
 __device__ __forceinline__ void tile_run(const GemmParams& p, const int row_base, const int e,
                                          const int nt, uint16_t (*s_a)[kTileRows][kAStride],
-                                         uint16_t* s_sc) {
+                                         uint16_t* s_sc, const int st_r) {
   constexpr bool UP = MODE != MODE_DOWN;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int c = lane & 15, g = lane >> 4, par = c & 1;
@@ -402,8 +402,7 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, const int row_base
   constexpr int kChunks = kVals / 8;                     // 16-byte loads per thread
   constexpr int kPerRow = 128 / kVals;
   static_assert(kVals == 32 || kVals == 16, "16 or 32 staged values per thread");
-  const int st_row = tid / kPerRow, st_c = tid % kPerRow;
-  const int st_r = p.sorted[row_base + st_row];
+  const int st_row = tid / kPerRow, st_c = tid % kPerRow;  // st_r = sorted[row_base + st_row]
   const bool st_ok = st_r >= 0;
   const auto ra = UP ? make_rsrc(p.a, p.a_bytes)
                      : make_rsrc(p.a + static_cast<int64_t>(row_base) * p.lda,
@@ -547,14 +546,29 @@ tile_gemm_kernel(const GemmParams p) {
   const int mt = kXcds * (q / p.n_tiles) + L % kXcds;
   const int nt = q % p.n_tiles;
   const int row_base = mt * kTileRows;
-  if (row_base >= p.offsets[p.E]) return;  // whole workgroup: tile past the padded total
-  const int nms = active_subtiles(p, row_base);
-  const int e = p.tile_expert[mt];
+  // every index the workgroup needs comes in one batch of loads before the
+  // first decision (a tile past the padded total reads a clamped tile)
+  const int rb = min(mt, p.tiles - 1) * kTileRows;
+  const int total = p.offsets[p.E];
+  const int e = p.tile_expert[rb / kTileRows];
+  int first[kTileMs];
+#pragma unroll
+  for (int ms = 0; ms < kTileMs; ++ms) first[ms] = p.sorted[rb + 16 * ms];
+  constexpr int kPerRow = 128 / (kTileRows * 128 / kTileThreads);  // staging threads per row
+  const int st_r = p.sorted[rb + static_cast<int>(threadIdx.x) / kPerRow];
+  // an empty statement that reads every index keeps the compiler from moving
+  // the loads behind the exit below (one round trip instead of several)
+  asm volatile("" : : "s"(total), "s"(e), "s"(first[0]), "s"(first[1]), "s"(first[2]), "s"(first[3]),
+               "v"(st_r));
+  if (row_base >= total) return;  // whole workgroup: tile past the padded total
+  int nms = 0;
+#pragma unroll
+  for (int ms = 0; ms < kTileMs; ++ms) nms += first[ms] >= 0 ? 1 : 0;
   switch (nms) {
-    case 1: tile_run<DT, LAYOUT, MODE, 1, SCL>(p, row_base, e, nt, s_a, s_sc); break;
-    case 2: tile_run<DT, LAYOUT, MODE, 2, SCL>(p, row_base, e, nt, s_a, s_sc); break;
-    case 3: tile_run<DT, LAYOUT, MODE, 3, SCL>(p, row_base, e, nt, s_a, s_sc); break;
-    default: tile_run<DT, LAYOUT, MODE, 4, SCL>(p, row_base, e, nt, s_a, s_sc); break;
+    case 1: tile_run<DT, LAYOUT, MODE, 1, SCL>(p, row_base, e, nt, s_a, s_sc, st_r); break;
+    case 2: tile_run<DT, LAYOUT, MODE, 2, SCL>(p, row_base, e, nt, s_a, s_sc, st_r); break;
+    case 3: tile_run<DT, LAYOUT, MODE, 3, SCL>(p, row_base, e, nt, s_a, s_sc, st_r); break;
+    default: tile_run<DT, LAYOUT, MODE, 4, SCL>(p, row_base, e, nt, s_a, s_sc, st_r); break;
   }
 }
 
@@ -676,9 +690,19 @@ down_resident_kernel(const GemmParams p) {
   const int mt = kXcds * (q / p.n_tiles) + L % kXcds;
   const int chunk = q % p.n_tiles;
   const int row_base = mt * kTileRows;
-  if (row_base >= p.offsets[p.E]) return;
-  const int nms = active_subtiles(p, row_base);
-  const int e = p.tile_expert[mt];
+  // every index the workgroup needs comes in one batch of loads before the
+  // first decision (see tile_gemm_kernel)
+  const int rb = min(mt, p.tiles - 1) * kTileRows;
+  const int total = p.offsets[p.E];
+  const int e = p.tile_expert[rb / kTileRows];
+  int first[kTileMs];
+#pragma unroll
+  for (int ms = 0; ms < kTileMs; ++ms) first[ms] = p.sorted[rb + 16 * ms];
+  asm volatile("" : : "s"(total), "s"(e), "s"(first[0]), "s"(first[1]), "s"(first[2]), "s"(first[3]));
+  if (row_base >= total) return;
+  int nms = 0;
+#pragma unroll
+  for (int ms = 0; ms < kTileMs; ++ms) nms += first[ms] >= 0 ? 1 : 0;
   switch (nms) {
     case 1: down_resident_run<DT, LAYOUT, 1, NKB>(p, row_base, e, chunk, s_ar); break;
     case 2: down_resident_run<DT, LAYOUT, 2, NKB>(p, row_base, e, chunk, s_ar); break;
@@ -706,14 +730,26 @@ up_splitk_kernel(const GemmParams p) {
   const int kc = (blockIdx.x / nchunk) % p.S;
   const int cc = blockIdx.x % nchunk;
   const int row_base = mt * kTileRows;
-  if (row_base >= p.offsets[p.E]) return;  // whole workgroup: tile past the padded total
+  // every index the workgroup needs comes in one batch of loads before the
+  // first decision (see tile_gemm_kernel)
+  const int rb = min(mt, p.tiles - 1) * kTileRows;
+  const int total = p.offsets[p.E];
+  const int e = p.tile_expert[rb / kTileRows];
+  int first[kTileMs];
+#pragma unroll
+  for (int ms = 0; ms < kTileMs; ++ms) first[ms] = p.sorted[rb + 16 * ms];
+  const int my_r0 = p.sorted[rb + (threadIdx.x & 15)];  // subtile 0: route of row l % 16
+  asm volatile("" : : "s"(total), "s"(e), "s"(first[0]), "s"(first[1]), "s"(first[2]), "s"(first[3]),
+               "v"(my_r0));
+  if (row_base >= total) return;  // whole workgroup: tile past the padded total
   const int nblk = (p.K + 127) >> 7;
   const int b0 = kc * p.cb;
   const int b1 = min(nblk, b0 + p.cb);
   if (b0 >= b1) return;
   const int kend = min(p.K, 128 * b1);
-  const int nms = active_subtiles(p, row_base);
-  const int e = p.tile_expert[mt];
+  int nms = 0;
+#pragma unroll
+  for (int ms = 0; ms < kTileMs; ++ms) nms += first[ms] >= 0 ? 1 : 0;
   const int stride = p.cb * 128 + 8;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int c = lane & 15, g = lane >> 4, par = c & 1;
@@ -727,16 +763,24 @@ up_splitk_kernel(const GemmParams p) {
     // token of each of the 16 rows (lane l: row l % 16), then every x chunk
     // in flight at once, then the LDS stores
     const int nch = (b1 - b0) * 16;
-    const int my_r = p.sorted[row_base + 16 * rp + c];
-    const int my_tok = my_r >= 0 ? my_r / p.top_k : -1;
+    const int my_r = rp == 0 ? my_r0 : p.sorted[row_base + 16 * rp + c];
+    // the route of each chunk's row, read per chunk (one batch, no lane
+    // exchange chain), then the chunks
+    int rr[kSplitkXLoads];
+#pragma unroll
+    for (int i = 0; i < kSplitkXLoads; ++i) {
+      const int idx = tid + kTileThreads * i;
+      const int row = min(idx / nch, 15);
+      rr[i] = p.sorted[row_base + 16 * rp + row];
+    }
     u32x4 xv[kSplitkXLoads];
 #pragma unroll
     for (int i = 0; i < kSplitkXLoads; ++i) {
       const int idx = tid + kTileThreads * i;
       const int row = idx / nch, ch = idx - row * nch;
-      const int tok = __shfl(my_tok, row & 15);
-      const bool ok = idx < 16 * nch && tok >= 0 && 128 * b0 + 8 * ch < p.K;
-      xv[i] = bload16(xr, 2u * static_cast<uint32_t>((ok ? tok : 0) * p.lda + 128 * b0 + 8 * ch), ok);
+      const bool ok = idx < 16 * nch && rr[i] >= 0 && 128 * b0 + 8 * ch < p.K;
+      xv[i] = bload16(xr, 2u * static_cast<uint32_t>((ok ? rr[i] / p.top_k : 0) * p.lda + 128 * b0 + 8 * ch),
+                      ok);
     }
 #pragma unroll
     for (int i = 0; i < kSplitkXLoads; ++i) {
