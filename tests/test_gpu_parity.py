@@ -231,6 +231,27 @@ def test_ragged_reduction_tails(per_channel, gated, dtype):
         assert_close(out, oracle_out(wl, Wc, tc), f"tails T={T} {force}")
 
 
+@pytest.mark.parametrize("H,I,gated,dtype", [
+    (6144, 192, True, torch.bfloat16), (320, 6144, False, torch.float16),
+    (5760, 320, True, torch.bfloat16)], ids=["up-phases", "down-phases", "up-pair-scales"])
+def test_long_reductions_scale_staging(H, I, gated, dtype):
+    """For tiles of one active subtile the streaming tile kernel stages group
+    scales in LDS: the whole reduction up to 176 groups, else in phases of
+    112 groups when K / 32 is a multiple of 8 (6144: 112 + 80, the up
+    projection prefetching, the down projection loading at the phase
+    boundary), else fetched with the weights (5760: 180 groups), as they are
+    for tiles of more subtiles.  T = 150 gives each expert a full tile and a
+    one-subtile tail, T = 12 one-subtile tiles only, T = 40 two subtiles."""
+    wl = synth.custom("scales", E=4, H=H, I=I, K=2, gated=gated, per_channel=False,
+                      dtype=dtype, seed=11)
+    Wc = synth.make_weights(wl, device="cpu")
+    Wg = Wc.to("cuda")
+    for T in (150, 12, 40):
+        tc = tokens(wl, T)
+        out = forward(wl, Wg, tc.to("cuda"), force_path=1, force_splitk=2)
+        assert_close(out, oracle_out(wl, Wc, tc), f"H={H} I={I} T={T}")
+
+
 # ---------------------------------------------------------------------------
 # determinism, invariances, graph replay
 # ---------------------------------------------------------------------------

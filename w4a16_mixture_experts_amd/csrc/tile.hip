@@ -13,17 +13,21 @@
 // route positions (four 16-row subtiles; empty subtiles are skipped) x 256
 // weight rows (gated: 128 gate + 128 up rows = 128 activation columns;
 // otherwise 256 output columns), over the whole reduction in 128-wide blocks:
-//   - the tile's activation rows for block b+1 are loaded while block b is
-//     computed (16 values per thread) and staged in a double-buffered LDS
-//     tile in A operand order, with each 32-value group's correction sum; UP
-//     mode gathers token rows of x, DOWN mode reads the activation rows of the
-//     tile's positions;
+//   - the tile's activation rows are staged in LDS in A operand order, two
+//     128-blocks per stage and two stages: while blocks 2s and 2s+1 are
+//     computed, blocks 2s+2 and 2s+3 (loaded one step earlier, 16 values
+//     per thread and block) are written to the other stage; UP mode gathers
+//     token rows of x, DOWN mode reads the activation rows of the tile's
+//     positions;
 //   - each wave streams its two 16-row weight subtiles with the lane layout
 //     described in device.h (16 bytes per lane = one quantization group,
-//     a 4x4 dword transpose across lane rows), prefetched one block ahead;
+//     a 4x4 dword transpose across lane rows), prefetched half a step ahead;
+//   - group scales: for a tile of one active subtile, the 256 rows' scales
+//     staged in LDS (the whole reduction, or phases of 112 groups);
+//     otherwise fetched with the weights, 16 bytes per row and block pair;
 //   - MFMA j of a block spans one quantization group: exact dequantization,
 //     the group scale applied to the FP32 result;
-//   - one barrier per block.
+//   - one barrier per two blocks.
 // The activation tile is as large as the weight block it meets, and the
 // workgroups of one tile are launched onto one XCD one after another (the
 // dispatcher deals consecutive workgroups to the 8 XCDs in turn), so the
@@ -41,16 +45,31 @@ constexpr int kTileMs = kTileRows / 16;      // 16-row subtiles
 constexpr int kTileThreads = 64 * kTileWaves;
 constexpr int kAStride = 128 + 8;            // staged row stride (16 B padding)
 constexpr int kXcds = 8;
-constexpr int kWRing = 2;                    // weight blocks in registers (1 in flight)
 constexpr int kNsub = 2;                     // 16-row weight subtiles per wave
 constexpr int kSplitkRing = 4;               // split-K: weight blocks in registers
 constexpr int kSplitkXLoads = 10;            // split-K: staged x chunks per thread (cb <= 19)
 constexpr int kSplitkScLoads = 10;           // split-K: 8-byte scale loads per lane (32 rows x cb <= 640)
-// streaming tile kernel with LDS-staged group scales: 16-byte chunks per
-// thread (256 rows x K/32 scales; K/32 <= 16 * kScLoads) and the LDS it needs
-constexpr int kScLoads = 15;
-constexpr int kScMaxGroups = 16 * kScLoads;
-inline size_t tile_scale_lds_bytes(int K) { return sizeof(uint16_t) * 256 * static_cast<size_t>(K / 32); }
+// Streaming tile kernel LDS: activations in two stages of two 128-blocks,
+// then (group layout) the group scales of the workgroup's 256 weight rows:
+// the whole reduction when it fits beside the stages (K / 32 <=
+// kScWholeGroups), else phases of kScPhaseGroups groups (K / 32 a multiple of
+// 8 then, so that a row's share of a phase is whole 16-byte chunks).
+constexpr int kStageElems = kTileRows * kAStride;  // one staged 128-block
+constexpr int kScWholeGroups = 176;                // 4 blocks + 2 * 256 * 176 B + 16 <= 160 KiB
+constexpr int kScWholeLoads = 256 * kScWholeGroups * 2 / 16 / kTileThreads;  // 16-byte chunks per thread
+constexpr int kScPhaseGroups = 112;                // 28 blocks
+constexpr int kScPhaseLoads = 256 * kScPhaseGroups * 2 / 16 / kTileThreads;
+static_assert(kScWholeLoads * 16 * kTileThreads == 256 * kScWholeGroups * 2, "whole chunks");
+static_assert(kScPhaseLoads * 16 * kTileThreads == 256 * kScPhaseGroups * 2, "phase chunks");
+static_assert(kScPhaseGroups % 8 == 0, "a phase is whole 128-block pairs");
+inline bool tile_scales_in_lds(int layout, int K) {
+  return layout == Q_GROUP_K && (K / 32 <= kScWholeGroups || (K / 32) % 8 == 0);
+}
+inline size_t tile_lds_bytes(bool scl, int K) {
+  size_t b = sizeof(uint16_t) * 4 * kStageElems;
+  if (scl) b += sizeof(uint16_t) * 256 * (K / 32 <= kScWholeGroups ? K / 32 : kScPhaseGroups) + 16;
+  return b;
+}
 
 template <int DT>
 __device__ __forceinline__ float scale_lo(uint32_t pair) { return H16<DT>::to_f32(pair & 0xffffu); }
@@ -378,14 +397,14 @@ __device__ __forceinline__ int active_subtiles(const GemmParams& p, int row_base
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// Streaming tile kernel: the reduction in 128-blocks, activations staged per
-// block into a double-buffered LDS tile.
+// Streaming tile kernel: the reduction in steps of two 128-blocks, the
+// activations of a step staged into one of two LDS stages (one barrier per
+// step).
 // ---------------------------------------------------------------------------
 
 template <int DT, int LAYOUT, int MODE, int NMS, bool SCL>
 __device__ __forceinline__ void tile_run(const GemmParams& p, const int row_base, const int e,
-                                         const int nt, uint16_t (*s_a)[kTileRows][kAStride],
-                                         uint16_t* s_sc, const int st_r) {
+                                         const int nt, uint16_t* s_lds, const int st_r) {
   constexpr bool UP = MODE != MODE_DOWN;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int c = lane & 15, g = lane >> 4, par = c & 1;
@@ -415,9 +434,9 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, const int row_base
     for (int h = 0; h < kChunks; ++h)
       v[h] = bload16(ra, st_off + 2u * (k0 + kVals * st_c + 8 * h), ok);
   };
-  // staged activations in A operand order
-  auto store_a = [&](int buf, const u32x4 (&v)[kChunks]) {
-    uint16_t* dst = &s_a[buf][st_row][kVals * st_c];
+  // one block's activations, in A operand order, into staged block `blk`
+  auto store_a = [&](uint16_t* blk, const u32x4 (&v)[kChunks]) {
+    uint16_t* dst = blk + st_row * kAStride + kVals * st_c;
 #pragma unroll
     for (int h = 0; h < kChunks; ++h)
       *reinterpret_cast<u32x4*>(dst + 8 * h) = UP ? permute_a(v[h]) : v[h];
@@ -429,105 +448,163 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, const int row_base
 #pragma unroll
     for (int s = 0; s < kNsub; ++s) acc[ms][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Pipeline.  Weights: a ring of kWRing register sets, block b + kWRing - 1
-  // is requested while block b is computed.  Activations: block b + 1 is
-  // staged into LDS at the end of step b from registers loaded two steps
-  // earlier.  The loop runs in whole rounds of the ring (register sets need
-  // compile-time indices); steps past the last block only issue masked loads.
-  WBlk<LAYOUT> wr[kWRing][kNsub];
-  u32x4 ar[2][kChunks];
-  const int nblk = (p.K + 127) >> 7;
-  if constexpr (SCL) {
-    // Group scales of the workgroup's 256 weight rows for the whole
-    // reduction, staged once: every row's scales are contiguous, and so are
-    // the rows of a range (gated: the 128 gate rows, then the 128 up rows),
-    // so the copy is linear and every load instruction covers whole cache
-    // lines.  Fetched per block from HBM, each scale load touched 16 lines
-    // for 128 useful bytes, and that cost a fifth of the kernel.
-    const int gpr = p.K >> 5;                        // groups (scales) per row
-    const uint32_t rbytes = 2u * gpr;                // bytes per row
+  // Group scales in LDS.  A row's scales are contiguous and so are the rows
+  // of a range (gated: the 128 gate rows, then the 128 up rows): the whole
+  // reduction's scales are one linear copy per range, every load covering
+  // whole cache lines (fetched per block from HBM, each scale load touched 16
+  // lines for 128 useful bytes).  A phase copies each row's share of the
+  // phase, whole 16-byte chunks.
+  const int gpr = p.K >> 5;  // groups (scales) per row
+  const uint32_t rbytes = 2u * gpr;
+  const bool whole = gpr <= kScWholeGroups;
+  const int pg = whole ? gpr : kScPhaseGroups;  // LDS scale row stride (groups)
+  uint16_t* const s_sc = s_lds + 4 * kStageElems;
+  // scale row (within the expert) of the workgroup's weight row r
+  auto sc_row = [&](int r) {
+    return MODE == MODE_UP_GATED ? (r < 128 ? 0 : p.up_rows - 128) + nt * kTileColsGated + r
+                                 : nt * kTileColsPlain + r;
+  };
+  auto load_whole = [&](u32x4 (&v)[kScWholeLoads]) {
     const int nranges = MODE == MODE_UP_GATED ? 2 : 1;
-    const int rrows = MODE == MODE_UP_GATED ? 128 : 256;     // rows per range
+    const int rrows = MODE == MODE_UP_GATED ? 128 : 256;                   // rows per range
     const uint32_t rchunks = static_cast<uint32_t>(rrows) * rbytes / 16;  // 16-byte chunks per range
-    u32x4 sv[kScLoads];
 #pragma unroll
-    for (int i = 0; i < kScLoads; ++i) {
+    for (int i = 0; i < kScWholeLoads; ++i) {
       const uint32_t ch = static_cast<uint32_t>(tid + kTileThreads * i);
       const int rg = ch < rchunks ? 0 : 1;
       const uint32_t lc = ch - rg * rchunks;
-      const int row0 = MODE == MODE_UP_GATED ? (rg ? p.up_rows : 0) + nt * kTileColsGated
-                                             : nt * kTileColsPlain;
-      sv[i] = bload16(wx.rs, static_cast<uint32_t>(row0) * rbytes + 16u * lc,
-                      rg < nranges && lc < rchunks);
+      v[i] = bload16(wx.rs, static_cast<uint32_t>(sc_row(rrows * rg)) * rbytes + 16u * lc,
+                     rg < nranges && lc < rchunks);
     }
-    load_a(0, ar[0]);
-    load_a(128, ar[1]);
-    load_wblk<LAYOUT, kNsub, SC_NONE>(wx, ws, 0, p.K, g, wr[0]);
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto store_whole = [&](const u32x4 (&v)[kScWholeLoads]) {
+    const uint32_t nchunks = 256u * rbytes / 16;
 #pragma unroll
-    for (int i = 0; i < kScLoads; ++i) {
+    for (int i = 0; i < kScWholeLoads; ++i) {
       const uint32_t ch = static_cast<uint32_t>(tid + kTileThreads * i);
-      if (ch < static_cast<uint32_t>(nranges) * rchunks)
-        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(s_sc) + 16u * ch) = sv[i];
+      if (ch < nchunks) *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(s_sc) + 16u * ch) = v[i];
     }
-    store_a(0, ar[0]);
-    load_a(256, ar[0]);
-    __syncthreads();
+  };
+  // phase ph: groups [kScPhaseGroups * ph, +kScPhaseGroups) of every row
+  auto load_phase = [&](int ph, u32x4 (&v)[kScPhaseLoads]) {
+    const int g0 = kScPhaseGroups * ph;
+    const int cpr = min(gpr - g0, kScPhaseGroups) >> 3;  // 16-byte chunks per row
+#pragma unroll
+    for (int i = 0; i < kScPhaseLoads; ++i) {
+      const int ch = tid + kTileThreads * i;
+      const int r = ch / cpr, part = ch - r * cpr;
+      v[i] = bload16(wx.rs, static_cast<uint32_t>(sc_row(r)) * rbytes + 2u * g0 + 16u * part,
+                     r < 256);
+    }
+  };
+  auto store_phase = [&](int ph, const u32x4 (&v)[kScPhaseLoads]) {
+    const int cpr = min(gpr - kScPhaseGroups * ph, kScPhaseGroups) >> 3;
+#pragma unroll
+    for (int i = 0; i < kScPhaseLoads; ++i) {
+      const int ch = tid + kTileThreads * i;
+      const int r = ch / cpr, part = ch - r * cpr;
+      if (r < 256)
+        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(s_sc) + 2 * kScPhaseGroups * r +
+                                  16 * part) = v[i];
+    }
+  };
+  // LDS rows of this lane's two weight rows; scales of block bp of the phase
+  int lrow[kNsub];
+#pragma unroll
+  for (int s2 = 0; s2 < kNsub; ++s2)
+    lrow[s2] = MODE == MODE_UP_GATED ? 128 * s2 + 16 * w + c : 32 * w + 16 * s2 + c;
+  auto set_scales = [&](int bp, WBlk<LAYOUT> (&b)[kNsub]) {
+#pragma unroll
+    for (int s2 = 0; s2 < kNsub; ++s2) {
+      const uint32_t* sp = reinterpret_cast<const uint32_t*>(s_sc + lrow[s2] * pg + 4 * bp);
+      b[s2].s0 = sp[0];
+      b[s2].s1 = sp[1];
+    }
+  };
 
-    // LDS rows of this lane's two weight rows
-    int lrow[kNsub];
-#pragma unroll
-    for (int s2 = 0; s2 < kNsub; ++s2)
-      lrow[s2] = MODE == MODE_UP_GATED ? 128 * s2 + 16 * w + c : 32 * w + 16 * s2 + c;
-    auto set_scales = [&](int blk, WBlk<LAYOUT> (&b)[kNsub]) {
-#pragma unroll
-      for (int s2 = 0; s2 < kNsub; ++s2) {
-        const uint32_t* sp =
-            reinterpret_cast<const uint32_t*>(s_sc + lrow[s2] * gpr + 4 * blk);
-        b[s2].s0 = sp[0];
-        b[s2].s1 = sp[1];
-      }
-    };
-    for (int blk0 = 0; blk0 < nblk; blk0 += 2) {
-      load_wblk<LAYOUT, kNsub, SC_NONE>(wx, ws, 128 * (blk0 + 1), p.K, g, wr[1]);
-      set_scales(blk0, wr[0]);
-      mma_block<DT, LAYOUT, NMS>(&s_a[0][0][0], kAStride, wr[0], acc, c, g, par);
-      store_a(1, ar[1]);
-      load_a(128 * (blk0 + 3), ar[1]);
-      __syncthreads();
-      load_wblk<LAYOUT, kNsub, SC_NONE>(wx, ws, 128 * (blk0 + 2), p.K, g, wr[0]);
-      if (blk0 + 1 < nblk) {
-        set_scales(blk0 + 1, wr[1]);
-        mma_block<DT, LAYOUT, NMS>(&s_a[1][0][0], kAStride, wr[1], acc, c, g, par);
-      }
-      store_a(0, ar[0]);
-      load_a(128 * (blk0 + 4), ar[0]);
-      __syncthreads();
+  // Pipeline.  Step s computes blocks 2s and 2s + 1 from stage s & 1 while
+  // the other stage receives blocks 2s + 2 and 2s + 3 (loaded one step
+  // earlier) and blocks 2s + 4 and 2s + 5 are requested.  Weights: a ring
+  // of two register sets, a block requested half a step before it is used
+  // (without LDS scales the pair's first block fetches both blocks' scales).
+  // Steps past the last block only issue masked loads.
+  constexpr int SC_FIRST = SCL ? SC_NONE : SC_PAIR_FIRST;
+  constexpr int SC_SECOND = SCL ? SC_NONE : SC_PAIR_SECOND;
+  WBlk<LAYOUT> wr[2][kNsub];
+  u32x4 an[2][kChunks];
+  const int nblk = (p.K + 127) >> 7;
+  const int nsteps = (nblk + 1) >> 1;
+  auto step = [&](int s, int pb0) {  // pb0: first block of the scale phase
+    const int b = 2 * s;
+    const uint16_t* sx = s_lds + 2 * kStageElems * (s & 1);
+    uint16_t* sy = s_lds + 2 * kStageElems * ((s & 1) ^ 1);
+    load_wblk<LAYOUT, kNsub, SC_SECOND>(wx, ws, 128 * (b + 1), p.K, g, wr[1]);
+    if constexpr (SCL) set_scales(b - pb0, wr[0]);
+    mma_block<DT, LAYOUT, NMS>(sx, kAStride, wr[0], acc, c, g, par);
+    if constexpr (!SCL) pass_scales<LAYOUT, kNsub>(wr[0], wr[1]);
+    store_a(sy, an[0]);
+    store_a(sy + kStageElems, an[1]);
+    load_a(128 * (b + 4), an[0]);
+    load_a(128 * (b + 5), an[1]);
+    load_wblk<LAYOUT, kNsub, SC_FIRST>(wx, ws, 128 * (b + 2), p.K, g, wr[0]);
+    if (b + 1 < nblk) {
+      if constexpr (SCL) set_scales(b + 1 - pb0, wr[1]);
+      mma_block<DT, LAYOUT, NMS>(sx + kStageElems, kAStride, wr[1], acc, c, g, par);
     }
-  } else {
-  load_a(0, ar[0]);
-  load_a(128, ar[1]);
-  static_assert(kWRing == 2, "blocks pair up with the ring (scales per block pair)");
-  load_wblk<LAYOUT, kNsub, SC_PAIR_FIRST>(wx, ws, 0, p.K, g, wr[0]);
-  store_a(0, ar[0]);
-  load_a(256, ar[0]);
+    __syncthreads();
+  };
+
+  // prologue: blocks 0 and 1 into stage 0 (with the first scales), blocks 2
+  // and 3 requested
+  load_a(0, an[0]);
+  load_a(128, an[1]);
+  load_wblk<LAYOUT, kNsub, SC_FIRST>(wx, ws, 0, p.K, g, wr[0]);
+  if constexpr (SCL) {
+    // the fences keep the compiler from pairing each load with its store
+    if (whole) {
+      u32x4 v[kScWholeLoads];
+      load_whole(v);
+      __builtin_amdgcn_sched_barrier(0);
+      store_whole(v);
+    } else {
+      u32x4 v[kScPhaseLoads];
+      load_phase(0, v);
+      __builtin_amdgcn_sched_barrier(0);
+      store_phase(0, v);
+    }
+  }
+  store_a(s_lds, an[0]);
+  store_a(s_lds + kStageElems, an[1]);
+  load_a(256, an[0]);
+  load_a(384, an[1]);
   __syncthreads();
 
-  for (int blk0 = 0; blk0 < nblk; blk0 += 2) {
-    // even block blk0 (first of its pair) in wr[0], odd block in wr[1]
-    load_wblk<LAYOUT, kNsub, SC_PAIR_SECOND>(wx, ws, 128 * (blk0 + 1), p.K, g, wr[1]);
-    mma_block<DT, LAYOUT, NMS>(&s_a[0][0][0], kAStride, wr[0], acc, c, g, par);
-    pass_scales<LAYOUT, kNsub>(wr[0], wr[1]);
-    store_a(1, ar[1]);
-    load_a(128 * (blk0 + 3), ar[1]);
-    __syncthreads();
-    load_wblk<LAYOUT, kNsub, SC_PAIR_FIRST>(wx, ws, 128 * (blk0 + 2), p.K, g, wr[0]);
-    if (blk0 + 1 < nblk)
-      mma_block<DT, LAYOUT, NMS>(&s_a[1][0][0], kAStride, wr[1], acc, c, g, par);
-    store_a(0, ar[0]);
-    load_a(128 * (blk0 + 4), ar[0]);
-    __syncthreads();
-  }
+  const int psteps = SCL && !whole ? kScPhaseGroups / 8 : nsteps;  // steps per scale phase
+  for (int s0 = 0; s0 < nsteps; s0 += psteps) {
+    const int s1 = min(nsteps, s0 + psteps);
+    // the next phase's scales are stored after the closing barrier of the
+    // phase's last step (no wave reads the old ones any more); the up
+    // projections request them before that step, the down projection (whose
+    // step holds more registers) after it
+    const bool next = SCL && s1 < nsteps;
+    for (int s = s0; s < (next ? s1 - 1 : s1); ++s) step(s, 2 * s0);
+    if constexpr (SCL) {
+      if (next) {
+        const int ph = s1 / psteps;
+        u32x4 v[kScPhaseLoads];
+        if constexpr (UP) {
+          load_phase(ph, v);
+          __builtin_amdgcn_sched_barrier(0);
+          step(s1 - 1, 2 * s0);
+        } else {
+          step(s1 - 1, 2 * s0);
+          load_phase(ph, v);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        store_phase(ph, v);
+        __syncthreads();
+      }
+    }
   }
   store_outputs<DT, MODE, NMS>(p, row_base, acc, col, on, g, valid_rows<NMS>(p, row_base, g));
 }
@@ -535,9 +612,9 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, const int row_base
 template <int DT, int LAYOUT, int MODE, bool SCL>
 __global__ void __launch_bounds__(kTileThreads)
 tile_gemm_kernel(const GemmParams p) {
-  __shared__ uint16_t s_a[2][kTileRows][kAStride];
-  extern __shared__ uint16_t s_dyn[];  // SCL: [256 rows][K / 32] group scales
-  uint16_t* s_sc = SCL ? s_dyn : nullptr;
+  // [2 stages][2 blocks][kTileRows][kAStride] activations, then (SCL) the
+  // group scales: [256 rows][K / 32] or [256 rows][kScPhaseGroups]
+  extern __shared__ __align__(16) uint16_t s_lds[];
 
   // workgroup L runs on XCD L % 8; XCD x takes tiles x, x + 8, ... and walks
   // the column tiles of each tile back to back
@@ -564,11 +641,15 @@ tile_gemm_kernel(const GemmParams p) {
   int nms = 0;
 #pragma unroll
   for (int ms = 0; ms < kTileMs; ++ms) nms += first[ms] >= 0 ? 1 : 0;
+  // LDS scales serve tiles of one active subtile, which stream weights at
+  // the memory's pace; with more subtiles the tile is bound by its MFMA and
+  // VALU issue, and scales fetched with the weights (per block pair) keep
+  // the register count lower and measured faster
   switch (nms) {
-    case 1: tile_run<DT, LAYOUT, MODE, 1, SCL>(p, row_base, e, nt, s_a, s_sc, st_r); break;
-    case 2: tile_run<DT, LAYOUT, MODE, 2, SCL>(p, row_base, e, nt, s_a, s_sc, st_r); break;
-    case 3: tile_run<DT, LAYOUT, MODE, 3, SCL>(p, row_base, e, nt, s_a, s_sc, st_r); break;
-    default: tile_run<DT, LAYOUT, MODE, 4, SCL>(p, row_base, e, nt, s_a, s_sc, st_r); break;
+    case 1: tile_run<DT, LAYOUT, MODE, 1, SCL>(p, row_base, e, nt, s_lds, st_r); break;
+    case 2: tile_run<DT, LAYOUT, MODE, 2, false>(p, row_base, e, nt, s_lds, st_r); break;
+    case 3: tile_run<DT, LAYOUT, MODE, 3, false>(p, row_base, e, nt, s_lds, st_r); break;
+    default: tile_run<DT, LAYOUT, MODE, 4, false>(p, row_base, e, nt, s_lds, st_r); break;
   }
 }
 
@@ -992,19 +1073,23 @@ hipError_t launch_splitk_act(const GemmParams& p, int dtype, bool gated, hipStre
 
 template <int DT, int LAYOUT, int MODE>
 static hipError_t launch_tile_k(const GemmParams& p, dim3 grid, hipStream_t st) {
-  // group scales staged in LDS when they fit (every group layout up to
-  // K = 32 * kScMaxGroups); otherwise fetched per block pair
-  if (LAYOUT == Q_GROUP_K && p.K / 32 <= kScMaxGroups) {
-    const size_t lds = tile_scale_lds_bytes(p.K);
-    const hipError_t err = allow_lds_tile(tile_gemm_kernel<DT, LAYOUT, MODE, true>, lds,
-                                          sizeof(uint16_t) * 2 * kTileRows * kAStride);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((tile_gemm_kernel<DT, LAYOUT, MODE, true>), grid, dim3(kTileThreads), lds, st,
-                       p);
-  } else {
-    hipLaunchKernelGGL((tile_gemm_kernel<DT, LAYOUT, MODE, false>), grid, dim3(kTileThreads), 0,
-                       st, p);
+  if constexpr (LAYOUT == Q_GROUP_K) {
+    if (tile_scales_in_lds(LAYOUT, p.K)) {
+      const size_t lds = tile_lds_bytes(true, p.K);
+      const hipError_t err = allow_lds_tile(tile_gemm_kernel<DT, LAYOUT, MODE, true>, lds);
+      if (err != hipSuccess) return err;
+      hipLaunchKernelGGL((tile_gemm_kernel<DT, LAYOUT, MODE, true>), grid, dim3(kTileThreads), lds,
+                         st, p);
+      return hipGetLastError();
+    }
   }
+  // per-channel scales, or group scales that neither fit whole nor split
+  // into phases: fetched with the weights, per block pair
+  const size_t lds = tile_lds_bytes(false, p.K);
+  const hipError_t err = allow_lds_tile(tile_gemm_kernel<DT, LAYOUT, MODE, false>, lds);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((tile_gemm_kernel<DT, LAYOUT, MODE, false>), grid, dim3(kTileThreads), lds, st,
+                     p);
   return hipGetLastError();
 }
 
