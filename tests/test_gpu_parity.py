@@ -34,7 +34,7 @@ ROUTE_CASES = [
     # T, K, E, E_global, offset, block_m
     (1, 8, 384, 384, 0, 16), (8, 8, 384, 384, 0, 16), (16, 2, 8, 8, 0, 16),
     (2048, 8, 384, 384, 0, 64), (4096, 6, 128, 128, 0, 64), (2048, 8, 32, 256, 0, 64),
-    (8192, 8, 384, 384, 0, 64),
+    (8192, 8, 384, 384, 0, 64), (300, 8, 384, 384, 0, 64), (129, 8, 60, 60, 0, 32),
     (7, 3, 5, 9, 2, 4), (33, 4, 60, 60, 0, 32), (100, 8, 1024, 1024, 0, 1),
     (5, 2, 8, 8, 0, 256), (0, 4, 8, 8, 0, 16),
 ]

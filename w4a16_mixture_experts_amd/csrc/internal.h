@@ -129,8 +129,9 @@ struct CombineParams {
   uint16_t* out;              // [T][H]
 };
 
-// Route preparation (three launches).  chunk_hist: kRouteChunksMax * E ints of
-// scratch, or null for a single-chunk (slower for many routes) preparation.
+// Route preparation (one launch up to 1024 routes, else two).  chunk_hist:
+// kRouteChunksMax * E ints of scratch, or null for a single-chunk (slower for
+// many routes) preparation.
 constexpr int kRouteChunksMax = 32;
 int route_prep_chunk(int R);
 hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, int32_t* counts,

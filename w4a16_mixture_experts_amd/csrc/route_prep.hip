@@ -15,8 +15,9 @@
 //   tile_expert[i]  expert of tile i (positions [i*block_m, (i+1)*block_m));
 //                   skipped when the pointer is null
 //
-// A stable counting sort without atomics.  Up to 1024 routes: one workgroup
-// (rp_fused_kernel).  Otherwise two launches:
+// A stable counting sort without atomics.  Up to kRpOneRoutes routes: one
+// workgroup (rp_one_kernel; beyond that, the scattered stores of `sorted`
+// are too many for one compute unit).  Otherwise two launches:
 //   1. rp_rank_kernel: workgroup c takes the contiguous chunk c of routes;
 //      each of its waves walks a slab of the chunk 64 routes at a time.
 //      Lanes holding the same expert are found with one ballot per expert-id
@@ -25,9 +26,10 @@
 //      waves gives each route's rank within the chunk (written to slot[r])
 //      and the chunk's per-expert counts (chunk_hist[c][e]).
 //   2. rp_scatter_kernel: each workgroup redoes the per-expert scan (chunk
-//      bases, totals, padded sizes, offsets) and scatters its chunk,
-//      p = offsets[e] + base[c][e] + rank; workgroup 0 writes counts,
-//      offsets, the padding and the tile -> expert map.
+//      bases, totals, padded sizes, offsets), scatters its chunk,
+//      p = offsets[e] + base[c][e] + rank, and writes the padding and the
+//      tile -> expert map of its share of the experts; workgroup 0 writes
+//      counts and offsets.
 // Ascending order within an expert follows from chunks, slabs, 64-route
 // pieces and lanes all being in route order.
 #include <algorithm>
@@ -49,54 +51,98 @@ __device__ __forceinline__ int local_expert(int32_t g, int E, int off) {
   return (e >= 0 && e < E) ? static_cast<int>(e) : -1;
 }
 
-// Padding positions (-1) and the tile -> expert map, one wave per expert at a
-// time so that each store instruction writes consecutive positions (a thread
-// per expert would scatter every store over 64 experts' ranges).
-__device__ __forceinline__ void fill_padding_and_tiles(int E, int bm, const int32_t* s_off,
-                                                       const int32_t* s_cnt, int32_t* sorted,
-                                                       int32_t* tile_expert, int waves) {
+// Padding positions (-1) and the tile -> expert map of experts [eb, ee).
+// Wave w takes experts eb + [w * per, (w + 1) * per) (per <= 64: E <= 64 *
+// waves); lane j reads the
+// bounds of the wave's j-th expert, then the wave walks its experts with
+// those values broadcast from lane j, each store instruction writing
+// consecutive positions of one expert (a thread per expert would scatter
+// every store over 64 experts' ranges).
+__device__ __forceinline__ void fill_padding_and_tiles(int eb, int ee, int bm,
+                                                       const int32_t* s_off, const int32_t* s_cnt,
+                                                       int32_t* sorted, int32_t* tile_expert,
+                                                       int waves) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int e = w; e < E; e += waves) {
-    const int beg = s_off[e], end = s_off[e + 1];
-    for (int p = beg + s_cnt[e] + lane; p < end; p += 64) sorted[p] = -1;
-    if (tile_expert != nullptr)
-      for (int i = beg / bm + lane; i < end / bm; i += 64) tile_expert[i] = e;
+  const int per = (ee - eb + waves - 1) / waves;
+  const int e0 = eb + w * per;
+  const int me = e0 + lane;
+  int pad_v = 0, end_v = 0, t0_v = 0, t1_v = 0;
+  if (lane < per && me < ee) {
+    const int beg = s_off[me];
+    end_v = s_off[me + 1];
+    pad_v = beg + s_cnt[me];
+    t0_v = beg / bm;
+    t1_v = end_v / bm;
+  }
+  const int n = min(per, ee - e0);
+  for (int j = 0; j < n; ++j) {
+    const int pad = __builtin_amdgcn_readlane(pad_v, j), end = __builtin_amdgcn_readlane(end_v, j);
+    for (int p = pad + lane; p < end; p += 64) sorted[p] = -1;
+    if (tile_expert != nullptr) {
+      const int t1 = __builtin_amdgcn_readlane(t1_v, j);
+      for (int i = __builtin_amdgcn_readlane(t0_v, j) + lane; i < t1; i += 64) tile_expert[i] = e0 + j;
+    }
   }
 }
 
 }  // namespace
 
-// Up to kRpFusedRoutes routes: the whole preparation in one workgroup (16
-// waves, one 64-route piece each).
-constexpr int kRpFusedRoutes = 1024;
+// Up to kRpOneRoutes routes: the whole preparation in one workgroup.  Wave w
+// takes the contiguous slab of np 64-route pieces starting at piece w * np
+// (NP >= np, a compile-time bound) and ranks its pieces in order, its LDS
+// histogram carrying the counts of its earlier pieces; the scan over the
+// waves' histograms gives each wave's base within an expert.
+// (Measured on the 384-expert workload: beyond 1024 routes, two launches
+// over 256-route chunks are faster.)
+constexpr int kRpOneMaxPieces = 1;
+constexpr int kRpOneRoutes = kRpOneMaxPieces * kRpScanThreads;
 
+template <int NP>
 __global__ void __launch_bounds__(kRpScanThreads)
-rp_fused_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm,
-                int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                int32_t* __restrict__ sorted, int32_t* __restrict__ slot,
-                int32_t* __restrict__ tile_expert) {
+rp_one_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm,
+              int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+              int32_t* __restrict__ sorted, int32_t* __restrict__ slot,
+              int32_t* __restrict__ tile_expert) {
   constexpr int kW = kRpScanThreads / 64;
   __shared__ int32_t hist[kW][kRpMaxExperts];
   __shared__ int32_t wave_tot[kW];
   __shared__ int32_t s_off[kRpMaxExperts + 1];
   __shared__ int32_t s_cnt[kRpMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int r = tid;  // route r = 64 w + lane: wave w holds the w-th piece
-  const int e = r < R ? local_expert(ids[r], E, off) : -1;
-  for (int x = lane; x < E; x += 64) hist[w][x] = 0;
-  // rank within the wave's piece (one ballot per expert-id bit)
+  const int np = ((R + 63) / 64 + kW - 1) / kW;  // pieces per wave
+  const int r0 = 64 * np * w + lane;              // route of piece 0 of this lane
+  int ev[NP];
+#pragma unroll
+  for (int q = 0; q < NP; ++q) {
+    const int r = r0 + 64 * q;
+    ev[q] = (q < np && r < R) ? local_expert(ids[r], E, off) : -1;
+  }
+  for (int x = lane; x < E; x += 64) hist[w][x] = 0;  // read back by this wave only
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
-  uint64_t match = __ballot(e >= 0);
-  for (int b = 0; b < nbits; ++b) {
-    const bool bit = (e >> b) & 1;
-    const uint64_t m = __ballot(bit);
-    match &= bit ? m : ~m;
-  }
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int rank = __popcll(match & below);
-  __syncthreads();
-  if (e >= 0 && rank == 0) hist[w][e] = __popcll(match);
+  // rank within the wave's slab: lanes of a piece holding the same expert are
+  // found with one ballot per expert-id bit
+  int rk[NP];
+#pragma unroll
+  for (int q = 0; q < NP; ++q) {
+    rk[q] = 0;
+    if (q < np) {
+      const int e = ev[q];
+      uint64_t match = __ballot(e >= 0);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        match &= bit ? m : ~m;
+      }
+      if (e >= 0) {
+        const int rank = __popcll(match & below);
+        const int before = hist[w][e];
+        if (rank == 0) hist[w][e] = before + __popcll(match);
+        rk[q] = before + rank;
+      }
+    }
+  }
   __syncthreads();
   // per expert: wave bases (in place), totals, padded sizes
   int padded = 0, total = 0;
@@ -137,16 +183,21 @@ rp_fused_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm,
     s_off[E] = wave_tot[kW - 1];
   }
   __syncthreads();
-  if (r < R) {
-    if (e >= 0) {
-      const int pos = s_off[e] + hist[w][e] + rank;
-      sorted[pos] = r;
-      slot[r] = pos;
-    } else {
-      slot[r] = -1;
+#pragma unroll
+  for (int q = 0; q < NP; ++q) {
+    const int r = r0 + 64 * q;
+    if (q < np && r < R) {
+      const int e = ev[q];
+      if (e >= 0) {
+        const int pos = s_off[e] + hist[w][e] + rk[q];
+        sorted[pos] = r;
+        slot[r] = pos;
+      } else {
+        slot[r] = -1;
+      }
     }
   }
-  fill_padding_and_tiles(E, bm, s_off, s_cnt, sorted, tile_expert, kW);
+  fill_padding_and_tiles(0, E, bm, s_off, s_cnt, sorted, tile_expert, kW);
 }
 
 __global__ void __launch_bounds__(kRpThreads)
@@ -155,8 +206,7 @@ rp_rank_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int chunk
   __shared__ int32_t hist[kRpWaves][kRpMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = blockIdx.x;
-  for (int e = lane; e < E; e += 64) hist[w][e] = 0;
-  __syncthreads();
+  for (int e = lane; e < E; e += 64) hist[w][e] = 0;  // read back by this wave only
 
   const int c_beg = c * chunk;
   const int c_end = min(R, c_beg + chunk);
@@ -167,8 +217,14 @@ rp_rank_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int chunk
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
 
-  // rank of each route within this wave's slab (ids of 4 pieces in flight)
+  // rank of each route within this wave's slab (ids of kRound pieces in
+  // flight).  A slab of one round keeps ids and ranks in registers for the
+  // pass after the scan; a longer one parks the ranks in slot[].
   constexpr int kRound = 4;
+  const bool one_round = slab <= 64 * kRound;
+  int ek[kRound], rk[kRound];
+#pragma unroll
+  for (int q = 0; q < kRound; ++q) ek[q] = -1, rk[q] = 0;
   for (int rb = r_beg; rb < r_end; rb += 64 * kRound) {
     int ev[kRound];
 #pragma unroll
@@ -178,7 +234,9 @@ rp_rank_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int chunk
     }
 #pragma unroll
     for (int q = 0; q < kRound; ++q) {
-      if (rb + 64 * q >= r_end) break;
+      ek[q] = ev[q];
+      rk[q] = 0;
+      if (rb + 64 * q >= r_end) continue;
       const int r = rb + 64 * q + lane;
       const int e = ev[q];
       uint64_t match = __ballot(e >= 0);
@@ -191,8 +249,9 @@ rp_rank_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int chunk
         const int rank = __popcll(match & below);
         const int before = hist[w][e];
         if (rank == 0) hist[w][e] = before + __popcll(match);
-        slot[r] = before + rank;  // temporary: rank within the wave's slab
-      } else if (r < r_end) {
+        rk[q] = before + rank;
+        if (!one_round) slot[r] = before + rank;  // rank within the wave's slab
+      } else if (!one_round && r < r_end) {
         slot[r] = -1;
       }
     }
@@ -211,11 +270,19 @@ rp_rank_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int chunk
   }
   __syncthreads();
   // rank within the chunk
-  for (int rb = r_beg; rb < r_end; rb += 64) {
-    const int r = rb + lane;
-    if (r < r_end) {
-      const int e = local_expert(ids[r], E, off);
-      if (e >= 0) slot[r] += hist[w][e];
+  if (one_round) {
+#pragma unroll
+    for (int q = 0; q < kRound; ++q) {
+      const int r = r_beg + 64 * q + lane;
+      if (r < r_end) slot[r] = ek[q] >= 0 ? rk[q] + hist[w][ek[q]] : -1;
+    }
+  } else {
+    for (int rb = r_beg; rb < r_end; rb += 64) {
+      const int r = rb + lane;
+      if (r < r_end) {
+        const int e = local_expert(ids[r], E, off);
+        if (e >= 0) slot[r] += hist[w][e];
+      }
     }
   }
 }
@@ -223,9 +290,10 @@ rp_rank_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int chunk
 // Every workgroup redoes the (small) per-expert scan, so that no separate
 // launch is needed: chunk counts of each expert (all loads in flight), the
 // totals, their padded sizes, the scan over experts; then workgroup c
-// scatters chunk c, and workgroup 0 also writes counts, offsets, padding and
-// the tile -> expert map.  chunk_hist may alias counts (one chunk: the only
-// workgroup reads a count before writing it, in the same thread).
+// scatters chunk c and writes the padding and tile map of its share of the
+// experts, and workgroup 0 writes counts and offsets.  chunk_hist may alias
+// counts (one chunk: the only workgroup reads a count before writing it, in
+// the same thread).
 __global__ void __launch_bounds__(kRpScanThreads)
 rp_scatter_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm, int chunk,
                   int n_chunks, const int32_t* chunk_hist, int32_t* counts,
@@ -238,6 +306,16 @@ rp_scatter_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm
   __shared__ int32_t s_base[kRpMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = blockIdx.x;
+  const int c_end = min(R, (c + 1) * chunk);
+  // a chunk of at most one route per thread: the route's expert and rank
+  // are requested with the chunk counts
+  const bool one_pass = chunk <= kRpScanThreads;
+  const int r1 = c * chunk + tid;
+  int e1 = -1, k1 = 0;
+  if (one_pass && r1 < c_end) {
+    e1 = local_expert(ids[r1], E, off);
+    k1 = slot[r1];
+  }
   int padded = 0, total = 0, base = 0;
   if (tid < E) {
     int n[kRouteChunksMax];
@@ -275,13 +353,20 @@ rp_scatter_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm
   }
   if (tid == 0) s_off[E] = wave_tot[kW - 1];
   __syncthreads();
-  const int c_end = min(R, (c + 1) * chunk);
-  for (int r = c * chunk + tid; r < c_end; r += kRpScanThreads) {
-    const int e = local_expert(ids[r], E, off);
-    if (e < 0) continue;  // slot[r] is already -1
-    const int pos = s_off[e] + s_base[e] + slot[r];
-    sorted[pos] = r;
-    slot[r] = pos;
+  if (one_pass) {
+    if (e1 >= 0) {  // slot[r1] is already -1 for an invalid route
+      const int pos = s_off[e1] + s_base[e1] + k1;
+      sorted[pos] = r1;
+      slot[r1] = pos;
+    }
+  } else {
+    for (int r = c * chunk + tid; r < c_end; r += kRpScanThreads) {
+      const int e = local_expert(ids[r], E, off);
+      if (e < 0) continue;
+      const int pos = s_off[e] + s_base[e] + slot[r];
+      sorted[pos] = r;
+      slot[r] = pos;
+    }
   }
   if (c == 0) {
     if (tid < E) {
@@ -289,14 +374,16 @@ rp_scatter_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm
       offsets[tid] = s_off[tid];
     }
     if (tid == 0) offsets[E] = s_off[E];
-    fill_padding_and_tiles(E, bm, s_off, s_cnt, sorted, tile_expert, kW);
   }
+  const int per_wg = (E + n_chunks - 1) / n_chunks;
+  const int eb = min(E, c * per_wg);
+  fill_padding_and_tiles(eb, min(E, eb + per_wg), bm, s_off, s_cnt, sorted, tile_expert, kW);
 }
 
 int route_prep_chunk(int R) {
-  // at most kRouteChunksMax chunks, at least 1024 routes per chunk
+  // at most kRouteChunksMax chunks, at least 256 routes per chunk
   const int per = (R + kRouteChunksMax - 1) / kRouteChunksMax;
-  return std::max(1024, (per + 63) & ~63);
+  return std::max(256, (per + 63) & ~63);
 }
 
 hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, int32_t* counts,
@@ -309,12 +396,12 @@ hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, 
   const int chunk = one ? std::max(R, 1) : route_prep_chunk(R);
   const int n_chunks = R > 0 ? (R + chunk - 1) / chunk : 0;
   int32_t* hist = one ? counts : chunk_hist;
-  if (R <= kRpFusedRoutes) {
-    hipLaunchKernelGGL(rp_fused_kernel, dim3(1), dim3(kRpScanThreads), 0, stream, ids, R, E, off,
-                       bm, counts, offsets, sorted, slot, tile_expert);
+  if (R <= kRpOneRoutes) {
+    hipLaunchKernelGGL(rp_one_kernel<kRpOneMaxPieces>, dim3(1), dim3(kRpScanThreads), 0, stream,
+                       ids, R, E, off, bm, counts, offsets, sorted, slot, tile_expert);
     return hipGetLastError();
   }
-  // R > kRpFusedRoutes here, so there is at least one chunk
+  // R > kRpOneRoutes here, so there is at least one chunk
   hipLaunchKernelGGL(rp_rank_kernel, dim3(n_chunks), dim3(kRpThreads), 0, stream, ids, R, E, off,
                      chunk, slot, hist);
   const hipError_t err = hipGetLastError();
