@@ -133,6 +133,103 @@ def source_hash(path):
     return h.hexdigest()
 
 
+def counter_pass(args, wl, sweep, dev):
+    """Inputs built on the host and copied over, then only library launches
+    (and device-to-device copies), for rocprofv3 counter runs that must not
+    see other device kernels.  The packed weights are random bytes and the
+    scales 1: the memory traffic of the kernels depends on the shapes and the
+    routing, which is the timed run's (same generator, same seeds), not on
+    the weight values.  With --copy-calibration-mib, three plain copies of
+    that size come first (the calibration for the byte counters)."""
+    import numpy as np
+    import torch
+
+    from w4a16_mixture_experts_amd import binding, synth
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32).to(dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[counters] copy calibration: 3 x {args.copy_calibration_mib} MiB copied")
+        del src, dst
+    rng = np.random.default_rng(0)
+    E, H, I, N1 = wl.num_experts, wl.hidden, wl.inter, wl.n1
+    if wl.per_channel:
+        shapes = [(E, N1 // 2, H), (E, N1), (E, H // 2, I), (E, H)]
+    else:
+        shapes = [(E, N1, H // 2), (E, N1, H // 32), (E, H, I // 2), (E, H, I // 32)]
+    ts = []
+    for i, sh in enumerate(shapes):
+        if i % 2 == 0:
+            ts.append(torch.from_numpy(rng.integers(0, 256, size=sh, dtype=np.uint8)).to(dev))
+        else:
+            ts.append(torch.ones(sh, dtype=wl.dtype).to(dev))
+    W = synth.Weights(*ts)
+    for T in sweep:
+        tok = synth.make_tokens(wl, T).to(dev)
+        for _ in range(args.steps):
+            binding.forward_workload(wl, W, tok)
+        torch.cuda.synchronize()
+        log(f"[counters] T={T}: {args.steps} forwards")
+
+
+# kernel whose HBM traffic the counter pass measures: the gate/up tile kernel
+# (group layout, bf16, LDS scales), as the profiler names it and as this
+# script prints it
+COUNTED = ("tile_gemm_kernel<0, 0, 0, true>", "tile_gemm_kernel<0, 0, 0>", "tile.hip")
+
+
+def summarize_counters(args, sweep):
+    """profiles/traffic.json from two --counter-pass runs (FETCH_SIZE, then
+    WRITE_SIZE, KiB per dispatch).  Each counter is scaled by known bytes /
+    counted bytes of the run's plain copies (--copy-calibration-mib each);
+    the counted kernel's launches come in sweep order, --steps per T."""
+    import csv
+
+    known = args.copy_calibration_mib * 1024 * 1024
+    if known <= 0:
+        raise SystemExit("--summarize-counters needs --copy-calibration-mib (the copies' size)")
+    per = {}
+    factors = {}
+    for name, path in zip(("FETCH_SIZE", "WRITE_SIZE"), args.summarize_counters):
+        with open(path) as f:
+            rows = [r for r in csv.DictReader(f) if r["Counter_Name"] == name]
+        # the calibration copies: the largest copy dispatches of the run
+        cb = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        big = max((int(r["Grid_Size"]) for r in cb), default=0)
+        copies = [float(r["Counter_Value"]) * 1024 for r in cb if int(r["Grid_Size"]) == big]
+        if not copies:
+            raise SystemExit(f"{path}: no calibration copies")
+        factors[name] = known / statistics.fmean(copies)
+        ks = [float(r["Counter_Value"]) * 1024 for r in rows if COUNTED[0] in r["Kernel_Name"]]
+        if len(ks) != args.steps * len(sweep):
+            raise SystemExit(f"{path}: {len(ks)} launches of {COUNTED[0]}, expected "
+                             f"{args.steps} x {len(sweep)}")
+        per[name] = {T: statistics.fmean(ks[i * args.steps:(i + 1) * args.steps]) * factors[name]
+                     for i, T in enumerate(sweep)}
+    by_t = {T: per["FETCH_SIZE"][T] + per["WRITE_SIZE"][T] for T in sweep}
+    src = os.path.join(ROOT, "w4a16_mixture_experts_amd", "csrc", COUNTED[2])
+    rec = {"kernels": {COUNTED[1]: {
+        "tokens": sweep,
+        "source": COUNTED[2],
+        "source_sha256": source_hash(src),
+        "hbm_bytes_per_launch": int(statistics.fmean(by_t.values())),
+        "hbm_bytes_by_tokens": {str(T): int(v) for T, v in by_t.items()},
+        "fetch_bytes_by_tokens": {str(T): int(v) for T, v in per["FETCH_SIZE"].items()},
+        "write_bytes_by_tokens": {str(T): int(v) for T, v in per["WRITE_SIZE"].items()},
+        "calibration": {"copy_bytes": known, "fetch_factor": round(factors["FETCH_SIZE"], 4),
+                        "write_factor": round(factors["WRITE_SIZE"], 4)},
+    }}}
+    out = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
 def cpu_baseline(wl, Wg, budget_s, min_s):
     """The CPU oracle (as it stands) on a bounded sample of the same sweep."""
     import numpy as np
@@ -185,9 +282,14 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="time eager calls instead")
     ap.add_argument("--graph-reps", type=int, default=10,
                     help="forwards per captured graph (G); per-forward time = graph time / G")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from the counter_collection.csv files of "
+                         "a --counter-pass run under rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="host-built inputs and library calls only (for counter runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="first run a plain elementwise copy (negation) of this many MiB "
-                         "three times: the known-size kernel that scales HBM counters")
+                    help="first run three plain copies of this many MiB: the known-size "
+                         "kernel that scales the HBM counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -199,6 +301,11 @@ def main():
 
     from w4a16_mixture_experts_amd import binding, synth
 
+    if args.summarize_counters:
+        sweep = [int(t) for t in args.tokens.split(",")] if args.tokens else \
+            list(synth.WORKLOADS[args.workload].tokens)
+        summarize_counters(args, sweep)
+        return
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
@@ -206,6 +313,10 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     sweep = [int(t) for t in args.tokens.split(",")] if args.tokens else list(wl.tokens)
     dtype_name = "fp16" if wl.dtype == torch.float16 else "bf16"
+
+    if args.counter_pass:
+        counter_pass(args, wl, sweep, dev)
+        return
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * 1024 * 1024 // 4
