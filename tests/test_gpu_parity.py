@@ -183,6 +183,29 @@ def test_single_expert_receives_everything():
     assert_close(out, ref, "one expert small-batch path")
 
 
+def test_activations_beyond_fp16_range():
+    """bf16 activations of magnitude 2^16 and more in tiles of several subtiles
+    (the fp16 route of the tile kernels cannot hold them): those tiles are
+    rerun with per-group scaling, so the affected rows stay exact and the
+    others are untouched.  Without the rerun, 1e6 would be clamped to 65504."""
+    wl = synth.WORKLOADS["tiny"]
+    Wc, Wg = weights("tiny")
+    tc = tokens(wl, 256)          # 512 routes over 8 experts: 64-row tiles of 4 subtiles
+    x = tc.x.clone()
+    big_rows = [3, 100, 200]
+    x[3, 7] = 3.0e5
+    x[100, 0] = -7.0e4
+    x[200, 255] = 1.0e6
+    t2 = synth.Tokens(x, tc.topk_ids, tc.topk_weights)
+    ref = oracle_out(wl, Wc, t2)
+    out = forward(wl, Wg, t2.to("cuda"), force_path=1).cpu()
+    rest = [r for r in range(256) if r not in big_rows]
+    assert_close(out[rest], ref[rest], "tiny T=256, rows without large activations")
+    for r in big_rows:
+        nrmse, _ = errors(out[r], ref[r])
+        assert nrmse <= 5e-3, (r, nrmse)
+
+
 def test_poisoned_workspace_and_output():
     """Workspace and output filled with NaN patterns before the call: nothing
     uninitialised may leak (empty split-K partitions, padding rows)."""

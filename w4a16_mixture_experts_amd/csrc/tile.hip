@@ -732,6 +732,36 @@ __device__ __forceinline__ void down_resident_run(const GemmParams& p, const int
   };
 
   static_assert(NKB == 1 || NKB == 2, "one or two 128-blocks per step");
+  // tiles of one or two subtiles hold few accumulators: their weights stream
+  // through a ring of four blocks, two column steps ahead (the register
+  // count of the kernel is set by the larger tiles)
+  constexpr bool kDeep = NKB == 2 && NMS <= 2;
+  if constexpr (kDeep) {
+    WBlk<LAYOUT> w[4][kNsub];
+    load_blk(step_begin, 0, w[0]);
+    load_blk(step_begin, 1, w[1]);
+    load_blk(step_begin + 1, 0, w[2]);
+    load_blk(step_begin + 1, 1, w[3]);
+    for (int st = step_begin; st < step_end; st += 2) {
+      zero_acc();
+      pass_scales<LAYOUT, kNsub>(w[0], w[1]);
+      mma_block<DT, LAYOUT, NMS, false>(s_ar, S, w[0], acc, c, g, par);
+      mma_block<DT, LAYOUT, NMS, false>(s_ar + 128, S, w[1], acc, c, g, par);
+      store_step(st);
+      load_blk(st + 2, 0, w[0]);
+      load_blk(st + 2, 1, w[1]);
+      if (st + 1 < step_end) {
+        zero_acc();
+        pass_scales<LAYOUT, kNsub>(w[2], w[3]);
+        mma_block<DT, LAYOUT, NMS, false>(s_ar, S, w[2], acc, c, g, par);
+        mma_block<DT, LAYOUT, NMS, false>(s_ar + 128, S, w[3], acc, c, g, par);
+        store_step(st + 1);
+      }
+      load_blk(st + 3, 0, w[2]);
+      load_blk(st + 3, 1, w[3]);
+    }
+    return;
+  }
   WBlk<LAYOUT> w0[kNsub], w1[kNsub];
   load_blk(step_begin, 0, w0);
   if constexpr (NKB == 2) {
@@ -760,8 +790,11 @@ __device__ __forceinline__ void down_resident_run(const GemmParams& p, const int
   }
 }
 
+// Four waves per SIMD (two workgroups per CU): twice the weight requests in
+// flight per CU; measured faster than one workgroup with more registers
+// although the four-subtile path then keeps a few values in scratch.
 template <int DT, int LAYOUT, int NKB>
-__global__ void __launch_bounds__(kTileThreads)
+__global__ void __launch_bounds__(kTileThreads, 4)
 down_resident_kernel(const GemmParams p) {
   __shared__ uint16_t s_ar[kTileRows * (NKB * 128 + 8)];
 
