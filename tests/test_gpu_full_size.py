@@ -12,7 +12,10 @@ from w4a16_mixture_experts_amd import synth
 pytestmark = pytest.mark.gpu
 
 FULL = [("kimi_tp8", 2048), ("kimi_tp8", 256), ("deepseek_local", 2048), ("per_channel", 256),
-        ("relu2_skew", 4096)]
+        ("relu2_skew", 4096),
+        # the interface's largest token count: 524,280 routes, about 8,600
+        # expert tiles, route preparation over its full 32 chunks
+        ("kimi_tp8", 65535)]
 
 
 @pytest.mark.parametrize("name,T", FULL)
