@@ -660,9 +660,16 @@ tile_gemm_kernel(const GemmParams p) {
 // requests the next step's weights while it computes the current one.
 // ---------------------------------------------------------------------------
 
+// Expert outputs of one column step leave through the wave's own LDS region
+// (rows of 32 columns, stride kOutStride): each lane then stores 16 bytes of
+// one row, eight lanes' worth of rows per instruction, instead of a 16-bit
+// value per lane per output.
+constexpr int kOutStride = 40;  // 16-bit elements per staged row (80 B)
+
 template <int DT, int LAYOUT, int NMS, int NKB>
 __device__ __forceinline__ void down_resident_run(const GemmParams& p, const int row_base,
-                                                  const int e, const int chunk, uint16_t* s_ar) {
+                                                  const int e, const int chunk, uint16_t* s_ar,
+                                                  uint16_t* s_out) {
   constexpr int S = NKB * 128 + 8;   // row stride of the resident tile
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int c = lane & 15, g = lane >> 4, par = c & 1;
@@ -724,11 +731,40 @@ __device__ __forceinline__ void down_resident_run(const GemmParams& p, const int
 #pragma unroll
       for (int k = 0; k < kNsub; ++k) acc[ms][k] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
+  // rows of the tile holding a route (bit r: tile row r)
+  const uint64_t rows_valid = __ballot(p.sorted[row_base + lane] >= 0);
+  const bool vec_out = (p.n_cols & 7) == 0;  // a 16-byte chunk is all in or all out
+  const auto ro = make_rsrc(p.out + static_cast<int64_t>(row_base) * p.ldo,
+                            static_cast<uint32_t>(2 * kTileRows * p.ldo));
   auto store_step = [&](int st) {
     int col[kNsub];
     bool on[kNsub];
     step_src(st, col, on);
-    store_outputs<DT, MODE_DOWN, NMS>(p, row_base, acc, col, on, g, vmask);
+    if (!vec_out) {
+      store_outputs<DT, MODE_DOWN, NMS>(p, row_base, acc, col, on, g, vmask);
+      return;
+    }
+    // lane (c, g) holds rows 16 ms + 4 g + i of columns 16 s + c
+#pragma unroll
+    for (int ms = 0; ms < NMS; ++ms)
+#pragma unroll
+      for (int s = 0; s < kNsub; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s_out[(16 * ms + 4 * g + i) * kOutStride + 16 * s + c] =
+              H16<DT>::from_f32(16.0f * acc[ms][s][i]);
+    // lane l: row 16 ms + l / 4, columns 8 (l % 4) .. + 8 of the wave's 32
+    const int n0 = st * kTileColsPlain + w * 32 + 8 * (lane & 3);
+    const bool col_ok = st < step_end && n0 < p.n_cols;
+#pragma unroll
+    for (int ms = 0; ms < NMS; ++ms) {
+      const int r = 16 * ms + (lane >> 2);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(s_out + r * kOutStride + 8 * (lane & 3));
+      const bool ok = col_ok && ((rows_valid >> r) & 1u);
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), ro,
+          ok ? 2u * static_cast<uint32_t>(r * p.ldo + n0) : kOob, 0, 0);
+    }
   };
 
   static_assert(NKB == 1 || NKB == 2, "one or two 128-blocks per step");
@@ -797,6 +833,7 @@ template <int DT, int LAYOUT, int NKB>
 __global__ void __launch_bounds__(kTileThreads, 4)
 down_resident_kernel(const GemmParams p) {
   __shared__ uint16_t s_ar[kTileRows * (NKB * 128 + 8)];
+  __shared__ __align__(16) uint16_t s_out[kTileWaves][kTileRows * kOutStride];
 
   // same XCD-aware order as the streaming kernel (n_tiles = column chunks)
   const int L = blockIdx.x;
@@ -818,10 +855,14 @@ down_resident_kernel(const GemmParams p) {
 #pragma unroll
   for (int ms = 0; ms < kTileMs; ++ms) nms += first[ms] >= 0 ? 1 : 0;
   switch (nms) {
-    case 1: down_resident_run<DT, LAYOUT, 1, NKB>(p, row_base, e, chunk, s_ar); break;
-    case 2: down_resident_run<DT, LAYOUT, 2, NKB>(p, row_base, e, chunk, s_ar); break;
-    case 3: down_resident_run<DT, LAYOUT, 3, NKB>(p, row_base, e, chunk, s_ar); break;
-    default: down_resident_run<DT, LAYOUT, 4, NKB>(p, row_base, e, chunk, s_ar); break;
+    case 1: down_resident_run<DT, LAYOUT, 1, NKB>(p, row_base, e, chunk, s_ar,
+                                                  s_out[threadIdx.x >> 6]); break;
+    case 2: down_resident_run<DT, LAYOUT, 2, NKB>(p, row_base, e, chunk, s_ar,
+                                                  s_out[threadIdx.x >> 6]); break;
+    case 3: down_resident_run<DT, LAYOUT, 3, NKB>(p, row_base, e, chunk, s_ar,
+                                                  s_out[threadIdx.x >> 6]); break;
+    default: down_resident_run<DT, LAYOUT, 4, NKB>(p, row_base, e, chunk, s_ar,
+                                                  s_out[threadIdx.x >> 6]); break;
   }
 }
 
