@@ -287,22 +287,42 @@ template <int DT>
 __global__ void __launch_bounds__(256)
 combine_kernel(const CombineParams p) {
   using T = H16<DT>;
+  constexpr int kBatch = 8;  // routes whose Y loads are in flight together
   const int t = blockIdx.y;
   const int col = (blockIdx.x * 256 + threadIdx.x) * 8;
-  if (col >= p.H) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < p.top_k; ++k) {
-    const int r = t * p.top_k + k;
-    const int pos = p.slot[r];
-    if (pos < 0) continue;
-    const float w = p.wts[r];
-    const u32x4 v = load16(p.y + static_cast<int64_t>(pos) * p.H + col);
+  for (int kb = 0; kb < p.top_k; kb += kBatch) {
+    // the token's slots and weights (wave-uniform), then every Y load of the
+    // batch: one buffer resource per route, empty for an invalid route (its
+    // loads return zeros), and columns past H read out of range as well
+    int pos[kBatch];
+    float wk[kBatch];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += w * T::to_f32(v[i] & 0xffffu);
-      acc[2 * i + 1] += w * T::to_f32(v[i] >> 16);
+    for (int k = 0; k < kBatch; ++k) {
+      const int r = t * p.top_k + kb + k;
+      pos[k] = kb + k < p.top_k ? p.slot[r] : -1;
+      wk[k] = kb + k < p.top_k ? p.wts[r] : 0.0f;
+    }
+    u32x4 v[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const bool ok = pos[k] >= 0;
+      const auto ry = make_rsrc(p.y + static_cast<int64_t>(ok ? pos[k] : 0) * p.H,
+                                ok ? static_cast<uint32_t>(2 * p.H) : 0u);
+      v[k] = bload16(ry, 2u * static_cast<uint32_t>(col), true);
+    }
+    // fixed order: ascending k, invalid routes contribute nothing
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      if (pos[k] < 0) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += wk[k] * T::to_f32(v[k][i] & 0xffffu);
+        acc[2 * i + 1] += wk[k] * T::to_f32(v[k][i] >> 16);
+      }
     }
   }
+  if (col >= p.H) return;
   u32x4 o;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
