@@ -59,6 +59,7 @@ def _load():
                                        P, P, P, P, P, P, P, P, P, i32]
     lib.oracle_moe_forward.restype = ctypes.c_int
     lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_route_topk.argtypes = [P, i64, i32, i32, i32, P, P]
     _lib = lib
     return lib
 
@@ -173,3 +174,16 @@ def moe_forward(x_bits, w13p, w13s, w2p, w2s, ids, wts, *, hidden: int, inter: i
                                     _p(yr) if yr is not None else None, nthreads)
     assert rc == 0, "oracle allocation failed"
     return (out, yr[: T * K]) if want_routes else out
+
+
+def route_topk(logits, top_k: int, renormalize: bool = False):
+    """Router scoring: (ids int32 [T, K], weights fp32 [T, K]) from fp32
+    logits [T, E_global]: softmax over all experts, the K largest in
+    descending order (ties to the lower id), renormalized over the K if asked."""
+    logits = _c(logits, np.float32)
+    T, Eg = logits.shape
+    ids = np.empty((T, top_k), np.int32)
+    wts = np.empty((T, top_k), np.float32)
+    _load().oracle_route_topk(_p(logits), T, Eg, top_k, 1 if renormalize else 0, _p(ids),
+                              _p(wts))
+    return ids, wts

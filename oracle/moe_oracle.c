@@ -374,6 +374,53 @@ int oracle_moe_forward(int64_t T, int32_t H, int32_t I, int32_t E, int32_t off, 
   return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Router scoring and top-k, the step before route preparation ([P2] Final  */
+/* performance: the timed region includes routing; the workloads' recipe:   */
+/* softmax of the router logits over all global experts, the K largest,     */
+/* no renormalisation unless asked).                                         */
+/* ------------------------------------------------------------------------ */
+
+/* For token t: p_e = exp(l_e - m) / sum_j exp(l_j - m) with m the largest
+ * logit (probabilities in double, rounded once to FP32); the K experts of
+ * largest probability in descending order, ties to the lower id.  The
+ * selection compares logits: the softmax is strictly increasing in the logit,
+ * so the order is the same, and no tie is decided between probabilities that
+ * only rounding made equal.  A logit of -inf has probability 0; if every
+ * logit of a token is -inf, every weight is 0 (ids still lowest first).
+ * renorm != 0: the K weights are divided by their sum (in top-k order). */
+void oracle_route_topk(const float* logits, int64_t T, int32_t Eg, int32_t K, int32_t renorm,
+                       int32_t* ids, float* weights) {
+  char* taken = (char*)malloc((size_t)Eg);
+  double* w = (double*)malloc(sizeof(double) * (size_t)K);
+  for (int64_t t = 0; t < T; ++t) {
+    const float* l = logits + t * Eg;
+    double m = -INFINITY;
+    for (int32_t e = 0; e < Eg; ++e)
+      if ((double)l[e] > m) m = l[e];
+    double z = 0.0;
+    if (m != -INFINITY)
+      for (int32_t e = 0; e < Eg; ++e) z += exp((double)l[e] - m);
+    memset(taken, 0, (size_t)Eg);
+    for (int32_t k = 0; k < K; ++k) {
+      int32_t best = -1;
+      for (int32_t e = 0; e < Eg; ++e)
+        if (!taken[e] && (best < 0 || l[e] > l[best])) best = e;  /* strict: lower id on ties */
+      taken[best] = 1;
+      ids[t * K + k] = best;
+      w[k] = (m == -INFINITY || l[best] == -INFINITY) ? 0.0 : exp((double)l[best] - m) / z;
+    }
+    if (renorm) {
+      double sum = 0.0;
+      for (int32_t k = 0; k < K; ++k) sum += w[k];
+      for (int32_t k = 0; k < K; ++k) w[k] = sum > 0.0 ? w[k] / sum : 0.0;
+    }
+    for (int32_t k = 0; k < K; ++k) weights[t * K + k] = (float)w[k];
+  }
+  free(taken);
+  free(w);
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

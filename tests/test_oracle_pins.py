@@ -438,3 +438,65 @@ def test_prepare_routes_brute_force(T, K, E, E_global, off, bm):
     for r, p in enumerate(slot):
         if p >= 0:
             assert srt[p] == r
+
+
+# ---------------------------------------------------------------------------
+# router scoring and top-k (softmax over all global experts, K largest)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,Eg,K", [(5, 8, 2), (7, 256, 8), (3, 384, 8), (4, 1024, 32)])
+def test_route_topk_matches_float64_softmax_topk(T, Eg, K):
+    """Random N(0,1) logits (no ties): same ids and order as torch's float64
+    softmax followed by topk, weights equal to the float64 probabilities."""
+    rng = np.random.default_rng(Eg + K)
+    logits = rng.standard_normal((T, Eg)).astype(np.float32)
+    ids, w = oracle.route_topk(logits, K)
+    p = torch.softmax(torch.from_numpy(logits).double(), dim=-1)
+    ref_w, ref_i = torch.topk(p, K, dim=-1)
+    np.testing.assert_array_equal(ids, ref_i.numpy())
+    np.testing.assert_allclose(w, ref_w.numpy(), rtol=1e-6, atol=0)
+
+
+def test_route_topk_closed_forms():
+    # probabilities 1/6, 2/6, 3/6: the two largest are experts 2 and 1
+    logits = np.log(np.array([[1.0, 2.0, 3.0]], np.float64)).astype(np.float32)
+    ids, w = oracle.route_topk(logits, 2)
+    np.testing.assert_array_equal(ids, [[2, 1]])
+    np.testing.assert_allclose(w, [[0.5, 1.0 / 3.0]], rtol=1e-6)
+    # equal logits: every probability 1/E, ids in ascending order
+    ids, w = oracle.route_topk(np.zeros((2, 12), np.float32), 5)
+    np.testing.assert_array_equal(ids, [[0, 1, 2, 3, 4]] * 2)
+    np.testing.assert_array_equal(w, np.full((2, 5), np.float32(1.0 / 12.0)))
+    # ties go to the lower id
+    ids, w = oracle.route_topk(np.array([[1, 3, 3, 2, 3]], np.float32), 4)
+    np.testing.assert_array_equal(ids, [[1, 2, 4, 3]])
+    assert w[0, 0] == w[0, 1] == w[0, 2] > w[0, 3]
+
+
+def test_route_topk_masked_experts_and_renormalization():
+    rng = np.random.default_rng(3)
+    logits = rng.standard_normal((6, 64)).astype(np.float32)
+    logits[:, 15::16] = -np.inf                   # masked experts never chosen
+    ids, w = oracle.route_topk(logits, 6)
+    assert not np.isin(ids, np.arange(15, 64, 16)).any()
+    p = np.exp(logits.astype(np.float64) - logits.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(w, np.take_along_axis(p, ids, 1), rtol=1e-6)
+    # renormalized: same ids, weights proportional, summing to 1
+    ids_r, w_r = oracle.route_topk(logits, 6, renormalize=True)
+    np.testing.assert_array_equal(ids_r, ids)
+    np.testing.assert_allclose(w_r.sum(axis=1), 1.0, rtol=1e-6)
+    np.testing.assert_allclose(w_r, w / w.sum(axis=1, keepdims=True), rtol=1e-6)
+    # a token whose logits are all -inf: zero weights, lowest ids
+    ids_m, w_m = oracle.route_topk(np.full((1, 8), -np.inf, np.float32), 3)
+    np.testing.assert_array_equal(ids_m, [[0, 1, 2]])
+    np.testing.assert_array_equal(w_m, np.zeros((1, 3), np.float32))
+
+
+def test_route_topk_shift_invariance():
+    rng = np.random.default_rng(4)
+    logits = rng.standard_normal((9, 384)).astype(np.float32)
+    ids, w = oracle.route_topk(logits, 8)
+    ids2, w2 = oracle.route_topk(logits + np.float32(4.0), 8)
+    np.testing.assert_array_equal(ids, ids2)
+    np.testing.assert_allclose(w, w2, rtol=1e-5)
