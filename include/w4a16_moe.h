@@ -184,6 +184,26 @@ w4a16_status_t w4a16_moe_prepare_routes(const w4a16_moe_desc_t* desc, const int3
 w4a16_status_t w4a16_unpack_int4(const uint8_t* packed, int64_t n_bytes, int8_t* out,
                                  w4a16_stream_t stream);
 
+/* Router scoring and top-k, the step before route preparation ([P2] Final
+ * performance: routing is timed with the MoE; [P1] Benchmark: FP32 routing
+ * weights, INT32 ids, no renormalization).  For each token t:
+ *   p_e = exp(l_e - max_j l_j) / sum_j exp(l_j - max_j l_j) over all
+ *   num_global_experts logits (FP32), then the top_k experts of largest p in
+ *   descending order, ties to the lower id; a logit of -inf has p = 0.
+ *   logits        [T][num_global_experts] fp32, device, row-major
+ *   topk_ids      [T][top_k] int32 out: global expert ids (feed
+ *                 w4a16_moe_forward, which masks ids outside its local range)
+ *   topk_weights  [T][top_k] fp32 out: p of each chosen expert, or p divided
+ *                 by the sum of the top_k p (in top-k order) if renormalize = 1
+ * Supported: 1 <= num_global_experts <= 1024, 1 <= top_k <= min(32,
+ * num_global_experts), 0 <= num_tokens <= 2^31 - 1.  T = 0 enqueues nothing.
+ * Errors are returned before anything is enqueued; NaN logits give an
+ * unspecified selection.  Results are bitwise repeatable. */
+w4a16_status_t w4a16_moe_route_topk(const float* logits, int64_t num_tokens,
+                                    int32_t num_global_experts, int32_t top_k,
+                                    int32_t renormalize, int32_t* topk_ids, float* topk_weights,
+                                    w4a16_stream_t stream);
+
 /* Static text for a status code. */
 const char* w4a16_status_string(w4a16_status_t status);
 

@@ -63,12 +63,13 @@ def lib():
     L.w4a16_moe_forward_timed.argtypes = [P, P, P, P, P, P, P, P, pdesc, P, sz, P, P, i32]
     L.w4a16_moe_prepare_routes.argtypes = [pdesc, P, i32, P, P, P, i64, P, P, P]
     L.w4a16_unpack_int4.argtypes = [P, i64, P, P]
+    L.w4a16_moe_route_topk.argtypes = [P, i64, i32, i32, i32, P, P, P]
     L.w4a16_status_string.argtypes = [i32]
     L.w4a16_status_string.restype = ctypes.c_char_p
     L.w4a16_last_error_message.restype = ctypes.c_char_p
     for f in ("w4a16_moe_workspace_size", "w4a16_moe_get_plan", "w4a16_moe_forward",
               "w4a16_moe_forward_timed",
-              "w4a16_moe_prepare_routes", "w4a16_unpack_int4"):
+              "w4a16_moe_prepare_routes", "w4a16_unpack_int4", "w4a16_moe_route_topk"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -240,3 +241,26 @@ def unpack_int4(packed: torch.Tensor, stream=None) -> torch.Tensor:
     out = torch.empty(packed.numel() * 2, dtype=torch.int8, device=packed.device)
     _check(lib().w4a16_unpack_int4(_ptr(packed), packed.numel(), _ptr(out), _stream(stream)))
     return out
+
+
+def route_topk(logits: torch.Tensor, top_k: int, renormalize: bool = False, out=None,
+               stream=None):
+    """Router scoring: (topk_ids int32 [T, K], topk_weights fp32 [T, K]) from fp32
+    logits [T, E_global] on the GPU (softmax over all experts, the K largest,
+    ties to the lower id; renormalized over the K if asked)."""
+    _dev("logits", logits, (torch.float32,))
+    if logits.dim() != 2:
+        raise ValueError("logits: expected [T, E_global]")
+    T, Eg = logits.shape
+    if out is None:
+        ids = torch.empty(T, top_k, dtype=torch.int32, device=logits.device)
+        wts = torch.empty(T, top_k, dtype=torch.float32, device=logits.device)
+    else:
+        ids, wts = out
+        _dev("topk_ids", ids, (torch.int32,), logits.device)
+        _dev("topk_weights", wts, (torch.float32,), logits.device)
+        if tuple(ids.shape) != (T, top_k) or tuple(wts.shape) != (T, top_k):
+            raise ValueError("out: expected two [T, top_k] tensors")
+    _check(lib().w4a16_moe_route_topk(_ptr(logits), T, Eg, top_k, 1 if renormalize else 0,
+                                      _ptr(ids), _ptr(wts), _stream(stream)))
+    return ids, wts

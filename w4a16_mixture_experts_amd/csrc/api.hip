@@ -621,4 +621,35 @@ w4a16_status_t w4a16_unpack_int4(const uint8_t* packed, int64_t n_bytes, int8_t*
   return hip_status(w4moe::launch_unpack(packed, n_bytes, out, stream), "unpack launch");
 }
 
+w4a16_status_t w4a16_moe_route_topk(const float* logits, int64_t num_tokens,
+                                    int32_t num_global_experts, int32_t top_k,
+                                    int32_t renormalize, int32_t* topk_ids, float* topk_weights,
+                                    w4a16_stream_t stream_) {
+  if (num_tokens < 0) return fail(W4A16_ERR_INVALID_ARG, "logits: num_tokens=%lld < 0", (long long)num_tokens);
+  if (num_tokens > INT32_MAX)
+    return fail(W4A16_ERR_UNSUPPORTED, "logits: num_tokens=%lld exceeds %d", (long long)num_tokens,
+                INT32_MAX);
+  if (num_global_experts < 1 || num_global_experts > w4moe::kRouterMaxExperts)
+    return fail(W4A16_ERR_UNSUPPORTED, "logits: num_global_experts=%d (1..%d)", num_global_experts,
+                w4moe::kRouterMaxExperts);
+  if (top_k < 1 || top_k > w4moe::kRouterMaxTopK || top_k > num_global_experts)
+    return fail(W4A16_ERR_UNSUPPORTED, "topk_ids: top_k=%d (1..min(%d, num_global_experts))", top_k,
+                w4moe::kRouterMaxTopK);
+  if (renormalize != 0 && renormalize != 1)
+    return fail(W4A16_ERR_INVALID_ARG, "renormalize: %d (0 or 1)", renormalize);
+  if (num_tokens == 0) return W4A16_OK;
+  const struct {
+    const void* p;
+    const char* name;
+  } ptrs[] = {{logits, "logits"}, {topk_ids, "topk_ids"}, {topk_weights, "topk_weights"}};
+  for (const auto& q : ptrs) {
+    if (q.p == nullptr) return fail(W4A16_ERR_INVALID_ARG, "%s: null pointer", q.name);
+    if (misaligned(q.p, 4)) return fail(W4A16_ERR_INVALID_ARG, "%s: address not 4-byte aligned", q.name);
+  }
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  return hip_status(w4moe::launch_router_topk(logits, static_cast<int>(num_tokens), num_global_experts,
+                                              top_k, renormalize, topk_ids, topk_weights, stream),
+                    "router launch");
+}
+
 }  // extern "C"

@@ -169,4 +169,10 @@ hipError_t launch_combine(const CombineParams& p, int dtype, int T, hipStream_t 
 
 hipError_t launch_unpack(const uint8_t* packed, int64_t n_bytes, int8_t* out, hipStream_t stream);
 
+// Router scoring and top-k (softmax over E_global logits, K largest).
+constexpr int kRouterMaxExperts = 1024;
+constexpr int kRouterMaxTopK = 32;
+hipError_t launch_router_topk(const float* logits, int T, int Eg, int K, int renorm, int32_t* ids,
+                              float* wts, hipStream_t stream);
+
 }  // namespace w4moe
