@@ -383,8 +383,26 @@ def main():
 
             g_cold = capture(cold_body)
             g_warm = capture(warm_body)
+        # router scoring + top-k on the same token batch (context: the step
+        # before the timed forward), timed the same way
+        ids_r = torch.empty(T, wl.top_k, dtype=torch.int32, device=dev)
+        w_r = torch.empty(T, wl.top_k, dtype=torch.float32, device=dev)
+
+        def route(tok=tok, ids_r=ids_r, w_r=w_r):
+            return binding.route_topk(tok.logits, wl.top_k, out=(ids_r, w_r))
+
+        route()
+        g_route = None
+        if not args.no_graph:
+            def route_body(route=route):
+                for _ in range(G):
+                    flush()
+                    route()
+
+            g_route = capture(route_body)
         stage_b, total_b, total_f, stage_f, D, Rv = workload_bytes_flops(wl, tok.topk_ids.cpu(), T)
         cases.append(dict(T=T, tok=tok, fwd=fwd, g_cold=g_cold, g_warm=g_warm, plan=plan,
+                          route=route, g_route=g_route, router=[],
                           stage_bytes=stage_b,
                           bytes=total_b, flops=total_f, stage_flops=stage_f, D=D, Rv=Rv,
                           cold=[], warm=[], stages={s: [] for s in STAGES}))
@@ -414,16 +432,32 @@ def main():
             flush()
             c["fwd"](stage_events=evs)
             evs[7 if c["plan"].path == 1 else 5].synchronize()
-            if not record:
-                continue
-            if c["g_cold"] is not None:
-                c["cold"].append((ev1.elapsed_time(ev2) - ev0.elapsed_time(ev1)) * 1e3 / G)
+            if record:
+                if c["g_cold"] is not None:
+                    c["cold"].append((ev1.elapsed_time(ev2) - ev0.elapsed_time(ev1)) * 1e3 / G)
+                else:
+                    c["cold"].append(ev0.elapsed_time(ev1) * 1e3)
+                for si, name in enumerate(STAGES):
+                    if name in ("route_prep", "combine") and c["plan"].path == 2:
+                        continue
+                    c["stages"][name].append(evs[2 * si].elapsed_time(evs[2 * si + 1]) * 1e3)
+            # router, cold, outside the forward's timing
+            if c["g_route"] is not None:
+                ev0.record()
+                graph_flush.replay()
+                ev1.record()
+                c["g_route"].replay()
+                ev2.record()
             else:
-                c["cold"].append(ev0.elapsed_time(ev1) * 1e3)
-            for si, name in enumerate(STAGES):
-                if name in ("route_prep", "combine") and c["plan"].path == 2:
-                    continue
-                c["stages"][name].append(evs[2 * si].elapsed_time(evs[2 * si + 1]) * 1e3)
+                flush()
+                ev0.record()
+                c["route"]()
+                ev1.record()
+                ev2.record()
+            ev2.synchronize()
+            if record:
+                c["router"].append(((ev1.elapsed_time(ev2) - ev0.elapsed_time(ev1)) / G
+                                    if c["g_route"] is not None else ev0.elapsed_time(ev1)) * 1e3)
 
     for _ in range(args.warmup):
         step(False)
@@ -471,6 +505,7 @@ def main():
             "plan": {"path": "small-batch" if c["plan"].path == 2 else "grouped",
                      "block_m": c["plan"].block_m, "k_slice": c["plan"].k_slice},
             "stage_us": {k: round(v, 3) for k, v in st.items()},
+            "router_us_cold": round(statistics.fmean(c["router"]), 3) if c["router"] else None,
             "stage_kernel": {k: kernel_name(wl, c["plan"], k) for k in st},
         }
         for k, v in st.items():

@@ -180,10 +180,12 @@ class Tokens:
     topk_weights: torch.Tensor  # [T, K] fp32
     skew_bias: float = 0.0
     hot_share: float = float("nan")
+    logits: Optional[torch.Tensor] = None  # [T, E_global] fp32 the routes came from
 
     def to(self, device) -> "Tokens":
         return Tokens(self.x.to(device), self.topk_ids.to(device), self.topk_weights.to(device),
-                      self.skew_bias, self.hot_share)
+                      self.skew_bias, self.hot_share,
+                      None if self.logits is None else self.logits.to(device))
 
 
 def _route(logits: torch.Tensor, k: int):
@@ -193,6 +195,16 @@ def _route(logits: torch.Tensor, k: int):
 
 
 HOT_EXPERTS = (0, 1, 2, 3)
+
+
+def _skew_logits(logits: torch.Tensor, b: float) -> torch.Tensor:
+    """The skewed workload's effective router logits: experts e = 15 (mod 16)
+    masked to -inf, the hot experts raised by b."""
+    E = logits.shape[1]
+    masked = torch.tensor([e % 16 == 15 for e in range(E)], device=logits.device)
+    hot = torch.zeros(E, dtype=torch.bool, device=logits.device)
+    hot[list(HOT_EXPERTS)] = True
+    return logits.masked_fill(masked, float("-inf")) + b * hot.float()
 
 
 def _skewed_route(logits: torch.Tensor, k: int, target: float = 0.25):
@@ -226,6 +238,7 @@ def make_tokens(wl: Workload, T: int, device="cpu", seed: Optional[int] = None) 
                          dtype=torch.float32)
     if wl.skew and T > 0:
         ids, w, b, sh = _skewed_route(logits, wl.top_k)
-        return Tokens(x.contiguous(), ids, w, b, sh)
+        eff = _skew_logits(logits, b)
+        return Tokens(x.contiguous(), ids, w, b, sh, eff.contiguous())
     ids, w = _route(logits, wl.top_k)
-    return Tokens(x.contiguous(), ids, w)
+    return Tokens(x.contiguous(), ids, w, logits=logits.contiguous())
