@@ -47,6 +47,9 @@ struct GemmParams {
   int R;                      // routes (T*K)
   const int32_t* slot;        // [R] route -> position, -1 for invalid routes
   int tiles;                  // entries of tile_expert (positions / bm)
+  // streaming tile kernel, bf16 group layout: non-null selects the exact
+  // fp16 route; one flag per workgroup (set when its tile is to be rerun)
+  int32_t* redo;
 };
 
 // small-batch path
@@ -155,6 +158,12 @@ hipError_t launch_down_resident(const GemmParams& p, int dtype, int layout, int 
                                 hipStream_t stream);
 hipError_t launch_tile_gemm(const GemmParams& p, int dtype, int layout, int mode, int max_tiles,
                             hipStream_t stream);
+// workgroups of the kernel that reruns flagged tiles of a fp16-route launch
+constexpr int kTileRedoWorkgroups = 256;
+// workgroups of a streaming tile launch (the size of its flag array)
+inline int64_t tile_launch_workgroups(int n_tiles, int64_t max_tiles) {
+  return 8 * static_cast<int64_t>(n_tiles) * ((max_tiles + 7) / 8);
+}
 
 hipError_t launch_decode_up(const DecodeUpParams& p, int dtype, int layout, bool gated, int nkb,
                             int grid_x, hipStream_t stream);

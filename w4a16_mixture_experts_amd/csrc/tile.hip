@@ -34,6 +34,8 @@
 // re-reads of a tile's activations by its column workgroups hit that XCD's L2.
 // Epilogue: UP writes the 16-bit activation (SiLU(gate)*up or ReLU^2) in A
 // operand order; DOWN writes the 16-bit expert outputs Y.
+#include <algorithm>
+
 #include "device.h"
 #include "internal.h"
 
@@ -313,6 +315,86 @@ __device__ __forceinline__ void mma_block2(const uint16_t* sa, int stride,
   }
 }
 
+// Exact dequantization to fp16 for bf16 activations and bf16 group scales.
+//   A bf16 activation converts to fp16 exactly when its magnitude is below
+//   2^16 (fp16 carries more significand bits; values below 2^-17 lose low
+//   bits, an error under 2^-24); the conversion rounds to nearest, so a
+//   magnitude of 2^16 or more (no bf16 value lies between fp16's largest
+//   65504 and 65520) becomes an infinity, which makes the tile's accumulators
+//   non-finite (an infinity times a zero weight is NaN).  Such a tile is
+//   rerun with the per-group form (tile_redo_kernel), which also gives
+//   infinite or NaN activations their plain meaning.  q * s, with q in [-8, 7] and a bf16
+//   scale s, has at most 3 + 8 significant bits, so it is exact in fp16 as
+//   well.  It is formed per value pair as one fused multiply-add
+//   (24 + q)/16 * 16s - 24s whose exact result is representable (16s and 24s
+//   are exact in fp16 for scales below 2730).  The MFMA then accumulates
+//   x * (q s) over every group in FP32: no per-group scaling and no
+//   correction term.
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v) {
+  // round to nearest (one packed conversion)
+  const f16x2 r = {static_cast<_Float16>(__uint_as_float(v << 16)),
+                   static_cast<_Float16>(__uint_as_float(v & 0xffff0000u))};
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
+  u32x4 r;
+  r[0] = bf16x2_to_f16x2(v[0]);
+  r[1] = bf16x2_to_f16x2(v[1]);
+  r[2] = bf16x2_to_f16x2(v[2]);
+  r[3] = bf16x2_to_f16x2(v[3]);
+  return r;
+}
+// (24 + q)/16 * 16s - 24s for one pair.  The operand comes in by value: a
+// bit cast applied directly to a vector element was compiled as a cast of
+// element 0 for every element.
+__device__ __forceinline__ uint32_t dequant_pair_f16(uint32_t q2, f16x2 s16, f16x2 m24) {
+  const f16x2 qv = __builtin_bit_cast(f16x2, q2);
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qv, s16, m24));
+}
+
+// acc += A[rows 0..16*NMS) x deq(W block)^T for one 128-block with the exact
+// fp16 dequantization above (A staged as fp16; group layout, bf16 scales in
+// wb[s].s0 / s1 as for mma_block).  acc holds the plain sum (no factor 16).
+template <int NMS, int NSUB = kNsub>
+__device__ __forceinline__ void mma_block_x(const uint16_t* sa, int stride,
+                                            const WBlk<Q_GROUP_K> (&wb)[NSUB],
+                                            f32x4 (&acc)[NMS][NSUB], int c, int g) {
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 af[NMS][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int ms = 0; ms < NMS; ++ms)
+      af[ms][j] = *reinterpret_cast<const u32x4*>(sa + (16 * ms + c) * stride + 32 * j + 8 * g);
+  uint32_t d[NSUB][4];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    d[s][0] = wb[s].d[0]; d[s][1] = wb[s].d[1]; d[s][2] = wb[s].d[2]; d[s][3] = wb[s].d[3];
+    transpose_rows4(d[s][0], d[s][1], d[s][2], d[s][3]);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    u32x4 bop[NSUB];
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      const uint32_t pr = (j < 2) ? wb[s].s0 : wb[s].s1;
+      const float sf = (j & 1) ? __uint_as_float(pr & 0xffff0000u) : __uint_as_float(pr << 16);
+      const f16x2 s16 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(16.0f * sf, 16.0f * sf));
+      const f16x2 m24 = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(-24.0f * sf, -24.0f * sf));
+      const u32x4 q = nibbles_to_h16<DT_FP16>(d[s][j]);
+      bop[s][0] = dequant_pair_f16(q[0], s16, m24);
+      bop[s][1] = dequant_pair_f16(q[1], s16, m24);
+      bop[s][2] = dequant_pair_f16(q[2], s16, m24);
+      bop[s][3] = dequant_pair_f16(q[3], s16, m24);
+    }
+#pragma unroll
+    for (int ms = 0; ms < NMS; ++ms)
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) acc[ms][s] = H16<DT_FP16>::mfma(af[ms][j], bop[s], acc[ms][s]);
+  }
+}
+
 // Valid rows of the lane's 16 * NMS output rows as a bit mask: bit 4ms + i
 // stands for tile row 16ms + 4g + i.
 template <int NMS>
@@ -402,10 +484,15 @@ __device__ __forceinline__ int active_subtiles(const GemmParams& p, int row_base
 // step).
 // ---------------------------------------------------------------------------
 
-template <int DT, int LAYOUT, int MODE, int NMS, bool SCL>
-__device__ __forceinline__ void tile_run(const GemmParams& p, const int row_base, const int e,
+// X16: the exact fp16 dequantization (bf16 activations and scales, group
+// layout); returns false, with nothing stored, if an accumulator is not
+// finite (an activation of magnitude 2^16 or more, an infinity or a NaN),
+// true otherwise.
+template <int DT, int LAYOUT, int MODE, int NMS, bool SCL, bool X16 = false>
+__device__ __forceinline__ bool tile_run(const GemmParams& p, const int row_base, const int e,
                                          const int nt, uint16_t* s_lds, const int st_r) {
   constexpr bool UP = MODE != MODE_DOWN;
+  static_assert(!X16 || (DT == DT_BF16 && LAYOUT == Q_GROUP_K && !SCL), "fp16 route");
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int c = lane & 15, g = lane >> 4, par = c & 1;
 
@@ -438,8 +525,14 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, const int row_base
   auto store_a = [&](uint16_t* blk, const u32x4 (&v)[kChunks]) {
     uint16_t* dst = blk + st_row * kAStride + kVals * st_c;
 #pragma unroll
-    for (int h = 0; h < kChunks; ++h)
-      *reinterpret_cast<u32x4*>(dst + 8 * h) = UP ? permute_a(v[h]) : v[h];
+    for (int h = 0; h < kChunks; ++h) {
+      const u32x4 a = UP ? permute_a(v[h]) : v[h];
+      if constexpr (X16) {
+        *reinterpret_cast<u32x4*>(dst + 8 * h) = bf16x8_to_f16x8(a);
+      } else {
+        *reinterpret_cast<u32x4*>(dst + 8 * h) = a;
+      }
+    }
   };
 
   f32x4 acc[NMS][kNsub];
@@ -540,7 +633,8 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, const int row_base
     uint16_t* sy = s_lds + 2 * kStageElems * ((s & 1) ^ 1);
     load_wblk<LAYOUT, kNsub, SC_SECOND>(wx, ws, 128 * (b + 1), p.K, g, wr[1]);
     if constexpr (SCL) set_scales(b - pb0, wr[0]);
-    mma_block<DT, LAYOUT, NMS>(sx, kAStride, wr[0], acc, c, g, par);
+    if constexpr (X16) mma_block_x<NMS>(sx, kAStride, wr[0], acc, c, g);
+    else mma_block<DT, LAYOUT, NMS>(sx, kAStride, wr[0], acc, c, g, par);
     if constexpr (!SCL) pass_scales<LAYOUT, kNsub>(wr[0], wr[1]);
     store_a(sy, an[0]);
     store_a(sy + kStageElems, an[1]);
@@ -549,7 +643,8 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, const int row_base
     load_wblk<LAYOUT, kNsub, SC_FIRST>(wx, ws, 128 * (b + 2), p.K, g, wr[0]);
     if (b + 1 < nblk) {
       if constexpr (SCL) set_scales(b + 1 - pb0, wr[1]);
-      mma_block<DT, LAYOUT, NMS>(sx + kStageElems, kAStride, wr[1], acc, c, g, par);
+      if constexpr (X16) mma_block_x<NMS>(sx + kStageElems, kAStride, wr[1], acc, c, g);
+      else mma_block<DT, LAYOUT, NMS>(sx + kStageElems, kAStride, wr[1], acc, c, g, par);
     }
     __syncthreads();
   };
@@ -606,19 +701,31 @@ __device__ __forceinline__ void tile_run(const GemmParams& p, const int row_base
       }
     }
   }
+  if constexpr (X16) {
+    bool bad = false;
+#pragma unroll
+    for (int ms = 0; ms < NMS; ++ms)
+#pragma unroll
+      for (int s2 = 0; s2 < kNsub; ++s2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bad |= !__builtin_isfinite(acc[ms][s2][i]);
+    if (__syncthreads_or(bad)) return false;
+    // the epilogue applies the per-group form's factor 16 (exact)
+#pragma unroll
+    for (int ms = 0; ms < NMS; ++ms)
+#pragma unroll
+      for (int s2 = 0; s2 < kNsub; ++s2) acc[ms][s2] *= 0.0625f;
+  }
   store_outputs<DT, MODE, NMS>(p, row_base, acc, col, on, g, valid_rows<NMS>(p, row_base, g));
+  return true;
 }
 
-template <int DT, int LAYOUT, int MODE, bool SCL>
-__global__ void __launch_bounds__(kTileThreads)
-tile_gemm_kernel(const GemmParams p) {
-  // [2 stages][2 blocks][kTileRows][kAStride] activations, then (SCL) the
-  // group scales: [256 rows][K / 32] or [256 rows][kScPhaseGroups]
-  extern __shared__ __align__(16) uint16_t s_lds[];
-
+// The work of tile-kernel workgroup L.  X16: tiles of several subtiles take
+// the exact fp16 route; returns false if such a tile must be rerun.
+template <int DT, int LAYOUT, int MODE, bool SCL, bool X16>
+__device__ __forceinline__ bool tile_work(const GemmParams& p, const int L, uint16_t* s_lds) {
   // workgroup L runs on XCD L % 8; XCD x takes tiles x, x + 8, ... and walks
   // the column tiles of each tile back to back
-  const int L = blockIdx.x;
   const int q = L / kXcds;
   const int mt = kXcds * (q / p.n_tiles) + L % kXcds;
   const int nt = q % p.n_tiles;
@@ -637,7 +744,7 @@ tile_gemm_kernel(const GemmParams p) {
   // the loads behind the exit below (one round trip instead of several)
   asm volatile("" : : "s"(total), "s"(e), "s"(first[0]), "s"(first[1]), "s"(first[2]), "s"(first[3]),
                "v"(st_r));
-  if (row_base >= total) return;  // whole workgroup: tile past the padded total
+  if (row_base >= total) return true;  // whole workgroup: tile past the padded total
   int nms = 0;
 #pragma unroll
   for (int ms = 0; ms < kTileMs; ++ms) nms += first[ms] >= 0 ? 1 : 0;
@@ -646,10 +753,38 @@ tile_gemm_kernel(const GemmParams p) {
   // VALU issue, and scales fetched with the weights (per block pair) keep
   // the register count lower and measured faster
   switch (nms) {
-    case 1: tile_run<DT, LAYOUT, MODE, 1, SCL>(p, row_base, e, nt, s_lds, st_r); break;
-    case 2: tile_run<DT, LAYOUT, MODE, 2, false>(p, row_base, e, nt, s_lds, st_r); break;
-    case 3: tile_run<DT, LAYOUT, MODE, 3, false>(p, row_base, e, nt, s_lds, st_r); break;
-    default: tile_run<DT, LAYOUT, MODE, 4, false>(p, row_base, e, nt, s_lds, st_r); break;
+    case 1: return tile_run<DT, LAYOUT, MODE, 1, SCL>(p, row_base, e, nt, s_lds, st_r);
+    case 2: return tile_run<DT, LAYOUT, MODE, 2, false, X16>(p, row_base, e, nt, s_lds, st_r);
+    case 3: return tile_run<DT, LAYOUT, MODE, 3, false, X16>(p, row_base, e, nt, s_lds, st_r);
+    default: return tile_run<DT, LAYOUT, MODE, 4, false, X16>(p, row_base, e, nt, s_lds, st_r);
+  }
+}
+
+template <int DT, int LAYOUT, int MODE, bool SCL, bool X16>
+__global__ void __launch_bounds__(kTileThreads)
+tile_gemm_kernel(const GemmParams p) {
+  // [2 stages][2 blocks][kTileRows][kAStride] activations, then (SCL) the
+  // group scales: [256 rows][K / 32] or [256 rows][kScPhaseGroups]
+  extern __shared__ __align__(16) uint16_t s_lds[];
+  // X16: every workgroup records whether its tile must be rerun (the flag
+  // array needs no clearing)
+  const bool done = tile_work<DT, LAYOUT, MODE, SCL, X16>(p, static_cast<int>(blockIdx.x), s_lds);
+  if constexpr (X16) {
+    if (threadIdx.x == 0) p.redo[blockIdx.x] = done ? 0 : 1;
+  }
+}
+
+// Reruns, with the per-group form, the tiles of a fp16-route launch of
+// n_wg workgroups whose activations left fp16's range (normally none: every
+// workgroup reads a flag or a few and exits).
+template <int DT, int LAYOUT, int MODE>
+__global__ void __launch_bounds__(kTileThreads)
+tile_redo_kernel(const GemmParams p, const int n_wg) {
+  extern __shared__ __align__(16) uint16_t s_lds[];
+  for (int L = blockIdx.x; L < n_wg; L += gridDim.x) {
+    if (p.redo[L] == 0) continue;  // uniform
+    tile_work<DT, LAYOUT, MODE, false, false>(p, L, s_lds);
+    __syncthreads();  // LDS reuse by the next tile
   }
 }
 
@@ -1145,26 +1280,47 @@ hipError_t launch_splitk_act(const GemmParams& p, int dtype, bool gated, hipStre
   return hipGetLastError();
 }
 
-template <int DT, int LAYOUT, int MODE>
-static hipError_t launch_tile_k(const GemmParams& p, dim3 grid, hipStream_t st) {
+template <int DT, int LAYOUT, int MODE, bool X16>
+static hipError_t launch_tile_kx(const GemmParams& p, dim3 grid, hipStream_t st) {
   if constexpr (LAYOUT == Q_GROUP_K) {
     if (tile_scales_in_lds(LAYOUT, p.K)) {
       const size_t lds = tile_lds_bytes(true, p.K);
-      const hipError_t err = allow_lds_tile(tile_gemm_kernel<DT, LAYOUT, MODE, true>, lds);
+      const hipError_t err = allow_lds_tile(tile_gemm_kernel<DT, LAYOUT, MODE, true, X16>, lds);
       if (err != hipSuccess) return err;
-      hipLaunchKernelGGL((tile_gemm_kernel<DT, LAYOUT, MODE, true>), grid, dim3(kTileThreads), lds,
-                         st, p);
+      hipLaunchKernelGGL((tile_gemm_kernel<DT, LAYOUT, MODE, true, X16>), grid, dim3(kTileThreads),
+                         lds, st, p);
       return hipGetLastError();
     }
   }
   // per-channel scales, or group scales that neither fit whole nor split
   // into phases: fetched with the weights, per block pair
   const size_t lds = tile_lds_bytes(false, p.K);
-  const hipError_t err = allow_lds_tile(tile_gemm_kernel<DT, LAYOUT, MODE, false>, lds);
+  const hipError_t err = allow_lds_tile(tile_gemm_kernel<DT, LAYOUT, MODE, false, X16>, lds);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((tile_gemm_kernel<DT, LAYOUT, MODE, false>), grid, dim3(kTileThreads), lds, st,
-                     p);
+  hipLaunchKernelGGL((tile_gemm_kernel<DT, LAYOUT, MODE, false, X16>), grid, dim3(kTileThreads), lds,
+                     st, p);
   return hipGetLastError();
+}
+
+template <int DT, int LAYOUT, int MODE>
+static hipError_t launch_tile_k(const GemmParams& p, dim3 grid, hipStream_t st) {
+  if constexpr (DT == DT_BF16 && LAYOUT == Q_GROUP_K) {
+    if (p.redo != nullptr) {
+      // fp16 route, then the rerun of flagged tiles (a few workgroups that
+      // each scan a share of the flags)
+      hipError_t err = launch_tile_kx<DT, LAYOUT, MODE, true>(p, grid, st);
+      if (err != hipSuccess) return err;
+      const size_t lds = tile_lds_bytes(false, p.K);
+      err = allow_lds_tile(tile_redo_kernel<DT, LAYOUT, MODE>, lds);
+      if (err != hipSuccess) return err;
+      const int n_wg = static_cast<int>(grid.x);
+      const dim3 rgrid(static_cast<unsigned>(std::min(n_wg, kTileRedoWorkgroups)));
+      hipLaunchKernelGGL((tile_redo_kernel<DT, LAYOUT, MODE>), rgrid, dim3(kTileThreads), lds, st,
+                         p, n_wg);
+      return hipGetLastError();
+    }
+  }
+  return launch_tile_kx<DT, LAYOUT, MODE, false>(p, grid, st);
 }
 
 template <int DT, int LAYOUT>
