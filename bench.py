@@ -177,9 +177,9 @@ def counter_pass(args, wl, sweep, dev):
 
 
 # kernel whose HBM traffic the counter pass measures: the gate/up tile kernel
-# (group layout, bf16, LDS scales), as the profiler names it and as this
-# script prints it
-COUNTED = ("tile_gemm_kernel<0, 0, 0, true>", "tile_gemm_kernel<0, 0, 0>", "tile.hip")
+# (group layout, bf16, LDS scales; per-group or fp16 route), as a prefix of
+# the names the profiler prints and as this script prints it
+COUNTED = ("tile_gemm_kernel<0, 0, 0, true,", "tile_gemm_kernel<0, 0, 0>", "tile.hip")
 
 
 def summarize_counters(args, sweep):
