@@ -179,12 +179,13 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
   // group scales): it drops the per-group scaling of the output, which pays
   // when tiles hold several 16-row subtiles; each such launch is followed by
   // a small launch that reruns tiles with activations outside fp16's range.
-  // Measured on the Kimi shard: 7 % faster gate/up at about 43 routes per
-  // expert (2048 tokens), no gain at about 21 (1024 tokens).
+  // Measured on the Kimi shard: 549 -> 532 us at about 43 routes per expert
+  // (2048 tokens), 373 -> 369 us at about 21 (1024 tokens); tiles of one
+  // subtile (5 routes per expert at 256 tokens) keep the per-group form.
   if (tile64 && pl.R > 0 && d->dtype == W4A16_DT_BF16 && d->qlayout == W4A16_Q_GROUP_K) {
     const double R = static_cast<double>(pl.R);
     const double D = std::max(1.0, E * (1.0 - std::pow(1.0 - 1.0 / E, R)));
-    pl.x16 = R / D >= 32.0;
+    pl.x16 = R / D >= 16.0;
   }
   pl.down_resident = tile64 && I <= w4moe::kResidentK;
   if (pl.down_resident) {

@@ -159,7 +159,8 @@ hipError_t launch_down_resident(const GemmParams& p, int dtype, int layout, int 
 hipError_t launch_tile_gemm(const GemmParams& p, int dtype, int layout, int mode, int max_tiles,
                             hipStream_t stream);
 // workgroups of the kernel that reruns flagged tiles of a fp16-route launch
-constexpr int kTileRedoWorkgroups = 256;
+// (one per XCD)
+constexpr int kTileRedoWorkgroups = 8;
 // workgroups of a streaming tile launch (the size of its flag array)
 inline int64_t tile_launch_workgroups(int n_tiles, int64_t max_tiles) {
   return 8 * static_cast<int64_t>(n_tiles) * ((max_tiles + 7) / 8);

@@ -775,16 +775,26 @@ tile_gemm_kernel(const GemmParams p) {
 }
 
 // Reruns, with the per-group form, the tiles of a fp16-route launch of
-// n_wg workgroups whose activations left fp16's range (normally none: every
-// workgroup reads a flag or a few and exits).
+// n_wg workgroups whose activations left fp16's range.  Workgroup b owns
+// flags b, b + G, b + 2G, ... (G workgroups); each pass reads one flag per
+// thread, and only a pass with a flag set walks its flags one by one
+// (normally none is: every workgroup makes one pass of loads and exits).
 template <int DT, int LAYOUT, int MODE>
 __global__ void __launch_bounds__(kTileThreads)
 tile_redo_kernel(const GemmParams p, const int n_wg) {
   extern __shared__ __align__(16) uint16_t s_lds[];
-  for (int L = blockIdx.x; L < n_wg; L += gridDim.x) {
-    if (p.redo[L] == 0) continue;  // uniform
-    tile_work<DT, LAYOUT, MODE, false, false>(p, L, s_lds);
-    __syncthreads();  // LDS reuse by the next tile
+  const int G = static_cast<int>(gridDim.x);
+  for (int base = static_cast<int>(blockIdx.x); base < n_wg; base += G * kTileThreads) {
+    const int L = base + G * static_cast<int>(threadIdx.x);
+    const bool f = L < n_wg && p.redo[L] != 0;
+    if (!__syncthreads_or(f)) continue;
+    for (int i = 0; i < kTileThreads; ++i) {
+      const int Li = base + G * i;
+      if (Li >= n_wg) break;
+      if (p.redo[Li] == 0) continue;  // uniform
+      tile_work<DT, LAYOUT, MODE, false, false>(p, Li, s_lds);
+      __syncthreads();  // LDS reuse by the next tile
+    }
   }
 }
 
