@@ -99,6 +99,10 @@ typedef struct {
                                  the expected routes per expert, 1 = split-K
                                  gate/up (partials + activation kernel), 2 = the
                                  streaming gate/up kernel                        */
+  int32_t num_global_experts; /* experts the routes are drawn over (a local share
+                                 of E of them); only the variant choice uses it
+                                 (expected valid routes per local expert).
+                                 0 = E; otherwise >= E                           */
 } w4a16_moe_desc_t;
 
 /* Variant the library runs for a descriptor (for tests and reports). */

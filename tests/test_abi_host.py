@@ -59,6 +59,7 @@ def good(**kw):
     ("force_block_m", 48, 1, "force_block_m"),
     ("force_path", 3, 1, "force_path"),
     ("force_splitk", 3, 1, "force_splitk"),
+    ("num_global_experts", 7, 1, "num_global_experts"),
 ])
 def test_descriptor_errors(field, value, status, needle):
     d = good()

@@ -26,7 +26,8 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
 class MoeDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_tokens", "hidden", "intermediate", "num_local_experts", "expert_offset", "top_k",
-        "group_size", "dtype", "act", "qlayout", "force_path", "force_block_m", "force_splitk")]
+        "group_size", "dtype", "act", "qlayout", "force_path", "force_block_m", "force_splitk",
+        "num_global_experts")]
 
 
 class MoePlan(ctypes.Structure):
@@ -106,14 +107,17 @@ def _dev(name: str, t: torch.Tensor, dtypes, device=None):
 def make_desc(*, num_tokens: int, hidden: int, intermediate: int, num_local_experts: int,
               top_k: int, expert_offset: int = 0, dtype=torch.bfloat16, gated: bool = True,
               per_channel: bool = False, group_size: int = 32, force_path: int = 0,
-              force_block_m: int = 0, force_splitk: int = 0) -> MoeDesc:
+              force_block_m: int = 0, force_splitk: int = 0,
+              num_global_experts: int = 0) -> MoeDesc:
     """force_path: 0 auto, 1 grouped, 2 small batch; force_block_m: 0 or 16/32/64;
-    force_splitk: 0 auto, 1 split-K gate/up, 2 streaming gate/up (64-row tiles)."""
+    force_splitk: 0 auto, 1 split-K gate/up, 2 streaming gate/up (64-row tiles);
+    num_global_experts: experts the routes are drawn over (0 = num_local_experts),
+    used only to choose the variant."""
     return MoeDesc(num_tokens, hidden, intermediate, num_local_experts, expert_offset, top_k,
                    group_size, DT_FP16 if dtype == torch.float16 else DT_BF16,
                    ACT_SILU_GATED if gated else ACT_RELU2,
                    Q_PER_CHANNEL if per_channel else Q_GROUP_K, force_path, force_block_m,
-                   force_splitk)
+                   force_splitk, num_global_experts)
 
 
 def workspace_size(desc: MoeDesc) -> int:
@@ -133,13 +137,15 @@ def desc_for(wl, T: int, **force) -> MoeDesc:
     return make_desc(num_tokens=T, hidden=wl.hidden, intermediate=wl.inter,
                      num_local_experts=wl.num_experts, top_k=wl.top_k,
                      expert_offset=wl.expert_offset, dtype=wl.dtype, gated=wl.gated,
-                     per_channel=wl.per_channel, **force)
+                     per_channel=wl.per_channel, num_global_experts=wl.num_global_experts,
+                     **force)
 
 
 def moe_forward(x, w13_packed, w13_scales, w2_packed, w2_scales, topk_ids, topk_weights, *,
                 intermediate: int, num_local_experts: int, expert_offset: int = 0,
                 gated: bool = True, per_channel: bool = False, out=None, workspace=None,
                 force_path: int = 0, force_block_m: int = 0, force_splitk: int = 0,
+                num_global_experts: int = 0,
                 stream=None, stage_events=None) -> torch.Tensor:
     """Local W4A16 MoE forward: returns out [T, H] in x's dtype.
 
@@ -175,7 +181,8 @@ def moe_forward(x, w13_packed, w13_scales, w2_packed, w2_scales, topk_ids, topk_
     desc = make_desc(num_tokens=T, hidden=H, intermediate=I, num_local_experts=E,
                      top_k=topk_ids.shape[1], expert_offset=expert_offset, dtype=x.dtype,
                      gated=gated, per_channel=per_channel, force_path=force_path,
-                     force_block_m=force_block_m, force_splitk=force_splitk)
+                     force_block_m=force_block_m, force_splitk=force_splitk,
+                     num_global_experts=num_global_experts)
     nbytes = workspace_size(desc)
     if out is None:
         out = torch.empty(T, H, dtype=x.dtype, device=dev)
@@ -206,7 +213,8 @@ def forward_workload(wl, W, tok, **kw) -> torch.Tensor:
     return moe_forward(tok.x, W.w13_packed, W.w13_scales, W.w2_packed, W.w2_scales,
                        tok.topk_ids, tok.topk_weights, intermediate=wl.inter,
                        num_local_experts=wl.num_experts, expert_offset=wl.expert_offset,
-                       gated=wl.gated, per_channel=wl.per_channel, **kw)
+                       gated=wl.gated, per_channel=wl.per_channel,
+                       num_global_experts=wl.num_global_experts, **kw)
 
 
 ROUTE_CHUNKS_MAX = 32

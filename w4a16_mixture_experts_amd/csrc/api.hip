@@ -88,6 +88,9 @@ w4a16_status_t check_desc(const w4a16_moe_desc_t* d) {
     return fail(W4A16_ERR_INVALID_ARG, "desc.force_path: %d (0, 1 or 2)", d->force_path);
   if (d->force_splitk < 0 || d->force_splitk > 2)
     return fail(W4A16_ERR_INVALID_ARG, "desc.force_splitk: %d (0, 1 or 2)", d->force_splitk);
+  if (d->num_global_experts != 0 && d->num_global_experts < d->num_local_experts)
+    return fail(W4A16_ERR_INVALID_ARG, "desc.num_global_experts: %d < num_local_experts %d",
+                d->num_global_experts, d->num_local_experts);
   return W4A16_OK;
 }
 
@@ -182,8 +185,12 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
   // Measured on the Kimi shard: 549 -> 532 us at about 43 routes per expert
   // (2048 tokens), 373 -> 369 us at about 21 (1024 tokens); tiles of one
   // subtile (5 routes per expert at 256 tokens) keep the per-group form.
+  // Routes are counted as valid in proportion to the local share of the
+  // global experts (uniform routing).
   if (tile64 && pl.R > 0 && d->dtype == W4A16_DT_BF16 && d->qlayout == W4A16_Q_GROUP_K) {
-    const double R = static_cast<double>(pl.R);
+    const double share =
+        d->num_global_experts > E ? static_cast<double>(E) / d->num_global_experts : 1.0;
+    const double R = static_cast<double>(pl.R) * share;
     const double D = std::max(1.0, E * (1.0 - std::pow(1.0 - 1.0 / E, R)));
     pl.x16 = R / D >= 16.0;
   }
