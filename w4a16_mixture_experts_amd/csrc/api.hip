@@ -47,7 +47,8 @@ struct Plan {
   int splitk_nc = 0, splitk_passes = 0;  // column chunks, column passes per chunk
   int64_t R = 0, P = 0, MT = 0, items = 0;
   int N1 = 0;
-  bool x16 = false;  // streaming tile launches take the exact fp16 route
+  bool x16 = false;       // streaming tile launches take the exact fp16 route
+  bool x16_down = false;  // so does the resident down GEMM
   size_t off_counts = 0, off_offsets = 0, off_slot = 0, off_sorted = 0, off_tile = 0,
          off_act = 0, off_y = 0, off_part = 0, off_chunks = 0, off_redo = 0, total = 0;
 };
@@ -195,6 +196,10 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
     pl.x16 = R / D >= 16.0;
   }
   pl.down_resident = tile64 && I <= w4moe::kResidentK;
+  // The down GEMM takes the fp16 route under the same condition (measured on
+  // the Kimi shard's resident kernel: 167 -> 148 us at 2048 tokens; tiles of
+  // one subtile were slower on it).
+  pl.x16_down = pl.x16;
   if (pl.down_resident) {
     const int64_t steps = pl.n_tiles_down;
     const int64_t mt = std::max<int64_t>(pl.MT, 1);
@@ -222,7 +227,7 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
     pl.off_y = take(sizeof(uint16_t) * pl.P * H);
     if (pl.splitk_S > 0)
       pl.off_part = take(sizeof(float) * static_cast<size_t>(pl.splitk_S) * pl.R * pl.N1);
-    if (pl.x16) {
+    if (pl.x16 || pl.x16_down) {
       const int64_t mt = std::max<int64_t>(pl.MT, 1);
       pl.off_redo = take(sizeof(int32_t) *
                          std::max(w4moe::tile_launch_workgroups(pl.n_tiles_up, mt),
@@ -541,7 +546,7 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
   dn.out = ybuf;
   dn.ldo = H;
   dn.n_tiles = pl.n_tiles_down;
-  dn.redo = pl.x16 && !pl.down_resident ? reinterpret_cast<int32_t*>(ws + pl.off_redo) : nullptr;
+  dn.redo = pl.x16_down ? reinterpret_cast<int32_t*>(ws + pl.off_redo) : nullptr;
   st = hip_status(evs.mark(4), "stage event");
   if (st != W4A16_OK) return st;
   dn.col_steps = pl.col_steps;

@@ -356,17 +356,21 @@ __device__ __forceinline__ uint32_t dequant_pair_f16(uint32_t q2, f16x2 s16, f16
 // acc += A[rows 0..16*NMS) x deq(W block)^T for one 128-block with the exact
 // fp16 dequantization above (A staged as fp16; group layout, bf16 scales in
 // wb[s].s0 / s1 as for mma_block).  acc holds the plain sum (no factor 16).
-template <int NMS, int NSUB = kNsub>
+template <int NMS, bool UPFRONT = true, int NSUB = kNsub>
 __device__ __forceinline__ void mma_block_x(const uint16_t* sa, int stride,
                                             const WBlk<Q_GROUP_K> (&wb)[NSUB],
                                             f32x4 (&acc)[NMS][NSUB], int c, int g) {
   __builtin_amdgcn_sched_barrier(0);
+  auto frag = [&](int ms, int j) {
+    return *reinterpret_cast<const u32x4*>(sa + (16 * ms + c) * stride + 32 * j + 8 * g);
+  };
   u32x4 af[NMS][4];
+  if constexpr (UPFRONT) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int ms = 0; ms < NMS; ++ms)
-      af[ms][j] = *reinterpret_cast<const u32x4*>(sa + (16 * ms + c) * stride + 32 * j + 8 * g);
+      for (int ms = 0; ms < NMS; ++ms) af[ms][j] = frag(ms, j);
+  }
   uint32_t d[NSUB][4];
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
@@ -389,9 +393,12 @@ __device__ __forceinline__ void mma_block_x(const uint16_t* sa, int stride,
       bop[s][3] = dequant_pair_f16(q[3], s16, m24);
     }
 #pragma unroll
-    for (int ms = 0; ms < NMS; ++ms)
+    for (int ms = 0; ms < NMS; ++ms) {
+      const u32x4 a = UPFRONT ? af[ms][j] : frag(ms, j);
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s) acc[ms][s] = H16<DT_FP16>::mfma(af[ms][j], bop[s], acc[ms][s]);
+      for (int s = 0; s < NSUB; ++s) acc[ms][s] = H16<DT_FP16>::mfma(a, bop[s], acc[ms][s]);
+    }
+    if constexpr (!UPFRONT) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -1011,6 +1018,284 @@ down_resident_kernel(const GemmParams p) {
   }
 }
 
+// down_resident_run with the exact fp16 route (bf16 activations and scales,
+// group layout; the per-group form stays a function of its own so that its
+// register allocation is untouched): the activation rows are staged as
+// fp16; returns false, with nothing stored, if one of them has magnitude
+// 2^16 or more (or is not finite).
+template <int DT, int LAYOUT, int NMS, int NKB, bool X16 = true>
+__device__ __forceinline__ bool down_resident_run_x16(const GemmParams& p, const int row_base,
+                                                  const int e, const int chunk, uint16_t* s_ar,
+                                                  uint16_t* s_out) {
+  static_assert(!X16 || (DT == DT_BF16 && LAYOUT == Q_GROUP_K), "fp16 route");
+  constexpr int S = NKB * 128 + 8;   // row stride of the resident tile
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int c = lane & 15, g = lane >> 4, par = c & 1;
+
+  // stage the tile's activation rows once (padding rows and columns past K
+  // read zeros)
+  {
+    constexpr int kPerRow = NKB * 16;                       // 16-byte chunks per row
+    constexpr int kIters = kTileRows * kPerRow / kTileThreads;
+    static_assert(kTileRows * kPerRow % kTileThreads == 0, "staging covers the tile");
+    const auto ra = make_rsrc(p.a + static_cast<int64_t>(row_base) * p.lda,
+                              static_cast<uint32_t>(2 * kTileRows * p.lda));
+    u32x4 v[kIters];
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      const int idx = tid + i * kTileThreads;
+      const int row = idx / kPerRow, ch = idx % kPerRow;
+      const bool ok = p.sorted[row_base + row] >= 0 && 8 * ch < p.K;
+      v[i] = bload16(ra, 2u * static_cast<uint32_t>(row * p.lda + 8 * ch), ok);
+    }
+    [[maybe_unused]] bool big = false;
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      const int idx = tid + i * kTileThreads;
+      const int row = idx / kPerRow, ch = idx % kPerRow;
+      if constexpr (X16) {
+        // bf16 exponent field 127 + 16 or more (Inf and NaN included)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          big |= (v[i][k] & 0x7FFFu) >= 0x4780u || (v[i][k] & 0x7FFF0000u) >= 0x47800000u;
+        *reinterpret_cast<u32x4*>(s_ar + row * S + 8 * ch) = bf16x8_to_f16x8(v[i]);
+      } else {
+        *reinterpret_cast<u32x4*>(s_ar + row * S + 8 * ch) = v[i];
+      }
+    }
+    if constexpr (X16) {
+      if (__syncthreads_or(big)) return false;
+    } else {
+      __syncthreads();
+    }
+  }
+
+  const int step_begin = chunk * p.col_steps;
+  const int step_end = min(step_begin + p.col_steps, (p.n_cols + kTileColsPlain - 1) / kTileColsPlain);
+
+  const WExpert wx = make_wexpert(p, e);
+  const uint32_t vmask = valid_rows<NMS>(p, row_base, g);
+  // wave w's columns in step st: st * 256 + 32 w + 16 k + c (k = subtile)
+  auto step_src = [&](int st, int (&col)[kNsub], bool (&on)[kNsub]) {
+    const int n0 = st * kTileColsPlain + w * 32;
+#pragma unroll
+    for (int k = 0; k < kNsub; ++k) {
+      col[k] = n0 + 16 * k + c;
+      on[k] = st < step_end && n0 + 16 * k < p.n_cols;
+    }
+    return make_wsrc<LAYOUT>(p.K, col, on);
+  };
+  // two register sets: the next block's weights are requested while the
+  // current block is computed
+  auto load_blk = [&](int st, int kb, WBlk<LAYOUT> (&wb)[kNsub]) {
+    int col[kNsub];
+    bool on[kNsub];
+    const WSrc<> ws = step_src(st, col, on);
+    if constexpr (NKB == 1) load_wblk<LAYOUT, kNsub, SC_SINGLE>(wx, ws, 128 * kb, p.K, g, wb);
+    else if (kb == 0) load_wblk<LAYOUT, kNsub, SC_PAIR_FIRST>(wx, ws, 0, p.K, g, wb);
+    else load_wblk<LAYOUT, kNsub, SC_PAIR_SECOND>(wx, ws, 128, p.K, g, wb);
+  };
+  f32x4 acc[NMS][kNsub];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int ms = 0; ms < NMS; ++ms)
+#pragma unroll
+      for (int k = 0; k < kNsub; ++k) acc[ms][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  // rows of the tile holding a route (bit r: tile row r)
+  const uint64_t rows_valid = __ballot(p.sorted[row_base + lane] >= 0);
+  const bool vec_out = (p.n_cols & 7) == 0;  // a 16-byte chunk is all in or all out
+  const auto ro = make_rsrc(p.out + static_cast<int64_t>(row_base) * p.ldo,
+                            static_cast<uint32_t>(2 * kTileRows * p.ldo));
+  auto mma = [&](const uint16_t* sa, const WBlk<LAYOUT> (&wb)[kNsub]) {
+    if constexpr (X16) mma_block_x<NMS, false>(sa, S, wb, acc, c, g);
+    else mma_block<DT, LAYOUT, NMS, false>(sa, S, wb, acc, c, g, par);
+  };
+  auto store_step = [&](int st) {
+    int col[kNsub];
+    bool on[kNsub];
+    step_src(st, col, on);
+    if constexpr (X16) {
+      // the stores apply the per-group form's factor 16 (exact)
+#pragma unroll
+      for (int ms = 0; ms < NMS; ++ms)
+#pragma unroll
+        for (int k = 0; k < kNsub; ++k) acc[ms][k] *= 0.0625f;
+    }
+    if (!vec_out) {
+      store_outputs<DT, MODE_DOWN, NMS>(p, row_base, acc, col, on, g, vmask);
+      return;
+    }
+    // lane (c, g) holds rows 16 ms + 4 g + i of columns 16 s + c
+#pragma unroll
+    for (int ms = 0; ms < NMS; ++ms)
+#pragma unroll
+      for (int s = 0; s < kNsub; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s_out[(16 * ms + 4 * g + i) * kOutStride + 16 * s + c] =
+              H16<DT>::from_f32(16.0f * acc[ms][s][i]);
+    // lane l: row 16 ms + l / 4, columns 8 (l % 4) .. + 8 of the wave's 32
+    const int n0 = st * kTileColsPlain + w * 32 + 8 * (lane & 3);
+    const bool col_ok = st < step_end && n0 < p.n_cols;
+#pragma unroll
+    for (int ms = 0; ms < NMS; ++ms) {
+      const int r = 16 * ms + (lane >> 2);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(s_out + r * kOutStride + 8 * (lane & 3));
+      const bool ok = col_ok && ((rows_valid >> r) & 1u);
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), ro,
+          ok ? 2u * static_cast<uint32_t>(r * p.ldo + n0) : kOob, 0, 0);
+    }
+  };
+
+  static_assert(NKB == 1 || NKB == 2, "one or two 128-blocks per step");
+  // tiles of one or two subtiles hold few accumulators: their weights stream
+  // through a ring of four blocks, two column steps ahead (the register
+  // count of the kernel is set by the larger tiles)
+  constexpr bool kDeep = NKB == 2 && NMS <= 2;
+  if constexpr (kDeep) {
+    WBlk<LAYOUT> w[4][kNsub];
+    load_blk(step_begin, 0, w[0]);
+    load_blk(step_begin, 1, w[1]);
+    load_blk(step_begin + 1, 0, w[2]);
+    load_blk(step_begin + 1, 1, w[3]);
+    for (int st = step_begin; st < step_end; st += 2) {
+      zero_acc();
+      pass_scales<LAYOUT, kNsub>(w[0], w[1]);
+      mma(s_ar, w[0]);
+      mma(s_ar + 128, w[1]);
+      store_step(st);
+      load_blk(st + 2, 0, w[0]);
+      load_blk(st + 2, 1, w[1]);
+      if (st + 1 < step_end) {
+        zero_acc();
+        pass_scales<LAYOUT, kNsub>(w[2], w[3]);
+        mma(s_ar, w[2]);
+        mma(s_ar + 128, w[3]);
+        store_step(st + 1);
+      }
+      load_blk(st + 3, 0, w[2]);
+      load_blk(st + 3, 1, w[3]);
+    }
+    return true;
+  }
+  WBlk<LAYOUT> w0[kNsub], w1[kNsub];
+  load_blk(step_begin, 0, w0);
+  if constexpr (NKB == 2) {
+    for (int st = step_begin; st < step_end; ++st) {
+      load_blk(st, 1, w1);
+      zero_acc();
+      mma(s_ar, w0);
+      pass_scales<LAYOUT, kNsub>(w0, w1);
+      load_blk(st + 1, 0, w0);
+      mma(s_ar + 128, w1);
+      store_step(st);
+    }
+  } else {
+    for (int st = step_begin; st < step_end; st += 2) {
+      load_blk(st + 1, 0, w1);
+      zero_acc();
+      mma(s_ar, w0);
+      store_step(st);
+      load_blk(st + 2, 0, w0);
+      if (st + 1 < step_end) {
+        zero_acc();
+        mma(s_ar, w1);
+        store_step(st + 1);
+      }
+    }
+  }
+  return true;
+}
+
+// The work of resident-kernel workgroup L on the fp16 route (false: rerun).
+template <int DT, int LAYOUT, int NKB>
+__device__ __forceinline__ bool down_work_x16(const GemmParams& p, const int L, uint16_t* s_ar,
+                                          uint16_t* s_out) {
+  // same XCD-aware order as the streaming kernel (n_tiles = column chunks)
+  const int q = L / kXcds;
+  const int mt = kXcds * (q / p.n_tiles) + L % kXcds;
+  const int chunk = q % p.n_tiles;
+  const int row_base = mt * kTileRows;
+  // every index the workgroup needs comes in one batch of loads before the
+  // first decision (see tile_work)
+  const int rb = min(mt, p.tiles - 1) * kTileRows;
+  const int total = p.offsets[p.E];
+  const int e = p.tile_expert[rb / kTileRows];
+  int first[kTileMs];
+#pragma unroll
+  for (int ms = 0; ms < kTileMs; ++ms) first[ms] = p.sorted[rb + 16 * ms];
+  asm volatile("" : : "s"(total), "s"(e), "s"(first[0]), "s"(first[1]), "s"(first[2]), "s"(first[3]));
+  if (row_base >= total) return true;
+  int nms = 0;
+#pragma unroll
+  for (int ms = 0; ms < kTileMs; ++ms) nms += first[ms] >= 0 ? 1 : 0;
+  switch (nms) {
+    case 1: return down_resident_run_x16<DT, LAYOUT, 1, NKB>(p, row_base, e, chunk, s_ar, s_out);
+    case 2: return down_resident_run_x16<DT, LAYOUT, 2, NKB>(p, row_base, e, chunk, s_ar, s_out);
+    case 3: return down_resident_run_x16<DT, LAYOUT, 3, NKB>(p, row_base, e, chunk, s_ar, s_out);
+    default: return down_resident_run_x16<DT, LAYOUT, 4, NKB>(p, row_base, e, chunk, s_ar, s_out);
+  }
+}
+
+// The work of resident-kernel workgroup L on the per-group form (for the
+// rerun of flagged workgroups).
+template <int DT, int LAYOUT, int NKB>
+__device__ __forceinline__ void down_work_pg(const GemmParams& p, const int L, uint16_t* s_ar,
+                                             uint16_t* s_out) {
+  const int q = L / kXcds;
+  const int mt = kXcds * (q / p.n_tiles) + L % kXcds;
+  const int chunk = q % p.n_tiles;
+  const int row_base = mt * kTileRows;
+  if (row_base >= p.offsets[p.E]) return;
+  int nms = 0;
+#pragma unroll
+  for (int ms = 0; ms < kTileMs; ++ms) nms += p.sorted[row_base + 16 * ms] >= 0 ? 1 : 0;
+  const int e = p.tile_expert[mt];
+  switch (nms) {
+    case 1: down_resident_run<DT, LAYOUT, 1, NKB>(p, row_base, e, chunk, s_ar, s_out); break;
+    case 2: down_resident_run<DT, LAYOUT, 2, NKB>(p, row_base, e, chunk, s_ar, s_out); break;
+    case 3: down_resident_run<DT, LAYOUT, 3, NKB>(p, row_base, e, chunk, s_ar, s_out); break;
+    default: down_resident_run<DT, LAYOUT, 4, NKB>(p, row_base, e, chunk, s_ar, s_out); break;
+  }
+}
+
+// The fp16-route resident kernel: every workgroup records whether it must be
+// rerun (the flag array needs no clearing).
+template <int DT, int LAYOUT, int NKB>
+__global__ void __launch_bounds__(kTileThreads, 4)
+down_resident_x16_kernel(const GemmParams p) {
+  __shared__ uint16_t s_ar[kTileRows * (NKB * 128 + 8)];
+  __shared__ __align__(16) uint16_t s_out[kTileWaves][kTileRows * kOutStride];
+  const bool done = down_work_x16<DT, LAYOUT, NKB>(p, static_cast<int>(blockIdx.x), s_ar,
+                                                  s_out[threadIdx.x >> 6]);
+  if (threadIdx.x == 0) p.redo[blockIdx.x] = done ? 0 : 1;
+}
+
+// Reruns, with the per-group form, the workgroups of a fp16-route resident
+// launch of n_wg workgroups that found an activation outside fp16's range
+// (flag scan as in tile_redo_kernel).
+template <int DT, int LAYOUT, int NKB>
+__global__ void __launch_bounds__(kTileThreads)
+down_redo_kernel(const GemmParams p, const int n_wg) {
+  __shared__ uint16_t s_ar[kTileRows * (NKB * 128 + 8)];
+  __shared__ __align__(16) uint16_t s_out[kTileWaves][kTileRows * kOutStride];
+  const int G = static_cast<int>(gridDim.x);
+  for (int base = static_cast<int>(blockIdx.x); base < n_wg; base += G * kTileThreads) {
+    const int L = base + G * static_cast<int>(threadIdx.x);
+    const bool f = L < n_wg && p.redo[L] != 0;
+    if (!__syncthreads_or(f)) continue;
+    for (int i = 0; i < kTileThreads; ++i) {
+      const int Li = base + G * i;
+      if (Li >= n_wg) break;
+      if (p.redo[Li] == 0) continue;  // uniform
+      down_work_pg<DT, LAYOUT, NKB>(p, Li, s_ar, s_out[threadIdx.x >> 6]);
+      __syncthreads();  // LDS reuse by the next workgroup's tile
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Split-K gate/up GEMM for tiles of few rows ([P1] Modification: small-batch
 // split-K).  Workgroup (tile, K chunk): the tile's x rows over the chunk stay
@@ -1343,13 +1628,30 @@ static hipError_t launch_tile_mode(const GemmParams& p, int mode, dim3 grid, hip
   }
 }
 
+template <int DT, int LAYOUT, int NKB>
+static hipError_t launch_resident_k(const GemmParams& p, dim3 grid, hipStream_t st) {
+  if constexpr (DT == DT_BF16 && LAYOUT == Q_GROUP_K) {
+    if (p.redo != nullptr) {
+      // fp16 route, then the rerun of flagged workgroups
+      hipLaunchKernelGGL((down_resident_x16_kernel<DT, LAYOUT, NKB>), grid, dim3(kTileThreads), 0,
+                         st, p);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      const int n_wg = static_cast<int>(grid.x);
+      const dim3 rgrid(static_cast<unsigned>(std::min(n_wg, kTileRedoWorkgroups)));
+      hipLaunchKernelGGL((down_redo_kernel<DT, LAYOUT, NKB>), rgrid, dim3(kTileThreads), 0, st, p,
+                         n_wg);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((down_resident_kernel<DT, LAYOUT, NKB>), grid, dim3(kTileThreads), 0, st, p);
+  return hipGetLastError();
+}
+
 template <int DT, int LAYOUT>
 static hipError_t launch_resident_dl(const GemmParams& p, dim3 grid, hipStream_t st) {
-  if (p.K <= 128)
-    hipLaunchKernelGGL((down_resident_kernel<DT, LAYOUT, 1>), grid, dim3(kTileThreads), 0, st, p);
-  else
-    hipLaunchKernelGGL((down_resident_kernel<DT, LAYOUT, 2>), grid, dim3(kTileThreads), 0, st, p);
-  return hipGetLastError();
+  return p.K <= 128 ? launch_resident_k<DT, LAYOUT, 1>(p, grid, st)
+                    : launch_resident_k<DT, LAYOUT, 2>(p, grid, st);
 }
 
 hipError_t launch_down_resident(const GemmParams& p, int dtype, int layout, int max_tiles,
