@@ -115,6 +115,18 @@ typedef struct {
   int64_t max_positions;      /* capacity of the padded route list               */
   int64_t max_tiles;          /* capacity of the expert tile list                */
   size_t workspace_bytes;     /* bytes w4a16_moe_forward needs                   */
+  int32_t fp16_route;         /* bit 0: the streaming gate/up tiles take the
+                                 exact fp16 route (bf16 activations, bf16 group
+                                 scales, enough routes per expert); bit 1: so
+                                 does the down GEMM                              */
+  int32_t rerun_flags_up;     /* int32 flags the gate/up fp16-route launch
+                                 writes (one per workgroup, 1 = its tile left
+                                 fp16's range and was rerun); 0 if none          */
+  int32_t rerun_flags_down;   /* likewise for the down GEMM                      */
+  size_t rerun_flags_offset;  /* workspace byte offset of the flag array both
+                                 launches write from index 0; after a forward it
+                                 holds the down launch's flags (0 if neither
+                                 launch exists)                                  */
 } w4a16_moe_plan_t;
 
 /* Bytes of device workspace w4a16_moe_forward needs for this descriptor

@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from w4a16_mixture_experts_amd import binding as B
 
@@ -149,6 +150,35 @@ def test_plans_by_route_count():
     p3 = B.get_plan(d)
     assert (p3.path, p3.block_m) == (1, 32)
     assert p3.workspace_bytes == B.workspace_size(d)
+
+
+def test_fp16_route_choice():
+    """The exact fp16 route is taken by the grouped path's streaming launches
+    when the expected valid routes per touched expert, R / (E (1 - (1 - 1/E)^R))
+    with R = T K scaled by the local share, reach 16; only for bf16
+    activations with group scales.  Its rerun flags sit in the workspace."""
+    kimi = dict(hidden=7168, intermediate=256, num_local_experts=384, top_k=8)
+    for T, want in ((1, 0), (32, 0), (256, 0), (512, 0), (1024, 3), (2048, 3)):
+        # 512 tokens: 10.7 routes per touched expert; 1024: 21.3
+        pl = B.get_plan(B.make_desc(num_tokens=T, **kimi))
+        assert pl.fp16_route == want, (T, pl.fp16_route)
+        if want:
+            assert pl.rerun_flags_up > 0 and pl.rerun_flags_down > 0
+            assert 0 < pl.rerun_flags_offset
+            assert (pl.rerun_flags_offset + 4 * max(pl.rerun_flags_up, pl.rerun_flags_down)
+                    <= pl.workspace_bytes)
+        else:
+            assert (pl.rerun_flags_up, pl.rerun_flags_down, pl.rerun_flags_offset) == (0, 0, 0)
+    assert B.get_plan(B.make_desc(num_tokens=2048, dtype=torch.float16, **kimi)).fp16_route == 0
+    assert B.get_plan(B.make_desc(num_tokens=2048, per_channel=True, **kimi)).fp16_route == 0
+    # a local share of 32 of 256 experts: 512 tokens give 4096 routes, 512
+    # of them valid in expectation, 16 per local expert
+    share = dict(hidden=7168, intermediate=2048, num_local_experts=32, top_k=8,
+                 num_global_experts=256)
+    assert B.get_plan(B.make_desc(num_tokens=256, **share)).fp16_route == 0
+    assert B.get_plan(B.make_desc(num_tokens=512, **share)).fp16_route == 3
+    # counted as if every route were local, 256 tokens would already qualify
+    assert B.get_plan(B.make_desc(num_tokens=256, **dict(share, num_global_experts=0))).fp16_route == 3
 
 
 def test_buffer_offset_limits():

@@ -5,6 +5,8 @@ Integer work (nibble unpacking, route tables) must match bit for bit; the
 FP32 oracle.  Sizes are chosen so the oracle finishes in seconds while still
 spanning several tiles, split-K partitions and ragged tails.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -202,6 +204,45 @@ def test_activations_beyond_fp16_range():
     rest = [r for r in range(256) if r not in big_rows]
     assert_close(out[rest], ref[rest], "tiny T=256, rows without large activations")
     for r in big_rows:
+        nrmse, _ = errors(out[r], ref[r])
+        assert nrmse <= 5e-3, (r, nrmse)
+
+
+@pytest.mark.parametrize("inter", [384, 256], ids=["streaming-down", "resident-down"])
+def test_fp16_route_rerun_flags(inter):
+    """The down GEMM's fp16-route launch (the streaming tile kernel for
+    I = 384, the resident one for I = 256) writes one flag per workgroup: all
+    zero for ordinary activations, and set for the tiles whose staged
+    activations reach 2^16 (large x rows make large silu(gate) * up), which
+    the rerun launch then recomputes per group.  The workspace starts filled
+    with 0xFF, so every flag having been written is checked too."""
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], name=f"tiny_i{inter}", inter=inter)
+    Wc = synth.make_weights(wl, device="cpu")
+    Wg = Wc.to("cuda")
+    tc = tokens(wl, 256)
+    d = binding.desc_for(wl, 256, force_path=1)
+    pl = binding.get_plan(d)
+    assert pl.fp16_route == 3 and pl.rerun_flags_down > 0
+    ws = torch.empty(binding.workspace_size(d), dtype=torch.uint8, device="cuda")
+    off, n = pl.rerun_flags_offset, pl.rerun_flags_down
+
+    def run(t):
+        ws.fill_(0xFF)
+        out = forward(wl, Wg, t.to("cuda"), force_path=1, workspace=ws).cpu()
+        return out, ws[off:off + 4 * n].view(torch.int32).cpu()
+
+    out, flags = run(tc)
+    assert_close(out, oracle_out(wl, Wc, tc), "tiny T=256, flags run")
+    assert int(flags.abs().sum()) == 0, flags
+    x = tc.x.clone()
+    x[3, 7] = 3.0e5
+    x[200, 255] = 1.0e6
+    t2 = synth.Tokens(x, tc.topk_ids, tc.topk_weights)
+    out, flags = run(t2)
+    assert bool(((flags == 0) | (flags == 1)).all()), flags
+    assert int(flags.sum()) >= 1
+    ref = oracle_out(wl, Wc, t2)
+    for r in range(256):
         nrmse, _ = errors(out[r], ref[r])
         assert nrmse <= 5e-3, (r, nrmse)
 

@@ -34,7 +34,9 @@ class MoePlan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("block_m", ctypes.c_int32),
                 ("k_slice", ctypes.c_int32), ("splitk_chunks", ctypes.c_int32),
                 ("max_positions", ctypes.c_int64), ("max_tiles", ctypes.c_int64),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("fp16_route", ctypes.c_int32),
+                ("rerun_flags_up", ctypes.c_int32), ("rerun_flags_down", ctypes.c_int32),
+                ("rerun_flags_offset", ctypes.c_size_t)]
 
 
 class W4A16Error(RuntimeError):

@@ -318,6 +318,14 @@ w4a16_status_t w4a16_moe_get_plan(const w4a16_moe_desc_t* desc, w4a16_moe_plan_t
   plan->max_positions = pl.P;
   plan->max_tiles = pl.MT;
   plan->workspace_bytes = pl.total;
+  const bool up16 = pl.path == 1 && pl.x16 && pl.splitk_S == 0;
+  const bool dn16 = pl.path == 1 && pl.x16_down;
+  const int64_t mt = std::max<int64_t>(pl.MT, 1);
+  plan->fp16_route = (up16 ? 1 : 0) | (dn16 ? 2 : 0);
+  plan->rerun_flags_up = up16 ? static_cast<int32_t>(w4moe::tile_launch_workgroups(pl.n_tiles_up, mt)) : 0;
+  plan->rerun_flags_down =
+      dn16 ? static_cast<int32_t>(w4moe::tile_launch_workgroups(pl.n_tiles_down, mt)) : 0;
+  plan->rerun_flags_offset = (up16 || dn16) ? pl.off_redo : 0;
   return W4A16_OK;
 }
 
