@@ -247,6 +247,26 @@ def test_fp16_route_rerun_flags(inter):
         assert nrmse <= 5e-3, (r, nrmse)
 
 
+@pytest.mark.parametrize("T,force", [(16, f) for f in VARIANTS] + [(256, dict(force_path=1))],
+                         ids=lambda v: v if isinstance(v, int) else
+                         "-".join(f"{k}{x}" for k, x in v.items()))
+def test_local_share_at_nonzero_offset(T, force):
+    """Experts 8..15 of 24 are local (an expert-parallel share that is not
+    the first): ids below 8 or from 16 on are other ranks' routes and add
+    nothing.  256 tokens take the exact fp16 route (about 21 valid routes per
+    local expert)."""
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], name="tiny_off8", num_global_experts=24,
+                             expert_offset=8)
+    Wc = synth.make_weights(wl, device="cpu")
+    tc = tokens(wl, T)
+    ids = tc.topk_ids
+    assert bool(((ids < 8) | (ids >= 16)).any()) and bool(((ids >= 8) & (ids < 16)).any())
+    if T == 256:
+        assert binding.get_plan(binding.desc_for(wl, T, **force)).fp16_route == 3
+    out = forward(wl, Wc.to("cuda"), tc.to("cuda"), **force)
+    assert_close(out, oracle_out(wl, Wc, tc), f"offset 8 of 24, T={T} {force}")
+
+
 def test_poisoned_workspace_and_output():
     """Workspace and output filled with NaN patterns before the call: nothing
     uninitialised may leak (empty split-K partitions, padding rows)."""
