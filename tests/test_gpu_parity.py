@@ -247,6 +247,40 @@ def test_fp16_route_rerun_flags(inter):
         assert nrmse <= 5e-3, (r, nrmse)
 
 
+@pytest.mark.parametrize("inter", [384, 256], ids=["streaming-down", "resident-down"])
+@pytest.mark.parametrize("which,factor", [("w13", 2.0 ** -12), ("w2", 2.0 ** -12),
+                                          ("w13", 2.0 ** 19), ("w2", 2.0 ** 19)],
+                         ids=["w13-tiny", "w2-tiny", "w13-huge", "w2-huge"])
+def test_fp16_route_scales_outside_exact_range(inter, which, factor):
+    """The fp16 route forms q * s exactly only for 2^-17 <= |s| <= 2720 (or
+    s = 0).  Scales multiplied by 2^-12 (all below 2^-17) or by 2^19 (1650
+    to 7600, across the upper bound) must send the affected workgroups to the
+    per-group rerun: every output row stays within the tolerance of the
+    oracle, relative to its own size.  For w13 the tokens are divided by the
+    same power of two, so that the activations between the two GEMMs keep
+    their ordinary size (tiny activations are the route's other limit)."""
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], name=f"tiny_i{inter}", inter=inter)
+    Wc = synth.make_weights(wl, device="cpu")
+    sc = getattr(Wc, f"{which}_scales")
+    setattr(Wc, f"{which}_scales", (sc.float() * factor).to(sc.dtype))  # exact: a power of two
+    tc = tokens(wl, 256)
+    if which == "w13":
+        tc = synth.Tokens((tc.x.float() / factor).to(tc.x.dtype), tc.topk_ids, tc.topk_weights)
+    d = binding.desc_for(wl, 256, force_path=1)
+    pl = binding.get_plan(d)
+    assert pl.fp16_route == 3
+    ws = torch.full((binding.workspace_size(d),), 0xFF, dtype=torch.uint8, device="cuda")
+    out = forward(wl, Wc.to("cuda"), tc.to("cuda"), force_path=1, workspace=ws).cpu()
+    ref = oracle_out(wl, Wc, tc)
+    for r in range(256):
+        nrmse, _ = errors(out[r], ref[r])
+        assert nrmse <= 5e-3, (r, nrmse)
+    if which == "w2":
+        off, n = pl.rerun_flags_offset, pl.rerun_flags_down
+        flags = ws[off:off + 4 * n].view(torch.int32).cpu()
+        assert int(flags.sum()) >= 1
+
+
 @pytest.mark.parametrize("T,force", [(16, f) for f in VARIANTS] + [(256, dict(force_path=1))],
                          ids=lambda v: v if isinstance(v, int) else
                          "-".join(f"{k}{x}" for k, x in v.items()))

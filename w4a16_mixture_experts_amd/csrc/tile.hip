@@ -325,9 +325,11 @@ __device__ __forceinline__ void mma_block2(const uint16_t* sa, int stride,
 //   rerun with the per-group form (tile_redo_kernel), which also gives
 //   infinite or NaN activations their plain meaning.  q * s, with q in [-8, 7] and a bf16
 //   scale s, has at most 3 + 8 significant bits, so it is exact in fp16 as
-//   well.  It is formed per value pair as one fused multiply-add
-//   (24 + q)/16 * 16s - 24s whose exact result is representable (16s and 24s
-//   are exact in fp16 for scales below 2730).  The MFMA then accumulates
+//   well when 2^-17 <= |s| <= 2720 (or s = 0): its lowest bit is then at
+//   least 2^-24, and 16s and 24s are exact fp16 values.  It is formed per
+//   value pair as one fused multiply-add (24 + q)/16 * 16s - 24s whose exact
+//   result is representable.  A scale outside that range (or an infinity or
+//   NaN) marks the tile for the same rerun.  The MFMA then accumulates
 //   x * (q s) over every group in FP32: no per-group scaling and no
 //   correction term.
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
@@ -353,13 +355,21 @@ __device__ __forceinline__ uint32_t dequant_pair_f16(uint32_t q2, f16x2 s16, f16
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(qv, s16, m24));
 }
 
+// bf16 magnitudes (sign cleared) of the group scales the fp16 route takes:
+// 2^-17 (0x3700) to 2720 (0x452A); a zero scale, exact as well, is sent to
+// the rerun too (one compare per scale instead of two)
+constexpr uint32_t kX16ScaleLo = 0x3700u;
+constexpr uint32_t kX16ScaleEnd = 0x452Bu;
+
 // acc += A[rows 0..16*NMS) x deq(W block)^T for one 128-block with the exact
 // fp16 dequantization above (A staged as fp16; group layout, bf16 scales in
 // wb[s].s0 / s1 as for mma_block).  acc holds the plain sum (no factor 16).
+// sbad is set if a group scale of the block lies outside the exact range
+// (lane g checks group g of its row, so the 64 lanes cover every scale).
 template <int NMS, bool UPFRONT = true, int NSUB = kNsub>
 __device__ __forceinline__ void mma_block_x(const uint16_t* sa, int stride,
                                             const WBlk<Q_GROUP_K> (&wb)[NSUB],
-                                            f32x4 (&acc)[NMS][NSUB], int c, int g) {
+                                            f32x4 (&acc)[NMS][NSUB], int c, int g, bool& sbad) {
   __builtin_amdgcn_sched_barrier(0);
   auto frag = [&](int ms, int j) {
     return *reinterpret_cast<const u32x4*>(sa + (16 * ms + c) * stride + 32 * j + 8 * g);
@@ -399,6 +409,14 @@ __device__ __forceinline__ void mma_block_x(const uint16_t* sa, int stride,
       for (int s = 0; s < NSUB; ++s) acc[ms][s] = H16<DT_FP16>::mfma(a, bop[s], acc[ms][s]);
     }
     if constexpr (!UPFRONT) __builtin_amdgcn_sched_barrier(0);
+  }
+  // range of the block's group scales, checked after its products are
+  // issued (the scales have arrived by then)
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    const uint32_t dw = (g & 2) ? wb[s].s1 : wb[s].s0;
+    const uint32_t mag = __builtin_amdgcn_ubfe(dw, 16 * (g & 1), 15);
+    sbad |= mag - kX16ScaleLo >= kX16ScaleEnd - kX16ScaleLo;  // 0 included: rerun, still exact
   }
 }
 
@@ -632,6 +650,7 @@ __device__ __forceinline__ bool tile_run(const GemmParams& p, const int row_base
   constexpr int SC_SECOND = SCL ? SC_NONE : SC_PAIR_SECOND;
   WBlk<LAYOUT> wr[2][kNsub];
   u32x4 an[2][kChunks];
+  bool sbad = false;  // X16: a group scale outside the route's exact range
   const int nblk = (p.K + 127) >> 7;
   const int nsteps = (nblk + 1) >> 1;
   auto step = [&](int s, int pb0) {  // pb0: first block of the scale phase
@@ -640,7 +659,7 @@ __device__ __forceinline__ bool tile_run(const GemmParams& p, const int row_base
     uint16_t* sy = s_lds + 2 * kStageElems * ((s & 1) ^ 1);
     load_wblk<LAYOUT, kNsub, SC_SECOND>(wx, ws, 128 * (b + 1), p.K, g, wr[1]);
     if constexpr (SCL) set_scales(b - pb0, wr[0]);
-    if constexpr (X16) mma_block_x<NMS>(sx, kAStride, wr[0], acc, c, g);
+    if constexpr (X16) mma_block_x<NMS>(sx, kAStride, wr[0], acc, c, g, sbad);
     else mma_block<DT, LAYOUT, NMS>(sx, kAStride, wr[0], acc, c, g, par);
     if constexpr (!SCL) pass_scales<LAYOUT, kNsub>(wr[0], wr[1]);
     store_a(sy, an[0]);
@@ -650,7 +669,7 @@ __device__ __forceinline__ bool tile_run(const GemmParams& p, const int row_base
     load_wblk<LAYOUT, kNsub, SC_FIRST>(wx, ws, 128 * (b + 2), p.K, g, wr[0]);
     if (b + 1 < nblk) {
       if constexpr (SCL) set_scales(b + 1 - pb0, wr[1]);
-      if constexpr (X16) mma_block_x<NMS>(sx + kStageElems, kAStride, wr[1], acc, c, g);
+      if constexpr (X16) mma_block_x<NMS>(sx + kStageElems, kAStride, wr[1], acc, c, g, sbad);
       else mma_block<DT, LAYOUT, NMS>(sx + kStageElems, kAStride, wr[1], acc, c, g, par);
     }
     __syncthreads();
@@ -716,7 +735,7 @@ __device__ __forceinline__ bool tile_run(const GemmParams& p, const int row_base
       for (int s2 = 0; s2 < kNsub; ++s2)
 #pragma unroll
         for (int i = 0; i < 4; ++i) bad |= !__builtin_isfinite(acc[ms][s2][i]);
-    if (__syncthreads_or(bad)) return false;
+    if (__syncthreads_or(bad || sbad)) return false;
     // the epilogue applies the per-group form's factor 16 (exact)
 #pragma unroll
     for (int ms = 0; ms < NMS; ++ms)
@@ -1107,8 +1126,9 @@ __device__ __forceinline__ bool down_resident_run_x16(const GemmParams& p, const
   const bool vec_out = (p.n_cols & 7) == 0;  // a 16-byte chunk is all in or all out
   const auto ro = make_rsrc(p.out + static_cast<int64_t>(row_base) * p.ldo,
                             static_cast<uint32_t>(2 * kTileRows * p.ldo));
+  bool sbad = false;  // X16: a group scale outside the route's exact range
   auto mma = [&](const uint16_t* sa, const WBlk<LAYOUT> (&wb)[kNsub]) {
-    if constexpr (X16) mma_block_x<NMS, false>(sa, S, wb, acc, c, g);
+    if constexpr (X16) mma_block_x<NMS, false>(sa, S, wb, acc, c, g, sbad);
     else mma_block<DT, LAYOUT, NMS, false>(sa, S, wb, acc, c, g, par);
   };
   auto store_step = [&](int st) {
@@ -1178,7 +1198,7 @@ __device__ __forceinline__ bool down_resident_run_x16(const GemmParams& p, const
       load_blk(st + 3, 0, w[2]);
       load_blk(st + 3, 1, w[3]);
     }
-    return true;
+    return !__syncthreads_or(sbad);  // stored outputs get rewritten by the rerun
   }
   WBlk<LAYOUT> w0[kNsub], w1[kNsub];
   load_blk(step_begin, 0, w0);
@@ -1206,7 +1226,7 @@ __device__ __forceinline__ bool down_resident_run_x16(const GemmParams& p, const
       }
     }
   }
-  return true;
+  return !__syncthreads_or(sbad);  // stored outputs get rewritten by the rerun
 }
 
 // The work of resident-kernel workgroup L on the fp16 route (false: rerun).
