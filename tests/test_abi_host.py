@@ -221,3 +221,28 @@ def test_small_batch_path_limits():
     assert "hidden" in ei.value.message
     d2.force_path = 0
     assert B.get_plan(d2).path == 1
+
+
+def test_fp16_route_exact_scale_range():
+    """The fp16 route forms q * s as (24 + q)/16 * 16s - 24s with one rounding
+    to fp16, exact when 16s, 24s and every q * s (q in [-8, 7]) are fp16
+    values.  Over every finite bf16 magnitude that holds exactly on
+    [2^-17, 2720] (bf16 bits 0x3700 to 0x452A), the range the kernels accept,
+    and fails just outside it."""
+    import numpy as np
+    bits = np.arange(1, 0x7F80, dtype=np.uint32)
+    s = (bits << 16).view(np.float32).astype(np.float64)
+
+    def rep(v):  # v exactly an fp16 value (finite)
+        with np.errstate(over="ignore"):
+            h = v.astype(np.float16)
+        return np.isfinite(h) & (h.astype(np.float64) == v)
+
+    ok = rep(16.0 * s) & rep(24.0 * s)
+    for q in range(-8, 8):
+        ok &= rep(q * s)
+    lo, end = 0x3700, 0x452B
+    inside = (bits >= lo) & (bits < end)
+    assert ok[inside].all()
+    assert not ok[bits == end].any() and not ok[bits == lo - 1].any()
+    assert not ok[bits >= end].any()
