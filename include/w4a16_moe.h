@@ -120,8 +120,10 @@ typedef struct {
                                  scales, enough routes per expert); bit 1: so
                                  does the down GEMM                              */
   int32_t rerun_flags_up;     /* int32 flags the gate/up fp16-route launch
-                                 writes (one per workgroup, 1 = its tile left
-                                 fp16's range and was rerun); 0 if none          */
+                                 writes (one per workgroup, 1 = its tile met an
+                                 activation of magnitude 2^16 or more, or a
+                                 group scale outside 2^-17..2720, and was rerun
+                                 per group); 0 if none                           */
   int32_t rerun_flags_down;   /* likewise for the down GEMM                      */
   size_t rerun_flags_offset;  /* workspace byte offset of the flag array both
                                  launches write from index 0; after a forward it
