@@ -103,6 +103,12 @@ typedef struct {
                                  of E of them); only the variant choice uses it
                                  (expected valid routes per local expert).
                                  0 = E; otherwise >= E                           */
+  int32_t no_fp16_route;      /* 0: the plan may take the exact fp16 route (bf16
+                                 activations and group scales, many routes per
+                                 expert); 1: never.  Set it for inputs whose
+                                 rows hold only activations below about 2^-14
+                                 in magnitude, which that route keeps with
+                                 fewer bits                                      */
 } w4a16_moe_desc_t;
 
 /* Variant the library runs for a descriptor (for tests and reports). */

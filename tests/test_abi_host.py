@@ -61,6 +61,7 @@ def good(**kw):
     ("force_path", 3, 1, "force_path"),
     ("force_splitk", 3, 1, "force_splitk"),
     ("num_global_experts", 7, 1, "num_global_experts"),
+    ("no_fp16_route", 2, 1, "no_fp16_route"),
 ])
 def test_descriptor_errors(field, value, status, needle):
     d = good()
@@ -170,6 +171,8 @@ def test_fp16_route_choice():
         else:
             assert (pl.rerun_flags_up, pl.rerun_flags_down, pl.rerun_flags_offset) == (0, 0, 0)
     assert B.get_plan(B.make_desc(num_tokens=2048, dtype=torch.float16, **kimi)).fp16_route == 0
+    off = B.get_plan(B.make_desc(num_tokens=2048, no_fp16_route=1, **kimi))
+    assert (off.fp16_route, off.rerun_flags_up, off.rerun_flags_down) == (0, 0, 0)
     assert B.get_plan(B.make_desc(num_tokens=2048, per_channel=True, **kimi)).fp16_route == 0
     # a local share of 32 of 256 experts: 512 tokens give 4096 routes, 512
     # of them valid in expectation, 16 per local expert

@@ -281,6 +281,26 @@ def test_fp16_route_scales_outside_exact_range(inter, which, factor):
         assert int(flags.sum()) >= 1
 
 
+def test_rows_of_tiny_activations_without_fp16_route():
+    """Rows whose activations all lie far below 2^-14 (x scaled by 2^-20):
+    with the fp16 route switched off in the descriptor every row, tiny or
+    not, stays within the tolerance of the oracle relative to its own size."""
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], name="tiny_i256", inter=256)
+    Wc = synth.make_weights(wl, device="cpu")
+    tc = tokens(wl, 256)
+    x = tc.x.clone()
+    tiny_rows = [5, 77, 200]
+    x[tiny_rows] = (x[tiny_rows].float() * 2.0 ** -20).to(x.dtype)
+    t2 = synth.Tokens(x, tc.topk_ids, tc.topk_weights)
+    assert binding.get_plan(binding.desc_for(wl, 256, force_path=1)).fp16_route == 3
+    assert binding.get_plan(binding.desc_for(wl, 256, force_path=1, no_fp16_route=1)).fp16_route == 0
+    out = forward(wl, Wc.to("cuda"), t2.to("cuda"), force_path=1, no_fp16_route=1).cpu()
+    ref = oracle_out(wl, Wc, t2)
+    for r in range(256):
+        nrmse, _ = errors(out[r], ref[r])
+        assert nrmse <= 5e-3, (r, nrmse)
+
+
 @pytest.mark.parametrize("T,force", [(16, f) for f in VARIANTS] + [(256, dict(force_path=1))],
                          ids=lambda v: v if isinstance(v, int) else
                          "-".join(f"{k}{x}" for k, x in v.items()))

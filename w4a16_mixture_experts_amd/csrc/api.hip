@@ -89,6 +89,8 @@ w4a16_status_t check_desc(const w4a16_moe_desc_t* d) {
     return fail(W4A16_ERR_INVALID_ARG, "desc.force_path: %d (0, 1 or 2)", d->force_path);
   if (d->force_splitk < 0 || d->force_splitk > 2)
     return fail(W4A16_ERR_INVALID_ARG, "desc.force_splitk: %d (0, 1 or 2)", d->force_splitk);
+  if (d->no_fp16_route != 0 && d->no_fp16_route != 1)
+    return fail(W4A16_ERR_INVALID_ARG, "desc.no_fp16_route: %d (0 or 1)", d->no_fp16_route);
   if (d->num_global_experts != 0 && d->num_global_experts < d->num_local_experts)
     return fail(W4A16_ERR_INVALID_ARG, "desc.num_global_experts: %d < num_local_experts %d",
                 d->num_global_experts, d->num_local_experts);
@@ -188,7 +190,8 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
   // subtile (5 routes per expert at 256 tokens) keep the per-group form.
   // Routes are counted as valid in proportion to the local share of the
   // global experts (uniform routing).
-  if (tile64 && pl.R > 0 && d->dtype == W4A16_DT_BF16 && d->qlayout == W4A16_Q_GROUP_K) {
+  if (tile64 && pl.R > 0 && d->dtype == W4A16_DT_BF16 && d->qlayout == W4A16_Q_GROUP_K &&
+      d->no_fp16_route == 0) {
     const double share =
         d->num_global_experts > E ? static_cast<double>(E) / d->num_global_experts : 1.0;
     const double R = static_cast<double>(pl.R) * share;
