@@ -106,6 +106,19 @@ w4a16_status_t check_desc(const w4a16_moe_desc_t* d) {
 //     gate/up GEMM per tile, the grouped down GEMM and the FP32 combine.
 //     block_m 64 (default): LDS-staged tiles that skip empty 16-row subtiles;
 //     16: the 8-wave split-reduction kernel; 32: register-fed tiles.
+// Expected routes per touched expert under uniform routing: R routes over E
+// experts touch E (1 - (1 - 1/E)^R) of them in expectation.  With a local
+// share (E of num_global_experts), routes are counted valid in proportion.
+double routes_per_touched_expert(const w4a16_moe_desc_t* d, int64_t routes, bool local_share) {
+  const double E = static_cast<double>(d->num_local_experts);
+  const double share = local_share && d->num_global_experts > d->num_local_experts
+                           ? E / d->num_global_experts
+                           : 1.0;
+  const double R = static_cast<double>(routes) * share;
+  const double D = std::max(1.0, E * (1.0 - std::pow(1.0 - 1.0 / E, R)));
+  return R / D;
+}
+
 Plan make_plan(const w4a16_moe_desc_t* d) {
   Plan pl;
   const int E = d->num_local_experts, H = d->hidden, I = d->intermediate, K = d->top_k;
@@ -149,14 +162,13 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
   const int cols_plain = tile64 ? w4moe::kTileColsPlain : w4moe::kWgColsPlain;
   pl.n_tiles_up = gated ? (I + cols_gated - 1) / cols_gated : (I + cols_plain - 1) / cols_plain;
   pl.n_tiles_down = (H + cols_plain - 1) / cols_plain;
-  // split-K gate/up when tiles are expected to hold few routes: the expected
-  // number of touched experts under uniform routing is E (1 - (1 - 1/E)^R)
+  // split-K gate/up when tiles are expected to hold few routes (every route
+  // counted, as when the crossover below was measured)
   if (tile64 && pl.R > 0) {
-    const double R = static_cast<double>(pl.R);
-    const double D = std::max(1.0, E * (1.0 - std::pow(1.0 - 1.0 / E, R)));
+    const double rpe_all = routes_per_touched_expert(d, pl.R, false);
     // measured crossover: split-K wins at ~1.4 routes per expert (Kimi shard,
     // 32 tokens), the streaming kernel at ~5 (256 tokens)
-    bool use = R / D <= 3.0;
+    bool use = rpe_all <= 3.0;
     if (d->force_splitk == 1) use = true;
     if (d->force_splitk == 2) use = false;
     if (use) {
@@ -192,11 +204,7 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
   // global experts (uniform routing).
   if (tile64 && pl.R > 0 && d->dtype == W4A16_DT_BF16 && d->qlayout == W4A16_Q_GROUP_K &&
       d->no_fp16_route == 0) {
-    const double share =
-        d->num_global_experts > E ? static_cast<double>(E) / d->num_global_experts : 1.0;
-    const double R = static_cast<double>(pl.R) * share;
-    const double D = std::max(1.0, E * (1.0 - std::pow(1.0 - 1.0 / E, R)));
-    pl.x16 = R / D >= 16.0;
+    pl.x16 = routes_per_touched_expert(d, pl.R, true) >= 16.0;
   }
   pl.down_resident = tile64 && I <= w4moe::kResidentK;
   // The down GEMM takes the fp16 route under the same condition (measured on
@@ -211,11 +219,7 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
     // Measured on the Kimi shard against a flat 2048: 1024 at 32 tokens
     // (down GEMM 55.4 -> 50.8 us; 512 was no better than 2048), 4096 at 2048
     // tokens (147.8 -> 141.2 us; 8192 was no better); 256 and 1024 tokens flat
-    const double share =
-        d->num_global_experts > E ? static_cast<double>(E) / d->num_global_experts : 1.0;
-    const double Rv = static_cast<double>(pl.R) * share;
-    const double Dv = std::max(1.0, E * (1.0 - std::pow(1.0 - 1.0 / E, Rv)));
-    const double rpe = Rv / Dv;  // expected valid routes per touched expert
+    const double rpe = routes_per_touched_expert(d, pl.R, true);
     const int64_t target = rpe < 4.0 ? 1024 : (rpe >= 32.0 ? 4096 : 2048);
     const int64_t chunks = std::min<int64_t>(steps, std::max<int64_t>(1, (target + mt - 1) / mt));
     pl.col_steps = static_cast<int>((steps + chunks - 1) / chunks);
