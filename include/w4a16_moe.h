@@ -93,22 +93,31 @@ typedef struct {
   int32_t force_path;         /* 0, 1 = grouped (route preparation, expert tiles,
                                  down GEMM, combine kernel), 2 = small batch (no
                                  route preparation; needs T*K <= 64)             */
-  int32_t force_block_m;      /* grouped path: 0 (= 64) or 16/32/64 rows per
-                                 expert tile                                     */
+  int32_t force_block_m;      /* grouped path: 0 or 64 (rows per expert tile;
+                                 tiles are always 64 rows, empty 16-row subtiles
+                                 skipped)                                        */
   int32_t force_splitk;       /* grouped path with 64-row tiles: 0 = choose from
                                  the expected routes per expert, 1 = split-K
                                  gate/up (partials + activation kernel), 2 = the
                                  streaming gate/up kernel                        */
   int32_t num_global_experts; /* experts the routes are drawn over (a local share
                                  of E of them); only the variant choice uses it
-                                 (expected valid routes per local expert).
+                                 (expected valid routes per local expert): ids
+                                 are not checked against it, any id outside
+                                 the local range is an invalid route.
                                  0 = E; otherwise >= E                           */
-  int32_t no_fp16_route;      /* 0: the plan may take the exact fp16 route (bf16
-                                 activations and group scales, many routes per
-                                 expert); 1: never.  Set it for inputs whose
-                                 rows hold only activations below about 2^-14
-                                 in magnitude, which that route keeps with
-                                 fewer bits                                      */
+  int32_t fp16_route;         /* 0 (default): every product is formed with
+                                 exact per-group scaling, for every finite
+                                 input.  1: opt in to the fp16 route (bf16
+                                 activations, bf16 group scales, 16 or more
+                                 expected routes per expert): activations are
+                                 staged as fp16, so an activation below 2^-14
+                                 in magnitude is rounded to a multiple of
+                                 2^-24 (an absolute error of at most 2^-25);
+                                 a row made only of such values keeps fewer
+                                 bits.  Activations of 2^16 or more and scales
+                                 outside 2^-17..2720 are detected and those
+                                 tiles recomputed per group                      */
 } w4a16_moe_desc_t;
 
 /* Variant the library runs for a descriptor (for tests and reports). */
@@ -131,14 +140,17 @@ typedef struct {
                                  group scale outside 2^-17..2720, and was rerun
                                  per group); 0 if none                           */
   int32_t rerun_flags_down;   /* likewise for the down GEMM                      */
-  size_t rerun_flags_offset;  /* workspace byte offset of the flag array both
-                                 launches write from index 0; after a forward it
-                                 holds the down launch's flags (0 if neither
-                                 launch exists)                                  */
+  size_t rerun_flags_offset;  /* workspace byte offset of the flags: the gate/up
+                                 launch's rerun_flags_up flags, then the down
+                                 launch's rerun_flags_down (0 if neither launch
+                                 exists)                                         */
 } w4a16_moe_plan_t;
 
 /* Bytes of device workspace w4a16_moe_forward needs for this descriptor
- * (depends on num_tokens).  Errors as for the forward's checks. */
+ * (depends on num_tokens: token counts stay dynamic while layouts are fixed,
+ * [P2] Description, "Contract"; the caller owns the scratch the non-fused
+ * finalization stores its 16-bit expert outputs in, same section).  Errors as
+ * for the forward's checks; *bytes is written only on W4A16_OK. */
 w4a16_status_t w4a16_moe_workspace_size(const w4a16_moe_desc_t* desc, size_t* bytes);
 
 /* The variant the forward will run for this descriptor. */
@@ -228,10 +240,16 @@ w4a16_status_t w4a16_moe_route_topk(const float* logits, int64_t num_tokens,
                                     int32_t renormalize, int32_t* topk_ids, float* topk_weights,
                                     w4a16_stream_t stream);
 
-/* Static text for a status code. */
+/* Static text for a status code (unsupported configurations are strict
+ * errors, not silent fallbacks: [P1] BC-breaking).  Never null; an unknown
+ * code gives "unknown status". */
 const char* w4a16_status_string(w4a16_status_t status);
 
-/* Thread-local text of the last rejected call on this thread ("" if none). */
+/* Thread-local text of the last rejected call on this thread ("" if none):
+ * the diagnostic names the offending tensor or descriptor field and the
+ * value that failed, instead of a bare assertion ([P3] Description, the
+ * alignment and shape diagnostics).  Owned by the library; valid until the
+ * next call on the same thread. */
 const char* w4a16_last_error_message(void);
 
 #ifdef __cplusplus

@@ -61,7 +61,8 @@ def good(**kw):
     ("force_path", 3, 1, "force_path"),
     ("force_splitk", 3, 1, "force_splitk"),
     ("num_global_experts", 7, 1, "num_global_experts"),
-    ("no_fp16_route", 2, 1, "no_fp16_route"),
+    ("force_block_m", 32, 1, "force_block_m"),
+    ("fp16_route", 2, 1, "fp16_route"),
 ])
 def test_descriptor_errors(field, value, status, needle):
     d = good()
@@ -147,21 +148,27 @@ def test_plans_by_route_count():
         num_tokens=32, hidden=7168, intermediate=256, num_local_experts=384, top_k=8))
     # forcing is honoured and the workspace follows the plan
     d = B.make_desc(num_tokens=16, hidden=256, intermediate=384, num_local_experts=8, top_k=2,
-                    force_block_m=32, force_path=1)
+                    force_block_m=64, force_path=1)
     p3 = B.get_plan(d)
-    assert (p3.path, p3.block_m) == (1, 32)
+    assert (p3.path, p3.block_m) == (1, 64)
     assert p3.workspace_bytes == B.workspace_size(d)
 
 
 def test_fp16_route_choice():
-    """The exact fp16 route is taken by the grouped path's streaming launches
-    when the expected valid routes per touched expert, R / (E (1 - (1 - 1/E)^R))
-    with R = T K scaled by the local share, reach 16; only for bf16
-    activations with group scales.  Its rerun flags sit in the workspace."""
+    """The fp16 route is opt-in (descriptor field fp16_route = 1); the default
+    plan forms every product with per-group scaling.  Opted in, the grouped
+    path's streaming launches take it when the expected valid routes per
+    touched expert, R / (E (1 - (1 - 1/E)^R)) with R = T K scaled by the local
+    share, reach 16; only for bf16 activations with group scales.  Its rerun
+    flags sit in the workspace."""
     kimi = dict(hidden=7168, intermediate=256, num_local_experts=384, top_k=8)
+    for T in (1, 32, 256, 1024, 2048):
+        pl = B.get_plan(B.make_desc(num_tokens=T, **kimi))
+        assert (pl.fp16_route, pl.rerun_flags_up, pl.rerun_flags_down,
+                pl.rerun_flags_offset) == (0, 0, 0, 0), T
     for T, want in ((1, 0), (32, 0), (256, 0), (512, 0), (1024, 3), (2048, 3)):
         # 512 tokens: 10.7 routes per touched expert; 1024: 21.3
-        pl = B.get_plan(B.make_desc(num_tokens=T, **kimi))
+        pl = B.get_plan(B.make_desc(num_tokens=T, fp16_route=1, **kimi))
         assert pl.fp16_route == want, (T, pl.fp16_route)
         if want:
             assert pl.rerun_flags_up > 0 and pl.rerun_flags_down > 0
@@ -170,14 +177,14 @@ def test_fp16_route_choice():
                     <= pl.workspace_bytes)
         else:
             assert (pl.rerun_flags_up, pl.rerun_flags_down, pl.rerun_flags_offset) == (0, 0, 0)
-    assert B.get_plan(B.make_desc(num_tokens=2048, dtype=torch.float16, **kimi)).fp16_route == 0
-    off = B.get_plan(B.make_desc(num_tokens=2048, no_fp16_route=1, **kimi))
-    assert (off.fp16_route, off.rerun_flags_up, off.rerun_flags_down) == (0, 0, 0)
-    assert B.get_plan(B.make_desc(num_tokens=2048, per_channel=True, **kimi)).fp16_route == 0
+    assert B.get_plan(B.make_desc(num_tokens=2048, dtype=torch.float16, fp16_route=1,
+                                  **kimi)).fp16_route == 0
+    assert B.get_plan(B.make_desc(num_tokens=2048, per_channel=True, fp16_route=1,
+                                  **kimi)).fp16_route == 0
     # a local share of 32 of 256 experts: 512 tokens give 4096 routes, 512
     # of them valid in expectation, 16 per local expert
     share = dict(hidden=7168, intermediate=2048, num_local_experts=32, top_k=8,
-                 num_global_experts=256)
+                 num_global_experts=256, fp16_route=1)
     assert B.get_plan(B.make_desc(num_tokens=256, **share)).fp16_route == 0
     assert B.get_plan(B.make_desc(num_tokens=512, **share)).fp16_route == 3
     # counted as if every route were local, 256 tokens would already qualify
@@ -249,3 +256,28 @@ def test_fp16_route_exact_scale_range():
     assert ok[inside].all()
     assert not ok[bits == end].any() and not ok[bits == lo - 1].any()
     assert not ok[bits >= end].any()
+
+
+def test_forward_rejects_wrong_out_shape(monkeypatch):
+    """An `out` of the wrong shape is refused by the binding before the
+    library is called (the kernels write T * H values through its pointer).
+    The device checks are bypassed so the shape check runs on host tensors;
+    the library would be reached only past it."""
+    import numpy as np  # noqa: F401
+    monkeypatch.setattr(B, "_dev", lambda *a, **k: None)
+    called = []
+    monkeypatch.setattr(B, "_check", lambda st: called.append(st))
+    T, H, I, E, K = 4, 256, 384, 8, 2
+    x = torch.zeros(T, H, dtype=torch.bfloat16)
+    w13 = torch.zeros(E, 2 * I, H // 2, dtype=torch.uint8)
+    s13 = torch.zeros(E, 2 * I, H // 32, dtype=torch.bfloat16)
+    w2 = torch.zeros(E, H, I // 2, dtype=torch.uint8)
+    s2 = torch.zeros(E, H, I // 32, dtype=torch.bfloat16)
+    ids = torch.zeros(T, K, dtype=torch.int32)
+    wts = torch.zeros(T, K, dtype=torch.float32)
+    for bad in ((T - 1, H), (T, H - 8), (T * H,)):
+        with pytest.raises(ValueError, match="out: shape"):
+            B.moe_forward(x, w13, s13, w2, s2, ids, wts, intermediate=I, num_local_experts=E,
+                          out=torch.zeros(*bad, dtype=torch.bfloat16))
+    # only the host-side workspace query ran, never the forward
+    assert all(st == 0 for st in called)

@@ -78,7 +78,7 @@ def test_route_prep_skewed_and_local_share():
 # forward parity, every variant on the small gated workload
 # ---------------------------------------------------------------------------
 
-VARIANTS = ([dict(force_path=2)] + [dict(force_path=1, force_block_m=bm) for bm in (16, 32, 64)]
+VARIANTS = ([dict(force_path=2), dict(force_path=1)]
             + [dict(force_path=1, force_splitk=sk) for sk in (1, 2)])
 
 
@@ -104,22 +104,20 @@ def test_configs_small_token_counts(name, T):
 
 @pytest.mark.parametrize("name,T,force", [
     ("kimi_tp8", 8, dict(force_path=1)), ("kimi_tp8", 4, dict(force_path=2)),
-    ("kimi_tp8", 8, dict(force_path=1, force_block_m=32)),
-    ("kimi_tp8", 32, dict(force_path=1, force_block_m=64)),
-    ("per_channel", 8, dict(force_path=1, force_block_m=16)),
-    ("per_channel", 8, dict(force_path=1, force_block_m=32)),
-    ("relu2_skew", 8, dict(force_path=2)),
-    ("relu2_skew", 32, dict(force_path=1, force_block_m=32)),
-    ("deepseek_local", 16, dict(force_path=1, force_block_m=32)),
-    ("deepseek_local", 16, dict(force_path=1, force_block_m=16)),
+    ("kimi_tp8", 8, dict(force_path=1, force_splitk=2)),
     ("kimi_tp8", 32, dict(force_path=1, force_splitk=1)),
     ("kimi_tp8", 32, dict(force_path=1, force_splitk=2)),
+    ("kimi_tp8", 256, dict(force_path=1, force_splitk=1)),
+    ("per_channel", 8, dict(force_path=1)),
     ("per_channel", 8, dict(force_path=1, force_splitk=1)),
+    ("per_channel", 8, dict(force_path=1, force_splitk=2)),
+    ("per_channel", 8, dict(force_path=2)),
+    ("relu2_skew", 8, dict(force_path=2)),
     ("relu2_skew", 32, dict(force_path=1, force_splitk=1)),
     ("relu2_skew", 32, dict(force_path=1, force_splitk=2)),
     ("deepseek_local", 16, dict(force_path=1, force_splitk=1)),
-    ("deepseek_local", 1, dict(force_path=2)),
-    ("per_channel", 8, dict(force_path=2))])
+    ("deepseek_local", 16, dict(force_path=1, force_splitk=2)),
+    ("deepseek_local", 1, dict(force_path=2))])
 def test_config_variants(name, T, force):
     wl = synth.WORKLOADS[name]
     Wc, Wg = weights(name)
@@ -178,16 +176,16 @@ def test_single_expert_receives_everything():
     ids = torch.full_like(tc.topk_ids, 3)       # duplicate ids: each route counts
     tc = synth.Tokens(tc.x, ids, tc.topk_weights)
     ref = oracle_out(wl, Wc, tc)
-    for bm in (16, 32, 64):
-        out = forward(wl, Wg, tc.to("cuda"), force_path=1, force_block_m=bm)
-        assert_close(out, ref, f"one expert bm={bm}")
+    for sk in (1, 2):
+        out = forward(wl, Wg, tc.to("cuda"), force_path=1, force_splitk=sk)
+        assert_close(out, ref, f"one expert force_splitk={sk}")
     out = forward(wl, Wg, tc.to("cuda"), force_path=2)           # 64 rows, 16 passes of 4
     assert_close(out, ref, "one expert small-batch path")
 
 
 def test_activations_beyond_fp16_range():
     """bf16 activations of magnitude 2^16 and more in tiles of several subtiles
-    (the fp16 route of the tile kernels cannot hold them): those tiles are
+    on the opted-in fp16 route (whose fp16 staging cannot hold them): those tiles are
     rerun with per-group scaling, so the affected rows stay exact and the
     others are untouched.  Without the rerun, 1e6 would be clamped to 65504."""
     wl = synth.WORKLOADS["tiny"]
@@ -200,7 +198,8 @@ def test_activations_beyond_fp16_range():
     x[200, 255] = 1.0e6
     t2 = synth.Tokens(x, tc.topk_ids, tc.topk_weights)
     ref = oracle_out(wl, Wc, t2)
-    out = forward(wl, Wg, t2.to("cuda"), force_path=1).cpu()
+    assert binding.get_plan(binding.desc_for(wl, 256, force_path=1, fp16_route=1)).fp16_route == 3
+    out = forward(wl, Wg, t2.to("cuda"), force_path=1, fp16_route=1).cpu()
     rest = [r for r in range(256) if r not in big_rows]
     assert_close(out[rest], ref[rest], "tiny T=256, rows without large activations")
     for r in big_rows:
@@ -220,15 +219,15 @@ def test_fp16_route_rerun_flags(inter):
     Wc = synth.make_weights(wl, device="cpu")
     Wg = Wc.to("cuda")
     tc = tokens(wl, 256)
-    d = binding.desc_for(wl, 256, force_path=1)
+    d = binding.desc_for(wl, 256, force_path=1, fp16_route=1)
     pl = binding.get_plan(d)
     assert pl.fp16_route == 3 and pl.rerun_flags_down > 0
     ws = torch.empty(binding.workspace_size(d), dtype=torch.uint8, device="cuda")
-    off, n = pl.rerun_flags_offset, pl.rerun_flags_down
+    off, n = pl.rerun_flags_offset + 4 * pl.rerun_flags_up, pl.rerun_flags_down
 
     def run(t):
         ws.fill_(0xFF)
-        out = forward(wl, Wg, t.to("cuda"), force_path=1, workspace=ws).cpu()
+        out = forward(wl, Wg, t.to("cuda"), force_path=1, fp16_route=1, workspace=ws).cpu()
         return out, ws[off:off + 4 * n].view(torch.int32).cpu()
 
     out, flags = run(tc)
@@ -266,25 +265,57 @@ def test_fp16_route_scales_outside_exact_range(inter, which, factor):
     tc = tokens(wl, 256)
     if which == "w13":
         tc = synth.Tokens((tc.x.float() / factor).to(tc.x.dtype), tc.topk_ids, tc.topk_weights)
-    d = binding.desc_for(wl, 256, force_path=1)
+    d = binding.desc_for(wl, 256, force_path=1, fp16_route=1)
     pl = binding.get_plan(d)
     assert pl.fp16_route == 3
     ws = torch.full((binding.workspace_size(d),), 0xFF, dtype=torch.uint8, device="cuda")
-    out = forward(wl, Wc.to("cuda"), tc.to("cuda"), force_path=1, workspace=ws).cpu()
+    out = forward(wl, Wc.to("cuda"), tc.to("cuda"), force_path=1, fp16_route=1,
+                  workspace=ws).cpu()
     ref = oracle_out(wl, Wc, tc)
     for r in range(256):
         nrmse, _ = errors(out[r], ref[r])
         assert nrmse <= 5e-3, (r, nrmse)
     if which == "w2":
-        off, n = pl.rerun_flags_offset, pl.rerun_flags_down
+        off, n = pl.rerun_flags_offset + 4 * pl.rerun_flags_up, pl.rerun_flags_down
+        flags = ws[off:off + 4 * n].view(torch.int32).cpu()
+        assert int(flags.sum()) >= 1
+    else:
+        off, n = pl.rerun_flags_offset, pl.rerun_flags_up
         flags = ws[off:off + 4 * n].view(torch.int32).cpu()
         assert int(flags.sum()) >= 1
 
 
-def test_rows_of_tiny_activations_without_fp16_route():
-    """Rows whose activations all lie far below 2^-14 (x scaled by 2^-20):
-    with the fp16 route switched off in the descriptor every row, tiny or
-    not, stays within the tolerance of the oracle relative to its own size."""
+def test_zero_group_scales_stay_on_fp16_route():
+    """All-zero weight groups (zero-padded or pruned weights) have scale 0,
+    which the fp16 route forms exactly: no workgroup is sent to the rerun
+    (every flag 0, each written: the workspace starts as 0xFF), and the
+    output matches the oracle row by row."""
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], name="tiny_i256", inter=256)
+    Wc = synth.make_weights(wl, device="cpu")
+    for name in ("w13", "w2"):
+        sc = getattr(Wc, f"{name}_scales").clone()
+        sc[:, :, ::3] = 0            # every third group of every row and expert
+        setattr(Wc, f"{name}_scales", sc)
+    tc = tokens(wl, 256)
+    d = binding.desc_for(wl, 256, force_path=1, fp16_route=1)
+    pl = binding.get_plan(d)
+    assert pl.fp16_route == 3
+    ws = torch.full((binding.workspace_size(d),), 0xFF, dtype=torch.uint8, device="cuda")
+    out = forward(wl, Wc.to("cuda"), tc.to("cuda"), force_path=1, fp16_route=1,
+                  workspace=ws).cpu()
+    n = pl.rerun_flags_up + pl.rerun_flags_down
+    off = pl.rerun_flags_offset
+    flags = ws[off:off + 4 * n].view(torch.int32).cpu()
+    assert int(flags.abs().sum()) == 0, flags
+    assert_close(out, oracle_out(wl, Wc, tc), "zero groups on the fp16 route")
+
+
+def test_rows_of_tiny_activations_default_plan_exact():
+    """Rows whose activations all lie far below 2^-14 (x scaled by 2^-20): the
+    default plan (fp16 route off) forms every product with per-group scaling,
+    so every row, tiny or not, stays within the tolerance of the oracle
+    relative to its own size, at a token count where the opted-in route
+    would be taken."""
     wl = dataclasses.replace(synth.WORKLOADS["tiny"], name="tiny_i256", inter=256)
     Wc = synth.make_weights(wl, device="cpu")
     tc = tokens(wl, 256)
@@ -292,23 +323,22 @@ def test_rows_of_tiny_activations_without_fp16_route():
     tiny_rows = [5, 77, 200]
     x[tiny_rows] = (x[tiny_rows].float() * 2.0 ** -20).to(x.dtype)
     t2 = synth.Tokens(x, tc.topk_ids, tc.topk_weights)
-    assert binding.get_plan(binding.desc_for(wl, 256, force_path=1)).fp16_route == 3
-    assert binding.get_plan(binding.desc_for(wl, 256, force_path=1, no_fp16_route=1)).fp16_route == 0
-    out = forward(wl, Wc.to("cuda"), t2.to("cuda"), force_path=1, no_fp16_route=1).cpu()
+    assert binding.get_plan(binding.desc_for(wl, 256, force_path=1, fp16_route=1)).fp16_route == 3
+    assert binding.get_plan(binding.desc_for(wl, 256, force_path=1)).fp16_route == 0
+    out = forward(wl, Wc.to("cuda"), t2.to("cuda"), force_path=1).cpu()
     ref = oracle_out(wl, Wc, t2)
-    for r in range(256):
-        nrmse, _ = errors(out[r], ref[r])
-        assert nrmse <= 5e-3, (r, nrmse)
+    assert_close(out, ref, "tiny rows, default plan")
 
 
-@pytest.mark.parametrize("T,force", [(16, f) for f in VARIANTS] + [(256, dict(force_path=1))],
+@pytest.mark.parametrize("T,force", [(16, f) for f in VARIANTS] + [
+    (256, dict(force_path=1)), (256, dict(force_path=1, fp16_route=1))],
                          ids=lambda v: v if isinstance(v, int) else
                          "-".join(f"{k}{x}" for k, x in v.items()))
 def test_local_share_at_nonzero_offset(T, force):
     """Experts 8..15 of 24 are local (an expert-parallel share that is not
     the first): ids below 8 or from 16 on are other ranks' routes and add
-    nothing.  256 tokens take the exact fp16 route (about 21 valid routes per
-    local expert)."""
+    nothing.  At 256 tokens an opted-in fp16 route is taken (about 21 valid
+    routes per local expert)."""
     wl = dataclasses.replace(synth.WORKLOADS["tiny"], name="tiny_off8", num_global_experts=24,
                              expert_offset=8)
     Wc = synth.make_weights(wl, device="cpu")
@@ -316,26 +346,66 @@ def test_local_share_at_nonzero_offset(T, force):
     ids = tc.topk_ids
     assert bool(((ids < 8) | (ids >= 16)).any()) and bool(((ids >= 8) & (ids < 16)).any())
     if T == 256:
-        assert binding.get_plan(binding.desc_for(wl, T, **force)).fp16_route == 3
+        want = 3 if force.get("fp16_route") else 0
+        assert binding.get_plan(binding.desc_for(wl, T, **force)).fp16_route == want
     out = forward(wl, Wc.to("cuda"), tc.to("cuda"), **force)
     assert_close(out, oracle_out(wl, Wc, tc), f"offset 8 of 24, T={T} {force}")
 
 
-def test_poisoned_workspace_and_output():
+POISON_CASES = [
+    ("tiny", 16, dict(force_path=2)), ("tiny", 16, dict(force_path=1)),
+    ("tiny", 16, dict(force_path=1, force_splitk=1)),
+    ("tiny", 16, dict(force_path=1, force_splitk=2)),
+    ("kimi_tp8", 32, dict()),                         # automatic plan: split-K
+    ("deepseek_local", 16, dict()),                   # split-K over column chunks
+    ("tiny", 256, dict(force_path=1, fp16_route=1)),
+]
+
+
+@pytest.mark.parametrize("name,T,force", POISON_CASES,
+                         ids=lambda v: "-".join(f"{k}{x}" for k, x in v.items())
+                         if isinstance(v, dict) else str(v))
+def test_poisoned_workspace_and_output(name, T, force):
     """Workspace and output filled with NaN patterns before the call: nothing
-    uninitialised may leak (empty split-K partitions, padding rows)."""
-    wl, Wc, Wg = _small()
-    tc = tokens(wl, 16)
+    uninitialised may leak (empty split-K partitions, padding rows, FP32
+    partials of routes that a chunk never touched)."""
+    wl = synth.WORKLOADS[name]
+    Wc, Wg = weights(name)
+    tc = tokens(wl, T)
     tg = tc.to("cuda")
     ref = oracle_out(wl, Wc, tc)
-    for force in (dict(force_path=2), dict(force_path=1, force_block_m=16),
-                  dict(force_path=1, force_block_m=64)):
-        d = binding.desc_for(wl, 16, **force)
-        ws = torch.full((binding.workspace_size(d),), 0xFF, dtype=torch.uint8, device="cuda")
-        out = torch.full((16, wl.hidden), float("nan"), dtype=wl.dtype, device="cuda")
-        binding.forward_workload(wl, Wg, tg, out=out, workspace=ws, **force)
+    d = binding.desc_for(wl, T, **force)
+    if name == "kimi_tp8":
+        assert binding.get_plan(d).splitk_chunks > 0
+    ws = torch.full((binding.workspace_size(d),), 0xFF, dtype=torch.uint8, device="cuda")
+    out = torch.full((T, wl.hidden), float("nan"), dtype=wl.dtype, device="cuda")
+    binding.forward_workload(wl, Wg, tg, out=out, workspace=ws, **force)
+    torch.cuda.synchronize()
+    assert_close(out, ref, f"poisoned {name} T={T} {force}")
+
+
+def test_workspace_reuse_across_token_counts():
+    """One workspace and one output buffer reused over token counts that fill
+    64-row tiles exactly, then leave ragged padded tails, then fill them again
+    (aligned -> padded -> aligned): every call matches a call on a fresh
+    NaN-poisoned workspace bit for bit, and the oracle."""
+    wl = synth.WORKLOADS["tiny"]
+    Wc, Wg = weights("tiny")
+    seq = [256, 100, 256, 37, 128]           # 8 experts, top-2: 64, ~25, 64, ~9, 32 per expert
+    big = max(binding.workspace_size(binding.desc_for(wl, t)) for t in seq)
+    ws = torch.full((big,), 0xFF, dtype=torch.uint8, device="cuda")
+    obuf = torch.full((max(seq) * wl.hidden,), float("nan"), dtype=wl.dtype, device="cuda")
+    for T in seq:
+        tc = tokens(wl, T)
+        tg = tc.to("cuda")
+        out = obuf[:T * wl.hidden].view(T, wl.hidden)
+        binding.forward_workload(wl, Wg, tg, out=out, workspace=ws)
+        fresh_ws = torch.full((binding.workspace_size(binding.desc_for(wl, T)),), 0xFF,
+                              dtype=torch.uint8, device="cuda")
+        fresh = binding.forward_workload(wl, Wg, tg, workspace=fresh_ws)
         torch.cuda.synchronize()
-        assert_close(out, ref, f"poisoned {force}")
+        assert torch.equal(out.view(torch.int16), fresh.view(torch.int16)), T
+        assert_close(out, oracle_out(wl, Wc, tc), f"reuse T={T}")
 
 
 def test_reduction_slices_cover_every_block():
@@ -363,7 +433,7 @@ def test_ragged_reduction_tails(per_channel, gated, dtype):
     Wg = Wc.to("cuda")
     for T, force in ((150, dict(force_path=1, force_splitk=2)),
                      (150, dict(force_path=1, force_splitk=1)), (40, dict(force_path=1)),
-                     (40, dict(force_path=1, force_block_m=32)), (20, dict(force_path=2))):
+                     (40, dict(force_path=1, force_splitk=1)), (20, dict(force_path=2))):
         tc = tokens(wl, T)
         out = forward(wl, Wg, tc.to("cuda"), **force)
         assert_close(out, oracle_out(wl, Wc, tc), f"tails T={T} {force}")
@@ -422,28 +492,46 @@ def test_gpu_invariances_bitwise(path):
     assert torch.equal(op.view(torch.int16), base[perm].view(torch.int16))
 
 
-def test_hip_graph_replay():
-    wl = synth.WORKLOADS["kimi_tp8"]
-    Wc, Wg = weights("kimi_tp8")
-    for T in (1, 32):
-        tg = tokens(wl, T, "cuda")
-        d = binding.desc_for(wl, T)
-        ws = torch.empty(binding.workspace_size(d), dtype=torch.uint8, device="cuda")
-        out = torch.empty(T, wl.hidden, dtype=wl.dtype, device="cuda")
-        eager = forward(wl, Wg, tg).clone()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            binding.forward_workload(wl, Wg, tg, out=out, workspace=ws)
-        torch.cuda.current_stream().wait_stream(s)
+GRAPH_CASES = [("kimi_tp8", 1, dict()), ("kimi_tp8", 32, dict()),
+               ("kimi_tp8", 256, dict(fp16_route=1)), ("kimi_tp8", 1024, dict(fp16_route=1)),
+               ("per_channel", 8, dict()), ("per_channel", 256, dict()),
+               ("relu2_skew", 32, dict()), ("relu2_skew", 1024, dict()),
+               ("deepseek_local", 16, dict())]
+
+
+@pytest.mark.parametrize("name,T,force", GRAPH_CASES,
+                         ids=lambda v: "-".join(f"{k}{x}" for k, x in v.items())
+                         if isinstance(v, dict) else str(v))
+def test_hip_graph_replay(name, T, force):
+    """The forward captured in a HIP graph replays to the eager result bit for
+    bit, three times, with eager work and synchronizations between replays
+    (small batch, split-K, streaming tiles, per-channel, ReLU^2 fp16, the
+    opted-in fp16 route with its rerun launches)."""
+    wl = synth.WORKLOADS[name]
+    Wc, Wg = weights(name)
+    tg = tokens(wl, T, "cuda")
+    d = binding.desc_for(wl, T, **force)
+    pl = binding.get_plan(d)
+    sys_msg = f"{name} T={T} plan path={pl.path} splitk={pl.splitk_chunks} fp16={pl.fp16_route}"
+    print(sys_msg, flush=True)
+    ws = torch.empty(binding.workspace_size(d), dtype=torch.uint8, device="cuda")
+    out = torch.empty(T, wl.hidden, dtype=wl.dtype, device="cuda")
+    eager = forward(wl, Wg, tg, **force).clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        binding.forward_workload(wl, Wg, tg, out=out, workspace=ws, **force)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        binding.forward_workload(wl, Wg, tg, out=out, workspace=ws, **force)
+    for _ in range(3):
+        out.zero_()
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            binding.forward_workload(wl, Wg, tg, out=out, workspace=ws)
-        for _ in range(3):
-            out.zero_()
-            torch.cuda.synchronize()
-            g.replay()
-            torch.cuda.synchronize()
-            assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
-            forward(wl, Wg, tg)                      # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
+        forward(wl, Wg, tg, **force)              # eager work between replays
+    if T <= 32:
+        assert_close(out, oracle_out(wl, Wc, tokens(wl, T)), f"graph {name} T={T}")

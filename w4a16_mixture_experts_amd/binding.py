@@ -27,7 +27,7 @@ class MoeDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_tokens", "hidden", "intermediate", "num_local_experts", "expert_offset", "top_k",
         "group_size", "dtype", "act", "qlayout", "force_path", "force_block_m", "force_splitk",
-        "num_global_experts", "no_fp16_route")]
+        "num_global_experts", "fp16_route")]
 
 
 class MoePlan(ctypes.Structure):
@@ -110,17 +110,17 @@ def make_desc(*, num_tokens: int, hidden: int, intermediate: int, num_local_expe
               top_k: int, expert_offset: int = 0, dtype=torch.bfloat16, gated: bool = True,
               per_channel: bool = False, group_size: int = 32, force_path: int = 0,
               force_block_m: int = 0, force_splitk: int = 0,
-              num_global_experts: int = 0, no_fp16_route: int = 0) -> MoeDesc:
-    """force_path: 0 auto, 1 grouped, 2 small batch; force_block_m: 0 or 16/32/64;
+              num_global_experts: int = 0, fp16_route: int = 0) -> MoeDesc:
+    """force_path: 0 auto, 1 grouped, 2 small batch; force_block_m: 0 or 64;
     force_splitk: 0 auto, 1 split-K gate/up, 2 streaming gate/up (64-row tiles);
     num_global_experts: experts the routes are drawn over (0 = num_local_experts),
-    used only to choose the variant; no_fp16_route: 1 keeps the plan off the
-    exact fp16 route."""
+    used only to choose the variant; fp16_route: 1 opts in to the fp16 route
+    (bf16 only; rows of activations all below about 2^-14 keep fewer bits)."""
     return MoeDesc(num_tokens, hidden, intermediate, num_local_experts, expert_offset, top_k,
                    group_size, DT_FP16 if dtype == torch.float16 else DT_BF16,
                    ACT_SILU_GATED if gated else ACT_RELU2,
                    Q_PER_CHANNEL if per_channel else Q_GROUP_K, force_path, force_block_m,
-                   force_splitk, num_global_experts, no_fp16_route)
+                   force_splitk, num_global_experts, fp16_route)
 
 
 def workspace_size(desc: MoeDesc) -> int:
@@ -148,7 +148,7 @@ def moe_forward(x, w13_packed, w13_scales, w2_packed, w2_scales, topk_ids, topk_
                 intermediate: int, num_local_experts: int, expert_offset: int = 0,
                 gated: bool = True, per_channel: bool = False, out=None, workspace=None,
                 force_path: int = 0, force_block_m: int = 0, force_splitk: int = 0,
-                num_global_experts: int = 0, no_fp16_route: int = 0,
+                num_global_experts: int = 0, fp16_route: int = 0,
                 stream=None, stage_events=None) -> torch.Tensor:
     """Local W4A16 MoE forward: returns out [T, H] in x's dtype.
 
@@ -185,12 +185,14 @@ def moe_forward(x, w13_packed, w13_scales, w2_packed, w2_scales, topk_ids, topk_
                      top_k=topk_ids.shape[1], expert_offset=expert_offset, dtype=x.dtype,
                      gated=gated, per_channel=per_channel, force_path=force_path,
                      force_block_m=force_block_m, force_splitk=force_splitk,
-                     num_global_experts=num_global_experts, no_fp16_route=no_fp16_route)
+                     num_global_experts=num_global_experts, fp16_route=fp16_route)
     nbytes = workspace_size(desc)
     if out is None:
         out = torch.empty(T, H, dtype=x.dtype, device=dev)
     else:
         _dev("out", out, (x.dtype,), dev)
+        if tuple(out.shape) != (T, H):
+            raise ValueError(f"out: shape {tuple(out.shape)}, expected {(T, H)}")
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     else:

@@ -39,7 +39,7 @@ w4a16_status_t fail(w4a16_status_t st, const char* fmt, ...) {
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Plan {
-  int path = 2, bm = 16, ms = 1, kslice = 128, nkb = 1, nkb_tile = 1;
+  int path = 2, bm = 64, kslice = 128, nkb = 1;
   int n_tiles_up = 0, n_tiles_down = 0, mode_up = 0;
   bool down_resident = false;  // grouped path: down GEMM with the tile's rows resident in LDS
   int col_steps = 0;
@@ -49,6 +49,7 @@ struct Plan {
   int N1 = 0;
   bool x16 = false;       // streaming tile launches take the exact fp16 route
   bool x16_down = false;  // so does the resident down GEMM
+  int64_t n_redo_up = 0, n_redo_down = 0;  // rerun flags of those launches
   size_t off_counts = 0, off_offsets = 0, off_slot = 0, off_sorted = 0, off_tile = 0,
          off_act = 0, off_y = 0, off_part = 0, off_chunks = 0, off_redo = 0, total = 0;
 };
@@ -82,15 +83,14 @@ w4a16_status_t check_desc(const w4a16_moe_desc_t* d) {
   const int64_t R = static_cast<int64_t>(d->num_tokens) * d->top_k;
   if (R > (int64_t(1) << 26))
     return fail(W4A16_ERR_UNSUPPORTED, "topk_ids: %lld routes exceed 2^26", (long long)R);
-  if (d->force_block_m != 0 && d->force_block_m != 16 && d->force_block_m != 32 &&
-      d->force_block_m != 64)
-    return fail(W4A16_ERR_INVALID_ARG, "desc.force_block_m: %d (0, 16, 32 or 64)", d->force_block_m);
+  if (d->force_block_m != 0 && d->force_block_m != 64)
+    return fail(W4A16_ERR_INVALID_ARG, "desc.force_block_m: %d (0 or 64)", d->force_block_m);
   if (d->force_path < 0 || d->force_path > 2)
     return fail(W4A16_ERR_INVALID_ARG, "desc.force_path: %d (0, 1 or 2)", d->force_path);
   if (d->force_splitk < 0 || d->force_splitk > 2)
     return fail(W4A16_ERR_INVALID_ARG, "desc.force_splitk: %d (0, 1 or 2)", d->force_splitk);
-  if (d->no_fp16_route != 0 && d->no_fp16_route != 1)
-    return fail(W4A16_ERR_INVALID_ARG, "desc.no_fp16_route: %d (0 or 1)", d->no_fp16_route);
+  if (d->fp16_route != 0 && d->fp16_route != 1)
+    return fail(W4A16_ERR_INVALID_ARG, "desc.fp16_route: %d (0 or 1)", d->fp16_route);
   if (d->num_global_experts != 0 && d->num_global_experts < d->num_local_experts)
     return fail(W4A16_ERR_INVALID_ARG, "desc.num_global_experts: %d < num_local_experts %d",
                 d->num_global_experts, d->num_local_experts);
@@ -102,10 +102,9 @@ w4a16_status_t check_desc(const w4a16_moe_desc_t* d) {
 //   path 2 (small batch): R <= 64.  No route preparation; the gate/up kernel
 //     finds each touched expert's rows in the ids and splits the reduction
 //     over 8 waves; the down kernel combines per token.
-//   path 1 (grouped): route preparation into block_m-row expert tiles, the
-//     gate/up GEMM per tile, the grouped down GEMM and the FP32 combine.
-//     block_m 64 (default): LDS-staged tiles that skip empty 16-row subtiles;
-//     16: the 8-wave split-reduction kernel; 32: register-fed tiles.
+//   path 1 (grouped): route preparation into 64-row expert tiles (empty
+//     16-row subtiles are skipped at run time), the gate/up GEMM per tile
+//     (streaming or split-K), the down GEMM and the FP32 combine.
 // Expected routes per touched expert under uniform routing: R routes over E
 // experts touch E (1 - (1 - 1/E)^R) of them in expectation.  With a local
 // share (E of num_global_experts), routes are counted valid in proportion.
@@ -140,31 +139,21 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
                   static_cast<int64_t>(K) * I <= w4moe::kDecActLoads * w4moe::kDecThreadsAll * 8)
                      ? 2 : 1;
 
-  // per-wave reduction slice of the split-reduction gate/up kernels
-  // (16 waves on the small-batch path, 8 on grouped 16-row tiles)
+  // per-wave reduction slice of the small-batch gate/up kernel (8 waves)
   const int up_blocks = (H + 127) / 128;
-  const int waves = 8;  // reduction slices of both split-reduction kernels
-  const int per_wave = (up_blocks + waves - 1) / waves;
+  const int per_wave = (up_blocks + w4moe::kSmallWaves - 1) / w4moe::kSmallWaves;
   pl.kslice = per_wave * 128;
-  pl.nkb = per_wave;  // small-batch kernel: exact; 16-row tile kernel: rounded to 1/2/4
-  pl.nkb_tile = per_wave <= 1 ? 1 : (per_wave <= 2 ? 2 : 4);
-
-  // 64-row tiles skip their empty 16-row subtiles, so they are the default at
-  // every route count; 16 and 32 remain selectable
-  pl.bm = d->force_block_m ? d->force_block_m : w4moe::kTileRows;
-  pl.ms = pl.bm / 16;
+  pl.nkb = per_wave;
 
   const int64_t touched = std::min<int64_t>(E, pl.R);
   pl.P = pl.R + touched * (pl.bm - 1);
   pl.MT = pl.P / pl.bm;
-  const bool tile64 = pl.bm == w4moe::kTileRows;
-  const int cols_gated = tile64 ? w4moe::kTileColsGated : w4moe::kWgColsGated;
-  const int cols_plain = tile64 ? w4moe::kTileColsPlain : w4moe::kWgColsPlain;
-  pl.n_tiles_up = gated ? (I + cols_gated - 1) / cols_gated : (I + cols_plain - 1) / cols_plain;
-  pl.n_tiles_down = (H + cols_plain - 1) / cols_plain;
+  pl.n_tiles_up = gated ? (I + w4moe::kTileColsGated - 1) / w4moe::kTileColsGated
+                        : (I + w4moe::kTileColsPlain - 1) / w4moe::kTileColsPlain;
+  pl.n_tiles_down = (H + w4moe::kTileColsPlain - 1) / w4moe::kTileColsPlain;
   // split-K gate/up when tiles are expected to hold few routes (every route
   // counted, as when the crossover below was measured)
-  if (tile64 && pl.R > 0) {
+  if (pl.R > 0) {
     const double rpe_all = routes_per_touched_expert(d, pl.R, false);
     // measured crossover: split-K wins at ~1.4 routes per expert (Kimi shard,
     // 32 tokens), the streaming kernel at ~5 (256 tokens)
@@ -202,11 +191,11 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
   // subtile (5 routes per expert at 256 tokens) keep the per-group form.
   // Routes are counted as valid in proportion to the local share of the
   // global experts (uniform routing).
-  if (tile64 && pl.R > 0 && d->dtype == W4A16_DT_BF16 && d->qlayout == W4A16_Q_GROUP_K &&
-      d->no_fp16_route == 0) {
+  if (pl.R > 0 && d->dtype == W4A16_DT_BF16 && d->qlayout == W4A16_Q_GROUP_K &&
+      d->fp16_route == 1) {
     pl.x16 = routes_per_touched_expert(d, pl.R, true) >= 16.0;
   }
-  pl.down_resident = tile64 && I <= w4moe::kResidentK;
+  pl.down_resident = I <= w4moe::kResidentK;
   // The down GEMM takes the fp16 route under the same condition (measured on
   // the Kimi shard's resident kernel: 167 -> 148 us at 2048 tokens; tiles of
   // one subtile were slower on it).
@@ -245,12 +234,13 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
     pl.off_y = take(sizeof(uint16_t) * pl.P * H);
     if (pl.splitk_S > 0)
       pl.off_part = take(sizeof(float) * static_cast<size_t>(pl.splitk_S) * pl.R * pl.N1);
-    if (pl.x16 || pl.x16_down) {
-      const int64_t mt = std::max<int64_t>(pl.MT, 1);
-      pl.off_redo = take(sizeof(int32_t) *
-                         std::max(w4moe::tile_launch_workgroups(pl.n_tiles_up, mt),
-                                  w4moe::tile_launch_workgroups(pl.n_tiles_down, mt)));
-    }
+    // rerun flags of the fp16-route launches: the gate/up launch's, then the
+    // down launch's
+    const int64_t mt = std::max<int64_t>(pl.MT, 1);
+    pl.n_redo_up = (pl.x16 && pl.splitk_S == 0) ? w4moe::tile_launch_workgroups(pl.n_tiles_up, mt) : 0;
+    pl.n_redo_down = pl.x16_down ? w4moe::tile_launch_workgroups(pl.n_tiles_down, mt) : 0;
+    if (pl.n_redo_up + pl.n_redo_down > 0)
+      pl.off_redo = take(sizeof(int32_t) * (pl.n_redo_up + pl.n_redo_down));
   }
   pl.total = off;
   return pl;
@@ -336,13 +326,11 @@ w4a16_status_t w4a16_moe_get_plan(const w4a16_moe_desc_t* desc, w4a16_moe_plan_t
   plan->max_positions = pl.P;
   plan->max_tiles = pl.MT;
   plan->workspace_bytes = pl.total;
-  const bool up16 = pl.path == 1 && pl.x16 && pl.splitk_S == 0;
-  const bool dn16 = pl.path == 1 && pl.x16_down;
-  const int64_t mt = std::max<int64_t>(pl.MT, 1);
+  const bool up16 = pl.path == 1 && pl.n_redo_up > 0;
+  const bool dn16 = pl.path == 1 && pl.n_redo_down > 0;
   plan->fp16_route = (up16 ? 1 : 0) | (dn16 ? 2 : 0);
-  plan->rerun_flags_up = up16 ? static_cast<int32_t>(w4moe::tile_launch_workgroups(pl.n_tiles_up, mt)) : 0;
-  plan->rerun_flags_down =
-      dn16 ? static_cast<int32_t>(w4moe::tile_launch_workgroups(pl.n_tiles_down, mt)) : 0;
+  plan->rerun_flags_up = up16 ? static_cast<int32_t>(pl.n_redo_up) : 0;
+  plan->rerun_flags_down = dn16 ? static_cast<int32_t>(pl.n_redo_down) : 0;
   plan->rerun_flags_offset = (up16 || dn16) ? pl.off_redo : 0;
   return W4A16_OK;
 }
@@ -409,28 +397,6 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
   const int64_t w2_sc = group ? static_cast<int64_t>(H) * (I / 32) : H;
   const bool gated = desc->act == W4A16_ACT_SILU_GATED;
 
-  w4moe::DecodeUpParams du{};
-  du.x = static_cast<const uint16_t*>(x);
-  du.lda = H;
-  du.ids = topk_ids;
-  du.R = static_cast<int>(pl.R);
-  du.top_k = K;
-  du.E = E;
-  du.off = desc->expert_offset;
-  du.sorted = sorted;
-  du.tile_expert = tile;
-  du.offsets = offsets;
-  du.wq = w13_packed;
-  du.ws = static_cast<const uint16_t*>(w13_scales);
-  du.wq_expert_bytes = w13_bytes;
-  du.ws_expert_elems = w13_sc;
-  du.K = H;
-  du.kslice = pl.kslice;
-  du.n_cols = I;
-  du.up_rows = I;
-  du.act = act;
-  du.ldo = I;
-
   if (pl.path == 2) {
     // small batch: FP32 pre-activations per touched expert (rows found in the
     // ids), then the activation, the down GEMM and the combine per token
@@ -495,13 +461,7 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
   // a2-a4: gathered gate/up (or w1) GEMM with the activation epilogue
   st = hip_status(evs.mark(2), "stage event");
   if (st != W4A16_OK) return st;
-  if (pl.bm == 16) {
-    du.rows_from_ids = 0;
-    du.act_by_route = 0;
-    st = hip_status(w4moe::launch_decode_up(du, desc->dtype, desc->qlayout, gated, pl.nkb_tile,
-                                            static_cast<int>(pl.MT), stream),
-                    "gate/up GEMM launch");
-  } else {
+  {
     w4moe::GemmParams up{};
     up.a = static_cast<const uint16_t*>(x);
     up.lda = H;
@@ -523,7 +483,7 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
     up.out = act;
     up.ldo = I;
     up.n_tiles = pl.n_tiles_up;
-    up.redo = pl.x16 ? reinterpret_cast<int32_t*>(ws + pl.off_redo) : nullptr;
+    up.redo = pl.n_redo_up > 0 ? reinterpret_cast<int32_t*>(ws + pl.off_redo) : nullptr;
     if (pl.splitk_S > 0) {
       up.redo = nullptr;
       up.part = reinterpret_cast<float*>(ws + pl.off_part);
@@ -540,13 +500,11 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
       if (st == W4A16_OK)
         st = hip_status(w4moe::launch_splitk_act(up, desc->dtype, gated, stream),
                         "activation launch");
-    } else
-    st = hip_status(pl.bm == w4moe::kTileRows
-                        ? w4moe::launch_tile_gemm(up, desc->dtype, desc->qlayout, pl.mode_up,
-                                                  static_cast<int>(pl.MT), stream)
-                        : w4moe::launch_grouped_gemm(up, desc->dtype, desc->qlayout, pl.ms,
-                                                     pl.mode_up, static_cast<int>(pl.MT), stream),
-                    "gate/up GEMM launch");
+    } else {
+      st = hip_status(w4moe::launch_tile_gemm(up, desc->dtype, desc->qlayout, pl.mode_up,
+                                              static_cast<int>(pl.MT), stream),
+                      "gate/up GEMM launch");
+    }
   }
   if (st == W4A16_OK) st = hip_status(evs.mark(3), "stage event");
   if (st != W4A16_OK) return st;
@@ -572,19 +530,17 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
   dn.out = ybuf;
   dn.ldo = H;
   dn.n_tiles = pl.n_tiles_down;
-  dn.redo = pl.x16_down ? reinterpret_cast<int32_t*>(ws + pl.off_redo) : nullptr;
+  dn.redo = pl.n_redo_down > 0
+                ? reinterpret_cast<int32_t*>(ws + pl.off_redo) + pl.n_redo_up
+                : nullptr;
   st = hip_status(evs.mark(4), "stage event");
   if (st != W4A16_OK) return st;
   dn.col_steps = pl.col_steps;
   st = hip_status(pl.down_resident
                       ? w4moe::launch_down_resident(dn, desc->dtype, desc->qlayout,
                                                     static_cast<int>(pl.MT), stream)
-                  : pl.bm == w4moe::kTileRows
-                      ? w4moe::launch_tile_gemm(dn, desc->dtype, desc->qlayout, w4moe::MODE_DOWN,
-                                                static_cast<int>(pl.MT), stream)
-                      : w4moe::launch_grouped_gemm(dn, desc->dtype, desc->qlayout, pl.ms,
-                                                   w4moe::MODE_DOWN, static_cast<int>(pl.MT),
-                                                   stream),
+                  : w4moe::launch_tile_gemm(dn, desc->dtype, desc->qlayout, w4moe::MODE_DOWN,
+                                            static_cast<int>(pl.MT), stream),
                   "down GEMM launch");
   if (st == W4A16_OK) st = hip_status(evs.mark(5), "stage event");
   if (st != W4A16_OK) return st;

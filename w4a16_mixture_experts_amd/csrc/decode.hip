@@ -9,19 +9,11 @@
 //        overhead"  Description, "Contract": FP32 combine in fixed top-k
 //        order before one 16-bit cast, no atomics.
 //
-// decode_up_kernel   grid (route slots or expert tiles) x (column tiles),
-//   8 waves.  Row source, selected by `rows_from_ids`:
-//     - from the ids themselves: the workgroup of route slot r reads all R
-//       ids, keeps the routes whose expert equals that of r (ascending), and
-//       proceeds only if r is the first of them, so every touched expert is
-//       handled exactly once and its weights are streamed once;
-//     - from a 16-row tile of the route-prepared list.
-//   The 8 waves split the reduction dim into contiguous slices; each wave's
-//   FP32 partial tile goes to LDS and wave 0 adds the slices in slice order,
-//   applies SiLU(gate)*up or ReLU^2 and writes the 16-bit activation rows.
-//   No partial sums leave the workgroup, so no cross-workgroup fence or
-//   counter is needed, and the result is independent of scheduling.
-//
+// small_h_kernel  grid (16-column weight subtiles) x (route slots), 8 waves:
+//   the workgroup of the first route of each touched expert (one ballot over
+//   the ids) computes that expert's FP32 pre-activations for every route of
+//   the expert, the reduction split over the 8 waves and summed in LDS in
+//   slice order.
 // decode_down_kernel  grid (32 output columns) x (tokens), 8 waves.  Work
 //   items are (route k, 256-wide slice of the reduction); each wave computes
 //   its items' 32 partial outputs in FP32 (one MFMA row: a route is a single
@@ -42,26 +34,6 @@ struct BBlk {
   uint32_t d[LAYOUT == Q_GROUP_K ? 4 : 8];
   uint32_t s[2];
 };
-
-template <int LAYOUT>
-__device__ __forceinline__ void ld_b(BBlk<LAYOUT>& b, const uint8_t* brow, const uint16_t* srow,
-                                     int k0, int ng, int g, bool on, const void* safe) {
-  if constexpr (LAYOUT == Q_GROUP_K) {
-    const u32x4 v = load16_if(on && g < ng, brow + (k0 >> 1) + 16 * g, safe);
-    b.d[0] = v[0]; b.d[1] = v[1]; b.d[2] = v[2]; b.d[3] = v[3];
-    const uint32_t* sp = reinterpret_cast<const uint32_t*>(srow + (k0 >> 5));
-    b.s[0] = load4_if(on, sp, safe);
-    b.s[1] = load4_if(on && ng > 2, sp + 1, safe);
-  } else {
-    const bool ok = on && g < ng;
-    const u32x4 v0 = load16_if(ok, brow + k0 + 32 * g, safe);
-    const u32x4 v1 = load16_if(ok, brow + k0 + 32 * g + 16, safe);
-    b.d[0] = v0[0]; b.d[1] = v0[1]; b.d[2] = v0[2]; b.d[3] = v0[3];
-    b.d[4] = v1[0]; b.d[5] = v1[1]; b.d[6] = v1[2]; b.d[7] = v1[3];
-    b.s[0] = b.s[1] = 0u;
-    (void)srow;
-  }
-}
 
 template <int LAYOUT>
 __device__ __forceinline__ void tr_b(BBlk<LAYOUT>& b) {
@@ -88,202 +60,12 @@ __device__ __forceinline__ float sc_of(uint32_t pair, int j) {
   return H16<DT>::to_f32((j & 1) ? (pair >> 16) : (pair & 0xffffu));
 }
 
-__device__ __forceinline__ u32x4 z4() {
-  u32x4 z;
-  z[0] = z[1] = z[2] = z[3] = 0u;
-  return z;
-}
-
 __device__ __forceinline__ int local_id(int32_t g, int E, int off) {
   const int64_t e = static_cast<int64_t>(g) - off;
   return (e >= 0 && e < E) ? static_cast<int>(e) : -1;
 }
 
 }  // namespace
-
-// ---------------------------------------------------------------------------
-// gate/up (or w1) GEMM for few rows per expert, reduction split over 8 waves
-// ---------------------------------------------------------------------------
-template <int DT, int LAYOUT, bool GATED, int NKB>
-__global__ void __launch_bounds__(kDecThreads)
-decode_up_kernel(const DecodeUpParams p) {
-  using T = H16<DT>;
-  constexpr int NSUB = 2;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int c = lane & 15, g = lane >> 4, par = c & 1;
-  const int nt = blockIdx.y;
-
-  __shared__ int s_rows[kDecMaxRows];
-  __shared__ int s_wcnt[kDecWaves];
-  __shared__ f32x4 s_red[kDecWaves][NSUB][64];
-
-  int M = 0, e = 0;
-  if (p.rows_from_ids) {
-    // rows: every route with the same expert as route slot blockIdx.x
-    const int r0 = blockIdx.x;
-    const int32_t gid = p.ids[r0];
-    e = local_id(gid, p.E, p.off);
-    if (e < 0) return;  // invalid route: nothing to do (uniform)
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = 0; base < p.R; base += kDecThreads) {
-      const int j = base + tid;
-      const bool m = (j < p.R) && (p.ids[j] == gid);
-      const uint64_t bal = __ballot(m);
-      if (lane == 0) s_wcnt[w] = __popcll(bal);
-      __syncthreads();
-      int before = M;
-      for (int v = 0; v < w; ++v) before += s_wcnt[v];
-      int tot = M;
-      for (int v = 0; v < kDecWaves; ++v) tot += s_wcnt[v];
-      if (m) {
-        const int idx = before + __popcll(bal & below);
-        if (idx < kDecMaxRows) s_rows[idx] = j;
-      }
-      M = tot;
-      __syncthreads();
-    }
-    if (s_rows[0] != r0) return;  // another slot owns this expert (uniform)
-    if (M > kDecMaxRows) M = kDecMaxRows;  // cannot happen for R <= kDecMaxRows
-  } else {
-    // rows: one 16-row tile of the route-prepared list
-    const int tile = blockIdx.x;
-    if (tile * 16 >= p.offsets[p.E]) return;
-    e = p.tile_expert[tile];
-    if (tid < 16) s_rows[tid] = p.sorted[tile * 16 + tid];
-    __syncthreads();
-    M = 0;
-    while (M < 16 && s_rows[M] >= 0) ++M;
-  }
-
-  // this workgroup's weight rows: gated -> 16 gate + 16 up rows, else 32 rows
-  int col[NSUB], wrow[NSUB];
-  bool on[NSUB];
-  if constexpr (GATED) {
-    const int i0 = nt * 16;
-    on[0] = on[1] = i0 < p.n_cols;
-    col[0] = col[1] = i0 + c;
-    wrow[0] = i0 + c;
-    wrow[1] = p.up_rows + i0 + c;
-  } else {
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      on[s] = nt * 32 + 16 * s < p.n_cols;
-      col[s] = nt * 32 + 16 * s + c;
-      wrow[s] = col[s];
-    }
-  }
-  const uint8_t* wq_e = p.wq + static_cast<int64_t>(e) * p.wq_expert_bytes;
-  const uint16_t* ws_e = p.ws + static_cast<int64_t>(e) * p.ws_expert_elems;
-  const uint8_t* brow[NSUB];
-  const uint16_t* srow[NSUB];
-  float scol[NSUB];
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    if constexpr (LAYOUT == Q_GROUP_K) {
-      brow[s] = wq_e + static_cast<int64_t>(wrow[s]) * (p.K >> 1);
-      srow[s] = ws_e + static_cast<int64_t>(wrow[s]) * (p.K >> 5);
-      scol[s] = 0.0f;
-    } else {
-      brow[s] = wq_e + static_cast<int64_t>(wrow[s] >> 1) * p.K;
-      srow[s] = nullptr;
-      scol[s] = on[s] ? T::to_f32(ws_e[wrow[s]]) : 0.0f;
-    }
-  }
-
-  u32x4 bconst;
-  bconst[0] = bconst[1] = bconst[2] = bconst[3] = T::kNegOneHalf2;
-  const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
-  const int kb = w * p.kslice;
-  const int ke = min(p.K, kb + p.kslice);
-
-  for (int m0 = 0; m0 < M; m0 += 16) {
-    // A row of this lane (row c of the 16-row subtile)
-    const uint16_t* arow = nullptr;
-    if (m0 + c < M) arow = p.x + static_cast<int64_t>(s_rows[m0 + c] / p.top_k) * p.lda;
-
-    f32x4 acc[NSUB];
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) acc[s] = fzero;
-
-    for (int kb0 = kb; kb0 < ke; kb0 += NKB * 128) {
-      // issue every weight load of this batch first (the HBM stream)
-      BBlk<LAYOUT> b[NKB][NSUB];
-#pragma unroll
-      for (int i = 0; i < NKB; ++i) {
-        const int k0 = kb0 + 128 * i;
-        const int ng = k0 < ke ? min(4, (ke - k0) >> 5) : 0;
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) ld_b<LAYOUT>(b[i][s], brow[s], srow[s], k0, ng, g, on[s] && ng > 0, p.wq);
-      }
-      // activations (L2-resident rows of x)
-      u32x4 a[NKB][4];
-#pragma unroll
-      for (int i = 0; i < NKB; ++i) {
-        const int k0 = kb0 + 128 * i;
-        const int ng = k0 < ke ? min(4, (ke - k0) >> 5) : 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          a[i][j] = permute_a(load16_if(arow != nullptr && j < ng, arow + k0 + 32 * j + 8 * g, p.x));
-      }
-#pragma unroll
-      for (int i = 0; i < NKB; ++i) {
-        const int k0 = kb0 + 128 * i;
-        if (k0 >= ke) break;
-        const int ng = min(4, (ke - k0) >> 5);
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) tr_b<LAYOUT>(b[i][s]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (j >= ng) break;
-          const f32x4 corr = T::mfma(a[i][j], bconst, fzero);
-#pragma unroll
-          for (int s = 0; s < NSUB; ++s) {
-            if (!on[s]) continue;
-            const float sc = (LAYOUT == Q_GROUP_K) ? sc_of<DT>(b[i][s].s[j >> 1], j) : scol[s];
-            const f32x4 t = T::mfma(a[i][j], b_op<DT, LAYOUT>(b[i][s], j, par), corr);
-            acc[s][0] = fmaf(sc, t[0], acc[s][0]);
-            acc[s][1] = fmaf(sc, t[1], acc[s][1]);
-            acc[s][2] = fmaf(sc, t[2], acc[s][2]);
-            acc[s][3] = fmaf(sc, t[3], acc[s][3]);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) s_red[w][s][lane] = acc[s];
-    __syncthreads();
-    if (w == 0) {
-      f32x4 v[NSUB];
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        v[s] = s_red[0][s][lane];
-        for (int q = 1; q < kDecWaves; ++q) {
-          const f32x4 u = s_red[q][s][lane];
-          v[s][0] += u[0]; v[s][1] += u[1]; v[s][2] += u[2]; v[s][3] += u[3];
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + 4 * g + i;
-        if (m >= M) continue;
-        const int64_t orow = p.act_by_route ? s_rows[m] : static_cast<int64_t>(blockIdx.x) * 16 + m;
-        uint16_t* o = p.act + orow * p.ldo;
-        if constexpr (GATED) {
-          if (on[0]) o[(col[0] & ~7) | a_pos(col[0] & 7)] =
-              T::from_f32(silu(16.0f * v[0][i]) * (16.0f * v[1][i]));
-        } else {
-#pragma unroll
-          for (int s = 0; s < NSUB; ++s) {
-            if (!on[s]) continue;
-            const float h = fmaxf(16.0f * v[s][i], 0.0f);
-            o[(col[s] & ~7) | a_pos(col[s] & 7)] = T::from_f32(h * h);
-          }
-        }
-      }
-    }
-    __syncthreads();
-  }
-}
 
 // ---------------------------------------------------------------------------
 // small batch gate/up (T*K <= 64): pre-activations h = x W13^T in FP32 for one
@@ -684,36 +466,6 @@ static hipError_t allow_lds(F* kernel, size_t lds) {
   if (lds <= 65536) return hipSuccess;
   return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-}
-
-// ---------------------------------------------------------------------------
-template <int DT, int LAYOUT, bool GATED>
-static hipError_t launch_dec_up_nkb(const DecodeUpParams& p, int nkb, dim3 grid, hipStream_t st) {
-  switch (nkb) {
-    case 1: hipLaunchKernelGGL((decode_up_kernel<DT, LAYOUT, GATED, 1>), grid, dim3(kDecThreads), 0, st, p); break;
-    case 2: hipLaunchKernelGGL((decode_up_kernel<DT, LAYOUT, GATED, 2>), grid, dim3(kDecThreads), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((decode_up_kernel<DT, LAYOUT, GATED, 4>), grid, dim3(kDecThreads), 0, st, p); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-template <int DT, int LAYOUT>
-static hipError_t launch_dec_up_g(const DecodeUpParams& p, bool gated, int nkb, dim3 grid,
-                                  hipStream_t st) {
-  return gated ? launch_dec_up_nkb<DT, LAYOUT, true>(p, nkb, grid, st)
-               : launch_dec_up_nkb<DT, LAYOUT, false>(p, nkb, grid, st);
-}
-
-hipError_t launch_decode_up(const DecodeUpParams& p, int dtype, int layout, bool gated, int nkb,
-                            int grid_x, hipStream_t stream) {
-  const int n_tiles = gated ? (p.n_cols + 15) / 16 : (p.n_cols + 31) / 32;
-  const dim3 grid(grid_x, n_tiles);
-  if (dtype == DT_BF16)
-    return layout == Q_GROUP_K ? launch_dec_up_g<DT_BF16, Q_GROUP_K>(p, gated, nkb, grid, stream)
-                               : launch_dec_up_g<DT_BF16, Q_PER_CHANNEL>(p, gated, nkb, grid, stream);
-  return layout == Q_GROUP_K ? launch_dec_up_g<DT_FP16, Q_GROUP_K>(p, gated, nkb, grid, stream)
-                             : launch_dec_up_g<DT_FP16, Q_PER_CHANNEL>(p, gated, nkb, grid, stream);
 }
 
 

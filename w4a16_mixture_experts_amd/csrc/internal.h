@@ -8,11 +8,6 @@ namespace w4moe {
 
 enum : int { MODE_UP_GATED = 0, MODE_UP_RELU2 = 1, MODE_DOWN = 2 };
 
-// Columns of the output one workgroup covers (4 waves).
-//   gated gate/up: 16 logical columns per wave (a gate and an up subtile)
-//   otherwise:     32 columns per wave (two subtiles)
-constexpr int kWgColsGated = 64;
-constexpr int kWgColsPlain = 128;
 constexpr int kCombineCols = 2048;
 constexpr int kTileRows = 64;        // route positions of one LDS-staged expert tile
 constexpr int kTileWaves = 8;
@@ -53,7 +48,6 @@ struct GemmParams {
 };
 
 // small-batch path
-constexpr int kDecMaxRows = 256;          // routes the row scan handles (T*K)
 constexpr int kDecMaxItems = 256;         // (route, slice) items per token
 constexpr int kDecDownSliceBlocks = 2;    // 128-blocks of the reduction per item
 // small-batch gate/up kernel (pre-activations h in FP32)
@@ -80,28 +74,6 @@ struct SmallHParams {
   int kslice;                 // per-wave slice of K, multiple of 128
   float* h;                   // [R][ldh] pre-activations (route-indexed)
   int ldh;                    // N1
-};
-
-struct DecodeUpParams {
-  const uint16_t* x;          // [T][lda]
-  int lda;
-  const int32_t* ids;         // [R] global ids (rows_from_ids)
-  int R, top_k, E, off;
-  int rows_from_ids;          // 1: rows = routes of one expert found in ids
-  const int32_t* sorted;      // rows_from_ids == 0: 16-row tiles of the route list
-  const int32_t* tile_expert;
-  const int32_t* offsets;
-  const uint8_t* wq;
-  const uint16_t* ws;
-  int64_t wq_expert_bytes;
-  int64_t ws_expert_elems;
-  int K;                      // reduction length (H)
-  int kslice;                 // per-wave slice of K, multiple of 128
-  int n_cols;                 // I
-  int up_rows;                // gated: I
-  uint16_t* act;              // activation rows (A operand order)
-  int ldo;
-  int act_by_route;           // 1: row = route index, 0: row = tile position
 };
 
 struct DecodeDownParams {
@@ -141,9 +113,6 @@ hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, 
                              int32_t* offsets, int32_t* sorted, int32_t* slot,
                              int32_t* tile_expert, int32_t* chunk_hist, hipStream_t stream);
 
-hipError_t launch_grouped_gemm(const GemmParams& p, int dtype, int layout, int ms, int mode,
-                               int max_tiles, hipStream_t stream);
-
 // 64-row expert tiles (route positions), LDS-staged activations
 constexpr int kResidentK = 256;      // reduction the resident down kernel holds in LDS
 constexpr int kSplitkNsub = 2;       // 16-row weight subtiles per wave in the split-K kernel
@@ -165,9 +134,6 @@ constexpr int kTileRedoWorkgroups = 8;
 inline int64_t tile_launch_workgroups(int n_tiles, int64_t max_tiles) {
   return 8 * static_cast<int64_t>(n_tiles) * ((max_tiles + 7) / 8);
 }
-
-hipError_t launch_decode_up(const DecodeUpParams& p, int dtype, int layout, bool gated, int nkb,
-                            int grid_x, hipStream_t stream);
 
 hipError_t launch_small_h(const SmallHParams& p, int dtype, int layout, int nkb, int n1,
                           hipStream_t stream);

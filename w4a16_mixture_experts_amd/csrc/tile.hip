@@ -356,8 +356,8 @@ __device__ __forceinline__ uint32_t dequant_pair_f16(uint32_t q2, f16x2 s16, f16
 }
 
 // bf16 magnitudes (sign cleared) of the group scales the fp16 route takes:
-// 2^-17 (0x3700) to 2720 (0x452A); a zero scale, exact as well, is sent to
-// the rerun too (one compare per scale instead of two)
+// 0, and 2^-17 (0x3700) to 2720 (0x452A); q * 0 is exact, so all-zero
+// groups (zero-padded or pruned weights) stay on the route
 constexpr uint32_t kX16ScaleLo = 0x3700u;
 constexpr uint32_t kX16ScaleEnd = 0x452Bu;
 
@@ -416,7 +416,7 @@ __device__ __forceinline__ void mma_block_x(const uint16_t* sa, int stride,
   for (int s = 0; s < NSUB; ++s) {
     const uint32_t dw = (g & 2) ? wb[s].s1 : wb[s].s0;
     const uint32_t mag = __builtin_amdgcn_ubfe(dw, 16 * (g & 1), 15);
-    sbad |= mag - kX16ScaleLo >= kX16ScaleEnd - kX16ScaleLo;  // 0 included: rerun, still exact
+    sbad |= (mag - kX16ScaleLo >= kX16ScaleEnd - kX16ScaleLo) & (mag != 0u);
   }
 }
 
