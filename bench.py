@@ -267,13 +267,97 @@ def cpu_baseline(wl, Wg, budget_s, min_s):
     return res, oracle.max_threads(), passes
 
 
+
+# SQ counters of one --counter-pass run under rocprofv3 --pmc (one pass: 8 SQ
+# counters and GRBM_GUI_ACTIVE).  MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES (summed
+# over the 1024 SIMDs) / (GRBM_GUI_ACTIVE of one XCD * 1024), the form of
+# rocprofv3's derived MfmaUtil; the CSV holds GRBM_GUI_ACTIVE summed over the
+# 8 XCDs.  Counted MFMA flops are the MOPS counters times 512 (their unit).
+SQ_SET = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+          "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
+          "SQ_LDS_BANK_CONFLICT", "SQ_WAVES")
+SIMDS = 256 * 4
+XCDS = 8
+GPU_CLOCK_GHZ = 2.4
+
+
+def summarize_sq(args, sweep):
+    """A text table per kernel and token count from the counter CSV of a
+    --counter-pass run (launches in sweep order, --steps per T)."""
+    import csv
+    import re
+
+    with open(args.summarize_sq) as f:
+        rows = list(csv.DictReader(f))
+    by_disp = {}
+    for r in rows:
+        d = by_disp.setdefault(r["Dispatch_Id"], {"kernel": r["Kernel_Name"], "c": {},
+                                                  "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    disp = [by_disp[k] for k in sorted(by_disp, key=int)]
+    # dispatches come in sweep order: each forward launches the same kernel
+    # sequence for a T, --steps times
+    def short(k):
+        return re.sub(r"\(w4moe::\w+\)$", "", k.replace("void w4moe::", ""))
+
+    # split into forwards: the first kernel of a forward is route preparation
+    # (grouped path) or small_h_kernel (small batch); a chunked preparation
+    # is two launches, rank then scatter
+    starts = [j for j, d in enumerate(disp)
+              if "rp_one" in d["kernel"] or "rp_rank" in d["kernel"]
+              or "small_h_kernel" in d["kernel"]]
+    fwd = [disp[a:b] for a, b in zip(starts, starts[1:] + [len(disp)])]
+    if len(fwd) != args.steps * len(sweep):
+        raise SystemExit(f"{len(fwd)} forwards in the counter file, expected {args.steps} x {len(sweep)}")
+    lines = []
+    agg = {}
+    for ti, T in enumerate(sweep):
+        for f in fwd[ti * args.steps:(ti + 1) * args.steps]:
+            for d in f:
+                a = agg.setdefault((T, short(d["kernel"])), {"n": 0, "ns": 0.0, "c": {}})
+                a["n"] += 1
+                a["ns"] += d["ns"]
+                for k, v in d["c"].items():
+                    a["c"][k] = a["c"].get(k, 0.0) + v
+    hdr = ("T", "kernel", "us/launch", "MFMA busy %", "MFMA TFLOP/s counted", "frac of 2.5 PF",
+           "VALU insts", "MFMA insts", "VALU:MFMA", "LDS insts", "LDS bank-conflict cycles")
+    lines.append(" | ".join(hdr))
+    for (T, k), a in agg.items():
+        n = a["n"]
+        c = {kk: v / n for kk, v in a["c"].items()}
+        us = a["ns"] / n / 1e3
+        gui = c.get("GRBM_GUI_ACTIVE", 0.0)
+        # GRBM_GUI_ACTIVE comes summed over the XCDs' GRBM instances
+        util = 100.0 * c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (gui / XCDS * SIMDS) if gui else 0.0
+        flops = 512.0 * (c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + c.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0))
+        tf = flops / (us * 1e-6) / 1e12 if us > 0 else 0.0
+        valu, mfma = c.get("SQ_INSTS_VALU", 0.0), c.get("SQ_INSTS_MFMA", 0.0)
+        lines.append(" | ".join([str(T), k, f"{us:.1f}", f"{util:.1f}", f"{tf:.1f}",
+                                 f"{tf / MFMA_PEAK_TFLOPS['bf16']:.3f}", f"{valu:.3e}",
+                                 f"{mfma:.3e}", f"{valu / mfma:.2f}" if mfma else "-",
+                                 f"{c.get('SQ_INSTS_LDS', 0.0):.3e}",
+                                 f"{c.get('SQ_LDS_BANK_CONFLICT', 0.0):.3e}"]))
+    print("\n".join(lines))
+
+
+def sweep_of(wl, args, headline):
+    if headline and args.tokens:
+        return [int(t) for t in args.tokens.split(",")]
+    return list(wl.tokens)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="kimi_tp8")
-    ap.add_argument("--tokens", default="", help="comma list (default: the workload's sweep)")
+    ap.add_argument("--workloads", default="kimi_tp8,deepseek_local,per_channel,relu2_skew,tiny",
+                    help="comma list; the first is the headline (value, roofline, cpu_baseline), "
+                         "the others are reported under other_workloads")
+    ap.add_argument("--workload", default="kimi_tp8",
+                    help="workload of --counter-pass / --summarize-* runs")
+    ap.add_argument("--tokens", default="", help="comma list for the headline workload "
+                                                 "(default: its sweep)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0,
                     help="stop the CPU oracle baseline once this much CPU time is spent")
@@ -285,6 +369,8 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from the counter_collection.csv files of "
                          "a --counter-pass run under rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE")
+    ap.add_argument("--summarize-sq", metavar="CSV",
+                    help="print a table of the SQ counters (SQ_SET) of a --counter-pass run")
     ap.add_argument("--counter-pass", action="store_true",
                     help="host-built inputs and library calls only (for counter runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -301,35 +387,26 @@ def main():
 
     from w4a16_mixture_experts_amd import binding, synth
 
-    if args.summarize_counters:
+    if args.summarize_counters or args.summarize_sq:
         sweep = [int(t) for t in args.tokens.split(",")] if args.tokens else \
             list(synth.WORKLOADS[args.workload].tokens)
-        summarize_counters(args, sweep)
+        if args.summarize_counters:
+            summarize_counters(args, sweep)
+        else:
+            summarize_sq(args, sweep)
         return
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    wl = synth.WORKLOADS[args.workload]
-    sweep = [int(t) for t in args.tokens.split(",")] if args.tokens else list(wl.tokens)
-    dtype_name = "fp16" if wl.dtype == torch.float16 else "bf16"
 
     if args.counter_pass:
+        wl = synth.WORKLOADS[args.workload]
+        sweep = [int(t) for t in args.tokens.split(",")] if args.tokens else list(wl.tokens)
         counter_pass(args, wl, sweep, dev)
         return
 
-    if args.copy_calibration_mib:
-        n = args.copy_calibration_mib * 1024 * 1024 // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        log(f"[bench] copy calibration: 3 x {args.copy_calibration_mib} MiB read + written")
-        del src, dst
-
-    log(f"[bench] generating {wl.name} weights on the GPU")
-    Wg = synth.make_weights(wl, device=dev)
+    names = [n for n in args.workloads.split(",") if n]
     flush_rows = torch.ones(16384, 8192, dtype=torch.int32, device=dev)   # 512 MiB
     flush_out = torch.empty(16384, dtype=torch.int32, device=dev)
 
@@ -354,110 +431,117 @@ def main():
         return g
 
     graph_flush = None if args.no_graph else capture(lambda: [flush() for _ in range(G)])
-
     torch.cuda.synchronize()
 
-    cases = []
-    for T in sweep:
-        tok = synth.make_tokens(wl, T).to(dev)
-        desc = binding.desc_for(wl, T)
-        plan = binding.get_plan(desc)
-        ws = torch.empty(max(1, binding.workspace_size(desc)), dtype=torch.uint8, device=dev)
-        out = torch.empty(T, wl.hidden, dtype=wl.dtype, device=dev)
+    def cold_graph(fn):
+        def body(fn=fn):
+            for _ in range(G):
+                flush()
+                fn()
+        return None if args.no_graph else capture(body)
 
-        def fwd(tok=tok, ws=ws, out=out, **kw):
-            return binding.forward_workload(wl, Wg, tok, out=out, workspace=ws, **kw)
+    # the streaming-read probe reads a buffer of the weight bytes a forward
+    # streams; one buffer as large as the largest such count
+    weights, cases = {}, []
+    for wi, name in enumerate(names):
+        wl = synth.WORKLOADS[name]
+        log(f"[bench] generating {wl.name} weights on the GPU")
+        Wg = synth.make_weights(wl, device=dev)
+        weights[name] = Wg
+        for T in sweep_of(wl, args, wi == 0):
+            tok = synth.make_tokens(wl, T).to(dev)
+            desc = binding.desc_for(wl, T)
+            plan = binding.get_plan(desc)
+            ws = torch.empty(max(1, binding.workspace_size(desc)), dtype=torch.uint8, device=dev)
+            out = torch.empty(T, wl.hidden, dtype=wl.dtype, device=dev)
 
-        fwd()
-        torch.cuda.synchronize()
-        g_cold = g_warm = None
-        if not args.no_graph:
-            def cold_body(fwd=fwd):
-                for _ in range(G):
-                    flush()
-                    fwd()
+            def fwd(tok=tok, ws=ws, out=out, Wg=Wg, wl=wl, **kw):
+                return binding.forward_workload(wl, Wg, tok, out=out, workspace=ws, **kw)
 
-            def warm_body(fwd=fwd):
-                for _ in range(G):
-                    fwd()
+            fwd()
+            torch.cuda.synchronize()
+            g_cold = cold_graph(fwd)
+            g_warm = None
+            if not args.no_graph:
+                def warm_body(fwd=fwd):
+                    for _ in range(G):
+                        fwd()
+                g_warm = capture(warm_body)
+            # router scoring + top-k on the same token batch (context: the step
+            # before the timed forward), timed the same way
+            ids_r = torch.empty(T, wl.top_k, dtype=torch.int32, device=dev)
+            w_r = torch.empty(T, wl.top_k, dtype=torch.float32, device=dev)
 
-            g_cold = capture(cold_body)
-            g_warm = capture(warm_body)
-        # router scoring + top-k on the same token batch (context: the step
-        # before the timed forward), timed the same way
-        ids_r = torch.empty(T, wl.top_k, dtype=torch.int32, device=dev)
-        w_r = torch.empty(T, wl.top_k, dtype=torch.float32, device=dev)
+            def route(tok=tok, ids_r=ids_r, w_r=w_r, k=wl.top_k):
+                return binding.route_topk(tok.logits, k, out=(ids_r, w_r))
 
-        def route(tok=tok, ids_r=ids_r, w_r=w_r):
-            return binding.route_topk(tok.logits, wl.top_k, out=(ids_r, w_r))
+            route()
+            g_route = cold_graph(route)
+            stage_b, total_b, total_f, stage_f, D, Rv = workload_bytes_flops(
+                wl, tok.topk_ids.cpu(), T)
+            cases.append(dict(wl=wl, head=wi == 0, T=T, tok=tok, fwd=fwd, g_cold=g_cold,
+                              g_warm=g_warm, plan=plan, route=route, g_route=g_route, router=[],
+                              stage_bytes=stage_b, bytes=total_b, flops=total_f,
+                              stage_flops=stage_f, D=D, Rv=Rv,
+                              wbytes=D * weight_bytes_per_expert(wl),
+                              cold=[], warm=[], probe=[], stages={s: [] for s in STAGES}))
+            log(f"[bench] {wl.name} T={T}: plan path={plan.path} splitk={plan.splitk_chunks} "
+                f"k_slice={plan.k_slice} touched experts={D}")
 
-        route()
-        g_route = None
-        if not args.no_graph:
-            def route_body(route=route):
-                for _ in range(G):
-                    flush()
-                    route()
+    pbytes = max(c["wbytes"] for c in cases)
+    probe_buf = torch.zeros(pbytes + 8192, dtype=torch.uint8, device=dev)
+    probe_sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for c in cases:
+        row = probe_row_bytes(c["wl"])
+        nb = c["wbytes"] // row * row
 
-            g_route = capture(route_body)
-        stage_b, total_b, total_f, stage_f, D, Rv = workload_bytes_flops(wl, tok.topk_ids.cpu(), T)
-        cases.append(dict(T=T, tok=tok, fwd=fwd, g_cold=g_cold, g_warm=g_warm, plan=plan,
-                          route=route, g_route=g_route, router=[],
-                          stage_bytes=stage_b,
-                          bytes=total_b, flops=total_f, stage_flops=stage_f, D=D, Rv=Rv,
-                          cold=[], warm=[], stages={s: [] for s in STAGES}))
-        log(f"[bench] T={T}: plan path={plan.path} block_m={plan.block_m} "
-            f"k_slice={plan.k_slice} touched experts={D}")
+        def probe(nb=nb, row=row):
+            binding.stream_probe(probe_buf, nb, row, probe_sink)
+
+        probe()
+        c["g_probe"] = cold_graph(probe)
+        c["probe_fn"] = probe
+        c["probe_bytes"] = nb
+    torch.cuda.synchronize()
 
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     ev2 = torch.cuda.Event(enable_timing=True)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
 
+    def time_cold(g, fn):
+        """Device time of fn on cold caches: graph difference, or eager."""
+        if g is not None:
+            ev0.record()
+            graph_flush.replay()
+            ev1.record()
+            g.replay()
+            ev2.record()
+            ev2.synchronize()
+            return (ev1.elapsed_time(ev2) - ev0.elapsed_time(ev1)) * 1e3 / G
+        flush()
+        ev0.record()
+        fn()
+        ev1.record()
+        ev1.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3
+
     def step(record):
         for c in cases:
-            if c["g_cold"] is not None:
-                # G x (evict, forward) minus G x (evict): per-forward device time
-                # without the per-launch submission latency
-                ev0.record()
-                graph_flush.replay()
-                ev1.record()
-                c["g_cold"].replay()
-                ev2.record()
-            else:
-                flush()
-                ev0.record()
-                c["fwd"]()
-                ev1.record()
+            t_cold = time_cold(c["g_cold"], c["fwd"])
             flush()
             c["fwd"](stage_events=evs)
             evs[7 if c["plan"].path == 1 else 5].synchronize()
+            t_route = time_cold(c["g_route"], c["route"])
+            t_probe = time_cold(c["g_probe"], c["probe_fn"])
             if record:
-                if c["g_cold"] is not None:
-                    c["cold"].append((ev1.elapsed_time(ev2) - ev0.elapsed_time(ev1)) * 1e3 / G)
-                else:
-                    c["cold"].append(ev0.elapsed_time(ev1) * 1e3)
+                c["cold"].append(t_cold)
+                c["router"].append(t_route)
+                c["probe"].append(t_probe)
                 for si, name in enumerate(STAGES):
                     if name in ("route_prep", "combine") and c["plan"].path == 2:
                         continue
                     c["stages"][name].append(evs[2 * si].elapsed_time(evs[2 * si + 1]) * 1e3)
-            # router, cold, outside the forward's timing
-            if c["g_route"] is not None:
-                ev0.record()
-                graph_flush.replay()
-                ev1.record()
-                c["g_route"].replay()
-                ev2.record()
-            else:
-                flush()
-                ev0.record()
-                c["route"]()
-                ev1.record()
-                ev2.record()
-            ev2.synchronize()
-            if record:
-                c["router"].append(((ev1.elapsed_time(ev2) - ev0.elapsed_time(ev1)) / G
-                                    if c["g_route"] is not None else ev0.elapsed_time(ev1)) * 1e3)
 
     for _ in range(args.warmup):
         step(False)
@@ -482,58 +566,78 @@ def main():
             ev1.synchronize()
             c["warm"].append(ev0.elapsed_time(ev1) * 1e3 / G)
 
-    lat_cold = {c["T"]: statistics.fmean(c["cold"]) for c in cases}
-    lat_warm = {c["T"]: statistics.median(c["warm"]) for c in cases}
-    geo = math.exp(sum(math.log(v) for v in lat_cold.values()) / len(lat_cold))
-    table = {}
-    per_kernel = {}   # kernel -> list of (duration us, algorithmic bytes, flops) per launch
-    for c in cases:
-        T = c["T"]
-        st = {k: statistics.fmean(v) for k, v in c["stages"].items() if v}
-        down_key = "down_gemm_fused" if c["plan"].path == 2 else "down_gemm"
-        row = {
-            "latency_us_cold": round(lat_cold[T], 3),
-            "latency_us_cold_median": round(statistics.median(c["cold"]), 3),
-            "latency_us_warm": round(lat_warm[T], 3),
-            "hbm_gbps_cold": round(c["bytes"] / lat_cold[T] / 1e3, 1),
-            "hbm_frac_cold": round(c["bytes"] / lat_cold[T] / 1e3 / HBM_PEAK_GBS, 4),
-            "tflops_cold": round(c["flops"] / lat_cold[T] / 1e6, 2),
-            "mfma_frac_cold": round(c["flops"] / lat_cold[T] / 1e6 / MFMA_PEAK_TFLOPS[dtype_name], 4),
-            "algorithmic_bytes": int(c["bytes"]),
-            "touched_experts": c["D"],
-            "valid_routes": c["Rv"],
-            "plan": {"path": "small-batch" if c["plan"].path == 2 else "grouped",
-                     "block_m": c["plan"].block_m, "k_slice": c["plan"].k_slice},
-            "stage_us": {k: round(v, 3) for k, v in st.items()},
-            "router_us_cold": round(statistics.fmean(c["router"]), 3) if c["router"] else None,
-            "stage_kernel": {k: kernel_name(wl, c["plan"], k) for k in st},
-        }
-        for k, v in st.items():
-            key = down_key if k == "down_gemm" else k
-            if key in c["stage_bytes"] and v > 0:
-                row.setdefault("stage_gbps", {})[k] = round(c["stage_bytes"][key] / v / 1e3, 1)
-                per_kernel.setdefault(kernel_name(wl, c["plan"], k), []).append(
-                    (v, c["stage_bytes"][key], c["stage_flops"].get(key, 0.0), T))
-        table[str(T)] = row
-
-    # dominant kernel: largest summed duration over the sweep; achieved = mean
-    # algorithmic bytes per launch / mean launch duration
-    kname, launches = max(per_kernel.items(), key=lambda kv: sum(x[0] for x in kv[1]))
-    dur = statistics.fmean(x[0] for x in launches)
-    bts = statistics.fmean(x[1] for x in launches)
-    fl = statistics.fmean(x[2] for x in launches)
-    achieved = bts / dur / 1e3
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+    def report(wcases):
+        wl = wcases[0]["wl"]
+        dtype_name = "fp16" if wl.dtype == torch.float16 else "bf16"
+        lat_cold = {c["T"]: statistics.fmean(c["cold"]) for c in wcases}
+        lat_warm = {c["T"]: statistics.median(c["warm"]) for c in wcases}
+        geo = math.exp(sum(math.log(v) for v in lat_cold.values()) / len(lat_cold))
+        table = {}
+        per_kernel = {}   # kernel -> list of (duration us, algorithmic bytes, flops, T) per launch
+        for c in wcases:
+            T = c["T"]
+            st = {k: statistics.fmean(v) for k, v in c["stages"].items() if v}
+            down_key = "down_gemm_fused" if c["plan"].path == 2 else "down_gemm"
+            pr = statistics.fmean(c["probe"])
+            row = {
+                "latency_us_cold": round(lat_cold[T], 3),
+                "latency_us_cold_median": round(statistics.median(c["cold"]), 3),
+                "latency_us_warm": round(lat_warm[T], 3),
+                "hbm_gbps_cold": round(c["bytes"] / lat_cold[T] / 1e3, 1),
+                "hbm_frac_cold": round(c["bytes"] / lat_cold[T] / 1e3 / HBM_PEAK_GBS, 4),
+                "tflops_cold": round(c["flops"] / lat_cold[T] / 1e6, 2),
+                "mfma_frac_cold": round(c["flops"] / lat_cold[T] / 1e6 /
+                                        MFMA_PEAK_TFLOPS[dtype_name], 4),
+                "algorithmic_bytes": int(c["bytes"]),
+                "touched_experts": c["D"],
+                "valid_routes": c["Rv"],
+                "plan": {"path": "small-batch" if c["plan"].path == 2 else "grouped",
+                         "splitk_chunks": c["plan"].splitk_chunks,
+                         "fp16_route": c["plan"].fp16_route},
+                "stage_us": {k: round(v, 3) for k, v in st.items()},
+                "router_us_cold": round(statistics.fmean(c["router"]), 3),
+                "stream_probe": {"bytes": c["probe_bytes"], "us_cold": round(pr, 3),
+                                 "gbps": round(c["probe_bytes"] / pr / 1e3, 1),
+                                 "frac": round(c["probe_bytes"] / pr / 1e3 / HBM_PEAK_GBS, 4),
+                                 "forward_over_probe": round(lat_cold[T] / pr, 3)},
+                "stage_kernel": {k: kernel_name(wl, c["plan"], k) for k in st},
+            }
+            for k, v in st.items():
+                key = down_key if k == "down_gemm" else k
+                if key in c["stage_bytes"] and v > 0:
+                    row.setdefault("stage_gbps", {})[k] = round(c["stage_bytes"][key] / v / 1e3, 1)
+                    per_kernel.setdefault(kernel_name(wl, c["plan"], k), []).append(
+                        (v, c["stage_bytes"][key], c["stage_flops"].get(key, 0.0), T))
+            table[str(T)] = row
+        # dominant kernel: largest summed duration over the sweep; achieved =
+        # mean algorithmic bytes per launch / mean launch duration
+        kname, launches = max(per_kernel.items(), key=lambda kv: sum(x[0] for x in kv[1]))
+        dur = statistics.fmean(x[0] for x in launches)
+        bts = statistics.fmean(x[1] for x in launches)
+        fl = statistics.fmean(x[2] for x in launches)
+        achieved = bts / dur / 1e3
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(kname, [x[3] for x in launches]),
                 "kernel": kname, "tokens": [x[3] for x in launches],
                 "avg_launch_us": round(dur, 3),
                 "algorithmic_bytes_per_launch": int(bts),
                 "mfma_frac": round(fl / dur / 1e6 / MFMA_PEAK_TFLOPS[dtype_name], 4)}
+        return wl, dtype_name, lat_cold, geo, table, roof
+
+    head_cases = [c for c in cases if c["head"]]
+    wl, dtype_name, lat_cold, geo, table, roofline = report(head_cases)
+    others = {}
+    for name in names[1:]:
+        wc = [c for c in cases if c["wl"].name == name]
+        owl, odt, olat, ogeo, otable, oroof = report(wc)
+        others[name] = {"workload": describe(owl), "dtype": odt, "tokens": list(olat),
+                        "geomean_us_cold": round(ogeo, 3), "per_tokens": otable,
+                        "dominant_kernel": oroof}
 
     cpu = None
     if not args.no_cpu_baseline:
-        res, cores, passes = cpu_baseline(wl, Wg, args.cpu_budget_s, args.cpu_min_s)
+        res, cores, passes = cpu_baseline(wl, weights[wl.name], args.cpu_budget_s, args.cpu_min_s)
         done = sorted(res)
         gpu_same = math.exp(sum(math.log(lat_cold[t]) for t in done) / len(done))
         cpu_geo = math.exp(sum(math.log(res[t]) for t in done) / len(done))
@@ -551,18 +655,15 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(sum(lat_cold.values()) / 1e3, 4),
+        "ms_per_step": round(sum(statistics.fmean(c["cold"]) for c in cases) / 1e3, 4),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": dtype_name,
         "data": "synthetic",
         "config": {
-            "workload": f"{wl.name}: {wl.num_experts} local experts (of {wl.num_global_experts}), "
-                        f"hidden {wl.hidden}, intermediate {wl.inter}, top-{wl.top_k}, "
-                        f"INT4 {'per-channel' if wl.per_channel else 'group-32'}, "
-                        f"{'SiLU-gated' if wl.gated else 'ReLU^2'}",
-            "tokens": sweep,
+            "workload": describe(wl),
+            "tokens": list(lat_cold),
             "value_definition": "geometric mean over the token sweep of the cold-cache "
                                 "device time of one forward: (graph of G x (cache eviction, "
                                 "forward) - graph of G x eviction) / G, mean over the timed "
@@ -571,11 +672,36 @@ def main():
             "parallelism": "single GPU",
             "per_tokens": table,
             "wall_s_timed_region": round(wall, 3),
+            "step": "one cold forward at every token count of every listed workload "
+                    "(the headline and other_workloads), plus the router and the "
+                    "streaming-read probe at the same token counts",
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "other_workloads": others,
     }
     print(json.dumps(line), flush=True)
+
+
+def describe(wl):
+    return (f"{wl.name}: {wl.num_experts} local experts (of {wl.num_global_experts}), "
+            f"hidden {wl.hidden}, intermediate {wl.inter}, top-{wl.top_k}, "
+            f"INT4 {'per-channel' if wl.per_channel else 'group-32'}, "
+            f"{'SiLU-gated' if wl.gated else 'ReLU^2'}")
+
+
+def weight_bytes_per_expert(wl):
+    E, H, I, N1 = wl.num_experts, wl.hidden, wl.inter, wl.n1
+    if wl.per_channel:
+        return N1 * H // 2 + N1 * 2 + H * I // 2 + H * 2
+    return N1 * H // 2 + N1 * (H // 32) * 2 + H * I // 2 + H * (I // 32) * 2
+
+
+def probe_row_bytes(wl):
+    """Row length of the probe: a packed gate/up weight row (H/2 bytes in the
+    group layout, H bytes per channel pair), rounded down to 64 bytes."""
+    r = wl.hidden if wl.per_channel else wl.hidden // 2
+    return max(64, min(8192, r // 64 * 64))
 
 
 if __name__ == "__main__":

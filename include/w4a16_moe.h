@@ -240,6 +240,20 @@ w4a16_status_t w4a16_moe_route_topk(const float* logits, int64_t num_tokens,
                                     int32_t renormalize, int32_t* topk_ids, float* topk_weights,
                                     w4a16_stream_t stream);
 
+/* Streaming-read probe (a measurement aid, not part of the forward): reads
+ * the first (bytes / row_bytes) * row_bytes bytes of `buf` once, with the
+ * access shape of the packed-weight stream (16 rows x 64 bytes per wave load
+ * instruction, rows of row_bytes, the 8 waves of a workgroup splitting each
+ * 16-row band), so that its time beside the forward's gives the achievable
+ * HBM read rate for the weight bytes a forward streams ([P2] Final
+ * performance times on cold caches; the weight stream is the roofline).
+ *   buf       device, 16-byte aligned, at least `bytes` long
+ *   row_bytes a multiple of 64, at most 8192
+ *   sink      device uint32; written only for one improbable data value
+ * Errors are returned before anything is enqueued. */
+w4a16_status_t w4a16_stream_probe(const uint8_t* buf, int64_t bytes, int32_t row_bytes,
+                                  uint32_t* sink, w4a16_stream_t stream);
+
 /* Static text for a status code (unsupported configurations are strict
  * errors, not silent fallbacks: [P1] BC-breaking).  Never null; an unknown
  * code gives "unknown status". */

@@ -67,12 +67,14 @@ def lib():
     L.w4a16_moe_prepare_routes.argtypes = [pdesc, P, i32, P, P, P, i64, P, P, P]
     L.w4a16_unpack_int4.argtypes = [P, i64, P, P]
     L.w4a16_moe_route_topk.argtypes = [P, i64, i32, i32, i32, P, P, P]
+    L.w4a16_stream_probe.argtypes = [P, i64, i32, P, P]
     L.w4a16_status_string.argtypes = [i32]
     L.w4a16_status_string.restype = ctypes.c_char_p
     L.w4a16_last_error_message.restype = ctypes.c_char_p
     for f in ("w4a16_moe_workspace_size", "w4a16_moe_get_plan", "w4a16_moe_forward",
               "w4a16_moe_forward_timed",
-              "w4a16_moe_prepare_routes", "w4a16_unpack_int4", "w4a16_moe_route_topk"):
+              "w4a16_moe_prepare_routes", "w4a16_unpack_int4", "w4a16_moe_route_topk",
+              "w4a16_stream_probe"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -277,3 +279,12 @@ def route_topk(logits: torch.Tensor, top_k: int, renormalize: bool = False, out=
     _check(lib().w4a16_moe_route_topk(_ptr(logits), T, Eg, top_k, 1 if renormalize else 0,
                                       _ptr(ids), _ptr(wts), _stream(stream)))
     return ids, wts
+
+
+def stream_probe(buf: torch.Tensor, nbytes: int, row_bytes: int, sink: torch.Tensor, stream=None):
+    """Streaming-read probe over the first nbytes of buf (uint8, GPU)."""
+    _dev("buf", buf, (torch.uint8,))
+    _dev("sink", sink, (torch.int32,), buf.device)
+    if nbytes > buf.numel():
+        raise ValueError(f"nbytes: {nbytes} exceeds buf ({buf.numel()} bytes)")
+    _check(lib().w4a16_stream_probe(_ptr(buf), nbytes, row_bytes, _ptr(sink), _stream(stream)))

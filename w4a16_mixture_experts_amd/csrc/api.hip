@@ -231,7 +231,7 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
     pl.off_sorted = take(sizeof(int32_t) * std::max<int64_t>(pl.P, 1));
     pl.off_tile = take(sizeof(int32_t) * std::max<int64_t>(pl.MT, 1));
     pl.off_act = take(sizeof(uint16_t) * pl.P * I);
-    pl.off_y = take(sizeof(uint16_t) * pl.P * H);
+    pl.off_y = take(sizeof(uint16_t) * std::max<int64_t>(pl.R, 1) * H);  // Y rows by route
     if (pl.splitk_S > 0)
       pl.off_part = take(sizeof(float) * static_cast<size_t>(pl.splitk_S) * pl.R * pl.N1);
     // rerun flags of the fp16-route launches: the gate/up launch's, then the
@@ -635,6 +635,23 @@ w4a16_status_t w4a16_unpack_int4(const uint8_t* packed, int64_t n_bytes, int8_t*
     return fail(W4A16_ERR_UNSUPPORTED, "n_bytes: %lld too large", (long long)n_bytes);
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   return hip_status(w4moe::launch_unpack(packed, n_bytes, out, stream), "unpack launch");
+}
+
+w4a16_status_t w4a16_stream_probe(const uint8_t* buf, int64_t bytes, int32_t row_bytes,
+                                  uint32_t* sink, w4a16_stream_t stream_) {
+  if (row_bytes <= 0 || row_bytes % 64 != 0 || row_bytes > w4moe::kProbeMaxRowBytes)
+    return fail(W4A16_ERR_INVALID_ARG, "row_bytes: %d (a multiple of 64, at most %d)", row_bytes,
+                w4moe::kProbeMaxRowBytes);
+  if (bytes < row_bytes)
+    return fail(W4A16_ERR_INVALID_ARG, "bytes: %lld below one row", (long long)bytes);
+  if (bytes / row_bytes > (int64_t(1) << 34))
+    return fail(W4A16_ERR_UNSUPPORTED, "bytes: %lld too large", (long long)bytes);
+  if (buf == nullptr) return fail(W4A16_ERR_INVALID_ARG, "buf: null pointer");
+  if (sink == nullptr) return fail(W4A16_ERR_INVALID_ARG, "sink: null pointer");
+  if (misaligned(buf, 16)) return fail(W4A16_ERR_INVALID_ARG, "buf: address not 16-byte aligned");
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  return hip_status(w4moe::launch_stream_probe(buf, bytes, row_bytes, sink, stream),
+                    "probe launch");
 }
 
 w4a16_status_t w4a16_moe_route_topk(const float* logits, int64_t num_tokens,

@@ -9,7 +9,8 @@
 //        for Cutlass fused MoE"  Checkpoint format (nibble packing).
 //
 // Kernels
-//   combine_kernel  out[t] = cast16(sum_k w[t,k] * Y[slot[t,k]]) in FP32.
+//   combine_kernel  out[t] = cast16(sum_k w[t,k] * Y[t*K+k]) in FP32 over the
+//                   valid routes (slot[t*K+k] >= 0).
 //   unpack_kernel   nibbles through the GEMMs' bit conversion, back to int8.
 #include "device.h"
 #include "internal.h"
@@ -40,8 +41,8 @@ combine_kernel(const CombineParams p) {
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const bool ok = pos[k] >= 0;
-      const auto ry = make_rsrc(p.y + static_cast<int64_t>(ok ? pos[k] : 0) * p.H,
-                                ok ? static_cast<uint32_t>(2 * p.H) : 0u);
+      const int64_t r = static_cast<int64_t>(t) * p.top_k + kb + k;  // Y row of the route
+      const auto ry = make_rsrc(p.y + (ok ? r : 0) * p.H, ok ? static_cast<uint32_t>(2 * p.H) : 0u);
       v[k] = bload16(ry, 2u * static_cast<uint32_t>(col), true);
     }
     // fixed order: ascending k, invalid routes contribute nothing

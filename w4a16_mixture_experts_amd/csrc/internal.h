@@ -31,7 +31,7 @@ struct GemmParams {
   const int32_t* offsets;     // [E+1]; offsets[E] = padded total
   int E;
   int bm;
-  uint16_t* out;              // UP: act [P][ldo]; DOWN: Y [P][ldo]
+  uint16_t* out;              // UP: act [P][ldo]; DOWN: Y [T*K][ldo] by route
   int ldo;
   int n_tiles;                // column tiles (resident down / split-K: column chunks)
   int col_steps;              // resident down / split-K: column passes per chunk
@@ -97,7 +97,7 @@ inline size_t decode_down_lds_bytes(int top_k, int I) {
 }
 
 struct CombineParams {
-  const uint16_t* y;          // [P][H]
+  const uint16_t* y;          // [T*K][H] expert outputs by route
   const int32_t* slot;        // [T*K]
   const float* wts;           // [T][K]
   int top_k, H;
@@ -144,6 +144,12 @@ hipError_t launch_decode_down(const DecodeDownParams& p, int dtype, int layout, 
 hipError_t launch_combine(const CombineParams& p, int dtype, int T, hipStream_t stream);
 
 hipError_t launch_unpack(const uint8_t* packed, int64_t n_bytes, int8_t* out, hipStream_t stream);
+
+// Streaming-read probe over [bytes / row_bytes][row_bytes] (row_bytes a
+// multiple of 64, at most 8 * 16 * 64).
+constexpr int kProbeMaxRowBytes = 8 * 16 * 64;
+hipError_t launch_stream_probe(const uint8_t* buf, int64_t bytes, int row_bytes, uint32_t* sink,
+                               hipStream_t stream);
 
 // Router scoring and top-k (softmax over E_global logits, K largest).
 constexpr int kRouterMaxExperts = 1024;

@@ -434,9 +434,10 @@ __device__ __forceinline__ uint32_t valid_rows(const GemmParams& p, int row_base
 }
 
 // Epilogue: lane (c, g) holds rows row_base + 16ms + 4g + i of column col[s].
-// UP writes the 16-bit activation in A operand order (padding rows get 0);
-// DOWN writes the 16-bit expert outputs of valid rows.  Stores go through a
-// buffer resource over the tile's 64 output rows (masked lanes store nothing).
+// UP writes the 16-bit activation in A operand order (padding rows get 0)
+// through a buffer resource over the tile's 64 rows (masked lanes store
+// nothing); DOWN writes the 16-bit expert outputs of valid rows into Y, whose
+// rows are indexed by route (t * K + k).
 template <int DT, int MODE, int NMS>
 __device__ __forceinline__ void store_outputs(const GemmParams& p, int row_base,
                                               const f32x4 (&acc)[NMS][kNsub],
@@ -462,9 +463,12 @@ __device__ __forceinline__ void store_outputs(const GemmParams& p, int row_base,
                   T::from_f32(valid ? h * h : 0.0f));
         }
       } else {
+        // expert outputs are rows of Y by route index (16-bit, H columns)
+        const int route = p.sorted[row_base + 16 * ms + 4 * g + i];
+        uint16_t* yrow = p.out + static_cast<int64_t>(valid ? route : 0) * p.ldo;
 #pragma unroll
         for (int s = 0; s < kNsub; ++s)
-          bstore2(ro, 2u * (rowoff + col[s]), on[s] && valid, T::from_f32(16.0f * acc[ms][s][i]));
+          if (on[s] && valid) yrow[col[s]] = T::from_f32(16.0f * acc[ms][s][i]);
       }
     }
   }
@@ -905,8 +909,10 @@ __device__ __forceinline__ void down_resident_run(const GemmParams& p, const int
   // rows of the tile holding a route (bit r: tile row r)
   const uint64_t rows_valid = __ballot(p.sorted[row_base + lane] >= 0);
   const bool vec_out = (p.n_cols & 7) == 0;  // a 16-byte chunk is all in or all out
-  const auto ro = make_rsrc(p.out + static_cast<int64_t>(row_base) * p.ldo,
-                            static_cast<uint32_t>(2 * kTileRows * p.ldo));
+  // route index of the row each lane stores in the vectorized epilogue
+  int route[NMS];
+#pragma unroll
+  for (int ms = 0; ms < NMS; ++ms) route[ms] = p.sorted[row_base + 16 * ms + (lane >> 2)];
   auto store_step = [&](int st) {
     int col[kNsub];
     bool on[kNsub];
@@ -932,9 +938,8 @@ __device__ __forceinline__ void down_resident_run(const GemmParams& p, const int
       const int r = 16 * ms + (lane >> 2);
       const u32x4 v = *reinterpret_cast<const u32x4*>(s_out + r * kOutStride + 8 * (lane & 3));
       const bool ok = col_ok && ((rows_valid >> r) & 1u);
-      __builtin_amdgcn_raw_buffer_store_b128(
-          __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), ro,
-          ok ? 2u * static_cast<uint32_t>(r * p.ldo + n0) : kOob, 0, 0);
+      // Y rows by route index
+      if (ok) *reinterpret_cast<u32x4*>(p.out + static_cast<int64_t>(route[ms]) * p.ldo + n0) = v;
     }
   };
 
@@ -1124,8 +1129,10 @@ __device__ __forceinline__ bool down_resident_run_x16(const GemmParams& p, const
   // rows of the tile holding a route (bit r: tile row r)
   const uint64_t rows_valid = __ballot(p.sorted[row_base + lane] >= 0);
   const bool vec_out = (p.n_cols & 7) == 0;  // a 16-byte chunk is all in or all out
-  const auto ro = make_rsrc(p.out + static_cast<int64_t>(row_base) * p.ldo,
-                            static_cast<uint32_t>(2 * kTileRows * p.ldo));
+  // route index of the row each lane stores in the vectorized epilogue
+  int route[NMS];
+#pragma unroll
+  for (int ms = 0; ms < NMS; ++ms) route[ms] = p.sorted[row_base + 16 * ms + (lane >> 2)];
   bool sbad = false;  // X16: a group scale outside the route's exact range
   auto mma = [&](const uint16_t* sa, const WBlk<LAYOUT> (&wb)[kNsub]) {
     if constexpr (X16) mma_block_x<NMS, false>(sa, S, wb, acc, c, g, sbad);
@@ -1163,9 +1170,8 @@ __device__ __forceinline__ bool down_resident_run_x16(const GemmParams& p, const
       const int r = 16 * ms + (lane >> 2);
       const u32x4 v = *reinterpret_cast<const u32x4*>(s_out + r * kOutStride + 8 * (lane & 3));
       const bool ok = col_ok && ((rows_valid >> r) & 1u);
-      __builtin_amdgcn_raw_buffer_store_b128(
-          __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), ro,
-          ok ? 2u * static_cast<uint32_t>(r * p.ldo + n0) : kOob, 0, 0);
+      // Y rows by route index
+      if (ok) *reinterpret_cast<u32x4*>(p.out + static_cast<int64_t>(route[ms]) * p.ldo + n0) = v;
     }
   };
 
