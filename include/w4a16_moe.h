@@ -192,6 +192,26 @@ w4a16_status_t w4a16_moe_forward_timed(const void* x, const uint8_t* w13_packed,
                                        size_t workspace_bytes, w4a16_stream_t stream,
                                        void* const* stage_events, int32_t n_events);
 
+/* w4a16_moe_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Arguments, checks and results are those of
+ * w4a16_moe_forward (same kernels, same plan, identical bits).  The scratch is
+ * a library-owned device array of W4A16_NOALLOC_SCRATCH_BYTES (128 MiB) on each
+ * GPU the library runs on, held until the process ends; its address is looked
+ * up (not allocated) at the first call on a GPU, with the caller's current
+ * device.  A descriptor whose workspace (w4a16_moe_workspace_size) exceeds it
+ * is rejected with W4A16_ERR_UNSUPPORTED before anything is enqueued (the Kimi
+ * shard shape fits up to about 960 tokens).  Every call on one GPU shares that
+ * array and leaves its contents behind: calls on one GPU must be ordered (one
+ * stream, or explicit dependencies); overlapping calls race and give wrong
+ * results.  No hipMalloc, hipFree or other allocating call is made. */
+#define W4A16_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+w4a16_status_t w4a16_moe_forward_noalloc(const void* x, const uint8_t* w13_packed,
+                                         const void* w13_scales, const uint8_t* w2_packed,
+                                         const void* w2_scales, const int32_t* topk_ids,
+                                         const float* topk_weights, void* out,
+                                         const w4a16_moe_desc_t* desc, w4a16_stream_t stream);
+
 /* Route preparation alone, with the same device code the forward runs ([P1]
  * Benchmark, "route preparation"; [P2] Description, route guards and padded
  * fallback).  Uses desc->num_tokens, top_k, num_local_experts, expert_offset.

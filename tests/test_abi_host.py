@@ -281,3 +281,17 @@ def test_forward_rejects_wrong_out_shape(monkeypatch):
                           out=torch.zeros(*bad, dtype=torch.bfloat16))
     # only the host-side workspace query ran, never the forward
     assert all(st == 0 for st in called)
+
+
+def test_no_alloc_forward_rejects_before_anything():
+    """The no-alloc forward checks the descriptor and the scratch limit before
+    it touches a pointer or the device (so this runs without a GPU)."""
+    L = B.lib()
+    small = B.make_desc(num_tokens=4, hidden=256, intermediate=384, num_local_experts=8, top_k=2)
+    big = B.make_desc(num_tokens=2048, hidden=7168, intermediate=256, num_local_experts=384,
+                      top_k=8)
+    assert B.workspace_size(small) <= B.NOALLOC_SCRATCH_BYTES < B.workspace_size(big)
+    st = L.w4a16_moe_forward_noalloc(*([None] * 8), ctypes.byref(big), None)
+    assert st == 2 and "no-alloc scratch" in L.w4a16_last_error_message().decode()
+    bad = B.make_desc(num_tokens=-1, hidden=256, intermediate=384, num_local_experts=8, top_k=2)
+    assert L.w4a16_moe_forward_noalloc(*([None] * 8), ctypes.byref(bad), None) == 1

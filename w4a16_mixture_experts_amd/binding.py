@@ -21,6 +21,7 @@ DT_BF16, DT_FP16 = 0, 1
 ACT_SILU_GATED, ACT_RELU2 = 0, 1
 Q_GROUP_K, Q_PER_CHANNEL = 0, 1
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP"}
+NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024   # W4A16_NOALLOC_SCRATCH_BYTES
 
 
 class MoeDesc(ctypes.Structure):
@@ -68,13 +69,14 @@ def lib():
     L.w4a16_unpack_int4.argtypes = [P, i64, P, P]
     L.w4a16_moe_route_topk.argtypes = [P, i64, i32, i32, i32, P, P, P]
     L.w4a16_stream_probe.argtypes = [P, i64, i32, P, P]
+    L.w4a16_moe_forward_noalloc.argtypes = [P, P, P, P, P, P, P, P, pdesc, P]
     L.w4a16_status_string.argtypes = [i32]
     L.w4a16_status_string.restype = ctypes.c_char_p
     L.w4a16_last_error_message.restype = ctypes.c_char_p
     for f in ("w4a16_moe_workspace_size", "w4a16_moe_get_plan", "w4a16_moe_forward",
               "w4a16_moe_forward_timed",
               "w4a16_moe_prepare_routes", "w4a16_unpack_int4", "w4a16_moe_route_topk",
-              "w4a16_stream_probe"):
+              "w4a16_stream_probe", "w4a16_moe_forward_noalloc"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -151,8 +153,12 @@ def moe_forward(x, w13_packed, w13_scales, w2_packed, w2_scales, topk_ids, topk_
                 gated: bool = True, per_channel: bool = False, out=None, workspace=None,
                 force_path: int = 0, force_block_m: int = 0, force_splitk: int = 0,
                 num_global_experts: int = 0, fp16_route: int = 0,
-                stream=None, stage_events=None) -> torch.Tensor:
+                stream=None, stage_events=None, no_alloc: bool = False) -> torch.Tensor:
     """Local W4A16 MoE forward: returns out [T, H] in x's dtype.
+
+    no_alloc: call w4a16_moe_forward_noalloc (the library's own scratch array
+    instead of a workspace; `out` should then be passed in as well, since
+    allocating it here would defeat the purpose).
 
     stage_events: optional list of up to 8 torch.cuda.Event(enable_timing=True);
     events 2i and 2i+1 are recorded around stage i (0 route preparation,
@@ -195,6 +201,13 @@ def moe_forward(x, w13_packed, w13_scales, w2_packed, w2_scales, topk_ids, topk_
         _dev("out", out, (x.dtype,), dev)
         if tuple(out.shape) != (T, H):
             raise ValueError(f"out: shape {tuple(out.shape)}, expected {(T, H)}")
+    if no_alloc:
+        if workspace is not None or stage_events is not None:
+            raise ValueError("no_alloc: takes no workspace and no stage events")
+        _check(lib().w4a16_moe_forward_noalloc(
+            _ptr(x), _ptr(w13_packed), _ptr(w13_scales), _ptr(w2_packed), _ptr(w2_scales),
+            _ptr(topk_ids), _ptr(topk_weights), _ptr(out), ctypes.byref(desc), _stream(stream)))
+        return out
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     else:

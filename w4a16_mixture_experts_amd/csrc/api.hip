@@ -13,6 +13,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <string>
 
 #include "../../include/w4a16_moe.h"
@@ -686,3 +687,66 @@ w4a16_status_t w4a16_moe_route_topk(const float* logits, int64_t num_tokens,
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Forward without a caller workspace (for callers that cannot allocate: code
+// under HIP graph capture, tight serving loops, harnesses that forbid
+// hipMalloc).  The scratch is a file-scope device array, one copy per GPU;
+// its device address is looked up once per device (with that device
+// current) and only that address is handed to kernels or copies.
+// ---------------------------------------------------------------------------
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[W4A16_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this GPU's scratch array (looked up on the first call).
+w4a16_status_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(W4A16_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(W4A16_ERR_UNSUPPORTED, "device %d: no-alloc scratch supports devices 0..%d", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(W4A16_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return W4A16_OK;
+}
+
+}  // namespace
+
+extern "C" w4a16_status_t w4a16_moe_forward_noalloc(
+    const void* x, const uint8_t* w13_packed, const void* w13_scales, const uint8_t* w2_packed,
+    const void* w2_scales, const int32_t* topk_ids, const float* topk_weights, void* out,
+    const w4a16_moe_desc_t* desc, w4a16_stream_t stream) {
+  w4a16_status_t st = check_desc(desc);
+  if (st != W4A16_OK) return st;
+  const Plan pl = make_plan(desc);
+  st = check_plan(desc, pl);
+  if (st != W4A16_OK) return st;
+  if (pl.total > static_cast<size_t>(W4A16_NOALLOC_SCRATCH_BYTES))
+    return fail(W4A16_ERR_UNSUPPORTED,
+                "workspace: %zu bytes needed exceed the no-alloc scratch of %zu bytes "
+                "(use w4a16_moe_forward with a caller workspace)",
+                pl.total, static_cast<size_t>(W4A16_NOALLOC_SCRATCH_BYTES));
+  if (desc->num_tokens == 0) return W4A16_OK;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != W4A16_OK) return st;
+  // nothing in the workspace has to start at zero: every kernel writes what
+  // a later one reads (flags included) within the same forward
+  return forward_impl(x, w13_packed, w13_scales, w2_packed, w2_scales, topk_ids, topk_weights,
+                      out, desc, ws, static_cast<size_t>(W4A16_NOALLOC_SCRATCH_BYTES), stream,
+                      nullptr, 0);
+}
