@@ -477,10 +477,24 @@ def main():
 
             route()
             g_route = cold_graph(route)
+            # the forward with the router fused in (same token batch, from its logits)
+            out_r = torch.empty(T, wl.hidden, dtype=wl.dtype, device=dev)
+            ids_f = torch.empty(T, wl.top_k, dtype=torch.int32, device=dev)
+            w_f = torch.empty(T, wl.top_k, dtype=torch.float32, device=dev)
+            ws_r = torch.empty(max(1, binding.workspace_size(desc)), dtype=torch.uint8,
+                               device=dev)
+
+            def routed(tok=tok, out_r=out_r, ids_f=ids_f, w_f=w_f, ws_r=ws_r, Wg=Wg, wl=wl, **kw):
+                return binding.forward_workload_routed(wl, Wg, tok, out=out_r, ids_out=(ids_f, w_f),
+                                                       workspace=ws_r, **kw)
+
+            routed()
+            g_routed = cold_graph(routed)
             stage_b, total_b, total_f, stage_f, D, Rv = workload_bytes_flops(
                 wl, tok.topk_ids.cpu(), T)
             cases.append(dict(wl=wl, head=wi == 0, T=T, tok=tok, fwd=fwd, g_cold=g_cold,
                               g_warm=g_warm, plan=plan, route=route, g_route=g_route, router=[],
+                              routed=routed, g_routed=g_routed, routed_cold=[], routed_stage=[],
                               stage_bytes=stage_b, bytes=total_b, flops=total_f,
                               stage_flops=stage_f, D=D, Rv=Rv,
                               wbytes=D * weight_bytes_per_expert(wl),
@@ -508,6 +522,7 @@ def main():
     ev1 = torch.cuda.Event(enable_timing=True)
     ev2 = torch.cuda.Event(enable_timing=True)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    evs_r = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
 
     def time_cold(g, fn):
         """Device time of fn on cold caches: graph difference, or eager."""
@@ -534,10 +549,20 @@ def main():
             evs[7 if c["plan"].path == 1 else 5].synchronize()
             t_route = time_cold(c["g_route"], c["route"])
             t_probe = time_cold(c["g_probe"], c["probe_fn"])
+            t_routed = time_cold(c["g_routed"], c["routed"])
+            # first stage of the routed forward: routing fused with route
+            # preparation (grouped path) or with the gate/up GEMM (small batch)
+            si = 0 if c["plan"].path == 1 else 1
+            flush()
+            c["routed"](stage_events=evs_r)
+            evs_r[7 if c["plan"].path == 1 else 5].synchronize()
+            t_rstage = evs_r[2 * si].elapsed_time(evs_r[2 * si + 1]) * 1e3
             if record:
                 c["cold"].append(t_cold)
                 c["router"].append(t_route)
                 c["probe"].append(t_probe)
+                c["routed_cold"].append(t_routed)
+                c["routed_stage"].append(t_rstage)
                 for si, name in enumerate(STAGES):
                     if name in ("route_prep", "combine") and c["plan"].path == 2:
                         continue
@@ -596,6 +621,14 @@ def main():
                          "fp16_route": c["plan"].fp16_route},
                 "stage_us": {k: round(v, 3) for k, v in st.items()},
                 "router_us_cold": round(statistics.fmean(c["router"]), 3),
+                "routed": {
+                    "latency_us_cold": round(statistics.fmean(c["routed_cold"]), 3),
+                    "fused_stage": "routing + route preparation" if c["plan"].path == 1
+                                   else "routing + gate/up GEMM",
+                    "fused_stage_us": round(statistics.fmean(c["routed_stage"]), 3),
+                    "unfused_us": round(statistics.fmean(c["router"]) + st.get(
+                        "route_prep" if c["plan"].path == 1 else "gate_up_gemm", 0.0), 3),
+                },
                 "stream_probe": {"bytes": c["probe_bytes"], "us_cold": round(pr, 3),
                                  "gbps": round(c["probe_bytes"] / pr / 1e3, 1),
                                  "frac": round(c["probe_bytes"] / pr / 1e3 / HBM_PEAK_GBS, 4),
@@ -673,8 +706,9 @@ def main():
             "per_tokens": table,
             "wall_s_timed_region": round(wall, 3),
             "step": "one cold forward at every token count of every listed workload "
-                    "(the headline and other_workloads), plus the router and the "
-                    "streaming-read probe at the same token counts",
+                    "(the headline and other_workloads), plus the router, the forward "
+                    "with the router fused in, and the streaming-read probe at the same "
+                    "token counts",
         },
         "roofline": roofline,
         "cpu_baseline": cpu,

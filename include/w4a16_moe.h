@@ -192,6 +192,40 @@ w4a16_status_t w4a16_moe_forward_timed(const void* x, const uint8_t* w13_packed,
                                        size_t workspace_bytes, w4a16_stream_t stream,
                                        void* const* stage_events, int32_t n_events);
 
+/* The forward with the router step fused in ([P2] Final performance: routing
+ * is timed as part of the MoE; [P1] Benchmark: FP32 routing weights, INT32
+ * ids, renormalization off in the measured workload).  Instead of ids and
+ * weights it takes the router logits and routes every token inside the
+ * forward's first launch (route preparation on the grouped path, the gate/up
+ * GEMM on the small-batch path), as w4a16_moe_route_topk defines it (softmax
+ * over all num_global_experts logits, the top_k largest in descending order,
+ * ties to the lower id, optional renormalization), then runs the forward of
+ * w4a16_moe_forward on those routes.
+ *   router_logits [T][num_global_experts] fp32, device (num_global_experts of
+ *                 the descriptor, 0 meaning num_local_experts; at most 1024,
+ *                 and top_k at most 32 and at most num_global_experts)
+ *   renormalize   0 or 1
+ *   topk_ids      [T][K] int32 OUT: the routed global ids (ids outside the
+ *                 local range are invalid routes of this share, as always)
+ *   topk_weights  [T][K] fp32 OUT: their weights
+ *   stage_events, n_events: as for w4a16_moe_forward_timed (NULL, 0 for none);
+ *                 stage 0 is routing with route preparation, and on the
+ *                 small-batch path stage 1 is routing with the gate/up GEMM.
+ * Identical ids and weights to w4a16_moe_route_topk (same device code),
+ * identical output bits to w4a16_moe_forward given those ids and weights.
+ * Routing runs inside the first launch for up to 16 tokens on the grouped
+ * path and up to 16 routes on the small-batch path (one token per wave);
+ * beyond that the router runs as a launch of its own first (one wave per
+ * token across the GPU is faster than several tokens per wave). */
+w4a16_status_t w4a16_moe_forward_routed(const void* x, const uint8_t* w13_packed,
+                                        const void* w13_scales, const uint8_t* w2_packed,
+                                        const void* w2_scales, const float* router_logits,
+                                        int32_t renormalize, int32_t* topk_ids,
+                                        float* topk_weights, void* out,
+                                        const w4a16_moe_desc_t* desc, void* workspace,
+                                        size_t workspace_bytes, w4a16_stream_t stream,
+                                        void* const* stage_events, int32_t n_events);
+
 /* w4a16_moe_forward without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc.  Arguments, checks and results are those of
@@ -233,6 +267,20 @@ w4a16_status_t w4a16_moe_prepare_routes(const w4a16_moe_desc_t* desc, const int3
                                         int32_t* sorted_routes, int64_t sorted_capacity,
                                         int32_t* route_slot, int32_t* chunk_scratch,
                                         w4a16_stream_t stream);
+
+/* Routing fused with route preparation alone, with the device code of
+ * w4a16_moe_forward_routed's grouped path ([P2] Final performance, routing
+ * timed with the MoE): w4a16_moe_route_topk's ids and weights written to
+ * topk_ids / topk_weights, and the tables of w4a16_moe_prepare_routes (same
+ * arguments and meaning) built from them.  Uses desc->num_tokens, top_k,
+ * num_local_experts, expert_offset and num_global_experts. */
+w4a16_status_t w4a16_moe_route_and_prepare(const w4a16_moe_desc_t* desc,
+                                           const float* router_logits, int32_t renormalize,
+                                           int32_t block_m, int32_t* topk_ids,
+                                           float* topk_weights, int32_t* counts,
+                                           int32_t* offsets, int32_t* sorted_routes,
+                                           int64_t sorted_capacity, int32_t* route_slot,
+                                           int32_t* chunk_scratch, w4a16_stream_t stream);
 
 /* Nibble unpacking with the device conversion the GEMMs use ([P3] Checkpoint
  * format): out[2i] = low nibble of packed[i], out[2i+1] = high nibble, both as

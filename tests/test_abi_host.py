@@ -295,3 +295,29 @@ def test_no_alloc_forward_rejects_before_anything():
     assert st == 2 and "no-alloc scratch" in L.w4a16_last_error_message().decode()
     bad = B.make_desc(num_tokens=-1, hidden=256, intermediate=384, num_local_experts=8, top_k=2)
     assert L.w4a16_moe_forward_noalloc(*([None] * 8), ctypes.byref(bad), None) == 1
+
+
+def test_routed_forward_argument_errors():
+    """The routed forward and route_and_prepare check the router arguments on
+    the host before anything is enqueued (no GPU needed)."""
+    L = B.lib()
+    P = ctypes.c_void_p
+    d = B.make_desc(num_tokens=4, hidden=256, intermediate=384, num_local_experts=8, top_k=2,
+                    num_global_experts=2000)
+    args = [P(0x1000)] * 5 + [P(0x1000), 0, P(0x1000), P(0x1000), P(0x1000), ctypes.byref(d),
+                              P(0x1000), 1 << 30, None, None, 0]
+    assert L.w4a16_moe_forward_routed(*args) == 2
+    assert "num_global_experts=2000" in L.w4a16_last_error_message().decode()
+    d.num_global_experts = 8
+    args[6] = 2
+    assert L.w4a16_moe_forward_routed(*args) == 1
+    assert "renormalize" in L.w4a16_last_error_message().decode()
+    args[6] = 0
+    args[5] = None
+    assert L.w4a16_moe_forward_routed(*args) == 1
+    assert "router_logits" in L.w4a16_last_error_message().decode()
+    d.top_k = 9           # more than the 8 global experts
+    st = L.w4a16_moe_route_and_prepare(ctypes.byref(d), P(0x1000), 0, 64, P(0x1000), P(0x1000),
+                                       P(0x1000), P(0x1000), P(0x1000), 1 << 20, P(0x1000), None,
+                                       None)
+    assert st == 2 and "top_k=9" in L.w4a16_last_error_message().decode()

@@ -70,13 +70,17 @@ def lib():
     L.w4a16_moe_route_topk.argtypes = [P, i64, i32, i32, i32, P, P, P]
     L.w4a16_stream_probe.argtypes = [P, i64, i32, P, P]
     L.w4a16_moe_forward_noalloc.argtypes = [P, P, P, P, P, P, P, P, pdesc, P]
+    L.w4a16_moe_forward_routed.argtypes = [P, P, P, P, P, P, i32, P, P, P, pdesc, P, sz, P, P,
+                                           i32]
+    L.w4a16_moe_route_and_prepare.argtypes = [pdesc, P, i32, i32, P, P, P, P, P, i64, P, P, P]
     L.w4a16_status_string.argtypes = [i32]
     L.w4a16_status_string.restype = ctypes.c_char_p
     L.w4a16_last_error_message.restype = ctypes.c_char_p
     for f in ("w4a16_moe_workspace_size", "w4a16_moe_get_plan", "w4a16_moe_forward",
               "w4a16_moe_forward_timed",
               "w4a16_moe_prepare_routes", "w4a16_unpack_int4", "w4a16_moe_route_topk",
-              "w4a16_stream_probe", "w4a16_moe_forward_noalloc"):
+              "w4a16_stream_probe", "w4a16_moe_forward_noalloc", "w4a16_moe_forward_routed",
+              "w4a16_moe_route_and_prepare"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -301,3 +305,111 @@ def stream_probe(buf: torch.Tensor, nbytes: int, row_bytes: int, sink: torch.Ten
     if nbytes > buf.numel():
         raise ValueError(f"nbytes: {nbytes} exceeds buf ({buf.numel()} bytes)")
     _check(lib().w4a16_stream_probe(_ptr(buf), nbytes, row_bytes, _ptr(sink), _stream(stream)))
+
+
+def moe_forward_routed(x, w13_packed, w13_scales, w2_packed, w2_scales, router_logits, *,
+                       top_k: int, intermediate: int, num_local_experts: int,
+                       expert_offset: int = 0, gated: bool = True, per_channel: bool = False,
+                       renormalize: bool = False, out=None, workspace=None, ids_out=None,
+                       force_path: int = 0, force_splitk: int = 0, fp16_route: int = 0,
+                       stream=None, stage_events=None):
+    """Forward with the router fused in: returns (out [T, H], topk_ids [T, K],
+    topk_weights [T, K]); router_logits [T, E_global] fp32 (E_global is their
+    width)."""
+    half = (torch.bfloat16, torch.float16)
+    _dev("x", x, half)
+    dev = x.device
+    T, H = x.shape
+    _dev("router_logits", router_logits, (torch.float32,), dev)
+    if router_logits.dim() != 2 or router_logits.shape[0] != T:
+        raise ValueError("router_logits: expected [T, E_global] matching x")
+    Eg = router_logits.shape[1]
+    for name, t in (("w13_packed", w13_packed), ("w2_packed", w2_packed)):
+        _dev(name, t, (torch.uint8,), dev)
+    for name, t in (("w13_scales", w13_scales), ("w2_scales", w2_scales)):
+        _dev(name, t, (x.dtype,), dev)
+    E, I = num_local_experts, intermediate
+    N1 = 2 * I if gated else I
+    want = ({"w13_packed": (E, N1 // 2, H), "w13_scales": (E, N1), "w2_packed": (E, H // 2, I),
+             "w2_scales": (E, H)} if per_channel else
+            {"w13_packed": (E, N1, H // 2), "w13_scales": (E, N1, H // 32),
+             "w2_packed": (E, H, I // 2), "w2_scales": (E, H, I // 32)})
+    for name, t in (("w13_packed", w13_packed), ("w13_scales", w13_scales),
+                    ("w2_packed", w2_packed), ("w2_scales", w2_scales)):
+        if tuple(t.shape) != want[name]:
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {want[name]}")
+    desc = make_desc(num_tokens=T, hidden=H, intermediate=I, num_local_experts=E, top_k=top_k,
+                     expert_offset=expert_offset, dtype=x.dtype, gated=gated,
+                     per_channel=per_channel, force_path=force_path, force_splitk=force_splitk,
+                     num_global_experts=Eg, fp16_route=fp16_route)
+    nbytes = workspace_size(desc)
+    if out is None:
+        out = torch.empty(T, H, dtype=x.dtype, device=dev)
+    else:
+        _dev("out", out, (x.dtype,), dev)
+        if tuple(out.shape) != (T, H):
+            raise ValueError(f"out: shape {tuple(out.shape)}, expected {(T, H)}")
+    if ids_out is None:
+        ids = torch.empty(T, top_k, dtype=torch.int32, device=dev)
+        wts = torch.empty(T, top_k, dtype=torch.float32, device=dev)
+    else:
+        ids, wts = ids_out
+        _dev("topk_ids", ids, (torch.int32,), dev)
+        _dev("topk_weights", wts, (torch.float32,), dev)
+        if tuple(ids.shape) != (T, top_k) or tuple(wts.shape) != (T, top_k):
+            raise ValueError("ids_out: expected two [T, top_k] tensors")
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    else:
+        _dev("workspace", workspace, (torch.uint8,), dev)
+    st = stream if stream is not None else torch.cuda.current_stream()
+    handles, n_ev = None, 0
+    if stage_events is not None:
+        for ev in stage_events:
+            if ev is not None and not ev.cuda_event:
+                ev.record(st)
+        handles = (ctypes.c_void_p * len(stage_events))(
+            *[ev.cuda_event if ev is not None else None for ev in stage_events])
+        n_ev = len(stage_events)
+    _check(lib().w4a16_moe_forward_routed(
+        _ptr(x), _ptr(w13_packed), _ptr(w13_scales), _ptr(w2_packed), _ptr(w2_scales),
+        _ptr(router_logits), 1 if renormalize else 0, _ptr(ids), _ptr(wts), _ptr(out),
+        ctypes.byref(desc), _ptr(workspace), workspace.numel(), _stream(st), handles, n_ev))
+    return out, ids, wts
+
+
+def forward_workload_routed(wl, W, tok, **kw):
+    """moe_forward_routed on synth.Weights / synth.Tokens already on the GPU
+    (the tokens' router logits instead of their ids and weights)."""
+    return moe_forward_routed(tok.x, W.w13_packed, W.w13_scales, W.w2_packed, W.w2_scales,
+                              tok.logits, top_k=wl.top_k, intermediate=wl.inter,
+                              num_local_experts=wl.num_experts, expert_offset=wl.expert_offset,
+                              gated=wl.gated, per_channel=wl.per_channel, **kw)
+
+
+def route_and_prepare(logits: torch.Tensor, top_k: int, num_local_experts: int,
+                      expert_offset: int, block_m: int, renormalize: bool = False, stream=None,
+                      chunked: bool = True):
+    """Routing fused with route preparation: (ids, weights, counts, offsets,
+    sorted, slot) from the device kernels."""
+    _dev("logits", logits, (torch.float32,))
+    T, Eg = logits.shape
+    R = T * top_k
+    E = num_local_experts
+    dev = logits.device
+    cap = R + min(E, R) * (block_m - 1)
+    ids = torch.empty(T, top_k, dtype=torch.int32, device=dev)
+    wts = torch.empty(T, top_k, dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    srt = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    slot = torch.empty(max(R, 1), dtype=torch.int32, device=dev)
+    desc = make_desc(num_tokens=T, hidden=64, intermediate=64, num_local_experts=E, top_k=top_k,
+                     expert_offset=expert_offset, num_global_experts=Eg)
+    scratch = (torch.empty(ROUTE_CHUNKS_MAX * E, dtype=torch.int32, device=dev)
+               if chunked else None)
+    _check(lib().w4a16_moe_route_and_prepare(
+        ctypes.byref(desc), _ptr(logits), 1 if renormalize else 0, block_m, _ptr(ids), _ptr(wts),
+        _ptr(counts), _ptr(offsets), _ptr(srt), cap, _ptr(slot),
+        _ptr(scratch) if chunked else None, _stream(stream)))
+    return ids, wts, counts, offsets, srt, slot[:R]

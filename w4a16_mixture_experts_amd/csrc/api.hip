@@ -19,6 +19,7 @@
 #include "../../include/w4a16_moe.h"
 #include "device.h"
 #include "internal.h"
+#include "router.h"
 
 static_assert(W4A16_ROUTE_CHUNKS_MAX == w4moe::kRouteChunksMax,
               "the header states the route scratch size");
@@ -349,11 +350,35 @@ struct StageEvents {
   }
 };
 
+// Checks of the router arguments of a routed call (logits [T][Eg] fp32).
+w4a16_status_t check_route(const w4a16_moe_desc_t* d, const float* logits, int renormalize,
+                           int* eg) {
+  const int Eg = d->num_global_experts > 0 ? d->num_global_experts : d->num_local_experts;
+  if (Eg > w4moe::kRouterMaxExperts)
+    return fail(W4A16_ERR_UNSUPPORTED, "router_logits: num_global_experts=%d exceeds %d", Eg,
+                w4moe::kRouterMaxExperts);
+  if (d->top_k > Eg)
+    return fail(W4A16_ERR_UNSUPPORTED, "topk_ids: top_k=%d exceeds num_global_experts=%d",
+                d->top_k, Eg);
+  if (renormalize != 0 && renormalize != 1)
+    return fail(W4A16_ERR_INVALID_ARG, "renormalize: %d (0 or 1)", renormalize);
+  if (d->num_tokens > 0 && logits == nullptr)
+    return fail(W4A16_ERR_INVALID_ARG, "router_logits: null pointer");
+  if (misaligned(logits, 4))
+    return fail(W4A16_ERR_INVALID_ARG, "router_logits: address not 4-byte aligned");
+  *eg = Eg;
+  return W4A16_OK;
+}
+
+// route != nullptr: the tokens are routed from route->logits inside the
+// forward's first launch, which writes topk_ids and topk_weights (the
+// caller's buffers, then read by the later kernels).
 w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void* w13_scales,
                             const uint8_t* w2_packed, const void* w2_scales,
                             const int32_t* topk_ids, const float* topk_weights, void* out,
                             const w4a16_moe_desc_t* desc, void* workspace, size_t workspace_bytes,
-                            w4a16_stream_t stream_, hipEvent_t* events, int n_events) {
+                            w4a16_stream_t stream_, hipEvent_t* events, int n_events,
+                            const w4moe::RouteArgs* route = nullptr) {
   w4a16_status_t st = check_desc(desc);
   if (st != W4A16_OK) return st;
   const Plan pl = make_plan(desc);
@@ -418,6 +443,19 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
     sh.kslice = pl.kslice;
     sh.h = reinterpret_cast<float*>(ws + pl.off_act);
     sh.ldh = pl.N1;
+    if (route != nullptr) {
+      if (route->Eg <= 64 * w4moe::kSmallRouteNpl && pl.R <= w4moe::kSmallRouteMaxRoutes) {
+        sh.ra = *route;  // routed inside the gate/up launch
+      } else {
+        // every gate/up workgroup routes all tokens itself, so beyond a few
+        // routes (or with more global experts than that launch routes) the
+        // router kernel runs first
+        st = hip_status(w4moe::launch_router_topk(route->logits, route->T, route->Eg, K,
+                                                  route->renorm, route->ids, route->wts, stream),
+                        "router launch");
+        if (st != W4A16_OK) return st;
+      }
+    }
     st = hip_status(evs.mark(2), "stage event");
     if (st != W4A16_OK) return st;
     st = hip_status(w4moe::launch_small_h(sh, desc->dtype, desc->qlayout, pl.nkb, pl.N1, stream),
@@ -454,8 +492,10 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
   st = hip_status(w4moe::launch_route_prep(topk_ids, static_cast<int>(pl.R), E,
                                            desc->expert_offset, pl.bm, counts, offsets, sorted,
                                            slot, tile,
-                                           reinterpret_cast<int32_t*>(ws + pl.off_chunks), stream),
-                  "route preparation launch");
+                                           reinterpret_cast<int32_t*>(ws + pl.off_chunks), stream,
+                                           K, route),
+                  route != nullptr ? "routing and route preparation launch"
+                                   : "route preparation launch");
   if (st == W4A16_OK) st = hip_status(evs.mark(1), "stage event");
   if (st != W4A16_OK) return st;
 
@@ -585,6 +625,81 @@ w4a16_status_t w4a16_moe_forward_timed(const void* x, const uint8_t* w13_packed,
   return forward_impl(x, w13_packed, w13_scales, w2_packed, w2_scales, topk_ids, topk_weights,
                       out, desc, workspace, workspace_bytes, stream,
                       reinterpret_cast<hipEvent_t*>(const_cast<void**>(stage_events)), n_events);
+}
+
+w4a16_status_t w4a16_moe_forward_routed(
+    const void* x, const uint8_t* w13_packed, const void* w13_scales, const uint8_t* w2_packed,
+    const void* w2_scales, const float* router_logits, int32_t renormalize, int32_t* topk_ids,
+    float* topk_weights, void* out, const w4a16_moe_desc_t* desc, void* workspace,
+    size_t workspace_bytes, w4a16_stream_t stream, void* const* stage_events, int32_t n_events) {
+  w4a16_status_t st = check_desc(desc);
+  if (st != W4A16_OK) return st;
+  int Eg = 0;
+  st = check_route(desc, router_logits, renormalize, &Eg);
+  if (st != W4A16_OK) return st;
+  w4moe::RouteArgs ra{};
+  ra.logits = router_logits;
+  ra.T = desc->num_tokens;
+  ra.Eg = Eg;
+  ra.renorm = renormalize;
+  ra.ids = topk_ids;
+  ra.wts = topk_weights;
+  return forward_impl(x, w13_packed, w13_scales, w2_packed, w2_scales, topk_ids, topk_weights,
+                      out, desc, workspace, workspace_bytes, stream,
+                      reinterpret_cast<hipEvent_t*>(const_cast<void**>(stage_events)), n_events,
+                      &ra);
+}
+
+w4a16_status_t w4a16_moe_route_and_prepare(const w4a16_moe_desc_t* desc,
+                                           const float* router_logits, int32_t renormalize,
+                                           int32_t block_m, int32_t* topk_ids,
+                                           float* topk_weights, int32_t* counts,
+                                           int32_t* offsets, int32_t* sorted_routes,
+                                           int64_t sorted_capacity, int32_t* route_slot,
+                                           int32_t* chunk_scratch, w4a16_stream_t stream_) {
+  if (desc == nullptr) return fail(W4A16_ERR_INVALID_ARG, "desc: null pointer");
+  if (desc->num_tokens < 0)
+    return fail(W4A16_ERR_INVALID_ARG, "desc.num_tokens: %d < 0", desc->num_tokens);
+  if (desc->top_k <= 0 || desc->top_k > w4moe::kRouterMaxTopK)
+    return fail(W4A16_ERR_INVALID_ARG, "desc.top_k: %d (1..%d)", desc->top_k,
+                w4moe::kRouterMaxTopK);
+  if (desc->num_local_experts <= 0 || desc->num_local_experts > 1024)
+    return fail(W4A16_ERR_INVALID_ARG, "desc.num_local_experts: %d (1..1024)",
+                desc->num_local_experts);
+  if (block_m < 1 || block_m > 256)
+    return fail(W4A16_ERR_INVALID_ARG, "block_m: %d (1..256)", block_m);
+  int Eg = 0;
+  w4a16_status_t st = check_route(desc, router_logits, renormalize, &Eg);
+  if (st != W4A16_OK) return st;
+  const int64_t R = static_cast<int64_t>(desc->num_tokens) * desc->top_k;
+  if (R > (int64_t(1) << 26))
+    return fail(W4A16_ERR_UNSUPPORTED, "topk_ids: %lld routes exceed 2^26", (long long)R);
+  const int64_t need = R + std::min<int64_t>(desc->num_local_experts, R) * (block_m - 1);
+  if (sorted_capacity < need)
+    return fail(W4A16_ERR_INVALID_ARG, "sorted_routes: capacity %lld < %lld",
+                (long long)sorted_capacity, (long long)need);
+  struct {
+    const void* p;
+    const char* name;
+  } ptrs[] = {{counts, "counts"}, {offsets, "offsets"}, {sorted_routes, "sorted_routes"},
+              {route_slot, "route_slot"}, {topk_ids, "topk_ids"}, {topk_weights, "topk_weights"}};
+  for (const auto& q : ptrs) {
+    if (q.p == nullptr && !(R == 0 && q.p != counts && q.p != offsets))
+      return fail(W4A16_ERR_INVALID_ARG, "%s: null pointer", q.name);
+  }
+  w4moe::RouteArgs ra{};
+  ra.logits = router_logits;
+  ra.T = desc->num_tokens;
+  ra.Eg = Eg;
+  ra.renorm = renormalize;
+  ra.ids = topk_ids;
+  ra.wts = topk_weights;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  return hip_status(w4moe::launch_route_prep(topk_ids, static_cast<int>(R),
+                                             desc->num_local_experts, desc->expert_offset,
+                                             block_m, counts, offsets, sorted_routes, route_slot,
+                                             nullptr, chunk_scratch, stream, desc->top_k, &ra),
+                    "routing and route preparation launch");
 }
 
 w4a16_status_t w4a16_moe_prepare_routes(const w4a16_moe_desc_t* desc, const int32_t* topk_ids,

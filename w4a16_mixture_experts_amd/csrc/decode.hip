@@ -21,6 +21,7 @@
 //   w[t,k] * (sum of k's slices in slice order) and cast once to 16 bits.
 #include "device.h"
 #include "internal.h"
+#include "router.h"
 
 namespace w4moe {
 
@@ -83,7 +84,12 @@ __device__ __forceinline__ int local_id(int32_t g, int E, int off) {
 // lanes read zeros, so nothing waits on a load before its use).  Each wave
 // stages only its own slice of x (no barrier), and one barrier precedes the
 // fixed-order sum over slices.  Two dependent memory round trips in all.
-template <int DT, int LAYOUT, int NKB>
+// ROUTE: the ids come from routing the tokens' logits first (router.h): wave
+// w routes tokens w, w + 8, ... into LDS (every workgroup the same way, so
+// each sees the same ids), and workgroup (0, 0) writes the ids and weights
+// out for the down kernel and the caller.  One barrier more; the logits load
+// takes the place of the ids load.
+template <int DT, int LAYOUT, int NKB, bool ROUTE>
 __global__ void __launch_bounds__(kSmallThreads)
 small_h_kernel(const SmallHParams p) {
   using T = H16<DT>;
@@ -99,10 +105,29 @@ small_h_kernel(const SmallHParams p) {
   extern __shared__ uint16_t s_dyn[];  // per wave [kSmallRows][kslice + 8] x (A order), then
                                        // per wave [16][32] group scales
   __shared__ float s_red[kSmallWaves][64];
+  __shared__ int32_t s_rid[ROUTE ? kSmallMaxRoutes : 1];
 
-  // rows: the routes whose id equals route r0's id (R <= 64: one load, one ballot)
-  const auto rids = make_rsrc(p.ids, 4u * static_cast<uint32_t>(p.R));
-  const int32_t my_id = static_cast<int32_t>(bload4(rids, 4u * lane, lane < p.R));
+  int32_t my_id;
+  if constexpr (ROUTE) {
+    const bool writer = blockIdx.x == 0 && blockIdx.y == 0;
+    route_tokens<kSmallRouteNpl>(p.ra, p.top_k, w, p.T, kSmallWaves, lane,
+                                 [&](int t, int id, float pw) {
+      if (lane < p.top_k) {
+        const int r = t * p.top_k + lane;
+        s_rid[r] = id;
+        if (writer) {
+          p.ra.ids[r] = id;
+          p.ra.wts[r] = pw;
+        }
+      }
+    });
+    __syncthreads();
+    my_id = lane < p.R ? s_rid[lane] : 0;
+  } else {
+    // rows: the routes whose id equals route r0's id (R <= 64: one load, one ballot)
+    const auto rids = make_rsrc(p.ids, 4u * static_cast<uint32_t>(p.R));
+    my_id = static_cast<int32_t>(bload4(rids, 4u * lane, lane < p.R));
+  }
   const int32_t gid = __builtin_amdgcn_readlane(my_id, r0);
   const int e = local_id(gid, p.E, p.off);
   if (e < 0) return;  // invalid route: nothing to do (uniform)
@@ -471,9 +496,17 @@ static hipError_t allow_lds(F* kernel, size_t lds) {
 
 template <int DT, int LAYOUT, int NKB>
 static hipError_t launch_small_h_k(const SmallHParams& p, dim3 grid, size_t lds, hipStream_t st) {
-  const hipError_t err = allow_lds(small_h_kernel<DT, LAYOUT, NKB>, lds);
+  if (p.ra.logits != nullptr) {
+    const hipError_t err = allow_lds(small_h_kernel<DT, LAYOUT, NKB, true>, lds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((small_h_kernel<DT, LAYOUT, NKB, true>), grid, dim3(kSmallThreads), lds,
+                       st, p);
+    return hipGetLastError();
+  }
+  const hipError_t err = allow_lds(small_h_kernel<DT, LAYOUT, NKB, false>, lds);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((small_h_kernel<DT, LAYOUT, NKB>), grid, dim3(kSmallThreads), lds, st, p);
+  hipLaunchKernelGGL((small_h_kernel<DT, LAYOUT, NKB, false>), grid, dim3(kSmallThreads), lds, st,
+                     p);
   return hipGetLastError();
 }
 

@@ -56,15 +56,27 @@ constexpr int kSmallWaves = 8;            // reduction slices
 constexpr int kSmallThreads = kSmallWaves * 64;
 constexpr int kSmallRows = 4;             // token rows per pass (MFMA rows 0, 4, 8, 12)
 constexpr int kSmallMaxSlice = 1024;      // reduction per slice: hidden <= 8 * 1024
+constexpr int kSmallRouteNpl = 8;         // routed: logits per lane (E_global <= 512)
+constexpr int kSmallRouteMaxRoutes = 16;  // routed inside the launch up to this T*K
 inline size_t small_h_lds_bytes(int kslice) {
   return sizeof(uint16_t) * static_cast<size_t>(kSmallWaves) * (kSmallRows * (kslice + 8) + 16 * 32);
 }
+
+// Router arguments (router.h) of a forward that routes the tokens itself:
+// logits [T][Eg] fp32 in, ids/wts [T][K] out; logits == nullptr: ids given.
+struct RouteArgs {
+  const float* logits;
+  int T, Eg, renorm;
+  int32_t* ids;
+  float* wts;
+};
 
 struct SmallHParams {
   const uint16_t* x;          // [T][lda]
   int lda;
   int T;                      // tokens (rows of x)
-  const int32_t* ids;         // [R] global ids
+  const int32_t* ids;         // [R] global ids (unless routed: ra.logits set)
+  RouteArgs ra;               // routed: ids and weights come from the logits
   int R, top_k, E, off;
   const uint8_t* wq;          // w13 packed, expert 0
   const uint16_t* ws;         // w13 scales, expert 0
@@ -107,11 +119,16 @@ struct CombineParams {
 // Route preparation (one launch up to 1024 routes, else two).  chunk_hist:
 // kRouteChunksMax * E ints of scratch, or null for a single-chunk (slower for
 // many routes) preparation.
+// With `route` (router logits instead of ids; see router.h) route->ids and
+// route->wts are written first: up to 16 tokens inside the one-workgroup
+// preparation launch (one token per wave), else by the router kernel before
+// the preparation.  top_k: routes per token.
 constexpr int kRouteChunksMax = 32;
 int route_prep_chunk(int R);
 hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, int32_t* counts,
                              int32_t* offsets, int32_t* sorted, int32_t* slot,
-                             int32_t* tile_expert, int32_t* chunk_hist, hipStream_t stream);
+                             int32_t* tile_expert, int32_t* chunk_hist, hipStream_t stream,
+                             int top_k = 1, const RouteArgs* route = nullptr);
 
 // 64-row expert tiles (route positions), LDS-staged activations
 constexpr int kResidentK = 256;      // reduction the resident down kernel holds in LDS

@@ -36,12 +36,13 @@
 
 #include "device.h"
 #include "internal.h"
+#include "router.h"
 
 namespace w4moe {
 
 namespace {
 
-constexpr int kRpThreads = 256;            // ranking/scatter workgroup (4 waves)
+constexpr int kRpThreads = 256;            // ranking workgroup (4 waves)
 constexpr int kRpWaves = kRpThreads / 64;
 constexpr int kRpScanThreads = 1024;       // one thread per expert (E <= 1024)
 constexpr int kRpMaxExperts = 1024;
@@ -97,25 +98,40 @@ __device__ __forceinline__ void fill_padding_and_tiles(int eb, int ee, int bm,
 constexpr int kRpOneMaxPieces = 1;
 constexpr int kRpOneRoutes = kRpOneMaxPieces * kRpScanThreads;
 
-template <int NP>
+// NPL > 0: the ids come from routing the tokens' logits first (router.h, NPL
+// logits per lane); wave w routes token w (at most 16 tokens), keeps the ids
+// in LDS and writes ids and weights out.
+template <int NP, int NPL>
 __global__ void __launch_bounds__(kRpScanThreads)
 rp_one_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm,
               int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
               int32_t* __restrict__ sorted, int32_t* __restrict__ slot,
-              int32_t* __restrict__ tile_expert) {
+              int32_t* __restrict__ tile_expert, int top_k, RouteArgs ra) {
   constexpr int kW = kRpScanThreads / 64;
   __shared__ int32_t hist[kW][kRpMaxExperts];
   __shared__ int32_t wave_tot[kW];
   __shared__ int32_t s_off[kRpMaxExperts + 1];
   __shared__ int32_t s_cnt[kRpMaxExperts];
+  __shared__ int32_t s_ids[NPL > 0 ? NP * kRpScanThreads : 1];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if constexpr (NPL > 0) {
+    route_tokens<NPL>(ra, top_k, w, ra.T, kW, lane, [&](int t, int id, float pw) {
+      if (lane < top_k) {
+        const int r = t * top_k + lane;
+        s_ids[r] = id;
+        ra.ids[r] = id;
+        ra.wts[r] = pw;
+      }
+    });
+    __syncthreads();
+  }
   const int np = ((R + 63) / 64 + kW - 1) / kW;  // pieces per wave
   const int r0 = 64 * np * w + lane;              // route of piece 0 of this lane
   int ev[NP];
 #pragma unroll
   for (int q = 0; q < NP; ++q) {
     const int r = r0 + 64 * q;
-    ev[q] = (q < np && r < R) ? local_expert(ids[r], E, off) : -1;
+    ev[q] = (q < np && r < R) ? local_expert(NPL > 0 ? s_ids[r] : ids[r], E, off) : -1;
   }
   for (int x = lane; x < E; x += 64) hist[w][x] = 0;  // read back by this wave only
   int nbits = 1;
@@ -203,14 +219,15 @@ rp_one_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm,
 __global__ void __launch_bounds__(kRpThreads)
 rp_rank_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int chunk,
                int32_t* __restrict__ slot, int32_t* __restrict__ chunk_hist) {
-  __shared__ int32_t hist[kRpWaves][kRpMaxExperts];
+  constexpr int NW = kRpWaves;
+  __shared__ int32_t hist[NW][kRpMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = blockIdx.x;
   for (int e = lane; e < E; e += 64) hist[w][e] = 0;  // read back by this wave only
 
   const int c_beg = c * chunk;
   const int c_end = min(R, c_beg + chunk);
-  const int slab = ((chunk + kRpWaves - 1) / kRpWaves + 63) & ~63;
+  const int slab = ((chunk + NW - 1) / NW + 63) & ~63;
   const int r_beg = c_beg + w * slab;
   const int r_end = min(c_end, r_beg + slab);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -258,10 +275,10 @@ rp_rank_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int chunk
   }
   __syncthreads();
   // per expert: wave bases within the chunk (in place) and the chunk total
-  for (int e = tid; e < E; e += kRpThreads) {
+  for (int e = tid; e < E; e += (NW * 64)) {
     int run = 0;
 #pragma unroll
-    for (int v = 0; v < kRpWaves; ++v) {
+    for (int v = 0; v < NW; ++v) {
       const int n = hist[v][e];
       hist[v][e] = run;
       run += n;
@@ -386,9 +403,17 @@ int route_prep_chunk(int R) {
   return std::max(256, (per + 63) & ~63);
 }
 
+// Up to this many tokens the one-workgroup preparation routes its tokens
+// itself (one token per wave); a wave routes a token in about 1300 dependent
+// VALU instructions, so more tokens per wave cost more than the router
+// launch they save, and the router kernel (one wave per token over the
+// whole GPU) runs first instead.
+constexpr int kRpRouteMaxTokens = kRpScanThreads / 64;
+
 hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, int32_t* counts,
                              int32_t* offsets, int32_t* sorted, int32_t* slot,
-                             int32_t* tile_expert, int32_t* chunk_hist, hipStream_t stream) {
+                             int32_t* tile_expert, int32_t* chunk_hist, hipStream_t stream,
+                             int top_k, const RouteArgs* route) {
   if (E < 1 || E > kRpMaxExperts || R < 0) return hipErrorInvalidValue;
   // without scratch: one chunk, whose counts live in `counts` itself (the
   // scan overwrites them with the totals) and whose base is 0
@@ -396,9 +421,33 @@ hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, 
   const int chunk = one ? std::max(R, 1) : route_prep_chunk(R);
   const int n_chunks = R > 0 ? (R + chunk - 1) / chunk : 0;
   int32_t* hist = one ? counts : chunk_hist;
+  if (route != nullptr && R > 0) {
+    const RouteArgs& ra = *route;
+    if (ra.Eg < 1 || ra.Eg > kRouterMaxExperts || top_k < 1 || top_k > kRouterMaxTopK ||
+        top_k > ra.Eg || static_cast<int64_t>(ra.T) * top_k != R)
+      return hipErrorInvalidValue;
+    if (R <= kRpOneRoutes && ra.T <= kRpRouteMaxTokens) {
+      auto k = rp_one_kernel<kRpOneMaxPieces, 16>;
+      switch (router_npl(ra.Eg)) {
+        case 1: k = rp_one_kernel<kRpOneMaxPieces, 1>; break;
+        case 2: k = rp_one_kernel<kRpOneMaxPieces, 2>; break;
+        case 4: k = rp_one_kernel<kRpOneMaxPieces, 4>; break;
+        case 8: k = rp_one_kernel<kRpOneMaxPieces, 8>; break;
+        default: break;
+      }
+      hipLaunchKernelGGL(k, dim3(1), dim3(kRpScanThreads), 0, stream, ids, R, E, off, bm, counts,
+                         offsets, sorted, slot, tile_expert, top_k, ra);
+      return hipGetLastError();
+    }
+    const hipError_t err = launch_router_topk(ra.logits, ra.T, ra.Eg, top_k, ra.renorm, ra.ids,
+                                              ra.wts, stream);
+    if (err != hipSuccess) return err;
+    ids = ra.ids;  // the preparation reads the ids the router wrote
+  }
   if (R <= kRpOneRoutes) {
-    hipLaunchKernelGGL(rp_one_kernel<kRpOneMaxPieces>, dim3(1), dim3(kRpScanThreads), 0, stream,
-                       ids, R, E, off, bm, counts, offsets, sorted, slot, tile_expert);
+    hipLaunchKernelGGL((rp_one_kernel<kRpOneMaxPieces, 0>), dim3(1), dim3(kRpScanThreads), 0,
+                       stream, ids, R, E, off, bm, counts, offsets, sorted, slot, tile_expert,
+                       top_k, RouteArgs{});
     return hipGetLastError();
   }
   // R > kRpOneRoutes here, so there is at least one chunk
