@@ -490,11 +490,27 @@ def main():
 
             routed()
             g_routed = cold_graph(routed)
+            # the fused finalize mode (grouped path): the combine inside the
+            # down launch, reported beside the default non-fused mode
+            fused = None
+            g_fused = None
+            if plan.path == 1:
+                ws_f = torch.empty(max(1, binding.workspace_size(binding.desc_for(
+                    wl, T, fused_finalize=1))), dtype=torch.uint8, device=dev)
+                out_f = torch.empty(T, wl.hidden, dtype=wl.dtype, device=dev)
+
+                def fused(tok=tok, ws_f=ws_f, out_f=out_f, Wg=Wg, wl=wl):
+                    return binding.forward_workload(wl, Wg, tok, out=out_f, workspace=ws_f,
+                                                    fused_finalize=1)
+
+                fused()
+                g_fused = cold_graph(fused)
             stage_b, total_b, total_f, stage_f, D, Rv = workload_bytes_flops(
                 wl, tok.topk_ids.cpu(), T)
             cases.append(dict(wl=wl, head=wi == 0, T=T, tok=tok, fwd=fwd, g_cold=g_cold,
                               g_warm=g_warm, plan=plan, route=route, g_route=g_route, router=[],
                               routed=routed, g_routed=g_routed, routed_cold=[], routed_stage=[],
+                              fused=fused, g_fused=g_fused, fused_cold=[],
                               stage_bytes=stage_b, bytes=total_b, flops=total_f,
                               stage_flops=stage_f, D=D, Rv=Rv,
                               wbytes=D * weight_bytes_per_expert(wl),
@@ -550,6 +566,7 @@ def main():
             t_route = time_cold(c["g_route"], c["route"])
             t_probe = time_cold(c["g_probe"], c["probe_fn"])
             t_routed = time_cold(c["g_routed"], c["routed"])
+            t_fused = time_cold(c["g_fused"], c["fused"]) if c["fused"] is not None else None
             # first stage of the routed forward: routing fused with route
             # preparation (grouped path) or with the gate/up GEMM (small batch)
             si = 0 if c["plan"].path == 1 else 1
@@ -563,6 +580,8 @@ def main():
                 c["probe"].append(t_probe)
                 c["routed_cold"].append(t_routed)
                 c["routed_stage"].append(t_rstage)
+                if t_fused is not None:
+                    c["fused_cold"].append(t_fused)
                 for si, name in enumerate(STAGES):
                     if name in ("route_prep", "combine") and c["plan"].path == 2:
                         continue
@@ -621,6 +640,8 @@ def main():
                          "fp16_route": c["plan"].fp16_route},
                 "stage_us": {k: round(v, 3) for k, v in st.items()},
                 "router_us_cold": round(statistics.fmean(c["router"]), 3),
+                "fused_finalize_us_cold": (round(statistics.fmean(c["fused_cold"]), 3)
+                                           if c["fused_cold"] else None),
                 "routed": {
                     "latency_us_cold": round(statistics.fmean(c["routed_cold"]), 3),
                     "fused_stage": "routing + route preparation" if c["plan"].path == 1

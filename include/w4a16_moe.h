@@ -118,6 +118,15 @@ typedef struct {
                                  bits.  Activations of 2^16 or more and scales
                                  outside 2^-17..2720 are detected and those
                                  tiles recomputed per group                      */
+  int32_t fused_finalize;     /* grouped path, the two finalize modes of [P2]
+                                 Description: 0 (default) non-fused, the 16-bit
+                                 expert outputs then a combine launch of its
+                                 own; 1 fused, the combine inside the down GEMM
+                                 launch (the workgroup whose arrival completes a
+                                 token's routes for a column chunk combines it;
+                                 not with the opted-in fp16 down route).  Same
+                                 bits either way; the fused mode is slower on
+                                 MI355X (one L2 write-back per workgroup).      */
 } w4a16_moe_desc_t;
 
 /* Variant the library runs for a descriptor (for tests and reports). */
@@ -140,6 +149,8 @@ typedef struct {
                                  group scale outside 2^-17..2720, and was rerun
                                  per group); 0 if none                           */
   int32_t rerun_flags_down;   /* likewise for the down GEMM                      */
+  int32_t fused_combine;      /* 1: the combine runs inside the down launch
+                                 (fused finalize)                                */
   size_t rerun_flags_offset;  /* workspace byte offset of the flags: the gate/up
                                  launch's rerun_flags_up flags, then the down
                                  launch's rerun_flags_down (0 if neither launch
@@ -169,7 +180,11 @@ w4a16_status_t w4a16_moe_get_plan(const w4a16_moe_desc_t* desc, w4a16_moe_plan_t
  *   workspace     device scratch of at least w4a16_moe_workspace_size bytes;
  *                 its contents on entry do not matter and are clobbered.
  * The result does not depend on scheduling: every sum has a fixed order, so
- * repeated calls with the same inputs and variant give identical bits. */
+ * repeated calls with the same inputs and variant give identical bits; the
+ * fused finalize (descriptor) gives the same bits as the non-fused one, the
+ * workgroup that combines a token being decided by integer arrival counters
+ * in the workspace ([P2] Description: no atomic or reduction into the
+ * output). */
 w4a16_status_t w4a16_moe_forward(const void* x, const uint8_t* w13_packed,
                                  const void* w13_scales, const uint8_t* w2_packed,
                                  const void* w2_scales, const int32_t* topk_ids,
@@ -180,8 +195,10 @@ w4a16_status_t w4a16_moe_forward(const void* x, const uint8_t* w13_packed,
 /* w4a16_moe_forward, plus stage timing: stage_events[2*i] and
  * stage_events[2*i+1] (hipEvent_t created by the caller; null entries are
  * skipped) are recorded on `stream` right before and after stage i:
- *   i = 0 route preparation, 1 gate/up GEMM, 2 down GEMM (fused with the
- *   combine in the per-token variant), 3 combine (grouped variant only).
+ *   i = 0 route preparation, 1 gate/up GEMM, 2 down GEMM (with the combine
+ *   when it runs inside the down launch: the small-batch path, and the
+ *   grouped path with fused_finalize = 1), 3 the combine launch (recorded
+ *   back to back, empty, when the combine is fused).
  * n_events is the length of stage_events (0..8).  Same results as the
  * forward; meant for benchmarks. */
 w4a16_status_t w4a16_moe_forward_timed(const void* x, const uint8_t* w13_packed,

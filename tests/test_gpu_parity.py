@@ -359,6 +359,8 @@ POISON_CASES = [
     ("kimi_tp8", 32, dict()),                         # automatic plan: split-K
     ("deepseek_local", 16, dict()),                   # split-K over column chunks
     ("tiny", 256, dict(force_path=1, fp16_route=1)),
+    ("kimi_tp8", 256, dict(fused_finalize=1)),        # arrival counters start as 0xFF..
+    ("deepseek_local", 16, dict(fused_finalize=1)),   # tokens without local routes
 ]
 
 
@@ -375,7 +377,7 @@ def test_poisoned_workspace_and_output(name, T, force):
     tg = tc.to("cuda")
     ref = oracle_out(wl, Wc, tc)
     d = binding.desc_for(wl, T, **force)
-    if name == "kimi_tp8":
+    if name == "kimi_tp8" and T == 32:
         assert binding.get_plan(d).splitk_chunks > 0
     ws = torch.full((binding.workspace_size(d),), 0xFF, dtype=torch.uint8, device="cuda")
     out = torch.full((T, wl.hidden), float("nan"), dtype=wl.dtype, device="cuda")
@@ -496,7 +498,8 @@ GRAPH_CASES = [("kimi_tp8", 1, dict()), ("kimi_tp8", 32, dict()),
                ("kimi_tp8", 256, dict(fp16_route=1)), ("kimi_tp8", 1024, dict(fp16_route=1)),
                ("per_channel", 8, dict()), ("per_channel", 256, dict()),
                ("relu2_skew", 32, dict()), ("relu2_skew", 1024, dict()),
-               ("deepseek_local", 16, dict())]
+               ("deepseek_local", 16, dict()), ("kimi_tp8", 256, dict(fused_finalize=1)),
+               ("relu2_skew", 1024, dict(fused_finalize=1))]
 
 
 @pytest.mark.parametrize("name,T,force", GRAPH_CASES,
@@ -535,3 +538,29 @@ def test_hip_graph_replay(name, T, force):
         forward(wl, Wg, tg, **force)              # eager work between replays
     if T <= 32:
         assert_close(out, oracle_out(wl, Wc, tokens(wl, T)), f"graph {name} T={T}")
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 256), ("kimi_tp8", 32), ("kimi_tp8", 256),
+                                    ("kimi_tp8", 2048), ("deepseek_local", 16),
+                                    ("deepseek_local", 512), ("per_channel", 256),
+                                    ("relu2_skew", 1024)])
+def test_fused_finalize_matches_separate_launch(name, T):
+    """The fused finalize (the combine inside the down launch: the workgroup
+    that completes a token's routes for a column chunk sums them in ascending
+    k) gives the same bits as the default combine launch of its own, for the
+    resident (I <= 256) and the streaming down kernels, tokens without local
+    routes included, and repeats bitwise (the arrival order varies from run
+    to run)."""
+    wl = synth.WORKLOADS[name]
+    _, Wg = weights(name)
+    tg = tokens(wl, T, "cuda")
+    assert binding.get_plan(binding.desc_for(wl, T)).fused_combine == 0
+    assert binding.get_plan(binding.desc_for(wl, T, fused_finalize=1)).fused_combine == 1
+    sep = forward(wl, Wg, tg)
+    for _ in range(3):
+        d = binding.desc_for(wl, T, fused_finalize=1)
+        ws = torch.full((binding.workspace_size(d),), 0xFF, dtype=torch.uint8, device="cuda")
+        out = torch.full((T, wl.hidden), float("nan"), dtype=wl.dtype, device="cuda")
+        binding.forward_workload(wl, Wg, tg, out=out, workspace=ws, fused_finalize=1)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), sep.view(torch.int16)), name

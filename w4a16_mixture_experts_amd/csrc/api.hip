@@ -52,8 +52,10 @@ struct Plan {
   bool x16 = false;       // streaming tile launches take the exact fp16 route
   bool x16_down = false;  // so does the resident down GEMM
   int64_t n_redo_up = 0, n_redo_down = 0;  // rerun flags of those launches
+  bool fused_fin = false;  // the combine runs inside the down launch
   size_t off_counts = 0, off_offsets = 0, off_slot = 0, off_sorted = 0, off_tile = 0,
-         off_act = 0, off_y = 0, off_part = 0, off_chunks = 0, off_redo = 0, total = 0;
+         off_act = 0, off_y = 0, off_part = 0, off_chunks = 0, off_redo = 0, off_fin = 0,
+         total = 0;
 };
 
 w4a16_status_t check_desc(const w4a16_moe_desc_t* d) {
@@ -93,6 +95,8 @@ w4a16_status_t check_desc(const w4a16_moe_desc_t* d) {
     return fail(W4A16_ERR_INVALID_ARG, "desc.force_splitk: %d (0, 1 or 2)", d->force_splitk);
   if (d->fp16_route != 0 && d->fp16_route != 1)
     return fail(W4A16_ERR_INVALID_ARG, "desc.fp16_route: %d (0 or 1)", d->fp16_route);
+  if (d->fused_finalize < 0 || d->fused_finalize > 1)
+    return fail(W4A16_ERR_INVALID_ARG, "desc.fused_finalize: %d (0 or 1)", d->fused_finalize);
   if (d->num_global_experts != 0 && d->num_global_experts < d->num_local_experts)
     return fail(W4A16_ERR_INVALID_ARG, "desc.num_global_experts: %d < num_local_experts %d",
                 d->num_global_experts, d->num_local_experts);
@@ -217,6 +221,15 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
     pl.n_tiles_down = static_cast<int>((steps + pl.col_steps - 1) / pl.col_steps);
   }
 
+  // fused finalize on request ([P2]'s fused mode: the combine inside the down
+  // launch, arrival counters per token and column chunk), except on the
+  // opted-in fp16 down route, whose rerun launch would count routes twice.
+  // Not the default: measured on MI355X it is about twice as slow as the
+  // combine launch of its own (Kimi shard down + combine at 256 tokens: 212
+  // against 110 us), since each workgroup's agent-scope release is an L2
+  // write-back
+  pl.fused_fin = pl.path == 1 && pl.R > 0 && !pl.x16_down && d->fused_finalize == 1;
+
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -236,6 +249,8 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
     pl.off_y = take(sizeof(uint16_t) * std::max<int64_t>(pl.R, 1) * H);  // Y rows by route
     if (pl.splitk_S > 0)
       pl.off_part = take(sizeof(float) * static_cast<size_t>(pl.splitk_S) * pl.R * pl.N1);
+    if (pl.fused_fin)
+      pl.off_fin = take(sizeof(int32_t) * static_cast<size_t>(d->num_tokens) * pl.n_tiles_down);
     // rerun flags of the fp16-route launches: the gate/up launch's, then the
     // down launch's
     const int64_t mt = std::max<int64_t>(pl.MT, 1);
@@ -334,6 +349,7 @@ w4a16_status_t w4a16_moe_get_plan(const w4a16_moe_desc_t* desc, w4a16_moe_plan_t
   plan->rerun_flags_up = up16 ? static_cast<int32_t>(pl.n_redo_up) : 0;
   plan->rerun_flags_down = dn16 ? static_cast<int32_t>(pl.n_redo_down) : 0;
   plan->rerun_flags_offset = (up16 || dn16) ? pl.off_redo : 0;
+  plan->fused_combine = pl.fused_fin ? 1 : 0;
   return W4A16_OK;
 }
 
@@ -489,11 +505,13 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
   // a1: route preparation into block_m-row expert tiles
   st = hip_status(evs.mark(0), "stage event");
   if (st != W4A16_OK) return st;
+  auto* fin_cnt = pl.fused_fin ? reinterpret_cast<int32_t*>(ws + pl.off_fin) : nullptr;
   st = hip_status(w4moe::launch_route_prep(topk_ids, static_cast<int>(pl.R), E,
                                            desc->expert_offset, pl.bm, counts, offsets, sorted,
                                            slot, tile,
                                            reinterpret_cast<int32_t*>(ws + pl.off_chunks), stream,
-                                           K, route),
+                                           K, route, fin_cnt,
+                                           static_cast<int64_t>(desc->num_tokens) * pl.n_tiles_down),
                   route != nullptr ? "routing and route preparation launch"
                                    : "route preparation launch");
   if (st == W4A16_OK) st = hip_status(evs.mark(1), "stage event");
@@ -574,6 +592,16 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
   dn.redo = pl.n_redo_down > 0
                 ? reinterpret_cast<int32_t*>(ws + pl.off_redo) + pl.n_redo_up
                 : nullptr;
+  if (pl.fused_fin) {
+    dn.fin_cnt = fin_cnt;
+    dn.wts = topk_weights;
+    dn.fin_out = static_cast<uint16_t*>(out);
+    dn.fin_chunks = pl.n_tiles_down;
+    dn.T = desc->num_tokens;
+    dn.slot = slot;
+    dn.n_main = static_cast<int>(
+        w4moe::tile_launch_workgroups(pl.n_tiles_down, std::max<int64_t>(pl.MT, 1)));
+  }
   st = hip_status(evs.mark(4), "stage event");
   if (st != W4A16_OK) return st;
   dn.col_steps = pl.col_steps;
@@ -586,7 +614,13 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
   if (st == W4A16_OK) st = hip_status(evs.mark(5), "stage event");
   if (st != W4A16_OK) return st;
 
-  // a6: FP32 combine in fixed top-k order, one 16-bit cast
+  // a6: FP32 combine in fixed top-k order, one 16-bit cast (inside the down
+  // launch when fused)
+  if (pl.fused_fin) {  // the combine stage is empty: events back to back
+    st = hip_status(evs.mark(6), "stage event");
+    if (st == W4A16_OK) st = hip_status(evs.mark(7), "stage event");
+    return st;
+  }
   w4moe::CombineParams cb{};
   cb.y = ybuf;
   cb.slot = slot;

@@ -45,7 +45,24 @@ struct GemmParams {
   // streaming tile kernel, bf16 group layout: non-null selects the exact
   // fp16 route; one flag per workgroup (set when its tile is to be rerun)
   int32_t* redo;
+  // DOWN with the combine fused in: non-null selects it.  fin_cnt holds one
+  // arrival counter per (token, column chunk), zeroed by route preparation;
+  // the workgroup whose arrival completes a token's valid routes for a chunk
+  // combines them (slot: route -> position, -1 invalid; wts [T][K]) into
+  // fin_out; workgroups from n_main on write zeros for tokens without a
+  // valid route.
+  int32_t* fin_cnt;
+  const float* wts;
+  uint16_t* fin_out;
+  int fin_chunks;
+  int T;
+  int n_main;
 };
+
+// Workgroups that zero the output rows of tokens without a valid route
+// (fused combine): one wave per token.
+constexpr int kFinZeroTokens = kTileWaves;
+inline int fin_zero_workgroups(int T) { return (T + kFinZeroTokens - 1) / kFinZeroTokens; }
 
 // small-batch path
 constexpr int kDecMaxItems = 256;         // (route, slice) items per token
@@ -125,10 +142,13 @@ struct CombineParams {
 // the preparation.  top_k: routes per token.
 constexpr int kRouteChunksMax = 32;
 int route_prep_chunk(int R);
+// zero: n_zero int32 that the preparation sets to 0 (the fused combine's
+// arrival counters), or null.
 hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, int32_t* counts,
                              int32_t* offsets, int32_t* sorted, int32_t* slot,
                              int32_t* tile_expert, int32_t* chunk_hist, hipStream_t stream,
-                             int top_k = 1, const RouteArgs* route = nullptr);
+                             int top_k = 1, const RouteArgs* route = nullptr,
+                             int32_t* zero = nullptr, int64_t n_zero = 0);
 
 // 64-row expert tiles (route positions), LDS-staged activations
 constexpr int kResidentK = 256;      // reduction the resident down kernel holds in LDS

@@ -106,8 +106,10 @@ __global__ void __launch_bounds__(kRpScanThreads)
 rp_one_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm,
               int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
               int32_t* __restrict__ sorted, int32_t* __restrict__ slot,
-              int32_t* __restrict__ tile_expert, int top_k, RouteArgs ra) {
+              int32_t* __restrict__ tile_expert, int top_k, RouteArgs ra,
+              int32_t* __restrict__ zero, int64_t n_zero) {
   constexpr int kW = kRpScanThreads / 64;
+  for (int64_t i = threadIdx.x; i < n_zero; i += kRpScanThreads) zero[i] = 0;
   __shared__ int32_t hist[kW][kRpMaxExperts];
   __shared__ int32_t wave_tot[kW];
   __shared__ int32_t s_off[kRpMaxExperts + 1];
@@ -218,8 +220,12 @@ rp_one_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm,
 
 __global__ void __launch_bounds__(kRpThreads)
 rp_rank_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int chunk,
-               int32_t* __restrict__ slot, int32_t* __restrict__ chunk_hist) {
+               int32_t* __restrict__ slot, int32_t* __restrict__ chunk_hist,
+               int32_t* __restrict__ zero, int64_t n_zero) {
   constexpr int NW = kRpWaves;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kRpThreads + threadIdx.x; i < n_zero;
+       i += static_cast<int64_t>(gridDim.x) * kRpThreads)
+    zero[i] = 0;
   __shared__ int32_t hist[NW][kRpMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = blockIdx.x;
@@ -413,8 +419,9 @@ constexpr int kRpRouteMaxTokens = kRpScanThreads / 64;
 hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, int32_t* counts,
                              int32_t* offsets, int32_t* sorted, int32_t* slot,
                              int32_t* tile_expert, int32_t* chunk_hist, hipStream_t stream,
-                             int top_k, const RouteArgs* route) {
+                             int top_k, const RouteArgs* route, int32_t* zero, int64_t n_zero) {
   if (E < 1 || E > kRpMaxExperts || R < 0) return hipErrorInvalidValue;
+  if (zero == nullptr) n_zero = 0;
   // without scratch: one chunk, whose counts live in `counts` itself (the
   // scan overwrites them with the totals) and whose base is 0
   const bool one = chunk_hist == nullptr;
@@ -436,7 +443,7 @@ hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, 
         default: break;
       }
       hipLaunchKernelGGL(k, dim3(1), dim3(kRpScanThreads), 0, stream, ids, R, E, off, bm, counts,
-                         offsets, sorted, slot, tile_expert, top_k, ra);
+                         offsets, sorted, slot, tile_expert, top_k, ra, zero, n_zero);
       return hipGetLastError();
     }
     const hipError_t err = launch_router_topk(ra.logits, ra.T, ra.Eg, top_k, ra.renorm, ra.ids,
@@ -447,12 +454,12 @@ hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, 
   if (R <= kRpOneRoutes) {
     hipLaunchKernelGGL((rp_one_kernel<kRpOneMaxPieces, 0>), dim3(1), dim3(kRpScanThreads), 0,
                        stream, ids, R, E, off, bm, counts, offsets, sorted, slot, tile_expert,
-                       top_k, RouteArgs{});
+                       top_k, RouteArgs{}, zero, n_zero);
     return hipGetLastError();
   }
   // R > kRpOneRoutes here, so there is at least one chunk
   hipLaunchKernelGGL(rp_rank_kernel, dim3(n_chunks), dim3(kRpThreads), 0, stream, ids, R, E, off,
-                     chunk, slot, hist);
+                     chunk, slot, hist, zero, n_zero);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(rp_scatter_kernel, dim3(n_chunks), dim3(kRpScanThreads), 0, stream, ids, R,

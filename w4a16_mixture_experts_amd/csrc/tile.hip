@@ -420,6 +420,109 @@ __device__ __forceinline__ void mma_block_x(const uint16_t* sa, int stride,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fused finalize: the combine inside the down GEMM launch ([P2] Description:
+// fused and non-fused finalize modes; "Contract": the 16-bit expert outputs
+// are combined in FP32 in fixed top-k order before one 16-bit cast, with no
+// atomic or reduction into the output).  Each down
+// workgroup, once its Y rows for output columns [c0, c1) are stored, releases
+// them device-wide and counts its routes as arrived, one counter per (token,
+// column chunk).  The workgroup whose arrival completes a token's valid
+// routes for the chunk acquires and combines that token: acc = sum over k
+// ascending of w[t,k] * Y[t*K+k] (valid routes only), cast once.  Which
+// workgroup does it changes nothing in the result.  The counters (integer
+// atomics) only decide who combines; no value is accumulated atomically.
+// ---------------------------------------------------------------------------
+// s_waitcnt vmcnt(0), other counters untouched (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+template <int DT>
+__device__ __forceinline__ void finalize_arrivals(const GemmParams& p, int row_base, int chunk,
+                                                  int c0, int c1) {
+  using T = H16<DT>;
+  __shared__ int s_rows[kTileRows];
+  __shared__ int s_nlast;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  // release, once per workgroup: every wave waits for its Y stores to reach
+  // the L2, then one agent-scope release (on this chip an L2 write-back, the
+  // dominant cost of the fused form) makes them visible device-wide before
+  // any of the workgroup's routes counts as arrived
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  if (w == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int route = p.sorted[row_base + lane];
+    bool last = false;
+    if (route >= 0) {
+      const int t = route / p.top_k;
+      int nvalid = 0;
+      for (int k = 0; k < p.top_k; ++k) nvalid += p.slot[t * p.top_k + k] >= 0 ? 1 : 0;
+      const int old = __hip_atomic_fetch_add(p.fin_cnt + static_cast<int64_t>(t) * p.fin_chunks + chunk,
+                                             1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = old == nvalid - 1;
+    }
+    const uint64_t m = __ballot(last);
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    if (last) s_rows[__popcll(m & below)] = route / p.top_k;
+    if (lane == 0) s_nlast = __popcll(m);
+  }
+  __syncthreads();
+  const int nlast = s_nlast;
+  if (nlast == 0) return;
+  // acquire: the other workgroups' Y rows of these tokens are visible
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int ng = (c1 - c0) / 8;  // 16-byte column groups of the chunk
+  constexpr int kB = 8;          // routes whose Y loads are in flight together
+  for (int i = tid; i < nlast * ng; i += kTileThreads) {
+    const int t = s_rows[i / ng];
+    const int col = c0 + 8 * (i % ng);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < p.top_k; kb += kB) {
+      u32x4 v[kB];
+      float wk[kB];
+      bool ok[kB];
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        const int r = t * p.top_k + kb + k;
+        ok[k] = kb + k < p.top_k && p.slot[r] >= 0;
+        wk[k] = ok[k] ? p.wts[r] : 0.0f;
+        v[k] = ok[k] ? *reinterpret_cast<const u32x4*>(p.out + static_cast<int64_t>(r) * p.ldo + col)
+                     : u32x4{0u, 0u, 0u, 0u};
+      }
+      // fixed order: ascending k, invalid routes contribute nothing
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        if (!ok[k]) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[2 * j] += wk[k] * T::to_f32(v[k][j] & 0xffffu);
+          acc[2 * j + 1] += wk[k] * T::to_f32(v[k][j] >> 16);
+        }
+      }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = static_cast<uint32_t>(T::from_f32(acc[2 * j])) |
+             (static_cast<uint32_t>(T::from_f32(acc[2 * j + 1])) << 16);
+    *reinterpret_cast<u32x4*>(p.fin_out + static_cast<int64_t>(t) * p.ldo + col) = o;
+  }
+}
+
+// Zeros of the output rows of tokens without a valid route (they never
+// arrive anywhere): workgroup z takes tokens kFinZeroTokens * z + wave.
+__device__ __forceinline__ void finalize_zero_rows(const GemmParams& p, int z) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = z * kFinZeroTokens + w;
+  if (t >= p.T) return;  // whole wave
+  const bool any = __ballot(lane < p.top_k && p.slot[t * p.top_k + lane] >= 0) != 0ull;
+  if (any) return;
+  uint16_t* row = p.fin_out + static_cast<int64_t>(t) * p.ldo;
+  for (int col = 8 * lane; col < p.n_cols; col += 8 * 64)
+    *reinterpret_cast<u32x4*>(row + col) = u32x4{0u, 0u, 0u, 0u};
+}
+
 // Valid rows of the lane's 16 * NMS output rows as a bit mask: bit 4ms + i
 // stands for tile row 16ms + 4g + i.
 template <int NMS>
@@ -796,11 +899,29 @@ tile_gemm_kernel(const GemmParams p) {
   // [2 stages][2 blocks][kTileRows][kAStride] activations, then (SCL) the
   // group scales: [256 rows][K / 32] or [256 rows][kScPhaseGroups]
   extern __shared__ __align__(16) uint16_t s_lds[];
+  const int L = static_cast<int>(blockIdx.x);
+  if constexpr (MODE == MODE_DOWN && !X16) {
+    if (p.fin_cnt != nullptr && L >= p.n_main) {  // fused combine: empty tokens' rows
+      finalize_zero_rows(p, L - p.n_main);
+      return;
+    }
+  }
   // X16: every workgroup records whether its tile must be rerun (the flag
   // array needs no clearing)
-  const bool done = tile_work<DT, LAYOUT, MODE, SCL, X16>(p, static_cast<int>(blockIdx.x), s_lds);
+  const bool done = tile_work<DT, LAYOUT, MODE, SCL, X16>(p, L, s_lds);
   if constexpr (X16) {
     if (threadIdx.x == 0) p.redo[blockIdx.x] = done ? 0 : 1;
+  }
+  if constexpr (MODE == MODE_DOWN && !X16) {
+    if (p.fin_cnt != nullptr) {
+      // the workgroup's tile and column tile (as tile_work derives them)
+      const int q = L / kXcds;
+      const int mt = kXcds * (q / p.n_tiles) + L % kXcds;
+      const int nt = q % p.n_tiles;
+      const int row_base = mt * kTileRows;
+      const int c0 = nt * kTileColsPlain, c1 = min(p.n_cols, c0 + kTileColsPlain);
+      if (row_base < p.offsets[p.E] && c0 < c1) finalize_arrivals<DT>(p, row_base, nt, c0, c1);
+    }
   }
 }
 
@@ -1013,6 +1134,10 @@ down_resident_kernel(const GemmParams p) {
 
   // same XCD-aware order as the streaming kernel (n_tiles = column chunks)
   const int L = blockIdx.x;
+  if (p.fin_cnt != nullptr && L >= p.n_main) {  // fused combine: empty tokens' rows
+    finalize_zero_rows(p, L - p.n_main);
+    return;
+  }
   const int q = L / kXcds;
   const int mt = kXcds * (q / p.n_tiles) + L % kXcds;
   const int chunk = q % p.n_tiles;
@@ -1039,6 +1164,11 @@ down_resident_kernel(const GemmParams p) {
                                                   s_out[threadIdx.x >> 6]); break;
     default: down_resident_run<DT, LAYOUT, 4, NKB>(p, row_base, e, chunk, s_ar,
                                                   s_out[threadIdx.x >> 6]); break;
+  }
+  if (p.fin_cnt != nullptr) {
+    const int c0 = chunk * p.col_steps * kTileColsPlain;
+    const int c1 = min(p.n_cols, c0 + p.col_steps * kTileColsPlain);
+    if (c0 < c1) finalize_arrivals<DT>(p, row_base, chunk, c0, c1);
   }
 }
 
@@ -1683,7 +1813,9 @@ static hipError_t launch_resident_dl(const GemmParams& p, dim3 grid, hipStream_t
 hipError_t launch_down_resident(const GemmParams& p, int dtype, int layout, int max_tiles,
                                 hipStream_t stream) {
   if (p.K > kResidentK || p.col_steps < 1) return hipErrorInvalidValue;
-  const dim3 grid(kXcds * p.n_tiles * ((max_tiles + kXcds - 1) / kXcds));
+  const int n_main = kXcds * p.n_tiles * ((max_tiles + kXcds - 1) / kXcds);
+  if (p.fin_cnt != nullptr && (p.n_main != n_main || p.redo != nullptr)) return hipErrorInvalidValue;
+  const dim3 grid(n_main + (p.fin_cnt != nullptr ? fin_zero_workgroups(p.T) : 0));
   if (dtype == DT_BF16)
     return layout == Q_GROUP_K ? launch_resident_dl<DT_BF16, Q_GROUP_K>(p, grid, stream)
                                : launch_resident_dl<DT_BF16, Q_PER_CHANNEL>(p, grid, stream);
@@ -1693,7 +1825,11 @@ hipError_t launch_down_resident(const GemmParams& p, int dtype, int layout, int 
 
 hipError_t launch_tile_gemm(const GemmParams& p, int dtype, int layout, int mode, int max_tiles,
                             hipStream_t stream) {
-  const dim3 grid(kXcds * p.n_tiles * ((max_tiles + kXcds - 1) / kXcds));
+  const int n_main = kXcds * p.n_tiles * ((max_tiles + kXcds - 1) / kXcds);
+  const bool fin = mode == MODE_DOWN && p.fin_cnt != nullptr;
+  if (p.fin_cnt != nullptr && (mode != MODE_DOWN || p.n_main != n_main || p.redo != nullptr))
+    return hipErrorInvalidValue;
+  const dim3 grid(n_main + (fin ? fin_zero_workgroups(p.T) : 0));
   if (dtype == DT_BF16)
     return layout == Q_GROUP_K ? launch_tile_mode<DT_BF16, Q_GROUP_K>(p, mode, grid, stream)
                                : launch_tile_mode<DT_BF16, Q_PER_CHANNEL>(p, mode, grid, stream);
