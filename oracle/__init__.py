@@ -26,7 +26,7 @@ _lib = None
 
 DT_BF16, DT_FP16 = 0, 1
 ACT_SILU_GATED, ACT_RELU2 = 0, 1
-Q_GROUP_K, Q_PER_CHANNEL = 0, 1
+Q_GROUP_K, Q_PER_CHANNEL, Q_FP4_GROUP_K = 0, 1, 2
 
 
 def build() -> str:
@@ -60,6 +60,9 @@ def _load():
     lib.oracle_moe_forward.restype = ctypes.c_int
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_route_topk.argtypes = [P, i64, i32, i32, i32, P, P]
+    lib.oracle_unpack_fp4.argtypes = [P, i64, P]
+    lib.oracle_e8m0_to_f32.argtypes = [P, i64, P]
+    lib.oracle_quantize_mxfp4.argtypes = [P, i64, i64, P, P]
     _lib = lib
     return lib
 
@@ -187,3 +190,29 @@ def route_topk(logits, top_k: int, renormalize: bool = False):
     _load().oracle_route_topk(_p(logits), T, Eg, top_k, 1 if renormalize else 0, _p(ids),
                               _p(wts))
     return ids, wts
+
+
+def unpack_fp4(packed) -> np.ndarray:
+    """E2M1 codes, two per byte (even index in the low nibble), as float32."""
+    b = _c(packed, np.uint8).ravel()
+    out = np.empty(2 * b.size, np.float32)
+    _load().oracle_unpack_fp4(_p(b), b.size, _p(out))
+    return out
+
+
+def e8m0_to_f32(codes) -> np.ndarray:
+    c = _c(codes, np.uint8).ravel()
+    out = np.empty(c.size, np.float32)
+    _load().oracle_e8m0_to_f32(_p(c), c.size, _p(out))
+    return out.reshape(np.shape(codes))
+
+
+def quantize_mxfp4(w):
+    """MXFP4 along the last axis in blocks of 32: (packed uint8 [.., cols/2],
+    E8M0 uint8 [.., cols/32])."""
+    w = _c(w, np.float32)
+    rows, cols = int(np.prod(w.shape[:-1])), w.shape[-1]
+    packed = np.empty((rows, cols // 2), np.uint8)
+    sc = np.empty((rows, cols // 32), np.uint8)
+    _load().oracle_quantize_mxfp4(_p(w), rows, cols, _p(packed), _p(sc))
+    return packed.reshape(*w.shape[:-1], cols // 2), sc.reshape(*w.shape[:-1], cols // 32)

@@ -35,6 +35,17 @@
  * combine).  Build with -ffp-contract=off so that no multiply-add is fused and
  * every sum is the plain ascending-index sum written below.
  *
+ * FP4 weights ([P2] Final performance measures the DeepSeek-like share with
+ * 4-bit floating-point (NVFP4) weights and BF16 activations): the variant
+ * built here is the OCP microscaling form that gfx950 supports natively,
+ * MXFP4 -- E2M1 codes (sign, 2 exponent bits with bias 1, 1 mantissa bit;
+ * magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte along K with the even
+ * index in the low nibble, one power-of-two scale (E8M0: 2^(e - 127)) per 32
+ * consecutive values of K.  The scale reaches the forward as a 16-bit float
+ * (every E8M0 power of two in the bf16 range is exact in bf16), so the FP4
+ * layout of the forward takes any 16-bit group scale; W = e2m1(code) * s is
+ * exact in FP32 (2 + 11 significant bits).
+ *
  * Readings of points the pages leave open (each is listed with its reason in
  * the design notes of the repository):
  *   - INT4 values are two's-complement signed (-8..7).
@@ -53,7 +64,7 @@
 
 enum { OR_DT_BF16 = 0, OR_DT_FP16 = 1 };
 enum { OR_ACT_SILU_GATED = 0, OR_ACT_RELU2 = 1 };
-enum { OR_Q_GROUP_K = 0, OR_Q_PER_CHANNEL = 1 };
+enum { OR_Q_GROUP_K = 0, OR_Q_PER_CHANNEL = 1, OR_Q_FP4_GROUP_K = 2 };
 
 /* ------------------------------------------------------------------------ */
 /* 16-bit float encodings (IEEE binary16 and bfloat16), written out by hand.  */
@@ -146,6 +157,88 @@ void oracle_pack_int4(const int8_t* q, int64_t n, uint8_t* out) {
 }
 
 /* ------------------------------------------------------------------------ */
+/* FP4 E2M1 and E8M0 (OCP microscaling formats).                             */
+/* ------------------------------------------------------------------------ */
+
+/* E2M1 code c (bit 3 sign, bits 2..1 exponent with bias 1, bit 0 mantissa):
+ * exponent 0 is subnormal, magnitude m * 0.5; otherwise (1 + m/2) * 2^(e-1). */
+static float e2m1_to_f32(int c) {
+  int sign = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+  float mag = (e == 0) ? 0.5f * (float)m : ldexpf(1.0f + 0.5f * (float)m, e - 1);
+  return sign ? -mag : mag;
+}
+
+void oracle_unpack_fp4(const uint8_t* packed, int64_t n_bytes, float* out) {
+  for (int64_t i = 0; i < n_bytes; ++i) {
+    out[2 * i] = e2m1_to_f32(packed[i] & 0xf);
+    out[2 * i + 1] = e2m1_to_f32(packed[i] >> 4);
+  }
+}
+
+/* E8M0: 2^(e - 127); e = 255 is NaN. */
+static float e8m0_to_f32(uint8_t e) { return e == 255 ? NAN : ldexpf(1.0f, (int)e - 127); }
+
+void oracle_e8m0_to_f32(const uint8_t* in, int64_t n, float* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = e8m0_to_f32(in[i]);
+}
+
+/* Nearest E2M1 code to v (|v| saturates at 6), ties to the code with an even
+ * mantissa bit: the magnitudes are walked in order and a tie goes to the
+ * candidate whose mantissa bit is 0. */
+static int f32_to_e2m1(float v) {
+  int sign = v < 0.0f || (v == 0.0f && signbit(v));
+  float a = fabsf(v);
+  int best = 0;
+  float best_d = INFINITY;
+  for (int c = 0; c < 8; ++c) {
+    float d = fabsf(a - e2m1_to_f32(c));
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  if (a > 6.0f) best = 7;  /* saturate (also catches values beyond the last midpoint) */
+  return (sign ? 8 : 0) | best;
+}
+
+/* MXFP4 quantization of w [rows][cols] along cols in blocks of 32: the shared
+ * exponent is floor(log2(max |w|)) - 2 (2 = the exponent of E2M1's largest
+ * magnitude), clamped to the E8M0 range; codes are w / 2^exp rounded to the
+ * nearest E2M1 value (ties to even, saturating).  A block of zeros gets
+ * E8M0 code 0 and zero codes.  packed [rows][cols/2], e8m0 [rows][cols/32]. */
+void oracle_quantize_mxfp4(const float* w, int64_t rows, int64_t cols, uint8_t* packed,
+                           uint8_t* e8m0) {
+  int64_t ng = cols / 32;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t g = 0; g < ng; ++g) {
+      const float* src = w + r * cols + g * 32;
+      float amax = 0.0f;
+      for (int j = 0; j < 32; ++j) {
+        float a = fabsf(src[j]);
+        if (a > amax) amax = a;
+      }
+      int e = 0;
+      int codes[32];
+      if (amax == 0.0f) {
+        for (int j = 0; j < 32; ++j) codes[j] = 0;
+      } else {
+        int ex;
+        (void)frexpf(amax, &ex);  /* amax = m * 2^ex, m in [0.5, 1): floor(log2 amax) = ex - 1 */
+        int x = ex - 1 - 2;
+        if (x < -127) x = -127;
+        if (x > 127) x = 127;
+        e = x + 127;
+        float s = ldexpf(1.0f, x);
+        for (int j = 0; j < 32; ++j) codes[j] = f32_to_e2m1(src[j] / s);
+      }
+      e8m0[r * ng + g] = (uint8_t)e;
+      for (int j = 0; j < 16; ++j)
+        packed[r * (cols / 2) + g * 16 + j] =
+            (uint8_t)((codes[2 * j] & 0xf) | ((codes[2 * j + 1] & 0xf) << 4));
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Symmetric quantization, scale = absmax / 7 ([P3] Checkpoint format).       */
 /* The scale is stored in 16 bits; q = clamp(round_half_even(w / s), -8, 7)   */
 /* with the division by the stored (rounded) scale; an all-zero group has     */
@@ -198,6 +291,7 @@ void oracle_quantize_per_channel(const float* w, int64_t rows, int64_t cols, int
 /* ------------------------------------------------------------------------ */
 /* Dequantization of one expert's matrix of logical shape [n_out][k_in].      */
 /* Group mode: packed [n_out][k_in/2] along K, scales [n_out][k_in/group].    */
+/* FP4 group mode: the same layout with E2M1 codes instead of INT4 values.   */
 /* Per-channel: packed [n_out/2][k_in] along N, scales [n_out].               */
 /* W[n][k] = float(q[n][k]) * float(s), exact in FP32.                       */
 /* ------------------------------------------------------------------------ */
@@ -209,6 +303,14 @@ void oracle_dequant_matrix(const uint8_t* packed, const uint16_t* scales, int64_
     for (int64_t k = 0; k < k_in; ++k) {
       int q;
       float s;
+      if (layout == OR_Q_FP4_GROUP_K) {
+        /* E2M1 codes along K, a 16-bit scale per group: exact in FP32 */
+        uint8_t b = packed[n * (k_in / 2) + k / 2];
+        float v = e2m1_to_f32((k % 2 == 0) ? (b & 0xf) : (b >> 4));
+        s = h16_to_f32(scales[n * (k_in / group) + k / group], dtype);
+        w_out[n * k_in + k] = v * s;
+        continue;
+      }
       if (layout == OR_Q_GROUP_K) {
         uint8_t b = packed[n * (k_in / 2) + k / 2];
         q = sext4((k % 2 == 0) ? (b & 0xf) : (b >> 4));
@@ -294,8 +396,9 @@ int oracle_moe_forward(int64_t T, int32_t H, int32_t I, int32_t E, int32_t off, 
   const int64_t R = T * (int64_t)K;
   /* bytes and scale entries per expert in each layout */
   const int64_t w13_bytes = N1 * H / 2, w2_bytes = (int64_t)H * I / 2;
-  const int64_t w13_sc = (layout == OR_Q_GROUP_K) ? N1 * (H / group) : N1;
-  const int64_t w2_sc = (layout == OR_Q_GROUP_K) ? (int64_t)H * (I / group) : H;
+  const int grouped = layout == OR_Q_GROUP_K || layout == OR_Q_FP4_GROUP_K;
+  const int64_t w13_sc = grouped ? N1 * (H / group) : N1;
+  const int64_t w2_sc = grouped ? (int64_t)H * (I / group) : H;
 
   float* Y = y_route ? y_route : (float*)malloc((size_t)(R > 0 ? R : 1) * H * sizeof(float));
   if (!Y) return -1;

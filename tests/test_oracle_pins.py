@@ -500,3 +500,163 @@ def test_route_topk_shift_invariance():
     ids2, w2 = oracle.route_topk(logits + np.float32(4.0), 8)
     np.testing.assert_array_equal(ids, ids2)
     np.testing.assert_allclose(w, w2, rtol=1e-5)
+
+
+# ---------------------------------------------------------------------------
+# FP4 (MXFP4: E2M1 codes, E8M0 block scales) weights
+# ---------------------------------------------------------------------------
+
+def _golden_table(name, conv):
+    out = []
+    for ln in open(os.path.join(GOLDEN, name)):
+        ln = ln.split("#")[0].strip()
+        if ln:
+            a, b = ln.split()[:2]
+            out.append(conv(a, b))
+    return out
+
+
+def _e2m1_golden():
+    tab = dict(_golden_table("fp4_e2m1.txt", lambda a, b: (int(a, 16), float(b))))
+    assert sorted(tab) == list(range(16))
+    return np.array([tab[c] for c in range(16)], np.float64)
+
+
+def np_dequant_fp4(packed, scales, dtype):
+    """fp64 [E, n, k] from E2M1 codes through the fixture's value table."""
+    tab = _e2m1_golden()
+    packed = np.asarray(packed, np.uint8)
+    codes = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), np.int64)
+    codes[..., 0::2] = packed & 0xF
+    codes[..., 1::2] = packed >> 4
+    return tab[codes] * np.repeat(np_h16(scales, dtype), 32, axis=-1)
+
+
+def test_fp4_code_table_exhaustive():
+    """Every byte: low nibble -> the even value, high nibble -> the odd one,
+    against the OCP value table of the fixture; signs of zero included."""
+    tab = _e2m1_golden()
+    b = np.arange(256, dtype=np.uint8)
+    got = oracle.unpack_fp4(b)
+    np.testing.assert_array_equal(got[0::2], tab[b & 0xF])
+    np.testing.assert_array_equal(got[1::2], tab[b >> 4])
+    np.testing.assert_array_equal(np.signbit(got[0::2]), (b & 0x8) != 0)
+    # the eight magnitudes, and symmetry
+    assert sorted(set(np.abs(tab).tolist())) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    np.testing.assert_array_equal(tab[8:], -tab[:8])
+
+
+def test_e8m0_decode_every_code():
+    e = np.arange(256, dtype=np.uint8)
+    got = oracle.e8m0_to_f32(e).astype(np.float64)
+    np.testing.assert_array_equal(got[:255], np.ldexp(1.0, e[:255].astype(np.int64) - 127))
+    assert np.isnan(got[255])
+
+
+def test_mxfp4_ties_fixture():
+    cases = _golden_table("mxfp4_ties.txt", lambda a, b: (float(a), int(b, 16)))
+    block = np.zeros(32, np.float32)
+    block[:len(cases)] = [v for v, _ in cases]
+    packed, sc = oracle.quantize_mxfp4(block[None])
+    assert sc[0, 0] == 127
+    codes = np.empty(32, np.int64)
+    codes[0::2], codes[1::2] = packed[0] & 0xF, packed[0] >> 4
+    for i, (v, want) in enumerate(cases):
+        assert codes[i] == want, (v, codes[i], want)
+    assert not codes[len(cases):].any()
+
+
+def test_mxfp4_round_trip_and_exponent():
+    """Blocks whose largest magnitude code is 4 or 6 keep their exponent:
+    quantize(code value * 2^x) gives back the codes and E8M0 x + 127, for
+    exponents across the E8M0 range that fp32 holds exactly."""
+    rng = np.random.default_rng(5)
+    tab = _e2m1_golden()
+    for x in (-120, -40, -7, 0, 3, 60, 120):
+        codes = rng.integers(0, 16, size=(8, 32))
+        codes[:, 0] = rng.choice([0x6, 0x7, 0xE, 0xF], size=8)   # a magnitude 4 or 6
+        w = (tab[codes] * 2.0 ** x).astype(np.float32)
+        packed, sc = oracle.quantize_mxfp4(w)
+        assert (sc == x + 127).all()
+        got = np.empty_like(codes)
+        got[:, 0::2], got[:, 1::2] = packed & 0xF, packed >> 4
+        np.testing.assert_array_equal(got, codes)
+    # an all-zero block: code 0 everywhere, E8M0 0
+    packed, sc = oracle.quantize_mxfp4(np.zeros((1, 64), np.float32))
+    assert not packed.any() and not sc.any()
+
+
+def test_generator_mxfp4_equals_oracle():
+    rng = np.random.default_rng(9)
+    w = (rng.standard_normal((48, 320)) * 0.02).astype(np.float32)
+    w[3, :32] = 0.0                                          # a zero block
+    w[4, 40] = 1e-3 * 2.0 ** -60                             # a block of tiny values
+    p, e = synth.quantize_mxfp4(torch.from_numpy(w))
+    po, eo = oracle.quantize_mxfp4(w)
+    np.testing.assert_array_equal(p.numpy(), po)
+    np.testing.assert_array_equal(e.numpy(), eo)
+    # the 16-bit scales are the exact powers of two
+    s16 = synth.e8m0_to_h16(torch.from_numpy(eo), torch.bfloat16)
+    np.testing.assert_array_equal(s16.float().numpy(), oracle.e8m0_to_f32(eo))
+
+
+def test_fp4_dequant_matrix_matches_numpy():
+    wl = synth.custom(E=1, H=64, I=96, K=1, fp4=True, seed=3)
+    W = synth.make_weights(wl)
+    got = oracle.dequant_matrix(W.w13_packed[0].numpy(), bits(W.w13_scales[0]), 2 * 96, 64,
+                                oracle.Q_FP4_GROUP_K, 32, oracle.DT_BF16)
+    want = np_dequant_fp4(W.w13_packed.numpy(), bits(W.w13_scales), oracle.DT_BF16)[0]
+    np.testing.assert_array_equal(got.astype(np.float64), want)        # exact in fp32
+
+
+def _fp4_closed_form(gated=True):
+    """As the INT4 closed form: gate weights 1.0 (code 0x2), up 2.0 (0x4),
+    down 1.0, scales 2^-6 and 2^-5, x = 1, H = 64, I = 32."""
+    H, I = 64, 32
+    N1 = 2 * I if gated else I
+    c13 = np.full((N1, H), 0x2, np.uint8)
+    if gated:
+        c13[I:] = 0x4
+    c2 = np.full((H, I), 0x2, np.uint8)
+    w13p = (c13[:, 0::2] | (c13[:, 1::2] << 4))[None].copy()
+    w2p = (c2[:, 0::2] | (c2[:, 1::2] << 4))[None].copy()
+    w13s = np.full((1, N1, H // 32), _bf16_bits(2.0 ** -6), np.uint16)
+    w2s = np.full((1, H, I // 32), _bf16_bits(2.0 ** -5), np.uint16)
+    x = np.full((1, H), _bf16_bits(1.0), np.uint16)
+    return oracle.moe_forward(x, w13p, w13s, w2p, w2s, np.zeros((1, 1), np.int32),
+                              np.ones((1, 1), np.float32), hidden=H, inter=I, num_experts=1,
+                              act=oracle.ACT_SILU_GATED if gated else oracle.ACT_RELU2,
+                              layout=oracle.Q_FP4_GROUP_K)
+
+
+def test_fp4_closed_form():
+    g = _golden_closed_form()
+    np.testing.assert_allclose(_fp4_closed_form(), g["gated_out"], rtol=1e-6)
+    np.testing.assert_allclose(_fp4_closed_form(gated=False), g["relu2_out_x_pos"], rtol=0)
+
+
+@pytest.mark.parametrize("gated,dtype", [(True, torch.bfloat16), (False, torch.float16)])
+def test_fp4_brute_force_dense_all_experts(gated, dtype):
+    E, H, I, K, T = 5, 64, 96, 2, 6
+    wl = synth.custom(E=E, H=H, I=I, K=K, gated=gated, dtype=dtype, fp4=True, seed=29)
+    W = synth.make_weights(wl)
+    tok = synth.make_tokens(wl, T)
+    ids = tok.topk_ids.numpy()
+    ids[1, 0] = E + 2                                          # an invalid route
+    dt = dt_code(wl)
+    out = oracle.moe_forward(
+        bits(tok.x), W.w13_packed.numpy(), bits(W.w13_scales), W.w2_packed.numpy(),
+        bits(W.w2_scales), ids, tok.topk_weights.numpy(), hidden=H, inter=I, num_experts=E,
+        act=oracle.ACT_SILU_GATED if gated else oracle.ACT_RELU2, layout=oracle.Q_FP4_GROUP_K,
+        dtype=dt)
+    w13 = np_dequant_fp4(W.w13_packed.numpy(), bits(W.w13_scales), dt)
+    w2 = np_dequant_fp4(W.w2_packed.numpy(), bits(W.w2_scales), dt)
+    x = np_h16(bits(tok.x), dt)
+    Y = np.stack([np_ffn(x, w13[e], w2[e], gated) for e in range(E)], axis=1)
+    M = np.zeros((T, E))
+    for t in range(T):
+        for k in range(K):
+            if 0 <= ids[t, k] < E:
+                M[t, ids[t, k]] += tok.topk_weights[t, k].item()
+    want = np.einsum("te,teh->th", M, Y)
+    np.testing.assert_allclose(out, want, rtol=1e-4, atol=1e-5 * np.abs(want).max())

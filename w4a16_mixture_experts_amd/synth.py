@@ -18,6 +18,10 @@ weights and router outputs):
                   #18313, Validation and Checkpoint format)
   relu2_skew      128 experts, H 2688, I 1856, top-6, non-gated ReLU^2, fp16,
                   skewed routing (TensorRT-LLM PR #18313, Validation)
+  *_fp4           the Kimi shard and the DeepSeek share with FP4 weights:
+                  MXFP4 (E2M1 codes, one power-of-two scale per 32 along K)
+                  standing in for the NVFP4 weights flashinfer PR #5186 (Final
+                  performance) measures, with 16-bit activations
 
 Recipe (fixed here, stated in the design notes):
   weights   fp32 ~ N(0, 0.02), drawn per expert in ascending order (w13_e then
@@ -29,6 +33,12 @@ Recipe (fixed here, stated in the design notes):
             rounded to the 16-bit dtype) and then router logits ~ N(0, 1)
             [T, E_global]; routing weights are softmax over all global experts,
             top-k (descending), no renormalisation; ids are int32.
+  fp4       the same fp32 weights quantized to MXFP4 in blocks of 32 along K:
+            exponent x = floor(log2(max |w|)) - 2, clamped to [-127, 127]
+            (E8M0 code x + 127; an all-zero block gets code 0 and zero
+            values), codes = w / 2^x rounded to the nearest E2M1 value (ties to
+            the even mantissa bit, saturating at 6); the 16-bit scale is
+            2^x, exact in bf16.
   skew      relu2_skew masks experts e % 16 == 15 (logit -inf, they receive no
             tokens) and adds a bias b to experts 0..3, with b found by
             bisection so that the share of routes on those four experts is the
@@ -59,6 +69,7 @@ class Workload:
     tokens: tuple             # token counts of the sweep
     seed: int
     skew: bool = False
+    fp4: bool = False         # MXFP4 (E2M1) weights instead of INT4 (group layout)
 
     @property
     def n1(self) -> int:
@@ -75,14 +86,18 @@ WORKLOADS = {
                             (1, 8, 256), 20260908),
     "relu2_skew": Workload("relu2_skew", 128, 128, 0, 2688, 1856, 6, False, False, torch.float16,
                            (32, 1024, 4096), 20260908, skew=True),
+    "kimi_tp8_fp4": Workload("kimi_tp8_fp4", 384, 384, 0, 7168, 256, 8, True, False,
+                             torch.bfloat16, (1, 8, 32, 256, 1024, 2048), 20260908, fp4=True),
+    "deepseek_local_fp4": Workload("deepseek_local_fp4", 32, 256, 0, 7168, 2048, 8, True, False,
+                                   torch.bfloat16, (1, 16, 128, 512, 2048), 20260908, fp4=True),
 }
 
 
 def custom(name="custom", *, E, H, I, K, gated=True, per_channel=False, dtype=torch.bfloat16,
-           E_global=None, offset=0, seed=0, skew=False) -> Workload:
+           E_global=None, offset=0, seed=0, skew=False, fp4=False) -> Workload:
     """A workload of any shape (tests use small ones)."""
     return Workload(name, E, E_global or E, offset, H, I, K, gated, per_channel, dtype, (), seed,
-                    skew)
+                    skew, fp4)
 
 
 # ---------------------------------------------------------------------------
@@ -123,6 +138,45 @@ def quantize_matrix(w: torch.Tensor, per_channel: bool, dtype: torch.dtype):
     return packed.contiguous(), s16.reshape(n_out, k_in // GROUP).contiguous()
 
 
+# magnitudes of the E2M1 codes 0..7 (bit 0 mantissa, bits 2..1 exponent with
+# bias 1; exponent 0 subnormal)
+E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def quantize_mxfp4(w: torch.Tensor):
+    """fp32 [n_out, k_in] -> (packed uint8 [n_out, k_in/2], E8M0 uint8 [n_out, k_in/32])."""
+    n_out, k_in = w.shape
+    wg = w.reshape(n_out, k_in // GROUP, GROUP)
+    amax = wg.abs().amax(dim=2)
+    _, ex = torch.frexp(amax)                     # amax = m * 2^ex, m in [0.5, 1)
+    zero = amax == 0
+    x = torch.clamp(ex.to(torch.int32) - 3, -127, 127)   # floor(log2 amax) - 2
+    x = torch.where(zero, torch.full_like(x, -127), x)
+    scale = torch.ldexp(torch.ones_like(amax), x.to(torch.float32))
+    v = wg / scale[..., None]
+    grid = torch.tensor(E2M1_GRID, dtype=torch.float32, device=w.device)
+    d = (v.abs()[..., None] - grid).abs()
+    is_min = d == d.amin(dim=-1, keepdim=True)
+    even = torch.tensor([True, False] * 4, device=w.device)
+    cand = is_min & even
+    idx = torch.where(cand.any(dim=-1), cand.to(torch.int8).argmax(dim=-1),
+                      is_min.to(torch.int8).argmax(dim=-1))
+    sign = (v < 0) | ((v == 0) & torch.signbit(v))
+    code = (idx + 8 * sign.to(idx.dtype)).to(torch.int16)
+    code = torch.where(zero[..., None], torch.zeros_like(code), code).reshape(n_out, k_in)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).to(torch.uint8)
+    return packed.contiguous(), (x + 127).to(torch.uint8).contiguous()
+
+
+def e8m0_to_h16(e8: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:
+    """E8M0 codes -> the 16-bit scale 2^(e - 127) (must be exact in dtype)."""
+    v = torch.ldexp(torch.ones(e8.shape, device=e8.device), e8.to(torch.float32) - 127)
+    s = v.to(dtype)
+    if not torch.equal(s.float(), v):
+        raise ValueError(f"E8M0 scale not exact in {dtype}")
+    return s
+
+
 @dataclasses.dataclass
 class Weights:
     w13_packed: torch.Tensor
@@ -152,6 +206,12 @@ def make_weights(wl: Workload, device="cpu", seed: Optional[int] = None,
     for e in range(E):
         w13 = torch.randn(N1, H, generator=g, device=device, dtype=torch.float32) * std
         w2 = torch.randn(H, I, generator=g, device=device, dtype=torch.float32) * std
+        if wl.fp4:
+            p13, e13 = quantize_mxfp4(w13)
+            p2, e2 = quantize_mxfp4(w2)
+            w13p[e], w13s[e] = p13, e8m0_to_h16(e13, wl.dtype)
+            w2p[e], w2s[e] = p2, e8m0_to_h16(e2, wl.dtype)
+            continue
         w13p[e], w13s[e] = quantize_matrix(w13, wl.per_channel, wl.dtype)
         w2p[e], w2s[e] = quantize_matrix(w2, wl.per_channel, wl.dtype)
     return Weights(w13p, w13s, w2p, w2s)
