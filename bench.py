@@ -254,7 +254,8 @@ def cpu_baseline(wl, Wg, budget_s, min_s):
                                hidden=wl.hidden, inter=wl.inter, num_experts=wl.num_experts,
                                expert_offset=wl.expert_offset,
                                act=oracle.ACT_SILU_GATED if wl.gated else oracle.ACT_RELU2,
-                               layout=oracle.Q_PER_CHANNEL if wl.per_channel else oracle.Q_GROUP_K,
+                               layout=(oracle.Q_PER_CHANNEL if wl.per_channel else
+                                       oracle.Q_FP4_GROUP_K if wl.fp4 else oracle.Q_GROUP_K),
                                dtype=oracle.DT_FP16 if wl.dtype == torch.float16 else oracle.DT_BF16)
             dt = time.perf_counter() - t0
             spent += dt
@@ -351,7 +352,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="kimi_tp8,deepseek_local,per_channel,relu2_skew,tiny",
+    ap.add_argument("--workloads", default="kimi_tp8,deepseek_local,per_channel,relu2_skew,tiny,"
+                                           "kimi_tp8_fp4,deepseek_local_fp4",
                     help="comma list; the first is the headline (value, roofline, cpu_baseline), "
                          "the others are reported under other_workloads")
     ap.add_argument("--workload", default="kimi_tp8",
@@ -741,7 +743,7 @@ def main():
 def describe(wl):
     return (f"{wl.name}: {wl.num_experts} local experts (of {wl.num_global_experts}), "
             f"hidden {wl.hidden}, intermediate {wl.inter}, top-{wl.top_k}, "
-            f"INT4 {'per-channel' if wl.per_channel else 'group-32'}, "
+            f"{'FP4 (MXFP4) group-32' if wl.fp4 else 'INT4 per-channel' if wl.per_channel else 'INT4 group-32'}, "
             f"{'SiLU-gated' if wl.gated else 'ReLU^2'}")
 
 

@@ -63,14 +63,23 @@ typedef enum { W4A16_ACT_SILU_GATED = 0, W4A16_ACT_RELU2 = 1 } w4a16_act_t;
  *                the reduction dim, packed along the reduction dim
  *                ([P1] BC-breaking, "INT4 group-size 32").
  *   PER_CHANNEL  one 16-bit scale per output channel, packed along the output
- *                dim ([P3] Description and Checkpoint format). */
-typedef enum { W4A16_Q_GROUP_K = 0, W4A16_Q_PER_CHANNEL = 1 } w4a16_qlayout_t;
+ *                dim ([P3] Description and Checkpoint format).
+ *   FP4_GROUP_K  FP4 weights: E2M1 codes (OCP microscaling element format: sign,
+ *                2 exponent bits with bias 1, 1 mantissa bit; magnitudes 0, 0.5,
+ *                1, 1.5, 2, 3, 4, 6) in the GROUP_K layout, two per byte along K,
+ *                one 16-bit scale per 32 values; W = e2m1 * scale, exact.  An
+ *                MXFP4 checkpoint's E8M0 scales 2^(e-127) convert exactly with
+ *                w4a16_e8m0_to_scales.  The 4-bit floating-point weights of
+ *                [P2] Final performance (NVFP4, BF16 activations) in the block
+ *                format gfx950 supports natively. */
+typedef enum { W4A16_Q_GROUP_K = 0, W4A16_Q_PER_CHANNEL = 1, W4A16_Q_FP4_GROUP_K = 2 } w4a16_qlayout_t;
 
 /* Problem descriptor (host memory, read during the call only).
  *   Logical weight shapes, with N1 = 2*I for SILU_GATED and N1 = I for RELU2:
  *     w13 [E][N1][H]   (gate/up, or w1)       w2 [E][H][I]   (down)
  *   Packed storage:
- *     GROUP_K:      w13_packed u8 [E][N1][H/2],   w13_scales [E][N1][H/32]
+ *     GROUP_K and FP4_GROUP_K:
+ *                   w13_packed u8 [E][N1][H/2],   w13_scales [E][N1][H/32]
  *                   w2_packed  u8 [E][H][I/2],    w2_scales  [E][H][I/32]
  *     PER_CHANNEL:  w13_packed u8 [E][N1/2][H],   w13_scales [E][N1]
  *                   w2_packed  u8 [E][H/2][I],    w2_scales  [E][H]
@@ -298,6 +307,18 @@ w4a16_status_t w4a16_moe_route_and_prepare(const w4a16_moe_desc_t* desc,
                                            int32_t* offsets, int32_t* sorted_routes,
                                            int64_t sorted_capacity, int32_t* route_slot,
                                            int32_t* chunk_scratch, w4a16_stream_t stream);
+
+/* Setup-time conversion of MXFP4 block scales (E8M0 codes e, value
+ * 2^(e - 127); OCP microscaling formats) to the 16-bit scales the
+ * FP4_GROUP_K layout takes (dtype W4A16_DT_BF16 or W4A16_DT_FP16; [P2] Final
+ * performance: FP4 weights, weight preparation outside the timed region).
+ *   e8m0   device, n codes
+ *   out    device, n 16-bit values; exact for every code in bf16 except 255
+ *          (NaN), in fp16 for 103 <= e <= 142
+ * A code that has no exact 16-bit value writes the nearest one (NaN for 255);
+ * n = 0 enqueues nothing. */
+w4a16_status_t w4a16_e8m0_to_scales(const uint8_t* e8m0, int64_t n, int32_t dtype, void* out,
+                                    w4a16_stream_t stream);
 
 /* Nibble unpacking with the device conversion the GEMMs use ([P3] Checkpoint
  * format): out[2i] = low nibble of packed[i], out[2i+1] = high nibble, both as

@@ -44,7 +44,8 @@ def oracle_out(wl, Wc, tok_cpu, rows=None):
         bits(Wc.w2_scales), ids.numpy(), w.numpy(), hidden=wl.hidden, inter=wl.inter,
         num_experts=wl.num_experts, expert_offset=wl.expert_offset,
         act=oracle.ACT_SILU_GATED if wl.gated else oracle.ACT_RELU2,
-        layout=oracle.Q_PER_CHANNEL if wl.per_channel else oracle.Q_GROUP_K,
+        layout=(oracle.Q_PER_CHANNEL if wl.per_channel
+                else oracle.Q_FP4_GROUP_K if wl.fp4 else oracle.Q_GROUP_K),
         dtype=oracle.DT_FP16 if wl.dtype == torch.float16 else oracle.DT_BF16)
 
 

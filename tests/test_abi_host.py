@@ -51,7 +51,7 @@ def good(**kw):
     ("top_k", 0, 1, "top_k"),
     ("dtype", 7, 1, "dtype"),
     ("act", 3, 1, "act"),
-    ("qlayout", 2, 1, "qlayout"),
+    ("qlayout", 3, 1, "qlayout"),
     ("num_local_experts", 2000, 2, "num_local_experts"),
     ("top_k", 33, 2, "top_k"),
     ("group_size", 64, 2, "group_size"),
@@ -321,3 +321,21 @@ def test_routed_forward_argument_errors():
                                        P(0x1000), P(0x1000), P(0x1000), 1 << 20, P(0x1000), None,
                                        None)
     assert st == 2 and "top_k=9" in L.w4a16_last_error_message().decode()
+
+
+def test_fp4_layout_descriptor():
+    """The FP4 group layout is accepted with group 32 and takes the INT4 group
+    layout's workspace; it never takes the fp16 route."""
+    kimi = dict(hidden=7168, intermediate=256, num_local_experts=384, top_k=8)
+    for T in (1, 32, 2048):
+        a = B.make_desc(num_tokens=T, **kimi)
+        f = B.make_desc(num_tokens=T, fp4=True, **kimi)
+        assert f.qlayout == 2
+        assert B.workspace_size(f) == B.workspace_size(a)
+        assert B.get_plan(f).path == B.get_plan(a).path
+    assert B.get_plan(B.make_desc(num_tokens=2048, fp4=True, fp16_route=1, **kimi)).fp16_route == 0
+    bad = B.make_desc(num_tokens=4, hidden=256, intermediate=384, num_local_experts=8, top_k=2,
+                      fp4=True, group_size=16)
+    with pytest.raises(B.W4A16Error) as ei:
+        B.workspace_size(bad)
+    assert ei.value.status == 2 and "group_size" in ei.value.message

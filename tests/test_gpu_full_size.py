@@ -30,6 +30,10 @@ def test_sweeps_are_covered():
              ("deepseek_local", 1), ("deepseek_local", 16), ("per_channel", 1),
              ("per_channel", 8), ("relu2_skew", 32)}
     covered = small | set(WHOLE) | set(SAMPLED)
+    # the FP4-weight workloads' sweeps are compared in test_gpu_fp4
+    fp4 = {(n, T) for n in ("kimi_tp8_fp4",) for T in (1, 8, 32, 256, 1024, 2048)} | {
+        (n, T) for n in ("deepseek_local_fp4",) for T in (1, 16, 128, 512, 2048)}
+    covered |= fp4
     for name, wl in synth.WORKLOADS.items():
         for T in wl.tokens:
             assert (name, T) in covered, (name, T)

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libw4a16moe.so")
 
 DT_BF16, DT_FP16 = 0, 1
 ACT_SILU_GATED, ACT_RELU2 = 0, 1
-Q_GROUP_K, Q_PER_CHANNEL = 0, 1
+Q_GROUP_K, Q_PER_CHANNEL, Q_FP4_GROUP_K = 0, 1, 2
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP"}
 NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024   # W4A16_NOALLOC_SCRATCH_BYTES
 
@@ -73,6 +73,7 @@ def lib():
     L.w4a16_moe_forward_routed.argtypes = [P, P, P, P, P, P, i32, P, P, P, pdesc, P, sz, P, P,
                                            i32]
     L.w4a16_moe_route_and_prepare.argtypes = [pdesc, P, i32, i32, P, P, P, P, P, i64, P, P, P]
+    L.w4a16_e8m0_to_scales.argtypes = [P, i64, i32, P, P]
     L.w4a16_status_string.argtypes = [i32]
     L.w4a16_status_string.restype = ctypes.c_char_p
     L.w4a16_last_error_message.restype = ctypes.c_char_p
@@ -80,7 +81,7 @@ def lib():
               "w4a16_moe_forward_timed",
               "w4a16_moe_prepare_routes", "w4a16_unpack_int4", "w4a16_moe_route_topk",
               "w4a16_stream_probe", "w4a16_moe_forward_noalloc", "w4a16_moe_forward_routed",
-              "w4a16_moe_route_and_prepare"):
+              "w4a16_moe_route_and_prepare", "w4a16_e8m0_to_scales"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -116,7 +117,8 @@ def _dev(name: str, t: torch.Tensor, dtypes, device=None):
 
 def make_desc(*, num_tokens: int, hidden: int, intermediate: int, num_local_experts: int,
               top_k: int, expert_offset: int = 0, dtype=torch.bfloat16, gated: bool = True,
-              per_channel: bool = False, group_size: int = 32, force_path: int = 0,
+              per_channel: bool = False, fp4: bool = False, group_size: int = 32,
+              force_path: int = 0,
               force_block_m: int = 0, force_splitk: int = 0,
               num_global_experts: int = 0, fp16_route: int = 0,
               fused_finalize: int = 0) -> MoeDesc:
@@ -129,7 +131,8 @@ def make_desc(*, num_tokens: int, hidden: int, intermediate: int, num_local_expe
     return MoeDesc(num_tokens, hidden, intermediate, num_local_experts, expert_offset, top_k,
                    group_size, DT_FP16 if dtype == torch.float16 else DT_BF16,
                    ACT_SILU_GATED if gated else ACT_RELU2,
-                   Q_PER_CHANNEL if per_channel else Q_GROUP_K, force_path, force_block_m,
+                   Q_PER_CHANNEL if per_channel else (Q_FP4_GROUP_K if fp4 else Q_GROUP_K),
+                   force_path, force_block_m,
                    force_splitk, num_global_experts, fp16_route, fused_finalize)
 
 
@@ -150,13 +153,14 @@ def desc_for(wl, T: int, **force) -> MoeDesc:
     return make_desc(num_tokens=T, hidden=wl.hidden, intermediate=wl.inter,
                      num_local_experts=wl.num_experts, top_k=wl.top_k,
                      expert_offset=wl.expert_offset, dtype=wl.dtype, gated=wl.gated,
-                     per_channel=wl.per_channel, num_global_experts=wl.num_global_experts,
-                     **force)
+                     per_channel=wl.per_channel, fp4=wl.fp4,
+                     num_global_experts=wl.num_global_experts, **force)
 
 
 def moe_forward(x, w13_packed, w13_scales, w2_packed, w2_scales, topk_ids, topk_weights, *,
                 intermediate: int, num_local_experts: int, expert_offset: int = 0,
-                gated: bool = True, per_channel: bool = False, out=None, workspace=None,
+                gated: bool = True, per_channel: bool = False, fp4: bool = False, out=None,
+                workspace=None,
                 force_path: int = 0, force_block_m: int = 0, force_splitk: int = 0,
                 num_global_experts: int = 0, fp16_route: int = 0, fused_finalize: int = 0,
                 stream=None, stage_events=None, no_alloc: bool = False) -> torch.Tensor:
@@ -197,7 +201,7 @@ def moe_forward(x, w13_packed, w13_scales, w2_packed, w2_scales, topk_ids, topk_
             raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {want[name]}")
     desc = make_desc(num_tokens=T, hidden=H, intermediate=I, num_local_experts=E,
                      top_k=topk_ids.shape[1], expert_offset=expert_offset, dtype=x.dtype,
-                     gated=gated, per_channel=per_channel, force_path=force_path,
+                     gated=gated, per_channel=per_channel, fp4=fp4, force_path=force_path,
                      force_block_m=force_block_m, force_splitk=force_splitk,
                      num_global_experts=num_global_experts, fp16_route=fp16_route,
                      fused_finalize=fused_finalize)
@@ -240,7 +244,7 @@ def forward_workload(wl, W, tok, **kw) -> torch.Tensor:
     return moe_forward(tok.x, W.w13_packed, W.w13_scales, W.w2_packed, W.w2_scales,
                        tok.topk_ids, tok.topk_weights, intermediate=wl.inter,
                        num_local_experts=wl.num_experts, expert_offset=wl.expert_offset,
-                       gated=wl.gated, per_channel=wl.per_channel,
+                       gated=wl.gated, per_channel=wl.per_channel, fp4=wl.fp4,
                        num_global_experts=wl.num_global_experts, **kw)
 
 
@@ -313,6 +317,7 @@ def stream_probe(buf: torch.Tensor, nbytes: int, row_bytes: int, sink: torch.Ten
 def moe_forward_routed(x, w13_packed, w13_scales, w2_packed, w2_scales, router_logits, *,
                        top_k: int, intermediate: int, num_local_experts: int,
                        expert_offset: int = 0, gated: bool = True, per_channel: bool = False,
+                       fp4: bool = False,
                        renormalize: bool = False, out=None, workspace=None, ids_out=None,
                        force_path: int = 0, force_splitk: int = 0, fp16_route: int = 0,
                        fused_finalize: int = 0, stream=None, stage_events=None):
@@ -343,7 +348,8 @@ def moe_forward_routed(x, w13_packed, w13_scales, w2_packed, w2_scales, router_l
             raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {want[name]}")
     desc = make_desc(num_tokens=T, hidden=H, intermediate=I, num_local_experts=E, top_k=top_k,
                      expert_offset=expert_offset, dtype=x.dtype, gated=gated,
-                     per_channel=per_channel, force_path=force_path, force_splitk=force_splitk,
+                     per_channel=per_channel, fp4=fp4, force_path=force_path,
+                     force_splitk=force_splitk,
                      num_global_experts=Eg, fp16_route=fp16_route, fused_finalize=fused_finalize)
     nbytes = workspace_size(desc)
     if out is None:
@@ -387,7 +393,7 @@ def forward_workload_routed(wl, W, tok, **kw):
     return moe_forward_routed(tok.x, W.w13_packed, W.w13_scales, W.w2_packed, W.w2_scales,
                               tok.logits, top_k=wl.top_k, intermediate=wl.inter,
                               num_local_experts=wl.num_experts, expert_offset=wl.expert_offset,
-                              gated=wl.gated, per_channel=wl.per_channel, **kw)
+                              gated=wl.gated, per_channel=wl.per_channel, fp4=wl.fp4, **kw)
 
 
 def route_and_prepare(logits: torch.Tensor, top_k: int, num_local_experts: int,
@@ -416,3 +422,13 @@ def route_and_prepare(logits: torch.Tensor, top_k: int, num_local_experts: int,
         _ptr(counts), _ptr(offsets), _ptr(srt), cap, _ptr(slot),
         _ptr(scratch) if chunked else None, _stream(stream)))
     return ids, wts, counts, offsets, srt, slot[:R]
+
+
+def e8m0_to_scales(e8m0: torch.Tensor, dtype=torch.bfloat16, stream=None) -> torch.Tensor:
+    """MXFP4 block scales (E8M0 codes) -> 16-bit scales 2^(e - 127) on the GPU."""
+    _dev("e8m0", e8m0, (torch.uint8,))
+    out = torch.empty(e8m0.shape, dtype=dtype, device=e8m0.device)
+    _check(lib().w4a16_e8m0_to_scales(_ptr(e8m0), e8m0.numel(),
+                                      DT_FP16 if dtype == torch.float16 else DT_BF16, _ptr(out),
+                                      _stream(stream)))
+    return out

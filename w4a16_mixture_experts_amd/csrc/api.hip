@@ -71,12 +71,13 @@ w4a16_status_t check_desc(const w4a16_moe_desc_t* d) {
     return fail(W4A16_ERR_INVALID_ARG, "desc.dtype: unknown value %d", d->dtype);
   if (d->act != W4A16_ACT_SILU_GATED && d->act != W4A16_ACT_RELU2)
     return fail(W4A16_ERR_INVALID_ARG, "desc.act: unknown value %d", d->act);
-  if (d->qlayout != W4A16_Q_GROUP_K && d->qlayout != W4A16_Q_PER_CHANNEL)
+  if (d->qlayout != W4A16_Q_GROUP_K && d->qlayout != W4A16_Q_PER_CHANNEL &&
+      d->qlayout != W4A16_Q_FP4_GROUP_K)
     return fail(W4A16_ERR_INVALID_ARG, "desc.qlayout: unknown value %d", d->qlayout);
   if (d->num_local_experts > 1024)
     return fail(W4A16_ERR_UNSUPPORTED, "desc.num_local_experts: %d > 1024", d->num_local_experts);
   if (d->top_k > 32) return fail(W4A16_ERR_UNSUPPORTED, "desc.top_k: %d > 32", d->top_k);
-  if (d->qlayout == W4A16_Q_GROUP_K && d->group_size != 32)
+  if (d->qlayout != W4A16_Q_PER_CHANNEL && d->group_size != 32)
     return fail(W4A16_ERR_UNSUPPORTED, "desc.group_size: %d (only 32 is supported)", d->group_size);
   if (d->hidden % 64 != 0)
     return fail(W4A16_ERR_UNSUPPORTED,
@@ -423,7 +424,7 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
   const StageEvents evs{events, n_events, stream};
   const int E = desc->num_local_experts, H = desc->hidden, I = desc->intermediate;
   const int K = desc->top_k;
-  const bool group = desc->qlayout == W4A16_Q_GROUP_K;
+  const bool group = desc->qlayout != W4A16_Q_PER_CHANNEL;  // INT4 or FP4 groups along K
   char* ws = static_cast<char*>(workspace);
   auto* counts = reinterpret_cast<int32_t*>(ws + pl.off_counts);
   auto* offsets = reinterpret_cast<int32_t*>(ws + pl.off_offsets);
@@ -802,6 +803,21 @@ w4a16_status_t w4a16_stream_probe(const uint8_t* buf, int64_t bytes, int32_t row
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   return hip_status(w4moe::launch_stream_probe(buf, bytes, row_bytes, sink, stream),
                     "probe launch");
+}
+
+w4a16_status_t w4a16_e8m0_to_scales(const uint8_t* e8m0, int64_t n, int32_t dtype, void* out,
+                                    w4a16_stream_t stream_) {
+  if (n < 0) return fail(W4A16_ERR_INVALID_ARG, "n: %lld < 0", (long long)n);
+  if (dtype != W4A16_DT_BF16 && dtype != W4A16_DT_FP16)
+    return fail(W4A16_ERR_INVALID_ARG, "dtype: unknown value %d", dtype);
+  if (n == 0) return W4A16_OK;
+  if (e8m0 == nullptr) return fail(W4A16_ERR_INVALID_ARG, "e8m0: null pointer");
+  if (out == nullptr) return fail(W4A16_ERR_INVALID_ARG, "out: null pointer");
+  if (misaligned(out, 2)) return fail(W4A16_ERR_INVALID_ARG, "out: address not 2-byte aligned");
+  if (n > (int64_t(1) << 36)) return fail(W4A16_ERR_UNSUPPORTED, "n: %lld too large", (long long)n);
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  return hip_status(w4moe::launch_e8m0_to_h16(e8m0, n, dtype, static_cast<uint16_t*>(out), stream),
+                    "scale conversion launch");
 }
 
 w4a16_status_t w4a16_moe_route_topk(const float* logits, int64_t num_tokens,

@@ -32,13 +32,13 @@ constexpr int kDecThreads = kDecWaves * 64;
 
 template <int LAYOUT>
 struct BBlk {
-  uint32_t d[LAYOUT == Q_GROUP_K ? 4 : 8];
+  uint32_t d[is_group(LAYOUT) ? 4 : 8];
   uint32_t s[2];
 };
 
 template <int LAYOUT>
 __device__ __forceinline__ void tr_b(BBlk<LAYOUT>& b) {
-  if constexpr (LAYOUT == Q_GROUP_K) {
+  if constexpr (is_group(LAYOUT)) {
     transpose_rows4(b.d[0], b.d[1], b.d[2], b.d[3]);
   } else {
     transpose_rows4(b.d[0], b.d[2], b.d[4], b.d[6]);
@@ -48,8 +48,8 @@ __device__ __forceinline__ void tr_b(BBlk<LAYOUT>& b) {
 
 template <int DT, int LAYOUT>
 __device__ __forceinline__ u32x4 b_op(const BBlk<LAYOUT>& b, int j, int par) {
-  if constexpr (LAYOUT == Q_GROUP_K) {
-    return nibbles_to_h16<DT>(b.d[j]);
+  if constexpr (is_group(LAYOUT)) {
+    return group_to_h16<DT, LAYOUT>(b.d[j]);
   } else {
     const int sh = 4 * par;
     return bytes_to_h16<DT>(b.d[2 * j] >> sh, b.d[2 * j + 1] >> sh);
@@ -93,7 +93,7 @@ template <int DT, int LAYOUT, int NKB, bool ROUTE>
 __global__ void __launch_bounds__(kSmallThreads)
 small_h_kernel(const SmallHParams p) {
   using T = H16<DT>;
-  constexpr bool GROUP = LAYOUT == Q_GROUP_K;
+  constexpr bool GROUP = is_group(LAYOUT);
   constexpr int CH = NKB * 16;  // 8-value chunks per staged x row of a slice
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int c = lane & 15, g = lane >> 4, par = c & 1;
@@ -255,7 +255,7 @@ small_h_kernel(const SmallHParams p) {
         if constexpr (GROUP) {
           const uint32_t pair = sc2[j >> 1];
           sc = T::to_f32((j & 1) ? (pair >> 16) : (pair & 0xffffu));
-          bop = nibbles_to_h16<DT>(d[j]);
+          bop = group_to_h16<DT, LAYOUT>(d[j]);
         } else {
           sc = scol;
           // sub-chunk j = dwords (2j, 2j+1) of the lane's 8
@@ -263,7 +263,8 @@ small_h_kernel(const SmallHParams p) {
           const uint32_t hi = (j < 2) ? d[2 * j + 1] : d2[2 * j - 3];
           bop = bytes_to_h16<DT>(lo >> (4 * par), hi >> (4 * par));
         }
-        const f32x4 corr = T::mfma(a, bconst, fzero);
+        // INT4: the -1.5 * sum(a) term of the (24 + q) / 16 encoding; FP4 needs none
+        const f32x4 corr = LAYOUT == Q_FP4_GROUP_K ? fzero : T::mfma(a, bconst, fzero);
         const f32x4 t = T::mfma(a, bop, corr);
         acc = fmaf(sc, t[0], acc);
       }
@@ -348,9 +349,9 @@ decode_down_kernel(const DecodeDownParams p) {
 
   // (3) weights of a work item (route k, reduction slice sl)
   const uint32_t boff[NSUB] = {
-      LAYOUT == Q_GROUP_K ? static_cast<uint32_t>(wrow[0]) * (p.I >> 1)
+      is_group(LAYOUT) ? static_cast<uint32_t>(wrow[0]) * (p.I >> 1)
                           : static_cast<uint32_t>(wrow[0] >> 1) * p.I,
-      LAYOUT == Q_GROUP_K ? static_cast<uint32_t>(wrow[1]) * (p.I >> 1)
+      is_group(LAYOUT) ? static_cast<uint32_t>(wrow[1]) * (p.I >> 1)
                           : static_cast<uint32_t>(wrow[1] >> 1) * p.I};
   auto load_item = [&](int it, BBlk<LAYOUT> (&b)[SL][NSUB], float (&scol)[NSUB], int& e) {
     const int k = it / nsl;
@@ -370,7 +371,7 @@ decode_down_kernel(const DecodeDownParams p) {
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) {
         const bool ok = e >= 0 && on[s] && ng > 0;
-        if constexpr (LAYOUT == Q_GROUP_K) {
+        if constexpr (is_group(LAYOUT)) {
           const u32x4 v = bload16(rw, boff[s] + (k0 >> 1) + 16 * g, ok && g < ng);
           b[i][s].d[0] = v[0]; b[i][s].d[1] = v[1]; b[i][s].d[2] = v[2]; b[i][s].d[3] = v[3];
           const uint32_t so = 2u * (static_cast<uint32_t>(wrow[s]) * (p.I >> 5) + (k0 >> 5));
@@ -389,7 +390,7 @@ decode_down_kernel(const DecodeDownParams p) {
     }
 #pragma unroll
     for (int s = 0; s < NSUB; ++s)
-      scol[s] = (LAYOUT == Q_GROUP_K)
+      scol[s] = (is_group(LAYOUT))
                     ? 0.0f
                     : T::to_f32(bload4(rs, (2u * wrow[s]) & ~3u, e >= 0 && on[s]) >> (16 * (wrow[s] & 1)));
   };
@@ -452,10 +453,10 @@ decode_down_kernel(const DecodeDownParams p) {
           a[1] = fa ? av[1] : 0u;
           a[2] = fa ? av[2] : 0u;
           a[3] = fa ? av[3] : 0u;
-          const f32x4 corr = T::mfma(a, bconst, fzero);
+          const f32x4 corr = LAYOUT == Q_FP4_GROUP_K ? fzero : T::mfma(a, bconst, fzero);
 #pragma unroll
           for (int s = 0; s < NSUB; ++s) {
-            float sc = (LAYOUT == Q_GROUP_K) ? sc_of<DT>(b[i][s].s[j >> 1], j) : scol[s];
+            float sc = (is_group(LAYOUT)) ? sc_of<DT>(b[i][s].s[j >> 1], j) : scol[s];
             sc = (gv && on[s]) ? sc : 0.0f;
             const f32x4 tt = T::mfma(a, b_op<DT, LAYOUT>(b[i][s], j, par), corr);
             y[s] = fmaf(sc, tt[0], y[s]);
@@ -533,8 +534,10 @@ hipError_t launch_small_h(const SmallHParams& p, int dtype, int layout, int nkb,
   const size_t lds = small_h_lds_bytes(p.kslice);
   if (dtype == DT_BF16)
     return layout == Q_GROUP_K ? launch_small_h_nkb<DT_BF16, Q_GROUP_K>(p, nkb, grid, lds, stream)
+         : layout == Q_FP4_GROUP_K ? launch_small_h_nkb<DT_BF16, Q_FP4_GROUP_K>(p, nkb, grid, lds, stream)
                                : launch_small_h_nkb<DT_BF16, Q_PER_CHANNEL>(p, nkb, grid, lds, stream);
   return layout == Q_GROUP_K ? launch_small_h_nkb<DT_FP16, Q_GROUP_K>(p, nkb, grid, lds, stream)
+       : layout == Q_FP4_GROUP_K ? launch_small_h_nkb<DT_FP16, Q_FP4_GROUP_K>(p, nkb, grid, lds, stream)
                              : launch_small_h_nkb<DT_FP16, Q_PER_CHANNEL>(p, nkb, grid, lds, stream);
 }
 
@@ -569,8 +572,10 @@ hipError_t launch_decode_down(const DecodeDownParams& p, int dtype, int layout, 
   const size_t lds = decode_down_lds_bytes(p.top_k, p.I);
   if (dtype == DT_BF16)
     return layout == Q_GROUP_K ? launch_dd<DT_BF16, Q_GROUP_K>(p, gated, grid, lds, stream)
+         : layout == Q_FP4_GROUP_K ? launch_dd<DT_BF16, Q_FP4_GROUP_K>(p, gated, grid, lds, stream)
                                : launch_dd<DT_BF16, Q_PER_CHANNEL>(p, gated, grid, lds, stream);
   return layout == Q_GROUP_K ? launch_dd<DT_FP16, Q_GROUP_K>(p, gated, grid, lds, stream)
+       : layout == Q_FP4_GROUP_K ? launch_dd<DT_FP16, Q_FP4_GROUP_K>(p, gated, grid, lds, stream)
                              : launch_dd<DT_FP16, Q_PER_CHANNEL>(p, gated, grid, lds, stream);
 }
 

@@ -26,6 +26,11 @@
 //   [x0,x4,x1,x5,x2,x6,x3,x7].  Intermediate activations written by the
 //   gate/up kernel are stored already in that order.
 //
+// FP4 weights (E2M1 codes, the OCP microscaling element format): each code
+//   becomes its exact value / 16 (e2m1_to_h16), so the MFMA computes
+//   sum_k a_k v_k / 16 directly, with no correction term, and the same group
+//   scale and final factor 16 apply.
+//
 // MFMA lane layout (v_mfma_f32_16x16x32_{bf16,f16}, wave64): lane l feeds
 //   row/column l%16 of A/B with 8 reduction values of slice l/16, and holds
 //   rows 4*(l/16) + i, column l%16 of the 16x16 FP32 result.
@@ -43,7 +48,10 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 enum : int { DT_BF16 = 0, DT_FP16 = 1 };
-enum : int { Q_GROUP_K = 0, Q_PER_CHANNEL = 1 };
+enum : int { Q_GROUP_K = 0, Q_PER_CHANNEL = 1, Q_FP4_GROUP_K = 2 };
+
+// Layouts with one scale per 32 values along K, packed along K (INT4 or FP4).
+__host__ __device__ constexpr bool is_group(int layout) { return layout != Q_PER_CHANNEL; }
 
 // Logical-to-storage position of value j (0..7) inside an 8-chunk of A.
 __host__ __device__ constexpr int a_pos(int j) { return j < 4 ? 2 * j : 2 * (j - 4) + 1; }
@@ -116,6 +124,69 @@ __device__ __forceinline__ u32x4 nibbles_to_h16(uint32_t d) {
   r[2] = (shr_signed<8 - T::kShift>(d) & T::kMask) ^ T::kBias;
   r[3] = (shr_signed<12 - T::kShift>(d) & T::kMask) ^ T::kBias;
   return r;
+}
+
+// FP4 (E2M1) codes -> 16-bit value / 16 (OCP microscaling formats: 1 sign
+// bit, 2 exponent bits with bias 1, 1 mantissa bit, exponent 0 subnormal).
+// The magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 divided by 16 are exact in bf16
+// and fp16; the division lets the FP4 layout share the INT4 layout's final
+// factor 16 and needs no correction term.  One dword of eight codes n0..n7
+// gives the same pairs as nibbles_to_h16: (n0,n4) (n1,n5) (n2,n6) (n3,n7).
+// The 16-bit patterns of the eight magnitudes come from two byte lookups
+// (v_perm_b32 with the 3-bit magnitude codes as selectors), the sign bit is
+// moved in place.
+template <int DT>
+struct Fp4Lut;
+template <>
+struct Fp4Lut<DT_BF16> {
+  // bf16 of 0, 1/32, 1/16, 3/32, 1/8, 3/16, 1/4, 3/8: high and low bytes
+  static constexpr uint32_t kHi03 = 0x3D3D3D00u, kHi47 = 0x3E3E3E3Eu;
+  static constexpr uint32_t kLo03 = 0xC0800000u, kLo47 = 0xC0804000u;
+  static constexpr bool kLowBytes = true;
+};
+template <>
+struct Fp4Lut<DT_FP16> {
+  // fp16 of the same values: the low bytes are all zero
+  static constexpr uint32_t kHi03 = 0x2E2C2800u, kHi47 = 0x36343230u;
+  static constexpr uint32_t kLo03 = 0u, kLo47 = 0u;
+  static constexpr bool kLowBytes = false;
+};
+
+template <int DT>
+__device__ __forceinline__ u32x4 e2m1_to_h16(uint32_t d) {
+  using L = Fp4Lut<DT>;
+  const uint32_t ev = d & 0x07070707u;          // magnitudes of n0 n2 n4 n6 (one per byte)
+  const uint32_t od = (d >> 4) & 0x07070707u;   // magnitudes of n1 n3 n5 n7
+  const uint32_t he = __builtin_amdgcn_perm(L::kHi47, L::kHi03, ev);
+  const uint32_t ho = __builtin_amdgcn_perm(L::kHi47, L::kHi03, od);
+  u32x4 r;
+  if constexpr (L::kLowBytes) {
+    const uint32_t le = __builtin_amdgcn_perm(L::kLo47, L::kLo03, ev);
+    const uint32_t lo = __builtin_amdgcn_perm(L::kLo47, L::kLo03, od);
+    r[0] = __builtin_amdgcn_perm(he, le, 0x06020400u);   // (n0, n4)
+    r[1] = __builtin_amdgcn_perm(ho, lo, 0x06020400u);   // (n1, n5)
+    r[2] = __builtin_amdgcn_perm(he, le, 0x07030501u);   // (n2, n6)
+    r[3] = __builtin_amdgcn_perm(ho, lo, 0x07030501u);   // (n3, n7)
+  } else {
+    // the low bytes come from a zero operand
+    r[0] = __builtin_amdgcn_perm(he, 0u, 0x06020400u);
+    r[1] = __builtin_amdgcn_perm(ho, 0u, 0x06020400u);
+    r[2] = __builtin_amdgcn_perm(he, 0u, 0x07030501u);
+    r[3] = __builtin_amdgcn_perm(ho, 0u, 0x07030501u);
+  }
+  // sign of n_i (bit 4i + 3) to bit 15 or 31 of its pair
+  r[0] |= (d << 12) & 0x80008000u;
+  r[1] |= (d << 8) & 0x80008000u;
+  r[2] |= (d << 4) & 0x80008000u;
+  r[3] |= d & 0x80008000u;
+  return r;
+}
+
+// B operand of one 32-value group in the group layouts (after the transpose).
+template <int DT, int LAYOUT>
+__device__ __forceinline__ u32x4 group_to_h16(uint32_t d) {
+  if constexpr (LAYOUT == Q_FP4_GROUP_K) return e2m1_to_h16<DT>(d);
+  else return nibbles_to_h16<DT>(d);
 }
 
 // Per-channel packing: bytes b0..b7 each hold the value of 8 consecutive

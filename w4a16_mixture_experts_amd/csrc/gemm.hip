@@ -12,6 +12,7 @@
 //   combine_kernel  out[t] = cast16(sum_k w[t,k] * Y[t*K+k]) in FP32 over the
 //                   valid routes (slot[t*K+k] >= 0).
 //   unpack_kernel   nibbles through the GEMMs' bit conversion, back to int8.
+//   e8m0_kernel     MXFP4 block scales to 16-bit scales (setup).
 #include "device.h"
 #include "internal.h"
 
@@ -85,6 +86,21 @@ unpack_kernel(const uint8_t* __restrict__ in, int64_t n, int8_t* __restrict__ ou
   }
 }
 
+// MXFP4 block scales: E8M0 code e -> 2^(e - 127) as a 16-bit float (the
+// FP32 value is exact; its 16-bit rounding is exact wherever the dtype holds
+// the power of two).
+template <int DT>
+__global__ void __launch_bounds__(256)
+e8m0_kernel(const uint8_t* __restrict__ in, int64_t n, uint16_t* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t e = in[i];
+  // 2^(e - 127): e >= 1 is a normal FP32 exponent field, e = 0 the subnormal 2^-127
+  const float v = e == 255u ? __uint_as_float(0x7FC00000u)
+                            : (e == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(e << 23));
+  out[i] = H16<DT>::from_f32(v);
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
@@ -103,6 +119,22 @@ hipError_t launch_unpack(const uint8_t* packed, int64_t n_bytes, int8_t* out, hi
   const int64_t blocks = (threads + 255) / 256;
   hipLaunchKernelGGL(unpack_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
                      packed, n_bytes, out);
+  return hipGetLastError();
+}
+
+}  // namespace w4moe
+
+namespace w4moe {
+
+hipError_t launch_e8m0_to_h16(const uint8_t* e8m0, int64_t n, int dtype, uint16_t* out,
+                              hipStream_t stream) {
+  const int64_t blocks = (n + 255) / 256;
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(e8m0_kernel<DT_BF16>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                       stream, e8m0, n, out);
+  else
+    hipLaunchKernelGGL(e8m0_kernel<DT_FP16>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                       stream, e8m0, n, out);
   return hipGetLastError();
 }
 

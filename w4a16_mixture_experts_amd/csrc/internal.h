@@ -181,6 +181,8 @@ hipError_t launch_decode_down(const DecodeDownParams& p, int dtype, int layout, 
 hipError_t launch_combine(const CombineParams& p, int dtype, int T, hipStream_t stream);
 
 hipError_t launch_unpack(const uint8_t* packed, int64_t n_bytes, int8_t* out, hipStream_t stream);
+hipError_t launch_e8m0_to_h16(const uint8_t* e8m0, int64_t n, int dtype, uint16_t* out,
+                              hipStream_t stream);
 
 // Streaming-read probe over [bytes / row_bytes][row_bytes] (row_bytes a
 // multiple of 64, at most 8 * 16 * 64).

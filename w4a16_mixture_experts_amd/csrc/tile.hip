@@ -65,7 +65,7 @@ static_assert(kScWholeLoads * 16 * kTileThreads == 256 * kScWholeGroups * 2, "wh
 static_assert(kScPhaseLoads * 16 * kTileThreads == 256 * kScPhaseGroups * 2, "phase chunks");
 static_assert(kScPhaseGroups % 8 == 0, "a phase is whole 128-block pairs");
 inline bool tile_scales_in_lds(int layout, int K) {
-  return layout == Q_GROUP_K && (K / 32 <= kScWholeGroups || (K / 32) % 8 == 0);
+  return is_group(layout) && (K / 32 <= kScWholeGroups || (K / 32) % 8 == 0);
 }
 inline size_t tile_lds_bytes(bool scl, int K) {
   size_t b = sizeof(uint16_t) * 4 * kStageElems;
@@ -134,7 +134,7 @@ __device__ __forceinline__ WExpert make_wexpert(const GemmParams& p, int e) {
 template <int LAYOUT, int NSUB = kNsub>
 __device__ __forceinline__ WSrc<NSUB> make_wsrc(int K, const int (&wrow)[NSUB],
                                                 const bool (&on)[NSUB]) {
-  constexpr bool GROUP = LAYOUT == Q_GROUP_K;
+  constexpr bool GROUP = is_group(LAYOUT);
   WSrc<NSUB> w;
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
@@ -156,7 +156,7 @@ __device__ __forceinline__ void load_wblk(const WExpert& x, const WSrc<NSUB>& w,
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
     const bool ok = w.on[s] && g < ng;
-    if constexpr (LAYOUT == Q_GROUP_K) {
+    if constexpr (is_group(LAYOUT)) {
       b[s].d = bload16(x.rw, w.boff[s] + (k0 >> 1) + 16 * g, ok);
       const uint32_t so = w.soff[s] + 2u * (k0 >> 5);
       if constexpr (SC == SC_PAIR_FIRST) {
@@ -179,7 +179,7 @@ __device__ __forceinline__ void load_wblk(const WExpert& x, const WSrc<NSUB>& w,
 template <int LAYOUT, int NSUB>
 __device__ __forceinline__ void pass_scales(const WBlk<LAYOUT> (&first)[NSUB],
                                             WBlk<LAYOUT> (&second)[NSUB]) {
-  if constexpr (LAYOUT == Q_GROUP_K) {
+  if constexpr (is_group(LAYOUT)) {
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
       second[s].s0 = first[s].s2;
@@ -198,7 +198,7 @@ __device__ __forceinline__ void mma_block(const uint16_t* sa, int stride,
                                           const WBlk<LAYOUT> (&wb)[NSUB],
                                           f32x4 (&acc)[NMS][NSUB], int c, int g, int par) {
   using T = H16<DT>;
-  constexpr bool GROUP = LAYOUT == Q_GROUP_K;
+  constexpr bool GROUP = is_group(LAYOUT);
   // scheduling fences keep the compiler from hoisting the LDS reads of later
   // blocks (or, without UPFRONT, of later groups) into this one, which would
   // hold every fragment live at once
@@ -235,7 +235,7 @@ __device__ __forceinline__ void mma_block(const uint16_t* sa, int stride,
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
       if constexpr (GROUP) {
-        bop[s] = nibbles_to_h16<DT>(d[s][j]);
+        bop[s] = group_to_h16<DT, LAYOUT>(d[s][j]);
         const uint32_t pr = (j < 2) ? wb[s].s0 : wb[s].s1;
         sc[s] = (j & 1) ? scale_hi<DT>(pr) : scale_lo<DT>(pr);
       } else {
@@ -249,7 +249,8 @@ __device__ __forceinline__ void mma_block(const uint16_t* sa, int stride,
 #pragma unroll
     for (int ms = 0; ms < NMS; ++ms) {
       const u32x4 a = UPFRONT ? af[ms][j] : frag(ms, j);
-      const f32x4 corr = T::mfma(a, bconst, fzero);
+      // INT4: the -1.5 * sum(a) term of the (24 + q) / 16 encoding; FP4 needs none
+      const f32x4 corr = LAYOUT == Q_FP4_GROUP_K ? fzero : T::mfma(a, bconst, fzero);
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) t[ms][s] = T::mfma(a, bop[s], corr);
     }
@@ -266,7 +267,7 @@ __device__ __forceinline__ void mma_block2(const uint16_t* sa, int stride,
                                            const WBlk<LAYOUT> (&wsc)[NSUB], int second,
                                            f32x4 (&acc)[NMS][NSUB], int c, int g, int par) {
   using T = H16<DT>;
-  constexpr bool GROUP = LAYOUT == Q_GROUP_K;
+  constexpr bool GROUP = is_group(LAYOUT);
   __builtin_amdgcn_sched_barrier(0);
   const u32x4 bconst = {T::kNegOneHalf2, T::kNegOneHalf2, T::kNegOneHalf2, T::kNegOneHalf2};
   const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
@@ -295,7 +296,7 @@ __device__ __forceinline__ void mma_block2(const uint16_t* sa, int stride,
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
       if constexpr (GROUP) {
-        bop[s] = nibbles_to_h16<DT>(d[s][j]);
+        bop[s] = group_to_h16<DT, LAYOUT>(d[s][j]);
         const uint32_t pr = second ? ((j < 2) ? wsc[s].s2 : wsc[s].s3)
                                    : ((j < 2) ? wsc[s].s0 : wsc[s].s1);
         sc[s] = (j & 1) ? scale_hi<DT>(pr) : scale_lo<DT>(pr);
@@ -307,7 +308,7 @@ __device__ __forceinline__ void mma_block2(const uint16_t* sa, int stride,
     f32x4 t[NMS][NSUB];
 #pragma unroll
     for (int ms = 0; ms < NMS; ++ms) {
-      const f32x4 corr = T::mfma(af[ms][j], bconst, fzero);
+      const f32x4 corr = LAYOUT == Q_FP4_GROUP_K ? fzero : T::mfma(af[ms][j], bconst, fzero);
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) t[ms][s] = T::mfma(af[ms][j], bop[s], corr);
     }
@@ -1550,7 +1551,7 @@ up_splitk_kernel(const GemmParams p) {
       for (int s = 0; s < NSUB; ++s) acc[0][s] = f32x4{0.f, 0.f, 0.f, 0.f};
       static_assert(kSplitkRing % 2 == 0, "block pairs must not straddle the ring");
       WBlk<LAYOUT> wr[kSplitkRing][NSUB];
-      if constexpr (LAYOUT == Q_GROUP_K) {
+      if constexpr (is_group(LAYOUT)) {
         // group scales of the wave's 32 rows over the chunk, staged in the
         // wave's own LDS region (read back only by the wave: no barrier);
         // 8 bytes (4 groups) per row and block
@@ -1695,7 +1696,7 @@ template <int DT, int LAYOUT>
 static hipError_t launch_splitk_dl(const GemmParams& p, int max_tiles, hipStream_t st) {
   // x slice [16][cb * 128 + 8], then (group layout) per wave [32][4 * cb] scales
   const size_t lds = sizeof(uint16_t) * (16 * (static_cast<size_t>(p.cb) * 128 + 8) +
-                                         (LAYOUT == Q_GROUP_K ? kTileWaves * 32 * 4 * p.cb : 0));
+                                         (is_group(LAYOUT) ? kTileWaves * 32 * 4 * p.cb : 0));
   const hipError_t err = allow_lds_tile(up_splitk_kernel<DT, LAYOUT, kSplitkNsub>, lds);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((up_splitk_kernel<DT, LAYOUT, kSplitkNsub>),
@@ -1712,8 +1713,10 @@ hipError_t launch_up_splitk(const GemmParams& p, int dtype, int layout, int max_
     return hipErrorInvalidValue;
   if (dtype == DT_BF16)
     return layout == Q_GROUP_K ? launch_splitk_dl<DT_BF16, Q_GROUP_K>(p, max_tiles, stream)
+         : layout == Q_FP4_GROUP_K ? launch_splitk_dl<DT_BF16, Q_FP4_GROUP_K>(p, max_tiles, stream)
                                : launch_splitk_dl<DT_BF16, Q_PER_CHANNEL>(p, max_tiles, stream);
   return layout == Q_GROUP_K ? launch_splitk_dl<DT_FP16, Q_GROUP_K>(p, max_tiles, stream)
+       : layout == Q_FP4_GROUP_K ? launch_splitk_dl<DT_FP16, Q_FP4_GROUP_K>(p, max_tiles, stream)
                              : launch_splitk_dl<DT_FP16, Q_PER_CHANNEL>(p, max_tiles, stream);
 }
 
@@ -1733,7 +1736,7 @@ hipError_t launch_splitk_act(const GemmParams& p, int dtype, bool gated, hipStre
 
 template <int DT, int LAYOUT, int MODE, bool X16>
 static hipError_t launch_tile_kx(const GemmParams& p, dim3 grid, hipStream_t st) {
-  if constexpr (LAYOUT == Q_GROUP_K) {
+  if constexpr (is_group(LAYOUT)) {
     if (tile_scales_in_lds(LAYOUT, p.K)) {
       const size_t lds = tile_lds_bytes(true, p.K);
       const hipError_t err = allow_lds_tile(tile_gemm_kernel<DT, LAYOUT, MODE, true, X16>, lds);
@@ -1818,8 +1821,10 @@ hipError_t launch_down_resident(const GemmParams& p, int dtype, int layout, int 
   const dim3 grid(n_main + (p.fin_cnt != nullptr ? fin_zero_workgroups(p.T) : 0));
   if (dtype == DT_BF16)
     return layout == Q_GROUP_K ? launch_resident_dl<DT_BF16, Q_GROUP_K>(p, grid, stream)
+         : layout == Q_FP4_GROUP_K ? launch_resident_dl<DT_BF16, Q_FP4_GROUP_K>(p, grid, stream)
                                : launch_resident_dl<DT_BF16, Q_PER_CHANNEL>(p, grid, stream);
   return layout == Q_GROUP_K ? launch_resident_dl<DT_FP16, Q_GROUP_K>(p, grid, stream)
+       : layout == Q_FP4_GROUP_K ? launch_resident_dl<DT_FP16, Q_FP4_GROUP_K>(p, grid, stream)
                              : launch_resident_dl<DT_FP16, Q_PER_CHANNEL>(p, grid, stream);
 }
 
@@ -1832,8 +1837,10 @@ hipError_t launch_tile_gemm(const GemmParams& p, int dtype, int layout, int mode
   const dim3 grid(n_main + (fin ? fin_zero_workgroups(p.T) : 0));
   if (dtype == DT_BF16)
     return layout == Q_GROUP_K ? launch_tile_mode<DT_BF16, Q_GROUP_K>(p, mode, grid, stream)
+         : layout == Q_FP4_GROUP_K ? launch_tile_mode<DT_BF16, Q_FP4_GROUP_K>(p, mode, grid, stream)
                                : launch_tile_mode<DT_BF16, Q_PER_CHANNEL>(p, mode, grid, stream);
   return layout == Q_GROUP_K ? launch_tile_mode<DT_FP16, Q_GROUP_K>(p, mode, grid, stream)
+       : layout == Q_FP4_GROUP_K ? launch_tile_mode<DT_FP16, Q_FP4_GROUP_K>(p, mode, grid, stream)
                              : launch_tile_mode<DT_FP16, Q_PER_CHANNEL>(p, mode, grid, stream);
 }
 
