@@ -61,6 +61,7 @@ def _load():
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_route_topk.argtypes = [P, i64, i32, i32, i32, P, P]
     lib.oracle_unpack_fp4.argtypes = [P, i64, P]
+    lib.oracle_repack_per_channel.argtypes = [P, P, i64, i64, P, P]
     lib.oracle_e8m0_to_f32.argtypes = [P, i64, P]
     lib.oracle_quantize_mxfp4.argtypes = [P, i64, i64, P, P]
     _lib = lib
@@ -216,3 +217,19 @@ def quantize_mxfp4(w):
     sc = np.empty((rows, cols // 32), np.uint8)
     _load().oracle_quantize_mxfp4(_p(w), rows, cols, _p(packed), _p(sc))
     return packed.reshape(*w.shape[:-1], cols // 2), sc.reshape(*w.shape[:-1], cols // 32)
+
+
+def repack_per_channel(packed, scales):
+    """Per-channel INT4 [E, n_out/2, k_in] + scales [E, n_out] -> group layout
+    [E, n_out, k_in/2] + scales [E, n_out, k_in/32] (16-bit patterns)."""
+    packed, scales = _c(packed, np.uint8), _c(scales, np.uint16)
+    E, half, k_in = packed.shape
+    n_out = 2 * half
+    op = np.empty((E, n_out, k_in // 2), np.uint8)
+    osc = np.empty((E, n_out, k_in // 32), np.uint16)
+    for e in range(E):
+        pe, se = np.ascontiguousarray(packed[e]), np.ascontiguousarray(scales[e])
+        ope, ose = np.empty((n_out, k_in // 2), np.uint8), np.empty((n_out, k_in // 32), np.uint16)
+        _load().oracle_repack_per_channel(_p(pe), _p(se), n_out, k_in, _p(ope), _p(ose))
+        op[e], osc[e] = ope, ose
+    return op, osc

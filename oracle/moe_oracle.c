@@ -325,6 +325,30 @@ void oracle_dequant_matrix(const uint8_t* packed, const uint16_t* scales, int64_
 }
 
 /* ------------------------------------------------------------------------ */
+/* Setup-only re-layout of per-channel INT4 ([P3] Checkpoint format: packed  */
+/* along the output dim, one scale per output channel) into the group        */
+/* layout (packed along K, one scale per 32 values): the values move, the     */
+/* channel scale is repeated for each of the row's groups, so                 */
+/* W[n][k] = q[n][k] * s[n] is unchanged ([P1] SGLang Marlin comparison:      */
+/* weight repacking is setup-only and excluded from timing).                  */
+/*   in:  packed [n_out/2][k_in], scales [n_out]                              */
+/*   out: packed [n_out][k_in/2], scales [n_out][k_in/32]                     */
+/* ------------------------------------------------------------------------ */
+
+void oracle_repack_per_channel(const uint8_t* packed, const uint16_t* scales, int64_t n_out,
+                               int64_t k_in, uint8_t* out_packed, uint16_t* out_scales) {
+  for (int64_t n = 0; n < n_out; ++n) {
+    for (int64_t k = 0; k < k_in; k += 2) {
+      uint8_t b0 = packed[(n / 2) * k_in + k], b1 = packed[(n / 2) * k_in + k + 1];
+      int q0 = (n % 2 == 0) ? (b0 & 0xf) : (b0 >> 4);   /* raw nibbles: two's complement kept */
+      int q1 = (n % 2 == 0) ? (b1 & 0xf) : (b1 >> 4);
+      out_packed[n * (k_in / 2) + k / 2] = (uint8_t)(q0 | (q1 << 4));
+    }
+    for (int64_t g = 0; g < k_in / 32; ++g) out_scales[n * (k_in / 32) + g] = scales[n];
+  }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Route preparation ([P1] Benchmark: "route preparation"; [P2] Description: */
 /* route guards, padded fallback; [P1] Modification: invalid routes, masked  */
 /* expert counts).                                                           */

@@ -660,3 +660,41 @@ def test_fp4_brute_force_dense_all_experts(gated, dtype):
                 M[t, ids[t, k]] += tok.topk_weights[t, k].item()
     want = np.einsum("te,teh->th", M, Y)
     np.testing.assert_allclose(out, want, rtol=1e-4, atol=1e-5 * np.abs(want).max())
+
+
+# ---------------------------------------------------------------------------
+# setup-only re-layout of per-channel weights into the group layout
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("gated", [True, False])
+def test_repack_per_channel_preserves_every_weight(gated):
+    """The repacked group-layout weights dequantize (numpy float64, written
+    independently) to exactly the per-channel weights, and the forward on
+    them equals the per-channel forward bit for bit (same products, same
+    ascending sums)."""
+    wl = synth.custom(E=3, H=128, I=96, K=2, gated=gated, per_channel=True, seed=13)
+    W = synth.make_weights(wl)
+    p13, s13 = oracle.repack_per_channel(W.w13_packed.numpy(), bits(W.w13_scales))
+    p2, s2 = oracle.repack_per_channel(W.w2_packed.numpy(), bits(W.w2_scales))
+    np.testing.assert_array_equal(
+        np_dequant(p13, s13, oracle.Q_GROUP_K, oracle.DT_BF16),
+        np_dequant(W.w13_packed.numpy(), bits(W.w13_scales), oracle.Q_PER_CHANNEL, oracle.DT_BF16))
+    np.testing.assert_array_equal(
+        np_dequant(p2, s2, oracle.Q_GROUP_K, oracle.DT_BF16),
+        np_dequant(W.w2_packed.numpy(), bits(W.w2_scales), oracle.Q_PER_CHANNEL, oracle.DT_BF16))
+    tok = synth.make_tokens(wl, 9)
+    a = run_oracle(wl, W, tok)
+    b = oracle.moe_forward(bits(tok.x), p13, s13, p2, s2, tok.topk_ids.numpy(),
+                           tok.topk_weights.numpy(), hidden=wl.hidden, inter=wl.inter,
+                           num_experts=wl.num_experts,
+                           act=oracle.ACT_SILU_GATED if gated else oracle.ACT_RELU2,
+                           layout=oracle.Q_GROUP_K)
+    np.testing.assert_array_equal(a, b)
+    # a hand-checked byte: channels 0 and 1 of k = 0, 1 packed along N as
+    # 0x9F (k=0: ch0 = -1, ch1 = -7) and 0x70 (k=1: ch0 = 0, ch1 = 7) become
+    # along K ch0: (-1, 0) -> 0x0F, ch1: (-7, 7) -> 0x79
+    pk = np.zeros((1, 1, 64), np.uint8)
+    pk[0, 0, 0], pk[0, 0, 1] = 0x9F, 0x70
+    rp, rs = oracle.repack_per_channel(pk, np.array([[0x3F80, 0x4000]], np.uint16))
+    assert rp[0, 0, 0] == 0x0F and rp[0, 1, 0] == 0x79
+    assert (rs[0, 0] == 0x3F80).all() and (rs[0, 1] == 0x4000).all()
