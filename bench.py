@@ -28,6 +28,7 @@ same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -507,12 +508,34 @@ def main():
 
                 fused()
                 g_fused = cold_graph(fused)
+            # per-channel weights re-laid once into the group layout (setup,
+            # outside the timed region): the forward then takes the group
+            # layout's kernels; reported beside the per-channel forward
+            rep = None
+            g_rep = None
+            if wl.per_channel:
+                if name + "/group" not in weights:
+                    p13, s13 = binding.repack_per_channel(Wg.w13_packed, Wg.w13_scales)
+                    p2, s2 = binding.repack_per_channel(Wg.w2_packed, Wg.w2_scales)
+                    weights[name + "/group"] = synth.Weights(p13, s13, p2, s2)
+                Wr = weights[name + "/group"]
+                wlr = dataclasses.replace(wl, per_channel=False)
+                ws_g = torch.empty(max(1, binding.workspace_size(binding.desc_for(wlr, T))),
+                                   dtype=torch.uint8, device=dev)
+                out_g = torch.empty(T, wl.hidden, dtype=wl.dtype, device=dev)
+
+                def rep(tok=tok, ws_g=ws_g, out_g=out_g, Wr=Wr, wlr=wlr):
+                    return binding.forward_workload(wlr, Wr, tok, out=out_g, workspace=ws_g)
+
+                rep()
+                g_rep = cold_graph(rep)
             stage_b, total_b, total_f, stage_f, D, Rv = workload_bytes_flops(
                 wl, tok.topk_ids.cpu(), T)
             cases.append(dict(wl=wl, head=wi == 0, T=T, tok=tok, fwd=fwd, g_cold=g_cold,
                               g_warm=g_warm, plan=plan, route=route, g_route=g_route, router=[],
                               routed=routed, g_routed=g_routed, routed_cold=[], routed_stage=[],
                               fused=fused, g_fused=g_fused, fused_cold=[],
+                              rep=rep, g_rep=g_rep, rep_cold=[],
                               stage_bytes=stage_b, bytes=total_b, flops=total_f,
                               stage_flops=stage_f, D=D, Rv=Rv,
                               wbytes=D * weight_bytes_per_expert(wl),
@@ -569,6 +592,7 @@ def main():
             t_probe = time_cold(c["g_probe"], c["probe_fn"])
             t_routed = time_cold(c["g_routed"], c["routed"])
             t_fused = time_cold(c["g_fused"], c["fused"]) if c["fused"] is not None else None
+            t_rep = time_cold(c["g_rep"], c["rep"]) if c["rep"] is not None else None
             # first stage of the routed forward: routing fused with route
             # preparation (grouped path) or with the gate/up GEMM (small batch)
             si = 0 if c["plan"].path == 1 else 1
@@ -584,6 +608,8 @@ def main():
                 c["routed_stage"].append(t_rstage)
                 if t_fused is not None:
                     c["fused_cold"].append(t_fused)
+                if t_rep is not None:
+                    c["rep_cold"].append(t_rep)
                 for si, name in enumerate(STAGES):
                     if name in ("route_prep", "combine") and c["plan"].path == 2:
                         continue
@@ -644,6 +670,8 @@ def main():
                 "router_us_cold": round(statistics.fmean(c["router"]), 3),
                 "fused_finalize_us_cold": (round(statistics.fmean(c["fused_cold"]), 3)
                                            if c["fused_cold"] else None),
+                "group_layout_repacked_us_cold": (round(statistics.fmean(c["rep_cold"]), 3)
+                                                  if c["rep_cold"] else None),
                 "routed": {
                     "latency_us_cold": round(statistics.fmean(c["routed_cold"]), 3),
                     "fused_stage": "routing + route preparation" if c["plan"].path == 1

@@ -320,6 +320,23 @@ w4a16_status_t w4a16_moe_route_and_prepare(const w4a16_moe_desc_t* desc,
 w4a16_status_t w4a16_e8m0_to_scales(const uint8_t* e8m0, int64_t n, int32_t dtype, void* out,
                                     w4a16_stream_t stream);
 
+/* Setup-only re-layout of per-channel INT4 weights into the GROUP_K layout
+ * ([P1] SGLang Marlin comparison: weight repacking is setup-only and outside
+ * the timed region; [P3] Checkpoint format for the per-channel input).  The
+ * values move from packing along the output dim to packing along K, and the
+ * output channel's scale is repeated for each 32-value group of its row, so
+ * every weight q[n][k] * s[n] is unchanged and the forward runs the group
+ * layout's kernels on the result (qlayout W4A16_Q_GROUP_K, group 32).
+ *   packed      [n_experts][n_out/2][k_in] u8 (PER_CHANNEL)
+ *   scales      [n_experts][n_out] 16-bit
+ *   out_packed  [n_experts][n_out][k_in/2] u8, 4-byte aligned (same size)
+ *   out_scales  [n_experts][n_out][k_in/32] 16-bit (k_in/32 times as many)
+ * n_out even, k_in a multiple of 64.  Bit-exact data movement. */
+w4a16_status_t w4a16_repack_per_channel(const uint8_t* packed, const void* scales,
+                                        int64_t n_experts, int32_t n_out, int32_t k_in,
+                                        uint8_t* out_packed, void* out_scales,
+                                        w4a16_stream_t stream);
+
 /* Nibble unpacking with the device conversion the GEMMs use ([P3] Checkpoint
  * format): out[2i] = low nibble of packed[i], out[2i+1] = high nibble, both as
  * two's-complement int8 in [-8, 7].  out holds 2*n_bytes int8. */

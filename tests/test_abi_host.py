@@ -339,3 +339,20 @@ def test_fp4_layout_descriptor():
     with pytest.raises(B.W4A16Error) as ei:
         B.workspace_size(bad)
     assert ei.value.status == 2 and "group_size" in ei.value.message
+
+
+def test_repack_per_channel_argument_errors():
+    L = B.lib()
+    P = ctypes.c_void_p
+    p = P(0x1000)
+    assert L.w4a16_repack_per_channel(p, p, 2, 63, 128, p, p, None) == 1
+    assert b"n_out" in L.w4a16_last_error_message()
+    assert L.w4a16_repack_per_channel(p, p, 2, 64, 96, p, p, None) == 2
+    assert b"k_in" in L.w4a16_last_error_message()
+    assert L.w4a16_repack_per_channel(p, None, 2, 64, 128, p, p, None) == 1
+    assert b"scales" in L.w4a16_last_error_message()
+    assert L.w4a16_repack_per_channel(p, p, 2, 64, 128, P(0x1002), p, None) == 1
+    assert b"aligned" in L.w4a16_last_error_message()
+    assert L.w4a16_repack_per_channel(p, p, -1, 64, 128, p, p, None) == 1
+    # no experts: nothing enqueued, OK with null pointers
+    assert L.w4a16_repack_per_channel(None, None, 0, 64, 128, None, None, None) == 0

@@ -74,6 +74,7 @@ def lib():
                                            i32]
     L.w4a16_moe_route_and_prepare.argtypes = [pdesc, P, i32, i32, P, P, P, P, P, i64, P, P, P]
     L.w4a16_e8m0_to_scales.argtypes = [P, i64, i32, P, P]
+    L.w4a16_repack_per_channel.argtypes = [P, P, i64, i32, i32, P, P, P]
     L.w4a16_status_string.argtypes = [i32]
     L.w4a16_status_string.restype = ctypes.c_char_p
     L.w4a16_last_error_message.restype = ctypes.c_char_p
@@ -81,7 +82,8 @@ def lib():
               "w4a16_moe_forward_timed",
               "w4a16_moe_prepare_routes", "w4a16_unpack_int4", "w4a16_moe_route_topk",
               "w4a16_stream_probe", "w4a16_moe_forward_noalloc", "w4a16_moe_forward_routed",
-              "w4a16_moe_route_and_prepare", "w4a16_e8m0_to_scales"):
+              "w4a16_moe_route_and_prepare", "w4a16_e8m0_to_scales",
+              "w4a16_repack_per_channel"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -432,3 +434,19 @@ def e8m0_to_scales(e8m0: torch.Tensor, dtype=torch.bfloat16, stream=None) -> tor
                                       DT_FP16 if dtype == torch.float16 else DT_BF16, _ptr(out),
                                       _stream(stream)))
     return out
+
+
+def repack_per_channel(packed: torch.Tensor, scales: torch.Tensor, stream=None):
+    """Per-channel INT4 [E, N/2, K] + scales [E, N] -> the group layout
+    [E, N, K/2] + scales [E, N, K/32] (setup-only, on the GPU)."""
+    _dev("packed", packed, (torch.uint8,))
+    _dev("scales", scales, (torch.bfloat16, torch.float16), packed.device)
+    E, half, K = packed.shape
+    N = 2 * half
+    if tuple(scales.shape) != (E, N):
+        raise ValueError(f"scales: shape {tuple(scales.shape)}, expected {(E, N)}")
+    op = torch.empty(E, N, K // 2, dtype=torch.uint8, device=packed.device)
+    osc = torch.empty(E, N, K // 32, dtype=scales.dtype, device=packed.device)
+    _check(lib().w4a16_repack_per_channel(_ptr(packed), _ptr(scales), E, N, K, _ptr(op), _ptr(osc),
+                                          _stream(stream)))
+    return op, osc

@@ -820,6 +820,36 @@ w4a16_status_t w4a16_e8m0_to_scales(const uint8_t* e8m0, int64_t n, int32_t dtyp
                     "scale conversion launch");
 }
 
+w4a16_status_t w4a16_repack_per_channel(const uint8_t* packed, const void* scales,
+                                        int64_t n_experts, int32_t n_out, int32_t k_in,
+                                        uint8_t* out_packed, void* out_scales,
+                                        w4a16_stream_t stream_) {
+  if (n_experts < 0) return fail(W4A16_ERR_INVALID_ARG, "n_experts: %lld < 0", (long long)n_experts);
+  if (n_out <= 0 || n_out % 2 != 0)
+    return fail(W4A16_ERR_INVALID_ARG, "packed: n_out=%d (a positive even count)", n_out);
+  if (k_in <= 0 || k_in % 64 != 0)
+    return fail(W4A16_ERR_UNSUPPORTED, "packed: k_in=%d is not a multiple of 64", k_in);
+  if (n_experts > 65535)
+    return fail(W4A16_ERR_UNSUPPORTED, "n_experts: %lld exceeds 65535", (long long)n_experts);
+  if (n_experts == 0) return W4A16_OK;
+  const struct {
+    const void* p;
+    const char* name;
+  } ptrs[] = {{packed, "packed"}, {scales, "scales"}, {out_packed, "out_packed"},
+              {out_scales, "out_scales"}};
+  for (const auto& q : ptrs)
+    if (q.p == nullptr) return fail(W4A16_ERR_INVALID_ARG, "%s: null pointer", q.name);
+  if (misaligned(out_packed, 4))
+    return fail(W4A16_ERR_INVALID_ARG, "out_packed: address not 4-byte aligned");
+  if (misaligned(scales, 2) || misaligned(out_scales, 2))
+    return fail(W4A16_ERR_INVALID_ARG, "scales/out_scales: address not 2-byte aligned");
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  return hip_status(w4moe::launch_repack_per_channel(
+                        packed, static_cast<const uint16_t*>(scales), n_experts, n_out, k_in,
+                        out_packed, static_cast<uint16_t*>(out_scales), stream),
+                    "repack launch");
+}
+
 w4a16_status_t w4a16_moe_route_topk(const float* logits, int64_t num_tokens,
                                     int32_t num_global_experts, int32_t top_k,
                                     int32_t renormalize, int32_t* topk_ids, float* topk_weights,

@@ -13,6 +13,7 @@
 //                   valid routes (slot[t*K+k] >= 0).
 //   unpack_kernel   nibbles through the GEMMs' bit conversion, back to int8.
 //   e8m0_kernel     MXFP4 block scales to 16-bit scales (setup).
+//   repack_pc_kernel  per-channel INT4 into the group layout (setup).
 #include "device.h"
 #include "internal.h"
 
@@ -101,6 +102,39 @@ e8m0_kernel(const uint8_t* __restrict__ in, int64_t n, uint16_t* __restrict__ ou
   out[i] = H16<DT>::from_f32(v);
 }
 
+// Setup-only re-layout of per-channel INT4 (packed along N, [E][N/2][K],
+// scales [E][N]) into the group layout (packed along K, [E][N][K/2], the
+// channel scale repeated per 32 values, [E][N][K/32]).  Thread i writes
+// output bytes 4i..4i+3 of one expert; the scales are written by the threads
+// of each row's first K/32 bytes.
+__global__ void __launch_bounds__(256)
+repack_pc_kernel(const uint8_t* __restrict__ in, const uint16_t* __restrict__ sc_in, int n_out,
+                 int k_in, uint8_t* __restrict__ out, uint16_t* __restrict__ sc_out) {
+  const int64_t e = blockIdx.y;
+  const int64_t per_e = static_cast<int64_t>(n_out) * (k_in / 2);   // output bytes per expert
+  const int64_t b0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (b0 >= per_e) return;
+  const uint8_t* src = in + e * per_e;   // the input has as many bytes per expert
+  const int n = static_cast<int>(b0 / (k_in / 2));
+  const int kb = static_cast<int>(b0 % (k_in / 2));   // first output byte within the row
+  const int sh = 4 * (n & 1);                          // odd channels: high nibbles
+  uint32_t word = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int k = 2 * (kb + j);
+    const uint32_t lo = (src[static_cast<int64_t>(n >> 1) * k_in + k] >> sh) & 0xFu;
+    const uint32_t hi = (src[static_cast<int64_t>(n >> 1) * k_in + k + 1] >> sh) & 0xFu;
+    word |= (lo | (hi << 4)) << (8 * j);
+  }
+  *reinterpret_cast<uint32_t*>(out + e * per_e + b0) = word;
+  // scales: the row's K/32 group scales, 4 per thread (K/2 bytes per row is a
+  // multiple of 4, so a thread's bytes stay in one row)
+  const int groups = k_in / 32;
+  const uint16_t s = sc_in[e * n_out + n];
+  for (int gi = kb; gi < min(groups, kb + 4); ++gi)
+    sc_out[(e * n_out + n) * groups + gi] = s;
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
@@ -135,6 +169,20 @@ hipError_t launch_e8m0_to_h16(const uint8_t* e8m0, int64_t n, int dtype, uint16_
   else
     hipLaunchKernelGGL(e8m0_kernel<DT_FP16>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                        stream, e8m0, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace w4moe
+
+namespace w4moe {
+
+hipError_t launch_repack_per_channel(const uint8_t* in, const uint16_t* sc_in, int64_t n_experts,
+                                     int n_out, int k_in, uint8_t* out, uint16_t* sc_out,
+                                     hipStream_t stream) {
+  const int64_t per_e = static_cast<int64_t>(n_out) * (k_in / 2);
+  const dim3 grid(static_cast<unsigned>((per_e / 4 + 255) / 256), static_cast<unsigned>(n_experts));
+  hipLaunchKernelGGL(repack_pc_kernel, grid, dim3(256), 0, stream, in, sc_in, n_out, k_in, out,
+                     sc_out);
   return hipGetLastError();
 }
 

@@ -183,6 +183,9 @@ hipError_t launch_combine(const CombineParams& p, int dtype, int T, hipStream_t 
 hipError_t launch_unpack(const uint8_t* packed, int64_t n_bytes, int8_t* out, hipStream_t stream);
 hipError_t launch_e8m0_to_h16(const uint8_t* e8m0, int64_t n, int dtype, uint16_t* out,
                               hipStream_t stream);
+hipError_t launch_repack_per_channel(const uint8_t* in, const uint16_t* sc_in, int64_t n_experts,
+                                     int n_out, int k_in, uint8_t* out, uint16_t* sc_out,
+                                     hipStream_t stream);
 
 // Streaming-read probe over [bytes / row_bytes][row_bytes] (row_bytes a
 // multiple of 64, at most 8 * 16 * 64).
