@@ -207,11 +207,20 @@ def test_small_batch_path_only_for_short_intermediate():
     kimi = dict(hidden=7168, intermediate=256, num_local_experts=384, top_k=8)
     assert B.get_plan(B.make_desc(num_tokens=1, **kimi)).path == 2
     assert B.get_plan(B.make_desc(num_tokens=8, **kimi)).path == 2
-    # DeepSeek-like local share (I = 2048): the grouped path even for 1 token,
+    # I = 2048, top-8, every route local: the grouped path even for 1 token,
     # with the split-K gate/up spread over column chunks
     ds = dict(hidden=7168, intermediate=2048, num_local_experts=32, top_k=8)
     p = B.get_plan(B.make_desc(num_tokens=1, **ds))
     assert p.path == 1 and p.splitk_chunks > 0
+    # the same experts as a share of 256 global ones (one local route per
+    # token expected): the small-batch path up to its 64 routes
+    for T in (1, 8):
+        assert B.get_plan(B.make_desc(num_tokens=T, num_global_experts=256, **ds)).path == 2
+    assert B.get_plan(B.make_desc(num_tokens=9, num_global_experts=256, **ds)).path == 1
+    # a quarter local: 2 expected local routes x I = 4096, small batch; two
+    # thirds local: 5.3 x I > 8192, grouped
+    assert B.get_plan(B.make_desc(num_tokens=1, num_global_experts=128, **ds)).path == 2
+    assert B.get_plan(B.make_desc(num_tokens=1, num_global_experts=48, **ds)).path == 1
 
 
 def test_small_batch_path_limits():

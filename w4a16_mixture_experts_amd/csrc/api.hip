@@ -137,14 +137,22 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
              ((down_blocks + w4moe::kDecDownSliceBlocks - 1) / w4moe::kDecDownSliceBlocks);
 
   if (d->force_path) pl.path = d->force_path;
-  // the small-batch down kernel stages every route's pre-activations per
-  // 32-column workgroup: measured faster than the grouped path for 1-8 tokens
-  // when top_k * I is small (the I=256 top-8 shard, the I=1408 top-4
-  // per-channel model), several times slower for the I=2048 top-8 share
-  else pl.path = (pl.R <= w4moe::kSmallMaxRoutes && pl.items <= w4moe::kDecMaxItems &&
-                  H <= 8 * w4moe::kSmallMaxSlice && static_cast<int64_t>(K) * I <= 8192 &&
-                  static_cast<int64_t>(K) * I <= w4moe::kDecActLoads * w4moe::kDecThreadsAll * 8)
-                     ? 2 : 1;
+  // the small-batch down kernel stages the pre-activations of every valid
+  // route of its token per 32-column workgroup, so the choice counts the
+  // routes expected to be local (in proportion to the local share of the
+  // global experts).  Measured faster than the grouped path for 1-8 tokens
+  // when that count times I is small: the I=256 top-8 shard, the I=1408
+  // top-4 per-channel model, the I=2048 top-8 share of 32 of 256 experts
+  // (one local route per token: 57 -> 16 us at 1 token, 96 -> 82 us at 8);
+  // several times slower for an I=2048 top-8 model whose routes are all local
+  else {
+    const double share = d->num_global_experts > E
+                             ? static_cast<double>(E) / d->num_global_experts : 1.0;
+    pl.path = (pl.R <= w4moe::kSmallMaxRoutes && pl.items <= w4moe::kDecMaxItems &&
+               H <= 8 * w4moe::kSmallMaxSlice && K * share * I <= 8192.0 &&
+               static_cast<int64_t>(K) * I <= w4moe::kDecActLoads * w4moe::kDecThreadsAll * 8)
+                  ? 2 : 1;
+  }
 
   // per-wave reduction slice of the small-batch gate/up kernel (8 waves)
   const int up_blocks = (H + 127) / 128;
