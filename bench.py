@@ -342,6 +342,29 @@ def summarize_sq(args, sweep):
     print("\n".join(lines))
 
 
+def summarize_trace(args):
+    """A markdown table of the library's kernels from the kernel_stats.csv of a
+    rocprofv3 --kernel-trace --stats run (all launches of the run)."""
+    import csv
+    import re
+
+    with open(args.summarize_trace) as f:
+        rows = list(csv.DictReader(f))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    lines = ["| kernel | calls | avg us | min us | max us | share of GPU time % |",
+             "|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"]
+        if "w4moe" not in name:
+            continue
+        short = re.sub(r"\(w4moe::\w+\)$", "", name.replace("void w4moe::", "").replace("w4moe::", ""))
+        short = re.sub(r"\([\w ,:*&]*\)$", "", short).replace("(anonymous namespace)::", "")
+        lines.append(f"| {short} | {int(r['Calls'])} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{100.0 * float(r['TotalDurationNs']) / total:.2f} |")
+    print("\n".join(lines))
+
+
 def sweep_of(wl, args, headline):
     if headline and args.tokens:
         return [int(t) for t in args.tokens.split(",")]
@@ -374,6 +397,9 @@ def main():
                          "a --counter-pass run under rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE")
     ap.add_argument("--summarize-sq", metavar="CSV",
                     help="print a table of the SQ counters (SQ_SET) of a --counter-pass run")
+    ap.add_argument("--summarize-trace", metavar="CSV",
+                    help="print a table of the library's kernels from a rocprofv3 "
+                         "--kernel-trace --stats kernel_stats.csv")
     ap.add_argument("--counter-pass", action="store_true",
                     help="host-built inputs and library calls only (for counter runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -385,6 +411,10 @@ def main():
         print(f"bench.py: this benchmark runs on one GPU; --gpus {args.gpus} is not supported "
               "(the local MoE path has no multi-GPU mode)", file=sys.stderr)
         sys.exit(2)
+
+    if args.summarize_trace:
+        summarize_trace(args)
+        return
 
     import torch
 
