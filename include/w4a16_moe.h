@@ -101,7 +101,7 @@ typedef struct {
   int32_t qlayout;            /* w4a16_qlayout_t                                  */
   int32_t force_path;         /* 0, 1 = grouped (route preparation, expert tiles,
                                  down GEMM, combine kernel), 2 = small batch (no
-                                 route preparation; needs T*K <= 64)             */
+                                 route preparation; needs T*K <= 128)            */
   int32_t force_block_m;      /* grouped path: 0 or 64 (rows per expert tile;
                                  tiles are always 64 rows, empty 16-row subtiles
                                  skipped)                                        */

@@ -213,10 +213,15 @@ def test_small_batch_path_only_for_short_intermediate():
     p = B.get_plan(B.make_desc(num_tokens=1, **ds))
     assert p.path == 1 and p.splitk_chunks > 0
     # the same experts as a share of 256 global ones (one local route per
-    # token expected): the small-batch path up to its 64 routes
+    # token expected): the small-batch path up to 64 routes (past them most
+    # of its gate/up workgroups would own no local expert)
     for T in (1, 8):
         assert B.get_plan(B.make_desc(num_tokens=T, num_global_experts=256, **ds)).path == 2
     assert B.get_plan(B.make_desc(num_tokens=9, num_global_experts=256, **ds)).path == 1
+    # every route local: the small-batch path up to 128 routes
+    for T in (9, 16):
+        assert B.get_plan(B.make_desc(num_tokens=T, **kimi)).path == 2
+    assert B.get_plan(B.make_desc(num_tokens=17, **kimi)).path == 1
     # a quarter local: 2 expected local routes x I = 4096, small batch; two
     # thirds local: 5.3 x I > 8192, grouped
     assert B.get_plan(B.make_desc(num_tokens=1, num_global_experts=128, **ds)).path == 2
@@ -224,13 +229,14 @@ def test_small_batch_path_only_for_short_intermediate():
 
 
 def test_small_batch_path_limits():
-    # more than 64 routes (one wave's ballot) cannot take the small-batch path
-    d = B.make_desc(num_tokens=9, hidden=256, intermediate=384, num_local_experts=8, top_k=8,
+    # more than 128 routes (two ballots of one wave) cannot take the
+    # small-batch path
+    d = B.make_desc(num_tokens=17, hidden=256, intermediate=384, num_local_experts=8, top_k=8,
                     force_path=2)
     with pytest.raises(B.W4A16Error) as ei:
         B.workspace_size(d)
     assert ei.value.status == 2 and "routes" in ei.value.message
-    d.num_tokens = 8
+    d.num_tokens = 16
     assert B.get_plan(d).path == 2
     # hidden sizes beyond 8 waves x 1024 cannot take it either
     d2 = B.make_desc(num_tokens=1, hidden=8256, intermediate=384, num_local_experts=8, top_k=2,

@@ -92,8 +92,9 @@ def test_tiny_all_variants(force):
 
 
 @pytest.mark.parametrize("name,T", [
-    ("kimi_tp8", 1), ("kimi_tp8", 8), ("kimi_tp8", 32), ("deepseek_local", 1),
-    ("deepseek_local", 16), ("per_channel", 1), ("per_channel", 8), ("relu2_skew", 32)])
+    ("kimi_tp8", 1), ("kimi_tp8", 8), ("kimi_tp8", 16), ("kimi_tp8", 32), ("deepseek_local", 1),
+    ("deepseek_local", 8), ("deepseek_local", 16), ("per_channel", 1), ("per_channel", 8),
+    ("per_channel", 32), ("relu2_skew", 32)])
 def test_configs_small_token_counts(name, T):
     wl = synth.WORKLOADS[name]
     Wc, Wg = weights(name)
@@ -117,7 +118,9 @@ def test_configs_small_token_counts(name, T):
     ("relu2_skew", 32, dict(force_path=1, force_splitk=2)),
     ("deepseek_local", 16, dict(force_path=1, force_splitk=1)),
     ("deepseek_local", 16, dict(force_path=1, force_splitk=2)),
-    ("deepseek_local", 1, dict(force_path=2))])
+    ("deepseek_local", 1, dict(force_path=2)),
+    ("kimi_tp8", 16, dict(force_path=2)), ("kimi_tp8", 16, dict(force_path=1)),
+    ("deepseek_local", 16, dict(force_path=1)), ("tiny", 64, dict(force_path=2))])
 def test_config_variants(name, T, force):
     wl = synth.WORKLOADS[name]
     Wc, Wg = weights(name)
@@ -181,6 +184,28 @@ def test_single_expert_receives_everything():
         assert_close(out, ref, f"one expert force_splitk={sk}")
     out = forward(wl, Wg, tc.to("cuda"), force_path=2)           # 64 rows, 16 passes of 4
     assert_close(out, ref, "one expert small-batch path")
+    # 128 routes, the expert's rows in both halves of the two ballots
+    tc = tokens(wl, 64)
+    ids = torch.full_like(tc.topk_ids, 3)
+    ids[5, 0] = 1                                 # another expert between them
+    tc = synth.Tokens(tc.x, ids, tc.topk_weights)
+    out = forward(wl, Wg, tc.to("cuda"), force_path=2)
+    assert_close(out, oracle_out(wl, Wc, tc), "one expert, 128 routes, small-batch path")
+
+
+def test_small_batch_expert_first_seen_past_route_64():
+    """An expert whose first route lies past route 64 (owned through the second
+    ballot), one spanning both halves, and invalid routes in both halves."""
+    wl, Wc, Wg = _small()
+    tc = tokens(wl, 64)                           # top-2: 128 routes
+    ids = torch.full_like(tc.topk_ids, 2)
+    ids.view(-1)[70:] = 5                         # expert 5 first seen at route 70
+    ids.view(-1)[40:80:7] = 6                     # expert 6 in both halves
+    ids.view(-1)[3] = -1
+    ids.view(-1)[100] = 99                        # invalid routes
+    tc = synth.Tokens(tc.x, ids, tc.topk_weights)
+    out = forward(wl, Wg, tc.to("cuda"), force_path=2)
+    assert_close(out, oracle_out(wl, Wc, tc), "experts past route 64")
 
 
 def test_activations_beyond_fp16_range():
@@ -360,7 +385,7 @@ POISON_CASES = [
     ("deepseek_local", 16, dict()),                   # split-K over column chunks
     ("tiny", 256, dict(force_path=1, fp16_route=1)),
     ("kimi_tp8", 256, dict(fused_finalize=1)),        # arrival counters start as 0xFF..
-    ("deepseek_local", 16, dict(fused_finalize=1)),   # tokens without local routes
+    ("deepseek_local", 16, dict(force_path=1, fused_finalize=1)),  # tokens without local routes
 ]
 
 
@@ -554,13 +579,14 @@ def test_fused_finalize_matches_separate_launch(name, T):
     wl = synth.WORKLOADS[name]
     _, Wg = weights(name)
     tg = tokens(wl, T, "cuda")
-    assert binding.get_plan(binding.desc_for(wl, T)).fused_combine == 0
-    assert binding.get_plan(binding.desc_for(wl, T, fused_finalize=1)).fused_combine == 1
-    sep = forward(wl, Wg, tg)
+    grouped = dict(force_path=1)  # the mode belongs to the grouped path
+    assert binding.get_plan(binding.desc_for(wl, T, **grouped)).fused_combine == 0
+    assert binding.get_plan(binding.desc_for(wl, T, fused_finalize=1, **grouped)).fused_combine == 1
+    sep = forward(wl, Wg, tg, **grouped)
     for _ in range(3):
-        d = binding.desc_for(wl, T, fused_finalize=1)
+        d = binding.desc_for(wl, T, fused_finalize=1, **grouped)
         ws = torch.full((binding.workspace_size(d),), 0xFF, dtype=torch.uint8, device="cuda")
         out = torch.full((T, wl.hidden), float("nan"), dtype=wl.dtype, device="cuda")
-        binding.forward_workload(wl, Wg, tg, out=out, workspace=ws, fused_finalize=1)
+        binding.forward_workload(wl, Wg, tg, out=out, workspace=ws, fused_finalize=1, **grouped)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), sep.view(torch.int16)), name

@@ -106,7 +106,7 @@ w4a16_status_t check_desc(const w4a16_moe_desc_t* d) {
 
 // Variant selection from the route count R = T*K ([P1] Modification:
 // route-count-based tile selection and small-batch split-K).
-//   path 2 (small batch): R <= 64.  No route preparation; the gate/up kernel
+//   path 2 (small batch): R <= 128.  No route preparation; the gate/up kernel
 //     finds each touched expert's rows in the ids and splits the reduction
 //     over 8 waves; the down kernel combines per token.
 //   path 1 (grouped): route preparation into 64-row expert tiles (empty
@@ -144,11 +144,19 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
   // when that count times I is small: the I=256 top-8 shard, the I=1408
   // top-4 per-channel model, the I=2048 top-8 share of 32 of 256 experts
   // (one local route per token: 57 -> 16 us at 1 token, 96 -> 82 us at 8);
-  // several times slower for an I=2048 top-8 model whose routes are all local
+  // several times slower for an I=2048 top-8 model whose routes are all local.
+  // Past 64 routes (the second ballot) only when every route is expected to
+  // be local: the gate/up grid has a workgroup per (16 columns, route slot),
+  // and one whose slot owns no local expert still pays the ids round trip
+  // before it exits.  Measured: the 384-expert shard at 12 and 16 tokens
+  // 125 -> 78 and 124 -> 94 us, the per-channel model at 16 and 32 tokens
+  // 111 -> 79 and 132 -> 123 us; the 32-of-256 share at 16 tokens 107 ->
+  // 170 us (about 29,000 of its 32,768 workgroups exit)
   else {
     const double share = d->num_global_experts > E
                              ? static_cast<double>(E) / d->num_global_experts : 1.0;
-    pl.path = (pl.R <= w4moe::kSmallMaxRoutes && pl.items <= w4moe::kDecMaxItems &&
+    const int64_t max_routes = share < 1.0 ? 64 : w4moe::kSmallMaxRoutes;
+    pl.path = (pl.R <= max_routes && pl.items <= w4moe::kDecMaxItems &&
                H <= 8 * w4moe::kSmallMaxSlice && K * share * I <= 8192.0 &&
                static_cast<int64_t>(K) * I <= w4moe::kDecActLoads * w4moe::kDecThreadsAll * 8)
                   ? 2 : 1;

@@ -10,8 +10,8 @@
 //        order before one 16-bit cast, no atomics.
 //
 // small_h_kernel  grid (16-column weight subtiles) x (route slots), 8 waves:
-//   the workgroup of the first route of each touched expert (one ballot over
-//   the ids) computes that expert's FP32 pre-activations for every route of
+//   the workgroup of the first route of each touched expert (two ballots
+//   over the <= 128 ids) computes that expert's FP32 pre-activations for every route of
 //   the expert, the reduction split over the 8 waves and summed in LDS in
 //   slice order.
 // decode_down_kernel  grid (32 output columns) x (tokens), 8 waves.  Work
@@ -69,7 +69,7 @@ __device__ __forceinline__ int local_id(int32_t g, int E, int off) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// small batch gate/up (T*K <= 64): pre-activations h = x W13^T in FP32 for one
+// small batch gate/up (T*K <= 128): pre-activations h = x W13^T in FP32 for one
 // 16-row weight subtile of one touched expert; 8 waves split the reduction.
 // ---------------------------------------------------------------------------
 // The rows of the expert come from one ballot over the ids; the workgroup of
@@ -107,7 +107,8 @@ small_h_kernel(const SmallHParams p) {
   __shared__ float s_red[kSmallWaves][64];
   __shared__ int32_t s_rid[ROUTE ? kSmallMaxRoutes : 1];
 
-  int32_t my_id;
+  // lane l holds the ids of routes l and l + 64 (R <= 128)
+  int32_t my_id, my_id1 = -1;
   if constexpr (ROUTE) {
     const bool writer = blockIdx.x == 0 && blockIdx.y == 0;
     route_tokens<kSmallRouteNpl>(p.ra, p.top_k, w, p.T, kSmallWaves, lane,
@@ -124,17 +125,23 @@ small_h_kernel(const SmallHParams p) {
     __syncthreads();
     my_id = lane < p.R ? s_rid[lane] : 0;
   } else {
-    // rows: the routes whose id equals route r0's id (R <= 64: one load, one ballot)
+    // rows: the routes whose id equals route r0's id (R <= 128: one load of
+    // two ids per lane, two ballots)
     const auto rids = make_rsrc(p.ids, 4u * static_cast<uint32_t>(p.R));
     my_id = static_cast<int32_t>(bload4(rids, 4u * lane, lane < p.R));
+    my_id1 = static_cast<int32_t>(bload4(rids, 4u * (lane + 64), lane + 64 < p.R));
   }
-  const int32_t gid = __builtin_amdgcn_readlane(my_id, r0);
+  const int32_t gid = r0 < 64 ? __builtin_amdgcn_readlane(my_id, r0)
+                              : __builtin_amdgcn_readlane(my_id1, r0 - 64);
   const int e = local_id(gid, p.E, p.off);
   if (e < 0) return;  // invalid route: nothing to do (uniform)
-  const uint64_t match = __ballot(lane < p.R && my_id == gid);
-  if (__builtin_ctzll(match) != r0) return;  // an earlier slot owns this expert (uniform)
-  const int M = __popcll(match);
-  const int my_tok = lane / p.top_k;  // token of route `lane`
+  const uint64_t match0 = __ballot(lane < p.R && my_id == gid);
+  const uint64_t match1 = __ballot(lane + 64 < p.R && my_id1 == gid);
+  const int first = match0 != 0 ? __builtin_ctzll(match0) : 64 + __builtin_ctzll(match1);
+  if (first != r0) return;  // an earlier slot owns this expert (uniform)
+  const int M = __popcll(match0) + __popcll(match1);
+  const int my_tok = lane / p.top_k;          // token of route `lane`
+  const int my_tok1 = (lane + 64) / p.top_k;  // token of route `lane + 64`
 
   const int wrow = nt * 16 + c;  // weight row (output column of h)
   const auto rw = make_rsrc(p.wq + static_cast<int64_t>(e) * p.wq_expert_bytes,
@@ -156,15 +163,27 @@ small_h_kernel(const SmallHParams p) {
 
   // one pass per 4 rows (more than 4 only if one expert takes more than 4 of
   // the routes; then the weights are streamed once per pass)
-  uint64_t rest = match;
+  uint64_t rest0 = match0, rest1 = match1;  // the expert's routes not yet taken
   for (int m0 = 0; m0 < M; m0 += kSmallRows) {
     const int nr = min(kSmallRows, M - m0);
     int rrow[kSmallRows], tok[kSmallRows];
 #pragma unroll
     for (int q = 0; q < kSmallRows; ++q) {
-      rrow[q] = (q < nr) ? __builtin_ctzll(rest) : r0;
-      if (q < nr) rest &= rest - 1;
-      tok[q] = __builtin_amdgcn_readlane(my_tok, rrow[q]);
+      rrow[q] = r0;
+      tok[q] = 0;
+      if (q < nr) {  // uniform
+        if (rest0 != 0) {
+          const int b = __builtin_ctzll(rest0);
+          rest0 &= rest0 - 1;
+          rrow[q] = b;
+          tok[q] = __builtin_amdgcn_readlane(my_tok, b);
+        } else {
+          const int b = __builtin_ctzll(rest1);
+          rest1 &= rest1 - 1;
+          rrow[q] = 64 + b;
+          tok[q] = __builtin_amdgcn_readlane(my_tok1, b);
+        }
+      }
     }
     // (1) this wave's slice of the staged rows (issued first: they are staged
     //     while the weights are still in flight): chunk idx -> row idx / CH

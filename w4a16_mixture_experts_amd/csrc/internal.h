@@ -68,7 +68,7 @@ inline int fin_zero_workgroups(int T) { return (T + kFinZeroTokens - 1) / kFinZe
 constexpr int kDecMaxItems = 256;         // (route, slice) items per token
 constexpr int kDecDownSliceBlocks = 2;    // 128-blocks of the reduction per item
 // small-batch gate/up kernel (pre-activations h in FP32)
-constexpr int kSmallMaxRoutes = 64;       // T*K: the row search is one wave's ballot
+constexpr int kSmallMaxRoutes = 128;      // T*K: the row search is two ballots of one wave
 constexpr int kSmallWaves = 8;            // reduction slices
 constexpr int kSmallThreads = kSmallWaves * 64;
 constexpr int kSmallRows = 4;             // token rows per pass (MFMA rows 0, 4, 8, 12)
