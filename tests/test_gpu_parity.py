@@ -193,6 +193,24 @@ def test_single_expert_receives_everything():
     assert_close(out, oracle_out(wl, Wc, tc), "one expert, 128 routes, small-batch path")
 
 
+def test_small_batch_more_distinct_experts_than_expected():
+    """When far fewer distinct local experts than routes are expected (here 8
+    local of 512 global experts: one distinct local expert expected at 32
+    tokens), the small-batch gate/up grid holds a few workgroup rows; when
+    every route is local, each row takes several of the 8 experts in turn."""
+    import dataclasses
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], name="tiny_g512", num_global_experts=512)
+    Wc = synth.make_weights(wl, device="cpu")
+    Wg = Wc.to("cuda")
+    for T in (16, 32):
+        tc = tokens(wl, T)
+        ids = (torch.arange(T * wl.top_k, dtype=torch.int32) % wl.num_experts).view(T, wl.top_k)
+        tc = synth.Tokens(tc.x, ids, tc.topk_weights)
+        assert binding.get_plan(binding.desc_for(wl, T)).path == 2
+        out = forward(wl, Wg, tc.to("cuda"))
+        assert_close(out, oracle_out(wl, Wc, tc), f"all routes local, T={T}")
+
+
 def test_small_batch_expert_first_seen_past_route_64():
     """An expert whose first route lies past route 64 (owned through the second
     ballot), one spanning both halves, and invalid routes in both halves."""

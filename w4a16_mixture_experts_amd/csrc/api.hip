@@ -47,6 +47,7 @@ struct Plan {
   int col_steps = 0;
   int splitk_S = 0, splitk_cb = 0;  // split-K gate/up chunks and blocks per chunk (0: off)
   int splitk_nc = 0, splitk_passes = 0;  // column chunks, column passes per chunk
+  int small_slots = 1;    // small batch: gate/up grid rows (distinct experts expected)
   int64_t R = 0, P = 0, MT = 0, items = 0;
   int N1 = 0;
   bool x16 = false;       // streaming tile launches take the exact fp16 route
@@ -136,6 +137,10 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
   pl.items = static_cast<int64_t>(K) *
              ((down_blocks + w4moe::kDecDownSliceBlocks - 1) / w4moe::kDecDownSliceBlocks);
 
+  // share of the routes expected to be local (uniform routing over the
+  // global experts)
+  const double share = d->num_global_experts > E
+                           ? static_cast<double>(E) / d->num_global_experts : 1.0;
   if (d->force_path) pl.path = d->force_path;
   // the small-batch down kernel stages the pre-activations of every valid
   // route of its token per 32-column workgroup, so the choice counts the
@@ -153,8 +158,6 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
   // 111 -> 79 and 132 -> 123 us; the 32-of-256 share at 16 tokens 107 ->
   // 170 us (about 29,000 of its 32,768 workgroups exit)
   else {
-    const double share = d->num_global_experts > E
-                             ? static_cast<double>(E) / d->num_global_experts : 1.0;
     const int64_t max_routes = share < 1.0 ? 64 : w4moe::kSmallMaxRoutes;
     pl.path = (pl.R <= max_routes && pl.items <= w4moe::kDecMaxItems &&
                H <= 8 * w4moe::kSmallMaxSlice && K * share * I <= 8192.0 &&
@@ -162,6 +165,21 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
                   ? 2 : 1;
   }
 
+  // small batch: one gate/up workgroup row per route slot, or, when far
+  // fewer distinct local experts than routes are expected, a row per
+  // distinct expert expected with a margin (a row takes a second expert when
+  // there are more).  The compact grid spares the rows whose slot owns no
+  // local expert their ids round trip, but every row then finds the owners
+  // with a chain of ballots, one per distinct expert: measured on the
+  // 32-of-256 share at 8 tokens 82 -> 74 us; with rows about as many as
+  // experts (the 60-expert model at 32 tokens) it was 123 -> 188 us
+  pl.small_slots = static_cast<int>(std::max<int64_t>(pl.R, 1));
+  if (pl.R > 0) {
+    const double Ed = static_cast<double>(E);
+    const double dexp = Ed * (1.0 - std::pow(1.0 - 1.0 / Ed, static_cast<double>(pl.R) * share));
+    const int64_t rows = static_cast<int64_t>(std::ceil(1.5 * dexp)) + 2;
+    if (2 * rows < pl.R) pl.small_slots = static_cast<int>(rows);
+  }
   // per-wave reduction slice of the small-batch gate/up kernel (8 waves)
   const int up_blocks = (H + 127) / 128;
   const int per_wave = (up_blocks + w4moe::kSmallWaves - 1) / w4moe::kSmallWaves;
@@ -465,6 +483,7 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
     sh.T = static_cast<int>(desc->num_tokens);
     sh.ids = topk_ids;
     sh.R = static_cast<int>(pl.R);
+    sh.slots = pl.small_slots;
     sh.top_k = K;
     sh.E = E;
     sh.off = desc->expert_offset;

@@ -131,173 +131,215 @@ small_h_kernel(const SmallHParams p) {
     my_id = static_cast<int32_t>(bload4(rids, 4u * lane, lane < p.R));
     my_id1 = static_cast<int32_t>(bload4(rids, 4u * (lane + 64), lane + 64 < p.R));
   }
-  const int32_t gid = r0 < 64 ? __builtin_amdgcn_readlane(my_id, r0)
-                              : __builtin_amdgcn_readlane(my_id1, r0 - 64);
-  const int e = local_id(gid, p.E, p.off);
-  if (e < 0) return;  // invalid route: nothing to do (uniform)
-  const uint64_t match0 = __ballot(lane < p.R && my_id == gid);
-  const uint64_t match1 = __ballot(lane + 64 < p.R && my_id1 == gid);
-  const int first = match0 != 0 ? __builtin_ctzll(match0) : 64 + __builtin_ctzll(match1);
-  if (first != r0) return;  // an earlier slot owns this expert (uniform)
-  const int M = __popcll(match0) + __popcll(match1);
+  // Grid rows.  One row per route slot (gridDim.y == R): row r works iff
+  // route r is the first route of a local expert.  Fewer rows (most routes
+  // expected not local): the owner slots, the first route of each distinct
+  // local expert, are found with one ballot per distinct local id, and row y
+  // takes the distinct experts y, y + rows, ...  (a serial chain of ballots:
+  // with one row per slot it would only delay the weight loads).
+  const bool direct = static_cast<int>(gridDim.y) == p.R;
+  uint64_t own0 = 0, own1 = 0;
+  int n_own = r0 + 1;  // direct: the loop below runs once, for slot r0
+  if (!direct) {
+    uint64_t rem0 = __ballot(lane < p.R && local_id(my_id, p.E, p.off) >= 0);
+    uint64_t rem1 = __ballot(lane + 64 < p.R && local_id(my_id1, p.E, p.off) >= 0);
+    while (rem0 != 0) {
+      const int j = __builtin_ctzll(rem0);
+      const int32_t v = __builtin_amdgcn_readlane(my_id, j);
+      own0 |= 1ull << j;
+      rem0 &= ~__ballot(my_id == v);
+      rem1 &= ~__ballot(my_id1 == v);
+    }
+    while (rem1 != 0) {
+      const int j = __builtin_ctzll(rem1);
+      const int32_t v = __builtin_amdgcn_readlane(my_id1, j);
+      own1 |= 1ull << j;
+      rem1 &= ~__ballot(my_id1 == v);
+    }
+    n_own = __popcll(own0) + __popcll(own1);
+  }
   const int my_tok = lane / p.top_k;          // token of route `lane`
   const int my_tok1 = (lane + 64) / p.top_k;  // token of route `lane + 64`
 
-  const int wrow = nt * 16 + c;  // weight row (output column of h)
-  const auto rw = make_rsrc(p.wq + static_cast<int64_t>(e) * p.wq_expert_bytes,
-                            static_cast<uint32_t>(p.wq_expert_bytes));
-  const auto rs = make_rsrc(p.ws + static_cast<int64_t>(e) * p.ws_expert_elems,
-                            static_cast<uint32_t>(2 * p.ws_expert_elems));
-  const auto rx = make_rsrc(p.x, 2u * static_cast<uint32_t>(p.T) * static_cast<uint32_t>(p.lda));
-  const uint32_t boff = GROUP ? static_cast<uint32_t>(wrow) * (p.K >> 1)
-                              : static_cast<uint32_t>(wrow >> 1) * p.K;
-  const uint32_t soff = GROUP ? 2u * static_cast<uint32_t>(wrow) * (p.K >> 5) : 2u * wrow;
-  const int xs = p.kslice + 8;  // staged x row stride (16 B padding)
-  uint16_t* my_x = s_dyn + w * kSmallRows * xs;
-  uint16_t* my_sc = s_dyn + kSmallWaves * kSmallRows * xs + w * 16 * 32;  // [16 rows][32 scales]
-  const int kb = w * p.kslice;
-  const int ke = min(p.K, kb + p.kslice);
-  const int q_row = c >> 2;
-  const u32x4 bconst = {T::kNegOneHalf2, T::kNegOneHalf2, T::kNegOneHalf2, T::kNegOneHalf2};
-  const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
+  for (int kx = r0; kx < n_own; kx += static_cast<int>(gridDim.y)) {
+    int slot = r0;  // the route slot that owns this row's expert
+    if (!direct) {  // the owner slot of distinct expert kx
+      uint64_t m0 = own0, m1 = own1;
+      const int c0 = __popcll(m0);
+      if (kx < c0) {
+        for (int i = 0; i < kx; ++i) m0 &= m0 - 1;
+        slot = __builtin_ctzll(m0);
+      } else {
+        for (int i = 0; i < kx - c0; ++i) m1 &= m1 - 1;
+        slot = 64 + __builtin_ctzll(m1);
+      }
+    }
+    const int32_t gid = slot < 64 ? __builtin_amdgcn_readlane(my_id, slot)
+                                  : __builtin_amdgcn_readlane(my_id1, slot - 64);
+    const int e = local_id(gid, p.E, p.off);
+    if (e < 0) return;  // direct: invalid route, nothing to do (uniform)
+    const uint64_t match0 = __ballot(lane < p.R && my_id == gid);
+    const uint64_t match1 = __ballot(lane + 64 < p.R && my_id1 == gid);
+    // direct: an earlier slot owns this expert (uniform)
+    if (slot != (match0 != 0 ? __builtin_ctzll(match0) : 64 + __builtin_ctzll(match1))) return;
+    const int M = __popcll(match0) + __popcll(match1);
 
-  // one pass per 4 rows (more than 4 only if one expert takes more than 4 of
-  // the routes; then the weights are streamed once per pass)
-  uint64_t rest0 = match0, rest1 = match1;  // the expert's routes not yet taken
-  for (int m0 = 0; m0 < M; m0 += kSmallRows) {
-    const int nr = min(kSmallRows, M - m0);
-    int rrow[kSmallRows], tok[kSmallRows];
-#pragma unroll
-    for (int q = 0; q < kSmallRows; ++q) {
-      rrow[q] = r0;
-      tok[q] = 0;
-      if (q < nr) {  // uniform
-        if (rest0 != 0) {
-          const int b = __builtin_ctzll(rest0);
-          rest0 &= rest0 - 1;
-          rrow[q] = b;
-          tok[q] = __builtin_amdgcn_readlane(my_tok, b);
-        } else {
-          const int b = __builtin_ctzll(rest1);
-          rest1 &= rest1 - 1;
-          rrow[q] = 64 + b;
-          tok[q] = __builtin_amdgcn_readlane(my_tok1, b);
+    const int wrow = nt * 16 + c;  // weight row (output column of h)
+    const auto rw = make_rsrc(p.wq + static_cast<int64_t>(e) * p.wq_expert_bytes,
+                              static_cast<uint32_t>(p.wq_expert_bytes));
+    const auto rs = make_rsrc(p.ws + static_cast<int64_t>(e) * p.ws_expert_elems,
+                              static_cast<uint32_t>(2 * p.ws_expert_elems));
+    const auto rx = make_rsrc(p.x, 2u * static_cast<uint32_t>(p.T) * static_cast<uint32_t>(p.lda));
+    const uint32_t boff = GROUP ? static_cast<uint32_t>(wrow) * (p.K >> 1)
+                                : static_cast<uint32_t>(wrow >> 1) * p.K;
+    const uint32_t soff = GROUP ? 2u * static_cast<uint32_t>(wrow) * (p.K >> 5) : 2u * wrow;
+    const int xs = p.kslice + 8;  // staged x row stride (16 B padding)
+    uint16_t* my_x = s_dyn + w * kSmallRows * xs;
+    uint16_t* my_sc = s_dyn + kSmallWaves * kSmallRows * xs + w * 16 * 32;  // [16 rows][32 scales]
+    const int kb = w * p.kslice;
+    const int ke = min(p.K, kb + p.kslice);
+    const int q_row = c >> 2;
+    const u32x4 bconst = {T::kNegOneHalf2, T::kNegOneHalf2, T::kNegOneHalf2, T::kNegOneHalf2};
+    const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
+
+    // one pass per 4 rows (more than 4 only if one expert takes more than 4 of
+    // the routes; then the weights are streamed once per pass)
+    uint64_t rest0 = match0, rest1 = match1;  // the expert's routes not yet taken
+    for (int m0 = 0; m0 < M; m0 += kSmallRows) {
+      const int nr = min(kSmallRows, M - m0);
+      int rrow[kSmallRows], tok[kSmallRows];
+  #pragma unroll
+      for (int q = 0; q < kSmallRows; ++q) {
+        rrow[q] = slot;
+        tok[q] = 0;
+        if (q < nr) {  // uniform
+          if (rest0 != 0) {
+            const int b = __builtin_ctzll(rest0);
+            rest0 &= rest0 - 1;
+            rrow[q] = b;
+            tok[q] = __builtin_amdgcn_readlane(my_tok, b);
+          } else {
+            const int b = __builtin_ctzll(rest1);
+            rest1 &= rest1 - 1;
+            rrow[q] = 64 + b;
+            tok[q] = __builtin_amdgcn_readlane(my_tok1, b);
+          }
         }
       }
-    }
-    // (1) this wave's slice of the staged rows (issued first: they are staged
-    //     while the weights are still in flight): chunk idx -> row idx / CH
-    u32x4 xv[NKB];
-#pragma unroll
-    for (int i = 0; i < NKB; ++i) {
-      const int idx = lane + 64 * i;
-      const int q = idx / CH, ck = idx - q * CH;
-      const int tq = q == 0 ? tok[0] : q == 1 ? tok[1] : q == 2 ? tok[2] : tok[3];
-      const bool ok = q < nr && kb + 8 * ck < ke;
-      xv[i] = bload16(rx, 2u * (static_cast<uint32_t>(tq) * p.lda + kb + 8 * ck), ok);
-    }
-    // (2) group scales of the slice (at most 64 bytes per row): one 16-byte
-    //     load per lane covers the wave's 16 rows (lane l: row l / 4, part
-    //     l % 4), staged in the wave's own LDS region
-    u32x4 scv;
-    uint32_t scol_bits = 0;
-    if constexpr (GROUP) {
-      const uint32_t so = 2u * (static_cast<uint32_t>(nt * 16 + (lane >> 2)) * (p.K >> 5) +
-                                (kb >> 5)) + 16u * (lane & 3);
-      scv = bload16(rs, so, kb < p.K);
-    } else {
-      scol_bits = bload4(rs, soff & ~3u, true) >> (16 * (wrow & 1));
-    }
-    // (3) every weight of this wave's slice (kslice <= NKB * 128)
-    u32x4 bw[NKB];
-    u32x4 bw2[GROUP ? 1 : NKB];
-#pragma unroll
-    for (int i = 0; i < NKB; ++i) {
-      const int k0 = kb + 128 * i;
-      const int ng = k0 < ke ? min(4, (ke - k0) >> 5) : 0;
+      // (1) this wave's slice of the staged rows (issued first: they are staged
+      //     while the weights are still in flight): chunk idx -> row idx / CH
+      u32x4 xv[NKB];
+  #pragma unroll
+      for (int i = 0; i < NKB; ++i) {
+        const int idx = lane + 64 * i;
+        const int q = idx / CH, ck = idx - q * CH;
+        const int tq = q == 0 ? tok[0] : q == 1 ? tok[1] : q == 2 ? tok[2] : tok[3];
+        const bool ok = q < nr && kb + 8 * ck < ke;
+        xv[i] = bload16(rx, 2u * (static_cast<uint32_t>(tq) * p.lda + kb + 8 * ck), ok);
+      }
+      // (2) group scales of the slice (at most 64 bytes per row): one 16-byte
+      //     load per lane covers the wave's 16 rows (lane l: row l / 4, part
+      //     l % 4), staged in the wave's own LDS region
+      u32x4 scv;
+      uint32_t scol_bits = 0;
       if constexpr (GROUP) {
-        bw[i] = bload16(rw, boff + (k0 >> 1) + 16 * g, g < ng);
+        const uint32_t so = 2u * (static_cast<uint32_t>(nt * 16 + (lane >> 2)) * (p.K >> 5) +
+                                  (kb >> 5)) + 16u * (lane & 3);
+        scv = bload16(rs, so, kb < p.K);
       } else {
-        bw[i] = bload16(rw, boff + k0 + 32 * g, g < ng);
-        bw2[i] = bload16(rw, boff + k0 + 32 * g + 16, g < ng);
+        scol_bits = bload4(rs, soff & ~3u, true) >> (16 * (wrow & 1));
       }
-    }
-    // every load above is issued before anything below is scheduled (the
-    // scheduler would otherwise sink weight loads next to their use)
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < NKB; ++i) {
-      const int idx = lane + 64 * i;
-      const int q = idx / CH, ck = idx - q * CH;
-      *reinterpret_cast<u32x4*>(my_x + q * xs + 8 * ck) = permute_a(xv[i]);
-    }
-    if constexpr (GROUP) *reinterpret_cast<u32x4*>(my_sc + 8 * lane) = scv;
-    // the wave reads back only what its own lanes wrote: LDS order suffices.
-    // Every lane feeds staged row c / 4: rows 4q of the MFMA carry route q;
-    // the other rows only reach outputs t[1..3], which are never used, and
-    // rows q >= nr are staged zeros whose outputs are never stored.
-    const uint16_t* arow = my_x + q_row * xs;
-    const float scol = T::to_f32(scol_bits & 0xffffu);
-
-    // A fragments of a block, read one block ahead of their use
-    u32x4 af[2][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) af[0][j] = *reinterpret_cast<const u32x4*>(arow + 32 * j + 8 * g);
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NKB; ++i) {
-      if (i + 1 < NKB) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          af[(i + 1) & 1][j] =
-              *reinterpret_cast<const u32x4*>(arow + 128 * (i + 1) + 32 * j + 8 * g);
-      }
-      uint32_t d[4], d2[4];
-      d[0] = bw[i][0]; d[1] = bw[i][1]; d[2] = bw[i][2]; d[3] = bw[i][3];
-      if constexpr (GROUP) {
-        transpose_rows4(d[0], d[1], d[2], d[3]);
-      } else {
-        d2[0] = bw2[i][0]; d2[1] = bw2[i][1]; d2[2] = bw2[i][2]; d2[3] = bw2[i][3];
-        // 8 dwords per lane: evens and odds transposed separately
-        transpose_rows4(d[0], d[2], d2[0], d2[2]);
-        transpose_rows4(d[1], d[3], d2[1], d2[3]);
-      }
-      u32x2 sc2 = {0u, 0u};
-      if constexpr (GROUP) sc2 = *reinterpret_cast<const u32x2*>(my_sc + 32 * c + 4 * i);
-      // groups past the end of the reduction have zero x and zero weights,
-      // so t = 0 there and the (finite) scale read beside them is harmless
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x4 a = af[i & 1][j];
-        float sc;
-        u32x4 bop;
+      // (3) every weight of this wave's slice (kslice <= NKB * 128)
+      u32x4 bw[NKB];
+      u32x4 bw2[GROUP ? 1 : NKB];
+  #pragma unroll
+      for (int i = 0; i < NKB; ++i) {
+        const int k0 = kb + 128 * i;
+        const int ng = k0 < ke ? min(4, (ke - k0) >> 5) : 0;
         if constexpr (GROUP) {
-          const uint32_t pair = sc2[j >> 1];
-          sc = T::to_f32((j & 1) ? (pair >> 16) : (pair & 0xffffu));
-          bop = group_to_h16<DT, LAYOUT>(d[j]);
+          bw[i] = bload16(rw, boff + (k0 >> 1) + 16 * g, g < ng);
         } else {
-          sc = scol;
-          // sub-chunk j = dwords (2j, 2j+1) of the lane's 8
-          const uint32_t lo = (j < 2) ? d[2 * j] : d2[2 * j - 4];
-          const uint32_t hi = (j < 2) ? d[2 * j + 1] : d2[2 * j - 3];
-          bop = bytes_to_h16<DT>(lo >> (4 * par), hi >> (4 * par));
+          bw[i] = bload16(rw, boff + k0 + 32 * g, g < ng);
+          bw2[i] = bload16(rw, boff + k0 + 32 * g + 16, g < ng);
         }
-        // INT4: the -1.5 * sum(a) term of the (24 + q) / 16 encoding; FP4 needs none
-        const f32x4 corr = LAYOUT == Q_FP4_GROUP_K ? fzero : T::mfma(a, bconst, fzero);
-        const f32x4 t = T::mfma(a, bop, corr);
-        acc = fmaf(sc, t[0], acc);
       }
+      // every load above is issued before anything below is scheduled (the
+      // scheduler would otherwise sink weight loads next to their use)
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int i = 0; i < NKB; ++i) {
+        const int idx = lane + 64 * i;
+        const int q = idx / CH, ck = idx - q * CH;
+        *reinterpret_cast<u32x4*>(my_x + q * xs + 8 * ck) = permute_a(xv[i]);
+      }
+      if constexpr (GROUP) *reinterpret_cast<u32x4*>(my_sc + 8 * lane) = scv;
+      // the wave reads back only what its own lanes wrote: LDS order suffices.
+      // Every lane feeds staged row c / 4: rows 4q of the MFMA carry route q;
+      // the other rows only reach outputs t[1..3], which are never used, and
+      // rows q >= nr are staged zeros whose outputs are never stored.
+      const uint16_t* arow = my_x + q_row * xs;
+      const float scol = T::to_f32(scol_bits & 0xffffu);
+
+      // A fragments of a block, read one block ahead of their use
+      u32x4 af[2][4];
+  #pragma unroll
+      for (int j = 0; j < 4; ++j) af[0][j] = *reinterpret_cast<const u32x4*>(arow + 32 * j + 8 * g);
+      float acc = 0.0f;
+  #pragma unroll
+      for (int i = 0; i < NKB; ++i) {
+        if (i + 1 < NKB) {
+  #pragma unroll
+          for (int j = 0; j < 4; ++j)
+            af[(i + 1) & 1][j] =
+                *reinterpret_cast<const u32x4*>(arow + 128 * (i + 1) + 32 * j + 8 * g);
+        }
+        uint32_t d[4], d2[4];
+        d[0] = bw[i][0]; d[1] = bw[i][1]; d[2] = bw[i][2]; d[3] = bw[i][3];
+        if constexpr (GROUP) {
+          transpose_rows4(d[0], d[1], d[2], d[3]);
+        } else {
+          d2[0] = bw2[i][0]; d2[1] = bw2[i][1]; d2[2] = bw2[i][2]; d2[3] = bw2[i][3];
+          // 8 dwords per lane: evens and odds transposed separately
+          transpose_rows4(d[0], d[2], d2[0], d2[2]);
+          transpose_rows4(d[1], d[3], d2[1], d2[3]);
+        }
+        u32x2 sc2 = {0u, 0u};
+        if constexpr (GROUP) sc2 = *reinterpret_cast<const u32x2*>(my_sc + 32 * c + 4 * i);
+        // groups past the end of the reduction have zero x and zero weights,
+        // so t = 0 there and the (finite) scale read beside them is harmless
+  #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 a = af[i & 1][j];
+          float sc;
+          u32x4 bop;
+          if constexpr (GROUP) {
+            const uint32_t pair = sc2[j >> 1];
+            sc = T::to_f32((j & 1) ? (pair >> 16) : (pair & 0xffffu));
+            bop = group_to_h16<DT, LAYOUT>(d[j]);
+          } else {
+            sc = scol;
+            // sub-chunk j = dwords (2j, 2j+1) of the lane's 8
+            const uint32_t lo = (j < 2) ? d[2 * j] : d2[2 * j - 4];
+            const uint32_t hi = (j < 2) ? d[2 * j + 1] : d2[2 * j - 3];
+            bop = bytes_to_h16<DT>(lo >> (4 * par), hi >> (4 * par));
+          }
+          // INT4: the -1.5 * sum(a) term of the (24 + q) / 16 encoding; FP4 needs none
+          const f32x4 corr = LAYOUT == Q_FP4_GROUP_K ? fzero : T::mfma(a, bconst, fzero);
+          const f32x4 t = T::mfma(a, bop, corr);
+          acc = fmaf(sc, t[0], acc);
+        }
+      }
+      s_red[w][lane] = acc;
+      __syncthreads();
+      // wave 0: slices in order; lane row g holds staged row g (element 0)
+      if (w == 0 && g < nr) {
+        float v = s_red[0][lane];
+        for (int q = 1; q < kSmallWaves; ++q) v += s_red[q][lane];
+        p.h[static_cast<int64_t>(rrow[g]) * p.ldh + wrow] = 16.0f * v;
+      }
+      __syncthreads();
     }
-    s_red[w][lane] = acc;
-    __syncthreads();
-    // wave 0: slices in order; lane row g holds staged row g (element 0)
-    if (w == 0 && g < nr) {
-      float v = s_red[0][lane];
-      for (int q = 1; q < kSmallWaves; ++q) v += s_red[q][lane];
-      p.h[static_cast<int64_t>(rrow[g]) * p.ldh + wrow] = 16.0f * v;
-    }
-    __syncthreads();
-  }
+  }  // distinct experts kx
 }
 
 // ---------------------------------------------------------------------------
@@ -549,7 +591,8 @@ static hipError_t launch_small_h_nkb(const SmallHParams& p, int nkb, dim3 grid, 
 
 hipError_t launch_small_h(const SmallHParams& p, int dtype, int layout, int nkb, int n1,
                           hipStream_t stream) {
-  const dim3 grid(n1 / 16, p.R);
+  if (p.R < 1 || p.R > kSmallMaxRoutes || p.slots < 1 || p.slots > p.R) return hipErrorInvalidValue;
+  const dim3 grid(n1 / 16, p.slots);
   const size_t lds = small_h_lds_bytes(p.kslice);
   if (dtype == DT_BF16)
     return layout == Q_GROUP_K ? launch_small_h_nkb<DT_BF16, Q_GROUP_K>(p, nkb, grid, lds, stream)

@@ -95,6 +95,8 @@ struct SmallHParams {
   const int32_t* ids;         // [R] global ids (unless routed: ra.logits set)
   RouteArgs ra;               // routed: ids and weights come from the logits
   int R, top_k, E, off;
+  int slots;                  // grid rows: workgroup row y takes distinct local
+                              // experts y, y + slots, ... (1 <= slots <= R)
   const uint8_t* wq;          // w13 packed, expert 0
   const uint16_t* ws;         // w13 scales, expert 0
   int64_t wq_expert_bytes;
