@@ -704,8 +704,10 @@ def main():
                                                   if c["rep_cold"] else None),
                 "routed": {
                     "latency_us_cold": round(statistics.fmean(c["routed_cold"]), 3),
-                    "fused_stage": "routing + route preparation" if c["plan"].path == 1
-                                   else "routing + gate/up GEMM",
+                    "fused_stage": ("routing + route preparation (one launch up to 16 tokens)"
+                                    if c["plan"].path == 1 else
+                                    "routing + gate/up GEMM (one launch up to 16 routes and "
+                                    "512 gate/up workgroups)"),
                     "fused_stage_us": round(statistics.fmean(c["routed_stage"]), 3),
                     "unfused_us": round(statistics.fmean(c["router"]) + st.get(
                         "route_prep" if c["plan"].path == 1 else "gate_up_gemm", 0.0), 3),

@@ -496,12 +496,13 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
     sh.h = reinterpret_cast<float*>(ws + pl.off_act);
     sh.ldh = pl.N1;
     if (route != nullptr) {
-      if (route->Eg <= 64 * w4moe::kSmallRouteNpl && pl.R <= w4moe::kSmallRouteMaxRoutes) {
+      if (route->Eg <= 64 * w4moe::kSmallRouteNpl && pl.R <= w4moe::kSmallRouteMaxRoutes &&
+          static_cast<int64_t>(pl.N1 / 16) * pl.small_slots <= w4moe::kSmallRouteMaxWorkgroups) {
         sh.ra = *route;  // routed inside the gate/up launch
       } else {
         // every gate/up workgroup routes all tokens itself, so beyond a few
-        // routes (or with more global experts than that launch routes) the
-        // router kernel runs first
+        // routes or workgroups (or with more global experts than that launch
+        // routes) the router kernel runs first
         st = hip_status(w4moe::launch_router_topk(route->logits, route->T, route->Eg, K,
                                                   route->renorm, route->ids, route->wts, stream),
                         "router launch");

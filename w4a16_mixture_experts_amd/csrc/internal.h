@@ -75,6 +75,11 @@ constexpr int kSmallRows = 4;             // token rows per pass (MFMA rows 0, 4
 constexpr int kSmallMaxSlice = 1024;      // reduction per slice: hidden <= 8 * 1024
 constexpr int kSmallRouteNpl = 8;         // routed: logits per lane (E_global <= 512)
 constexpr int kSmallRouteMaxRoutes = 16;  // routed inside the launch up to this T*K
+// ... and at most this many gate/up workgroups: each of them routes the
+// tokens itself (the same bits in every one), which beyond about two
+// workgroups per CU costs more than the router launch it saves (the 32-of-256
+// share at 1 token, 2048 workgroups: 23 -> 41 us)
+constexpr int kSmallRouteMaxWorkgroups = 512;
 inline size_t small_h_lds_bytes(int kslice) {
   return sizeof(uint16_t) * static_cast<size_t>(kSmallWaves) * (kSmallRows * (kslice + 8) + 16 * 32);
 }
