@@ -15,7 +15,7 @@
 //   the expert, the reduction split over the 8 waves and summed in LDS in
 //   slice order.
 // decode_down_kernel  grid (32 output columns) x (tokens), 8 waves.  Work
-//   items are (route k, 256-wide slice of the reduction); each wave computes
+//   items are (valid route k, 256-wide slice of the reduction); each wave computes
 //   its items' 32 partial outputs in FP32 (one MFMA row: a route is a single
 //   activation row) into LDS; then 32 lanes add, for k = 0..K-1 in order,
 //   w[t,k] * (sum of k's slices in slice order) and cast once to 16 bits.
@@ -351,28 +351,34 @@ small_h_kernel(const SmallHParams p) {
 // routes and the weights of each wave's first work item (raw buffer loads:
 // masked lanes read zeros, nothing waits on a load before its use).
 // SiLU(gate)*up or ReLU^2 is computed once per value, rounded to 16 bits and
-// staged in LDS in A operand order.  Work items are (route k, 256-wide slice
-// of the reduction); each wave computes its items' 32 partial outputs (one
-// MFMA row: a route is a single activation row) into LDS; then 32 lanes add,
-// for k = 0..K-1 in order, w[t,k] * (sum of k's slices in slice order) and
-// cast once.
-template <int DT, int LAYOUT, bool GATED, int AL>
+// staged in LDS in A operand order.  Work items are (valid route k, 256-wide
+// slice of the reduction): invalid routes take none; each wave computes its
+// items' 32 partial outputs (one MFMA row: a route is a single activation row)
+// into LDS, and with PF (more items than waves possible) the loads of its next
+// item are in flight while it computes one; then 32 lanes add, for k =
+// 0..K-1 in order, w[t,k] * (sum of k's slices in slice order) over the valid
+// routes and cast once.
+template <int DT, int LAYOUT, bool GATED, int AL, bool PF>
 __global__ void __launch_bounds__(kDecThreads)
 decode_down_kernel(const DecodeDownParams p) {
   using T = H16<DT>;
   constexpr int NSUB = 2;
   constexpr int SL = kDecDownSliceBlocks;  // blocks of 128 per item
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  // the wave index as a wave-uniform value: items, routes and expert ids
+  // derived from it stay scalar (buffer descriptors included)
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int c = lane & 15, g = lane >> 4, par = c & 1;
   const int n0 = blockIdx.x * 32;
   const int t = blockIdx.y;
   const int nblk = (p.I + 127) / 128;
   const int nsl = (nblk + SL - 1) / SL;
-  const int items = p.top_k * nsl;
   const int as = p.I + 8;                  // staged activation row stride
 
-  extern __shared__ uint16_t s_act[];      // [top_k][I + 8], A operand order
-  __shared__ float s_y[kDecMaxItems][32];
+  extern __shared__ uint16_t s_dyn[];      // [top_k][I + 8] activations (A operand
+                                           // order), then [top_k * nsl][32] partials
+  uint16_t* const s_act = s_dyn;
+  float (*const s_y)[32] = reinterpret_cast<float (*)[32]>(
+      s_dyn + static_cast<size_t>(p.top_k) * as);
 
   // (1) the token's routes: lane k < top_k holds id, local expert and weight
   const uint32_t r_base = static_cast<uint32_t>(t) * p.top_k;
@@ -380,6 +386,10 @@ decode_down_kernel(const DecodeDownParams p) {
   const auto rwts = make_rsrc(p.wts + r_base, 4u * p.top_k);
   const int e_lane = local_id(static_cast<int32_t>(bload4(rids, 4u * lane, lane < p.top_k)), p.E, p.off);
   const float wt_lane = __uint_as_float(bload4(rwts, 4u * lane, lane < p.top_k));
+  // work items are (valid route, slice): item it is slice it % nsl of the
+  // (it / nsl)-th valid route in top-k order (invalid routes take no item)
+  const uint32_t vmask = static_cast<uint32_t>(__ballot(lane < p.top_k && e_lane >= 0));
+  const int items = __popc(vmask) * nsl;
 
   bool on[NSUB];
   int wrow[NSUB];
@@ -398,7 +408,7 @@ decode_down_kernel(const DecodeDownParams p) {
   for (int i = 0; i < AL; ++i) {
     const int idx = tid + kDecThreads * i;
     const int k = idx < nch ? idx / ich : 0, cc = idx < nch ? idx - k * ich : 0;
-    const bool ok = idx < nch && __shfl(e_lane, k) >= 0;
+    const bool ok = idx < nch && ((vmask >> k) & 1u) != 0;
     const uint32_t off = 4u * (static_cast<uint32_t>(k) * p.ldh + 8 * cc);
     hg[i][0] = __builtin_bit_cast(f32x4, bload16(rh, off, ok));
     hg[i][1] = __builtin_bit_cast(f32x4, bload16(rh, off + 16, ok));
@@ -408,21 +418,28 @@ decode_down_kernel(const DecodeDownParams p) {
     }
   }
 
-  // (3) weights of a work item (route k, reduction slice sl)
+  // (3) weights of a work item (route k, reduction slice sl); an item past
+  // the last loads nothing (e = -1)
   const uint32_t boff[NSUB] = {
       is_group(LAYOUT) ? static_cast<uint32_t>(wrow[0]) * (p.I >> 1)
                           : static_cast<uint32_t>(wrow[0] >> 1) * p.I,
       is_group(LAYOUT) ? static_cast<uint32_t>(wrow[1]) * (p.I >> 1)
                           : static_cast<uint32_t>(wrow[1] >> 1) * p.I};
+  auto item_route = [&](int it) {  // top-k index of item it's route
+    uint32_t m = vmask;
+    for (int i = it / nsl; i > 0; --i) m &= m - 1;
+    return __builtin_ctz(m);
+  };
   auto load_item = [&](int it, BBlk<LAYOUT> (&b)[SL][NSUB], float (&scol)[NSUB], int& e) {
-    const int k = it / nsl;
-    e = __builtin_amdgcn_readlane(e_lane, k);
+    const bool have = it < items;
+    const int k = have ? item_route(it) : 0;
+    e = have ? __builtin_amdgcn_readlane(e_lane, k) : -1;
     const int ee = e >= 0 ? e : 0;
     const auto rw = make_rsrc(p.wq + static_cast<int64_t>(ee) * p.wq_expert_bytes,
                               static_cast<uint32_t>(p.wq_expert_bytes));
     const auto rs = make_rsrc(p.ws + static_cast<int64_t>(ee) * p.ws_expert_elems,
                               static_cast<uint32_t>(2 * p.ws_expert_elems));
-    const int sl = it - k * nsl;
+    const int sl = it % nsl;
     const int kb = sl * SL * 128;
     const int ke = min(p.I, kb + SL * 128);
 #pragma unroll
@@ -456,17 +473,18 @@ decode_down_kernel(const DecodeDownParams p) {
                     : T::to_f32(bload4(rs, (2u * wrow[s]) & ~3u, e >= 0 && on[s]) >> (16 * (wrow[s] & 1)));
   };
 
-  BBlk<LAYOUT> b[SL][NSUB];
-  float scol[NSUB];
-  int e_cur = -1;
-  if (w < items) load_item(w, b, scol, e_cur);
+  BBlk<LAYOUT> b[PF ? 2 : 1][SL][NSUB];
+  float scol[PF ? 2 : 1][NSUB];
+  int e_cur[PF ? 2 : 1];
+  load_item(w, b[0], scol[0], e_cur[0]);
 
-  // (4) activation: computed once per value, 16-bit, A operand order
+  // (4) activation of the valid routes: computed once per value, 16-bit, A
+  // operand order (the rows of invalid routes are never read)
 #pragma unroll
   for (int i = 0; i < AL; ++i) {
     const int idx = tid + kDecThreads * i;
-    if (idx < nch) {
-      const int k = idx / ich, cc = idx - k * ich;
+    const int k = idx < nch ? idx / ich : 0, cc = idx - k * ich;
+    if (idx < nch && ((vmask >> k) & 1u) != 0) {
       float v[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -490,11 +508,12 @@ decode_down_kernel(const DecodeDownParams p) {
 
   const u32x4 bconst = {T::kNegOneHalf2, T::kNegOneHalf2, T::kNegOneHalf2, T::kNegOneHalf2};
   const f32x4 fzero = {0.f, 0.f, 0.f, 0.f};
-  for (int it = w; it < items; it += kDecWaves) {
-    if (it != w) load_item(it, b, scol, e_cur);
-    const int k = it / nsl, sl = it - k * nsl;
+  // one item's 32 partial outputs into s_y[it]
+  auto compute_item = [&](int it, BBlk<LAYOUT> (&bb)[SL][NSUB], const float (&sc_col)[NSUB],
+                          int e) {
+    const int k = item_route(it), sl = it % nsl;
     float y[NSUB] = {0.0f, 0.0f};
-    if (e_cur >= 0) {
+    if (e >= 0) {
       const uint16_t* arow = s_act + k * as;
       const int kb = sl * SL * 128;
       const int ke = min(p.I, kb + SL * 128);
@@ -503,7 +522,7 @@ decode_down_kernel(const DecodeDownParams p) {
         const int k0 = kb + 128 * i;
         const int ng = k0 < ke ? min(4, (ke - k0) >> 5) : 0;
 #pragma unroll
-        for (int s = 0; s < NSUB; ++s) tr_b<LAYOUT>(b[i][s]);
+        for (int s = 0; s < NSUB; ++s) tr_b<LAYOUT>(bb[i][s]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const bool gv = j < ng;
@@ -517,9 +536,9 @@ decode_down_kernel(const DecodeDownParams p) {
           const f32x4 corr = LAYOUT == Q_FP4_GROUP_K ? fzero : T::mfma(a, bconst, fzero);
 #pragma unroll
           for (int s = 0; s < NSUB; ++s) {
-            float sc = (is_group(LAYOUT)) ? sc_of<DT>(b[i][s].s[j >> 1], j) : scol[s];
+            float sc = (is_group(LAYOUT)) ? sc_of<DT>(bb[i][s].s[j >> 1], j) : sc_col[s];
             sc = (gv && on[s]) ? sc : 0.0f;
-            const f32x4 tt = T::mfma(a, b_op<DT, LAYOUT>(b[i][s], j, par), corr);
+            const f32x4 tt = T::mfma(a, b_op<DT, LAYOUT>(bb[i][s], j, par), corr);
             y[s] = fmaf(sc, tt[0], y[s]);
           }
         }
@@ -529,16 +548,34 @@ decode_down_kernel(const DecodeDownParams p) {
       s_y[it][c] = y[0];
       s_y[it][16 + c] = y[1];
     }
+  };
+  if constexpr (PF) {
+    // two register sets used alternately: the next item's loads (masked
+    // past the last) are in flight while an item is computed
+    for (int it = w; it < items; it += 2 * kDecWaves) {
+      load_item(it + kDecWaves, b[1], scol[1], e_cur[1]);
+      compute_item(it, b[0], scol[0], e_cur[0]);
+      if (it + kDecWaves >= items) break;
+      load_item(it + 2 * kDecWaves, b[0], scol[0], e_cur[0]);
+      compute_item(it + kDecWaves, b[1], scol[1], e_cur[1]);
+    }
+  } else {
+    for (int it = w; it < items; it += kDecWaves) {
+      if (it != w) load_item(it, b[0], scol[0], e_cur[0]);
+      compute_item(it, b[0], scol[0], e_cur[0]);
+    }
   }
   __syncthreads();
   if (tid < 32) {
     float acc = 0.0f;
+    int kv = 0;  // items of the valid routes before route k
     for (int k = 0; k < p.top_k; ++k) {
-      if (__builtin_amdgcn_readlane(e_lane, k) < 0) continue;  // invalid route: nothing
-      float y = s_y[k * nsl][tid];
-      for (int sl = 1; sl < nsl; ++sl) y += s_y[k * nsl + sl][tid];
+      if (((vmask >> k) & 1u) == 0) continue;  // invalid route: nothing
+      float y = s_y[kv * nsl][tid];
+      for (int sl = 1; sl < nsl; ++sl) y += s_y[kv * nsl + sl][tid];
       const float wk = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(wt_lane), k));
       acc += wk * (16.0f * y);
+      ++kv;
     }
     if (n0 + tid < p.H) p.out[static_cast<int64_t>(t) * p.H + n0 + tid] = T::from_f32(acc);
   }
@@ -605,9 +642,19 @@ hipError_t launch_small_h(const SmallHParams& p, int dtype, int layout, int nkb,
 
 template <int DT, int LAYOUT, bool GATED, int AL>
 static hipError_t launch_dd_k(const DecodeDownParams& p, dim3 grid, size_t lds, hipStream_t st) {
-  const hipError_t err = allow_lds(decode_down_kernel<DT, LAYOUT, GATED, AL>, lds);
+  // items (valid routes x slices) can outnumber the waves: prefetching variant
+  const int nsl = ((p.I + 127) / 128 + kDecDownSliceBlocks - 1) / kDecDownSliceBlocks;
+  if (p.top_k * nsl > kDecWaves) {
+    const hipError_t err = allow_lds(decode_down_kernel<DT, LAYOUT, GATED, AL, true>, lds);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((decode_down_kernel<DT, LAYOUT, GATED, AL, true>), grid, dim3(kDecThreads),
+                       lds, st, p);
+    return hipGetLastError();
+  }
+  const hipError_t err = allow_lds(decode_down_kernel<DT, LAYOUT, GATED, AL, false>, lds);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((decode_down_kernel<DT, LAYOUT, GATED, AL>), grid, dim3(kDecThreads), lds, st, p);
+  hipLaunchKernelGGL((decode_down_kernel<DT, LAYOUT, GATED, AL, false>), grid, dim3(kDecThreads),
+                     lds, st, p);
   return hipGetLastError();
 }
 

@@ -129,7 +129,10 @@ struct DecodeDownParams {
 constexpr int kDecThreadsAll = 512;       // threads of the small-batch down kernel
 constexpr int kDecActLoads = 8;           // activation chunks per thread: top_k * I <= 8 * 512 * 8
 inline size_t decode_down_lds_bytes(int top_k, int I) {
-  return sizeof(uint16_t) * static_cast<size_t>(top_k) * (I + 8);
+  // the activations [top_k][I + 8] 16-bit, then FP32 partials [items][32]
+  const int nsl = ((I + 127) / 128 + kDecDownSliceBlocks - 1) / kDecDownSliceBlocks;
+  return sizeof(uint16_t) * static_cast<size_t>(top_k) * (I + 8) +
+         sizeof(float) * 32 * static_cast<size_t>(top_k) * nsl;
 }
 
 struct CombineParams {
