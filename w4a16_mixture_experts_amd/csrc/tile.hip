@@ -35,6 +35,7 @@
 // Epilogue: UP writes the 16-bit activation (SiLU(gate)*up or ReLU^2) in A
 // operand order; DOWN writes the 16-bit expert outputs Y.
 #include <algorithm>
+#include <type_traits>
 
 #include "device.h"
 #include "internal.h"
@@ -78,8 +79,10 @@ __device__ __forceinline__ float scale_lo(uint32_t pair) { return H16<DT>::to_f3
 template <int DT>
 __device__ __forceinline__ float scale_hi(uint32_t pair) { return H16<DT>::to_f32(pair >> 16); }
 
-// acc += s * t for every output of a group (s: this lane's column scale)
-template <int NMS, int NSUB>
+// acc += s * t for every output of a group (s: this lane's column scale);
+// NI = 1: only element 0 of each lane (rows 0, 4, 8 and 12 of a subtile
+// whose routes sit there), the other rows' products are never used
+template <int NMS, int NSUB, int NI = 4>
 __device__ __forceinline__ void scale_accumulate(f32x4 (&acc)[NMS][NSUB],
                                                  const f32x4 (&t)[NMS][NSUB],
                                                  const float (&sc)[NSUB]) {
@@ -88,7 +91,7 @@ __device__ __forceinline__ void scale_accumulate(f32x4 (&acc)[NMS][NSUB],
 #pragma unroll
     for (int s = 0; s < NSUB; ++s)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[ms][s][i] = fmaf(sc[s], t[ms][s][i], acc[ms][s][i]);
+      for (int i = 0; i < NI; ++i) acc[ms][s][i] = fmaf(sc[s], t[ms][s][i], acc[ms][s][i]);
 }
 
 // One 128-wide reduction block of one 16-row weight subtile, as one lane holds
@@ -193,7 +196,7 @@ __device__ __forceinline__ void pass_scales(const WBlk<LAYOUT> (&first)[NSUB],
 // All A fragments are read first (LDS latency paid once per block); the
 // correction -1.5 * sum(a) of each group comes from one MFMA against a
 // constant operand.
-template <int DT, int LAYOUT, int NMS, bool UPFRONT = true, int NSUB = kNsub>
+template <int DT, int LAYOUT, int NMS, bool UPFRONT = true, int NSUB = kNsub, int NI = 4>
 __device__ __forceinline__ void mma_block(const uint16_t* sa, int stride,
                                           const WBlk<LAYOUT> (&wb)[NSUB],
                                           f32x4 (&acc)[NMS][NSUB], int c, int g, int par) {
@@ -254,14 +257,14 @@ __device__ __forceinline__ void mma_block(const uint16_t* sa, int stride,
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) t[ms][s] = T::mfma(a, bop[s], corr);
     }
-    scale_accumulate<NMS, NSUB>(acc, t, sc);
+    scale_accumulate<NMS, NSUB, NI>(acc, t, sc);
     if constexpr (!UPFRONT) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // mma_block with the group scales taken from the first block of the pair
 // (`second` selects its upper half); per-channel layouts use wb's own scale.
-template <int DT, int LAYOUT, int NMS, int NSUB>
+template <int DT, int LAYOUT, int NMS, int NSUB, int NI = 4>
 __device__ __forceinline__ void mma_block2(const uint16_t* sa, int stride,
                                            const WBlk<LAYOUT> (&wb)[NSUB],
                                            const WBlk<LAYOUT> (&wsc)[NSUB], int second,
@@ -312,7 +315,7 @@ __device__ __forceinline__ void mma_block2(const uint16_t* sa, int stride,
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) t[ms][s] = T::mfma(af[ms][j], bop[s], corr);
     }
-    scale_accumulate<NMS, NSUB>(acc, t, sc);
+    scale_accumulate<NMS, NSUB, NI>(acc, t, sc);
   }
 }
 
@@ -1506,6 +1509,11 @@ up_splitk_kernel(const GemmParams p) {
     // in flight at once, then the LDS stores
     const int nch = (b1 - b0) * 16;
     const int my_r = rp == 0 ? my_r0 : p.sorted[row_base + 16 * rp + c];
+    // a subtile of at most 4 routes (valid rows are a prefix) puts route q
+    // on MFMA row 4q: each lane's element 0 then carries one route, and the
+    // group scale is applied to that element alone (the other rows stay
+    // zero and their products are dropped)
+    const bool row4 = __ballot(lane < 16 && my_r >= 0) < 16;  // routes on rows 0..3 only
     // the route of each chunk's row, read per chunk (one batch, no lane
     // exchange chain), then the chunks
     int rr[kSplitkXLoads];
@@ -1513,7 +1521,8 @@ up_splitk_kernel(const GemmParams p) {
     for (int i = 0; i < kSplitkXLoads; ++i) {
       const int idx = tid + kTileThreads * i;
       const int row = min(idx / nch, 15);
-      rr[i] = p.sorted[row_base + 16 * rp + row];
+      const int src = row4 ? ((row & 3) == 0 ? row >> 2 : -1) : row;
+      rr[i] = src >= 0 ? p.sorted[row_base + 16 * rp + src] : -1;
     }
     u32x4 xv[kSplitkXLoads];
 #pragma unroll
@@ -1531,112 +1540,121 @@ up_splitk_kernel(const GemmParams p) {
       if (idx < 16 * nch) *reinterpret_cast<u32x4*>(s_x + row * stride + 8 * ch) = permute_a(xv[i]);
     }
     __syncthreads();
+    // the route of each accumulator element (element i of lane row g: tile
+    // row 4g + i; with row4 only element 0 is used, for row g)
     int rts[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rts[i] = __shfl(my_r, 4 * g + i);
+    for (int i = 0; i < 4; ++i) rts[i] = __shfl(my_r, row4 ? g : 4 * g + i);
 
-    const int n_end = min(p.n_cols, (cc + 1) * p.col_steps * kPassRows);
-    for (int n0 = cc * p.col_steps * kPassRows; n0 < n_end; n0 += kPassRows) {
-      int wrow[NSUB];
-      bool on[NSUB];
+    // the column passes, with NI accumulator elements per lane scaled
+    auto stream = [&](auto ni_tag) {
+      constexpr int NI = decltype(ni_tag)::value;
+      const int n_end = min(p.n_cols, (cc + 1) * p.col_steps * kPassRows);
+      for (int n0 = cc * p.col_steps * kPassRows; n0 < n_end; n0 += kPassRows) {
+        int wrow[NSUB];
+        bool on[NSUB];
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        const int r0 = n0 + (w * NSUB + s) * 16;
-        wrow[s] = r0 + c;
-        on[s] = r0 < p.n_cols;
-      }
-      const WSrc<NSUB> ws = make_wsrc<LAYOUT, NSUB>(p.K, wrow, on);
-      f32x4 acc[1][NSUB];
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) acc[0][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-      static_assert(kSplitkRing % 2 == 0, "block pairs must not straddle the ring");
-      WBlk<LAYOUT> wr[kSplitkRing][NSUB];
-      if constexpr (is_group(LAYOUT)) {
-        // group scales of the wave's 32 rows over the chunk, staged in the
-        // wave's own LDS region (read back only by the wave: no barrier);
-        // 8 bytes (4 groups) per row and block
-        const int nb = b1 - b0;
-        uint16_t* my_sc = s_x + 16 * stride + w * 32 * 4 * p.cb;  // [32 rows][4 * cb]
-        {
-          u32x2 sv[kSplitkScLoads];
-#pragma unroll
-          for (int i = 0; i < kSplitkScLoads; ++i) {
-            const int idx = lane + 64 * i;           // (row, block) = (idx / nb, idx % nb)
-            const int row = idx / nb, blk = idx - row * nb;
-            const int grow = n0 + 16 * w * NSUB + row;  // weight row
-            const bool ok = row < 32 && grow < p.n_cols;
-            const uint32_t so = 2u * (static_cast<uint32_t>(grow) * (p.K >> 5) + 4 * (b0 + blk));
-            sv[i] = __builtin_bit_cast(
-                u32x2, __builtin_amdgcn_raw_buffer_load_b64(wx.rs, ok ? so : kOob, 0, 0));
-          }
-          // the first weight blocks go out before the scales are stored
-#pragma unroll
-          for (int i = 0; i < kSplitkRing - 1; ++i)
-            load_wblk<LAYOUT, NSUB, SC_NONE>(wx, ws, 128 * (b0 + i), kend, g, wr[i]);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int i = 0; i < kSplitkScLoads; ++i) {
-            const int idx = lane + 64 * i;
-            const int row = idx / nb, blk = idx - row * nb;
-            if (row < 32) *reinterpret_cast<u32x2*>(my_sc + row * 4 * p.cb + 4 * blk) = sv[i];
-          }
+        for (int s = 0; s < NSUB; ++s) {
+          const int r0 = n0 + (w * NSUB + s) * 16;
+          wrow[s] = r0 + c;
+          on[s] = r0 < p.n_cols;
         }
-        for (int b = b0; b < b1; b += kSplitkRing) {
+        const WSrc<NSUB> ws = make_wsrc<LAYOUT, NSUB>(p.K, wrow, on);
+        f32x4 acc[1][NSUB];
 #pragma unroll
-          for (int u = 0; u < kSplitkRing; ++u) {
-            load_wblk<LAYOUT, NSUB, SC_NONE>(wx, ws, 128 * (b + u + kSplitkRing - 1), kend, g,
-                                             wr[(u + kSplitkRing - 1) % kSplitkRing]);
-            if (b + u < b1) {
+        for (int s = 0; s < NSUB; ++s) acc[0][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+        static_assert(kSplitkRing % 2 == 0, "block pairs must not straddle the ring");
+        WBlk<LAYOUT> wr[kSplitkRing][NSUB];
+        if constexpr (is_group(LAYOUT)) {
+          // group scales of the wave's 32 rows over the chunk, staged in the
+          // wave's own LDS region (read back only by the wave: no barrier);
+          // 8 bytes (4 groups) per row and block
+          const int nb = b1 - b0;
+          uint16_t* my_sc = s_x + 16 * stride + w * 32 * 4 * p.cb;  // [32 rows][4 * cb]
+          {
+            u32x2 sv[kSplitkScLoads];
 #pragma unroll
-              for (int s2 = 0; s2 < NSUB; ++s2) {
-                const u32x2 sp = *reinterpret_cast<const u32x2*>(
-                    my_sc + (16 * s2 + c) * 4 * p.cb + 4 * (b + u - b0));
-                wr[u][s2].s0 = sp[0];
-                wr[u][s2].s1 = sp[1];
+            for (int i = 0; i < kSplitkScLoads; ++i) {
+              const int idx = lane + 64 * i;           // (row, block) = (idx / nb, idx % nb)
+              const int row = idx / nb, blk = idx - row * nb;
+              const int grow = n0 + 16 * w * NSUB + row;  // weight row
+              const bool ok = row < 32 && grow < p.n_cols;
+              const uint32_t so = 2u * (static_cast<uint32_t>(grow) * (p.K >> 5) + 4 * (b0 + blk));
+              sv[i] = __builtin_bit_cast(
+                  u32x2, __builtin_amdgcn_raw_buffer_load_b64(wx.rs, ok ? so : kOob, 0, 0));
+            }
+            // the first weight blocks go out before the scales are stored
+#pragma unroll
+            for (int i = 0; i < kSplitkRing - 1; ++i)
+              load_wblk<LAYOUT, NSUB, SC_NONE>(wx, ws, 128 * (b0 + i), kend, g, wr[i]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < kSplitkScLoads; ++i) {
+              const int idx = lane + 64 * i;
+              const int row = idx / nb, blk = idx - row * nb;
+              if (row < 32) *reinterpret_cast<u32x2*>(my_sc + row * 4 * p.cb + 4 * blk) = sv[i];
+            }
+          }
+          for (int b = b0; b < b1; b += kSplitkRing) {
+#pragma unroll
+            for (int u = 0; u < kSplitkRing; ++u) {
+              load_wblk<LAYOUT, NSUB, SC_NONE>(wx, ws, 128 * (b + u + kSplitkRing - 1), kend, g,
+                                               wr[(u + kSplitkRing - 1) % kSplitkRing]);
+              if (b + u < b1) {
+#pragma unroll
+                for (int s2 = 0; s2 < NSUB; ++s2) {
+                  const u32x2 sp = *reinterpret_cast<const u32x2*>(
+                      my_sc + (16 * s2 + c) * 4 * p.cb + 4 * (b + u - b0));
+                  wr[u][s2].s0 = sp[0];
+                  wr[u][s2].s1 = sp[1];
+                }
+                mma_block<DT, LAYOUT, 1, true, NSUB, NI>(s_x + 128 * (b + u - b0), stride, wr[u],
+                                                         acc, c, g, par);
               }
-              mma_block<DT, LAYOUT, 1, true, NSUB>(s_x + 128 * (b + u - b0), stride, wr[u], acc, c,
-                                                   g, par);
+            }
+          }
+        } else {
+          // ring of kSplitkRing register sets: block b + kSplitkRing - 1 is
+          // requested while block b is computed (loads past the chunk are
+          // masked); block b0 + i into wr[slot], `first` = i is even
+          auto load_i = [&](int i, int slot, bool first) {
+            if (first)
+              load_wblk<LAYOUT, NSUB, SC_PAIR_FIRST>(wx, ws, 128 * (b0 + i), kend, g, wr[slot]);
+            else
+              load_wblk<LAYOUT, NSUB, SC_PAIR_SECOND>(wx, ws, 128 * (b0 + i), kend, g, wr[slot]);
+          };
+#pragma unroll
+          for (int i = 0; i < kSplitkRing - 1; ++i) load_i(i, i, i % 2 == 0);
+          for (int b = b0; b < b1; b += kSplitkRing) {
+#pragma unroll
+            for (int u = 0; u < kSplitkRing; ++u) {
+              // the second block of a pair reads its scales from the first
+              // block's registers, so the load that refills that slot (the
+              // next pair's first block) is issued after it
+              if (u % 2 == 0)
+                load_i(b - b0 + u + kSplitkRing - 1, (u + kSplitkRing - 1) % kSplitkRing, false);
+              if (b + u < b1)
+                mma_block2<DT, LAYOUT, 1, NSUB, NI>(s_x + 128 * (b + u - b0), stride, wr[u],
+                                                    wr[u & ~1], u % 2, acc, c, g, par);
+              if (u % 2 == 1)
+                load_i(b - b0 + u + kSplitkRing - 1, (u + kSplitkRing - 1) % kSplitkRing, true);
             }
           }
         }
-      } else {
-        // ring of kSplitkRing register sets: block b + kSplitkRing - 1 is
-        // requested while block b is computed (loads past the chunk are
-        // masked); block b0 + i into wr[slot], `first` = i is even
-        auto load_i = [&](int i, int slot, bool first) {
-          if (first)
-            load_wblk<LAYOUT, NSUB, SC_PAIR_FIRST>(wx, ws, 128 * (b0 + i), kend, g, wr[slot]);
-          else
-            load_wblk<LAYOUT, NSUB, SC_PAIR_SECOND>(wx, ws, 128 * (b0 + i), kend, g, wr[slot]);
-        };
+        // FP32 partials of valid rows: lane (c, g) element i holds route
+        // rts[i], weight row wrow[s]
 #pragma unroll
-        for (int i = 0; i < kSplitkRing - 1; ++i) load_i(i, i, i % 2 == 0);
-        for (int b = b0; b < b1; b += kSplitkRing) {
+        for (int i = 0; i < NI; ++i) {
+          if (rts[i] < 0) continue;
+          float* prow = p.part + (static_cast<int64_t>(kc) * p.R + rts[i]) * p.n_cols;
 #pragma unroll
-          for (int u = 0; u < kSplitkRing; ++u) {
-            // the second block of a pair reads its scales from the first
-            // block's registers, so the load that refills that slot (the
-            // next pair's first block) is issued after it
-            if (u % 2 == 0)
-              load_i(b - b0 + u + kSplitkRing - 1, (u + kSplitkRing - 1) % kSplitkRing, false);
-            if (b + u < b1)
-              mma_block2<DT, LAYOUT, 1, NSUB>(s_x + 128 * (b + u - b0), stride, wr[u], wr[u & ~1],
-                                              u % 2, acc, c, g, par);
-            if (u % 2 == 1)
-              load_i(b - b0 + u + kSplitkRing - 1, (u + kSplitkRing - 1) % kSplitkRing, true);
-          }
+          for (int s = 0; s < NSUB; ++s)
+            if (on[s]) prow[wrow[s]] = 16.0f * acc[0][s][i];
         }
       }
-      // FP32 partials of valid rows: lane (c, g) holds rows 4g + i, row wrow[s]
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (rts[i] < 0) continue;
-        float* prow = p.part + (static_cast<int64_t>(kc) * p.R + rts[i]) * p.n_cols;
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s)
-          if (on[s]) prow[wrow[s]] = 16.0f * acc[0][s][i];
-      }
-    }
+    };
+    if (row4) stream(std::integral_constant<int, 1>{});
+    else stream(std::integral_constant<int, 4>{});
   }
 }
 
