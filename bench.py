@@ -283,13 +283,13 @@ XCDS = 8
 GPU_CLOCK_GHZ = 2.4
 
 
-def summarize_sq(args, sweep):
-    """A text table per kernel and token count from the counter CSV of a
+def counter_agg(path, args, sweep):
+    """{(T, kernel): {"n", "ns", "c": {counter: sum}}} from the counter CSV of a
     --counter-pass run (launches in sweep order, --steps per T)."""
     import csv
     import re
 
-    with open(args.summarize_sq) as f:
+    with open(path) as f:
         rows = list(csv.DictReader(f))
     by_disp = {}
     for r in rows:
@@ -300,7 +300,8 @@ def summarize_sq(args, sweep):
     # dispatches come in sweep order: each forward launches the same kernel
     # sequence for a T, --steps times
     def short(k):
-        return re.sub(r"\(w4moe::\w+\)$", "", k.replace("void w4moe::", ""))
+        k = k.replace("void w4moe::", "").replace("w4moe::", "")
+        return re.sub(r"\([\w ,:*&]*\)$", "", k)
 
     # split into forwards: the first kernel of a forward is route preparation
     # (grouped path) or small_h_kernel (small batch); a chunked preparation
@@ -311,7 +312,6 @@ def summarize_sq(args, sweep):
     fwd = [disp[a:b] for a, b in zip(starts, starts[1:] + [len(disp)])]
     if len(fwd) != args.steps * len(sweep):
         raise SystemExit(f"{len(fwd)} forwards in the counter file, expected {args.steps} x {len(sweep)}")
-    lines = []
     agg = {}
     for ti, T in enumerate(sweep):
         for f in fwd[ti * args.steps:(ti + 1) * args.steps]:
@@ -321,6 +321,14 @@ def summarize_sq(args, sweep):
                 a["ns"] += d["ns"]
                 for k, v in d["c"].items():
                     a["c"][k] = a["c"].get(k, 0.0) + v
+    return agg
+
+
+def summarize_sq(args, sweep):
+    """A text table per kernel and token count from the counter CSV of a
+    --counter-pass run (launches in sweep order, --steps per T)."""
+    agg = counter_agg(args.summarize_sq, args, sweep)
+    lines = []
     hdr = ("T", "kernel", "us/launch", "MFMA busy %", "MFMA TFLOP/s counted", "frac of 2.5 PF",
            "VALU insts", "MFMA insts", "VALU:MFMA", "LDS insts", "LDS bank-conflict cycles")
     lines.append(" | ".join(hdr))
@@ -339,6 +347,45 @@ def summarize_sq(args, sweep):
                                  f"{mfma:.3e}", f"{valu / mfma:.2f}" if mfma else "-",
                                  f"{c.get('SQ_INSTS_LDS', 0.0):.3e}",
                                  f"{c.get('SQ_LDS_BANK_CONFLICT', 0.0):.3e}"]))
+    print("\n".join(lines))
+
+
+# Stall and latency counters, one rocprofv3 --pmc pass each (STALL_PASSES).
+# VmemLatency and LdsLatency are rocprofv3's derived cycles per vector-memory
+# (LDS) instruction in flight; the SQ_WAIT_* / SQ_ACTIVE_* counters are
+# wave-cycles, divided here by SQ_WAVE_CYCLES (the share of a wave's life).
+STALL_PASSES = (
+    ("VmemLatency",),
+    ("LdsLatency",),
+    ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
+     "SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS"),
+    ("MemUnitStalled", "TCP_TCC_READ_REQ_LATENCY_sum", "TCP_TCC_READ_REQ_sum"),
+)
+
+
+def summarize_stalls(args, sweep):
+    """A text table of STALL_PASSES per kernel and token count from the
+    counter CSVs of one --counter-pass run per pass (comma list, pass order)."""
+    merged = {}
+    for path in args.summarize_stalls.split(","):
+        for key, a in counter_agg(path, args, sweep).items():
+            m = merged.setdefault(key, {"n": a["n"], "ns": a["ns"], "c": {}})
+            for k, v in a["c"].items():
+                m["c"][k] = v / a["n"]
+    lines = [" | ".join(("T", "kernel", "us/launch", "VMEM latency cyc", "LDS latency cyc",
+                         "TA stalled %", "L1->L2 read latency cyc", "waiting %", "waiting to issue %",
+                         "issuing %", "VALU issuing %"))]
+    for (T, k), m in merged.items():
+        c = m["c"]
+        wc = c.get("SQ_WAVE_CYCLES", 0.0)
+        pct = (lambda x: f"{100.0 * c.get(x, 0.0) / wc:.0f}") if wc else (lambda x: "-")
+        rq = c.get("TCP_TCC_READ_REQ_sum", 0.0)
+        lat = f"{c.get('TCP_TCC_READ_REQ_LATENCY_sum', 0.0) / rq:.0f}" if rq else "-"
+        lines.append(" | ".join([str(T), k, f"{m['ns'] / m['n'] / 1e3:.1f}",
+                                 f"{c.get('VmemLatency', 0.0):.0f}", f"{c.get('LdsLatency', 0.0):.0f}",
+                                 f"{c.get('MemUnitStalled', 0.0):.1f}", lat, pct("SQ_WAIT_ANY"),
+                                 pct("SQ_WAIT_INST_ANY"), pct("SQ_ACTIVE_INST_ANY"),
+                                 pct("SQ_ACTIVE_INST_VALU")]))
     print("\n".join(lines))
 
 
@@ -397,6 +444,9 @@ def main():
                          "a --counter-pass run under rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE")
     ap.add_argument("--summarize-sq", metavar="CSV",
                     help="print a table of the SQ counters (SQ_SET) of a --counter-pass run")
+    ap.add_argument("--summarize-stalls", metavar="CSVS",
+                    help="print a table of the stall counters (STALL_PASSES) from one "
+                         "--counter-pass run per pass (comma list of their CSVs, in pass order)")
     ap.add_argument("--summarize-trace", metavar="CSV",
                     help="print a table of the library's kernels from a rocprofv3 "
                          "--kernel-trace --stats kernel_stats.csv")
@@ -420,13 +470,15 @@ def main():
 
     from w4a16_mixture_experts_amd import binding, synth
 
-    if args.summarize_counters or args.summarize_sq:
+    if args.summarize_counters or args.summarize_sq or args.summarize_stalls:
         sweep = [int(t) for t in args.tokens.split(",")] if args.tokens else \
             list(synth.WORKLOADS[args.workload].tokens)
         if args.summarize_counters:
             summarize_counters(args, sweep)
-        else:
+        elif args.summarize_sq:
             summarize_sq(args, sweep)
+        else:
+            summarize_stalls(args, sweep)
         return
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.lib()  # fail loudly if the HIP library is missing
