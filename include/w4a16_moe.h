@@ -136,6 +136,12 @@ typedef struct {
                                  not with the opted-in fp16 down route).  Same
                                  bits either way; the fused mode is slower on
                                  MI355X (one L2 write-back per workgroup).      */
+  int32_t force_tile_order;   /* grouped path: 0 = choose from the expected
+                                 routes per expert, 1 = tiles in route order, 2 =
+                                 the tile launches (streaming gate/up, down)
+                                 take tiles by descending count of non-empty
+                                 16-row subtiles, written by route preparation.
+                                 Same bits either way.                           */
 } w4a16_moe_desc_t;
 
 /* Variant the library runs for a descriptor (for tests and reports). */
@@ -164,6 +170,7 @@ typedef struct {
                                  launch's rerun_flags_up flags, then the down
                                  launch's rerun_flags_down (0 if neither launch
                                  exists)                                         */
+  int32_t tile_order;         /* 1: the tile launches take tiles biggest first   */
 } w4a16_moe_plan_t;
 
 /* Bytes of device workspace w4a16_moe_forward needs for this descriptor

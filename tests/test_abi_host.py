@@ -9,6 +9,7 @@ import pytest
 import torch
 
 from w4a16_mixture_experts_amd import binding as B
+from w4a16_mixture_experts_amd import synth as S
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
                       "w4a16_moe.h")
@@ -371,3 +372,13 @@ def test_repack_per_channel_argument_errors():
     assert L.w4a16_repack_per_channel(p, p, -1, 64, 128, p, p, None) == 1
     # no experts: nothing enqueued, OK with null pointers
     assert L.w4a16_repack_per_channel(None, None, 0, 64, 128, None, None, None) == 0
+
+
+def test_tile_order_chosen_between_12_and_128_routes_per_expert():
+    """The grouped path takes tiles biggest first where tile sizes mix."""
+    wl = S.WORKLOADS["kimi_tp8"]
+    for T, want in ((256, 0), (1024, 1), (2048, 1)):
+        assert B.get_plan(B.desc_for(wl, T)).tile_order == want, T
+    assert B.get_plan(B.desc_for(wl, 8)).tile_order == 0   # small batch
+    # 192 routes per expert: mostly full tiles
+    assert B.get_plan(B.desc_for(S.WORKLOADS["relu2_skew"], 4096)).tile_order == 0

@@ -28,7 +28,7 @@ class MoeDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_tokens", "hidden", "intermediate", "num_local_experts", "expert_offset", "top_k",
         "group_size", "dtype", "act", "qlayout", "force_path", "force_block_m", "force_splitk",
-        "num_global_experts", "fp16_route", "fused_finalize")]
+        "num_global_experts", "fp16_route", "fused_finalize", "force_tile_order")]
 
 
 class MoePlan(ctypes.Structure):
@@ -37,7 +37,8 @@ class MoePlan(ctypes.Structure):
                 ("max_positions", ctypes.c_int64), ("max_tiles", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_size_t), ("fp16_route", ctypes.c_int32),
                 ("rerun_flags_up", ctypes.c_int32), ("rerun_flags_down", ctypes.c_int32),
-                ("fused_combine", ctypes.c_int32), ("rerun_flags_offset", ctypes.c_size_t)]
+                ("fused_combine", ctypes.c_int32), ("rerun_flags_offset", ctypes.c_size_t),
+                ("tile_order", ctypes.c_int32)]
 
 
 class W4A16Error(RuntimeError):
@@ -123,19 +124,21 @@ def make_desc(*, num_tokens: int, hidden: int, intermediate: int, num_local_expe
               force_path: int = 0,
               force_block_m: int = 0, force_splitk: int = 0,
               num_global_experts: int = 0, fp16_route: int = 0,
-              fused_finalize: int = 0) -> MoeDesc:
+              fused_finalize: int = 0, force_tile_order: int = 0) -> MoeDesc:
     """force_path: 0 auto, 1 grouped, 2 small batch; force_block_m: 0 or 64;
     force_splitk: 0 auto, 1 split-K gate/up, 2 streaming gate/up (64-row tiles);
     num_global_experts: experts the routes are drawn over (0 = num_local_experts),
     used only to choose the variant; fp16_route: 1 opts in to the fp16 route
     (bf16 only; rows of activations all below about 2^-14 keep fewer bits);
-    fused_finalize: 1 runs the combine inside the down GEMM launch (grouped path)."""
+    fused_finalize: 1 runs the combine inside the down GEMM launch (grouped path);
+    force_tile_order: grouped path, 0 auto, 1 tiles in route order, 2 biggest first."""
     return MoeDesc(num_tokens, hidden, intermediate, num_local_experts, expert_offset, top_k,
                    group_size, DT_FP16 if dtype == torch.float16 else DT_BF16,
                    ACT_SILU_GATED if gated else ACT_RELU2,
                    Q_PER_CHANNEL if per_channel else (Q_FP4_GROUP_K if fp4 else Q_GROUP_K),
                    force_path, force_block_m,
-                   force_splitk, num_global_experts, fp16_route, fused_finalize)
+                   force_splitk, num_global_experts, fp16_route, fused_finalize,
+                   force_tile_order)
 
 
 def workspace_size(desc: MoeDesc) -> int:
@@ -165,6 +168,7 @@ def moe_forward(x, w13_packed, w13_scales, w2_packed, w2_scales, topk_ids, topk_
                 workspace=None,
                 force_path: int = 0, force_block_m: int = 0, force_splitk: int = 0,
                 num_global_experts: int = 0, fp16_route: int = 0, fused_finalize: int = 0,
+                force_tile_order: int = 0,
                 stream=None, stage_events=None, no_alloc: bool = False) -> torch.Tensor:
     """Local W4A16 MoE forward: returns out [T, H] in x's dtype.
 
@@ -206,7 +210,7 @@ def moe_forward(x, w13_packed, w13_scales, w2_packed, w2_scales, topk_ids, topk_
                      gated=gated, per_channel=per_channel, fp4=fp4, force_path=force_path,
                      force_block_m=force_block_m, force_splitk=force_splitk,
                      num_global_experts=num_global_experts, fp16_route=fp16_route,
-                     fused_finalize=fused_finalize)
+                     fused_finalize=fused_finalize, force_tile_order=force_tile_order)
     nbytes = workspace_size(desc)
     if out is None:
         out = torch.empty(T, H, dtype=x.dtype, device=dev)
@@ -322,7 +326,8 @@ def moe_forward_routed(x, w13_packed, w13_scales, w2_packed, w2_scales, router_l
                        fp4: bool = False,
                        renormalize: bool = False, out=None, workspace=None, ids_out=None,
                        force_path: int = 0, force_splitk: int = 0, fp16_route: int = 0,
-                       fused_finalize: int = 0, stream=None, stage_events=None):
+                       fused_finalize: int = 0, force_tile_order: int = 0, stream=None,
+                       stage_events=None):
     """Forward with the router fused in: returns (out [T, H], topk_ids [T, K],
     topk_weights [T, K]); router_logits [T, E_global] fp32 (E_global is their
     width)."""
@@ -352,7 +357,8 @@ def moe_forward_routed(x, w13_packed, w13_scales, w2_packed, w2_scales, router_l
                      expert_offset=expert_offset, dtype=x.dtype, gated=gated,
                      per_channel=per_channel, fp4=fp4, force_path=force_path,
                      force_splitk=force_splitk,
-                     num_global_experts=Eg, fp16_route=fp16_route, fused_finalize=fused_finalize)
+                     num_global_experts=Eg, fp16_route=fp16_route, fused_finalize=fused_finalize,
+                     force_tile_order=force_tile_order)
     nbytes = workspace_size(desc)
     if out is None:
         out = torch.empty(T, H, dtype=x.dtype, device=dev)

@@ -54,7 +54,9 @@ struct Plan {
   bool x16_down = false;  // so does the resident down GEMM
   int64_t n_redo_up = 0, n_redo_down = 0;  // rerun flags of those launches
   bool fused_fin = false;  // the combine runs inside the down launch
+  bool tile_sort = false;  // tile launches take tiles biggest first (tile order)
   size_t off_counts = 0, off_offsets = 0, off_slot = 0, off_sorted = 0, off_tile = 0,
+         off_order = 0,
          off_act = 0, off_y = 0, off_part = 0, off_chunks = 0, off_redo = 0, off_fin = 0,
          total = 0;
 };
@@ -93,6 +95,9 @@ w4a16_status_t check_desc(const w4a16_moe_desc_t* d) {
     return fail(W4A16_ERR_INVALID_ARG, "desc.force_block_m: %d (0 or 64)", d->force_block_m);
   if (d->force_path < 0 || d->force_path > 2)
     return fail(W4A16_ERR_INVALID_ARG, "desc.force_path: %d (0, 1 or 2)", d->force_path);
+  if (d->force_tile_order < 0 || d->force_tile_order > 2)
+    return fail(W4A16_ERR_INVALID_ARG, "desc.force_tile_order: %d (0, 1 or 2)",
+                d->force_tile_order);
   if (d->force_splitk < 0 || d->force_splitk > 2)
     return fail(W4A16_ERR_INVALID_ARG, "desc.force_splitk: %d (0, 1 or 2)", d->force_splitk);
   if (d->fp16_route != 0 && d->fp16_route != 1)
@@ -237,6 +242,22 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
     pl.x16 = routes_per_touched_expert(d, pl.R, true) >= 16.0;
   }
   pl.down_resident = I <= w4moe::kResidentK;
+  // Tile order: with many routes per expert the tiles differ in size (two to
+  // four non-empty subtiles around 43 routes per expert, a full tile and a
+  // tail around 64), and workgroups taken in route order leave the last ones
+  // on each CU at random sizes (the SQ busy counters of the Kimi shard's
+  // gate/up at 2048 tokens: shader engines idle 17 % of the launch); the
+  // biggest tiles first end the launch sooner.  It costs each workgroup one
+  // more round trip before its loads.  Measured, forward: the Kimi shard 510
+  // -> 495 us at 2048 tokens, 361 -> 358 at 1024, 281 -> 283 at 256; the
+  // 32-of-256 share 461 -> 423 at 2048, 231 -> 227 at 512; the skewed ReLU^2
+  // model (mostly full tiles) 1035 -> 1055 at 4096 tokens, 355 -> 357 at 1024.
+  if (pl.path == 1 && pl.R > 0) {
+    const double rpe = routes_per_touched_expert(d, pl.R, true);
+    pl.tile_sort = rpe >= w4moe::kTileSortMinRoutes && rpe <= w4moe::kTileSortMaxRoutes;
+    if (d->force_tile_order == 1) pl.tile_sort = false;
+    if (d->force_tile_order == 2) pl.tile_sort = true;
+  }
   // The down GEMM takes the fp16 route under the same condition (measured on
   // the Kimi shard's resident kernel: 167 -> 148 us at 2048 tokens; tiles of
   // one subtile were slower on it).
@@ -280,6 +301,7 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
     pl.off_slot = take(sizeof(int32_t) * std::max<int64_t>(pl.R, 1));
     pl.off_sorted = take(sizeof(int32_t) * std::max<int64_t>(pl.P, 1));
     pl.off_tile = take(sizeof(int32_t) * std::max<int64_t>(pl.MT, 1));
+    if (pl.tile_sort) pl.off_order = take(sizeof(int32_t) * std::max<int64_t>(pl.MT, 1));
     pl.off_act = take(sizeof(uint16_t) * pl.P * I);
     pl.off_y = take(sizeof(uint16_t) * std::max<int64_t>(pl.R, 1) * H);  // Y rows by route
     if (pl.splitk_S > 0)
@@ -385,6 +407,7 @@ w4a16_status_t w4a16_moe_get_plan(const w4a16_moe_desc_t* desc, w4a16_moe_plan_t
   plan->rerun_flags_down = dn16 ? static_cast<int32_t>(pl.n_redo_down) : 0;
   plan->rerun_flags_offset = (up16 || dn16) ? pl.off_redo : 0;
   plan->fused_combine = pl.fused_fin ? 1 : 0;
+  plan->tile_order = pl.tile_sort ? 1 : 0;
   return W4A16_OK;
 }
 
@@ -465,6 +488,7 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
   auto* slot = reinterpret_cast<int32_t*>(ws + pl.off_slot);
   auto* sorted = reinterpret_cast<int32_t*>(ws + pl.off_sorted);
   auto* tile = reinterpret_cast<int32_t*>(ws + pl.off_tile);
+  auto* order = pl.tile_sort ? reinterpret_cast<int32_t*>(ws + pl.off_order) : nullptr;
   auto* act = reinterpret_cast<uint16_t*>(ws + pl.off_act);
   auto* ybuf = reinterpret_cast<uint16_t*>(ws + pl.off_y);
 
@@ -548,7 +572,8 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
                                            slot, tile,
                                            reinterpret_cast<int32_t*>(ws + pl.off_chunks), stream,
                                            K, route, fin_cnt,
-                                           static_cast<int64_t>(desc->num_tokens) * pl.n_tiles_down),
+                                           static_cast<int64_t>(desc->num_tokens) * pl.n_tiles_down,
+                                           order),
                   route != nullptr ? "routing and route preparation launch"
                                    : "route preparation launch");
   if (st == W4A16_OK) st = hip_status(evs.mark(1), "stage event");
@@ -572,6 +597,7 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
     up.n_cols = I;
     up.up_rows = I;
     up.tile_expert = tile;
+    up.tile_order = pl.splitk_S > 0 ? nullptr : order;  // split-K: tiles of similar size
     up.tiles = static_cast<int>(pl.MT);
     up.offsets = offsets;
     up.E = E;
@@ -619,6 +645,7 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
   dn.n_cols = H;
   dn.up_rows = 0;
   dn.tile_expert = tile;
+  dn.tile_order = order;
   dn.tiles = static_cast<int>(pl.MT);
   dn.offsets = offsets;
   dn.E = E;

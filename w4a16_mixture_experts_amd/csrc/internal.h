@@ -28,6 +28,9 @@ struct GemmParams {
   int n_cols;                 // logical output columns (I for gated UP)
   int up_rows;                // gated: row offset of the up weights (= I)
   const int32_t* tile_expert; // [max tiles]
+  // null, or the used tiles by descending count of non-empty 16-row
+  // subtiles: workgroups take tile_order[position] instead of the position
+  const int32_t* tile_order;
   const int32_t* offsets;     // [E+1]; offsets[E] = padded total
   int E;
   int bm;
@@ -158,10 +161,15 @@ hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, 
                              int32_t* offsets, int32_t* sorted, int32_t* slot,
                              int32_t* tile_expert, int32_t* chunk_hist, hipStream_t stream,
                              int top_k = 1, const RouteArgs* route = nullptr,
-                             int32_t* zero = nullptr, int64_t n_zero = 0);
+                             int32_t* zero = nullptr, int64_t n_zero = 0,
+                             int32_t* tile_order = nullptr);
 
 // 64-row expert tiles (route positions), LDS-staged activations
 constexpr int kResidentK = 256;      // reduction the resident down kernel holds in LDS
+// tile launches take tiles biggest first between these expected valid routes
+// per touched expert (tiles of mixed sizes; far above, most tiles are full)
+constexpr double kTileSortMinRoutes = 12.0;
+constexpr double kTileSortMaxRoutes = 128.0;
 constexpr int kSplitkNsub = 2;       // 16-row weight subtiles per wave in the split-K kernel
 constexpr int kSplitkPassRows = kTileWaves * 16 * kSplitkNsub;  // weight rows per column pass
 constexpr int kSplitkMaxLds = 78 * 1024;   // two workgroups per CU

@@ -14,6 +14,8 @@
 //   slot[r]         p of route r, or -1 for an invalid route
 //   tile_expert[i]  expert of tile i (positions [i*block_m, (i+1)*block_m));
 //                   skipped when the pointer is null
+//   tile_order[k]   optional: the used tiles by descending count of non-empty
+//                   block_m/4-row subtiles, ties in tile order
 //
 // A stable counting sort without atomics.  Up to kRpOneRoutes routes: one
 // workgroup (rp_one_kernel; beyond that, the scattered stores of `sorted`
@@ -86,6 +88,78 @@ __device__ __forceinline__ void fill_padding_and_tiles(int eb, int ee, int bm,
   }
 }
 
+// tile_order (optional): the used 64-row tiles by descending count of
+// non-empty 16-row subtiles (4, 3, 2, 1), ties in tile order: a stable
+// counting sort over four buckets.  An expert of n routes has n / 64 full
+// tiles and, if n % 64 > 0, a last tile of ceil((n % 64) / 16) subtiles; the
+// four per-expert bucket counts are scanned over the experts (thread e:
+// expert e, E <= 1024), and each workgroup writes the entries of the tiles of
+// experts [eb, ee).  All threads of the workgroup call it (it has barriers).
+// The tile kernels take tiles in this order, so the last workgroups to start
+// on a CU are the shortest.
+__device__ __forceinline__ void write_tile_order(int E, int bm, const int32_t* s_off,
+                                                 const int32_t* s_cnt, int eb, int ee,
+                                                 int32_t* tile_order, int32_t (*s_tot)[16]) {
+  constexpr int kW = kRpScanThreads / 64;
+  static_assert(kW <= 16, "wave totals");
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int sub = bm / 4;  // rows per subtile (16 for 64-row tiles)
+  int n[4] = {0, 0, 0, 0};
+  int full = 0, part_b = -1;
+  if (tid < E) {
+    const int cnt = s_cnt[tid];
+    full = cnt / bm;
+    const int rem = cnt - full * bm;
+    n[0] = full;
+    if (rem > 0) {
+      part_b = 4 - (rem + sub - 1) / sub;
+      n[part_b] += 1;
+    }
+  }
+  int incl[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    incl[b] = n[b];
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl[b], d, 64);
+      if (lane >= d) incl[b] += v;
+    }
+    if (lane == 63) s_tot[b][w] = incl[b];
+  }
+  __syncthreads();
+  if (w == 0) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      int t = (lane < kW) ? s_tot[b][lane] : 0;
+      for (int d = 1; d < kW; d <<= 1) {
+        const int v = __shfl_up(t, d, 64);
+        if (lane >= d) t += v;
+      }
+      if (lane < kW) s_tot[b][lane] = t;  // inclusive over the waves
+    }
+  }
+  __syncthreads();
+  if (tid >= eb && tid < ee) {
+    int start[4];
+    start[0] = 0;
+#pragma unroll
+    for (int b = 1; b < 4; ++b) start[b] = start[b - 1] + s_tot[b - 1][kW - 1];
+    int ex[4];  // tiles of each bucket before expert tid
+#pragma unroll
+    for (int b = 0; b < 4; ++b) ex[b] = incl[b] - n[b] + (w > 0 ? s_tot[b][w - 1] : 0);
+    const int t0 = s_off[tid] / bm;
+    for (int j = 0; j < full; ++j) tile_order[start[0] + ex[0] + j] = t0 + j;
+    if (part_b >= 0) {
+      const int pb = part_b == 0 ? full : 0;  // after the expert's full tiles in bucket 0
+      int sb = 0, eb2 = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        if (b == part_b) sb = start[b], eb2 = ex[b];
+      tile_order[sb + eb2 + pb] = t0 + full;
+    }
+  }
+}
+
 }  // namespace
 
 // Up to kRpOneRoutes routes: the whole preparation in one workgroup.  Wave w
@@ -107,7 +181,7 @@ rp_one_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm,
               int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
               int32_t* __restrict__ sorted, int32_t* __restrict__ slot,
               int32_t* __restrict__ tile_expert, int top_k, RouteArgs ra,
-              int32_t* __restrict__ zero, int64_t n_zero) {
+              int32_t* __restrict__ zero, int64_t n_zero, int32_t* __restrict__ tile_order) {
   constexpr int kW = kRpScanThreads / 64;
   for (int64_t i = threadIdx.x; i < n_zero; i += kRpScanThreads) zero[i] = 0;
   __shared__ int32_t hist[kW][kRpMaxExperts];
@@ -216,6 +290,10 @@ rp_one_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm,
     }
   }
   fill_padding_and_tiles(0, E, bm, s_off, s_cnt, sorted, tile_expert, kW);
+  if (tile_order != nullptr) {
+    __shared__ int32_t s_tot[4][16];
+    write_tile_order(E, bm, s_off, s_cnt, 0, E, tile_order, s_tot);
+  }
 }
 
 __global__ void __launch_bounds__(kRpThreads)
@@ -321,7 +399,8 @@ __global__ void __launch_bounds__(kRpScanThreads)
 rp_scatter_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm, int chunk,
                   int n_chunks, const int32_t* chunk_hist, int32_t* counts,
                   int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
-                  int32_t* __restrict__ slot, int32_t* __restrict__ tile_expert) {
+                  int32_t* __restrict__ slot, int32_t* __restrict__ tile_expert,
+                  int32_t* __restrict__ tile_order) {
   constexpr int kW = kRpScanThreads / 64;
   __shared__ int32_t wave_tot[kW];
   __shared__ int32_t s_off[kRpMaxExperts + 1];
@@ -401,6 +480,10 @@ rp_scatter_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm
   const int per_wg = (E + n_chunks - 1) / n_chunks;
   const int eb = min(E, c * per_wg);
   fill_padding_and_tiles(eb, min(E, eb + per_wg), bm, s_off, s_cnt, sorted, tile_expert, kW);
+  if (tile_order != nullptr) {
+    __shared__ int32_t s_tot[4][16];
+    write_tile_order(E, bm, s_off, s_cnt, eb, min(E, eb + per_wg), tile_order, s_tot);
+  }
 }
 
 int route_prep_chunk(int R) {
@@ -419,8 +502,10 @@ constexpr int kRpRouteMaxTokens = kRpScanThreads / 64;
 hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, int32_t* counts,
                              int32_t* offsets, int32_t* sorted, int32_t* slot,
                              int32_t* tile_expert, int32_t* chunk_hist, hipStream_t stream,
-                             int top_k, const RouteArgs* route, int32_t* zero, int64_t n_zero) {
+                             int top_k, const RouteArgs* route, int32_t* zero, int64_t n_zero,
+                             int32_t* tile_order) {
   if (E < 1 || E > kRpMaxExperts || R < 0) return hipErrorInvalidValue;
+  if (tile_order != nullptr && bm % 4 != 0) return hipErrorInvalidValue;
   if (zero == nullptr) n_zero = 0;
   // without scratch: one chunk, whose counts live in `counts` itself (the
   // scan overwrites them with the totals) and whose base is 0
@@ -443,7 +528,7 @@ hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, 
         default: break;
       }
       hipLaunchKernelGGL(k, dim3(1), dim3(kRpScanThreads), 0, stream, ids, R, E, off, bm, counts,
-                         offsets, sorted, slot, tile_expert, top_k, ra, zero, n_zero);
+                         offsets, sorted, slot, tile_expert, top_k, ra, zero, n_zero, tile_order);
       return hipGetLastError();
     }
     const hipError_t err = launch_router_topk(ra.logits, ra.T, ra.Eg, top_k, ra.renorm, ra.ids,
@@ -454,7 +539,7 @@ hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, 
   if (R <= kRpOneRoutes) {
     hipLaunchKernelGGL((rp_one_kernel<kRpOneMaxPieces, 0>), dim3(1), dim3(kRpScanThreads), 0,
                        stream, ids, R, E, off, bm, counts, offsets, sorted, slot, tile_expert,
-                       top_k, RouteArgs{}, zero, n_zero);
+                       top_k, RouteArgs{}, zero, n_zero, tile_order);
     return hipGetLastError();
   }
   // R > kRpOneRoutes here, so there is at least one chunk
@@ -464,7 +549,7 @@ hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, 
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(rp_scatter_kernel, dim3(n_chunks), dim3(kRpScanThreads), 0, stream, ids, R,
                      E, off, bm, chunk, n_chunks, hist, counts, offsets, sorted, slot,
-                     tile_expert);
+                     tile_expert, tile_order);
   return hipGetLastError();
 }
 

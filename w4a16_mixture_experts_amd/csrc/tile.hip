@@ -603,6 +603,28 @@ __device__ __forceinline__ void wave_columns(const GemmParams& p, int nt, int w,
   }
 }
 
+// Workgroup L's place in the tile order and its column tile: workgroup L
+// runs on XCD L % 8, XCD x takes positions x, x + 8, ... and walks the column
+// tiles of each back to back (a tile's activation rows are then read through
+// one L2).
+__device__ __forceinline__ int tile_position(const GemmParams& p, int L, int& nt) {
+  const int q = L / kXcds;
+  nt = q % p.n_tiles;
+  return kXcds * (q / p.n_tiles) + L % kXcds;
+}
+
+// The tile at position k: tile_order[k] with a tile order (the used tiles,
+// biggest first), else k; -1 for a position past the used tiles (tile order
+// only: one round trip for the padded total and the entry).  Without an
+// order a position past the used tiles is found later, from its row base.
+__device__ __forceinline__ int tile_at(const GemmParams& p, int k) {
+  if (p.tile_order == nullptr) return k;
+  const int total = p.offsets[p.E];
+  const int o = p.tile_order[min(k, p.tiles - 1)];
+  asm volatile("" : : "s"(total), "s"(o));  // both loads in flight together
+  return k * kTileRows < total ? o : -1;
+}
+
 // Active 16-row subtiles of a tile: valid routes come first, so they are a
 // prefix (uniform).
 __device__ __forceinline__ int active_subtiles(const GemmParams& p, int row_base) {
@@ -861,11 +883,9 @@ __device__ __forceinline__ bool tile_run(const GemmParams& p, const int row_base
 // the exact fp16 route; returns false if such a tile must be rerun.
 template <int DT, int LAYOUT, int MODE, bool SCL, bool X16>
 __device__ __forceinline__ bool tile_work(const GemmParams& p, const int L, uint16_t* s_lds) {
-  // workgroup L runs on XCD L % 8; XCD x takes tiles x, x + 8, ... and walks
-  // the column tiles of each tile back to back
-  const int q = L / kXcds;
-  const int mt = kXcds * (q / p.n_tiles) + L % kXcds;
-  const int nt = q % p.n_tiles;
+  int nt;
+  const int mt = tile_at(p, tile_position(p, L, nt));
+  if (mt < 0) return true;  // whole workgroup: position past the used tiles
   const int row_base = mt * kTileRows;
   // every index the workgroup needs comes in one batch of loads before the
   // first decision (a tile past the padded total reads a clamped tile)
@@ -919,12 +939,12 @@ tile_gemm_kernel(const GemmParams p) {
   if constexpr (MODE == MODE_DOWN && !X16) {
     if (p.fin_cnt != nullptr) {
       // the workgroup's tile and column tile (as tile_work derives them)
-      const int q = L / kXcds;
-      const int mt = kXcds * (q / p.n_tiles) + L % kXcds;
-      const int nt = q % p.n_tiles;
+      int nt;
+      const int mt = tile_at(p, tile_position(p, L, nt));
       const int row_base = mt * kTileRows;
       const int c0 = nt * kTileColsPlain, c1 = min(p.n_cols, c0 + kTileColsPlain);
-      if (row_base < p.offsets[p.E] && c0 < c1) finalize_arrivals<DT>(p, row_base, nt, c0, c1);
+      if (mt >= 0 && row_base < p.offsets[p.E] && c0 < c1)
+        finalize_arrivals<DT>(p, row_base, nt, c0, c1);
     }
   }
 }
@@ -1142,9 +1162,9 @@ down_resident_kernel(const GemmParams p) {
     finalize_zero_rows(p, L - p.n_main);
     return;
   }
-  const int q = L / kXcds;
-  const int mt = kXcds * (q / p.n_tiles) + L % kXcds;
-  const int chunk = q % p.n_tiles;
+  int chunk;
+  const int mt = tile_at(p, tile_position(p, L, chunk));
+  if (mt < 0) return;  // position past the used tiles
   const int row_base = mt * kTileRows;
   // every index the workgroup needs comes in one batch of loads before the
   // first decision (see tile_gemm_kernel)
@@ -1374,9 +1394,9 @@ template <int DT, int LAYOUT, int NKB>
 __device__ __forceinline__ bool down_work_x16(const GemmParams& p, const int L, uint16_t* s_ar,
                                           uint16_t* s_out) {
   // same XCD-aware order as the streaming kernel (n_tiles = column chunks)
-  const int q = L / kXcds;
-  const int mt = kXcds * (q / p.n_tiles) + L % kXcds;
-  const int chunk = q % p.n_tiles;
+  int chunk;
+  const int mt = tile_at(p, tile_position(p, L, chunk));
+  if (mt < 0) return true;  // position past the used tiles
   const int row_base = mt * kTileRows;
   // every index the workgroup needs comes in one batch of loads before the
   // first decision (see tile_work)
@@ -1404,9 +1424,9 @@ __device__ __forceinline__ bool down_work_x16(const GemmParams& p, const int L, 
 template <int DT, int LAYOUT, int NKB>
 __device__ __forceinline__ void down_work_pg(const GemmParams& p, const int L, uint16_t* s_ar,
                                              uint16_t* s_out) {
-  const int q = L / kXcds;
-  const int mt = kXcds * (q / p.n_tiles) + L % kXcds;
-  const int chunk = q % p.n_tiles;
+  int chunk;
+  const int mt = tile_at(p, tile_position(p, L, chunk));
+  if (mt < 0) return;  // position past the used tiles
   const int row_base = mt * kTileRows;
   if (row_base >= p.offsets[p.E]) return;
   int nms = 0;
