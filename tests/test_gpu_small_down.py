@@ -6,7 +6,7 @@ of the 8 waves, and a token with no valid route, against the oracle."""
 import pytest
 import torch
 
-from moe_check import assert_close, forward, oracle_out, tokens
+from moe_check import assert_close, forward, oracle_out, tokens, weights
 from w4a16_mixture_experts_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -34,3 +34,19 @@ def test_valid_route_items(I, per_channel, valid):
     out = forward(wl, Wg, tc.to("cuda"), force_path=2)
     assert not out[3].any()
     assert_close(out, oracle_out(wl, Wc, tc), f"I={I} valid={valid}")
+
+
+@pytest.mark.parametrize("name,T", [("kimi_tp8", 7), ("kimi_tp8", 13), ("deepseek_local", 5),
+                                    ("per_channel", 11), ("tiny", 9)])
+def test_odd_token_counts_with_an_empty_token(name, T):
+    """Odd token counts, one token's routes all invalid (its output row is
+    zero and its down workgroups take no item)."""
+    wl = synth.WORKLOADS[name]
+    Wc, Wg = weights(name)
+    tc = tokens(wl, T)
+    ids = tc.topk_ids.clone()
+    ids[T // 2, :] = -1
+    tc = synth.Tokens(tc.x, ids, tc.topk_weights)
+    out = forward(wl, Wg, tc.to("cuda"), force_path=2)
+    assert not out[T // 2].any()
+    assert_close(out, oracle_out(wl, Wc, tc), f"{name} T={T} empty token")

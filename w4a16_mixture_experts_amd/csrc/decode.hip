@@ -642,9 +642,9 @@ hipError_t launch_small_h(const SmallHParams& p, int dtype, int layout, int nkb,
 
 template <int DT, int LAYOUT, bool GATED, int AL>
 static hipError_t launch_dd_k(const DecodeDownParams& p, dim3 grid, size_t lds, hipStream_t st) {
-  // items (valid routes x slices) can outnumber the waves: prefetching variant
-  const int nsl = ((p.I + 127) / 128 + kDecDownSliceBlocks - 1) / kDecDownSliceBlocks;
-  if (p.top_k * nsl > kDecWaves) {
+  // items (valid routes x slices) expected to outnumber the waves: the
+  // prefetching variant (two register sets; fewer workgroups per CU)
+  if (p.prefetch) {
     const hipError_t err = allow_lds(decode_down_kernel<DT, LAYOUT, GATED, AL, true>, lds);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((decode_down_kernel<DT, LAYOUT, GATED, AL, true>), grid, dim3(kDecThreads),

@@ -127,9 +127,12 @@ struct DecodeDownParams {
   int top_k, E, off;
   int I, H;
   uint16_t* out;              // [T][H]
+  int prefetch;               // 1: the variant that loads a wave's next item while
+                              // it computes one (more items than waves expected)
 };
 
 constexpr int kDecThreadsAll = 512;       // threads of the small-batch down kernel
+constexpr int kDecWavesAll = kDecThreadsAll / 64;
 constexpr int kDecActLoads = 8;           // activation chunks per thread: top_k * I <= 8 * 512 * 8
 inline size_t decode_down_lds_bytes(int top_k, int I) {
   // the activations [top_k][I + 8] 16-bit, then FP32 partials [items][32]
