@@ -131,54 +131,43 @@ __device__ __forceinline__ u32x4 nibbles_to_h16(uint32_t d) {
 // The magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 divided by 16 are exact in bf16
 // and fp16; the division lets the FP4 layout share the INT4 layout's final
 // factor 16 and needs no correction term.  One dword of eight codes n0..n7
-// gives the same pairs as nibbles_to_h16: (n0,n4) (n1,n5) (n2,n6) (n3,n7).
-// The 16-bit patterns of the eight magnitudes come from two byte lookups
-// (v_perm_b32 with the 3-bit magnitude codes as selectors), the sign bit is
-// moved in place.
+// (byte b: n_2b in its low nibble, n_2b+1 in its high one) gives the same
+// pairs as nibbles_to_h16: (n0,n4) (n1,n5) (n2,n6) (n3,n7).  gfx950 converts
+// the two codes of a byte in one instruction (v_cvt_scalef32_pk_*_fp4, the
+// value times an FP32 scale, here 1/16: exact); byte permutes then pair the
+// codes four apart.
 template <int DT>
-struct Fp4Lut;
+__device__ __forceinline__ uint32_t fp4_byte_to_h16(uint32_t d, int b);
 template <>
-struct Fp4Lut<DT_BF16> {
-  // bf16 of 0, 1/32, 1/16, 3/32, 1/8, 3/16, 1/4, 3/8: high and low bytes
-  static constexpr uint32_t kHi03 = 0x3D3D3D00u, kHi47 = 0x3E3E3E3Eu;
-  static constexpr uint32_t kLo03 = 0xC0800000u, kLo47 = 0xC0804000u;
-  static constexpr bool kLowBytes = true;
-};
+__device__ __forceinline__ uint32_t fp4_byte_to_h16<DT_BF16>(uint32_t d, int b) {
+  switch (b) {  // the byte select is an immediate
+    case 0: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 0.0625f, 0));
+    case 1: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 0.0625f, 1));
+    case 2: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 0.0625f, 2));
+    default: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 0.0625f, 3));
+  }
+}
 template <>
-struct Fp4Lut<DT_FP16> {
-  // fp16 of the same values: the low bytes are all zero
-  static constexpr uint32_t kHi03 = 0x2E2C2800u, kHi47 = 0x36343230u;
-  static constexpr uint32_t kLo03 = 0u, kLo47 = 0u;
-  static constexpr bool kLowBytes = false;
-};
+__device__ __forceinline__ uint32_t fp4_byte_to_h16<DT_FP16>(uint32_t d, int b) {
+  switch (b) {
+    case 0: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 0.0625f, 0));
+    case 1: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 0.0625f, 1));
+    case 2: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 0.0625f, 2));
+    default: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 0.0625f, 3));
+  }
+}
 
 template <int DT>
 __device__ __forceinline__ u32x4 e2m1_to_h16(uint32_t d) {
-  using L = Fp4Lut<DT>;
-  const uint32_t ev = d & 0x07070707u;          // magnitudes of n0 n2 n4 n6 (one per byte)
-  const uint32_t od = (d >> 4) & 0x07070707u;   // magnitudes of n1 n3 n5 n7
-  const uint32_t he = __builtin_amdgcn_perm(L::kHi47, L::kHi03, ev);
-  const uint32_t ho = __builtin_amdgcn_perm(L::kHi47, L::kHi03, od);
+  const uint32_t c0 = fp4_byte_to_h16<DT>(d, 0);  // (n0, n1)
+  const uint32_t c1 = fp4_byte_to_h16<DT>(d, 1);  // (n2, n3)
+  const uint32_t c2 = fp4_byte_to_h16<DT>(d, 2);  // (n4, n5)
+  const uint32_t c3 = fp4_byte_to_h16<DT>(d, 3);  // (n6, n7)
   u32x4 r;
-  if constexpr (L::kLowBytes) {
-    const uint32_t le = __builtin_amdgcn_perm(L::kLo47, L::kLo03, ev);
-    const uint32_t lo = __builtin_amdgcn_perm(L::kLo47, L::kLo03, od);
-    r[0] = __builtin_amdgcn_perm(he, le, 0x06020400u);   // (n0, n4)
-    r[1] = __builtin_amdgcn_perm(ho, lo, 0x06020400u);   // (n1, n5)
-    r[2] = __builtin_amdgcn_perm(he, le, 0x07030501u);   // (n2, n6)
-    r[3] = __builtin_amdgcn_perm(ho, lo, 0x07030501u);   // (n3, n7)
-  } else {
-    // the low bytes come from a zero operand
-    r[0] = __builtin_amdgcn_perm(he, 0u, 0x06020400u);
-    r[1] = __builtin_amdgcn_perm(ho, 0u, 0x06020400u);
-    r[2] = __builtin_amdgcn_perm(he, 0u, 0x07030501u);
-    r[3] = __builtin_amdgcn_perm(ho, 0u, 0x07030501u);
-  }
-  // sign of n_i (bit 4i + 3) to bit 15 or 31 of its pair
-  r[0] |= (d << 12) & 0x80008000u;
-  r[1] |= (d << 8) & 0x80008000u;
-  r[2] |= (d << 4) & 0x80008000u;
-  r[3] |= d & 0x80008000u;
+  r[0] = __builtin_amdgcn_perm(c2, c0, 0x05040100u);  // (n0, n4)
+  r[1] = __builtin_amdgcn_perm(c2, c0, 0x07060302u);  // (n1, n5)
+  r[2] = __builtin_amdgcn_perm(c3, c1, 0x05040100u);  // (n2, n6)
+  r[3] = __builtin_amdgcn_perm(c3, c1, 0x07060302u);  // (n3, n7)
   return r;
 }
 
