@@ -350,6 +350,18 @@ w4a16_status_t w4a16_repack_per_channel(const uint8_t* packed, const void* scale
 w4a16_status_t w4a16_unpack_int4(const uint8_t* packed, int64_t n_bytes, int8_t* out,
                                  w4a16_stream_t stream);
 
+/* FP4 (E2M1) decoding with the device conversion the GEMMs use ([P2]
+ * Description, "Tests": the W4A4 cases kept beside W4A16; the element format
+ * of the OCP microscaling specification): out[2i] = value of the low nibble
+ * of packed[i], out[2i+1] = of the high nibble, as FP32 (exact: 0, +-0.5,
+ * +-1, +-1.5, +-2, +-3, +-4, +-6, the sign of zero kept), the values passing
+ * through the dtype's 16-bit form (dtype W4A16_DT_BF16 or W4A16_DT_FP16).
+ * out holds 2*n_bytes floats; n_bytes = 0 enqueues nothing.  Errors:
+ * W4A16_ERR_INVALID_ARG (negative size, unknown dtype, null pointer),
+ * W4A16_ERR_UNSUPPORTED (n_bytes above 2^33). */
+w4a16_status_t w4a16_decode_fp4(const uint8_t* packed, int64_t n_bytes, int32_t dtype, float* out,
+                                w4a16_stream_t stream);
+
 /* Router scoring and top-k, the step before route preparation ([P2] Final
  * performance: routing is timed with the MoE; [P1] Benchmark: FP32 routing
  * weights, INT32 ids, no renormalization).  For each token t:

@@ -122,6 +122,13 @@ def test_prepare_routes_and_unpack_argument_errors():
     assert L.w4a16_unpack_int4(None, 16, P(0x1000), None) == 1
     assert L.w4a16_unpack_int4(P(0x1000), -1, P(0x1000), None) == 1
     assert L.w4a16_unpack_int4(None, 0, None, None) == 0
+    # FP4 decode: size, dtype and pointers checked before any launch
+    assert L.w4a16_decode_fp4(P(0x1000), -1, 0, P(0x1000), None) == 1
+    assert L.w4a16_decode_fp4(P(0x1000), 16, 7, P(0x1000), None) == 1
+    assert b"dtype" in L.w4a16_last_error_message()
+    assert L.w4a16_decode_fp4(None, 16, 0, P(0x1000), None) == 1
+    assert L.w4a16_decode_fp4(P(0x1000), 16, 1, None, None) == 1
+    assert L.w4a16_decode_fp4(None, 0, 0, None, None) == 0
 
 
 def test_plans_by_route_count():

@@ -1,10 +1,13 @@
 """GPU parity of the FP4-weight layout (E2M1 codes along K, a 16-bit scale per
 32 values; MXFP4 scales converted exactly) through the C ABI against the CPU
-oracle: the E8M0 scale conversion bit-exact, the forward within the NRMSE
+oracle: the device E2M1 decode (the GEMMs' conversion) bit-exact against the
+element format's table for every byte at every place in a dword, the E8M0
+scale conversion bit-exact, the forward within the NRMSE
 bar on every variant (small batch, streaming and split-K gate/up, resident
 and streaming down, fused finalize), ragged reductions, both 16-bit types,
 and the Kimi-shard and DeepSeek-share shapes at full size."""
 import dataclasses
+import os
 
 import numpy as np
 import pytest
@@ -15,6 +18,37 @@ from moe_check import assert_close, forward, oracle_out, tokens, weights
 from w4a16_mixture_experts_amd import binding, synth
 
 pytestmark = pytest.mark.gpu
+
+
+def _e2m1_table():
+    """The element format's 16 values (tests/golden/fp4_e2m1.txt)."""
+    tab = {}
+    with open(os.path.join(os.path.dirname(__file__), "golden", "fp4_e2m1.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                code, val = line.split()
+                tab[int(code, 16)] = np.float32(float(val))
+    assert sorted(tab) == list(range(16))
+    return tab
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("n", [1024, 1027, 3])
+def test_device_e2m1_decode_bit_exact(dtype, n):
+    """Every byte value at each of the four byte places of a dword (the
+    conversion pairs the codes of a dword four apart), a ragged tail, both
+    16-bit types: the values and the signs of zero as the table gives them."""
+    tab = _e2m1_table()
+    b = np.concatenate([np.repeat(np.arange(256, dtype=np.uint8), 4),
+                        np.array([0x8F, 0x07, 0xF8], np.uint8)])[:n]
+    got = binding.decode_fp4(torch.from_numpy(b).cuda(), dtype)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    want = np.empty(2 * n, np.float32)
+    want[0::2] = [tab[int(x) & 0xF] for x in b]
+    want[1::2] = [tab[int(x) >> 4] for x in b]
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+    np.testing.assert_array_equal(got, oracle.unpack_fp4(b))
 
 
 def test_e8m0_conversion_bit_exact():

@@ -68,6 +68,7 @@ def lib():
     L.w4a16_moe_forward_timed.argtypes = [P, P, P, P, P, P, P, P, pdesc, P, sz, P, P, i32]
     L.w4a16_moe_prepare_routes.argtypes = [pdesc, P, i32, P, P, P, i64, P, P, P]
     L.w4a16_unpack_int4.argtypes = [P, i64, P, P]
+    L.w4a16_decode_fp4.argtypes = [P, i64, i32, P, P]
     L.w4a16_moe_route_topk.argtypes = [P, i64, i32, i32, i32, P, P, P]
     L.w4a16_stream_probe.argtypes = [P, i64, i32, P, P]
     L.w4a16_moe_forward_noalloc.argtypes = [P, P, P, P, P, P, P, P, pdesc, P]
@@ -81,7 +82,7 @@ def lib():
     L.w4a16_last_error_message.restype = ctypes.c_char_p
     for f in ("w4a16_moe_workspace_size", "w4a16_moe_get_plan", "w4a16_moe_forward",
               "w4a16_moe_forward_timed",
-              "w4a16_moe_prepare_routes", "w4a16_unpack_int4", "w4a16_moe_route_topk",
+              "w4a16_moe_prepare_routes", "w4a16_unpack_int4", "w4a16_decode_fp4", "w4a16_moe_route_topk",
               "w4a16_stream_probe", "w4a16_moe_forward_noalloc", "w4a16_moe_forward_routed",
               "w4a16_moe_route_and_prepare", "w4a16_e8m0_to_scales",
               "w4a16_repack_per_channel"):
@@ -285,6 +286,17 @@ def unpack_int4(packed: torch.Tensor, stream=None) -> torch.Tensor:
     _dev("packed", packed, (torch.uint8,))
     out = torch.empty(packed.numel() * 2, dtype=torch.int8, device=packed.device)
     _check(lib().w4a16_unpack_int4(_ptr(packed), packed.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def decode_fp4(packed: torch.Tensor, dtype=torch.bfloat16, stream=None) -> torch.Tensor:
+    """E2M1 codes (two per byte, the even index in the low nibble) through the
+    GEMMs' device conversion, as float32."""
+    _dev("packed", packed, (torch.uint8,))
+    out = torch.empty(packed.numel() * 2, dtype=torch.float32, device=packed.device)
+    _check(lib().w4a16_decode_fp4(_ptr(packed), packed.numel(),
+                                  DT_FP16 if dtype == torch.float16 else DT_BF16, _ptr(out),
+                                  _stream(stream)))
     return out
 
 

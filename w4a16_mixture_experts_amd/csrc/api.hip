@@ -862,6 +862,23 @@ w4a16_status_t w4a16_unpack_int4(const uint8_t* packed, int64_t n_bytes, int8_t*
   return hip_status(w4moe::launch_unpack(packed, n_bytes, out, stream), "unpack launch");
 }
 
+w4a16_status_t w4a16_decode_fp4(const uint8_t* packed, int64_t n_bytes, int32_t dtype, float* out,
+                                w4a16_stream_t stream_) {
+  if (n_bytes < 0) return fail(W4A16_ERR_INVALID_ARG, "n_bytes: %lld < 0", (long long)n_bytes);
+  if (dtype != W4A16_DT_BF16 && dtype != W4A16_DT_FP16)
+    return fail(W4A16_ERR_INVALID_ARG, "dtype: %d (bf16 or fp16)", dtype);
+  if (n_bytes == 0) return W4A16_OK;
+  if (packed == nullptr) return fail(W4A16_ERR_INVALID_ARG, "packed: null pointer");
+  if (out == nullptr) return fail(W4A16_ERR_INVALID_ARG, "out: null pointer");
+  if (n_bytes > (int64_t(1) << 33))
+    return fail(W4A16_ERR_UNSUPPORTED, "n_bytes: %lld too large", (long long)n_bytes);
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  return hip_status(w4moe::launch_decode_fp4(packed, n_bytes, dtype == W4A16_DT_BF16 ? w4moe::DT_BF16
+                                                                                  : w4moe::DT_FP16,
+                                             out, stream),
+                    "FP4 decode launch");
+}
+
 w4a16_status_t w4a16_stream_probe(const uint8_t* buf, int64_t bytes, int32_t row_bytes,
                                   uint32_t* sink, w4a16_stream_t stream_) {
   if (row_bytes <= 0 || row_bytes % 64 != 0 || row_bytes > w4moe::kProbeMaxRowBytes)

@@ -12,6 +12,7 @@
 //   combine_kernel  out[t] = cast16(sum_k w[t,k] * Y[t*K+k]) in FP32 over the
 //                   valid routes (slot[t*K+k] >= 0).
 //   unpack_kernel   nibbles through the GEMMs' bit conversion, back to int8.
+//   decode_fp4_kernel  E2M1 codes through the GEMMs' conversion, back to FP32.
 //   e8m0_kernel     MXFP4 block scales to 16-bit scales (setup).
 //   repack_pc_kernel  per-channel INT4 into the group layout (setup).
 #include "device.h"
@@ -87,6 +88,26 @@ unpack_kernel(const uint8_t* __restrict__ in, int64_t n, int8_t* __restrict__ ou
   }
 }
 
+// Test export: FP4 (E2M1) codes through the conversion the GEMMs use (each
+// value / 16 as a 16-bit float), back to FP32 values (times 16: exact).
+// Four bytes (eight codes) per thread, in the GEMMs' pair order.
+template <int DT>
+__global__ void __launch_bounds__(256)
+decode_fp4_kernel(const uint8_t* __restrict__ in, int64_t n, float* __restrict__ out) {
+  using T = H16<DT>;
+  const int64_t b0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (b0 >= n) return;
+  const int nb = static_cast<int>(min<int64_t>(4, n - b0));
+  uint32_t d = 0;
+  for (int q = 0; q < nb; ++q) d |= static_cast<uint32_t>(in[b0 + q]) << (8 * q);
+  const u32x4 h = e2m1_to_h16<DT>(d);  // (n_j, n_j+4) in dword j
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (j < 2 * nb) out[2 * b0 + j] = 16.0f * T::to_f32(h[j] & 0xffffu);
+    if (j + 4 < 2 * nb) out[2 * b0 + j + 4] = 16.0f * T::to_f32(h[j] >> 16);
+  }
+}
+
 // MXFP4 block scales: E8M0 code e -> 2^(e - 127) as a 16-bit float (the
 // FP32 value is exact; its 16-bit rounding is exact wherever the dtype holds
 // the power of two).
@@ -145,6 +166,17 @@ hipError_t launch_combine(const CombineParams& p, int dtype, int T, hipStream_t 
     hipLaunchKernelGGL((combine_kernel<DT_BF16>), grid, dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL((combine_kernel<DT_FP16>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_fp4(const uint8_t* packed, int64_t n_bytes, int dtype, float* out,
+                             hipStream_t stream) {
+  const int64_t threads = (n_bytes + 3) / 4;
+  const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(decode_fp4_kernel<DT_BF16>, grid, dim3(256), 0, stream, packed, n_bytes, out);
+  else
+    hipLaunchKernelGGL(decode_fp4_kernel<DT_FP16>, grid, dim3(256), 0, stream, packed, n_bytes, out);
   return hipGetLastError();
 }
 

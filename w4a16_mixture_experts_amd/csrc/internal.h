@@ -202,6 +202,8 @@ hipError_t launch_decode_down(const DecodeDownParams& p, int dtype, int layout, 
 hipError_t launch_combine(const CombineParams& p, int dtype, int T, hipStream_t stream);
 
 hipError_t launch_unpack(const uint8_t* packed, int64_t n_bytes, int8_t* out, hipStream_t stream);
+hipError_t launch_decode_fp4(const uint8_t* packed, int64_t n_bytes, int dtype, float* out,
+                             hipStream_t stream);
 hipError_t launch_e8m0_to_h16(const uint8_t* e8m0, int64_t n, int dtype, uint16_t* out,
                               hipStream_t stream);
 hipError_t launch_repack_per_channel(const uint8_t* in, const uint16_t* sc_in, int64_t n_experts,
