@@ -18,8 +18,8 @@
 //                   block_m/4-row subtiles, ties in tile order
 //
 // A stable counting sort without atomics.  Up to kRpOneRoutes routes: one
-// workgroup (rp_one_kernel; beyond that, the scattered stores of `sorted`
-// are too many for one compute unit).  Otherwise two launches:
+// workgroup (rp_one_kernel), which sorts the routes in LDS and writes the
+// padded list in order.  Otherwise two launches:
 //   1. rp_rank_kernel: workgroup c takes the contiguous chunk c of routes;
 //      each of its waves walks a slab of the chunk 64 routes at a time.
 //      Lanes holding the same expert are found with one ballot per expert-id
@@ -35,6 +35,7 @@
 // Ascending order within an expert follows from chunks, slabs, 64-route
 // pieces and lanes all being in route order.
 #include <algorithm>
+#include <cstdint>
 
 #include "device.h"
 #include "internal.h"
@@ -54,6 +55,31 @@ __device__ __forceinline__ int local_expert(int32_t g, int E, int off) {
   return (e >= 0 && e < E) ? static_cast<int>(e) : -1;
 }
 
+// The wave's index in the workgroup, as a value the compiler knows is the
+// same in every lane (wave-strided loops then run on scalar counters).
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+}
+
+// Inclusive prefix sum over the lanes of a wave (kRowsOnly: over each 16-lane
+// row).  Shift-and-add steps of 1, 2, 4 and 8 lanes inside the rows through
+// DPP row shifts (a lane shifted in from outside its row reads 0); then the
+// total of rows 0 and 2 is added to rows 1 and 3 (broadcast of lanes 15 and
+// 47), and the total of rows 0-1 to rows 2-3 (broadcast of lane 31).  No LDS
+// round trip, unlike a shuffle.
+template <bool kRowsOnly = false>
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  if (!kRowsOnly) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  }
+  return x;
+}
+
 // Padding positions (-1) and the tile -> expert map of experts [eb, ee).
 // Wave w takes experts eb + [w * per, (w + 1) * per) (per <= 64: E <= 64 *
 // waves); lane j reads the
@@ -65,7 +91,7 @@ __device__ __forceinline__ void fill_padding_and_tiles(int eb, int ee, int bm,
                                                        const int32_t* s_off, const int32_t* s_cnt,
                                                        int32_t* sorted, int32_t* tile_expert,
                                                        int waves) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = wave_id();
   const int per = (ee - eb + waves - 1) / waves;
   const int e0 = eb + w * per;
   const int me = e0 + lane;
@@ -102,7 +128,7 @@ __device__ __forceinline__ void write_tile_order(int E, int bm, const int32_t* s
                                                  int32_t* tile_order, int32_t (*s_tot)[16]) {
   constexpr int kW = kRpScanThreads / 64;
   static_assert(kW <= 16, "wave totals");
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int sub = bm / 4;  // rows per subtile (16 for 64-row tiles)
   int n[4] = {0, 0, 0, 0};
   int full = 0, part_b = -1;
@@ -119,34 +145,24 @@ __device__ __forceinline__ void write_tile_order(int E, int bm, const int32_t* s
   int incl[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    incl[b] = n[b];
-    for (int d = 1; d < 64; d <<= 1) {
-      const int v = __shfl_up(incl[b], d, 64);
-      if (lane >= d) incl[b] += v;
-    }
-    if (lane == 63) s_tot[b][w] = incl[b];
-  }
-  __syncthreads();
-  if (w == 0) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      int t = (lane < kW) ? s_tot[b][lane] : 0;
-      for (int d = 1; d < kW; d <<= 1) {
-        const int v = __shfl_up(t, d, 64);
-        if (lane >= d) t += v;
-      }
-      if (lane < kW) s_tot[b][lane] = t;  // inclusive over the waves
-    }
+    incl[b] = wave_incl_scan(n[b]);
+    if (lane == 63) s_tot[b][w] = incl[b];  // per-wave totals
   }
   __syncthreads();
   if (tid >= eb && tid < ee) {
-    int start[4];
-    start[0] = 0;
+    int start[4], ex[4];  // first entry of each bucket; its tiles before expert tid
+    int run = 0;
 #pragma unroll
-    for (int b = 1; b < 4; ++b) start[b] = start[b - 1] + s_tot[b - 1][kW - 1];
-    int ex[4];  // tiles of each bucket before expert tid
+    for (int b = 0; b < 4; ++b) {
+      start[b] = run;
+      ex[b] = incl[b] - n[b];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) ex[b] = incl[b] - n[b] + (w > 0 ? s_tot[b][w - 1] : 0);
+      for (int v = 0; v < kW; ++v) {
+        const int t = s_tot[b][v];
+        run += t;
+        if (v < w) ex[b] += t;
+      }
+    }
     const int t0 = s_off[tid] / bm;
     for (int j = 0; j < full; ++j) tile_order[start[0] + ex[0] + j] = t0 + j;
     if (part_b >= 0) {
@@ -166,30 +182,43 @@ __device__ __forceinline__ void write_tile_order(int E, int bm, const int32_t* s
 // takes the contiguous slab of np 64-route pieces starting at piece w * np
 // (NP >= np, a compile-time bound) and ranks its pieces in order, its LDS
 // histogram carrying the counts of its earlier pieces; the scan over the
-// waves' histograms gives each wave's base within an expert.
+// waves' histograms gives each wave's base within an expert.  The routes are
+// then gathered into an LDS list by expert and rank, each tile records its
+// first list entry and valid rows, and the padded list is written tile by
+// tile in one pass: consecutive lanes, every position once, no per-expert
+// loop (which a wave walks serially, instruction by instruction).
 // (Measured on the 384-expert workload: beyond 1024 routes, two launches
 // over 256-route chunks are faster.)
 constexpr int kRpOneMaxPieces = 1;
 constexpr int kRpOneRoutes = kRpOneMaxPieces * kRpScanThreads;
+// tiles of at most kRpOneRoutes routes: an expert of n > 0 routes has
+// ceil(n / block_m) <= n tiles
+constexpr int kRpOneTiles = kRpOneRoutes;
 
 // NPL > 0: the ids come from routing the tokens' logits first (router.h, NPL
 // logits per lane); wave w routes token w (at most 16 tokens), keeps the ids
 // in LDS and writes ids and weights out.
 template <int NP, int NPL>
 __global__ void __launch_bounds__(kRpScanThreads)
-rp_one_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm,
+rp_one_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm, int cap,
               int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
               int32_t* __restrict__ sorted, int32_t* __restrict__ slot,
               int32_t* __restrict__ tile_expert, int top_k, RouteArgs ra,
               int32_t* __restrict__ zero, int64_t n_zero, int32_t* __restrict__ tile_order) {
   constexpr int kW = kRpScanThreads / 64;
+  static_assert(kW <= 16, "wave totals");
   for (int64_t i = threadIdx.x; i < n_zero; i += kRpScanThreads) zero[i] = 0;
   __shared__ int32_t hist[kW][kRpMaxExperts];
-  __shared__ int32_t wave_tot[kW];
+  __shared__ int32_t wave_tot[2][kW];
   __shared__ int32_t s_off[kRpMaxExperts + 1];
   __shared__ int32_t s_cnt[kRpMaxExperts];
+  __shared__ int32_t s_pre[kRpMaxExperts];
   __shared__ int32_t s_ids[NPL > 0 ? NP * kRpScanThreads : 1];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // route list: the route of rank k of expert e at s_pre[e] + k (one spare
+  // entry: a tile's rows past its valid ones read at most one past the end)
+  __shared__ int32_t s_route[kRpOneRoutes + 1];
+  __shared__ int2 s_tile[kRpOneTiles];  // per tile: first list entry, valid rows
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   if constexpr (NPL > 0) {
     route_tokens<NPL>(ra, top_k, w, ra.T, kW, lane, [&](int t, int id, float pw) {
       if (lane < top_k) {
@@ -236,60 +265,99 @@ rp_one_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm,
     }
   }
   __syncthreads();
-  // per expert: wave bases (in place), totals, padded sizes
+  // per expert: wave bases (in place, all loads in flight first), totals,
+  // padded sizes
   int padded = 0, total = 0;
   if (tid < E) {
+    int n[kW];
+#pragma unroll
+    for (int v = 0; v < kW; ++v) n[v] = hist[v][tid];
 #pragma unroll
     for (int v = 0; v < kW; ++v) {
-      const int n = hist[v][tid];
       hist[v][tid] = total;
-      total += n;
+      total += n[v];
     }
     counts[tid] = total;
     padded = (total + bm - 1) / bm * bm;
   }
-  int incl = padded;
-  for (int d = 1; d < 64; d <<= 1) {
-    const int v = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += v;
-  }
-  if (lane == 63) wave_tot[w] = incl;
-  __syncthreads();
-  if (w == 0) {
-    int t = (lane < kW) ? wave_tot[lane] : 0;
-    for (int d = 1; d < kW; d <<= 1) {
-      const int v = __shfl_up(t, d, 64);
-      if (lane >= d) t += v;
-    }
-    if (lane < kW) wave_tot[lane] = t;
+  // prefixes over the experts of the padded sizes (first positions) and of
+  // the totals (first entries of the route list below)
+  const int incl_p = wave_incl_scan(padded);
+  const int incl_c = wave_incl_scan(total);
+  if (lane == 63) {
+    wave_tot[0][w] = incl_p;
+    wave_tot[1][w] = incl_c;
   }
   __syncthreads();
-  const int excl = incl - padded + (w > 0 ? wave_tot[w - 1] : 0);
+  int P = 0, excl = incl_p - padded, pre = incl_c - total;
+#pragma unroll
+  for (int v = 0; v < kW; ++v) {
+    const int tp = wave_tot[0][v], tc = wave_tot[1][v];
+    P += tp;
+    if (v < w) excl += tp, pre += tc;
+  }
+  const int n_tiles = min(P / bm, min(cap / bm, kRpOneTiles));
   if (tid < E) {
     offsets[tid] = excl;
     s_off[tid] = excl;
     s_cnt[tid] = total;
+    s_pre[tid] = pre;
+    // each tile of the expert: its first route-list entry and valid rows
+    const int t0 = excl / bm;
+    for (int j = 0, k = 0; k < total && t0 + j < n_tiles; ++j, k += bm) {
+      s_tile[t0 + j] = make_int2(pre + k, min(bm, total - k));
+      if (tile_expert != nullptr) tile_expert[t0 + j] = tid;
+    }
   }
   if (tid == 0) {
-    offsets[E] = wave_tot[kW - 1];
-    s_off[E] = wave_tot[kW - 1];
+    offsets[E] = P;
+    s_off[E] = P;
   }
   __syncthreads();
+  // the route list: routes by expert, then rank (route order)
 #pragma unroll
   for (int q = 0; q < NP; ++q) {
     const int r = r0 + 64 * q;
     if (q < np && r < R) {
       const int e = ev[q];
       if (e >= 0) {
-        const int pos = s_off[e] + hist[w][e] + rk[q];
-        sorted[pos] = r;
-        slot[r] = pos;
+        const int k = hist[w][e] + rk[q];
+        slot[r] = s_off[e] + k;
+        s_route[s_pre[e] + k] = r;
       } else {
         slot[r] = -1;
       }
     }
   }
-  fill_padding_and_tiles(0, E, bm, s_off, s_cnt, sorted, tile_expert, kW);
+  __syncthreads();
+  // the padded list, tile by tile (a wave per tile, lane j: row j): the
+  // route-list entry of a valid row, -1 in padding; every position written
+  // once, by consecutive lanes.  With 64-row tiles, four tiles per pass keep
+  // their LDS reads in flight together.
+  if (bm == 64) {
+    constexpr int U = 4;
+    for (int i0 = w; i0 < n_tiles; i0 += U * kW) {
+      int2 inf[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) inf[u] = s_tile[min(i0 + u * kW, n_tiles - 1)];
+      int rv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) rv[u] = s_route[inf[u].x + min(lane, inf[u].y)];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * kW;
+        if (i < n_tiles) sorted[i * 64 + lane] = lane < inf[u].y ? rv[u] : -1;
+      }
+    }
+  } else {
+    for (int i = w; i < n_tiles; i += kW) {
+      const int2 inf = s_tile[i];
+      for (int j = lane; j < bm; j += 64) {
+        const int rv = s_route[inf.x + min(j, inf.y)];
+        sorted[i * bm + j] = j < inf.y ? rv : -1;
+      }
+    }
+  }
   if (tile_order != nullptr) {
     __shared__ int32_t s_tot[4][16];
     write_tile_order(E, bm, s_off, s_cnt, 0, E, tile_order, s_tot);
@@ -305,7 +373,7 @@ rp_rank_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int chunk
        i += static_cast<int64_t>(gridDim.x) * kRpThreads)
     zero[i] = 0;
   __shared__ int32_t hist[NW][kRpMaxExperts];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int c = blockIdx.x;
   for (int e = lane; e < E; e += 64) hist[w][e] = 0;  // read back by this wave only
 
@@ -406,7 +474,7 @@ rp_scatter_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm
   __shared__ int32_t s_off[kRpMaxExperts + 1];
   __shared__ int32_t s_cnt[kRpMaxExperts];
   __shared__ int32_t s_base[kRpMaxExperts];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int c = blockIdx.x;
   const int c_end = min(R, (c + 1) * chunk);
   // a chunk of at most one route per thread: the route's expert and rank
@@ -431,29 +499,22 @@ rp_scatter_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm
     }
     padded = (total + bm - 1) / bm * bm;
   }
-  int incl = padded;
-  for (int d = 1; d < 64; d <<= 1) {
-    const int v = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += v;
-  }
+  const int incl = wave_incl_scan(padded);
   if (lane == 63) wave_tot[w] = incl;
   __syncthreads();
-  if (w == 0) {
-    int t = (lane < kW) ? wave_tot[lane] : 0;
-    for (int d = 1; d < kW; d <<= 1) {
-      const int v = __shfl_up(t, d, 64);
-      if (lane >= d) t += v;
-    }
-    if (lane < kW) wave_tot[lane] = t;  // inclusive totals per wave
+  int P = 0, excl = incl - padded;
+#pragma unroll
+  for (int v = 0; v < kW; ++v) {
+    const int t = wave_tot[v];
+    P += t;
+    if (v < w) excl += t;
   }
-  __syncthreads();
-  const int excl = incl - padded + (w > 0 ? wave_tot[w - 1] : 0);
   if (tid < E) {
     s_off[tid] = excl;
     s_cnt[tid] = total;
     s_base[tid] = base;
   }
-  if (tid == 0) s_off[E] = wave_tot[kW - 1];
+  if (tid == 0) s_off[E] = P;
   __syncthreads();
   if (one_pass) {
     if (e1 >= 0) {  // slot[r1] is already -1 for an invalid route
@@ -504,8 +565,12 @@ hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, 
                              int32_t* tile_expert, int32_t* chunk_hist, hipStream_t stream,
                              int top_k, const RouteArgs* route, int32_t* zero, int64_t n_zero,
                              int32_t* tile_order) {
-  if (E < 1 || E > kRpMaxExperts || R < 0) return hipErrorInvalidValue;
+  if (E < 1 || E > kRpMaxExperts || R < 0 || bm < 1) return hipErrorInvalidValue;
   if (tile_order != nullptr && bm % 4 != 0) return hipErrorInvalidValue;
+  // positions the padded list may take (its callers' capacity)
+  const int64_t cap64 = R + std::min<int64_t>(E, R) * (bm - 1);
+  if (cap64 > INT32_MAX) return hipErrorInvalidValue;
+  const int cap = static_cast<int>(cap64);
   if (zero == nullptr) n_zero = 0;
   // without scratch: one chunk, whose counts live in `counts` itself (the
   // scan overwrites them with the totals) and whose base is 0
@@ -527,8 +592,9 @@ hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, 
         case 8: k = rp_one_kernel<kRpOneMaxPieces, 8>; break;
         default: break;
       }
-      hipLaunchKernelGGL(k, dim3(1), dim3(kRpScanThreads), 0, stream, ids, R, E, off, bm, counts,
-                         offsets, sorted, slot, tile_expert, top_k, ra, zero, n_zero, tile_order);
+      hipLaunchKernelGGL(k, dim3(1), dim3(kRpScanThreads), 0, stream, ids, R, E, off, bm, cap,
+                         counts, offsets, sorted, slot, tile_expert, top_k, ra, zero, n_zero,
+                         tile_order);
       return hipGetLastError();
     }
     const hipError_t err = launch_router_topk(ra.logits, ra.T, ra.Eg, top_k, ra.renorm, ra.ids,
@@ -538,8 +604,8 @@ hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, 
   }
   if (R <= kRpOneRoutes) {
     hipLaunchKernelGGL((rp_one_kernel<kRpOneMaxPieces, 0>), dim3(1), dim3(kRpScanThreads), 0,
-                       stream, ids, R, E, off, bm, counts, offsets, sorted, slot, tile_expert,
-                       top_k, RouteArgs{}, zero, n_zero, tile_order);
+                       stream, ids, R, E, off, bm, cap, counts, offsets, sorted, slot,
+                       tile_expert, top_k, RouteArgs{}, zero, n_zero, tile_order);
     return hipGetLastError();
   }
   // R > kRpOneRoutes here, so there is at least one chunk
