@@ -39,6 +39,9 @@ ROUTE_CASES = [
     (8192, 8, 384, 384, 0, 64), (300, 8, 384, 384, 0, 64), (129, 8, 60, 60, 0, 32),
     (7, 3, 5, 9, 2, 4), (33, 4, 60, 60, 0, 32), (100, 8, 1024, 1024, 0, 1),
     (5, 2, 8, 8, 0, 256), (0, 4, 8, 8, 0, 16),
+    # one workgroup with 2 route pieces per wave, and two launches above it
+    (256, 8, 384, 384, 0, 64), (512, 8, 384, 384, 0, 64), (513, 8, 384, 384, 0, 64),
+    (170, 12, 60, 64, 2, 128), (1000, 4, 1024, 1024, 0, 16),
 ]
 
 

@@ -149,7 +149,7 @@ struct CombineParams {
   uint16_t* out;              // [T][H]
 };
 
-// Route preparation (one launch up to 1024 routes, else two).  chunk_hist:
+// Route preparation (one launch up to 2048 routes, else two).  chunk_hist:
 // kRouteChunksMax * E ints of scratch, or null for a single-chunk (slower for
 // many routes) preparation.
 // With `route` (router logits instead of ids; see router.h) route->ids and

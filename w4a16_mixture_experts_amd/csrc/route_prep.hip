@@ -187,13 +187,11 @@ __device__ __forceinline__ void write_tile_order(int E, int bm, const int32_t* s
 // first list entry and valid rows, and the padded list is written tile by
 // tile in one pass: consecutive lanes, every position once, no per-expert
 // loop (which a wave walks serially, instruction by instruction).
-// (Measured on the 384-expert workload: beyond 1024 routes, two launches
-// over 256-route chunks are faster.)
-constexpr int kRpOneMaxPieces = 1;
+// (Measured: up to 2048 routes, one workgroup beats the two launches by 0-2
+// us; at 4 pieces per wave, 3072 and 4096 routes on the 384-expert shard, it
+// is 1-4 us slower.)
+constexpr int kRpOneMaxPieces = 2;
 constexpr int kRpOneRoutes = kRpOneMaxPieces * kRpScanThreads;
-// tiles of at most kRpOneRoutes routes: an expert of n > 0 routes has
-// ceil(n / block_m) <= n tiles
-constexpr int kRpOneTiles = kRpOneRoutes;
 
 // NPL > 0: the ids come from routing the tokens' logits first (router.h, NPL
 // logits per lane); wave w routes token w (at most 16 tokens), keeps the ids
@@ -216,8 +214,11 @@ rp_one_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm, in
   __shared__ int32_t s_ids[NPL > 0 ? NP * kRpScanThreads : 1];
   // route list: the route of rank k of expert e at s_pre[e] + k (one spare
   // entry: a tile's rows past its valid ones read at most one past the end)
-  __shared__ int32_t s_route[kRpOneRoutes + 1];
-  __shared__ int2 s_tile[kRpOneTiles];  // per tile: first list entry, valid rows
+  __shared__ int32_t s_route[NP * kRpScanThreads + 1];
+  // per tile: first list entry, valid rows (an expert of n > 0 routes has
+  // ceil(n / block_m) <= n tiles)
+  constexpr int kTiles = NP * kRpScanThreads;
+  __shared__ int2 s_tile[kTiles];
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   if constexpr (NPL > 0) {
     route_tokens<NPL>(ra, top_k, w, ra.T, kW, lane, [&](int t, int id, float pw) {
@@ -296,7 +297,7 @@ rp_one_kernel(const int32_t* __restrict__ ids, int R, int E, int off, int bm, in
     P += tp;
     if (v < w) excl += tp, pre += tc;
   }
-  const int n_tiles = min(P / bm, min(cap / bm, kRpOneTiles));
+  const int n_tiles = min(P / bm, min(cap / bm, kTiles));
   if (tid < E) {
     offsets[tid] = excl;
     s_off[tid] = excl;
@@ -583,13 +584,13 @@ hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, 
     if (ra.Eg < 1 || ra.Eg > kRouterMaxExperts || top_k < 1 || top_k > kRouterMaxTopK ||
         top_k > ra.Eg || static_cast<int64_t>(ra.T) * top_k != R)
       return hipErrorInvalidValue;
-    if (R <= kRpOneRoutes && ra.T <= kRpRouteMaxTokens) {
-      auto k = rp_one_kernel<kRpOneMaxPieces, 16>;
+    if (R <= kRpScanThreads && ra.T <= kRpRouteMaxTokens) {
+      auto k = rp_one_kernel<1, 16>;
       switch (router_npl(ra.Eg)) {
-        case 1: k = rp_one_kernel<kRpOneMaxPieces, 1>; break;
-        case 2: k = rp_one_kernel<kRpOneMaxPieces, 2>; break;
-        case 4: k = rp_one_kernel<kRpOneMaxPieces, 4>; break;
-        case 8: k = rp_one_kernel<kRpOneMaxPieces, 8>; break;
+        case 1: k = rp_one_kernel<1, 1>; break;
+        case 2: k = rp_one_kernel<1, 2>; break;
+        case 4: k = rp_one_kernel<1, 4>; break;
+        case 8: k = rp_one_kernel<1, 8>; break;
         default: break;
       }
       hipLaunchKernelGGL(k, dim3(1), dim3(kRpScanThreads), 0, stream, ids, R, E, off, bm, cap,
@@ -603,9 +604,14 @@ hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, 
     ids = ra.ids;  // the preparation reads the ids the router wrote
   }
   if (R <= kRpOneRoutes) {
-    hipLaunchKernelGGL((rp_one_kernel<kRpOneMaxPieces, 0>), dim3(1), dim3(kRpScanThreads), 0,
-                       stream, ids, R, E, off, bm, cap, counts, offsets, sorted, slot,
-                       tile_expert, top_k, RouteArgs{}, zero, n_zero, tile_order);
+    static_assert(kRpOneMaxPieces == 1 || kRpOneMaxPieces == 2 || kRpOneMaxPieces == 4,
+                  "pieces per wave");
+    auto k = rp_one_kernel<1, 0>;
+    if (R > 2 * kRpScanThreads) k = rp_one_kernel<(kRpOneMaxPieces > 2 ? 4 : 1), 0>;
+    else if (R > kRpScanThreads) k = rp_one_kernel<(kRpOneMaxPieces > 1 ? 2 : 1), 0>;
+    hipLaunchKernelGGL(k, dim3(1), dim3(kRpScanThreads), 0, stream, ids, R, E, off, bm, cap,
+                       counts, offsets, sorted, slot, tile_expert, top_k, RouteArgs{}, zero,
+                       n_zero, tile_order);
     return hipGetLastError();
   }
   // R > kRpOneRoutes here, so there is at least one chunk
