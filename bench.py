@@ -98,12 +98,17 @@ def kernel_name(wl, plan, stage):
     if plan.block_m != 64:
         return f"block_m {plan.block_m} {stage}"
     if stage == "gate_up_gemm":
+        if plan.splitk_chunks and plan.act_in_down:
+            return f"up_splitk_kernel<{dt}, {lay}, 2>"
         if plan.splitk_chunks:
             return (f"up_splitk_kernel<{dt}, {lay}, 2> + "
                     f"splitk_act_kernel<{dt}, {'true' if wl.gated else 'false'}>")
         return f"tile_gemm_kernel<{dt}, {lay}, {0 if wl.gated else 1}>"
     if wl.inter <= 256:   # the reduction fits the resident down kernel
-        return f"down_resident_kernel<{dt}, {lay}, {1 if wl.inter <= 128 else 2}>"
+        nkb = 1 if wl.inter <= 128 else 2
+        if plan.act_in_down:   # activations formed from the split-K partials
+            return f"down_resident_kernel<{dt}, {lay}, {nkb}, true>"
+        return f"down_resident_kernel<{dt}, {lay}, {nkb}>"
     return f"tile_gemm_kernel<{dt}, {lay}, 2>"
 
 

@@ -171,6 +171,9 @@ typedef struct {
                                  launch's rerun_flags_down (0 if neither launch
                                  exists)                                         */
   int32_t tile_order;         /* 1: the tile launches take tiles biggest first   */
+  int32_t act_in_down;        /* 1: split-K gate/up, and the down launch forms
+                                 the activations from its partials (no
+                                 activation launch)                              */
 } w4a16_moe_plan_t;
 
 /* Bytes of device workspace w4a16_moe_forward needs for this descriptor

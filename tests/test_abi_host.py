@@ -389,3 +389,22 @@ def test_tile_order_chosen_between_12_and_128_routes_per_expert():
     assert B.get_plan(B.desc_for(wl, 8)).tile_order == 0   # small batch
     # 192 routes per expert: mostly full tiles
     assert B.get_plan(B.desc_for(S.WORKLOADS["relu2_skew"], 4096)).tile_order == 0
+
+
+def test_activations_formed_in_the_down_launch_after_split_k():
+    """Split-K gate/up followed by the resident down kernel runs no activation
+    launch; the streaming gate/up, or a down GEMM that does not hold the
+    reduction in LDS, keeps it."""
+    wl = S.WORKLOADS["kimi_tp8"]
+    for T, want in ((32, 1), (128, 1), (256, 0), (2048, 0)):
+        p = B.get_plan(B.desc_for(wl, T))
+        assert p.act_in_down == want, T
+        assert want == 0 or p.splitk_chunks > 0
+    assert B.get_plan(B.desc_for(wl, 8)).act_in_down == 0   # small batch
+    # forced split-K at 256 tokens still pairs with the resident down kernel
+    assert B.get_plan(B.desc_for(wl, 256, force_path=1, force_splitk=1)).act_in_down == 1
+    for name, wl in S.WORKLOADS.items():
+        for T in (32, 256):
+            p = B.get_plan(B.desc_for(wl, T))
+            if p.act_in_down:
+                assert p.splitk_chunks > 0 and wl.inter <= 256, (name, T)

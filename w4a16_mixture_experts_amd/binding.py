@@ -38,7 +38,7 @@ class MoePlan(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t), ("fp16_route", ctypes.c_int32),
                 ("rerun_flags_up", ctypes.c_int32), ("rerun_flags_down", ctypes.c_int32),
                 ("fused_combine", ctypes.c_int32), ("rerun_flags_offset", ctypes.c_size_t),
-                ("tile_order", ctypes.c_int32)]
+                ("tile_order", ctypes.c_int32), ("act_in_down", ctypes.c_int32)]
 
 
 class W4A16Error(RuntimeError):

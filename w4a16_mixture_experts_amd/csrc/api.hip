@@ -54,6 +54,9 @@ struct Plan {
   bool x16_down = false;  // so does the resident down GEMM
   int64_t n_redo_up = 0, n_redo_down = 0;  // rerun flags of those launches
   bool fused_fin = false;  // the combine runs inside the down launch
+  // split-K gate/up with the resident down kernel: the down kernel forms the
+  // activations from the partials while staging (no activation launch)
+  bool act_in_down = false;
   bool tile_sort = false;  // tile launches take tiles biggest first (tile order)
   size_t off_counts = 0, off_offsets = 0, off_slot = 0, off_sorted = 0, off_tile = 0,
          off_order = 0,
@@ -262,6 +265,10 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
   // the Kimi shard's resident kernel: 167 -> 148 us at 2048 tokens; tiles of
   // one subtile were slower on it).
   pl.x16_down = pl.x16;
+  // Measured on the Kimi shard (one workgroup-pass of loads per tile: the
+  // padding rows load nothing): the activation launch and its dependent
+  // start are saved at 32-128 tokens.
+  pl.act_in_down = pl.path == 1 && pl.splitk_S > 0 && pl.down_resident && !pl.x16_down;
   if (pl.down_resident) {
     const int64_t steps = pl.n_tiles_down;
     const int64_t mt = std::max<int64_t>(pl.MT, 1);
@@ -408,6 +415,7 @@ w4a16_status_t w4a16_moe_get_plan(const w4a16_moe_desc_t* desc, w4a16_moe_plan_t
   plan->rerun_flags_offset = (up16 || dn16) ? pl.off_redo : 0;
   plan->fused_combine = pl.fused_fin ? 1 : 0;
   plan->tile_order = pl.tile_sort ? 1 : 0;
+  plan->act_in_down = pl.act_in_down ? 1 : 0;
   return W4A16_OK;
 }
 
@@ -630,7 +638,7 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
       st = hip_status(w4moe::launch_up_splitk(up, desc->dtype, desc->qlayout,
                                               static_cast<int>(pl.MT), stream),
                       "gate/up GEMM launch");
-      if (st == W4A16_OK)
+      if (st == W4A16_OK && !pl.act_in_down)
         st = hip_status(w4moe::launch_splitk_act(up, desc->dtype, gated, stream),
                         "activation launch");
     } else {
@@ -680,6 +688,13 @@ w4a16_status_t forward_impl(const void* x, const uint8_t* w13_packed, const void
   st = hip_status(evs.mark(4), "stage event");
   if (st != W4A16_OK) return st;
   dn.col_steps = pl.col_steps;
+  if (pl.act_in_down) {
+    dn.part = reinterpret_cast<float*>(ws + pl.off_part);
+    dn.S = pl.splitk_S;
+    dn.R = static_cast<int>(pl.R);
+    dn.part_ld = pl.N1;
+    dn.up_rows = gated ? I : 0;
+  }
   st = hip_status(pl.down_resident
                       ? w4moe::launch_down_resident(dn, desc->dtype, desc->qlayout,
                                                     static_cast<int>(pl.MT), stream)

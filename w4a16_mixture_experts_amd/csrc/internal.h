@@ -43,6 +43,10 @@ struct GemmParams {
   int S;                      // reduction chunks
   int cb;                     // 128-blocks per chunk
   int R;                      // routes (T*K)
+  // resident down kernel: non-null part selects activations formed from the
+  // split-K partials [S][R][part_ld] while staging (the up values of a
+  // partial row at column offset up_rows; 0: ReLU^2) instead of reading `a`
+  int part_ld;
   const int32_t* slot;        // [R] route -> position, -1 for invalid routes
   int tiles;                  // entries of tile_expert (positions / bm)
   // streaming tile kernel, bf16 group layout: non-null selects the exact

@@ -986,7 +986,66 @@ tile_redo_kernel(const GemmParams p, const int n_wg) {
 // value per lane per output.
 constexpr int kOutStride = 40;  // 16-bit elements per staged row (80 B)
 
-template <int DT, int LAYOUT, int NMS, int NKB>
+// Activation values i0 .. i0 + 7 of route r from the split-K partials
+// [S][R][ld] FP32: the chunks summed in order 0 .. S-1 (four chunks' loads in
+// flight at a time), then SiLU(gate) * up (gated: the up values at column
+// offset `up` of a partial row) or ReLU^2 (up == 0), one 16-bit rounding
+// each; packed in A operand order.  The activation kernel and the resident
+// down kernel's staging both form activations here, so their bits agree.
+template <int DT>
+__device__ __forceinline__ u32x4 act_from_partials(const float* part, int S, int R, int ld,
+                                                   int up, int r, int i0) {
+  float h[8], u[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) h[j] = u[j] = 0.0f;
+  for (int kb = 0; kb < S; kb += 4) {
+    f32x4 a[4][2], b[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a[j][0] = a[j][1] = b[j][0] = b[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (kb + j < S) {
+        const float* row = part + (static_cast<int64_t>(kb + j) * R + r) * ld + i0;
+        a[j][0] = *reinterpret_cast<const f32x4*>(row);
+        a[j][1] = *reinterpret_cast<const f32x4*>(row + 4);
+        if (up > 0) {
+          b[j][0] = *reinterpret_cast<const f32x4*>(row + up);
+          b[j][1] = *reinterpret_cast<const f32x4*>(row + up + 4);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (kb + j < S) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          h[q] += a[j][0][q];
+          h[4 + q] += a[j][1][q];
+          u[q] += b[j][0][q];
+          u[4 + q] += b[j][1][q];
+        }
+      }
+    }
+  }
+  uint16_t o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float v;
+    if (up > 0) {
+      v = silu(h[j]) * u[j];
+    } else {
+      const float z = fmaxf(h[j], 0.0f);
+      v = z * z;
+    }
+    o[a_pos(j)] = H16<DT>::from_f32(v);
+  }
+  u32x4 v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    v[q] = static_cast<uint32_t>(o[2 * q]) | (static_cast<uint32_t>(o[2 * q + 1]) << 16);
+  return v;
+}
+
+template <int DT, int LAYOUT, int NMS, int NKB, bool PART = false>
 __device__ __forceinline__ void down_resident_run(const GemmParams& p, const int row_base,
                                                   const int e, const int chunk, uint16_t* s_ar,
                                                   uint16_t* s_out) {
@@ -996,7 +1055,27 @@ __device__ __forceinline__ void down_resident_run(const GemmParams& p, const int
 
   // stage the tile's activation rows once (padding rows and columns past K
   // read zeros)
-  {
+  if constexpr (PART) {
+    // from the split-K partials of the gate/up launch.  Rows past the NMS
+    // non-empty subtiles hold no route: their passes load nothing.
+    constexpr int kPerRow = NKB * 16;                   // 8-value chunks per row
+    constexpr int kRowsPer = kTileThreads / kPerRow;    // rows per pass
+    constexpr int kIters = kTileRows / kRowsPer;
+    static_assert(kTileRows % kRowsPer == 0, "staging passes");
+    const int srt = p.sorted[row_base + lane];          // every wave: all 64 rows
+#pragma unroll
+    for (int i = 0; i < kIters; ++i) {
+      const int idx = tid + i * kTileThreads;
+      const int row = idx / kPerRow, ch = idx % kPerRow;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (kRowsPer * i < 16 * NMS) {
+        const int r = __shfl(srt, row, 64);
+        if (r >= 0 && 8 * ch < p.K)
+          v = act_from_partials<DT>(p.part, p.S, p.R, p.part_ld, p.up_rows, r, 8 * ch);
+      }
+      *reinterpret_cast<u32x4*>(s_ar + row * S + 8 * ch) = v;
+    }
+  } else {
     constexpr int kPerRow = NKB * 16;                       // 16-byte chunks per row
     constexpr int kIters = kTileRows * kPerRow / kTileThreads;
     static_assert(kTileRows * kPerRow % kTileThreads == 0, "staging covers the tile");
@@ -1150,7 +1229,9 @@ __device__ __forceinline__ void down_resident_run(const GemmParams& p, const int
 // Four waves per SIMD (two workgroups per CU): twice the weight requests in
 // flight per CU; measured faster than one workgroup with more registers
 // although the four-subtile path then keeps a few values in scratch.
-template <int DT, int LAYOUT, int NKB>
+// PART: the activations come from split-K partials (a separate instance, so
+// that the plain kernel's register allocation is not affected).
+template <int DT, int LAYOUT, int NKB, bool PART = false>
 __global__ void __launch_bounds__(kTileThreads, 4)
 down_resident_kernel(const GemmParams p) {
   __shared__ uint16_t s_ar[kTileRows * (NKB * 128 + 8)];
@@ -1180,13 +1261,13 @@ down_resident_kernel(const GemmParams p) {
 #pragma unroll
   for (int ms = 0; ms < kTileMs; ++ms) nms += first[ms] >= 0 ? 1 : 0;
   switch (nms) {
-    case 1: down_resident_run<DT, LAYOUT, 1, NKB>(p, row_base, e, chunk, s_ar,
+    case 1: down_resident_run<DT, LAYOUT, 1, NKB, PART>(p, row_base, e, chunk, s_ar,
                                                   s_out[threadIdx.x >> 6]); break;
-    case 2: down_resident_run<DT, LAYOUT, 2, NKB>(p, row_base, e, chunk, s_ar,
+    case 2: down_resident_run<DT, LAYOUT, 2, NKB, PART>(p, row_base, e, chunk, s_ar,
                                                   s_out[threadIdx.x >> 6]); break;
-    case 3: down_resident_run<DT, LAYOUT, 3, NKB>(p, row_base, e, chunk, s_ar,
+    case 3: down_resident_run<DT, LAYOUT, 3, NKB, PART>(p, row_base, e, chunk, s_ar,
                                                   s_out[threadIdx.x >> 6]); break;
-    default: down_resident_run<DT, LAYOUT, 4, NKB>(p, row_base, e, chunk, s_ar,
+    default: down_resident_run<DT, LAYOUT, 4, NKB, PART>(p, row_base, e, chunk, s_ar,
                                                   s_out[threadIdx.x >> 6]); break;
   }
   if (p.fin_cnt != nullptr) {
@@ -1678,13 +1759,11 @@ up_splitk_kernel(const GemmParams p) {
   }
 }
 
-// act[slot[r]] for route r from its split-K partials: the chunks summed in
-// order 0..S-1, then SiLU(gate) * up (or ReLU^2), one 16-bit rounding, stored
-// in A operand order.  One thread per 8 consecutive activation columns.
+// act[slot[r]] for route r from its split-K partials (act_from_partials).
+// One thread per 8 consecutive activation columns.
 template <int DT, bool GATED>
 __global__ void __launch_bounds__(256)
 splitk_act_kernel(const GemmParams p) {
-  using T = H16<DT>;
   const int I = p.ldo;
   const int per_row = I / 8;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -1693,34 +1772,8 @@ splitk_act_kernel(const GemmParams p) {
   if (r >= p.R) return;
   const int pos = p.slot[r];
   if (pos < 0) return;  // invalid route: no position, nothing reads it
-  float h[8], u[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) h[j] = u[j] = 0.0f;
-  for (int kc = 0; kc < p.S; ++kc) {
-    const float* row = p.part + (static_cast<int64_t>(kc) * p.R + r) * p.n_cols;
-    const f32x4 a = *reinterpret_cast<const f32x4*>(row + i0);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(row + i0 + 4);
-    h[0] += a[0]; h[1] += a[1]; h[2] += a[2]; h[3] += a[3];
-    h[4] += b[0]; h[5] += b[1]; h[6] += b[2]; h[7] += b[3];
-    if constexpr (GATED) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(row + I + i0);
-      const f32x4 y = *reinterpret_cast<const f32x4*>(row + I + i0 + 4);
-      u[0] += x[0]; u[1] += x[1]; u[2] += x[2]; u[3] += x[3];
-      u[4] += y[0]; u[5] += y[1]; u[6] += y[2]; u[7] += y[3];
-    }
-  }
-  uint16_t o[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float a;
-    if constexpr (GATED) a = silu(h[j]) * u[j];
-    else { const float z = fmaxf(h[j], 0.0f); a = z * z; }
-    o[a_pos(j)] = T::from_f32(a);
-  }
-  u32x4 v;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) v[q] = static_cast<uint32_t>(o[2 * q]) | (static_cast<uint32_t>(o[2 * q + 1]) << 16);
-  *reinterpret_cast<u32x4*>(p.out + static_cast<int64_t>(pos) * I + i0) = v;
+  *reinterpret_cast<u32x4*>(p.out + static_cast<int64_t>(pos) * I + i0) =
+      act_from_partials<DT>(p.part, p.S, p.R, p.n_cols, GATED ? I : 0, r, i0);
 }
 
 template <typename F>
@@ -1841,7 +1894,12 @@ static hipError_t launch_resident_k(const GemmParams& p, dim3 grid, hipStream_t 
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((down_resident_kernel<DT, LAYOUT, NKB>), grid, dim3(kTileThreads), 0, st, p);
+  if (p.part != nullptr)
+    hipLaunchKernelGGL((down_resident_kernel<DT, LAYOUT, NKB, true>), grid, dim3(kTileThreads), 0,
+                       st, p);
+  else
+    hipLaunchKernelGGL((down_resident_kernel<DT, LAYOUT, NKB>), grid, dim3(kTileThreads), 0, st,
+                       p);
   return hipGetLastError();
 }
 
@@ -1854,6 +1912,12 @@ static hipError_t launch_resident_dl(const GemmParams& p, dim3 grid, hipStream_t
 hipError_t launch_down_resident(const GemmParams& p, int dtype, int layout, int max_tiles,
                                 hipStream_t stream) {
   if (p.K > kResidentK || p.col_steps < 1) return hipErrorInvalidValue;
+  // activations from split-K partials: whole 8-value chunks inside a partial
+  // row, and not with the fp16 route (whose rerun reads the activations)
+  if (p.part != nullptr &&
+      (p.redo != nullptr || p.S < 1 || p.R < 1 || p.K % 8 != 0 || p.up_rows < 0 ||
+       p.up_rows + p.K > p.part_ld || (p.up_rows > 0 && p.up_rows < p.K)))
+    return hipErrorInvalidValue;
   const int n_main = kXcds * p.n_tiles * ((max_tiles + kXcds - 1) / kXcds);
   if (p.fin_cnt != nullptr && (p.n_main != n_main || p.redo != nullptr)) return hipErrorInvalidValue;
   const dim3 grid(n_main + (p.fin_cnt != nullptr ? fin_zero_workgroups(p.T) : 0));
