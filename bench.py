@@ -108,7 +108,7 @@ def kernel_name(wl, plan, stage):
         nkb = 1 if wl.inter <= 128 else 2
         if plan.act_in_down:   # activations formed from the split-K partials
             return f"down_resident_kernel<{dt}, {lay}, {nkb}, true>"
-        return f"down_resident_kernel<{dt}, {lay}, {nkb}>"
+        return f"down_resident_kernel<{dt}, {lay}, {nkb}, false>"
     return f"tile_gemm_kernel<{dt}, {lay}, 2>"
 
 
