@@ -216,10 +216,11 @@ def test_small_batch_path_only_for_short_intermediate():
     assert B.get_plan(B.make_desc(num_tokens=1, **kimi)).path == 2
     assert B.get_plan(B.make_desc(num_tokens=8, **kimi)).path == 2
     # I = 2048, top-8, every route local: the grouped path even for 1 token,
-    # with the split-K gate/up spread over column chunks
+    # with the streaming gate/up (16 column tiles per expert tile; forced
+    # split-K measured 107 us against 81)
     ds = dict(hidden=7168, intermediate=2048, num_local_experts=32, top_k=8)
     p = B.get_plan(B.make_desc(num_tokens=1, **ds))
-    assert p.path == 1 and p.splitk_chunks > 0
+    assert p.path == 1 and p.splitk_chunks == 0
     # the same experts as a share of 256 global ones (one local route per
     # token expected): the small-batch path up to 64 routes (past them most
     # of its gate/up workgroups would own no local expert)
@@ -396,7 +397,7 @@ def test_activations_formed_in_the_down_launch_after_split_k():
     launch; the streaming gate/up, or a down GEMM that does not hold the
     reduction in LDS, keeps it."""
     wl = S.WORKLOADS["kimi_tp8"]
-    for T, want in ((32, 1), (128, 1), (256, 0), (2048, 0)):
+    for T, want in ((32, 1), (64, 1), (48, 0), (128, 0), (256, 0), (2048, 0)):
         p = B.get_plan(B.desc_for(wl, T))
         assert p.act_in_down == want, T
         assert want == 0 or p.splitk_chunks > 0
@@ -408,3 +409,22 @@ def test_activations_formed_in_the_down_launch_after_split_k():
             p = B.get_plan(B.desc_for(wl, T))
             if p.act_in_down:
                 assert p.splitk_chunks > 0 and wl.inter <= 256, (name, T)
+
+
+def test_split_k_only_where_the_streaming_grid_underfills():
+    """Split-K gate/up is chosen for few routes per expert, a resident down
+    kernel, and a streaming grid (touched experts x column tiles, one
+    workgroup per CU) whose last round would be less than 0.8 full."""
+    wl = S.WORKLOADS["kimi_tp8"]
+    # 2 column tiles per expert tile; expected touched experts of 384
+    for T, want in ((32, True), (48, False), (64, True), (80, False), (96, False), (128, False)):
+        p = B.get_plan(B.desc_for(wl, T))
+        assert (p.splitk_chunks > 0) == want, T
+    # larger intermediates: the streaming kernel at every token count
+    for name in ("deepseek_local", "relu2_skew", "per_channel"):
+        for T in (16, 32, 48, 64, 96, 128):
+            p = B.get_plan(B.desc_for(S.WORKLOADS[name], T))
+            assert p.splitk_chunks == 0, (name, T)
+    # forcing still selects either form
+    assert B.get_plan(B.desc_for(wl, 128, force_path=1, force_splitk=1)).splitk_chunks > 0
+    assert B.get_plan(B.desc_for(wl, 32, force_path=1, force_splitk=2)).splitk_chunks == 0

@@ -201,12 +201,24 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
                         : (I + w4moe::kTileColsPlain - 1) / w4moe::kTileColsPlain;
   pl.n_tiles_down = (H + w4moe::kTileColsPlain - 1) / w4moe::kTileColsPlain;
   // split-K gate/up when tiles are expected to hold few routes (every route
-  // counted, as when the crossover below was measured)
+  // counted) and the streaming launch would leave much of its last round of
+  // workgroups (one per CU) empty, and only before the resident down kernel,
+  // which then forms the activations from the partials (no activation launch;
+  // N1 small, so are the partials).  Measured, forced split-K against the
+  // streaming kernel (cold us): Kimi shard 153 / 161 at 32 tokens (fill 0.73),
+  // 237 / 244 at 64 (0.74), even at 80 (0.83), 181 streaming against 197 at
+  // 48 (0.95) and 255-269 against 276-296 at 96-128 (0.86-0.93); with a
+  // larger intermediate (the DeepSeek share, the per-channel model, the
+  // skewed ReLU^2 model: 8-16 column tiles per expert tile) the streaming
+  // kernel won at every token count from 16 to 128, by 9-54 us.
   if (pl.R > 0) {
     const double rpe_all = routes_per_touched_expert(d, pl.R, false);
-    // measured crossover: split-K wins at ~1.4 routes per expert (Kimi shard,
-    // 32 tokens), the streaming kernel at ~5 (256 tokens)
-    bool use = rpe_all <= 3.0;
+    const double Ed = static_cast<double>(E);
+    const double touched =
+        std::max(1.0, Ed * (1.0 - std::pow(1.0 - 1.0 / Ed, static_cast<double>(pl.R))));
+    const double wgs = touched * pl.n_tiles_up;
+    const double fill = wgs / (w4moe::kComputeUnits * std::ceil(wgs / w4moe::kComputeUnits));
+    bool use = rpe_all <= 3.0 && I <= w4moe::kResidentK && fill < 0.8;
     if (d->force_splitk == 1) use = true;
     if (d->force_splitk == 2) use = false;
     if (use) {

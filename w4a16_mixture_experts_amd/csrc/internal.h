@@ -8,6 +8,7 @@ namespace w4moe {
 
 enum : int { MODE_UP_GATED = 0, MODE_UP_RELU2 = 1, MODE_DOWN = 2 };
 
+constexpr int kComputeUnits = 256;   // MI355X
 constexpr int kCombineCols = 2048;
 constexpr int kTileRows = 64;        // route positions of one LDS-staged expert tile
 constexpr int kTileWaves = 8;
