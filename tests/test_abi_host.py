@@ -222,19 +222,33 @@ def test_small_batch_path_only_for_short_intermediate():
     p = B.get_plan(B.make_desc(num_tokens=1, **ds))
     assert p.path == 1 and p.splitk_chunks == 0
     # the same experts as a share of 256 global ones (one local route per
-    # token expected): the small-batch path up to 64 routes (past them most
+    # token expected): the small-batch path up to 96 routes (past them most
     # of its gate/up workgroups would own no local expert)
-    for T in (1, 8):
+    for T in (1, 8, 12):
         assert B.get_plan(B.make_desc(num_tokens=T, num_global_experts=256, **ds)).path == 2
-    assert B.get_plan(B.make_desc(num_tokens=9, num_global_experts=256, **ds)).path == 1
+    assert B.get_plan(B.make_desc(num_tokens=13, num_global_experts=256, **ds)).path == 1
     # every route local: the small-batch path up to 128 routes
     for T in (9, 16):
         assert B.get_plan(B.make_desc(num_tokens=T, **kimi)).path == 2
     assert B.get_plan(B.make_desc(num_tokens=17, **kimi)).path == 1
     # a quarter local: 2 expected local routes x I = 4096, small batch; two
-    # thirds local: 5.3 x I > 8192, grouped
+    # thirds local: 5.3 x I = 10,923, still small batch; four fifths local:
+    # 6.4 x I = 13,107 > 12,288, grouped
     assert B.get_plan(B.make_desc(num_tokens=1, num_global_experts=128, **ds)).path == 2
-    assert B.get_plan(B.make_desc(num_tokens=1, num_global_experts=48, **ds)).path == 1
+    assert B.get_plan(B.make_desc(num_tokens=1, num_global_experts=48, **ds)).path == 2
+    assert B.get_plan(B.make_desc(num_tokens=1, num_global_experts=40, **ds)).path == 1
+
+
+def test_small_batch_path_bounded_by_its_working_workgroups():
+    """Past a few tokens the small-batch gate/up grid's working workgroups,
+    (N1 / 16) x the local experts expected, decide: at most 7,400."""
+    pc = S.WORKLOADS["per_channel"]     # N1 / 16 = 176, 60 experts
+    assert B.get_plan(B.desc_for(pc, 16)).path == 2    # about 6,970
+    assert B.get_plan(B.desc_for(pc, 24)).path == 1    # about 8,450
+    r2 = S.WORKLOADS["relu2_skew"]      # N1 / 16 = 116, 128 experts, top-6, I = 1856
+    for T in (1, 8):
+        assert B.get_plan(B.desc_for(r2, T)).path == 2
+    assert B.get_plan(B.desc_for(r2, 16)).path == 1    # about 7,790
 
 
 def test_small_batch_path_limits():

@@ -123,7 +123,11 @@ def test_configs_small_token_counts(name, T):
     ("deepseek_local", 16, dict(force_path=1, force_splitk=2)),
     ("deepseek_local", 1, dict(force_path=2)),
     ("kimi_tp8", 16, dict(force_path=2)), ("kimi_tp8", 16, dict(force_path=1)),
-    ("deepseek_local", 16, dict(force_path=1)), ("tiny", 64, dict(force_path=2))])
+    ("deepseek_local", 16, dict(force_path=1)), ("tiny", 64, dict(force_path=2)),
+    # the automatic plan at the edges of the small-batch rule
+    ("relu2_skew", 1, dict()), ("relu2_skew", 12, dict()), ("deepseek_local", 12, dict()),
+    ("per_channel", 16, dict()), ("per_channel", 24, dict()), ("kimi_tp8", 48, dict()),
+    ("kimi_tp8", 64, dict())])
 def test_config_variants(name, T, force):
     wl = synth.WORKLOADS[name]
     Wc, Wg = weights(name)

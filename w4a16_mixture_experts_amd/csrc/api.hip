@@ -165,10 +165,25 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
   // 125 -> 78 and 124 -> 94 us, the per-channel model at 16 and 32 tokens
   // 111 -> 79 and 132 -> 123 us; the 32-of-256 share at 16 tokens 107 ->
   // 170 us (about 29,000 of its 32,768 workgroups exit)
+  // Refined by forced runs of both paths (cold us, small batch / grouped):
+  // - the work of the gate/up grid, (N1 / 16) x the local experts expected,
+  //   decides past a few tokens: the per-channel model 78 / 89 at 16 tokens
+  //   (about 6,970 working workgroups) but 107 / 91 at 24 (8,450) and 133 /
+  //   92 at 32; the skewed ReLU^2 model 72 / 95 at 8 tokens (4,640) but 121 /
+  //   114 at 16 (7,790); the 384-expert shard 86 / 92 at 16 (3,490);
+  // - K x local share x I up to 12,288: the skewed ReLU^2 model (top-6, I =
+  //   1856: 11,136) 24 / 50 us at 1 token and 72 / 95 at 8;
+  // - the 32-of-256 share up to 96 routes: 67 / 82 at 12 tokens, 123 / 106
+  //   at 16.
   else {
-    const int64_t max_routes = share < 1.0 ? 64 : w4moe::kSmallMaxRoutes;
+    const int64_t max_routes = share < 1.0 ? 96 : w4moe::kSmallMaxRoutes;
+    const double Ed = static_cast<double>(E);
+    const double local = static_cast<double>(pl.R) * share;
+    const double dexp = Ed * (1.0 - std::pow(1.0 - 1.0 / Ed, local));
+    const double working = (pl.N1 / 16) * dexp;
     pl.path = (pl.R <= max_routes && pl.items <= w4moe::kDecMaxItems &&
-               H <= 8 * w4moe::kSmallMaxSlice && K * share * I <= 8192.0 &&
+               H <= 8 * w4moe::kSmallMaxSlice && K * share * I <= 12288.0 &&
+               working <= 7400.0 &&
                static_cast<int64_t>(K) * I <= w4moe::kDecActLoads * w4moe::kDecThreadsAll * 8)
                   ? 2 : 1;
   }
