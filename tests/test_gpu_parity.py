@@ -407,7 +407,9 @@ POISON_CASES = [
     ("tiny", 16, dict(force_path=1, force_splitk=1)),
     ("tiny", 16, dict(force_path=1, force_splitk=2)),
     ("kimi_tp8", 32, dict()),                         # automatic plan: split-K
-    ("deepseek_local", 16, dict()),                   # split-K over column chunks
+    ("deepseek_local", 16, dict()),                   # automatic plan: streaming tiles
+    ("deepseek_local", 16, dict(force_path=1, force_splitk=1)),  # split-K over column
+                                                      # chunks, activation launch
     ("tiny", 256, dict(force_path=1, fp16_route=1)),
     ("kimi_tp8", 256, dict(fused_finalize=1)),        # arrival counters start as 0xFF..
     ("deepseek_local", 16, dict(force_path=1, fused_finalize=1)),  # tokens without local routes
