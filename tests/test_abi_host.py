@@ -396,14 +396,19 @@ def test_repack_per_channel_argument_errors():
     assert L.w4a16_repack_per_channel(None, None, 0, 64, 128, None, None, None) == 0
 
 
-def test_tile_order_chosen_between_12_and_128_routes_per_expert():
-    """The grouped path takes tiles biggest first where tile sizes mix."""
+def test_tile_order_chosen_between_9_and_80_routes_per_expert():
+    """The grouped path takes tiles biggest first where tile sizes mix and the
+    launch has more than one round of workgroups (one per CU)."""
     wl = S.WORKLOADS["kimi_tp8"]
-    for T, want in ((256, 0), (1024, 1), (2048, 1)):
+    for T, want in ((256, 0), (512, 1), (1024, 1), (2048, 1), (4096, 0)):
         assert B.get_plan(B.desc_for(wl, T)).tile_order == want, T
     assert B.get_plan(B.desc_for(wl, 8)).tile_order == 0   # small batch
-    # 192 routes per expert: mostly full tiles
-    assert B.get_plan(B.desc_for(S.WORKLOADS["relu2_skew"], 4096)).tile_order == 0
+    r2 = S.WORKLOADS["relu2_skew"]
+    assert B.get_plan(B.desc_for(r2, 1024)).tile_order == 1   # 48 routes per expert
+    assert B.get_plan(B.desc_for(r2, 2048)).tile_order == 0   # 96: mostly full tiles
+    assert B.get_plan(B.desc_for(r2, 4096)).tile_order == 0
+    # 64 routes per expert, but 24 workgroups: one round, no tail to shorten
+    assert B.get_plan(B.desc_for(S.WORKLOADS["tiny"], 256)).tile_order == 0
 
 
 def test_activations_formed_in_the_down_launch_after_split_k():

@@ -282,9 +282,21 @@ Plan make_plan(const w4a16_moe_desc_t* d) {
   // -> 495 us at 2048 tokens, 361 -> 358 at 1024, 281 -> 283 at 256; the
   // 32-of-256 share 461 -> 423 at 2048, 231 -> 227 at 512; the skewed ReLU^2
   // model (mostly full tiles) 1035 -> 1055 at 4096 tokens, 355 -> 357 at 1024.
+  // Refined by forced runs (route order / biggest first, cold us): the Kimi
+  // shard 313 / 307 at 512 tokens (10.7 routes per expert); the DeepSeek
+  // share 236 / 224, 276 / 266, 463 / 447 at 512-2048 (16-64); the
+  // per-channel model 109 / 106 and 235 / 228 at 256 and 1024 (17, 68); the
+  // skewed ReLU^2 model 363 / 354 at 1024 (48) but 626 / 652 at 2048 (96);
+  // the tiny model 26 / 27 at 256, whose 24 workgroups are one round: the
+  // order only shortens the tail of a launch of several rounds.
   if (pl.path == 1 && pl.R > 0) {
     const double rpe = routes_per_touched_expert(d, pl.R, true);
-    pl.tile_sort = rpe >= w4moe::kTileSortMinRoutes && rpe <= w4moe::kTileSortMaxRoutes;
+    const double Ed = static_cast<double>(E);
+    const double local = static_cast<double>(pl.R) * share;
+    const double touched = Ed * (1.0 - std::pow(1.0 - 1.0 / Ed, local));
+    const double wgs = touched * std::ceil(rpe / pl.bm) * pl.n_tiles_up;
+    pl.tile_sort = rpe >= w4moe::kTileSortMinRoutes && rpe <= w4moe::kTileSortMaxRoutes &&
+                   wgs > w4moe::kComputeUnits;
     if (d->force_tile_order == 1) pl.tile_sort = false;
     if (d->force_tile_order == 2) pl.tile_sort = true;
   }

@@ -176,8 +176,8 @@ hipError_t launch_route_prep(const int32_t* ids, int R, int E, int off, int bm, 
 constexpr int kResidentK = 256;      // reduction the resident down kernel holds in LDS
 // tile launches take tiles biggest first between these expected valid routes
 // per touched expert (tiles of mixed sizes; far above, most tiles are full)
-constexpr double kTileSortMinRoutes = 12.0;
-constexpr double kTileSortMaxRoutes = 128.0;
+constexpr double kTileSortMinRoutes = 9.0;
+constexpr double kTileSortMaxRoutes = 80.0;
 constexpr int kSplitkNsub = 2;       // 16-row weight subtiles per wave in the split-K kernel
 constexpr int kSplitkPassRows = kTileWaves * 16 * kSplitkNsub;  // weight rows per column pass
 constexpr int kSplitkMaxLds = 78 * 1024;   // two workgroups per CU
