@@ -61,22 +61,19 @@ __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
 }
 
-// Inclusive prefix sum over the lanes of a wave (kRowsOnly: over each 16-lane
-// row).  Shift-and-add steps of 1, 2, 4 and 8 lanes inside the rows through
-// DPP row shifts (a lane shifted in from outside its row reads 0); then the
-// total of rows 0 and 2 is added to rows 1 and 3 (broadcast of lanes 15 and
-// 47), and the total of rows 0-1 to rows 2-3 (broadcast of lane 31).  No LDS
-// round trip, unlike a shuffle.
-template <bool kRowsOnly = false>
+// Inclusive prefix sum over the 64 lanes of a wave.  Shift-and-add steps of
+// 1, 2, 4 and 8 lanes inside each 16-lane row through DPP row shifts (a lane
+// shifted in from outside its row reads 0); then the totals of rows 0 and 2
+// are added to rows 1 and 3 (broadcast of lanes 15 and 47), and the total of
+// rows 0-1 to rows 2-3 (broadcast of lane 31).  No LDS round trip, unlike a
+// shuffle.
 __device__ __forceinline__ int wave_incl_scan(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
-  if (!kRowsOnly) {
-    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
-    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  }
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return x;
 }
 
